@@ -1,0 +1,316 @@
+"""Python handle on the CPU oracle (``oracle/qt_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: the slow, plain float64 reference the HIP path is
+checked against.  Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU
+baseline leg of ``bench.py`` may import this package; the library under
+``streaming_tts_decode_amd`` never does, and the two share no code.
+
+Functions whose result has no independent pin say so in their docstring
+("parity unpinned"); every other one is pinned by ``tests/test_oracle_*.py``.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "qt_oracle.c")
+_LIB = os.path.join(_HERE, "liborc.so")
+_lib = None
+
+MODE_FULL, MODE_TALKER, MODE_PREDICTOR = 0, 1, 2
+_MODES = {"full": MODE_FULL, "talker": MODE_TALKER, "predictor": MODE_PREDICTOR}
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (portable x86-64 code, no fast-math)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        cmd = ["gcc", "-std=c99", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall",
+               "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+# ---------------------------------------------------------------- ctypes types
+class Dims(C.Structure):
+    _fields_ = [("layers", C.c_int32), ("hidden", C.c_int32), ("n_q", C.c_int32),
+                ("n_kv", C.c_int32), ("head_dim", C.c_int32), ("ffn", C.c_int32),
+                ("rope_theta", C.c_double), ("eps", C.c_double)]
+
+
+class Mat(C.Structure):
+    _fields_ = [("w", C.c_void_p), ("q", C.c_void_p), ("s", C.c_void_p),
+                ("rows", C.c_int32), ("cols", C.c_int32)]
+
+
+class Layer(C.Structure):
+    _fields_ = [("in_norm", C.c_void_p), ("q_norm", C.c_void_p), ("k_norm", C.c_void_p),
+                ("post_norm", C.c_void_p), ("q", Mat), ("k", Mat), ("v", Mat), ("o", Mat),
+                ("gate", Mat), ("up", Mat), ("down", Mat)]
+
+
+class Stack(C.Structure):
+    _fields_ = [("dims", Dims), ("layers", C.POINTER(Layer)), ("final_norm", C.c_void_p)]
+
+
+class Model(C.Structure):
+    _fields_ = [("talker", Stack), ("predictor", Stack), ("codec_head", Mat),
+                ("projection", Mat), ("lm_heads", C.POINTER(Mat)),
+                ("embeds", C.POINTER(C.c_void_p)), ("talker_vocab", C.c_int32),
+                ("code_vocab", C.c_int32), ("cb0_range", C.c_int32),
+                ("n_codebooks", C.c_int32)]
+
+
+_dp = C.POINTER(C.c_double)
+_ip = C.POINTER(C.c_int32)
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        L = C.CDLL(_LIB)
+        L.orc_bf16_to_f64.restype = C.c_double
+        L.orc_bf16_to_f64.argtypes = [C.c_uint16]
+        L.orc_rmsnorm.argtypes = [_dp, C.c_void_p, C.c_int32, C.c_double, _dp]
+        L.orc_rope.argtypes = [_dp, C.c_int32, C.c_int64, C.c_double]
+        L.orc_silu.restype = C.c_double
+        L.orc_silu.argtypes = [C.c_double]
+        L.orc_linear.argtypes = [C.POINTER(Mat), _dp, _dp]
+        L.orc_attend.argtypes = [_dp, _dp, _dp, C.c_int32, C.c_int64, C.c_int32, _dp]
+        L.orc_gqa.argtypes = [_dp, _dp, _dp, C.c_int32, C.c_int32, C.c_int32, C.c_int32, _dp]
+        L.orc_argmax.restype = C.c_int32
+        L.orc_argmax.argtypes = [_dp, C.c_int32]
+        L.orc_quantize_int8.restype = C.c_int64
+        L.orc_quantize_int8.argtypes = [C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_void_p]
+        L.orc_stack_forward.restype = C.c_int32
+        L.orc_stack_forward.argtypes = [C.POINTER(Stack), _dp, C.c_int32, C.c_int32, _dp, _dp,
+                                        C.c_int32]
+        L.orc_frame.restype = C.c_int32
+        L.orc_frame.argtypes = [C.POINTER(Model), C.c_int32, _dp, _dp, C.c_int32, _dp, _dp,
+                                C.c_int32, _ip, _ip, _dp, _dp, _ip, _dp]
+        _lib = L
+    return _lib
+
+
+def _d(a):
+    return a.ctypes.data_as(_dp)
+
+
+def _f64(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    b = np.asarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+# ---------------------------------------------------------------- pieces
+def rmsnorm(x, g_bits, eps: float = 1e-6) -> np.ndarray:
+    x = _f64(x).copy()
+    g = np.ascontiguousarray(g_bits, dtype=np.uint16)
+    y = np.empty_like(x)
+    lib().orc_rmsnorm(_d(x), g.ctypes.data, x.size, eps, _d(y))
+    return y
+
+
+def rope(v, pos: int, theta: float = 1e6) -> np.ndarray:
+    v = _f64(v).copy()
+    lib().orc_rope(_d(v), v.size, int(pos), theta)
+    return v
+
+
+def silu(z: float) -> float:
+    return lib().orc_silu(float(z))
+
+
+def attend(q, K, V) -> np.ndarray:
+    q, K, V = _f64(q), _f64(K), _f64(V)
+    n, d = K.shape
+    out = np.empty(d)
+    lib().orc_attend(_d(q), _d(K), _d(V), n, d, d, _d(out))
+    return out
+
+
+def gqa(q, K, V) -> np.ndarray:
+    """q [n_q, d]; K, V [n_pos, n_kv, d] -> [n_q, d]."""
+    q, K, V = _f64(q), _f64(K), _f64(V)
+    n_q, d = q.shape
+    n_pos, n_kv, _ = K.shape
+    out = np.empty((n_q, d))
+    lib().orc_gqa(_d(q), _d(K), _d(V), n_pos, n_q, n_kv, d, _d(out))
+    return out
+
+
+def argmax(v) -> int:
+    v = _f64(v)
+    return int(lib().orc_argmax(_d(v), v.size))
+
+
+def quantize_int8(w_bits):
+    """Per-row symmetric INT8 of a bf16 [rows, cols] matrix -> (q int8, s float32)."""
+    w = np.ascontiguousarray(w_bits, dtype=np.uint16)
+    rows, cols = w.shape
+    q = np.empty((rows, cols), dtype=np.int8)
+    s = np.empty(rows, dtype=np.float32)
+    lib().orc_quantize_int8(w.ctypes.data, rows, cols, q.ctypes.data, s.ctypes.data)
+    return q, s
+
+
+def linear(w_bits, x, q=None, s=None) -> np.ndarray:
+    w = np.ascontiguousarray(w_bits, dtype=np.uint16)
+    m = Mat()
+    m.rows, m.cols = w.shape
+    m.w = w.ctypes.data
+    if q is not None:
+        q = np.ascontiguousarray(q, dtype=np.int8)
+        s = np.ascontiguousarray(s, dtype=np.float32)
+        m.q, m.s = q.ctypes.data, s.ctypes.data
+    x = _f64(x)
+    y = np.empty(m.rows)
+    lib().orc_linear(C.byref(m), _d(x), _d(y))
+    return y
+
+
+# ---------------------------------------------------------------- model
+class OracleModel:
+    """The oracle's view of one set of model weights.
+
+    ``weights`` maps tensor name -> bfloat16 bits (np.uint16).  With
+    ``int8=True`` every linear weight is quantized by the oracle's own
+    quantizer at construction (embeddings and norm gains stay bf16)."""
+
+    def __init__(self, dims, weights: dict, int8: bool = False):
+        self.dims = dims
+        self.int8 = int8
+        self._keep = []
+        self.quantized = {}
+        W = {k: np.ascontiguousarray(v, dtype=np.uint16) for k, v in weights.items()}
+        self._keep.append(W)
+
+        def mat(name):
+            w = W[name]
+            m = Mat()
+            m.rows, m.cols = w.shape
+            m.w = w.ctypes.data
+            if int8:
+                q, s = quantize_int8(w)
+                self.quantized[name] = (q, s)
+                self._keep += [q, s]
+                m.q, m.s = q.ctypes.data, s.ctypes.data
+            return m
+
+        def stack(prefix, d):
+            arr = (Layer * d.layers)()
+            for l in range(d.layers):
+                p = f"{prefix}.layers.{l}."
+                L = arr[l]
+                L.in_norm = W[p + "input_norm"].ctypes.data
+                L.q_norm = W[p + "q_norm"].ctypes.data
+                L.k_norm = W[p + "k_norm"].ctypes.data
+                L.post_norm = W[p + "post_norm"].ctypes.data
+                L.q, L.k, L.v = mat(p + "q_proj"), mat(p + "k_proj"), mat(p + "v_proj")
+                L.o = mat(p + "o_proj")
+                L.gate, L.up, L.down = mat(p + "gate_proj"), mat(p + "up_proj"), mat(p + "down_proj")
+            self._keep.append(arr)
+            s = Stack()
+            s.dims = Dims(d.layers, d.hidden, d.n_q, d.n_kv, d.head_dim, d.ffn,
+                          float(d.rope_theta), float(d.eps))
+            s.layers = C.cast(arr, C.POINTER(Layer))
+            s.final_norm = W[prefix + ".final_norm"].ctypes.data
+            return s
+
+        m = Model()
+        m.talker = stack("talker", dims.talker)
+        m.predictor = stack("predictor", dims.predictor)
+        m.codec_head = mat("talker.codec_head")
+        m.projection = mat("projection")
+        heads = (Mat * dims.n_steps)()
+        embeds = (C.c_void_p * dims.n_steps)()
+        for i in range(dims.n_steps):
+            heads[i] = mat(f"predictor.lm_head.{i}")
+            embeds[i] = W[f"predictor.codec_embed.{i}"].ctypes.data
+        self._keep += [heads, embeds]
+        m.lm_heads = C.cast(heads, C.POINTER(Mat))
+        m.embeds = C.cast(embeds, C.POINTER(C.c_void_p))
+        m.talker_vocab, m.code_vocab = dims.talker_vocab, dims.code_vocab
+        m.cb0_range, m.n_codebooks = dims.cb0_range, dims.n_codebooks
+        self.model = m
+        self.stacks = {"talker": m.talker, "predictor": m.predictor}
+
+    # -- a session's Talker cache, float64 [layers, cap, n_kv, hd]
+    def new_cache(self, capacity: int, k_bits=None, v_bits=None, which="talker"):
+        d = getattr(self.dims, which)
+        shape = (d.layers, capacity, d.n_kv, d.head_dim)
+        kc, vc = np.zeros(shape), np.zeros(shape)
+        if k_bits is not None:
+            L = k_bits.shape[1]
+            kc[:, :L] = bf16_to_f64(k_bits)
+            vc[:, :L] = bf16_to_f64(v_bits)
+        return kc, vc
+
+    def stack_forward(self, which: str, x, pos0: int, kc, vc) -> np.ndarray:
+        x = _f64(x).copy()
+        n_new = x.shape[0]
+        rc = lib().orc_stack_forward(C.byref(self.stacks[which]), _d(x), n_new, pos0,
+                                     _d(kc), _d(vc), kc.shape[1])
+        if rc:
+            raise ValueError(f"orc_stack_forward failed ({rc})")
+        return x
+
+    def frame(self, mode: str, kc=None, vc=None, length: int = 0, talker_in=None,
+              h_in=None, tok0: int = 0, forced=None):
+        """One frame for one session.  Returns (outputs dict, new length)."""
+        d = self.dims
+        L = C.c_int32(length)
+        logits0 = np.zeros(d.talker_vocab)
+        logits_pred = np.zeros((d.n_steps, d.code_vocab))
+        tokens = np.full(d.n_codebooks, -1, dtype=np.int32)
+        h_out = np.zeros(d.talker.hidden)
+        ti = _f64(talker_in) if talker_in is not None else None
+        hi = _f64(h_in) if h_in is not None else None
+        fz = np.ascontiguousarray(forced, dtype=np.int32) if forced is not None else None
+        if kc is None:
+            kc, vc = np.zeros((1,)), np.zeros((1,))
+            cap = 0
+        else:
+            cap = kc.shape[1]
+        rc = lib().orc_frame(C.byref(self.model), _MODES[mode],
+                             _d(ti) if ti is not None else None,
+                             _d(hi) if hi is not None else None, int(tok0),
+                             _d(kc), _d(vc), cap, C.byref(L),
+                             fz.ctypes.data_as(_ip) if fz is not None else None,
+                             _d(logits0), _d(logits_pred), tokens.ctypes.data_as(_ip), _d(h_out))
+        if rc:
+            raise ValueError(f"orc_frame failed ({rc})")
+        return {"logits0": logits0, "logits_pred": logits_pred, "tokens": tokens,
+                "h": h_out}, L.value
+
+    def run_session(self, mode: str, frames: int, talker_in=None, k_bits=None, v_bits=None,
+                    length: int = 0, h_in=None, tok0=None, forced=None):
+        """Run `frames` consecutive frames of one session (free-running unless
+        `forced` [frames, n_codebooks] is given).  Inputs are bf16 bits:
+        talker_in / h_in [frames, talker hidden]; k_bits / v_bits
+        [layers, length, n_kv, hd].  Returns stacked outputs."""
+        d = self.dims
+        kc = vc = None
+        if mode != "predictor":
+            kc, vc = self.new_cache(length + frames, k_bits, v_bits)
+        outs = {"logits0": [], "logits_pred": [], "tokens": [], "h": []}
+        L = length
+        for f in range(frames):
+            o, L = self.frame(mode, kc, vc, L,
+                              talker_in=bf16_to_f64(talker_in[f]) if talker_in is not None else None,
+                              h_in=bf16_to_f64(h_in[f]) if h_in is not None else None,
+                              tok0=int(tok0[f]) if tok0 is not None else 0,
+                              forced=forced[f] if forced is not None else None)
+            for k in outs:
+                outs[k].append(o[k])
+        return {k: np.stack(v) for k, v in outs.items()}
