@@ -1,0 +1,206 @@
+#!/usr/bin/env python3
+"""Throughput of the lockstep decode frame on one MI355X.
+
+A step is one decode frame for every session of the workload: the 28-layer
+Talker step, codec head + greedy codebook 0, the 2048->1024 projection and the
+15 code-predictor steps, replayed from one captured HIP graph.  The headline
+workload is the B=32 full frame (ragged Talker KV 512..2048 positions in
+16-token pages, 25 consecutive frames per sequence, bf16 weights); B=1 and
+B=6 frames are reported beside it.  Inputs are seeded synthetic tensors, already
+resident in device memory when the timed region starts.
+
+Prints one JSON line (rank 0).  `value` is codec frames per second (one codec
+frame = 16 codebook tokens for one session).
+"""
+import argparse
+import dataclasses
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+
+
+def weight_bytes(d, int8: bool) -> int:
+    """Logical weight bytes one frame streams: every decode GEMM weight once per
+    use for the whole batch (predictor layers once per predictor step)."""
+    def mat(n, k):
+        return n * k + 4 * n if int8 else 2 * n * k
+
+    def layer(x):
+        return (mat(x.q_dim + 2 * x.kv_dim, x.hidden) + mat(x.hidden, x.q_dim)
+                + mat(2 * x.ffn, x.hidden) + mat(x.hidden, x.ffn)
+                + 2 * (2 * x.hidden + 2 * x.head_dim))
+    t, p = d.talker, d.predictor
+    talker = t.layers * layer(t) + mat(d.talker_vocab + p.hidden, t.hidden) + 2 * t.hidden
+    pred_step = p.layers * layer(p) + mat(d.code_vocab, p.hidden) + 2 * p.hidden
+    return talker + d.n_steps * pred_step
+
+
+def frame_bytes(d, lengths, int8: bool) -> int:
+    """Algorithmic bytes of one frame: weights (above) plus, per session, the
+    Talker K/V read over positions 0..L (L = cached length before the frame), the
+    appended K/V, the embedding rows, the input and the fp32 logits and tokens."""
+    t = d.talker
+    kv_pos = t.layers * t.n_kv * t.head_dim * 2 * 2  # K and V, bf16, all layers
+    per_sess = 0
+    for L in lengths:
+        per_sess += kv_pos * (int(L) + 1) + kv_pos
+        per_sess += d.n_steps * d.predictor.hidden * 2 + t.hidden * 2
+        per_sess += 4 * (d.talker_vocab + d.n_steps * d.code_vocab) + 4 * d.n_codebooks
+    return weight_bytes(d, int8) + per_sess
+
+
+def run_workload(pm, w, steps, warmup, log):
+    import numpy as np
+    import torch
+
+    import synth
+    from streaming_tts_decode_amd.runtime import setup_workload
+    frames = max(w.frames, steps + warmup)
+    wcap = dataclasses.replace(w, frames=frames)
+    dec, lengths = setup_workload(wcap, pm)
+    ins = synth.frame_inputs(w)["talker_in"]  # [w.frames, B, H]
+    talker_all = torch.from_numpy(ins.view(np.int16)).to(dec.dev)
+    g = dec.capture("full", forced=False)
+    L0 = dec.kv_len.clone()
+    stream = torch.cuda.current_stream()
+    for f in range(warmup):
+        dec.talker_in.copy_(talker_all[f % w.frames], non_blocking=True)
+        dec.replay(g)
+    torch.cuda.synchronize()
+    dec.kv_len.copy_(L0)
+    dec.status.zero_()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for f in range(steps):
+        dec.talker_in.copy_(talker_all[f % w.frames], non_blocking=True)
+        dec.replay(g)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1)
+    status = int(dec.status.item())
+    if status:
+        raise RuntimeError(f"{w.name}: device status {status:#x}")
+    nbytes = sum(frame_bytes(w.dims, lengths + f, pm.int8) for f in range(steps))
+    res = {
+        "workload": w.name, "batch": w.batch, "frames": steps,
+        "ms_per_frame": ms / steps, "codec_frames_per_s": w.batch * steps / (ms / 1e3),
+        "hbm_gbs_algorithmic": nbytes / (ms / 1e3) / 1e9,
+        "bytes_per_frame": nbytes / steps, "wall_s": wall,
+    }
+    res["hbm_frac"] = res["hbm_gbs_algorithmic"] / HBM_PEAK_GBS
+    log(f"[bench] {res}")
+    dec.close()
+    return res, lengths
+
+
+def cpu_baseline(w, weights, seconds: float, log):
+    """The oracle, as it stands, on the host cores: session 0 of the workload,
+    consecutive frames until `seconds` of CPU work have run."""
+    import oracle
+    import synth
+    d = w.dims
+    t = d.talker
+    orc = oracle.OracleModel(d, weights, int8=w.int8)
+    L = int(w.lengths()[0])
+    kb, vb = synth.gen_kv(w.name, 0, t.layers, L, t.n_kv, t.head_dim)
+    ins = synth.frame_inputs(w)["talker_in"][:, 0]
+    kc, vc = orc.new_cache(L + w.frames, kb, vb)
+    n, length = 0, L
+    t0 = time.perf_counter()
+    while n < w.frames and (n == 0 or time.perf_counter() - t0 < seconds):
+        _, length = orc.frame("full", kc, vc, length, talker_in=oracle.bf16_to_f64(ins[n]))
+        n += 1
+    el = time.perf_counter() - t0
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    res = {"value": n / el, "unit": "codec frames/s", "cores": cores, "kind": "oracle",
+           "sample": f"{w.name} session 0 (L={L}), {n} consecutive full frames, float64 C oracle, "
+                     f"{el:.1f} s"}
+    log(f"[cpu] {res}")
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=25)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="C4")
+    ap.add_argument("--also", default="B1,C3", help="extra workloads reported beside the headline")
+    ap.add_argument("--int8", action="store_true", help="INT8 weight-only decode")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs on exactly one GPU (sessions shard across GPUs with no "
+              "communication; multi-GPU runs are not part of it)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import streaming_tts_decode_amd as qt
+    import synth
+    from streaming_tts_decode_amd.runtime import PackedModel
+
+    qt.lib()  # fails loudly if the HIP library is missing
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+
+    def log(msg):
+        print(msg, file=sys.stderr, flush=True)
+
+    head = synth.WORKLOADS[args.workload]
+    if args.int8:
+        head = dataclasses.replace(head, int8=True)
+    d = head.dims
+    log(f"[bench] generating weights")
+    W = synth.gen_weights(d)
+    pm = PackedModel(d, W, int8=head.int8)
+    main_res, lengths = run_workload(pm, head, args.steps, args.warmup, log)
+    extra = {}
+    for name in [x for x in args.also.split(",") if x]:
+        w = dataclasses.replace(synth.WORKLOADS[name], int8=head.int8)
+        r, _ = run_workload(pm, w, args.steps, args.warmup, log)
+        extra[f"B{w.batch}"] = {k: r[k] for k in ("codec_frames_per_s", "ms_per_frame",
+                                                  "hbm_gbs_algorithmic", "hbm_frac")}
+    pm.close()
+    cpu = None if args.no_cpu_baseline else cpu_baseline(head, W, args.cpu_seconds, log)
+
+    out = {
+        "metric": "codec frames/sec (Talker step + 15 code-predictor steps per session frame)",
+        "value": main_res["codec_frames_per_s"],
+        "unit": "codec frames/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_res["ms_per_frame"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8" if head.int8 else "bf16",
+        "data": "synthetic: seeded N(0,0.02) bf16 weights, N(0,1) inputs and prefilled KV",
+        "config": {"workload": f"{head.name}: {head.note}", "batch": head.batch,
+                   "kv_len": f"{head.len_lo}..{head.len_hi} (ragged, 16-token pages)",
+                   "frames_per_sequence": head.frames, "graph": True,
+                   "parallelism": "single GPU"},
+        "frame_hbm_gbs": main_res["hbm_gbs_algorithmic"],
+        "frame_hbm_frac": main_res["hbm_frac"],
+        "bytes_per_frame": main_res["bytes_per_frame"],
+        "other_batches": extra,
+        "roofline": None,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

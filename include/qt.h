@@ -1,0 +1,223 @@
+/*
+ * qt.h -- C ABI of the MI355X (gfx950) lockstep decode-frame library (libqt.so).
+ *
+ * One call decodes one codec frame for every active session of a
+ * Qwen3-TTS-style speech model: a Talker decoder step that emits codebook 0,
+ * the Talker-to-predictor projection, then the code-predictor steps that emit
+ * codebooks 1 .. n_codebooks-1.  Every shared weight matrix is streamed once
+ * per use for the whole batch, and all per-session state (KV pages, lengths,
+ * tokens) stays in caller-owned buffers.
+ *
+ * Sources for the operations (the pages define what is computed, not these
+ * signatures):
+ *  - "Qwen3-TTS Native v0.3.0" release notes, What changed: one batched call per
+ *    frame runs the talker and the 15-step code predictor for every active
+ *    session, each shared weight read once per frame, per-session KV and state
+ *    kept request-local; the whole frame captured once per session tuple and
+ *    replayed as a graph; opt-in INT8 weight-only decode, per-output-channel
+ *    symmetric, quantized at engine load from the BF16 weights.
+ *  - qwen.lukaloehr.com llms.txt: the token is handed from talker to predictor
+ *    device to device.
+ *  - M* "Qwen3-TTS PR 5": Graph section (paged KV, RoPE positions as Talker
+ *    resources); What changed (Talker 2048 -> predictor 1024 projection; weight
+ *    loading checks coverage in both directions); Parity section (teacher-forced
+ *    logits).
+ *  - decomputer.nl article on Qwen3-TTS serving, sections 3 and 5: the code
+ *    predictor always runs 15 steps per frame on a preallocated KV cache; no
+ *    needless CPU-GPU synchronisation.
+ *
+ * Conventions
+ *  - Every pointer documented "device" is a HIP device pointer on the current
+ *    device; "host" pointers are ordinary host memory.  The library never
+ *    allocates device memory: the caller passes every buffer (packed weights,
+ *    workspace, KV pages, inputs, outputs).
+ *  - bf16 tensors are raw bfloat16 bit patterns (uint16), row-major.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Calls that take a
+ *    stream only enqueue work on it and never synchronise the host.
+ *  - Errors: every function returns a qt_status; host-detectable problems are
+ *    reported before anything is enqueued.  qt_last_error() gives a
+ *    thread-local description of the most recent failure.  Conditions only the
+ *    device can see (a session whose cache is full, a page id out of range, a
+ *    token out of range, a NaN logit) OR a bit into the caller's `status` word
+ *    and skip that session's writes; the host reads the word whenever it likes.
+ *  - Handles (qt_model, qt_graph) are opaque host objects owned by the caller
+ *    and released with the matching destroy call.  A qt_model refers to the
+ *    caller's packed-weight buffer, which must outlive it.
+ */
+#ifndef QT_H
+#define QT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QT_ABI_VERSION 1
+
+typedef enum {
+  QT_OK = 0,
+  QT_E_INVALID_ARG = 1,       /* null pointer, non-positive size, bad enum value */
+  QT_E_SHAPE = 2,             /* a dimension the kernels do not support, or a tensor shape mismatch */
+  QT_E_DTYPE = 3,             /* a tensor of the wrong element type */
+  QT_E_MISSING_TENSOR = 4,    /* qt_load_weights: an expected weight is absent */
+  QT_E_UNEXPECTED_TENSOR = 5, /* qt_load_weights: an unknown or duplicated weight name */
+  QT_E_CAPACITY = 6,          /* a buffer smaller than required, or a batch above the workspace's */
+  QT_E_STATE = 7,             /* the handle is not usable for this call */
+  QT_E_HIP = 8,               /* a HIP runtime call failed; see qt_last_error() */
+  QT_E_UNSUPPORTED = 9        /* a valid request this build does not implement */
+} qt_status;
+
+typedef enum { QT_BF16 = 0, QT_F32 = 1, QT_I8 = 2, QT_I32 = 3 } qt_dtype;
+
+typedef enum {
+  QT_MODE_FULL = 0,      /* Talker step + projection + all predictor steps */
+  QT_MODE_TALKER = 1,    /* Talker step and codebook 0 only */
+  QT_MODE_PREDICTOR = 2  /* projection + predictor steps from a given hidden state and token */
+} qt_mode;
+
+/* Bits OR-ed into qt_frame_outputs.status by the device. */
+#define QT_STATUS_KV_OVERFLOW 1u /* kv_len[b] + 1 > max_pages * page_size: session b skipped */
+#define QT_STATUS_BAD_PAGE 2u    /* a page id outside [0, num_pages): that page is read as zeros */
+#define QT_STATUS_BAD_TOKEN 4u   /* a forced / input token outside the code vocabulary: 0 used */
+#define QT_STATUS_NAN 8u         /* a NaN logit was produced */
+
+/* One decoder stack (Qwen3-style: pre-norm, q/k RMSNorm, rotate-half RoPE,
+ * grouped-query attention, SwiGLU).  This build supports head_dim = 128,
+ * n_q_heads = 2 * n_kv_heads, hidden, n_q_heads*head_dim and ffn multiples
+ * of 512. */
+typedef struct {
+  int32_t layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn;
+  float rope_theta, rms_eps;
+} qt_decoder_cfg;
+
+typedef struct {
+  qt_decoder_cfg talker, predictor;
+  int32_t talker_vocab; /* rows of the Talker codec head (3072) */
+  int32_t code_vocab;   /* rows of each predictor embedding and head (2048) */
+  int32_t cb0_range;    /* codebook-0 argmax runs over [0, cb0_range) (2048) */
+  int32_t n_codebooks;  /* 1 Talker codebook + (n_codebooks - 1) predictor steps, 2..16 */
+  int32_t page_size;    /* Talker KV page size in positions; this build: 16 */
+} qt_model_cfg;
+
+/* A named source tensor for qt_load_weights: device pointer, bf16, [rows, cols];
+ * vectors (norm gains) are rows = 1, cols = n. */
+typedef struct {
+  const char* name;
+  const void* data;
+  int32_t dtype;
+  int64_t rows, cols;
+} qt_tensor;
+
+typedef struct qt_model qt_model;
+typedef struct qt_graph qt_graph;
+
+typedef struct {
+  int32_t batch;             /* B >= 1 active sessions */
+  int32_t* kv_len;           /* device int32 [B]: Talker positions already cached per session;
+                                the frame appends at position kv_len[b] and then adds 1
+                                (FULL and TALKER modes) */
+  const int32_t* page_table; /* device int32 [B][max_pages]: page id of positions
+                                [i*page_size, (i+1)*page_size) of session b */
+  int32_t max_pages;         /* row length of page_table; capacity = max_pages * page_size */
+} qt_sessions;
+
+typedef struct {
+  void* k_pages;     /* device bf16 [talker layers][num_pages][n_kv][page_size][head_dim] */
+  void* v_pages;     /* same layout; cached keys are stored after q/k-norm and RoPE */
+  int32_t num_pages;
+} qt_kv_caches;
+
+typedef struct {
+  int32_t mode;            /* qt_mode */
+  const void* talker_in;   /* device bf16 [B][talker hidden]: the Talker input (FULL, TALKER) */
+  const void* h_in;        /* device bf16 [B][talker hidden]: the post-norm Talker hidden (PREDICTOR) */
+  const int32_t* tok0_in;  /* device int32 [B]: codebook-0 tokens (PREDICTOR) */
+  const int32_t* forced;   /* device int32 [B][n_codebooks] or NULL: teacher forcing; predictor
+                              step k embeds forced[b][k-1] instead of the frame's own token */
+} qt_frame_inputs;
+
+typedef struct {
+  float* logits0;      /* device f32 [B][talker_vocab] (FULL, TALKER) */
+  float* logits_pred;  /* device f32 [B][n_codebooks-1][code_vocab] (FULL, PREDICTOR) */
+  int32_t* tokens;     /* device int32 [B][n_codebooks]: the frame's greedy tokens (lowest index
+                          wins ties); TALKER fills column 0, PREDICTOR copies tok0_in into it */
+  uint32_t* status;    /* device uint32 [1]: QT_STATUS_* bits are OR-ed in; the caller clears it */
+} qt_frame_outputs;
+
+/* Text of the last failure on this thread ("" if none). */
+const char* qt_last_error(void);
+int32_t qt_abi_version(void);
+
+/* Check that the configuration is one the kernels support.  QT_E_SHAPE otherwise. */
+qt_status qt_validate_cfg(const qt_model_cfg* cfg);
+
+/* Bytes of the packed-weight buffer for this configuration (int8_mode 0: bf16, 1: INT8). */
+qt_status qt_packed_bytes(const qt_model_cfg* cfg, int32_t int8_mode, uint64_t* bytes);
+
+/* Bytes of the per-call workspace for up to max_batch sessions and page tables of
+ * max_pages entries. */
+qt_status qt_workspace_bytes(const qt_model_cfg* cfg, int32_t max_batch, int32_t max_pages,
+                             uint64_t* bytes);
+
+/* Validate and pack the model weights into the caller's device buffer `packed`
+ * (at least qt_packed_bytes bytes, 256-byte aligned).  `tensors` (host array of
+ * n_tensors entries) must name every expected weight exactly once with the
+ * expected shape and dtype bf16, and nothing else (checked in both directions:
+ * QT_E_MISSING_TENSOR / QT_E_UNEXPECTED_TENSOR / QT_E_SHAPE / QT_E_DTYPE).
+ * Names: talker.layers.{l}.{input_norm,q_proj,k_proj,v_proj,q_norm,k_norm,o_proj,
+ * post_norm,gate_proj,up_proj,down_proj}, talker.final_norm, talker.codec_head,
+ * projection, predictor.layers.{l}.{...same...}, predictor.final_norm,
+ * predictor.codec_embed.{i}, predictor.lm_head.{i} for i < n_codebooks-1.
+ * int8_mode 1 quantizes every decode GEMM weight (attention, FFN, projection, codec
+ * head and predictor heads) with qt_quantize_int8's arithmetic; embeddings and norm
+ * gains stay bf16.  Packing is enqueued on `stream`; the source tensors may be
+ * freed once it has completed.  *out receives a handle for qt_frame_decode. */
+qt_status qt_load_weights(const qt_model_cfg* cfg, const qt_tensor* tensors, int32_t n_tensors,
+                          int32_t int8_mode, void* packed, uint64_t packed_bytes, void* stream,
+                          qt_model** out);
+
+/* Per-output-channel symmetric INT8 ("Qwen3-TTS Native v0.3.0", What changed):
+ * for each row r of the device bf16 [rows, cols] matrix w,
+ *   scale[r] = f32(max_k |w[r][k]|) / 127   (IEEE float32 divide),
+ *   q[r][k]  = clamp(round_half_even(f32(w[r][k]) / scale[r]), -127, 127)
+ * with an all-zero row giving scale 0 and q 0.  q (device int8 [rows, cols]) and
+ * scale (device f32 [rows]) are written on `stream`. */
+qt_status qt_quantize_int8(const void* w_bf16, int64_t rows, int64_t cols, int8_t* q,
+                           float* scale, void* stream);
+
+/* Copy the packed INT8 form of the named decode weight back out in its source row
+ * order: q (device int8 [rows, cols]) and scale (device f32 [rows]).  For checking
+ * that the weights a model decodes with are the quantizer's output.  QT_E_STATE if
+ * the model was loaded in bf16 mode. */
+qt_status qt_model_export_int8(const qt_model* model, const char* name, int8_t* q, float* scale,
+                               void* stream);
+
+/* Decode one frame for all sessions (see qt_mode).  Enqueues every kernel of the frame
+ * on `stream` and returns without synchronising.  `workspace` is a device buffer of at
+ * least qt_workspace_bytes(cfg, B, max_pages) bytes; the caller must not touch it while
+ * a frame that uses it is in flight, and concurrent frames need separate workspaces.
+ * Outputs are overwritten; kv_len is advanced on the device. */
+qt_status qt_frame_decode(qt_model* model, const qt_sessions* sessions, const qt_kv_caches* kv,
+                          const qt_frame_inputs* in, const qt_frame_outputs* out, void* workspace,
+                          uint64_t workspace_bytes, void* stream);
+
+/* Capture the same frame as qt_frame_decode into a HIP graph and instantiate it.  The
+ * graph bakes in every pointer and the batch size: the caller keeps all buffers alive
+ * and at the same addresses until qt_graph_destroy, and changes per-frame data only by
+ * rewriting buffer contents (inputs, forced tokens, kv_len). */
+qt_status qt_frame_graph_create(qt_model* model, const qt_sessions* sessions,
+                                const qt_kv_caches* kv, const qt_frame_inputs* in,
+                                const qt_frame_outputs* out, void* workspace,
+                                uint64_t workspace_bytes, qt_graph** out_graph);
+
+/* Replay a captured frame on `stream` (enqueue only). */
+qt_status qt_frame_graph_launch(qt_graph* graph, void* stream);
+
+void qt_graph_destroy(qt_graph* graph);
+void qt_model_destroy(qt_model* model);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

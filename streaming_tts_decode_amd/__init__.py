@@ -1,0 +1,211 @@
+"""Python binding of libqt.so, the gfx950 lockstep decode-frame library.
+
+The functions below carry the C ABI's names (see include/qt.h) and only
+marshal arguments: every step of the frame runs in the library's HIP kernels.
+Importing this package never falls back to anything else: if libqt.so is
+missing or cannot be loaded, `lib()` raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libqt.so")
+
+QT_OK = 0
+STATUS_NAMES = {0: "QT_OK", 1: "QT_E_INVALID_ARG", 2: "QT_E_SHAPE", 3: "QT_E_DTYPE",
+                4: "QT_E_MISSING_TENSOR", 5: "QT_E_UNEXPECTED_TENSOR", 6: "QT_E_CAPACITY",
+                7: "QT_E_STATE", 8: "QT_E_HIP", 9: "QT_E_UNSUPPORTED"}
+QT_BF16, QT_F32, QT_I8, QT_I32 = 0, 1, 2, 3
+MODE_FULL, MODE_TALKER, MODE_PREDICTOR = 0, 1, 2
+MODES = {"full": MODE_FULL, "talker": MODE_TALKER, "predictor": MODE_PREDICTOR}
+STATUS_KV_OVERFLOW, STATUS_BAD_PAGE, STATUS_BAD_TOKEN, STATUS_NAN = 1, 2, 4, 8
+
+EXPORTED = ["qt_last_error", "qt_abi_version", "qt_validate_cfg", "qt_packed_bytes",
+            "qt_workspace_bytes", "qt_load_weights", "qt_quantize_int8", "qt_model_export_int8",
+            "qt_frame_decode", "qt_frame_graph_create", "qt_frame_graph_launch",
+            "qt_graph_destroy", "qt_model_destroy"]
+
+
+class QtError(RuntimeError):
+    def __init__(self, status: int, fn: str, msg: str):
+        super().__init__(f"{fn}: {STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+class DecoderCfg(C.Structure):
+    _fields_ = [("layers", C.c_int32), ("hidden", C.c_int32), ("n_q_heads", C.c_int32),
+                ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32), ("ffn", C.c_int32),
+                ("rope_theta", C.c_float), ("rms_eps", C.c_float)]
+
+
+class ModelCfg(C.Structure):
+    _fields_ = [("talker", DecoderCfg), ("predictor", DecoderCfg), ("talker_vocab", C.c_int32),
+                ("code_vocab", C.c_int32), ("cb0_range", C.c_int32), ("n_codebooks", C.c_int32),
+                ("page_size", C.c_int32)]
+
+
+class Tensor(C.Structure):
+    _fields_ = [("name", C.c_char_p), ("data", C.c_void_p), ("dtype", C.c_int32),
+                ("rows", C.c_int64), ("cols", C.c_int64)]
+
+
+class Sessions(C.Structure):
+    _fields_ = [("batch", C.c_int32), ("kv_len", C.c_void_p), ("page_table", C.c_void_p),
+                ("max_pages", C.c_int32)]
+
+
+class KvCaches(C.Structure):
+    _fields_ = [("k_pages", C.c_void_p), ("v_pages", C.c_void_p), ("num_pages", C.c_int32)]
+
+
+class FrameInputs(C.Structure):
+    _fields_ = [("mode", C.c_int32), ("talker_in", C.c_void_p), ("h_in", C.c_void_p),
+                ("tok0_in", C.c_void_p), ("forced", C.c_void_p)]
+
+
+class FrameOutputs(C.Structure):
+    _fields_ = [("logits0", C.c_void_p), ("logits_pred", C.c_void_p), ("tokens", C.c_void_p),
+                ("status", C.c_void_p)]
+
+
+_lib = None
+_P = C.c_void_p
+
+
+def lib():
+    """Load libqt.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m streaming_tts_decode_amd.build` (hipcc, gfx950)")
+        L = C.CDLL(LIB_PATH)
+        st = C.c_int
+        L.qt_last_error.restype = C.c_char_p
+        L.qt_last_error.argtypes = []
+        L.qt_abi_version.restype = C.c_int32
+        L.qt_validate_cfg.restype = st
+        L.qt_validate_cfg.argtypes = [C.POINTER(ModelCfg)]
+        L.qt_packed_bytes.restype = st
+        L.qt_packed_bytes.argtypes = [C.POINTER(ModelCfg), C.c_int32, C.POINTER(C.c_uint64)]
+        L.qt_workspace_bytes.restype = st
+        L.qt_workspace_bytes.argtypes = [C.POINTER(ModelCfg), C.c_int32, C.c_int32,
+                                         C.POINTER(C.c_uint64)]
+        L.qt_load_weights.restype = st
+        L.qt_load_weights.argtypes = [C.POINTER(ModelCfg), C.POINTER(Tensor), C.c_int32, C.c_int32,
+                                      _P, C.c_uint64, _P, C.POINTER(_P)]
+        L.qt_quantize_int8.restype = st
+        L.qt_quantize_int8.argtypes = [_P, C.c_int64, C.c_int64, _P, _P, _P]
+        L.qt_model_export_int8.restype = st
+        L.qt_model_export_int8.argtypes = [_P, C.c_char_p, _P, _P, _P]
+        frame_args = [_P, C.POINTER(Sessions), C.POINTER(KvCaches), C.POINTER(FrameInputs),
+                      C.POINTER(FrameOutputs), _P, C.c_uint64]
+        L.qt_frame_decode.restype = st
+        L.qt_frame_decode.argtypes = frame_args + [_P]
+        L.qt_frame_graph_create.restype = st
+        L.qt_frame_graph_create.argtypes = frame_args + [C.POINTER(_P)]
+        L.qt_frame_graph_launch.restype = st
+        L.qt_frame_graph_launch.argtypes = [_P, _P]
+        L.qt_graph_destroy.restype = None
+        L.qt_graph_destroy.argtypes = [_P]
+        L.qt_model_destroy.restype = None
+        L.qt_model_destroy.argtypes = [_P]
+        _lib = L
+    return _lib
+
+
+def _check(status: int, fn: str):
+    if status != QT_OK:
+        raise QtError(status, fn, lib().qt_last_error().decode())
+
+
+def make_cfg(dims) -> ModelCfg:
+    """qt_model_cfg from a dimension record with talker/predictor sub-records."""
+    def dec(d):
+        return DecoderCfg(d.layers, d.hidden, d.n_q, d.n_kv, d.head_dim, d.ffn,
+                          float(d.rope_theta), float(d.eps))
+    return ModelCfg(dec(dims.talker), dec(dims.predictor), dims.talker_vocab, dims.code_vocab,
+                    dims.cb0_range, dims.n_codebooks, dims.page_size)
+
+
+# --------------------------------------------------------------------------- ABI calls
+def qt_last_error() -> str:
+    return lib().qt_last_error().decode()
+
+
+def qt_abi_version() -> int:
+    return lib().qt_abi_version()
+
+
+def qt_validate_cfg(cfg: ModelCfg) -> None:
+    _check(lib().qt_validate_cfg(C.byref(cfg)), "qt_validate_cfg")
+
+
+def qt_packed_bytes(cfg: ModelCfg, int8_mode: int) -> int:
+    n = C.c_uint64()
+    _check(lib().qt_packed_bytes(C.byref(cfg), int8_mode, C.byref(n)), "qt_packed_bytes")
+    return n.value
+
+
+def qt_workspace_bytes(cfg: ModelCfg, max_batch: int, max_pages: int) -> int:
+    n = C.c_uint64()
+    _check(lib().qt_workspace_bytes(C.byref(cfg), max_batch, max_pages, C.byref(n)),
+           "qt_workspace_bytes")
+    return n.value
+
+
+def qt_load_weights(cfg: ModelCfg, tensors, int8_mode: int, packed_ptr: int, packed_bytes: int,
+                    stream: int = 0) -> int:
+    """tensors: iterable of (name, device_ptr, dtype, rows, cols).  Returns the model handle."""
+    tensors = list(tensors)
+    arr = (Tensor * len(tensors))()
+    names = []
+    for i, (name, ptr, dt, rows, cols) in enumerate(tensors):
+        nb = name.encode()
+        names.append(nb)
+        arr[i] = Tensor(nb, ptr, dt, rows, cols)
+    out = _P()
+    _check(lib().qt_load_weights(C.byref(cfg), arr, len(tensors), int8_mode, packed_ptr,
+                                 packed_bytes, stream, C.byref(out)), "qt_load_weights")
+    return out.value
+
+
+def qt_quantize_int8(w_ptr: int, rows: int, cols: int, q_ptr: int, scale_ptr: int,
+                     stream: int = 0) -> None:
+    _check(lib().qt_quantize_int8(w_ptr, rows, cols, q_ptr, scale_ptr, stream), "qt_quantize_int8")
+
+
+def qt_model_export_int8(model: int, name: str, q_ptr: int, scale_ptr: int, stream: int = 0) -> None:
+    _check(lib().qt_model_export_int8(model, name.encode(), q_ptr, scale_ptr, stream),
+           "qt_model_export_int8")
+
+
+def qt_frame_decode(model: int, sessions: Sessions, kv: KvCaches, inputs: FrameInputs,
+                    outputs: FrameOutputs, workspace_ptr: int, workspace_bytes: int,
+                    stream: int = 0) -> None:
+    _check(lib().qt_frame_decode(model, C.byref(sessions), C.byref(kv), C.byref(inputs),
+                                 C.byref(outputs), workspace_ptr, workspace_bytes, stream),
+           "qt_frame_decode")
+
+
+def qt_frame_graph_create(model: int, sessions: Sessions, kv: KvCaches, inputs: FrameInputs,
+                          outputs: FrameOutputs, workspace_ptr: int, workspace_bytes: int) -> int:
+    g = _P()
+    _check(lib().qt_frame_graph_create(model, C.byref(sessions), C.byref(kv), C.byref(inputs),
+                                       C.byref(outputs), workspace_ptr, workspace_bytes,
+                                       C.byref(g)), "qt_frame_graph_create")
+    return g.value
+
+
+def qt_frame_graph_launch(graph: int, stream: int = 0) -> None:
+    _check(lib().qt_frame_graph_launch(graph, stream), "qt_frame_graph_launch")
+
+
+def qt_graph_destroy(graph: int) -> None:
+    lib().qt_graph_destroy(graph)
+
+
+def qt_model_destroy(model: int) -> None:
+    lib().qt_model_destroy(model)

@@ -1,0 +1,751 @@
+// C ABI of the lockstep decode-frame library: argument validation, weight
+// packing, workspace layout, the per-frame kernel sequence and its HIP graph.
+// The kernels themselves live in qt_kernels.hip.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <map>
+#include <string>
+#include <vector>
+
+#include "qt.h"
+#include "qt_internal.h"
+
+using namespace qt;
+
+namespace {
+
+thread_local std::string g_err;
+
+qt_status fail(qt_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+qt_status ok() { return QT_OK; }
+
+#define QT_HIP(expr)                                                                   \
+  do {                                                                                 \
+    hipError_t e_ = (expr);                                                            \
+    if (e_ != hipSuccess)                                                              \
+      return fail(QT_E_HIP, "%s failed: %s", #expr, hipGetErrorString(e_));            \
+  } while (0)
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxBatch = 32;  // predictor step 1 carries 2B rows; the GEMMs take up to 64
+
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+// ------------------------------------------------------------------ packed layout
+struct MatSlot {
+  size_t w = 0, s = 0;  // byte offsets of the weight rows and (INT8) the scales
+  int N = 0, K = 0;
+};
+struct LayerSlots {
+  size_t in_norm = 0, q_norm = 0, k_norm = 0, post_norm = 0;
+  MatSlot qkv, o, gu, down;  // gu: gate and up rows interleaved (gate n at 2n, up n at 2n+1)
+};
+struct Plan {
+  std::vector<LayerSlots> tl, pl;
+  size_t t_final = 0, p_final = 0;
+  MatSlot t_head;  // codec head rows [0, talker_vocab) then projection rows
+  std::vector<size_t> embeds;
+  std::vector<MatSlot> heads;
+  size_t total = 0;
+};
+
+struct Planner {
+  size_t off = 0;
+  bool i8 = false;
+  size_t vec(int n) {
+    size_t o = off;
+    off = align_up(off + (size_t)n * 2);
+    return o;
+  }
+  MatSlot mat(int N, int K) {
+    MatSlot m;
+    m.N = N;
+    m.K = K;
+    m.w = off;
+    off = align_up(off + (size_t)N * K * (i8 ? 1 : 2));
+    if (i8) {
+      m.s = off;
+      off = align_up(off + (size_t)N * 4);
+    }
+    return m;
+  }
+};
+
+Plan make_plan(const qt_model_cfg& c, bool i8) {
+  Planner P;
+  P.i8 = i8;
+  Plan plan;
+  auto layers = [&](const qt_decoder_cfg& d, std::vector<LayerSlots>& v) {
+    const int qd = d.n_q_heads * d.head_dim, kvd = d.n_kv_heads * d.head_dim;
+    for (int l = 0; l < d.layers; ++l) {
+      LayerSlots L;
+      L.in_norm = P.vec(d.hidden);
+      L.q_norm = P.vec(d.head_dim);
+      L.k_norm = P.vec(d.head_dim);
+      L.post_norm = P.vec(d.hidden);
+      L.qkv = P.mat(qd + 2 * kvd, d.hidden);
+      L.o = P.mat(d.hidden, qd);
+      L.gu = P.mat(2 * d.ffn, d.hidden);
+      L.down = P.mat(d.hidden, d.ffn);
+      v.push_back(L);
+    }
+  };
+  layers(c.talker, plan.tl);
+  plan.t_final = P.vec(c.talker.hidden);
+  plan.t_head = P.mat(c.talker_vocab + c.predictor.hidden, c.talker.hidden);
+  layers(c.predictor, plan.pl);
+  plan.p_final = P.vec(c.predictor.hidden);
+  for (int i = 0; i < c.n_codebooks - 1; ++i) {
+    plan.embeds.push_back(P.vec(c.code_vocab * c.predictor.hidden));
+    plan.heads.push_back(P.mat(c.code_vocab, c.predictor.hidden));
+  }
+  plan.total = P.off;
+  return plan;
+}
+
+// Where each source tensor goes in the packed buffer.
+enum Kind { K_VEC, K_MAT, K_EMBED };
+struct Dest {
+  Kind kind;
+  int64_t rows, cols;
+  size_t vec_off = 0;      // K_VEC / K_EMBED
+  const MatSlot* mat = nullptr;
+  int row0 = 0, step = 1;  // K_MAT: source row i -> packed row row0 + i*step
+};
+
+std::map<std::string, Dest> make_dests(const qt_model_cfg& c, const Plan& plan) {
+  std::map<std::string, Dest> m;
+  auto vec = [&](const std::string& n, int len, size_t off) {
+    Dest d{K_VEC, 1, len};
+    d.vec_off = off;
+    m[n] = d;
+  };
+  auto mat = [&](const std::string& n, int64_t rows, int64_t cols, const MatSlot* s, int row0,
+                 int step) {
+    Dest d{K_MAT, rows, cols};
+    d.mat = s;
+    d.row0 = row0;
+    d.step = step;
+    m[n] = d;
+  };
+  auto layers = [&](const char* prefix, const qt_decoder_cfg& d, const std::vector<LayerSlots>& v) {
+    const int qd = d.n_q_heads * d.head_dim, kvd = d.n_kv_heads * d.head_dim;
+    for (int l = 0; l < d.layers; ++l) {
+      const std::string p = std::string(prefix) + ".layers." + std::to_string(l) + ".";
+      const LayerSlots& L = v[l];
+      vec(p + "input_norm", d.hidden, L.in_norm);
+      vec(p + "q_norm", d.head_dim, L.q_norm);
+      vec(p + "k_norm", d.head_dim, L.k_norm);
+      vec(p + "post_norm", d.hidden, L.post_norm);
+      mat(p + "q_proj", qd, d.hidden, &L.qkv, 0, 1);
+      mat(p + "k_proj", kvd, d.hidden, &L.qkv, qd, 1);
+      mat(p + "v_proj", kvd, d.hidden, &L.qkv, qd + kvd, 1);
+      mat(p + "o_proj", d.hidden, qd, &L.o, 0, 1);
+      mat(p + "gate_proj", d.ffn, d.hidden, &L.gu, 0, 2);
+      mat(p + "up_proj", d.ffn, d.hidden, &L.gu, 1, 2);
+      mat(p + "down_proj", d.hidden, d.ffn, &L.down, 0, 1);
+    }
+  };
+  layers("talker", c.talker, plan.tl);
+  vec("talker.final_norm", c.talker.hidden, plan.t_final);
+  mat("talker.codec_head", c.talker_vocab, c.talker.hidden, &plan.t_head, 0, 1);
+  mat("projection", c.predictor.hidden, c.talker.hidden, &plan.t_head, c.talker_vocab, 1);
+  layers("predictor", c.predictor, plan.pl);
+  vec("predictor.final_norm", c.predictor.hidden, plan.p_final);
+  for (int i = 0; i < c.n_codebooks - 1; ++i) {
+    Dest e{K_EMBED, c.code_vocab, c.predictor.hidden};
+    e.vec_off = plan.embeds[i];
+    m["predictor.codec_embed." + std::to_string(i)] = e;
+    mat("predictor.lm_head." + std::to_string(i), c.code_vocab, c.predictor.hidden,
+        &plan.heads[i], 0, 1);
+  }
+  return m;
+}
+
+qt_status check_decoder(const qt_decoder_cfg& d, const char* which) {
+  if (d.layers < 1 || d.layers > 256)
+    return fail(QT_E_SHAPE, "%s.layers = %d: expected 1..256", which, d.layers);
+  if (d.head_dim != kHeadDim)
+    return fail(QT_E_SHAPE, "%s.head_dim = %d: this build supports 128", which, d.head_dim);
+  if (d.n_kv_heads < 1 || d.n_q_heads != 2 * d.n_kv_heads)
+    return fail(QT_E_SHAPE, "%s: n_q_heads (%d) must be 2 * n_kv_heads (%d)", which, d.n_q_heads,
+                d.n_kv_heads);
+  if (d.hidden < 512 || d.hidden % 512 || d.hidden > 16384)
+    return fail(QT_E_SHAPE, "%s.hidden = %d: expected a multiple of 512 up to 16384", which, d.hidden);
+  if ((d.n_q_heads * d.head_dim) % 512)
+    return fail(QT_E_SHAPE, "%s: n_q_heads * head_dim must be a multiple of 512", which);
+  if (d.ffn < 512 || d.ffn % 512 || d.ffn > 32768)
+    return fail(QT_E_SHAPE, "%s.ffn = %d: expected a multiple of 512 up to 32768", which, d.ffn);
+  if (!(d.rms_eps > 0.f) || !(d.rope_theta > 1.f))
+    return fail(QT_E_SHAPE, "%s: rms_eps must be > 0 and rope_theta > 1", which);
+  return ok();
+}
+
+qt_status check_cfg(const qt_model_cfg* c) {
+  if (!c) return fail(QT_E_INVALID_ARG, "cfg is NULL");
+  qt_status st = check_decoder(c->talker, "talker");
+  if (st) return st;
+  if ((st = check_decoder(c->predictor, "predictor"))) return st;
+  if (c->talker_vocab < 64 || c->talker_vocab % 64)
+    return fail(QT_E_SHAPE, "talker_vocab = %d: expected a positive multiple of 64", c->talker_vocab);
+  if (c->code_vocab < 64 || c->code_vocab % 64)
+    return fail(QT_E_SHAPE, "code_vocab = %d: expected a positive multiple of 64", c->code_vocab);
+  if (c->cb0_range < 1 || c->cb0_range > c->talker_vocab || c->cb0_range > c->code_vocab)
+    return fail(QT_E_SHAPE, "cb0_range = %d: expected 1..min(talker_vocab, code_vocab)", c->cb0_range);
+  if (c->n_codebooks < 2 || c->n_codebooks > 16)
+    return fail(QT_E_SHAPE, "n_codebooks = %d: expected 2..16", c->n_codebooks);
+  if (c->page_size != kPage)
+    return fail(QT_E_SHAPE, "page_size = %d: this build supports 16", c->page_size);
+  return ok();
+}
+
+// ------------------------------------------------------------------ workspace layout
+struct Ws {
+  size_t x_t, x_p, u, u_lo, qkv, o, o_lo, ffn, ffn_lo, pk, pv, part, cnt, keys, total;
+  int u_ld, qkv_ld, o_ld, f_ld;
+  long long pk_sess;  // elements per session in the predictor cache
+};
+
+Ws make_ws(const qt_model_cfg& c, int B, int max_pages) {
+  const qt_decoder_cfg &t = c.talker, &p = c.predictor;
+  Ws w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  const int M = 2 * B;
+  w.u_ld = t.hidden > p.hidden ? t.hidden : p.hidden;
+  const int tq = (t.n_q_heads + 2 * t.n_kv_heads) * t.head_dim;
+  const int pq = (p.n_q_heads + 2 * p.n_kv_heads) * p.head_dim;
+  w.qkv_ld = tq > pq ? tq : pq;
+  w.o_ld = t.n_q_heads * t.head_dim > p.n_q_heads * p.head_dim ? t.n_q_heads * t.head_dim
+                                                                 : p.n_q_heads * p.head_dim;
+  w.f_ld = t.ffn > p.ffn ? t.ffn : p.ffn;
+  w.x_t = take((size_t)B * t.hidden * 4);
+  w.x_p = take((size_t)M * p.hidden * 4);
+  w.u = take((size_t)M * w.u_ld * 2);
+  w.u_lo = take((size_t)M * w.u_ld * 2);
+  w.qkv = take((size_t)M * w.qkv_ld * 4);
+  w.o = take((size_t)M * w.o_ld * 2);
+  w.o_lo = take((size_t)M * w.o_ld * 2);
+  w.ffn = take((size_t)M * w.f_ld * 2);
+  w.ffn_lo = take((size_t)M * w.f_ld * 2);
+  w.pk_sess = (long long)p.layers * c.n_codebooks * p.n_kv_heads * p.head_dim;
+  w.pk = take((size_t)B * w.pk_sess * 2);
+  w.pv = take((size_t)B * w.pk_sess * 2);
+  w.part = take((size_t)B * t.n_q_heads * (size_t)max_pages * (kHeadDim + 2) * 4);
+  w.cnt = take((size_t)B * t.n_kv_heads * 4);
+  w.keys = take((size_t)B * c.n_codebooks * 8);
+  w.total = off;
+  return w;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ model handle
+struct qt_model {
+  qt_model_cfg cfg;
+  int i8;
+  Plan plan;
+  std::map<std::string, Dest> dests;
+  char* base;  // packed buffer (device)
+  uint64_t bytes;
+};
+
+struct qt_graph {
+  hipGraph_t graph;
+  hipGraphExec_t exec;
+};
+
+namespace {
+
+const uint16_t* vp(const qt_model* m, size_t off) { return (const uint16_t*)(m->base + off); }
+
+GemmArgs gemm_base(const qt_model* m, const MatSlot& s, const uint16_t* act,
+                   const uint16_t* act_lo, int act_ld, int M, uint32_t* status) {
+  GemmArgs a{};
+  a.W = m->base + s.w;
+  a.scale = m->i8 ? (const float*)(m->base + s.s) : nullptr;
+  a.N = s.N;
+  a.K = s.K;
+  a.row0 = 0;
+  a.nrows = s.N;
+  a.act = act;
+  a.act_lo = act_lo;
+  a.act_ld = act_ld;
+  a.M = M;
+  a.status = status;
+  return a;
+}
+
+#define QT_LAUNCH(expr)                                                                \
+  do {                                                                                 \
+    hipError_t e_ = (expr);                                                            \
+    if (e_ != hipSuccess)                                                              \
+      return fail(QT_E_HIP, "launch %s failed: %s", #expr, hipGetErrorString(e_));     \
+  } while (0)
+
+qt_status check_frame_args(const qt_model* m, const qt_sessions* ss, const qt_kv_caches* kv,
+                           const qt_frame_inputs* in, const qt_frame_outputs* out, void* ws,
+                           uint64_t ws_bytes) {
+  if (!m) return fail(QT_E_INVALID_ARG, "model is NULL");
+  if (!ss || !kv || !in || !out) return fail(QT_E_INVALID_ARG, "a descriptor is NULL");
+  if (!ws) return fail(QT_E_INVALID_ARG, "workspace is NULL");
+  if (in->mode < QT_MODE_FULL || in->mode > QT_MODE_PREDICTOR)
+    return fail(QT_E_INVALID_ARG, "mode = %d is not a qt_mode", in->mode);
+  if (ss->batch < 1) return fail(QT_E_INVALID_ARG, "batch = %d: expected >= 1", ss->batch);
+  if (ss->batch > kMaxBatch)
+    return fail(QT_E_UNSUPPORTED, "batch = %d: this build decodes at most %d sessions per call",
+                ss->batch, kMaxBatch);
+  if (!out->tokens || !out->status) return fail(QT_E_INVALID_ARG, "outputs.tokens/status is NULL");
+  const bool talker = in->mode != QT_MODE_PREDICTOR;
+  if (talker) {
+    if (!in->talker_in) return fail(QT_E_INVALID_ARG, "inputs.talker_in is NULL");
+    if (!out->logits0) return fail(QT_E_INVALID_ARG, "outputs.logits0 is NULL");
+    if (!ss->kv_len || !ss->page_table) return fail(QT_E_INVALID_ARG, "sessions.kv_len/page_table is NULL");
+    if (ss->max_pages < 1) return fail(QT_E_INVALID_ARG, "sessions.max_pages = %d", ss->max_pages);
+    if (!kv->k_pages || !kv->v_pages) return fail(QT_E_INVALID_ARG, "kv pages are NULL");
+    if (kv->num_pages < 1) return fail(QT_E_INVALID_ARG, "kv.num_pages = %d", kv->num_pages);
+    if (((uintptr_t)kv->k_pages | (uintptr_t)kv->v_pages) & 15)
+      return fail(QT_E_INVALID_ARG, "kv pages must be 16-byte aligned");
+  } else {
+    if (!in->h_in || !in->tok0_in) return fail(QT_E_INVALID_ARG, "inputs.h_in/tok0_in is NULL");
+  }
+  if (in->mode != QT_MODE_TALKER && !out->logits_pred)
+    return fail(QT_E_INVALID_ARG, "outputs.logits_pred is NULL");
+  if ((uintptr_t)ws & (kAlign - 1)) return fail(QT_E_INVALID_ARG, "workspace must be 256-byte aligned");
+  const int mp = talker ? ss->max_pages : 1;
+  const Ws w = make_ws(m->cfg, ss->batch, mp);
+  if (ws_bytes < w.total)
+    return fail(QT_E_CAPACITY, "workspace has %llu bytes, this call needs %llu",
+                (unsigned long long)ws_bytes, (unsigned long long)w.total);
+  return ok();
+}
+
+// Enqueue one frame.  Arguments are validated by the caller.
+qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_caches* kv,
+                        const qt_frame_inputs* in, const qt_frame_outputs* out, void* wsp,
+                        hipStream_t st) {
+  const qt_model_cfg& c = m->cfg;
+  const qt_decoder_cfg &T = c.talker, &Pd = c.predictor;
+  const int B = ss->batch, ncb = c.n_codebooks, mode = in->mode;
+  const bool talker = mode != QT_MODE_PREDICTOR;
+  const int max_pages = talker ? ss->max_pages : 1;
+  const Ws w = make_ws(c, B, max_pages);
+  char* ws = (char*)wsp;
+  float* x_t = (float*)(ws + w.x_t);
+  float* x_p = (float*)(ws + w.x_p);
+  uint16_t* u = (uint16_t*)(ws + w.u);
+  uint16_t* u_lo = (uint16_t*)(ws + w.u_lo);
+  float* qkv = (float*)(ws + w.qkv);
+  uint16_t* o = (uint16_t*)(ws + w.o);
+  uint16_t* o_lo = (uint16_t*)(ws + w.o_lo);
+  uint16_t* ffn = (uint16_t*)(ws + w.ffn);
+  uint16_t* ffn_lo = (uint16_t*)(ws + w.ffn_lo);
+  unsigned long long* keys = (unsigned long long*)(ws + w.keys);
+  unsigned* cnt = (unsigned*)(ws + w.cnt);
+  const int capacity = max_pages * kPage;
+
+  FrameBeginArgs fb{};
+  fb.mode = mode;
+  fb.B = B;
+  fb.Ht = T.hidden;
+  fb.ncb = ncb;
+  fb.n_kv = T.n_kv_heads;
+  fb.capacity = capacity;
+  fb.talker_in = (const uint16_t*)in->talker_in;
+  fb.h_in = (const uint16_t*)in->h_in;
+  fb.tok0_in = in->tok0_in;
+  fb.kv_len = ss->kv_len;
+  fb.x_t = x_t;
+  fb.u = u;
+  fb.u_ld = w.u_ld;
+  fb.keys = keys;
+  fb.counters = cnt;
+  fb.status = out->status;
+  QT_LAUNCH(launch_frame_begin(fb, st));
+
+  // one decoder layer over M rows of residual x (row stride H)
+  auto layer = [&](const qt_decoder_cfg& d, const LayerSlots& L, float* x, int M,
+                   auto&& attention) -> qt_status {
+    QT_LAUNCH(launch_rmsnorm(x, d.hidden, vp(m, L.in_norm), d.hidden, d.rms_eps, u, u_lo, w.u_ld, M, st));
+    GemmArgs g = gemm_base(m, L.qkv, u, u_lo, w.u_ld, M, out->status);
+    g.epi = EPI_STORE;
+    g.out_f32 = qkv;
+    g.out_ld = w.qkv_ld;
+    QT_LAUNCH(launch_gemm(g, st));
+    qt_status s2 = attention();
+    if (s2) return s2;
+    g = gemm_base(m, L.o, o, o_lo, w.o_ld, M, out->status);
+    g.epi = EPI_RESID;
+    g.out_f32 = x;
+    g.out_ld = d.hidden;
+    QT_LAUNCH(launch_gemm(g, st));
+    QT_LAUNCH(launch_rmsnorm(x, d.hidden, vp(m, L.post_norm), d.hidden, d.rms_eps, u, u_lo, w.u_ld, M, st));
+    g = gemm_base(m, L.gu, u, u_lo, w.u_ld, M, out->status);
+    g.epi = EPI_SWIGLU;
+    g.out_bf16 = ffn;
+    g.out_bf16_lo = ffn_lo;
+    g.out_ld = w.f_ld;
+    QT_LAUNCH(launch_gemm(g, st));
+    g = gemm_base(m, L.down, ffn, ffn_lo, w.f_ld, M, out->status);
+    g.epi = EPI_RESID;
+    g.out_f32 = x;
+    g.out_ld = d.hidden;
+    QT_LAUNCH(launch_gemm(g, st));
+    return ok();
+  };
+
+  GemmArgs head = gemm_base(m, m->plan.t_head, u, u_lo, w.u_ld, B, out->status);
+  head.epi = EPI_HEAD;
+  head.logits = out->logits0;
+  head.logits_ld = c.talker_vocab;
+  head.n_logits = c.talker_vocab;
+  head.argmax_range = c.cb0_range;
+  head.keys = keys;
+  head.keys_ld = ncb;
+  head.out_f32 = x_p;  // projection rows land in predictor rows [0, B)
+  head.out_ld = Pd.hidden;
+
+  if (talker) {
+    const int pps_raw = (B * T.n_kv_heads * max_pages + 2047) / 2048;
+    const int pps = pps_raw < 1 ? 1 : (pps_raw > kMaxPagesPerSplit ? kMaxPagesPerSplit : pps_raw);
+    const int n_splits = (max_pages + pps - 1) / pps;
+    const size_t layer_elems = (size_t)kv->num_pages * T.n_kv_heads * kPage * kHeadDim;
+    for (int l = 0; l < T.layers; ++l) {
+      const LayerSlots& L = m->plan.tl[l];
+      qt_status s = layer(T, L, x_t, B, [&]() -> qt_status {
+        AttnPagedArgs a{};
+        a.qkv = qkv;
+        a.qkv_ld = w.qkv_ld;
+        a.n_q = T.n_q_heads;
+        a.n_kv = T.n_kv_heads;
+        a.q_norm = vp(m, L.q_norm);
+        a.k_norm = vp(m, L.k_norm);
+        a.eps = T.rms_eps;
+        a.k_pool = (uint16_t*)kv->k_pages + (size_t)l * layer_elems;
+        a.v_pool = (uint16_t*)kv->v_pages + (size_t)l * layer_elems;
+        a.num_pages = kv->num_pages;
+        a.page_table = ss->page_table;
+        a.max_pages = max_pages;
+        a.kv_len = ss->kv_len;
+        a.pages_per_split = pps;
+        a.n_splits = n_splits;
+        a.part = (float*)(ws + w.part);
+        a.counters = cnt;
+        a.o = o;
+        a.o_lo = o_lo;
+        a.o_ld = w.o_ld;
+        a.status = out->status;
+        QT_LAUNCH(launch_attn_paged(a, B, T.rope_theta, st));
+        return ok();
+      });
+      if (s) return s;
+    }
+    QT_LAUNCH(launch_rmsnorm(x_t, T.hidden, vp(m, m->plan.t_final), T.hidden, T.rms_eps, u, u_lo, w.u_ld, B, st));
+    head.nrows = mode == QT_MODE_TALKER ? c.talker_vocab : c.talker_vocab + Pd.hidden;
+    QT_LAUNCH(launch_gemm(head, st));
+  } else {
+    // projection only, from the caller's bf16 hidden state (copied into u by frame_begin)
+    head.act_lo = nullptr;
+    head.row0 = c.talker_vocab;
+    head.nrows = Pd.hidden;
+    QT_LAUNCH(launch_gemm(head, st));
+  }
+
+  if (mode != QT_MODE_TALKER) {
+    for (int k = 1; k < ncb; ++k) {
+      const int M = (k == 1) ? 2 * B : B;
+      const int emb_row = (k == 1) ? B : 0;
+      EmbedArgs e{};
+      e.B = B;
+      e.H = Pd.hidden;
+      e.vocab = c.code_vocab;
+      e.ncb = ncb;
+      e.step = k;
+      e.table = vp(m, m->plan.embeds[k - 1]);
+      e.keys = keys;
+      e.forced = in->forced;
+      e.x = x_p;
+      e.row_off = emb_row;
+      e.status = out->status;
+      QT_LAUNCH(launch_embed(e, st));
+      for (int l = 0; l < Pd.layers; ++l) {
+        const LayerSlots& L = m->plan.pl[l];
+        qt_status s = layer(Pd, L, x_p, M, [&]() -> qt_status {
+          AttnPredArgs a{};
+          a.qkv = qkv;
+          a.qkv_ld = w.qkv_ld;
+          a.n_q = Pd.n_q_heads;
+          a.n_kv = Pd.n_kv_heads;
+          a.B = B;
+          a.q_norm = vp(m, L.q_norm);
+          a.k_norm = vp(m, L.k_norm);
+          a.eps = Pd.rms_eps;
+          const size_t lay = (size_t)l * ncb * Pd.n_kv_heads * kHeadDim;
+          a.k_cache = (uint16_t*)(ws + w.pk) + lay;
+          a.v_cache = (uint16_t*)(ws + w.pv) + lay;
+          a.sess_stride = w.pk_sess;
+          a.pos0 = (k == 1) ? 0 : k;
+          a.n_new = (k == 1) ? 2 : 1;
+          a.o = o;
+          a.o_lo = o_lo;
+          a.o_ld = w.o_ld;
+          QT_LAUNCH(launch_attn_pred(a, Pd.rope_theta, st));
+          return ok();
+        });
+        if (s) return s;
+      }
+      QT_LAUNCH(launch_rmsnorm(x_p + (size_t)emb_row * Pd.hidden, Pd.hidden, vp(m, m->plan.p_final),
+                               Pd.hidden, Pd.rms_eps, u, u_lo, w.u_ld, B, st));
+      GemmArgs g = gemm_base(m, m->plan.heads[k - 1], u, u_lo, w.u_ld, B, out->status);
+      g.epi = EPI_HEAD;
+      g.logits = out->logits_pred + (size_t)(k - 1) * c.code_vocab;
+      g.logits_ld = (ncb - 1) * c.code_vocab;
+      g.n_logits = c.code_vocab;
+      g.argmax_range = c.code_vocab;
+      g.keys = keys + k;
+      g.keys_ld = ncb;
+      QT_LAUNCH(launch_gemm(g, st));
+    }
+  }
+
+  FrameEndArgs fe{};
+  fe.mode = mode;
+  fe.B = B;
+  fe.ncb = ncb;
+  fe.capacity = capacity;
+  fe.keys = keys;
+  fe.tokens = out->tokens;
+  fe.kv_len = ss->kv_len;
+  QT_LAUNCH(launch_frame_end(fe, st));
+  return ok();
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ exported
+extern "C" {
+
+const char* qt_last_error(void) { return g_err.c_str(); }
+
+int32_t qt_abi_version(void) { return QT_ABI_VERSION; }
+
+qt_status qt_validate_cfg(const qt_model_cfg* cfg) { return check_cfg(cfg); }
+
+qt_status qt_packed_bytes(const qt_model_cfg* cfg, int32_t int8_mode, uint64_t* bytes) {
+  qt_status st = check_cfg(cfg);
+  if (st) return st;
+  if (!bytes) return fail(QT_E_INVALID_ARG, "bytes is NULL");
+  if (int8_mode != 0 && int8_mode != 1) return fail(QT_E_INVALID_ARG, "int8_mode must be 0 or 1");
+  *bytes = make_plan(*cfg, int8_mode == 1).total;
+  return ok();
+}
+
+qt_status qt_workspace_bytes(const qt_model_cfg* cfg, int32_t max_batch, int32_t max_pages,
+                             uint64_t* bytes) {
+  qt_status st = check_cfg(cfg);
+  if (st) return st;
+  if (!bytes) return fail(QT_E_INVALID_ARG, "bytes is NULL");
+  if (max_batch < 1 || max_pages < 1)
+    return fail(QT_E_INVALID_ARG, "max_batch and max_pages must be >= 1");
+  if (max_batch > kMaxBatch)
+    return fail(QT_E_UNSUPPORTED, "max_batch = %d: this build decodes at most %d sessions per call",
+                max_batch, kMaxBatch);
+  *bytes = make_ws(*cfg, max_batch, max_pages).total;
+  return ok();
+}
+
+qt_status qt_load_weights(const qt_model_cfg* cfg, const qt_tensor* tensors, int32_t n_tensors,
+                          int32_t int8_mode, void* packed, uint64_t packed_bytes, void* stream,
+                          qt_model** out) {
+  qt_status st = check_cfg(cfg);
+  if (st) return st;
+  if (!out) return fail(QT_E_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (!tensors || n_tensors < 1) return fail(QT_E_INVALID_ARG, "tensors is NULL or empty");
+  if (!packed) return fail(QT_E_INVALID_ARG, "packed buffer is NULL");
+  if ((uintptr_t)packed & (kAlign - 1)) return fail(QT_E_INVALID_ARG, "packed buffer must be 256-byte aligned");
+  if (int8_mode != 0 && int8_mode != 1) return fail(QT_E_INVALID_ARG, "int8_mode must be 0 or 1");
+  const bool i8 = int8_mode == 1;
+  Plan plan = make_plan(*cfg, i8);
+  if (packed_bytes < plan.total)
+    return fail(QT_E_CAPACITY, "packed buffer has %llu bytes, needs %llu",
+                (unsigned long long)packed_bytes, (unsigned long long)plan.total);
+  qt_model* m = new qt_model();
+  m->cfg = *cfg;
+  m->i8 = i8;
+  m->plan = plan;
+  m->dests = make_dests(*cfg, m->plan);
+  m->base = (char*)packed;
+  m->bytes = packed_bytes;
+
+  // coverage in both directions, shapes and dtypes, before any copy is enqueued
+  std::map<std::string, const qt_tensor*> seen;
+  for (int i = 0; i < n_tensors; ++i) {
+    const qt_tensor& t = tensors[i];
+    if (!t.name) {
+      delete m;
+      return fail(QT_E_INVALID_ARG, "tensor %d has no name", i);
+    }
+    auto it = m->dests.find(t.name);
+    if (it == m->dests.end()) {
+      delete m;
+      return fail(QT_E_UNEXPECTED_TENSOR, "unexpected tensor '%s'", t.name);
+    }
+    if (seen.count(t.name)) {
+      delete m;
+      return fail(QT_E_UNEXPECTED_TENSOR, "tensor '%s' given twice", t.name);
+    }
+    seen[t.name] = &t;
+    if (t.dtype != QT_BF16) {
+      delete m;
+      return fail(QT_E_DTYPE, "tensor '%s' has dtype %d, expected bf16", t.name, t.dtype);
+    }
+    if (t.rows != it->second.rows || t.cols != it->second.cols) {
+      delete m;
+      return fail(QT_E_SHAPE, "tensor '%s' is [%lld, %lld], expected [%lld, %lld]", t.name,
+                  (long long)t.rows, (long long)t.cols, (long long)it->second.rows,
+                  (long long)it->second.cols);
+    }
+    if (!t.data) {
+      delete m;
+      return fail(QT_E_INVALID_ARG, "tensor '%s' has no data", t.name);
+    }
+  }
+  for (const auto& kvp : m->dests) {
+    if (!seen.count(kvp.first)) {
+      std::string name = kvp.first;
+      delete m;
+      return fail(QT_E_MISSING_TENSOR, "missing tensor '%s'", name.c_str());
+    }
+  }
+
+  hipStream_t s = (hipStream_t)stream;
+  for (const auto& kvp : seen) {
+    const Dest& d = m->dests[kvp.first];
+    const qt_tensor& t = *kvp.second;
+    hipError_t e = hipSuccess;
+    if (d.kind == K_VEC || d.kind == K_EMBED) {
+      e = hipMemcpyAsync(m->base + d.vec_off, t.data, (size_t)t.rows * t.cols * 2,
+                         hipMemcpyDeviceToDevice, s);
+    } else if (!i8) {
+      const size_t rowb = (size_t)d.cols * 2;
+      e = hipMemcpy2DAsync(m->base + d.mat->w + (size_t)d.row0 * rowb, rowb * d.step, t.data, rowb,
+                           rowb, (size_t)d.rows, hipMemcpyDeviceToDevice, s);
+    } else {
+      int8_t* q = (int8_t*)(m->base + d.mat->w) + (size_t)d.row0 * d.cols;
+      float* sc = (float*)(m->base + d.mat->s) + d.row0;
+      e = launch_quantize((const uint16_t*)t.data, d.rows, d.cols, q, (long long)d.cols * d.step, sc,
+                          d.step, s);
+    }
+    if (e != hipSuccess) {
+      delete m;
+      return fail(QT_E_HIP, "packing '%s' failed: %s", kvp.first.c_str(), hipGetErrorString(e));
+    }
+  }
+  *out = m;
+  return ok();
+}
+
+qt_status qt_quantize_int8(const void* w_bf16, int64_t rows, int64_t cols, int8_t* q, float* scale,
+                           void* stream) {
+  if (!w_bf16 || !q || !scale) return fail(QT_E_INVALID_ARG, "a pointer is NULL");
+  if (rows < 1 || cols < 1) return fail(QT_E_INVALID_ARG, "rows and cols must be >= 1");
+  if (rows > 0x7fffffffLL) return fail(QT_E_SHAPE, "rows = %lld: at most 2^31-1", (long long)rows);
+  QT_HIP(launch_quantize((const uint16_t*)w_bf16, rows, cols, q, cols, scale, 1, (hipStream_t)stream));
+  return ok();
+}
+
+qt_status qt_model_export_int8(const qt_model* m, const char* name, int8_t* q, float* scale,
+                               void* stream) {
+  if (!m || !name || !q || !scale) return fail(QT_E_INVALID_ARG, "a pointer is NULL");
+  if (!m->i8) return fail(QT_E_STATE, "model was loaded in bf16 mode");
+  auto it = m->dests.find(name);
+  if (it == m->dests.end() || it->second.kind != K_MAT)
+    return fail(QT_E_INVALID_ARG, "'%s' is not a decode GEMM weight", name);
+  const Dest& d = it->second;
+  hipStream_t s = (hipStream_t)stream;
+  QT_HIP(hipMemcpy2DAsync(q, (size_t)d.cols, m->base + d.mat->w + (size_t)d.row0 * d.cols,
+                          (size_t)d.cols * d.step, (size_t)d.cols, (size_t)d.rows,
+                          hipMemcpyDeviceToDevice, s));
+  QT_HIP(hipMemcpy2DAsync(scale, 4, m->base + d.mat->s + (size_t)d.row0 * 4, (size_t)4 * d.step, 4,
+                          (size_t)d.rows, hipMemcpyDeviceToDevice, s));
+  return ok();
+}
+
+qt_status qt_frame_decode(qt_model* model, const qt_sessions* sessions, const qt_kv_caches* kv,
+                          const qt_frame_inputs* in, const qt_frame_outputs* out, void* workspace,
+                          uint64_t workspace_bytes, void* stream) {
+  qt_status st = check_frame_args(model, sessions, kv, in, out, workspace, workspace_bytes);
+  if (st) return st;
+  return enqueue_frame(model, sessions, kv, in, out, workspace, (hipStream_t)stream);
+}
+
+qt_status qt_frame_graph_create(qt_model* model, const qt_sessions* sessions, const qt_kv_caches* kv,
+                                const qt_frame_inputs* in, const qt_frame_outputs* out,
+                                void* workspace, uint64_t workspace_bytes, qt_graph** out_graph) {
+  if (!out_graph) return fail(QT_E_INVALID_ARG, "out_graph is NULL");
+  *out_graph = nullptr;
+  qt_status st = check_frame_args(model, sessions, kv, in, out, workspace, workspace_bytes);
+  if (st) return st;
+  hipStream_t cs;
+  QT_HIP(hipStreamCreateWithFlags(&cs, hipStreamNonBlocking));
+  hipError_t e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) {
+    (void)hipStreamDestroy(cs);
+    return fail(QT_E_HIP, "hipStreamBeginCapture failed: %s", hipGetErrorString(e));
+  }
+  st = enqueue_frame(model, sessions, kv, in, out, workspace, cs);
+  hipGraph_t g = nullptr;
+  e = hipStreamEndCapture(cs, &g);
+  (void)hipStreamDestroy(cs);
+  if (st) {
+    if (g) (void)hipGraphDestroy(g);
+    return st;
+  }
+  if (e != hipSuccess) return fail(QT_E_HIP, "hipStreamEndCapture failed: %s", hipGetErrorString(e));
+  hipGraphExec_t ex;
+  e = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    (void)hipGraphDestroy(g);
+    return fail(QT_E_HIP, "hipGraphInstantiate failed: %s", hipGetErrorString(e));
+  }
+  qt_graph* gr = new qt_graph();
+  gr->graph = g;
+  gr->exec = ex;
+  *out_graph = gr;
+  return ok();
+}
+
+qt_status qt_frame_graph_launch(qt_graph* graph, void* stream) {
+  if (!graph) return fail(QT_E_INVALID_ARG, "graph is NULL");
+  QT_HIP(hipGraphLaunch(graph->exec, (hipStream_t)stream));
+  return ok();
+}
+
+void qt_graph_destroy(qt_graph* graph) {
+  if (!graph) return;
+  (void)hipGraphExecDestroy(graph->exec);
+  (void)hipGraphDestroy(graph->graph);
+  delete graph;
+}
+
+void qt_model_destroy(qt_model* model) { delete model; }
+
+}  // extern "C"

@@ -1,0 +1,204 @@
+"""Device-memory plumbing around the C ABI, with PyTorch as the allocator.
+
+`Decoder` owns every buffer one qt_frame_decode call needs: the packed
+weights, the workspace, the Talker KV page pools and page tables, and the
+input/output tensors.  It lays prefilled per-session caches out into pages and
+fills descriptors; all decoding happens inside libqt.so.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import (FrameInputs, FrameOutputs, KvCaches, MODES, QT_BF16, Sessions, make_cfg,
+               qt_frame_decode, qt_frame_graph_create, qt_frame_graph_launch, qt_graph_destroy,
+               qt_load_weights, qt_model_destroy, qt_packed_bytes, qt_workspace_bytes)
+
+PAGE = 16
+
+
+def _aligned(torch, nbytes: int, device, align: int = 256):
+    buf = torch.empty(nbytes + align, dtype=torch.uint8, device=device)
+    off = (-buf.data_ptr()) % align
+    return buf, buf.data_ptr() + off
+
+
+def _bits(torch, a: np.ndarray, device):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)).to(device)
+
+
+class PackedModel:
+    """The model's weights packed by qt_load_weights into one device buffer.
+
+    weights: name -> bfloat16 bits (np.uint16), as produced by synth.gen_weights."""
+
+    def __init__(self, dims, weights: dict, int8: bool = False, device="cuda"):
+        import torch
+        self.torch = torch
+        self.dims = dims
+        self.dev = torch.device(device)
+        self.cfg = make_cfg(dims)
+        self.int8 = int8
+        stream = torch.cuda.current_stream(self.dev)
+        src, table = {}, []
+        for name, arr in weights.items():
+            t = _bits(torch, arr, self.dev)
+            src[name] = t
+            rows, cols = (1, arr.shape[0]) if arr.ndim == 1 else arr.shape
+            table.append((name, t.data_ptr(), QT_BF16, int(rows), int(cols)))
+        self.packed_bytes = qt_packed_bytes(self.cfg, int(int8))
+        self._packed_buf, self.packed_ptr = _aligned(torch, self.packed_bytes, self.dev)
+        self.handle = qt_load_weights(self.cfg, table, int(int8), self.packed_ptr,
+                                      self.packed_bytes, stream.cuda_stream)
+        torch.cuda.synchronize(self.dev)
+        del src
+
+    def close(self):
+        if self.handle:
+            qt_model_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class Decoder:
+    """Buffers for up to `batch` sessions of one PackedModel.
+
+    max_pages: page-table row length (capacity = max_pages * 16 positions).
+    num_pages: size of the shared page pool (default batch * max_pages)."""
+
+    def __init__(self, model: PackedModel, batch: int = 1, max_pages: int = 1,
+                 num_pages: int | None = None, page_seed: int = 1234):
+        import torch
+        self.torch = torch
+        self.pm = model
+        self.model = model.handle
+        dims = model.dims
+        self.dims = dims
+        self.dev = model.dev
+        self.B = batch
+        self.max_pages = max_pages
+        self.num_pages = num_pages if num_pages is not None else batch * max_pages
+        self.cfg = model.cfg
+        self.int8 = model.int8
+
+        t, p = dims.talker, dims.predictor
+        self.ws_bytes = qt_workspace_bytes(self.cfg, batch, max_pages)
+        self._ws_buf, self.ws_ptr = _aligned(torch, self.ws_bytes, self.dev)
+        shape = (t.layers, self.num_pages, t.n_kv, PAGE, t.head_dim)
+        self.k_pages = torch.zeros(shape, dtype=torch.int16, device=self.dev)
+        self.v_pages = torch.zeros(shape, dtype=torch.int16, device=self.dev)
+        rng = np.random.default_rng(page_seed)
+        perm = rng.permutation(self.num_pages).astype(np.int32)
+        table_np = np.full((batch, max_pages), -1, dtype=np.int32)
+        for b in range(batch):
+            chunk = perm[b * max_pages:(b + 1) * max_pages]
+            table_np[b, :len(chunk)] = chunk
+        self.page_table_np = table_np
+        self.page_table = torch.from_numpy(table_np).to(self.dev)
+        self.kv_len = torch.zeros(batch, dtype=torch.int32, device=self.dev)
+
+        self.talker_in = torch.zeros((batch, t.hidden), dtype=torch.int16, device=self.dev)
+        self.h_in = torch.zeros((batch, t.hidden), dtype=torch.int16, device=self.dev)
+        self.tok0_in = torch.zeros(batch, dtype=torch.int32, device=self.dev)
+        self.forced = torch.zeros((batch, dims.n_codebooks), dtype=torch.int32, device=self.dev)
+        self.logits0 = torch.zeros((batch, dims.talker_vocab), dtype=torch.float32, device=self.dev)
+        self.logits_pred = torch.zeros((batch, dims.n_steps, dims.code_vocab), dtype=torch.float32,
+                                       device=self.dev)
+        self.tokens = torch.zeros((batch, dims.n_codebooks), dtype=torch.int32, device=self.dev)
+        self.status = torch.zeros(1, dtype=torch.int32, device=self.dev)
+        self.graphs = []
+
+    # ------------------------------------------------------------------ state
+    def load_session_kv(self, b: int, k_bits: np.ndarray, v_bits: np.ndarray):
+        """Lay a session's prefilled cache ([layers, L, n_kv, hd] bf16 bits) out
+        into its pages and set kv_len[b] = L."""
+        torch = self.torch
+        layers, L, nkv, hd = k_bits.shape
+        npg = -(-L // PAGE)
+        if npg > self.max_pages:
+            raise ValueError(f"session {b}: {L} positions need {npg} pages > {self.max_pages}")
+        if npg:
+            pages = torch.from_numpy(self.page_table_np[b, :npg].astype(np.int64)).to(self.dev)
+            for src, pool in ((k_bits, self.k_pages), (v_bits, self.v_pages)):
+                x = np.zeros((layers, npg * PAGE, nkv, hd), dtype=np.uint16)
+                x[:, :L] = src
+                t = _bits(torch, x, self.dev).view(layers, npg, PAGE, nkv, hd).permute(0, 1, 3, 2, 4)
+                pool[:, pages] = t
+        self.kv_len[b] = L
+
+    def set_lengths(self, lengths):
+        self.kv_len.copy_(self.torch.as_tensor(np.asarray(lengths, dtype=np.int32)))
+
+    def set_inputs(self, talker_in=None, h_in=None, tok0=None, forced=None):
+        torch = self.torch
+        if talker_in is not None:
+            self.talker_in.copy_(_bits(torch, talker_in, self.dev))
+        if h_in is not None:
+            self.h_in.copy_(_bits(torch, h_in, self.dev))
+        if tok0 is not None:
+            self.tok0_in.copy_(torch.as_tensor(np.asarray(tok0, dtype=np.int32)))
+        if forced is not None:
+            self.forced.copy_(torch.as_tensor(np.asarray(forced, dtype=np.int32)))
+
+    # ------------------------------------------------------------------ descriptors
+    def _descs(self, mode: str, forced: bool, batch: int | None = None):
+        B = batch or self.B
+        ss = Sessions(B, self.kv_len.data_ptr(), self.page_table.data_ptr(), self.max_pages)
+        kv = KvCaches(self.k_pages.data_ptr(), self.v_pages.data_ptr(), self.num_pages)
+        fi = FrameInputs(MODES[mode], self.talker_in.data_ptr(), self.h_in.data_ptr(),
+                         self.tok0_in.data_ptr(), self.forced.data_ptr() if forced else None)
+        fo = FrameOutputs(self.logits0.data_ptr(), self.logits_pred.data_ptr(),
+                          self.tokens.data_ptr(), self.status.data_ptr())
+        return ss, kv, fi, fo
+
+    def decode(self, mode: str = "full", forced: bool = False, batch: int | None = None):
+        """Enqueue one frame on the current stream (no host synchronisation)."""
+        ss, kv, fi, fo = self._descs(mode, forced, batch)
+        qt_frame_decode(self.model, ss, kv, fi, fo, self.ws_ptr, self.ws_bytes,
+                        self.torch.cuda.current_stream(self.dev).cuda_stream)
+
+    def capture(self, mode: str = "full", forced: bool = False) -> int:
+        ss, kv, fi, fo = self._descs(mode, forced)
+        g = qt_frame_graph_create(self.model, ss, kv, fi, fo, self.ws_ptr, self.ws_bytes)
+        self.graphs.append(g)
+        return g
+
+    def replay(self, graph: int):
+        qt_frame_graph_launch(graph, self.torch.cuda.current_stream(self.dev).cuda_stream)
+
+    def close(self):
+        for g in self.graphs:
+            qt_graph_destroy(g)
+        self.graphs = []
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def setup_workload(w, model: PackedModel, kv_pool=None):
+    """A Decoder for workload `w` (a synth.Workload) with every session's
+    prefilled Talker cache laid out into its pages.  Returns (decoder, lengths)."""
+    import synth
+    from concurrent.futures import ThreadPoolExecutor
+    d = w.dims
+    lengths = w.lengths()
+    dec = Decoder(model, batch=w.batch, max_pages=w.max_pages())
+    if w.mode != "predictor":
+        t = d.talker
+        with ThreadPoolExecutor(synth._threads()) as pool:
+            for b in range(w.batch):
+                if kv_pool is not None and b in kv_pool:
+                    kb, vb = kv_pool[b]
+                else:
+                    kb, vb = synth.gen_kv(w.name, b, t.layers, int(lengths[b]), t.n_kv, t.head_dim,
+                                          pool=pool)
+                dec.load_session_kv(b, kb, vb)
+    dec.torch.cuda.synchronize(dec.dev)
+    return dec, lengths

@@ -243,10 +243,13 @@ class Workload:
     graph: bool = False
     dims: ModelDims = field(default=FULL)
     note: str = ""
+    lens: tuple = ()       # explicit per-session lengths (overrides the range)
 
     def lengths(self, seed: int = BASE_SEED) -> np.ndarray:
         if self.mode == "predictor":
             return np.zeros(self.batch, dtype=np.int32)
+        if self.lens:
+            return np.asarray(self.lens, dtype=np.int32)
         if self.len_lo == self.len_hi:
             return np.full(self.batch, self.len_lo, dtype=np.int32)
         return uniform_ints(f"{self.name}.kv_len", self.batch, self.len_lo, self.len_hi, seed)

@@ -1,0 +1,267 @@
+"""GPU tests on the reduced model and the INT8 quantizer: batch sizes across the
+VALU (M <= 8) and MFMA (M > 8) GEMM paths, ragged and boundary KV lengths,
+determinism, graph replay, paging invariance, device status bits, and the
+bit-exact INT8 quantizer on every decode weight of the full model."""
+import numpy as np
+import pytest
+
+import synth
+from tests.gpu_cases import log, run_frames
+from tests.parity import compare
+
+pytestmark = pytest.mark.gpu
+
+S = synth.SMALL
+
+
+def small_w(name, mode="full", batch=1, frames=2, lens=(), lo=0, hi=0, **kw):
+    return synth.Workload(name, mode, batch=batch, frames=frames, len_lo=lo, len_hi=hi,
+                          dims=S, lens=tuple(lens), **kw)
+
+
+# ----------------------------------------------------------------- batch sizes / paths
+@pytest.mark.parametrize("B", [1, 2, 3, 5, 8, 9, 16, 20, 32])
+def test_small_batches_match_oracle(small_pm, orc_small, B):
+    """B <= 4 keeps every GEMM on the VALU path (predictor step 1 has 2B rows);
+    B >= 5 moves step 1 to MFMA, B >= 9 moves every GEMM to MFMA."""
+    lens = [(37 * b + 5) % 90 for b in range(B)]
+    w = small_w(f"S{B}", batch=B, frames=2, lens=lens)
+    run_frames(small_pm, orc_small, w, check=range(B))
+
+
+def test_small_boundary_lengths(small_pm, orc_small):
+    """Empty caches and page-boundary lengths (the new token opens a page, fills
+    its last slot, or lands in a fresh split)."""
+    lens = [0, 1, 15, 16, 17, 31, 32, 127, 128, 129, 255, 256]
+    w = small_w("Sedge", batch=len(lens), frames=3, lens=lens)
+    run_frames(small_pm, orc_small, w, check=range(len(lens)))
+
+
+def test_small_long_context_many_splits(small_pm, orc_small):
+    """B=2 with ~1.5k positions: the split-KV partials and their merge."""
+    w = small_w("Slong", batch=2, frames=2, lens=[1500, 700])
+    run_frames(small_pm, orc_small, w, check=[0, 1])
+
+
+def test_small_graph_replay(small_pm, orc_small):
+    w = small_w("Sgraph", batch=6, frames=4, lens=[3, 40, 77, 16, 130, 0], graph=True)
+    run_frames(small_pm, orc_small, w, check=range(6), use_graph=True)
+
+
+@pytest.mark.parametrize("mode", ["talker", "predictor"])
+def test_small_modes(small_pm, orc_small, mode):
+    w = small_w(f"Smode{mode}", mode=mode, batch=3, frames=2, lens=[5, 20, 33])
+    run_frames(small_pm, orc_small, w, check=range(3))
+
+
+# ----------------------------------------------------------------- invariances
+def _run_eager(dec, w, frames_inputs, forced, use_graph=False, mode="full"):
+    torch = dec.torch
+    g = dec.capture(mode, forced=True) if use_graph else None
+    outs = []
+    for f in range(w.frames):
+        dec.set_inputs(talker_in=frames_inputs["talker_in"][f], forced=forced[f])
+        if g is not None:
+            dec.replay(g)
+        else:
+            dec.decode(mode, forced=True)
+        torch.cuda.synchronize()
+        outs.append((dec.logits0.cpu().numpy().copy(), dec.logits_pred.cpu().numpy().copy(),
+                     dec.tokens.cpu().numpy().copy()))
+    return outs
+
+
+def _fresh(small_pm, w, page_seed=1234):
+    from streaming_tts_decode_amd.runtime import Decoder
+    t = S.talker
+    dec = Decoder(small_pm, batch=w.batch, max_pages=w.max_pages(), page_seed=page_seed)
+    for b, L in enumerate(w.lengths()):
+        kb, vb = synth.gen_kv(w.name, b, t.layers, int(L), t.n_kv, t.head_dim)
+        dec.load_session_kv(b, kb, vb)
+    return dec
+
+
+def _forced(w):
+    rng = np.random.default_rng(5)
+    return rng.integers(0, S.cb0_range, size=(w.frames, w.batch, S.n_codebooks)).astype(np.int32)
+
+
+def test_replays_are_bitwise_deterministic_and_equal_eager(small_pm):
+    w = small_w("Sdet", batch=4, frames=3, lens=[600, 5, 333, 48])
+    fi, fz = synth.frame_inputs(w), _forced(w)
+    runs = []
+    for use_graph in (False, False, True, True):
+        dec = _fresh(small_pm, w)
+        runs.append(_run_eager(dec, w, fi, fz, use_graph=use_graph))
+        dec.close()
+    for r in runs[1:]:
+        for a, b in zip(runs[0], r):
+            for x, y in zip(a, b):
+                np.testing.assert_array_equal(x, y)
+
+
+def test_page_permutation_invariance(small_pm):
+    w = small_w("Sperm", batch=3, frames=2, lens=[200, 17, 90])
+    fi, fz = synth.frame_inputs(w), _forced(w)
+    a = _run_eager(_fresh(small_pm, w, page_seed=1), w, fi, fz)
+    b = _run_eager(_fresh(small_pm, w, page_seed=2), w, fi, fz)
+    for x, y in zip(a, b):
+        for u, v in zip(x, y):
+            np.testing.assert_array_equal(u, v)
+
+
+def test_lockstep_batch_equals_single_sessions(small_pm):
+    w = small_w("Slock", batch=6, frames=2, lens=[10, 50, 90, 130, 170, 210])
+    fi, fz = synth.frame_inputs(w), _forced(w)
+    batch = _run_eager(_fresh(small_pm, w), w, fi, fz)
+    lens = w.lengths()
+    for b in range(w.batch):
+        w1 = small_w("Slock", batch=1, frames=2, lens=[int(lens[b])])
+        dec = _fresh(small_pm, w1)
+        t = S.talker
+        kb, vb = synth.gen_kv("Slock", b, t.layers, int(lens[b]), t.n_kv, t.head_dim)
+        dec.load_session_kv(0, kb, vb)
+        single = _run_eager(dec, w1, {"talker_in": fi["talker_in"][:, b:b + 1]}, fz[:, b:b + 1])
+        for f in range(w.frames):
+            compare(single[f][0][0], batch[f][0][b], S.cb0_range, label=f"lockstep s{b} f{f} cb0")
+            compare(single[f][1][0], batch[f][1][b], label=f"lockstep s{b} f{f} pred")
+
+
+def test_talker_mode_equals_full_mode_codebook0(small_pm):
+    w = small_w("Stm", batch=3, frames=1, lens=[9, 99, 199])
+    fi, fz = synth.frame_inputs(w), _forced(w)
+    full = _run_eager(_fresh(small_pm, w), w, fi, fz, mode="full")
+    talk = _run_eager(_fresh(small_pm, w), w, fi, fz, mode="talker")
+    np.testing.assert_array_equal(full[0][0], talk[0][0])
+    np.testing.assert_array_equal(full[0][2][:, 0], talk[0][2][:, 0])
+
+
+# ----------------------------------------------------------------- device status
+def test_capacity_overflow_is_flagged_and_skipped(small_pm, orc_small):
+    from streaming_tts_decode_amd import STATUS_KV_OVERFLOW
+    w = small_w("Sover", batch=2, frames=1, lens=[20, 30])
+    dec = _fresh(small_pm, w)
+    cap = dec.max_pages * 16
+    dec.kv_len[1] = cap  # session 1 is full
+    fi = synth.frame_inputs(w)
+    dec.set_inputs(talker_in=fi["talker_in"][0])
+    dec.status.zero_()
+    dec.decode("full")
+    dec.torch.cuda.synchronize()
+    st = int(dec.status.item())
+    assert st & STATUS_KV_OVERFLOW
+    kv = dec.kv_len.cpu().numpy()
+    assert kv[1] == cap and kv[0] == 21
+    # session 0 is still decoded correctly
+    t = S.talker
+    kb, vb = synth.gen_kv("Sover", 0, t.layers, 20, t.n_kv, t.head_dim)
+    o = orc_small.run_session("talker", 1, talker_in=fi["talker_in"][:, 0], k_bits=kb, v_bits=vb,
+                              length=20)
+    compare(dec.logits0.cpu().numpy()[0:1], o["logits0"], S.cb0_range, label="overflow s0")
+
+
+def test_bad_page_and_bad_token_are_flagged(small_pm):
+    from streaming_tts_decode_amd import STATUS_BAD_PAGE, STATUS_BAD_TOKEN
+    w = small_w("Sbad", batch=2, frames=1, lens=[40, 40])
+    dec = _fresh(small_pm, w)
+    fi = synth.frame_inputs(w)
+    pt = dec.page_table.cpu().numpy()
+    pt[0, 1] = dec.num_pages + 7  # out of range, read as zeros
+    dec.page_table.copy_(dec.torch.from_numpy(pt))
+    forced = np.zeros((2, S.n_codebooks), dtype=np.int32)
+    forced[1, 2] = S.code_vocab + 3  # out of range
+    dec.set_inputs(talker_in=fi["talker_in"][0], forced=forced)
+    dec.status.zero_()
+    dec.decode("full", forced=True)
+    dec.torch.cuda.synchronize()
+    st = int(dec.status.item())
+    assert st & STATUS_BAD_PAGE and st & STATUS_BAD_TOKEN
+    assert np.all(np.isfinite(dec.logits_pred.cpu().numpy()))
+
+
+# ----------------------------------------------------------------- ABI errors needing a model
+def test_frame_argument_errors(small_pm):
+    import streaming_tts_decode_amd as qt
+    from streaming_tts_decode_amd.runtime import Decoder
+    dec = Decoder(small_pm, batch=2, max_pages=4)
+    ss, kv, fi, fo = dec._descs("full", False)
+    with pytest.raises(qt.QtError) as e:
+        qt.qt_frame_decode(dec.model, ss, kv, fi, fo, dec.ws_ptr, 1024)
+    assert e.value.status == 6  # QT_E_CAPACITY
+    ss.batch = 33
+    with pytest.raises(qt.QtError) as e:
+        qt.qt_frame_decode(dec.model, ss, kv, fi, fo, dec.ws_ptr, dec.ws_bytes)
+    assert e.value.status == 9  # QT_E_UNSUPPORTED
+    ss.batch = 2
+    fi.mode = 7
+    with pytest.raises(qt.QtError) as e:
+        qt.qt_frame_decode(dec.model, ss, kv, fi, fo, dec.ws_ptr, dec.ws_bytes)
+    assert e.value.status == 1
+    fi.mode = 0
+    fi.talker_in = None
+    with pytest.raises(qt.QtError):
+        qt.qt_frame_decode(dec.model, ss, kv, fi, fo, dec.ws_ptr, dec.ws_bytes)
+
+
+# ----------------------------------------------------------------- INT8 quantizer
+def _gpu_quantize(torch, w_bits):
+    import streaming_tts_decode_amd as qt
+    rows, cols = w_bits.shape
+    w = torch.from_numpy(np.ascontiguousarray(w_bits).view(np.int16)).cuda()
+    q = torch.empty((rows, cols), dtype=torch.int8, device="cuda")
+    s = torch.empty(rows, dtype=torch.float32, device="cuda")
+    qt.qt_quantize_int8(w.data_ptr(), rows, cols, q.data_ptr(), s.data_ptr(),
+                        torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    return q.cpu().numpy(), s.cpu().numpy()
+
+
+def test_quantizer_edge_rows(gpu):
+    import os
+
+    import oracle
+    import torch
+    rows = []
+    for line in open(os.path.join(os.path.dirname(__file__), "golden", "int8_ties.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        rows.append(np.array([float(t) for t in line.split("|")[0].split()], dtype=np.float32))
+    for r in rows:
+        wb = synth._to_bf16_bits(r)[None]
+        q, s = _gpu_quantize(torch, wb)
+        qo, so = oracle.quantize_int8(wb)
+        np.testing.assert_array_equal(q, qo)
+        np.testing.assert_array_equal(s.view(np.uint32), so.view(np.uint32))
+    for shape in [(3, 7), (5, 1000), (2, 257), (1, 1)]:
+        wb = synth.normal_bf16(f"qedge{shape}", shape, 0.0, 0.02)
+        wb[0] = 0  # an all-zero row
+        q, s = _gpu_quantize(torch, wb)
+        qo, so = oracle.quantize_int8(wb)
+        np.testing.assert_array_equal(q, qo)
+        np.testing.assert_array_equal(s.view(np.uint32), so.view(np.uint32))
+
+
+def test_quantizer_bit_exact_every_decode_weight(gpu, full_weights, orc_full_i8):
+    import torch
+    names = synth.linear_names(synth.FULL)
+    for i, name in enumerate(names):
+        q, s = _gpu_quantize(torch, full_weights[name])
+        qo, so = orc_full_i8.quantized[name]
+        if not (np.array_equal(q, qo) and np.array_equal(s.view(np.uint32), so.view(np.uint32))):
+            raise AssertionError(f"{name}: INT8 weights or scales differ from the oracle")
+    log(f"[int8] {len(names)} decode weights bit-exact")
+
+
+def test_int8_model_uses_quantizer_output(full_pm_i8, orc_full_i8):
+    import streaming_tts_decode_amd as qt
+    import torch
+    for name in synth.linear_names(synth.FULL):
+        qo, so = orc_full_i8.quantized[name]
+        q = torch.empty(qo.shape, dtype=torch.int8, device="cuda")
+        s = torch.empty(so.shape, dtype=torch.float32, device="cuda")
+        qt.qt_model_export_int8(full_pm_i8.handle, name, q.data_ptr(), s.data_ptr(),
+                                torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(q.cpu().numpy(), qo, err_msg=name)
+        np.testing.assert_array_equal(s.cpu().numpy().view(np.uint32), so.view(np.uint32),
+                                      err_msg=name)
