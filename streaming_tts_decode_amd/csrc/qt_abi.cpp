@@ -214,11 +214,14 @@ qt_status check_cfg(const qt_model_cfg* c) {
 
 // ------------------------------------------------------------------ workspace layout
 struct Ws {
-  size_t x_t, x_p, u, u_lo, qkv, o, o_lo, ffn, ffn_lo, pk, pv, part, cnt, keys, total;
-  int u_ld, qkv_ld, o_ld, f_ld;
+  size_t x_t, x_p, ss_t, ss_p, ut, ut_lo, up, up_lo, qkv, o, o_lo, ffn, ffn_lo, pk, pv, part, cnt,
+      keys, total;
+  int qkv_ld, o_ld, f_ld;
   long long pk_sess;  // elements per session in the predictor cache
 };
 
+// Residual rows carry sums of squares per producing row block; a GEMM row block
+// is at least 4 rows, so hidden/4 slots per row always suffice.
 Ws make_ws(const qt_model_cfg& c, int B, int max_pages) {
   const qt_decoder_cfg &t = c.talker, &p = c.predictor;
   Ws w{};
@@ -229,7 +232,6 @@ Ws make_ws(const qt_model_cfg& c, int B, int max_pages) {
     return o;
   };
   const int M = 2 * B;
-  w.u_ld = t.hidden > p.hidden ? t.hidden : p.hidden;
   const int tq = (t.n_q_heads + 2 * t.n_kv_heads) * t.head_dim;
   const int pq = (p.n_q_heads + 2 * p.n_kv_heads) * p.head_dim;
   w.qkv_ld = tq > pq ? tq : pq;
@@ -238,8 +240,12 @@ Ws make_ws(const qt_model_cfg& c, int B, int max_pages) {
   w.f_ld = t.ffn > p.ffn ? t.ffn : p.ffn;
   w.x_t = take((size_t)B * t.hidden * 4);
   w.x_p = take((size_t)M * p.hidden * 4);
-  w.u = take((size_t)M * w.u_ld * 2);
-  w.u_lo = take((size_t)M * w.u_ld * 2);
+  w.ss_t = take((size_t)(t.hidden / 4) * B * 4);
+  w.ss_p = take((size_t)(p.hidden / 4) * M * 4);
+  w.ut = take((size_t)B * t.hidden * 2);
+  w.ut_lo = take((size_t)B * t.hidden * 2);
+  w.up = take((size_t)M * p.hidden * 2);
+  w.up_lo = take((size_t)M * p.hidden * 2);
   w.qkv = take((size_t)M * w.qkv_ld * 4);
   w.o = take((size_t)M * w.o_ld * 2);
   w.o_lo = take((size_t)M * w.o_ld * 2);
@@ -276,8 +282,9 @@ namespace {
 
 const uint16_t* vp(const qt_model* m, size_t off) { return (const uint16_t*)(m->base + off); }
 
-GemmArgs gemm_base(const qt_model* m, const MatSlot& s, const uint16_t* act,
-                   const uint16_t* act_lo, int act_ld, int M, uint32_t* status) {
+// GEMM over a packed matrix with hi/lo bf16 activations (act_lo may be null).
+GemmArgs gemm_act(const qt_model* m, const MatSlot& s, const uint16_t* act,
+                  const uint16_t* act_lo, int act_ld, int M, uint32_t* status) {
   GemmArgs a{};
   a.W = m->base + s.w;
   a.scale = m->i8 ? (const float*)(m->base + s.s) : nullptr;
@@ -290,6 +297,19 @@ GemmArgs gemm_base(const qt_model* m, const MatSlot& s, const uint16_t* act,
   a.act_ld = act_ld;
   a.M = M;
   a.status = status;
+  return a;
+}
+
+// GEMM whose input is an RMSNorm: u = hi/lo(x * gain) as left by the producer of x,
+// whose sums of squares sit in `slots` slots of ss (stride ss_ld).
+GemmArgs gemm_norm(const qt_model* m, const MatSlot& s, const uint16_t* u, const uint16_t* u_lo,
+                   int u_ld, const float* ss, int ss_ld, int slots, float eps, int M,
+                   uint32_t* status) {
+  GemmArgs a = gemm_act(m, s, u, u_lo, u_ld, M, status);
+  a.ss_in = ss;
+  a.ss_in_ld = ss_ld;
+  a.ss_in_slots = slots;
+  a.norm_eps = eps;
   return a;
 }
 
@@ -338,6 +358,12 @@ qt_status check_frame_args(const qt_model* m, const qt_sessions* ss, const qt_kv
 }
 
 // Enqueue one frame.  Arguments are validated by the caller.
+//
+// Per Talker layer: [QKV GEMM on RMSNorm(x)] -> [paged attention: q/k-norm, RoPE,
+// KV append, split-KV merge] -> [o-proj GEMM, x += ; RMS statistics of x] ->
+// [gate/up GEMM on RMSNorm(x), SwiGLU] -> [down GEMM, x += ; RMS statistics].
+// Then the codec head (+ projection rows into the predictor's residual), and
+// per predictor step: [embedding gather] -> 5 such layers -> [step head].
 qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_caches* kv,
                         const qt_frame_inputs* in, const qt_frame_outputs* out, void* wsp,
                         hipStream_t st) {
@@ -350,8 +376,12 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
   char* ws = (char*)wsp;
   float* x_t = (float*)(ws + w.x_t);
   float* x_p = (float*)(ws + w.x_p);
-  uint16_t* u = (uint16_t*)(ws + w.u);
-  uint16_t* u_lo = (uint16_t*)(ws + w.u_lo);
+  float* ss_t = (float*)(ws + w.ss_t);
+  float* ss_p = (float*)(ws + w.ss_p);
+  uint16_t* ut = (uint16_t*)(ws + w.ut);
+  uint16_t* ut_lo = (uint16_t*)(ws + w.ut_lo);
+  uint16_t* up = (uint16_t*)(ws + w.up);
+  uint16_t* up_lo = (uint16_t*)(ws + w.up_lo);
   float* qkv = (float*)(ws + w.qkv);
   uint16_t* o = (uint16_t*)(ws + w.o);
   uint16_t* o_lo = (uint16_t*)(ws + w.o_lo);
@@ -368,59 +398,77 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
   fb.ncb = ncb;
   fb.n_kv = T.n_kv_heads;
   fb.capacity = capacity;
+  fb.eps = T.rms_eps;
   fb.talker_in = (const uint16_t*)in->talker_in;
-  fb.h_in = (const uint16_t*)in->h_in;
   fb.tok0_in = in->tok0_in;
   fb.kv_len = ss->kv_len;
   fb.x_t = x_t;
-  fb.u = u;
-  fb.u_ld = w.u_ld;
+  fb.ss_t = ss_t;
+  fb.gain = vp(m, m->plan.tl[0].in_norm);
+  fb.u_hi = ut;
+  fb.u_lo = ut_lo;
   fb.keys = keys;
   fb.counters = cnt;
   fb.status = out->status;
   QT_LAUNCH(launch_frame_begin(fb, st));
 
-  // one decoder layer over M rows of residual x (row stride H)
-  auto layer = [&](const qt_decoder_cfg& d, const LayerSlots& L, float* x, int M,
-                   auto&& attention) -> qt_status {
-    QT_LAUNCH(launch_rmsnorm(x, d.hidden, vp(m, L.in_norm), d.hidden, d.rms_eps, u, u_lo, w.u_ld, M, st));
-    GemmArgs g = gemm_base(m, L.qkv, u, u_lo, w.u_ld, M, out->status);
+  auto run = [&](GemmArgs& g) -> qt_status {
+    QT_LAUNCH(launch_gemm(g, st));
+    return ok();
+  };
+  // A GEMM that writes residual / projection rows v also writes u = hi/lo(v * gain)
+  // for the next RMSNorm and one sum-of-squares slot per row block; returns the
+  // number of rows per block.
+  auto produce = [&](GemmArgs& g, const uint16_t* gain, uint16_t* u, uint16_t* u_lo, int u_ld,
+                     float* ss, int ss_ld) -> int {
+    g.u_gain = gain;
+    g.u_hi = u;
+    g.u_lo = u_lo;
+    g.u_ld = u_ld;
+    g.ss_out = ss;
+    g.ss_out_ld = ss_ld;
+    return plan_gemm(g.nrows, g.K, g.M, g.scale != nullptr).rows_per_block;
+  };
+
+  // One decoder layer over M rows of residual x (row stride = hidden).  u / u_lo:
+  // the normalised-input buffer of the stack; ss / ss_ld: sums of squares of x;
+  // *slots: how many slots the last producer of x left; next_gain: gain of the
+  // norm that follows the layer.
+  auto layer = [&](const qt_decoder_cfg& d, const LayerSlots& L, float* x, uint16_t* u,
+                   uint16_t* u_lo, float* ss, int ss_ld, int* slots, const uint16_t* next_gain,
+                   int M, auto&& attention) -> qt_status {
+    qt_status r;
+    GemmArgs g = gemm_norm(m, L.qkv, u, u_lo, d.hidden, ss, ss_ld, *slots, d.rms_eps, M,
+                           out->status);
     g.epi = EPI_STORE;
     g.out_f32 = qkv;
     g.out_ld = w.qkv_ld;
-    QT_LAUNCH(launch_gemm(g, st));
-    qt_status s2 = attention();
-    if (s2) return s2;
-    g = gemm_base(m, L.o, o, o_lo, w.o_ld, M, out->status);
+    if ((r = run(g))) return r;
+    if ((r = attention())) return r;
+    g = gemm_act(m, L.o, o, o_lo, w.o_ld, M, out->status);
     g.epi = EPI_RESID;
     g.out_f32 = x;
     g.out_ld = d.hidden;
-    QT_LAUNCH(launch_gemm(g, st));
-    QT_LAUNCH(launch_rmsnorm(x, d.hidden, vp(m, L.post_norm), d.hidden, d.rms_eps, u, u_lo, w.u_ld, M, st));
-    g = gemm_base(m, L.gu, u, u_lo, w.u_ld, M, out->status);
+    *slots = d.hidden / produce(g, vp(m, L.post_norm), u, u_lo, d.hidden, ss, ss_ld);
+    if ((r = run(g))) return r;
+    g = gemm_norm(m, L.gu, u, u_lo, d.hidden, ss, ss_ld, *slots, d.rms_eps, M, out->status);
     g.epi = EPI_SWIGLU;
     g.out_bf16 = ffn;
     g.out_bf16_lo = ffn_lo;
     g.out_ld = w.f_ld;
-    QT_LAUNCH(launch_gemm(g, st));
-    g = gemm_base(m, L.down, ffn, ffn_lo, w.f_ld, M, out->status);
+    if ((r = run(g))) return r;
+    g = gemm_act(m, L.down, ffn, ffn_lo, w.f_ld, M, out->status);
     g.epi = EPI_RESID;
     g.out_f32 = x;
     g.out_ld = d.hidden;
-    QT_LAUNCH(launch_gemm(g, st));
-    return ok();
+    *slots = d.hidden / produce(g, next_gain, u, u_lo, d.hidden, ss, ss_ld);
+    return run(g);
   };
+  int t_slots = 1, p_slots = 1;
+  const int ss_t_ld = B, ss_p_ld = 2 * B;
 
-  GemmArgs head = gemm_base(m, m->plan.t_head, u, u_lo, w.u_ld, B, out->status);
-  head.epi = EPI_HEAD;
-  head.logits = out->logits0;
-  head.logits_ld = c.talker_vocab;
-  head.n_logits = c.talker_vocab;
-  head.argmax_range = c.cb0_range;
-  head.keys = keys;
-  head.keys_ld = ncb;
-  head.out_f32 = x_p;  // projection rows land in predictor rows [0, B)
-  head.out_ld = Pd.hidden;
+  GemmArgs head = gemm_act(m, m->plan.t_head, (const uint16_t*)in->h_in, nullptr, T.hidden, B,
+                           out->status);
 
   if (talker) {
     const int pps_raw = (B * T.n_kv_heads * max_pages + 2047) / 2048;
@@ -429,7 +477,10 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
     const size_t layer_elems = (size_t)kv->num_pages * T.n_kv_heads * kPage * kHeadDim;
     for (int l = 0; l < T.layers; ++l) {
       const LayerSlots& L = m->plan.tl[l];
-      qt_status s = layer(T, L, x_t, B, [&]() -> qt_status {
+      const uint16_t* next_gain =
+          vp(m, l + 1 < T.layers ? m->plan.tl[l + 1].in_norm : m->plan.t_final);
+      qt_status s = layer(T, L, x_t, ut, ut_lo, ss_t, ss_t_ld, &t_slots, next_gain, B,
+                          [&]() -> qt_status {
         AttnPagedArgs a{};
         a.qkv = qkv;
         a.qkv_ld = w.qkv_ld;
@@ -457,15 +508,29 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
       });
       if (s) return s;
     }
-    QT_LAUNCH(launch_rmsnorm(x_t, T.hidden, vp(m, m->plan.t_final), T.hidden, T.rms_eps, u, u_lo, w.u_ld, B, st));
+    head = gemm_norm(m, m->plan.t_head, ut, ut_lo, T.hidden, ss_t, ss_t_ld, t_slots, T.rms_eps, B,
+                     out->status);
     head.nrows = mode == QT_MODE_TALKER ? c.talker_vocab : c.talker_vocab + Pd.hidden;
-    QT_LAUNCH(launch_gemm(head, st));
   } else {
-    // projection only, from the caller's bf16 hidden state (copied into u by frame_begin)
-    head.act_lo = nullptr;
+    // projection only, from the caller's bf16 post-norm Talker hidden state
     head.row0 = c.talker_vocab;
     head.nrows = Pd.hidden;
-    QT_LAUNCH(launch_gemm(head, st));
+  }
+  head.epi = EPI_HEAD;
+  head.logits = out->logits0;
+  head.logits_ld = c.talker_vocab;
+  head.n_logits = c.talker_vocab;
+  head.argmax_range = c.cb0_range;
+  head.keys = keys;
+  head.keys_ld = ncb;
+  head.out_f32 = x_p;  // projection rows land in predictor rows [0, B)
+  head.out_ld = Pd.hidden;
+  if (mode != QT_MODE_TALKER)
+    p_slots = Pd.hidden / produce(head, vp(m, m->plan.pl[0].in_norm), up, up_lo, Pd.hidden, ss_p,
+                                  ss_p_ld);
+  {
+    qt_status s = run(head);
+    if (s) return s;
   }
 
   if (mode != QT_MODE_TALKER) {
@@ -478,16 +543,27 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
       e.vocab = c.code_vocab;
       e.ncb = ncb;
       e.step = k;
+      e.eps = Pd.rms_eps;
       e.table = vp(m, m->plan.embeds[k - 1]);
       e.keys = keys;
       e.forced = in->forced;
       e.x = x_p;
+      e.ss = ss_p;
+      e.ss_ld = ss_p_ld;
+      if (k > 1) p_slots = 1;  // rows [0, B) are all new
+      e.ss_slots = p_slots;
+      e.gain = vp(m, m->plan.pl[0].in_norm);
+      e.u_hi = up;
+      e.u_lo = up_lo;
       e.row_off = emb_row;
       e.status = out->status;
       QT_LAUNCH(launch_embed(e, st));
       for (int l = 0; l < Pd.layers; ++l) {
         const LayerSlots& L = m->plan.pl[l];
-        qt_status s = layer(Pd, L, x_p, M, [&]() -> qt_status {
+        const uint16_t* next_gain =
+            vp(m, l + 1 < Pd.layers ? m->plan.pl[l + 1].in_norm : m->plan.p_final);
+        qt_status s = layer(Pd, L, x_p, up, up_lo, ss_p, ss_p_ld, &p_slots, next_gain, M,
+                            [&]() -> qt_status {
           AttnPredArgs a{};
           a.qkv = qkv;
           a.qkv_ld = w.qkv_ld;
@@ -511,9 +587,9 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
         });
         if (s) return s;
       }
-      QT_LAUNCH(launch_rmsnorm(x_p + (size_t)emb_row * Pd.hidden, Pd.hidden, vp(m, m->plan.p_final),
-                               Pd.hidden, Pd.rms_eps, u, u_lo, w.u_ld, B, st));
-      GemmArgs g = gemm_base(m, m->plan.heads[k - 1], u, u_lo, w.u_ld, B, out->status);
+      GemmArgs g = gemm_norm(m, m->plan.heads[k - 1], up + (size_t)emb_row * Pd.hidden,
+                             up_lo + (size_t)emb_row * Pd.hidden, Pd.hidden, ss_p + emb_row, ss_p_ld,
+                             p_slots, Pd.rms_eps, B, out->status);
       g.epi = EPI_HEAD;
       g.logits = out->logits_pred + (size_t)(k - 1) * c.code_vocab;
       g.logits_ld = (ncb - 1) * c.code_vocab;
@@ -521,7 +597,8 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
       g.argmax_range = c.code_vocab;
       g.keys = keys + k;
       g.keys_ld = ncb;
-      QT_LAUNCH(launch_gemm(g, st));
+      qt_status s = run(g);
+      if (s) return s;
     }
   }
 

@@ -32,8 +32,14 @@ struct GemmArgs {
   int N, K;               // full matrix
   int row0, nrows;        // rows [row0, row0+nrows) are computed
   const uint16_t* act;    // bf16 [M][act_ld]: high part of the activations
-  const uint16_t* act_lo; // bf16 [M][act_ld]: low part (act + act_lo ~ the fp32 value), or nullptr
+  const uint16_t* act_lo; // bf16 [M][act_ld]: low part, or nullptr
   int act_ld, M;
+  // Consumer of an RMSNorm: the activations are x * gain (left by the producer of
+  // x), so every output is multiplied by inv[m] = 1/sqrt(sum_s ss_in[s*ss_in_ld+m]/K
+  // + eps), the producer's per-row-block sums of squares.  ss_in == nullptr: none.
+  const float* ss_in;
+  int ss_in_ld, ss_in_slots;
+  float norm_eps;
   int epi;
   float* out_f32;
   int out_ld;
@@ -44,6 +50,23 @@ struct GemmArgs {
   unsigned long long* keys;  // greedy keys, one per m, stride keys_ld
   int keys_ld;
   uint32_t* status;
+  // Producer of an RMSNorm input (EPI_RESID rows, EPI_HEAD projection rows): for
+  // every written value v at output column c, u_hi/u_lo[m*u_ld + c] = hi/lo of
+  // v * u_gain[c] (the next norm's gain), and per row block the sum of squares of
+  // the block's values in ss_out[slot*ss_out_ld + m].  u_gain == nullptr: none.
+  const uint16_t* u_gain;
+  uint16_t* u_hi;
+  uint16_t* u_lo;
+  int u_ld;
+  float* ss_out;
+  int ss_out_ld;
+};
+
+// Launch shape chosen for one GEMM (see plan_gemm).
+struct GemmPlan {
+  bool mfma;
+  int mt, mp, rw, ni, rt, nw;
+  int rows_per_block, row_blocks;
 };
 
 struct AttnPagedArgs {
@@ -84,24 +107,32 @@ struct AttnPredArgs {
 
 struct FrameBeginArgs {
   int mode, B, Ht, ncb, n_kv, capacity;
+  float eps;
   const uint16_t* talker_in;
-  const uint16_t* h_in;
   const int32_t* tok0_in;
   const int32_t* kv_len;
   float* x_t;              // [B][Ht] f32
-  uint16_t* u;             // [B][u_ld] bf16 (PREDICTOR: h_in copied here)
-  int u_ld;
+  float* ss_t;             // [B]: sum of squares of the talker input rows (one slot)
+  const uint16_t* gain;    // [Ht]: gain of the first Talker norm
+  uint16_t* u_hi;          // [B][Ht]: hi/lo of x * gain
+  uint16_t* u_lo;
   unsigned long long* keys;  // [B][ncb]
-  unsigned* counters;        // [B][n_kv]
+  unsigned* counters;        // [B][n_kv] attention counters, zeroed
   uint32_t* status;
 };
 
 struct EmbedArgs {
   int B, H, vocab, ncb, step;   // step k >= 1 embeds the token of codebook k-1
+  float eps;
   const uint16_t* table;        // [vocab][H]
   const unsigned long long* keys;
   const int32_t* forced;        // [B][ncb] or nullptr
   float* x;                     // [rows][H]
+  float* ss;                    // sums of squares: slot 0 of the written rows, other slots zero
+  int ss_ld, ss_slots;
+  const uint16_t* gain;         // [H]: gain of the first predictor norm
+  uint16_t* u_hi;               // [rows][H]: hi/lo of x * gain
+  uint16_t* u_lo;
   int row_off;
   uint32_t* status;
 };
@@ -114,8 +145,7 @@ struct FrameEndArgs {
 };
 
 // launchers (enqueue only; shapes are validated by the caller)
-hipError_t launch_rmsnorm(const float* x, int x_ld, const uint16_t* g, int K, float eps,
-                          uint16_t* u, uint16_t* u_lo, int u_ld, int M, hipStream_t s);
+GemmPlan plan_gemm(int nrows, int K, int M, bool i8);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 hipError_t launch_attn_paged(const AttnPagedArgs& a, int B, float theta, hipStream_t s);
 hipError_t launch_attn_pred(const AttnPredArgs& a, float theta, hipStream_t s);

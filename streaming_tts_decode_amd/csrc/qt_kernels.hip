@@ -7,396 +7,13 @@
 // bf16, accumulation fp32, residual streams fp32, KV caches bf16.
 #include <math.h>
 
+#include "qt_device.h"
 #include "qt_internal.h"
 
 namespace qt {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-constexpr float kInvSqrtHd = 0.08838834764831845f;  // 1/sqrt(128)
-
-__device__ __forceinline__ float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
-__device__ __forceinline__ float bf_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
-__device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
-
-// float -> bfloat16 bits, round to nearest even (NaN stays NaN).
-__device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-
-// x ~ hi + lo with both parts bfloat16 (x - hi is exact in fp32).
-__device__ __forceinline__ void split_bf16(float x, uint16_t* hi, uint16_t* lo, size_t i) {
-  const uint16_t h = f2bf(x);
-  hi[i] = h;
-  lo[i] = f2bf(x - bf2f(h));
-}
-
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
-                                         __builtin_bit_cast(bf16x2, b), c, false);
-}
-
-__device__ __forceinline__ float dot8(const uint4& w, const uint4& x, float c) {
-  c = dot2(w.x, x.x, c);
-  c = dot2(w.y, x.y, c);
-  c = dot2(w.z, x.z, c);
-  return dot2(w.w, x.w, c);
-}
-
-// Two signed int8 (bytes 2i, 2i+1 of word) -> packed bf16 pair.  |q| <= 127 is
-// exact in bfloat16, so taking the high half of the float is exact.
-__device__ __forceinline__ uint32_t i8pair_to_bf16x2(uint32_t word, int i) {
-  const float lo = (float)(int)(int8_t)(word >> (16 * i));
-  const float hi = (float)(int)(int8_t)(word >> (16 * i + 8));
-  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
-}
-
-// Greedy key: order-preserving float bits in the high word, (~index) in the low
-// word, so a 64-bit max picks the largest value and, among equal values, the
-// lowest index.  -0 is folded onto +0 so that the two compare equal.
-__device__ __forceinline__ unsigned long long greedy_key(float v, int idx) {
-  v += 0.0f;
-  uint32_t u = __float_as_uint(v);
-  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ((unsigned long long)u << 32) | (unsigned long long)(0xffffffffu - (uint32_t)idx);
-}
-__device__ __forceinline__ int key_index(unsigned long long k) {
-  return (int)(0xffffffffu - (uint32_t)(k & 0xffffffffull));
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
-__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    unsigned long long w = __shfl_xor(v, o);
-    v = w > v ? w : v;
-  }
-  return v;
-}
-
-template <int V>
-struct Log2 {
-  static constexpr int value = 1 + Log2<V / 2>::value;
-};
-template <>
-struct Log2<1> {
-  static constexpr int value = 0;
-};
-
-// Sum V values held by every lane over the 64 lanes of the wave.  After the
-// call, lane l holds the total of value index (l >> (6 - log2 V)).  Halving
-// exchange: each step sends half of the remaining values to the partner lane.
-template <int V>
-__device__ __forceinline__ float transpose_reduce(float (&v)[V], int lane) {
-  constexpr int P = Log2<V>::value;
-#pragma unroll
-  for (int s = 0; s < P; ++s) {
-    const int h = (V >> s) >> 1;
-    const int o = 32 >> s;
-    const bool up = (lane & o) != 0;
-#pragma unroll
-    for (int i = 0; i < h; ++i) {
-      const float send = up ? v[i] : v[i + h];
-      const float keep = up ? v[i + h] : v[i];
-      v[i] = keep + __shfl_xor(send, o);
-    }
-  }
-  float r = v[0];
-#pragma unroll
-  for (int o = 32 >> P; o >= 1; o >>= 1) r += __shfl_xor(r, o);
-  return r;
-}
-
-__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
-
-// Epilogue over a block's finished tile: tile[r * tld + m] is the dot product
-// of weight row n0 + r with activation row m (before the INT8 scale).
-__device__ void gemm_epilogue(const GemmArgs& a, int n0, int rows, const float* tile, int tld) {
-  const int M = a.M;
-  const int tid = threadIdx.x, nthr = blockDim.x;
-  if (a.epi == EPI_SWIGLU) {
-    for (int e = tid; e < (rows >> 1) * M; e += nthr) {
-      const int pr = e / M, m = e - pr * M;
-      const int n = n0 + 2 * pr;
-      float g = tile[(2 * pr) * tld + m], u = tile[(2 * pr + 1) * tld + m];
-      if (a.scale) {
-        g *= a.scale[n];
-        u *= a.scale[n + 1];
-      }
-      split_bf16(silu(g) * u, a.out_bf16, a.out_bf16_lo, (size_t)m * a.out_ld + (n >> 1));
-    }
-    return;
-  }
-  for (int e = tid; e < rows * M; e += nthr) {
-    const int r = e / M, m = e - r * M;
-    const int n = n0 + r;
-    float y = tile[r * tld + m];
-    if (a.scale) y *= a.scale[n];
-    if (a.epi == EPI_STORE) {
-      a.out_f32[(size_t)m * a.out_ld + n] = y;
-    } else if (a.epi == EPI_RESID) {
-      a.out_f32[(size_t)m * a.out_ld + n] += y;
-    } else {  // EPI_HEAD
-      if (n < a.n_logits)
-        a.logits[(size_t)m * a.logits_ld + n] = y;
-      else
-        a.out_f32[(size_t)m * a.out_ld + (n - a.n_logits)] = y;
-    }
-  }
-  if (a.epi == EPI_HEAD && n0 < a.argmax_range) {
-    const int lane = tid & 63, wave = tid >> 6, nw = nthr >> 6;
-    for (int m = wave; m < M; m += nw) {
-      unsigned long long best = 0;
-      bool nan = false;
-      for (int r = lane; r < rows; r += 64) {
-        const int n = n0 + r;
-        if (n >= a.argmax_range) break;
-        float y = tile[r * tld + m];
-        if (a.scale) y *= a.scale[n];
-        if (y != y) {
-          nan = true;
-          continue;
-        }
-        const unsigned long long k = greedy_key(y, n);
-        best = k > best ? k : best;
-      }
-      best = wave_max_u64(best);
-      if (nan) atomicOr(a.status, QT_STATUS_NAN);
-      if (lane == 0 && best) atomicMax(&a.keys[(size_t)m * a.keys_ld], best);
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// Skinny GEMM, VALU path (M <= 8 activation rows).
-// Block = 4 waves; wave w owns weight rows n0 + w*RW .. +RW and walks the whole
-// K range with 16-byte chunks per lane (lane-contiguous, so one wave load is
-// 1 KB of one row); activations come from L1/L2.  The RW x MP partial sums are
-// reduced across the wave with a halving exchange; no cross-wave reduction.
-template <int MP, int RW, bool I8>
-__global__ __launch_bounds__(256) void k_gemm_valu(GemmArgs a) {
-  constexpr int V = MP * RW;
-  constexpr int P = Log2<V>::value;
-  __shared__ float tile[4 * RW * MP];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n0 = a.row0 + blockIdx.x * 4 * RW;
-  const int nw0 = n0 + wave * RW;
-  const int M = a.M;
-  float acc[RW][MP];
-#pragma unroll
-  for (int r = 0; r < RW; ++r)
-#pragma unroll
-    for (int b = 0; b < MP; ++b) acc[r][b] = 0.0f;
-
-  if (!I8) {
-    const int KC = a.K >> 3;  // 8 bf16 per 16-byte chunk
-    const uint4* W = reinterpret_cast<const uint4*>(a.W);
-#pragma unroll 2
-    for (int kc = lane; kc < KC; kc += 64) {
-      uint4 x[MP], xl[MP];
-#pragma unroll
-      for (int b = 0; b < MP; ++b) {
-        x[b] = make_uint4(0, 0, 0, 0);
-        xl[b] = make_uint4(0, 0, 0, 0);
-        if (b < M) {
-          x[b] = reinterpret_cast<const uint4*>(a.act + (size_t)b * a.act_ld)[kc];
-          if (a.act_lo) xl[b] = reinterpret_cast<const uint4*>(a.act_lo + (size_t)b * a.act_ld)[kc];
-        }
-      }
-      uint4 w[RW];
-#pragma unroll
-      for (int r = 0; r < RW; ++r) w[r] = W[(size_t)(nw0 + r) * KC + kc];
-#pragma unroll
-      for (int r = 0; r < RW; ++r)
-#pragma unroll
-        for (int b = 0; b < MP; ++b) acc[r][b] = dot8(w[r], xl[b], dot8(w[r], x[b], acc[r][b]));
-    }
-  } else {
-    const int KC = a.K >> 4;  // 16 int8 per 16-byte chunk
-    const uint4* W = reinterpret_cast<const uint4*>(a.W);
-#pragma unroll 2
-    for (int kc = lane; kc < KC; kc += 64) {
-      uint4 x0[MP], x1[MP], l0[MP], l1[MP];
-#pragma unroll
-      for (int b = 0; b < MP; ++b) {
-        x0[b] = x1[b] = l0[b] = l1[b] = make_uint4(0, 0, 0, 0);
-        if (b < M) {
-          const uint4* p = reinterpret_cast<const uint4*>(a.act + (size_t)b * a.act_ld);
-          x0[b] = p[2 * kc];
-          x1[b] = p[2 * kc + 1];
-          if (a.act_lo) {
-            const uint4* pl = reinterpret_cast<const uint4*>(a.act_lo + (size_t)b * a.act_ld);
-            l0[b] = pl[2 * kc];
-            l1[b] = pl[2 * kc + 1];
-          }
-        }
-      }
-      uint4 wq[RW];
-#pragma unroll
-      for (int r = 0; r < RW; ++r) wq[r] = W[(size_t)(nw0 + r) * KC + kc];
-#pragma unroll
-      for (int r = 0; r < RW; ++r) {
-        uint4 wa, wb;  // 16 int8 -> 16 bf16
-        wa.x = i8pair_to_bf16x2(wq[r].x, 0);
-        wa.y = i8pair_to_bf16x2(wq[r].x, 1);
-        wa.z = i8pair_to_bf16x2(wq[r].y, 0);
-        wa.w = i8pair_to_bf16x2(wq[r].y, 1);
-        wb.x = i8pair_to_bf16x2(wq[r].z, 0);
-        wb.y = i8pair_to_bf16x2(wq[r].z, 1);
-        wb.z = i8pair_to_bf16x2(wq[r].w, 0);
-        wb.w = i8pair_to_bf16x2(wq[r].w, 1);
-#pragma unroll
-        for (int b = 0; b < MP; ++b)
-          acc[r][b] = dot8(wb, l1[b], dot8(wa, l0[b], dot8(wb, x1[b], dot8(wa, x0[b], acc[r][b]))));
-      }
-    }
-  }
-
-  float flat[V];
-#pragma unroll
-  for (int r = 0; r < RW; ++r)
-#pragma unroll
-    for (int b = 0; b < MP; ++b) flat[r * MP + b] = acc[r][b];
-  const float tot = transpose_reduce<V>(flat, lane);
-  if ((lane & ((64 >> P) - 1)) == 0) {
-    const int idx = lane >> (6 - P);
-    tile[(wave * RW + idx / MP) * MP + (idx % MP)] = tot;
-  }
-  __syncthreads();
-  gemm_epilogue(a, n0, 4 * RW, tile, MP);
-}
-
-// ---------------------------------------------------------------------------
-// Skinny GEMM, MFMA path (8 < M <= 64).  v_mfma_f32_16x16x32_bf16 with the
-// weight rows as the A operand (16 rows) and the activation rows as the B
-// operand (16 columns per tile, MT tiles).  Lane l feeds row (l & 15) at a
-// 32-element K slice starting at 32*(l >> 4) of every 128-element K step, and
-// the four MFMAs of the step take its four 8-element pieces; A and B use the
-// same K permutation, so the sum over K is unchanged.  The 4 waves of a block
-// split K; their accumulators are summed in a fixed order through LDS.
-template <int MT, int RT, bool I8>
-__global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs a) {
-  __shared__ float red[4][RT][MT][64][4];
-  __shared__ float tile[RT * 16 * MT * 16];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int i = lane & 15, q = lane >> 4;
-  const int n0 = a.row0 + blockIdx.x * RT * 16;
-  const int Kw = a.K >> 2;
-  const int kbeg = wave * Kw;
-  const int M = a.M;
-  f32x4 acc[RT][MT];
-#pragma unroll
-  for (int r = 0; r < RT; ++r)
-#pragma unroll
-    for (int t = 0; t < MT; ++t) acc[r][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int kb = kbeg; kb < kbeg + Kw; kb += 128) {
-    bf16x8 bop[MT][4], bol[MT][4];
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      const int m = t * 16 + i;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        bop[t][s] = __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
-        bol[t][s] = bop[t][s];
-      }
-      if (m < M) {
-        const size_t off = (size_t)m * a.act_ld + kb + 32 * q;
-        const uint4* p = reinterpret_cast<const uint4*>(a.act + off);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) bop[t][s] = __builtin_bit_cast(bf16x8, p[s]);
-        if (a.act_lo) {
-          const uint4* pl = reinterpret_cast<const uint4*>(a.act_lo + off);
-#pragma unroll
-          for (int s = 0; s < 4; ++s) bol[t][s] = __builtin_bit_cast(bf16x8, pl[s]);
-        }
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < RT; ++r) {
-      const int n = n0 + r * 16 + i;
-      bf16x8 aop[4];
-      if (!I8) {
-        const uint4* p = reinterpret_cast<const uint4*>(
-            reinterpret_cast<const uint16_t*>(a.W) + (size_t)n * a.K + kb + 32 * q);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) aop[s] = __builtin_bit_cast(bf16x8, p[s]);
-      } else {
-        const uint4* p = reinterpret_cast<const uint4*>(
-            reinterpret_cast<const int8_t*>(a.W) + (size_t)n * a.K + kb + 32 * q);
-        const uint4 w0 = p[0], w1 = p[1];
-        const uint32_t words[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          uint4 c;
-          c.x = i8pair_to_bf16x2(words[2 * s], 0);
-          c.y = i8pair_to_bf16x2(words[2 * s], 1);
-          c.z = i8pair_to_bf16x2(words[2 * s + 1], 0);
-          c.w = i8pair_to_bf16x2(words[2 * s + 1], 1);
-          aop[s] = __builtin_bit_cast(bf16x8, c);
-        }
-      }
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-#pragma unroll
-        for (int t = 0; t < MT; ++t) {
-          acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[s], bop[t][s], acc[r][t], 0, 0, 0);
-          acc[r][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[s], bol[t][s], acc[r][t], 0, 0, 0);
-        }
-    }
-  }
-
-#pragma unroll
-  for (int r = 0; r < RT; ++r)
-#pragma unroll
-    for (int t = 0; t < MT; ++t)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) red[wave][r][t][lane][j] = acc[r][t][j];
-  __syncthreads();
-  // D layout of the 16x16 output: lane l, element j holds row 4*(l>>4)+j, column l&15.
-  constexpr int TLD = MT * 16;
-  for (int e = threadIdx.x; e < RT * MT * 256; e += 256) {
-    const int j = e & 3, l = (e >> 2) & 63, t = (e >> 8) % MT, r = (e >> 8) / MT;
-    const float s = red[0][r][t][l][j] + red[1][r][t][l][j] + red[2][r][t][l][j] + red[3][r][t][l][j];
-    tile[(r * 16 + 4 * (l >> 4) + j) * TLD + t * 16 + (l & 15)] = s;
-  }
-  __syncthreads();
-  gemm_epilogue(a, n0, RT * 16, tile, TLD);
-}
-
-// ---------------------------------------------------------------------------
-// Row RMSNorm: u = x / sqrt(mean(x^2) + eps) * g as a hi/lo bf16 pair.  One block per row.
-__global__ __launch_bounds__(256) void k_rmsnorm(const float* x, int x_ld, const uint16_t* g,
-                                                 int K, float eps, uint16_t* u, uint16_t* u_lo,
-                                                 int u_ld) {
-  __shared__ float part[4];
-  const int row = blockIdx.x, tid = threadIdx.x;
-  const float* xr = x + (size_t)row * x_ld;
-  float ss = 0.f;
-  for (int k = tid; k < K; k += 256) ss += xr[k] * xr[k];
-  ss = wave_sum(ss);
-  if ((tid & 63) == 0) part[tid >> 6] = ss;
-  __syncthreads();
-  const float tot = part[0] + part[1] + part[2] + part[3];
-  const float inv = 1.0f / sqrtf(tot / (float)K + eps);
-  const size_t base = (size_t)row * u_ld;
-  for (int k = tid; k < K; k += 256) split_bf16(xr[k] * inv * bf2f(g[k]), u, u_lo, base + k);
-}
+using namespace dev;
 
 // Per-head RMSNorm + rotate-half RoPE of one 128-vector held by 128 threads
 // (thread d of the group holds element d).  `buf` is a 128-float LDS slot used
@@ -613,32 +230,36 @@ __global__ __launch_bounds__(256) void k_attn_paged(AttnPagedArgs a, float theta
     split_bf16(out / lstat[jj], a.o, a.o_lo, orow);
     return;
   }
+  // Publish this split's partial with device-coherent stores, wait until they
+  // are performed, then count the split in.  The last split to arrive reads all
+  // partials with device-coherent loads.  (A full agent-scope fence here would
+  // write back and invalidate the whole L2 of the XCD once per block.)
   float* pp = a.part + (((size_t)b * a.n_q + j0 + jj) * a.n_splits + s) * 130;
-  pp[2 + d] = out;
+  dev_store(pp + 2 + d, out);
   if (d == 0) {
-    pp[0] = mstat[jj];
-    pp[1] = lstat[jj];
+    dev_store(pp, mstat[jj]);
+    dev_store(pp + 1, lstat[jj]);
   }
-  __threadfence();
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  unsigned* cnt = &a.counters[(size_t)b * a.n_kv + h];
   if (tid == 0) {
-    const unsigned prev = atomicAdd(&a.counters[(size_t)b * a.n_kv + h], 1u);
+    const unsigned prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = (prev == (unsigned)(n_active - 1));
   }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
   const float* pb = a.part + ((size_t)b * a.n_q + j0 + jj) * a.n_splits * 130;
   float M = -INFINITY;
-  for (int ss = 0; ss < n_active; ++ss) M = fmaxf(M, pb[ss * 130]);
+  for (int ss = 0; ss < n_active; ++ss) M = fmaxf(M, dev_load(pb + ss * 130));
   float L = 0.f, O = 0.f;
   for (int ss = 0; ss < n_active; ++ss) {
-    const float w = expf(pb[ss * 130] - M);
-    L = fmaf(pb[ss * 130 + 1], w, L);
-    O = fmaf(pb[ss * 130 + 2 + d], w, O);
+    const float w = expf(dev_load(pb + ss * 130) - M);
+    L = fmaf(dev_load(pb + ss * 130 + 1), w, L);
+    O = fmaf(dev_load(pb + ss * 130 + 2 + d), w, O);
   }
   split_bf16(O / L, a.o, a.o_lo, orow);
-  if (tid == 0) a.counters[(size_t)b * a.n_kv + h] = 0u;
+  if (tid == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------
@@ -753,17 +374,28 @@ __global__ __launch_bounds__(256) void k_attn_pred(AttnPredArgs a, float theta_l
 }
 
 // ---------------------------------------------------------------------------
+// Frame entry: Talker input rows to fp32 with their sums of squares, capacity
+// check, greedy keys and attention counters cleared.
 __global__ __launch_bounds__(256) void k_frame_begin(FrameBeginArgs a) {
+  __shared__ float part[4];
   const int b = blockIdx.x, tid = threadIdx.x;
   if (a.mode != QT_MODE_PREDICTOR) {
-    for (int i = tid; i < a.Ht; i += 256)
-      a.x_t[(size_t)b * a.Ht + i] = bf2f(a.talker_in[(size_t)b * a.Ht + i]);
+    float ss = 0.f;
+    for (int i = tid; i < a.Ht; i += 256) {
+      const size_t e = (size_t)b * a.Ht + i;
+      const float v = bf2f(a.talker_in[e]);
+      a.x_t[e] = v;
+      split_bf16(v * bf2f(a.gain[i]), a.u_hi, a.u_lo, e);
+      ss = fmaf(v, v, ss);
+    }
+    ss = wave_sum(ss);
+    if ((tid & 63) == 0) part[tid >> 6] = ss;
+    __syncthreads();
     if (tid == 0) {
+      a.ss_t[b] = part[0] + part[1] + part[2] + part[3];
       const int p = a.kv_len[b];
       if (p < 0 || p + 1 > a.capacity) atomicOr(a.status, QT_STATUS_KV_OVERFLOW);
     }
-  } else {
-    for (int i = tid; i < a.Ht; i += 256) a.u[(size_t)b * a.u_ld + i] = a.h_in[(size_t)b * a.Ht + i];
   }
   for (int k = tid; k < a.ncb; k += 256) {
     unsigned long long key = 0;
@@ -773,7 +405,10 @@ __global__ __launch_bounds__(256) void k_frame_begin(FrameBeginArgs a) {
   if (tid < a.n_kv) a.counters[(size_t)b * a.n_kv + tid] = 0u;
 }
 
+// Predictor step input: row E_step[token] (token = forced, or the previous step's
+// greedy token) to fp32, with its sum of squares.
 __global__ __launch_bounds__(256) void k_embed(EmbedArgs a) {
+  __shared__ float part[4];
   const int b = blockIdx.x, tid = threadIdx.x;
   int tok = a.forced ? a.forced[(size_t)b * a.ncb + a.step - 1]
                      : key_index(a.keys[(size_t)b * a.ncb + a.step - 1]);
@@ -783,7 +418,20 @@ __global__ __launch_bounds__(256) void k_embed(EmbedArgs a) {
   }
   const uint16_t* src = a.table + (size_t)tok * a.H;
   float* dst = a.x + (size_t)(a.row_off + b) * a.H;
-  for (int i = tid; i < a.H; i += 256) dst[i] = bf2f(src[i]);
+  float ss = 0.f;
+  const size_t ub = (size_t)(a.row_off + b) * a.H;
+  for (int i = tid; i < a.H; i += 256) {
+    const float v = bf2f(src[i]);
+    dst[i] = v;
+    split_bf16(v * bf2f(a.gain[i]), a.u_hi, a.u_lo, ub + i);
+    ss = fmaf(v, v, ss);
+  }
+  ss = wave_sum(ss);
+  if ((tid & 63) == 0) part[tid >> 6] = ss;
+  __syncthreads();
+  const int m = a.row_off + b;
+  for (int sl = tid; sl < a.ss_slots; sl += 256)
+    a.ss[(size_t)sl * a.ss_ld + m] = sl == 0 ? part[0] + part[1] + part[2] + part[3] : 0.f;
 }
 
 __global__ __launch_bounds__(256) void k_frame_end(FrameEndArgs a) {
@@ -827,63 +475,9 @@ __global__ __launch_bounds__(256) void k_quantize(const uint16_t* w, long long c
   }
 }
 
-inline int pow2_at_least(int m) {
-  int p = 1;
-  while (p < m) p <<= 1;
-  return p;
-}
-
-template <int MP, bool I8>
-hipError_t gemm_valu_mp(const GemmArgs& a, hipStream_t s) {
-  if (a.nrows >= 4096) {
-    hipLaunchKernelGGL((k_gemm_valu<MP, 4, I8>), dim3(a.nrows / 16), dim3(256), 0, s, a);
-  } else {
-    hipLaunchKernelGGL((k_gemm_valu<MP, 2, I8>), dim3(a.nrows / 8), dim3(256), 0, s, a);
-  }
-  return hipGetLastError();
-}
-
-template <int MT, bool I8>
-hipError_t gemm_mfma_mt(const GemmArgs& a, hipStream_t s) {
-  if (a.nrows >= 4096) {
-    hipLaunchKernelGGL((k_gemm_mfma<MT, 2, I8>), dim3(a.nrows / 32), dim3(256), 0, s, a);
-  } else {
-    hipLaunchKernelGGL((k_gemm_mfma<MT, 1, I8>), dim3(a.nrows / 16), dim3(256), 0, s, a);
-  }
-  return hipGetLastError();
-}
-
-template <bool I8>
-hipError_t gemm_dispatch(const GemmArgs& a, hipStream_t s) {
-  if (a.M <= 8) {
-    switch (pow2_at_least(a.M)) {
-      case 1: return gemm_valu_mp<1, I8>(a, s);
-      case 2: return gemm_valu_mp<2, I8>(a, s);
-      case 4: return gemm_valu_mp<4, I8>(a, s);
-      default: return gemm_valu_mp<8, I8>(a, s);
-    }
-  }
-  if (a.M <= 16) return gemm_mfma_mt<1, I8>(a, s);
-  if (a.M <= 32) return gemm_mfma_mt<2, I8>(a, s);
-  return gemm_mfma_mt<4, I8>(a, s);
-}
-
 }  // namespace
 
 // --------------------------------------------------------------------------- launchers
-hipError_t launch_rmsnorm(const float* x, int x_ld, const uint16_t* g, int K, float eps,
-                          uint16_t* u, uint16_t* u_lo, int u_ld, int M, hipStream_t s) {
-  hipLaunchKernelGGL(k_rmsnorm, dim3(M), dim3(256), 0, s, x, x_ld, g, K, eps, u, u_lo, u_ld);
-  return hipGetLastError();
-}
-
-hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
-  if (a.M < 1 || a.M > 64 || a.nrows <= 0 || (a.nrows % 64) || (a.K % 512) ||
-      (a.epi == EPI_SWIGLU && (a.row0 & 1)))
-    return hipErrorInvalidValue;
-  return a.scale ? gemm_dispatch<true>(a, s) : gemm_dispatch<false>(a, s);
-}
-
 hipError_t launch_attn_paged(const AttnPagedArgs& a, int B, float theta, hipStream_t s) {
   if (a.pages_per_split < 1 || a.pages_per_split > kMaxPagesPerSplit || a.n_q != 2 * a.n_kv)
     return hipErrorInvalidValue;
