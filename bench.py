@@ -24,6 +24,30 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 
+# HBM bytes per launch of a kernel, from two rocprofv3 --pmc runs of this script
+# (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by 1 GiB / the same
+# counter's reading for calibration_copy().  Keyed by (workload, kernel symbol), with
+# the digest of the kernel sources the counters were taken on: once the kernels
+# change, the entry no longer applies and `traffic` is reported as null.
+PMC_TRAFFIC = {}
+KERNEL_SOURCES = ["qt_gemm.hip", "qt_kernels.hip", "qt_device.h", "qt_internal.h"]
+
+
+def kernel_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "streaming_tts_decode_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def pmc_traffic(workload: str, kernel: str):
+    e = PMC_TRAFFIC.get((workload, kernel))
+    if e is None or e["digest"] != kernel_digest():
+        return None
+    return e["bytes_per_launch"]
+
 
 def weight_bytes(d, int8: bool) -> int:
     """Logical weight bytes one frame streams: every decode GEMM weight once per
@@ -55,13 +79,55 @@ def frame_bytes(d, lengths, int8: bool) -> int:
     return weight_bytes(d, int8) + per_sess
 
 
-def run_workload(pm, w, steps, warmup, log):
+def launch_bytes(d, kind, li, lengths, int8: bool) -> int:
+    """Algorithmic bytes of one kernel launch of a frame whose sessions hold
+    `lengths` cached Talker positions.
+      GEMM:        the weight [n, k] once (bf16: 2nk; INT8: nk + 4n of row scales), plus
+                   the f32 logits a head writes (4 * m * n_logits); activations are
+                   not counted (they could stay on chip).
+      attn_paged:  per session, this layer's K and V over positions 0..L_b (the cache
+                   plus the new one) and the appended pair: 4 * n_kv * head_dim * (L_b + 2).
+      embed:       one bf16 embedding row per session.
+      others:      0 (predictor K/V is frame-local and could stay on chip)."""
+    if kind == "gemm":
+        w = li.n * li.k + 4 * li.n if li.int8 else 2 * li.n * li.k
+        return w + 4 * li.m * li.n_logits
+    if kind == "attn_paged":
+        t = d.talker
+        return int(sum(4 * t.n_kv * t.head_dim * (int(L) + 2) for L in lengths))
+    if kind == "embed":
+        return li.m * d.predictor.hidden * 2
+    return 0
+
+
+def trace_frames(dec, d, lengths, n, int8, log):
+    """Run n frames whose every kernel carries start/stop events stamped with its
+    own begin and end; aggregate by kernel symbol: launches, summed milliseconds,
+    summed algorithmic bytes."""
+    per = {}
+    for f in range(n):
+        for name, kind, li, ms in dec.trace("full", forced=False):
+            e = per.setdefault(name, {"kind": kind, "launches": 0, "ms": 0.0, "bytes": 0})
+            e["launches"] += 1
+            e["ms"] += ms
+            e["bytes"] += launch_bytes(d, kind, li, lengths + f, int8)
+    total = sum(e["ms"] for e in per.values())
+    for name, e in sorted(per.items(), key=lambda kv: -kv[1]["ms"]):
+        e["avg_us"] = 1e3 * e["ms"] / e["launches"]
+        e["gbs"] = e["bytes"] / (e["ms"] / 1e3) / 1e9
+        e["share"] = e["ms"] / total
+        log(f"[trace] {name:28s} {e['launches'] / n:6.0f}/frame {e['avg_us']:9.2f} us "
+            f"{e['gbs']:8.1f} GB/s {100 * e['share']:5.1f}%")
+    return per, total / n
+
+
+def run_workload(pm, w, steps, warmup, log, n_trace=0):
     import numpy as np
     import torch
 
     import synth
     from streaming_tts_decode_amd.runtime import setup_workload
-    frames = max(w.frames, steps + warmup)
+    frames = max(w.frames, steps + warmup + n_trace)
     wcap = dataclasses.replace(w, frames=frames)
     dec, lengths = setup_workload(wcap, pm)
     ins = synth.frame_inputs(w)["talker_in"]  # [w.frames, B, H]
@@ -91,16 +157,53 @@ def run_workload(pm, w, steps, warmup, log):
     if status:
         raise RuntimeError(f"{w.name}: device status {status:#x}")
     nbytes = sum(frame_bytes(w.dims, lengths + f, pm.int8) for f in range(steps))
+    per, traced_ms = (trace_frames(dec, w.dims, lengths + steps, n_trace, pm.int8, log)
+                      if n_trace else (None, None))
     res = {
         "workload": w.name, "batch": w.batch, "frames": steps,
         "ms_per_frame": ms / steps, "codec_frames_per_s": w.batch * steps / (ms / 1e3),
         "hbm_gbs_algorithmic": nbytes / (ms / 1e3) / 1e9,
         "bytes_per_frame": nbytes / steps, "wall_s": wall,
+        "kernels": per, "traced_ms_per_frame": traced_ms,
     }
     res["hbm_frac"] = res["hbm_gbs_algorithmic"] / HBM_PEAK_GBS
-    log(f"[bench] {res}")
+    log(f"[bench] { {k: v for k, v in res.items() if k != 'kernels'} }")
     dec.close()
     return res, lengths
+
+
+def roofline(res, n_trace):
+    """The kernel symbol with the largest share of the traced frames' time, against
+    the HBM roofline: algorithmic bytes per launch / average launch duration."""
+    per = res["kernels"]
+    name = max(per, key=lambda k: per[k]["ms"])
+    e = per[name]
+    return {
+        "bound": "hbm", "kernel": name,
+        "achieved": e["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": e["gbs"] / HBM_PEAK_GBS,
+        "traffic": pmc_traffic(res["workload"], name),
+        "avg_launch_us": e["avg_us"], "launches_per_frame": e["launches"] / n_trace,
+        "algorithmic_bytes_per_launch": e["bytes"] / e["launches"],
+        "share_of_frame": e["share"],
+        "timing": f"start/stop HIP events stamped by each kernel (hipExtLaunchKernel) over "
+                  f"{n_trace} frames on the frame's stream",
+    }
+
+
+def calibration_copy(log):
+    """A plain 1 GiB device-to-device copy: the byte count hardware counters read for
+    it calibrates their readings of the decode kernels."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[calib] copied {n} bytes device to device")
+    del src, dst
 
 
 def cpu_baseline(w, weights, seconds: float, log):
@@ -139,6 +242,8 @@ def main():
     ap.add_argument("--int8", action="store_true", help="INT8 weight-only decode")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--trace-frames", type=int, default=5,
+                    help="eager frames timed launch by launch for the roofline")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -162,10 +267,12 @@ def main():
     if args.int8:
         head = dataclasses.replace(head, int8=True)
     d = head.dims
+    log(f"[bench] kernel sources digest {kernel_digest()}")
     log(f"[bench] generating weights")
     W = synth.gen_weights(d)
     pm = PackedModel(d, W, int8=head.int8)
-    main_res, lengths = run_workload(pm, head, args.steps, args.warmup, log)
+    main_res, lengths = run_workload(pm, head, args.steps, args.warmup, log,
+                                     n_trace=max(1, args.trace_frames))
     extra = {}
     for name in [x for x in args.also.split(",") if x]:
         w = dataclasses.replace(synth.WORKLOADS[name], int8=head.int8)
@@ -173,6 +280,7 @@ def main():
         extra[f"B{w.batch}"] = {k: r[k] for k in ("codec_frames_per_s", "ms_per_frame",
                                                   "hbm_gbs_algorithmic", "hbm_frac")}
     pm.close()
+    calibration_copy(log)
     cpu = None if args.no_cpu_baseline else cpu_baseline(head, W, args.cpu_seconds, log)
 
     out = {
@@ -196,7 +304,7 @@ def main():
         "frame_hbm_frac": main_res["hbm_frac"],
         "bytes_per_frame": main_res["bytes_per_frame"],
         "other_batches": extra,
-        "roofline": None,
+        "roofline": roofline(main_res, max(1, args.trace_frames)),
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

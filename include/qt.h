@@ -217,6 +217,56 @@ qt_status qt_frame_graph_launch(qt_graph* graph, void* stream);
 void qt_graph_destroy(qt_graph* graph);
 void qt_model_destroy(qt_model* model);
 
+/* ------------------------------------------------------------------ tracing
+ * Per-kernel timing of one frame, for measuring each kernel against the memory
+ * roofline.  A frame is launched as a sequence of kernels; qt_frame_trace enqueues
+ * exactly the kernels qt_frame_decode enqueues, with the same arguments, each
+ * through hipExtLaunchKernel with a start and a stop event that the runtime stamps
+ * with that kernel's own begin and end (dispatch gaps between kernels are not in
+ * the intervals).  The frame's results are the same as qt_frame_decode's. */
+typedef enum {
+  QT_KERNEL_FRAME_BEGIN = 0, /* k_frame_begin: per-session entry state */
+  QT_KERNEL_GEMM = 1,        /* k_gemm_valu / k_gemm_mfma: one weight matrix over m rows */
+  QT_KERNEL_ATTN_PAGED = 2,  /* k_attn_paged: Talker q/k-norm, RoPE, KV append, paged attention */
+  QT_KERNEL_ATTN_PRED = 3,   /* k_attn_pred: the same over the predictor's frame-local KV */
+  QT_KERNEL_EMBED = 4,       /* k_embed: codebook-embedding gather of a predictor step */
+  QT_KERNEL_FRAME_END = 5    /* k_frame_end: tokens out, kv_len advance */
+} qt_kernel_kind;
+
+typedef struct {
+  int32_t kind;     /* qt_kernel_kind */
+  int32_t step;     /* 0: Talker or frame entry/exit; k in 1..n_codebooks-1: predictor step k */
+  int32_t layer;    /* decoder layer of the launch, -1 if none */
+  int32_t m;        /* GEMM: activation rows; other kernels: sessions */
+  int32_t n, k;     /* GEMM: weight rows and columns streamed (W is [n, k]); else 0 */
+  int32_t int8;     /* GEMM: 1 if the weight is INT8 + f32 row scales, 0 if bf16 */
+  int32_t n_logits; /* GEMM: f32 logits written per row (head GEMMs), else 0 */
+  char name[40];    /* kernel symbol with its template arguments, e.g. "k_gemm_mfma<2,2,false>" */
+} qt_launch_info;
+
+typedef struct qt_trace qt_trace;
+
+/* Create a trace handle holding timing events for up to max_launches launches. */
+qt_status qt_trace_create(int32_t max_launches, qt_trace** out);
+
+/* Number of kernel launches one frame of this mode and batch makes. */
+qt_status qt_frame_launch_count(const qt_model_cfg* cfg, int32_t mode, int32_t* n);
+
+/* Enqueue one frame exactly as qt_frame_decode (same arguments and checks) with the
+ * trace's events recorded around its launches.  QT_E_CAPACITY, before anything is
+ * enqueued, if the frame has more launches than the trace holds. */
+qt_status qt_frame_trace(qt_model* model, const qt_sessions* sessions, const qt_kv_caches* kv,
+                         const qt_frame_inputs* in, const qt_frame_outputs* out, void* workspace,
+                         uint64_t workspace_bytes, void* stream, qt_trace* trace);
+
+/* Wait for the last traced frame to finish and read it back: info[i] (host array) and
+ * ms[i] = milliseconds from begin to end of launch i, for i < *n.  QT_E_CAPACITY
+ * if max < the number of launches; QT_E_STATE if no frame has been traced. */
+qt_status qt_trace_read(qt_trace* trace, qt_launch_info* info, float* ms, int32_t max,
+                        int32_t* n);
+
+void qt_trace_destroy(qt_trace* trace);
+
 #ifdef __cplusplus
 }
 #endif

@@ -25,7 +25,10 @@ STATUS_KV_OVERFLOW, STATUS_BAD_PAGE, STATUS_BAD_TOKEN, STATUS_NAN = 1, 2, 4, 8
 EXPORTED = ["qt_last_error", "qt_abi_version", "qt_validate_cfg", "qt_packed_bytes",
             "qt_workspace_bytes", "qt_load_weights", "qt_quantize_int8", "qt_model_export_int8",
             "qt_frame_decode", "qt_frame_graph_create", "qt_frame_graph_launch",
-            "qt_graph_destroy", "qt_model_destroy"]
+            "qt_graph_destroy", "qt_model_destroy", "qt_trace_create", "qt_frame_launch_count",
+            "qt_frame_trace", "qt_trace_read", "qt_trace_destroy"]
+KERNEL_KINDS = {0: "frame_begin", 1: "gemm", 2: "attn_paged", 3: "attn_pred", 4: "embed",
+                5: "frame_end"}
 
 
 class QtError(RuntimeError):
@@ -70,6 +73,12 @@ class FrameOutputs(C.Structure):
                 ("status", C.c_void_p)]
 
 
+class LaunchInfo(C.Structure):
+    _fields_ = [("kind", C.c_int32), ("step", C.c_int32), ("layer", C.c_int32), ("m", C.c_int32),
+                ("n", C.c_int32), ("k", C.c_int32), ("int8", C.c_int32), ("n_logits", C.c_int32),
+                ("name", C.c_char * 40)]
+
+
 _lib = None
 _P = C.c_void_p
 
@@ -112,6 +121,17 @@ def lib():
         L.qt_graph_destroy.argtypes = [_P]
         L.qt_model_destroy.restype = None
         L.qt_model_destroy.argtypes = [_P]
+        L.qt_trace_create.restype = st
+        L.qt_trace_create.argtypes = [C.c_int32, C.POINTER(_P)]
+        L.qt_frame_launch_count.restype = st
+        L.qt_frame_launch_count.argtypes = [C.POINTER(ModelCfg), C.c_int32, C.POINTER(C.c_int32)]
+        L.qt_frame_trace.restype = st
+        L.qt_frame_trace.argtypes = frame_args + [_P, _P]
+        L.qt_trace_read.restype = st
+        L.qt_trace_read.argtypes = [_P, C.POINTER(LaunchInfo), C.POINTER(C.c_float), C.c_int32,
+                                    C.POINTER(C.c_int32)]
+        L.qt_trace_destroy.restype = None
+        L.qt_trace_destroy.argtypes = [_P]
         _lib = L
     return _lib
 
@@ -209,3 +229,36 @@ def qt_graph_destroy(graph: int) -> None:
 
 def qt_model_destroy(model: int) -> None:
     lib().qt_model_destroy(model)
+
+
+def qt_trace_create(max_launches: int) -> int:
+    t = _P()
+    _check(lib().qt_trace_create(max_launches, C.byref(t)), "qt_trace_create")
+    return t.value
+
+
+def qt_frame_launch_count(cfg: ModelCfg, mode: int) -> int:
+    n = C.c_int32()
+    _check(lib().qt_frame_launch_count(C.byref(cfg), mode, C.byref(n)), "qt_frame_launch_count")
+    return n.value
+
+
+def qt_frame_trace(model: int, sessions: Sessions, kv: KvCaches, inputs: FrameInputs,
+                   outputs: FrameOutputs, workspace_ptr: int, workspace_bytes: int, stream: int,
+                   trace: int) -> None:
+    _check(lib().qt_frame_trace(model, C.byref(sessions), C.byref(kv), C.byref(inputs),
+                                C.byref(outputs), workspace_ptr, workspace_bytes, stream, trace),
+           "qt_frame_trace")
+
+
+def qt_trace_read(trace: int, max_launches: int):
+    """[(LaunchInfo, milliseconds)] of the last traced frame (waits for it)."""
+    info = (LaunchInfo * max_launches)()
+    ms = (C.c_float * max_launches)()
+    n = C.c_int32()
+    _check(lib().qt_trace_read(trace, info, ms, max_launches, C.byref(n)), "qt_trace_read")
+    return [(info[i], float(ms[i])) for i in range(n.value)]
+
+
+def qt_trace_destroy(trace: int) -> None:
+    lib().qt_trace_destroy(trace)

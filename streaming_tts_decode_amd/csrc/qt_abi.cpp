@@ -16,6 +16,10 @@
 
 using namespace qt;
 
+namespace qt {
+thread_local LaunchEvents g_launch_events;
+}
+
 namespace {
 
 thread_local std::string g_err;
@@ -32,6 +36,16 @@ qt_status fail(qt_status st, const char* fmt, ...) {
 
 qt_status ok() { return QT_OK; }
 
+// Launches of one frame: entry, per Talker layer QKV / attention / o / gate-up /
+// down, the head GEMM, per predictor step the gather, 5-kernel layers and the step
+// head, and the exit kernel.
+int frame_launches(const qt_model_cfg& c, int mode) {
+  int n = 3;  // entry, head GEMM, exit
+  if (mode != QT_MODE_PREDICTOR) n += 5 * c.talker.layers;
+  if (mode != QT_MODE_TALKER) n += (c.n_codebooks - 1) * (2 + 5 * c.predictor.layers);
+  return n;
+}
+
 #define QT_HIP(expr)                                                                   \
   do {                                                                                 \
     hipError_t e_ = (expr);                                                            \
@@ -45,6 +59,16 @@ constexpr int kMaxBatch = 32;  // predictor step 1 carries 2B rows; the GEMMs ta
 size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
 // ------------------------------------------------------------------ packed layout
+}  // namespace
+
+struct qt_trace {
+  std::vector<hipEvent_t> ev;  // start and stop of every launch
+  std::vector<qt_launch_info> info;
+  int n = -1;                  // launches of the last traced frame
+};
+
+namespace {
+
 struct MatSlot {
   size_t w = 0, s = 0;  // byte offsets of the weight rows and (INT8) the scales
   int N = 0, K = 0;
@@ -366,7 +390,7 @@ qt_status check_frame_args(const qt_model* m, const qt_sessions* ss, const qt_kv
 // per predictor step: [embedding gather] -> 5 such layers -> [step head].
 qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_caches* kv,
                         const qt_frame_inputs* in, const qt_frame_outputs* out, void* wsp,
-                        hipStream_t st) {
+                        hipStream_t st, qt_trace* tr = nullptr) {
   const qt_model_cfg& c = m->cfg;
   const qt_decoder_cfg &T = c.talker, &Pd = c.predictor;
   const int B = ss->batch, ncb = c.n_codebooks, mode = in->mode;
@@ -391,6 +415,45 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
   unsigned* cnt = (unsigned*)(ws + w.cnt);
   const int capacity = max_pages * kPage;
 
+  // Tracing: the next launch carries start/stop events stamped by the kernel itself.
+  int cur_step = 0, cur_layer = -1;
+  struct EventsOff {
+    ~EventsOff() { g_launch_events = LaunchEvents{}; }
+  } events_off;
+  if (tr) tr->n = 0;
+  auto mark = [&](int kind, const char* name, int rows, const GemmArgs* g) -> qt_status {
+    if (!tr) return ok();
+    if (tr->n >= (int)tr->info.size())
+      return fail(QT_E_CAPACITY, "trace holds %d launches", (int)tr->info.size());
+    qt_launch_info& li = tr->info[tr->n];
+    memset(&li, 0, sizeof li);
+    li.kind = kind;
+    li.step = cur_step;
+    li.layer = cur_layer;
+    li.m = rows;
+    if (g) {
+      li.n = g->nrows;
+      li.k = g->K;
+      li.int8 = g->scale != nullptr;
+      if (g->epi == EPI_HEAD) {
+        const int hi = g->row0 + g->nrows < g->n_logits ? g->row0 + g->nrows : g->n_logits;
+        li.n_logits = hi > g->row0 ? hi - g->row0 : 0;
+      }
+      gemm_kernel_name(*g, li.name, (int)sizeof li.name);
+    } else {
+      snprintf(li.name, sizeof li.name, "%s", name);
+    }
+    g_launch_events.start = tr->ev[2 * tr->n];
+    g_launch_events.stop = tr->ev[2 * tr->n + 1];
+    ++tr->n;
+    return ok();
+  };
+#define QT_MARK(...)                    \
+  do {                                  \
+    qt_status m_ = mark(__VA_ARGS__);   \
+    if (m_) return m_;                  \
+  } while (0)
+
   FrameBeginArgs fb{};
   fb.mode = mode;
   fb.B = B;
@@ -410,9 +473,11 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
   fb.keys = keys;
   fb.counters = cnt;
   fb.status = out->status;
+  QT_MARK(QT_KERNEL_FRAME_BEGIN, "k_frame_begin", B, nullptr);
   QT_LAUNCH(launch_frame_begin(fb, st));
 
   auto run = [&](GemmArgs& g) -> qt_status {
+    QT_MARK(QT_KERNEL_GEMM, nullptr, g.M, &g);
     QT_LAUNCH(launch_gemm(g, st));
     return ok();
   };
@@ -476,6 +541,7 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
     const int n_splits = (max_pages + pps - 1) / pps;
     const size_t layer_elems = (size_t)kv->num_pages * T.n_kv_heads * kPage * kHeadDim;
     for (int l = 0; l < T.layers; ++l) {
+      cur_layer = l;
       const LayerSlots& L = m->plan.tl[l];
       const uint16_t* next_gain =
           vp(m, l + 1 < T.layers ? m->plan.tl[l + 1].in_norm : m->plan.t_final);
@@ -503,11 +569,13 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
         a.o_lo = o_lo;
         a.o_ld = w.o_ld;
         a.status = out->status;
+        QT_MARK(QT_KERNEL_ATTN_PAGED, "k_attn_paged", B, nullptr);
         QT_LAUNCH(launch_attn_paged(a, B, T.rope_theta, st));
         return ok();
       });
       if (s) return s;
     }
+    cur_layer = -1;
     head = gemm_norm(m, m->plan.t_head, ut, ut_lo, T.hidden, ss_t, ss_t_ld, t_slots, T.rms_eps, B,
                      out->status);
     head.nrows = mode == QT_MODE_TALKER ? c.talker_vocab : c.talker_vocab + Pd.hidden;
@@ -557,8 +625,12 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
       e.u_lo = up_lo;
       e.row_off = emb_row;
       e.status = out->status;
+      cur_step = k;
+      cur_layer = -1;
+      QT_MARK(QT_KERNEL_EMBED, "k_embed", B, nullptr);
       QT_LAUNCH(launch_embed(e, st));
       for (int l = 0; l < Pd.layers; ++l) {
+        cur_layer = l;
         const LayerSlots& L = m->plan.pl[l];
         const uint16_t* next_gain =
             vp(m, l + 1 < Pd.layers ? m->plan.pl[l + 1].in_norm : m->plan.p_final);
@@ -582,11 +654,13 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
           a.o = o;
           a.o_lo = o_lo;
           a.o_ld = w.o_ld;
+          QT_MARK(QT_KERNEL_ATTN_PRED, "k_attn_pred", B, nullptr);
           QT_LAUNCH(launch_attn_pred(a, Pd.rope_theta, st));
           return ok();
         });
         if (s) return s;
       }
+      cur_layer = -1;
       GemmArgs g = gemm_norm(m, m->plan.heads[k - 1], up + (size_t)emb_row * Pd.hidden,
                              up_lo + (size_t)emb_row * Pd.hidden, Pd.hidden, ss_p + emb_row, ss_p_ld,
                              p_slots, Pd.rms_eps, B, out->status);
@@ -610,8 +684,12 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
   fe.keys = keys;
   fe.tokens = out->tokens;
   fe.kv_len = ss->kv_len;
+  cur_step = 0;
+  cur_layer = -1;
+  QT_MARK(QT_KERNEL_FRAME_END, "k_frame_end", B, nullptr);
   QT_LAUNCH(launch_frame_end(fe, st));
   return ok();
+#undef QT_MARK
 }
 
 }  // namespace
@@ -824,5 +902,71 @@ void qt_graph_destroy(qt_graph* graph) {
 }
 
 void qt_model_destroy(qt_model* model) { delete model; }
+
+qt_status qt_trace_create(int32_t max_launches, qt_trace** out) {
+  if (!out) return fail(QT_E_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  if (max_launches < 1 || max_launches > (1 << 20))
+    return fail(QT_E_INVALID_ARG, "max_launches = %d", max_launches);
+  qt_trace* t = new qt_trace();
+  t->info.resize(max_launches);
+  for (int i = 0; i < 2 * max_launches; ++i) {
+    hipEvent_t e;
+    hipError_t r = hipEventCreate(&e);
+    if (r != hipSuccess) {
+      qt_trace_destroy(t);
+      return fail(QT_E_HIP, "hipEventCreate failed: %s", hipGetErrorString(r));
+    }
+    t->ev.push_back(e);
+  }
+  *out = t;
+  return ok();
+}
+
+qt_status qt_frame_launch_count(const qt_model_cfg* cfg, int32_t mode, int32_t* n) {
+  qt_status st = check_cfg(cfg);
+  if (st) return st;
+  if (!n) return fail(QT_E_INVALID_ARG, "n is NULL");
+  if (mode < QT_MODE_FULL || mode > QT_MODE_PREDICTOR)
+    return fail(QT_E_INVALID_ARG, "mode = %d is not a qt_mode", mode);
+  *n = frame_launches(*cfg, mode);
+  return ok();
+}
+
+qt_status qt_frame_trace(qt_model* model, const qt_sessions* sessions, const qt_kv_caches* kv,
+                         const qt_frame_inputs* in, const qt_frame_outputs* out, void* workspace,
+                         uint64_t workspace_bytes, void* stream, qt_trace* trace) {
+  if (!trace) return fail(QT_E_INVALID_ARG, "trace is NULL");
+  qt_status st = check_frame_args(model, sessions, kv, in, out, workspace, workspace_bytes);
+  if (st) return st;
+  const int need = frame_launches(model->cfg, in->mode);
+  if (need > (int)trace->info.size())
+    return fail(QT_E_CAPACITY, "the frame makes %d launches, the trace holds %d", need,
+                (int)trace->info.size());
+  trace->n = -1;
+  st = enqueue_frame(model, sessions, kv, in, out, workspace, (hipStream_t)stream, trace);
+  if (st) trace->n = -1;
+  return st;
+}
+
+qt_status qt_trace_read(qt_trace* trace, qt_launch_info* info, float* ms, int32_t max,
+                        int32_t* n) {
+  if (!trace || !info || !ms || !n) return fail(QT_E_INVALID_ARG, "a pointer is NULL");
+  if (trace->n < 0) return fail(QT_E_STATE, "no frame has been traced");
+  if (max < trace->n) return fail(QT_E_CAPACITY, "%d launches, room for %d", trace->n, max);
+  if (trace->n > 0) QT_HIP(hipEventSynchronize(trace->ev[2 * trace->n - 1]));
+  for (int i = 0; i < trace->n; ++i) {
+    info[i] = trace->info[i];
+    QT_HIP(hipEventElapsedTime(&ms[i], trace->ev[2 * i], trace->ev[2 * i + 1]));
+  }
+  *n = trace->n;
+  return ok();
+}
+
+void qt_trace_destroy(qt_trace* trace) {
+  if (!trace) return;
+  for (hipEvent_t e : trace->ev) (void)hipEventDestroy(e);
+  delete trace;
+}
 
 }  // extern "C"

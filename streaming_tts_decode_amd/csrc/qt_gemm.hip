@@ -20,6 +20,8 @@
 // RMSNorm is split between producer and consumer: the GEMM (or kernel) that
 // writes a residual row v also writes hi/lo(v * gain) and the row block's sum of
 // squares; the consuming GEMM multiplies its outputs by 1/rms from those sums.
+#include <stdio.h>
+
 #include "qt_device.h"
 #include "qt_internal.h"
 
@@ -340,18 +342,18 @@ template <int MP, bool I8>
 hipError_t valu_ni(const GemmArgs& a, int ni, hipStream_t s) {
   const dim3 grid(a.nrows / 4);
   switch (ni) {
-    case 1: hipLaunchKernelGGL((k_gemm_valu<MP, 1, I8>), grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_gemm_valu<MP, 2, I8>), grid, dim3(256), 0, s, a); break;
-    case 3: hipLaunchKernelGGL((k_gemm_valu<MP, 3, I8>), grid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((k_gemm_valu<MP, 4, I8>), grid, dim3(256), 0, s, a); break;
+    case 1: launch_kernel((k_gemm_valu<MP, 1, I8>), grid, dim3(256), s, a); break;
+    case 2: launch_kernel((k_gemm_valu<MP, 2, I8>), grid, dim3(256), s, a); break;
+    case 3: launch_kernel((k_gemm_valu<MP, 3, I8>), grid, dim3(256), s, a); break;
+    case 4: launch_kernel((k_gemm_valu<MP, 4, I8>), grid, dim3(256), s, a); break;
     default:
       if constexpr (I8) {
-        hipLaunchKernelGGL((k_gemm_valu<MP, 6, I8>), grid, dim3(256), 0, s, a);
+        launch_kernel((k_gemm_valu<MP, 6, I8>), grid, dim3(256), s, a);
       } else {
         if (ni <= 6)
-          hipLaunchKernelGGL((k_gemm_valu<MP, 6, I8>), grid, dim3(256), 0, s, a);
+          launch_kernel((k_gemm_valu<MP, 6, I8>), grid, dim3(256), s, a);
         else
-          hipLaunchKernelGGL((k_gemm_valu<MP, 12, I8>), grid, dim3(256), 0, s, a);
+          launch_kernel((k_gemm_valu<MP, 12, I8>), grid, dim3(256), s, a);
       }
       break;
   }
@@ -363,9 +365,9 @@ hipError_t gemm_dispatch(const GemmArgs& a, const GemmPlan& p, hipStream_t s) {
   if (p.mfma) {
     const dim3 grid(a.nrows / 16), block(64 * kMfmaWaves);
     if (p.mt == 1)
-      hipLaunchKernelGGL((k_gemm_mfma<1, 2, I8>), grid, block, 0, s, a);
+      launch_kernel((k_gemm_mfma<1, 2, I8>), grid, block, s, a);
     else
-      hipLaunchKernelGGL((k_gemm_mfma<2, 2, I8>), grid, block, 0, s, a);
+      launch_kernel((k_gemm_mfma<2, 2, I8>), grid, block, s, a);
     return hipGetLastError();
   }
   return p.mp == 1 ? valu_ni<1, I8>(a, p.ni, s) : valu_ni<2, I8>(a, p.ni, s);
@@ -391,6 +393,15 @@ GemmPlan plan_gemm(int nrows, int K, int M, bool i8) {
   }
   p.row_blocks = nrows / p.rows_per_block;
   return p;
+}
+
+void gemm_kernel_name(const GemmArgs& a, char* buf, int len) {
+  const bool i8 = a.scale != nullptr;
+  const GemmPlan p = plan_gemm(a.nrows, a.K, a.M, i8);
+  if (p.mfma)
+    snprintf(buf, len, "k_gemm_mfma<%d,2,%s>", p.mt, i8 ? "true" : "false");
+  else
+    snprintf(buf, len, "k_gemm_valu<%d,%d,%s>", p.mp, p.ni, i8 ? "true" : "false");
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {

@@ -2,6 +2,7 @@
 // kernels (qt_kernels.hip).  Not installed; not part of the public ABI.
 #pragma once
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 #include <stdint.h>
 
 #include "qt.h"
@@ -61,6 +62,23 @@ struct GemmArgs {
   float* ss_out;
   int ss_out_ld;
 };
+
+// Timing events attached to the next kernel launch on this thread (tracing only):
+// when set, the launch goes through hipExtLaunchKernelGGL, which stamps `start` and
+// `stop` with the kernel's own begin and end.
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+extern thread_local LaunchEvents g_launch_events;
+
+template <typename Kernel, typename... Args>
+inline void launch_kernel(Kernel kernel, dim3 grid, dim3 block, hipStream_t s, Args... args) {
+  if (g_launch_events.start)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, s, g_launch_events.start, g_launch_events.stop,
+                          0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+}
 
 // Launch shape chosen for one GEMM (see plan_gemm).
 struct GemmPlan {
@@ -146,6 +164,8 @@ struct FrameEndArgs {
 
 // launchers (enqueue only; shapes are validated by the caller)
 GemmPlan plan_gemm(int nrows, int K, int M, bool i8);
+// Kernel symbol (with template arguments) that launch_gemm picks for these arguments.
+void gemm_kernel_name(const GemmArgs& a, char* buf, int len);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 hipError_t launch_attn_paged(const AttnPagedArgs& a, int B, float theta, hipStream_t s);
 hipError_t launch_attn_pred(const AttnPredArgs& a, float theta, hipStream_t s);

@@ -481,7 +481,7 @@ __global__ __launch_bounds__(256) void k_quantize(const uint16_t* w, long long c
 hipError_t launch_attn_paged(const AttnPagedArgs& a, int B, float theta, hipStream_t s) {
   if (a.pages_per_split < 1 || a.pages_per_split > kMaxPagesPerSplit || a.n_q != 2 * a.n_kv)
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_attn_paged, dim3(a.n_splits, a.n_kv, B), dim3(256), 0, s, a,
+  launch_kernel(k_attn_paged, dim3(a.n_splits, a.n_kv, B), dim3(256), s, a,
                      (float)log2((double)theta));
   return hipGetLastError();
 }
@@ -489,23 +489,23 @@ hipError_t launch_attn_paged(const AttnPagedArgs& a, int B, float theta, hipStre
 hipError_t launch_attn_pred(const AttnPredArgs& a, float theta, hipStream_t s) {
   if (a.n_new < 1 || a.n_new > 2 || a.pos0 < 0 || a.pos0 + a.n_new > 16 || a.n_q != 2 * a.n_kv)
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_attn_pred, dim3(a.n_kv, a.B), dim3(256), 0, s, a,
+  launch_kernel(k_attn_pred, dim3(a.n_kv, a.B), dim3(256), s, a,
                      (float)log2((double)theta));
   return hipGetLastError();
 }
 
 hipError_t launch_frame_begin(const FrameBeginArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_frame_begin, dim3(a.B), dim3(256), 0, s, a);
+  launch_kernel(k_frame_begin, dim3(a.B), dim3(256), s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_embed(const EmbedArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_embed, dim3(a.B), dim3(256), 0, s, a);
+  launch_kernel(k_embed, dim3(a.B), dim3(256), s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_frame_end(const FrameEndArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_frame_end, dim3((a.B * a.ncb + 255) / 256), dim3(256), 0, s, a);
+  launch_kernel(k_frame_end, dim3((a.B * a.ncb + 255) / 256), dim3(256), s, a);
   return hipGetLastError();
 }
 
@@ -513,7 +513,7 @@ hipError_t launch_quantize(const uint16_t* w, long long rows, long long cols, in
                            long long q_row_stride, float* scale, long long scale_stride,
                            hipStream_t s) {
   if (rows <= 0 || cols <= 0 || rows > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_quantize, dim3((unsigned)rows), dim3(256), 0, s, w, cols, q, q_row_stride,
+  launch_kernel(k_quantize, dim3((unsigned)rows), dim3(256), s, w, cols, q, q_row_stride,
                      scale, scale_stride);
   return hipGetLastError();
 }

@@ -9,9 +9,11 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import (FrameInputs, FrameOutputs, KvCaches, MODES, QT_BF16, Sessions, make_cfg,
-               qt_frame_decode, qt_frame_graph_create, qt_frame_graph_launch, qt_graph_destroy,
-               qt_load_weights, qt_model_destroy, qt_packed_bytes, qt_workspace_bytes)
+from . import (KERNEL_KINDS, FrameInputs, FrameOutputs, KvCaches, MODES, QT_BF16, Sessions,
+               make_cfg, qt_frame_decode, qt_frame_graph_create, qt_frame_graph_launch,
+               qt_frame_launch_count, qt_frame_trace, qt_graph_destroy, qt_load_weights,
+               qt_model_destroy, qt_packed_bytes, qt_trace_create, qt_trace_destroy,
+               qt_trace_read, qt_workspace_bytes)
 
 PAGE = 16
 
@@ -111,6 +113,7 @@ class Decoder:
         self.tokens = torch.zeros((batch, dims.n_codebooks), dtype=torch.int32, device=self.dev)
         self.status = torch.zeros(1, dtype=torch.int32, device=self.dev)
         self.graphs = []
+        self._trace = None
 
     # ------------------------------------------------------------------ state
     def load_session_kv(self, b: int, k_bits: np.ndarray, v_bits: np.ndarray):
@@ -161,6 +164,18 @@ class Decoder:
         qt_frame_decode(self.model, ss, kv, fi, fo, self.ws_ptr, self.ws_bytes,
                         self.torch.cuda.current_stream(self.dev).cuda_stream)
 
+    def trace(self, mode: str = "full", forced: bool = False):
+        """Run one frame as decode() does with an event around every launch; waits for
+        it and returns [(kernel name, kind, info, ms)] in launch order."""
+        if self._trace is None:
+            self._trace_n = qt_frame_launch_count(self.cfg, MODES["full"])
+            self._trace = qt_trace_create(self._trace_n)
+        ss, kv, fi, fo = self._descs(mode, forced)
+        qt_frame_trace(self.model, ss, kv, fi, fo, self.ws_ptr, self.ws_bytes,
+                       self.torch.cuda.current_stream(self.dev).cuda_stream, self._trace)
+        return [(li.name.decode(), KERNEL_KINDS[li.kind], li, ms)
+                for li, ms in qt_trace_read(self._trace, self._trace_n)]
+
     def capture(self, mode: str = "full", forced: bool = False) -> int:
         ss, kv, fi, fo = self._descs(mode, forced)
         g = qt_frame_graph_create(self.model, ss, kv, fi, fo, self.ws_ptr, self.ws_bytes)
@@ -174,6 +189,9 @@ class Decoder:
         for g in self.graphs:
             qt_graph_destroy(g)
         self.graphs = []
+        if self._trace is not None:
+            qt_trace_destroy(self._trace)
+            self._trace = None
 
     def __del__(self):
         try:

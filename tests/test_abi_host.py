@@ -145,6 +145,33 @@ def test_frame_and_quantize_argument_errors(qt):
     lib.qt_model_destroy(None)
 
 
+def test_frame_launch_count(qt):
+    """Launches per frame: entry + exit + the head GEMM; 5 per Talker layer (QKV,
+    attention, o, gate/up, down); per predictor step a gather, 5 per layer, a head."""
+    for dims in (synth.FULL, synth.SMALL):
+        c = qt.make_cfg(dims)
+        t, p, steps = dims.talker.layers, dims.predictor.layers, dims.n_codebooks - 1
+        assert qt.qt_frame_launch_count(c, qt.MODE_FULL) == 3 + 5 * t + steps * (2 + 5 * p)
+        assert qt.qt_frame_launch_count(c, qt.MODE_TALKER) == 3 + 5 * t
+        assert qt.qt_frame_launch_count(c, qt.MODE_PREDICTOR) == 3 + steps * (2 + 5 * p)
+    assert qt.qt_frame_launch_count(qt.make_cfg(synth.FULL), qt.MODE_FULL) == 548
+    with pytest.raises(qt.QtError) as e:
+        qt.qt_frame_launch_count(qt.make_cfg(synth.FULL), 7)
+    assert e.value.status == 1
+
+
+def test_trace_argument_errors(qt):
+    lib = qt.lib()
+    t = C.c_void_p()
+    assert lib.qt_trace_create(0, C.byref(t)) == 1
+    assert lib.qt_trace_create(-5, C.byref(t)) == 1
+    assert lib.qt_trace_create(10, None) == 1
+    assert lib.qt_frame_trace(None, None, None, None, None, None, 0, None, None) == 1
+    n = C.c_int32()
+    assert lib.qt_trace_read(None, None, None, 0, C.byref(n)) == 1
+    lib.qt_trace_destroy(None)
+
+
 def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     import streaming_tts_decode_amd as qt
     monkeypatch.setattr(qt, "_lib", None)

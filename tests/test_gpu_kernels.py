@@ -55,7 +55,7 @@ def test_small_modes(small_pm, orc_small, mode):
 
 
 # ----------------------------------------------------------------- invariances
-def _run_eager(dec, w, frames_inputs, forced, use_graph=False, mode="full"):
+def _run_eager(dec, w, frames_inputs, forced, use_graph=False, mode="full", traces=None):
     torch = dec.torch
     g = dec.capture(mode, forced=True) if use_graph else None
     outs = []
@@ -63,6 +63,8 @@ def _run_eager(dec, w, frames_inputs, forced, use_graph=False, mode="full"):
         dec.set_inputs(talker_in=frames_inputs["talker_in"][f], forced=forced[f])
         if g is not None:
             dec.replay(g)
+        elif traces is not None:
+            traces.append(dec.trace(mode, forced=True))
         else:
             dec.decode(mode, forced=True)
         torch.cuda.synchronize()
@@ -98,6 +100,49 @@ def test_replays_are_bitwise_deterministic_and_equal_eager(small_pm):
         for a, b in zip(runs[0], r):
             for x, y in zip(a, b):
                 np.testing.assert_array_equal(x, y)
+
+
+@pytest.mark.parametrize("mode", ["full", "predictor"])
+def test_traced_frame_equals_untraced(small_pm, mode):
+    """qt_frame_trace runs the same kernels as qt_frame_decode: identical outputs,
+    one timed interval per launch, and launch records that match the frame's structure."""
+    import streaming_tts_decode_amd as qt
+    w = small_w("Strace", batch=3, frames=2, lens=[40, 300, 7])
+    fi, fz = synth.frame_inputs(w), _forced(w)
+    plain = _run_eager(_fresh(small_pm, w), w, fi, fz, mode=mode)
+    traces = []
+    dec = _fresh(small_pm, w)
+    traced = _run_eager(dec, w, fi, fz, mode=mode, traces=traces)
+    dec.close()
+    for a, b in zip(plain, traced):
+        for x, y in zip(a, b):
+            np.testing.assert_array_equal(x, y)
+    t, p = S.talker, S.predictor
+    n_steps = S.n_codebooks - 1
+    for rec in traces:
+        assert len(rec) == qt.qt_frame_launch_count(small_pm.cfg, qt.MODES[mode])
+        assert rec[0][1] == "frame_begin" and rec[-1][1] == "frame_end"
+        assert all(ms > 0 for *_, ms in rec)
+        kinds = [k for _, k, _, _ in rec]
+        gemms = [li for _, k, li, _ in rec if k == "gemm"]
+        n_tl = t.layers if mode == "full" else 0
+        assert kinds.count("attn_paged") == n_tl
+        assert kinds.count("attn_pred") == n_steps * p.layers
+        assert kinds.count("embed") == n_steps
+        assert len(gemms) == 4 * n_tl + 1 + n_steps * (4 * p.layers + 1)
+        for name, kind, li, _ in rec:
+            assert name.startswith("k_" + ("gemm" if kind == "gemm" else kind))
+        # one QKV GEMM per layer with the fused [q; k; v] shape, rows = sessions
+        # (predictor step 1 carries two positions per session)
+        qkv_n = lambda d: (d.n_q + 2 * d.n_kv) * d.head_dim
+        for li in gemms:
+            if li.n == qkv_n(t) and li.k == t.hidden and li.step == 0:
+                assert li.m == w.batch
+            if li.n == qkv_n(p) and li.k == p.hidden:
+                assert li.m == (2 if li.step == 1 else 1) * w.batch
+        heads = [li for li in gemms if li.n_logits]
+        assert len(heads) == (1 if mode == "full" else 0) + n_steps
+        assert all(li.n_logits == S.code_vocab for li in heads if li.step > 0)
 
 
 def test_page_permutation_invariance(small_pm):
