@@ -239,13 +239,17 @@ qt_status check_cfg(const qt_model_cfg* c) {
 // ------------------------------------------------------------------ workspace layout
 struct Ws {
   size_t x_t, x_p, ss_t, ss_p, ut, ut_lo, up, up_lo, qkv, o, o_lo, ffn, ffn_lo, pk, pv, part, cnt,
-      keys, total;
+      cand, total;
   int qkv_ld, o_ld, f_ld;
+  int cand_ld;        // greedy-key candidates per (codebook, session)
   long long pk_sess;  // elements per session in the predictor cache
 };
 
-// Residual rows carry sums of squares per producing row block; a GEMM row block
-// is at least 4 rows, so hidden/4 slots per row always suffice.
+int key_blocks(int range) { return (range + kKeyBlock - 1) / kKeyBlock; }
+
+// Residual rows carry sums of squares per producing 16-row block, so hidden/16
+// slots per row.  Activation buffers are chunked [cols/8][rows][8] with rows = B
+// (Talker) or 2B (predictor, whose step 1 carries two positions per session).
 Ws make_ws(const qt_model_cfg& c, int B, int max_pages) {
   const qt_decoder_cfg &t = c.talker, &p = c.predictor;
   Ws w{};
@@ -264,8 +268,8 @@ Ws make_ws(const qt_model_cfg& c, int B, int max_pages) {
   w.f_ld = t.ffn > p.ffn ? t.ffn : p.ffn;
   w.x_t = take((size_t)B * t.hidden * 4);
   w.x_p = take((size_t)M * p.hidden * 4);
-  w.ss_t = take((size_t)(t.hidden / 4) * B * 4);
-  w.ss_p = take((size_t)(p.hidden / 4) * M * 4);
+  w.ss_t = take((size_t)(t.hidden / kGemmRows) * B * 4);
+  w.ss_p = take((size_t)(p.hidden / kGemmRows) * M * 4);
   w.ut = take((size_t)B * t.hidden * 2);
   w.ut_lo = take((size_t)B * t.hidden * 2);
   w.up = take((size_t)M * p.hidden * 2);
@@ -280,7 +284,9 @@ Ws make_ws(const qt_model_cfg& c, int B, int max_pages) {
   w.pv = take((size_t)B * w.pk_sess * 2);
   w.part = take((size_t)B * t.n_q_heads * (size_t)max_pages * (kHeadDim + 2) * 4);
   w.cnt = take((size_t)B * t.n_kv_heads * 4);
-  w.keys = take((size_t)B * c.n_codebooks * 8);
+  w.cand_ld = key_blocks(c.cb0_range) > key_blocks(c.code_vocab) ? key_blocks(c.cb0_range)
+                                                                  : key_blocks(c.code_vocab);
+  w.cand = take((size_t)c.n_codebooks * B * w.cand_ld * 8);
   w.total = off;
   return w;
 }
@@ -411,7 +417,9 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
   uint16_t* o_lo = (uint16_t*)(ws + w.o_lo);
   uint16_t* ffn = (uint16_t*)(ws + w.ffn);
   uint16_t* ffn_lo = (uint16_t*)(ws + w.ffn_lo);
-  unsigned long long* keys = (unsigned long long*)(ws + w.keys);
+  unsigned long long* cand = (unsigned long long*)(ws + w.cand);
+  const int cand_ld = w.cand_ld;
+  const int ld_t = B, ld_p = 2 * B;  // rows of the chunked activation buffers
   unsigned* cnt = (unsigned*)(ws + w.cnt);
   const int capacity = max_pages * kPage;
 
@@ -470,7 +478,9 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
   fb.gain = vp(m, m->plan.tl[0].in_norm);
   fb.u_hi = ut;
   fb.u_lo = ut_lo;
-  fb.keys = keys;
+  fb.h_in = (const uint16_t*)in->h_in;
+  fb.cand = cand;
+  fb.cand_ld = cand_ld;
   fb.counters = cnt;
   fb.status = out->status;
   QT_MARK(QT_KERNEL_FRAME_BEGIN, "k_frame_begin", B, nullptr);
@@ -496,44 +506,43 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
   };
 
   // One decoder layer over M rows of residual x (row stride = hidden).  u / u_lo:
-  // the normalised-input buffer of the stack; ss / ss_ld: sums of squares of x;
-  // *slots: how many slots the last producer of x left; next_gain: gain of the
-  // norm that follows the layer.
+  // the normalised-input buffer of the stack; ld: rows of the stack's chunked
+  // activation buffers; ss / ss_ld: sums of squares of x; *slots: how many slots
+  // the last producer of x left; next_gain: gain of the norm that follows the layer.
   auto layer = [&](const qt_decoder_cfg& d, const LayerSlots& L, float* x, uint16_t* u,
-                   uint16_t* u_lo, float* ss, int ss_ld, int* slots, const uint16_t* next_gain,
-                   int M, auto&& attention) -> qt_status {
+                   uint16_t* u_lo, int ld, float* ss, int ss_ld, int* slots,
+                   const uint16_t* next_gain, int M, auto&& attention) -> qt_status {
     qt_status r;
-    GemmArgs g = gemm_norm(m, L.qkv, u, u_lo, d.hidden, ss, ss_ld, *slots, d.rms_eps, M,
-                           out->status);
+    GemmArgs g = gemm_norm(m, L.qkv, u, u_lo, ld, ss, ss_ld, *slots, d.rms_eps, M, out->status);
     g.epi = EPI_STORE;
     g.out_f32 = qkv;
     g.out_ld = w.qkv_ld;
     if ((r = run(g))) return r;
     if ((r = attention())) return r;
-    g = gemm_act(m, L.o, o, o_lo, w.o_ld, M, out->status);
+    g = gemm_act(m, L.o, o, o_lo, ld, M, out->status);
     g.epi = EPI_RESID;
     g.out_f32 = x;
     g.out_ld = d.hidden;
-    *slots = d.hidden / produce(g, vp(m, L.post_norm), u, u_lo, d.hidden, ss, ss_ld);
+    *slots = d.hidden / produce(g, vp(m, L.post_norm), u, u_lo, ld, ss, ss_ld);
     if ((r = run(g))) return r;
-    g = gemm_norm(m, L.gu, u, u_lo, d.hidden, ss, ss_ld, *slots, d.rms_eps, M, out->status);
+    g = gemm_norm(m, L.gu, u, u_lo, ld, ss, ss_ld, *slots, d.rms_eps, M, out->status);
     g.epi = EPI_SWIGLU;
-    g.out_bf16 = ffn;
-    g.out_bf16_lo = ffn_lo;
-    g.out_ld = w.f_ld;
+    g.u_hi = ffn;
+    g.u_lo = ffn_lo;
+    g.u_ld = ld;
     if ((r = run(g))) return r;
-    g = gemm_act(m, L.down, ffn, ffn_lo, w.f_ld, M, out->status);
+    g = gemm_act(m, L.down, ffn, ffn_lo, ld, M, out->status);
     g.epi = EPI_RESID;
     g.out_f32 = x;
     g.out_ld = d.hidden;
-    *slots = d.hidden / produce(g, next_gain, u, u_lo, d.hidden, ss, ss_ld);
+    *slots = d.hidden / produce(g, next_gain, u, u_lo, ld, ss, ss_ld);
     return run(g);
   };
   int t_slots = 1, p_slots = 1;
   const int ss_t_ld = B, ss_p_ld = 2 * B;
 
-  GemmArgs head = gemm_act(m, m->plan.t_head, (const uint16_t*)in->h_in, nullptr, T.hidden, B,
-                           out->status);
+  // predictor mode: the entry kernel copies h_in into ut (no lo part, no norm)
+  GemmArgs head = gemm_act(m, m->plan.t_head, ut, nullptr, ld_t, B, out->status);
 
   if (talker) {
     const int pps_raw = (B * T.n_kv_heads * max_pages + 2047) / 2048;
@@ -545,7 +554,7 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
       const LayerSlots& L = m->plan.tl[l];
       const uint16_t* next_gain =
           vp(m, l + 1 < T.layers ? m->plan.tl[l + 1].in_norm : m->plan.t_final);
-      qt_status s = layer(T, L, x_t, ut, ut_lo, ss_t, ss_t_ld, &t_slots, next_gain, B,
+      qt_status s = layer(T, L, x_t, ut, ut_lo, ld_t, ss_t, ss_t_ld, &t_slots, next_gain, B,
                           [&]() -> qt_status {
         AttnPagedArgs a{};
         a.qkv = qkv;
@@ -567,7 +576,7 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
         a.counters = cnt;
         a.o = o;
         a.o_lo = o_lo;
-        a.o_ld = w.o_ld;
+        a.o_ld = ld_t;
         a.status = out->status;
         QT_MARK(QT_KERNEL_ATTN_PAGED, "k_attn_paged", B, nullptr);
         QT_LAUNCH(launch_attn_paged(a, B, T.rope_theta, st));
@@ -576,7 +585,7 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
       if (s) return s;
     }
     cur_layer = -1;
-    head = gemm_norm(m, m->plan.t_head, ut, ut_lo, T.hidden, ss_t, ss_t_ld, t_slots, T.rms_eps, B,
+    head = gemm_norm(m, m->plan.t_head, ut, ut_lo, ld_t, ss_t, ss_t_ld, t_slots, T.rms_eps, B,
                      out->status);
     head.nrows = mode == QT_MODE_TALKER ? c.talker_vocab : c.talker_vocab + Pd.hidden;
   } else {
@@ -589,12 +598,12 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
   head.logits_ld = c.talker_vocab;
   head.n_logits = c.talker_vocab;
   head.argmax_range = c.cb0_range;
-  head.keys = keys;
-  head.keys_ld = ncb;
+  head.cand = cand;  // codebook 0: [B][cand_ld]
+  head.cand_ld = cand_ld;
   head.out_f32 = x_p;  // projection rows land in predictor rows [0, B)
   head.out_ld = Pd.hidden;
   if (mode != QT_MODE_TALKER)
-    p_slots = Pd.hidden / produce(head, vp(m, m->plan.pl[0].in_norm), up, up_lo, Pd.hidden, ss_p,
+    p_slots = Pd.hidden / produce(head, vp(m, m->plan.pl[0].in_norm), up, up_lo, ld_p, ss_p,
                                   ss_p_ld);
   {
     qt_status s = run(head);
@@ -613,7 +622,9 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
       e.step = k;
       e.eps = Pd.rms_eps;
       e.table = vp(m, m->plan.embeds[k - 1]);
-      e.keys = keys;
+      e.cand = cand;
+      e.cand_ld = cand_ld;
+      e.n_cand = key_blocks(k == 1 ? c.cb0_range : c.code_vocab);
       e.forced = in->forced;
       e.x = x_p;
       e.ss = ss_p;
@@ -623,6 +634,7 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
       e.gain = vp(m, m->plan.pl[0].in_norm);
       e.u_hi = up;
       e.u_lo = up_lo;
+      e.u_ld = ld_p;
       e.row_off = emb_row;
       e.status = out->status;
       cur_step = k;
@@ -634,7 +646,7 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
         const LayerSlots& L = m->plan.pl[l];
         const uint16_t* next_gain =
             vp(m, l + 1 < Pd.layers ? m->plan.pl[l + 1].in_norm : m->plan.p_final);
-        qt_status s = layer(Pd, L, x_p, up, up_lo, ss_p, ss_p_ld, &p_slots, next_gain, M,
+        qt_status s = layer(Pd, L, x_p, up, up_lo, ld_p, ss_p, ss_p_ld, &p_slots, next_gain, M,
                             [&]() -> qt_status {
           AttnPredArgs a{};
           a.qkv = qkv;
@@ -653,7 +665,7 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
           a.n_new = (k == 1) ? 2 : 1;
           a.o = o;
           a.o_lo = o_lo;
-          a.o_ld = w.o_ld;
+          a.o_ld = ld_p;
           QT_MARK(QT_KERNEL_ATTN_PRED, "k_attn_pred", B, nullptr);
           QT_LAUNCH(launch_attn_pred(a, Pd.rope_theta, st));
           return ok();
@@ -661,16 +673,17 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
         if (s) return s;
       }
       cur_layer = -1;
-      GemmArgs g = gemm_norm(m, m->plan.heads[k - 1], up + (size_t)emb_row * Pd.hidden,
-                             up_lo + (size_t)emb_row * Pd.hidden, Pd.hidden, ss_p + emb_row, ss_p_ld,
-                             p_slots, Pd.rms_eps, B, out->status);
+      // the step's head reads the last position: rows [emb_row, emb_row + B)
+      GemmArgs g = gemm_norm(m, m->plan.heads[k - 1], up + (size_t)emb_row * 8,
+                             up_lo + (size_t)emb_row * 8, ld_p, ss_p + emb_row, ss_p_ld, p_slots,
+                             Pd.rms_eps, B, out->status);
       g.epi = EPI_HEAD;
       g.logits = out->logits_pred + (size_t)(k - 1) * c.code_vocab;
       g.logits_ld = (ncb - 1) * c.code_vocab;
       g.n_logits = c.code_vocab;
       g.argmax_range = c.code_vocab;
-      g.keys = keys + k;
-      g.keys_ld = ncb;
+      g.cand = cand + (size_t)k * B * cand_ld;
+      g.cand_ld = cand_ld;
       qt_status s = run(g);
       if (s) return s;
     }
@@ -681,7 +694,10 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
   fe.B = B;
   fe.ncb = ncb;
   fe.capacity = capacity;
-  fe.keys = keys;
+  fe.cand = cand;
+  fe.cand_ld = cand_ld;
+  fe.n_cand0 = key_blocks(c.cb0_range);
+  fe.n_cand = key_blocks(c.code_vocab);
   fe.tokens = out->tokens;
   fe.kv_len = ss->kv_len;
   cur_step = 0;
@@ -800,14 +816,12 @@ qt_status qt_load_weights(const qt_model_cfg* cfg, const qt_tensor* tensors, int
       e = hipMemcpyAsync(m->base + d.vec_off, t.data, (size_t)t.rows * t.cols * 2,
                          hipMemcpyDeviceToDevice, s);
     } else if (!i8) {
-      const size_t rowb = (size_t)d.cols * 2;
-      e = hipMemcpy2DAsync(m->base + d.mat->w + (size_t)d.row0 * rowb, rowb * d.step, t.data, rowb,
-                           rowb, (size_t)d.rows, hipMemcpyDeviceToDevice, s);
+      e = launch_pack_tiled((const uint16_t*)t.data, (int)d.rows, (int)d.cols,
+                            (uint16_t*)(m->base + d.mat->w), d.row0, d.step, s);
     } else {
-      int8_t* q = (int8_t*)(m->base + d.mat->w) + (size_t)d.row0 * d.cols;
       float* sc = (float*)(m->base + d.mat->s) + d.row0;
-      e = launch_quantize((const uint16_t*)t.data, d.rows, d.cols, q, (long long)d.cols * d.step, sc,
-                          d.step, s);
+      e = launch_quantize((const uint16_t*)t.data, d.rows, d.cols, (int8_t*)(m->base + d.mat->w),
+                          d.step, sc, d.step, (int)d.cols, d.row0, s);
     }
     if (e != hipSuccess) {
       delete m;
@@ -823,7 +837,8 @@ qt_status qt_quantize_int8(const void* w_bf16, int64_t rows, int64_t cols, int8_
   if (!w_bf16 || !q || !scale) return fail(QT_E_INVALID_ARG, "a pointer is NULL");
   if (rows < 1 || cols < 1) return fail(QT_E_INVALID_ARG, "rows and cols must be >= 1");
   if (rows > 0x7fffffffLL) return fail(QT_E_SHAPE, "rows = %lld: at most 2^31-1", (long long)rows);
-  QT_HIP(launch_quantize((const uint16_t*)w_bf16, rows, cols, q, cols, scale, 1, (hipStream_t)stream));
+  QT_HIP(launch_quantize((const uint16_t*)w_bf16, rows, cols, q, cols, scale, 1, 0, 0,
+                         (hipStream_t)stream));
   return ok();
 }
 
@@ -836,9 +851,8 @@ qt_status qt_model_export_int8(const qt_model* m, const char* name, int8_t* q, f
     return fail(QT_E_INVALID_ARG, "'%s' is not a decode GEMM weight", name);
   const Dest& d = it->second;
   hipStream_t s = (hipStream_t)stream;
-  QT_HIP(hipMemcpy2DAsync(q, (size_t)d.cols, m->base + d.mat->w + (size_t)d.row0 * d.cols,
-                          (size_t)d.cols * d.step, (size_t)d.cols, (size_t)d.rows,
-                          hipMemcpyDeviceToDevice, s));
+  QT_HIP(launch_untile_i8((const int8_t*)(m->base + d.mat->w), (int)d.rows, (int)d.cols, d.row0,
+                          d.step, q, s));
   QT_HIP(hipMemcpy2DAsync(scale, 4, m->base + d.mat->s + (size_t)d.row0 * 4, (size_t)4 * d.step, 4,
                           (size_t)d.rows, hipMemcpyDeviceToDevice, s));
   return ok();

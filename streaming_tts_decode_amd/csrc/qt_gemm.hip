@@ -2,24 +2,31 @@
 //   y[m][n] = sum_k W[n][k] * act[m][k]   (times scale[n] for INT8 weights)
 // for M = 1..64 activation rows (sessions, or 2 x sessions at predictor step 1).
 //
-// Every weight byte is read once per call for all M rows, and a block issues all
-// of its weight and activation loads of a step group before any arithmetic, so
-// a call costs about one memory round trip (these GEMMs are latency-bound at small
-// batch).  No block waits on another block.
-//  * VALU (M <= 2): a 4-wave block owns 4 weight rows, one per wave; lanes walk K
-//    in 16-byte chunks (one wave load = 1 KB of a row); v_dot2_f32_bf16.
-//  * MFMA (M >= 3): v_mfma_f32_16x16x32_bf16 with weight rows as the A operand.
-//    An 8-wave block owns 16 weight rows; wave w takes the 128-wide K steps
-//    w, w+8, ... two at a time, and the waves' 16x16 accumulator tiles are summed
-//    in a fixed order through LDS.  Within a step, lane (i, q) (i = lane & 15,
-//    q = lane >> 4) feeds row i with elements [32s + 8q, +8) to the s-th MFMA, so
-//    the four lanes of a row read 64 contiguous bytes per load instruction; the
-//    activation operand uses the same mapping.
+// Every weight byte is read once per call for all M rows.  A block owns 16
+// weight rows over the whole of K; its waves take the K steps round-robin
+// (wave w: steps w, w+NW, ...), G steps per load group, and issue all loads of a
+// group before any arithmetic.  The waves' partial sums are added in a fixed
+// order through LDS, so results do not depend on timing, and no block waits on
+// another block.
 //
-// Activations are a bf16 hi/lo pair (hi + lo carries ~16 bits of the fp32 value).
-// RMSNorm is split between producer and consumer: the GEMM (or kernel) that
-// writes a residual row v also writes hi/lo(v * gain) and the row block's sum of
-// squares; the consuming GEMM multiplies its outputs by 1/rms from those sums.
+// Memory layouts (see qt_internal.h) make every load a contiguous piece:
+//  * weights are packed in 1 KB tiles holding exactly the 16x32 A operand of a
+//    v_mfma_f32_16x16x32_bf16 (bf16) or of two of them (int8), so one wave load
+//    instruction reads 1 KB of contiguous memory;
+//  * activations are "chunked", [K/8][rows][8], so the 16 rows of an 8-wide K
+//    chunk that one MFMA B operand needs are 256 contiguous bytes.
+// Lane (i, q) (i = lane & 15, q = lane >> 4) holds weight row i, K elements
+// [8q, 8q+8) of each 32-wide step.
+//  * MFMA form (M >= 3): the activation rows are the 16-column B operand tiles.
+//  * VALU form (M <= 2): each lane forms v_dot2_f32_bf16 products of its weight
+//    piece with the (broadcast) activation piece of the same K range; the four
+//    lanes of a row are summed with cross-lane adds.
+//
+// Activations are a bf16 hi/lo pair (hi + lo carries ~16 bits of the fp32 value),
+// each multiplied by the weights.  RMSNorm is split between producer and consumer:
+// the GEMM (or kernel) that writes a residual row v also writes hi/lo(v * gain)
+// and the 16-row block's sum of squares; the consuming GEMM multiplies its
+// outputs by 1/rms from those sums.
 #include <stdio.h>
 
 #include "qt_device.h"
@@ -69,16 +76,30 @@ __device__ __forceinline__ void ss_finish(const GemmArgs& a, int first, int step
   }
 }
 
-// Epilogue over the final tile: tile[r * tld + m] is row n0 + r, activation row m
-// (before the INT8 scale and the RMSNorm factor).
-__device__ void gemm_epilogue(const GemmArgs& a, int rpb, int n0, float* tile, int tld,
+// Eight values to chunked hi/lo bf16 pieces (16 bytes each).
+__device__ __forceinline__ void split8(const float (&v)[8], uint4& hi, uint4& lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint16_t h0 = f2bf(v[2 * p]), h1 = f2bf(v[2 * p + 1]);
+    const uint16_t l0 = f2bf(v[2 * p] - bf2f(h0)), l1 = f2bf(v[2 * p + 1] - bf2f(h1));
+    h[p] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+    l[p] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+  }
+  hi = make_uint4(h[0], h[1], h[2], h[3]);
+  lo = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
+// Epilogue over the block's tile: tile[r * tld + m] is weight row n0 + r (r < 16),
+// activation row m, before the INT8 scale and the RMSNorm factor.
+__device__ void gemm_epilogue(const GemmArgs& a, int n0, float* tile, int tld,
                               const float* s_inv) {
+  constexpr int R = kGemmRows;
   const int M = a.M;
   const int tid = threadIdx.x, nthr = blockDim.x;
-  const int lane = tid & 63, wave = tid >> 6, nw = nthr >> 6;
   if (a.scale || a.ss_in) {
-    for (int e = tid; e < rpb * M; e += nthr) {
-      const int r = e / M, m = e - r * M;
+    for (int e = tid; e < R * M; e += nthr) {
+      const int m = e >> 4, r = e & 15;
       float y = tile[r * tld + m];
       if (a.scale) y *= a.scale[n0 + r];
       if (a.ss_in) y *= s_inv[m];
@@ -86,333 +107,307 @@ __device__ void gemm_epilogue(const GemmArgs& a, int rpb, int n0, float* tile, i
     }
     __syncthreads();
   }
-  if (a.epi == EPI_SWIGLU) {
-    for (int e = tid; e < (rpb >> 1) * M; e += nthr) {
-      const int pr = e / M, m = e - pr * M;
-      const int n = n0 + 2 * pr;
-      const float g = tile[(2 * pr) * tld + m], u = tile[(2 * pr + 1) * tld + m];
-      split_bf16(silu(g) * u, a.out_bf16, a.out_bf16_lo, (size_t)m * a.out_ld + (n >> 1));
+  if (a.epi == EPI_STORE) {
+    for (int e = tid; e < R * M; e += nthr) {
+      const int m = e >> 4, r = e & 15;
+      a.out_f32[(size_t)m * a.out_ld + n0 + r] = tile[r * tld + m];
     }
     return;
   }
-  // first output row of residual / projection values (-1: none in this GEMM)
-  const int base = a.epi == EPI_RESID ? 0 : (a.epi == EPI_HEAD ? a.n_logits : -1);
-  for (int e = tid; e < rpb * M; e += nthr) {
-    const int r = e / M, m = e - r * M;
-    const int n = n0 + r;
+  if (a.epi == EPI_SWIGLU) {
+    // rows 2p (gate) and 2p+1 (up) -> output column n0/2 + p: one 8-wide chunk per m
+    for (int m = tid; m < M; m += nthr) {
+      float v[8];
+#pragma unroll
+      for (int p = 0; p < 8; ++p) v[p] = silu(tile[(2 * p) * tld + m]) * tile[(2 * p + 1) * tld + m];
+      uint4 hi, lo;
+      split8(v, hi, lo);
+      const size_t o = chunked(m, n0 >> 1, a.u_ld);
+      *reinterpret_cast<uint4*>(a.u_hi + o) = hi;
+      *reinterpret_cast<uint4*>(a.u_lo + o) = lo;
+    }
+    return;
+  }
+  if (a.epi == EPI_HEAD && n0 < a.n_logits) {
+    for (int e = tid; e < R * M; e += nthr) {
+      const int m = e >> 4, r = e & 15;
+      a.logits[(size_t)m * a.logits_ld + n0 + r] = tile[r * tld + m];
+    }
+    if (n0 < a.argmax_range) {
+      // greedy-key candidate of these 16 rows (lowest index wins ties; NaN flagged)
+      for (int m = tid; m < M; m += nthr) {
+        unsigned long long best = 0;
+        bool nan = false;
+        for (int r = 0; r < R && n0 + r < a.argmax_range; ++r) {
+          const float y = tile[r * tld + m];
+          if (y != y) {
+            nan = true;
+            continue;
+          }
+          const unsigned long long k = greedy_key(y, n0 + r);
+          best = k > best ? k : best;
+        }
+        a.cand[(size_t)m * a.cand_ld + n0 / kKeyBlock] = best;
+        if (nan) atomicOr(a.status, QT_STATUS_NAN);
+      }
+    }
+    return;
+  }
+  // residual rows (EPI_RESID: x += y) or projection rows (EPI_HEAD: x = y)
+  const int base = a.epi == EPI_RESID ? 0 : a.n_logits;
+  const int c0 = n0 - base;
+  for (int e = tid; e < R * M; e += nthr) {
+    const int m = e >> 4, r = e & 15;
+    float* p = a.out_f32 + (size_t)m * a.out_ld + c0 + r;
     float v = tile[r * tld + m];
-    if (a.epi == EPI_STORE) {
-      a.out_f32[(size_t)m * a.out_ld + n] = v;
-      continue;
-    }
-    if (a.epi == EPI_RESID) {
-      float* p = a.out_f32 + (size_t)m * a.out_ld + n;
-      v += *p;
-      *p = v;
-    } else if (n < a.n_logits) {  // EPI_HEAD logits
-      a.logits[(size_t)m * a.logits_ld + n] = v;
-      continue;
-    } else {  // EPI_HEAD projection rows
-      a.out_f32[(size_t)m * a.out_ld + (n - a.n_logits)] = v;
-    }
+    if (a.epi == EPI_RESID) v += *p;
+    *p = v;
     tile[r * tld + m] = v;
-    if (a.u_gain) {
-      const int c = n - base;
-      split_bf16(v * bf2f(a.u_gain[c]), a.u_hi, a.u_lo, (size_t)m * a.u_ld + c);
-    }
   }
-  if (a.epi == EPI_HEAD && n0 < a.argmax_range) {
-    for (int m = wave; m < M; m += nw) {
-      unsigned long long best = 0;
-      bool nan = false;
-      for (int r = lane; r < rpb; r += 64) {
-        const int n = n0 + r;
-        if (n >= a.argmax_range) break;
-        const float y = tile[r * tld + m];
-        if (y != y) {
-          nan = true;
-          continue;
-        }
-        const unsigned long long k = greedy_key(y, n);
-        best = k > best ? k : best;
-      }
-      best = wave_max_u64(best);
-      if (nan) atomicOr(a.status, QT_STATUS_NAN);
-      if (lane == 0 && best) atomicMax(&a.keys[(size_t)m * a.keys_ld], best);
-    }
-  }
-  if (!a.ss_out || base < 0 || n0 < base) return;
-  const int slot = (n0 - base) / rpb;
+  if (!a.u_gain) return;
   __syncthreads();
-  for (int m = wave; m < M; m += nw) {
+  // the next norm's input (two 8-wide chunks) and this block's sum of squares
+  for (int m = tid; m < M; m += nthr) {
     float ss = 0.f;
-    for (int r = lane; r < rpb; r += 64) {
-      const float v = tile[r * tld + m];
-      ss = fmaf(v, v, ss);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float x = tile[(8 * h + j) * tld + m];
+        ss = fmaf(x, x, ss);
+        v[j] = x * bf2f(a.u_gain[c0 + 8 * h + j]);
+      }
+      uint4 hi, lo;
+      split8(v, hi, lo);
+      const size_t o = chunked(m, c0 + 8 * h, a.u_ld);
+      *reinterpret_cast<uint4*>(a.u_hi + o) = hi;
+      *reinterpret_cast<uint4*>(a.u_lo + o) = lo;
     }
-    ss = wave_sum(ss);
-    if (lane == 0) a.ss_out[(size_t)slot * a.ss_out_ld + m] = ss;
+    a.ss_out[(size_t)(c0 / R) * a.ss_out_ld + m] = ss;
   }
 }
 
-// ------------------------------------------------------------------ VALU path
-// Block = 4 waves, one weight row each; lane l loads chunks l, l+64, ... (NI per
-// lane) of the row and of every activation row before any arithmetic.
-template <int MP, int NI, bool I8>
-__global__ __launch_bounds__(256) void k_gemm_valu(GemmArgs a) {
-  constexpr int EPC = I8 ? 16 : 8;  // weight elements per 16-byte chunk
-  constexpr int G = EPC / 8;        // 8-element activation groups per chunk
-  __shared__ float tile[4 * MP];
-  __shared__ float s_inv[MP];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n0 = a.row0 + blockIdx.x * 4;
-  const int n = n0 + wave;
-  const int M = a.M;
-  const int KC = a.K / EPC;
-  const uint4* W = reinterpret_cast<const uint4*>(a.W);
-
-  float ssr[kSsRegs];
-  int ss_per_lane = 0;
-  if (a.ss_in && wave < MP) ss_prefetch(a, wave, 4, ssr, ss_per_lane);
-
-  uint4 w[NI];
-  uint4 xh[NI][G][MP], xl[NI][G][MP];
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int c = lane + 64 * i;
-    w[i] = c < KC ? W[(size_t)n * KC + c] : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const int k = c * EPC + 8 * g;
-#pragma unroll
-      for (int b = 0; b < MP; ++b) {
-        xh[i][g][b] = xl[i][g][b] = make_uint4(0, 0, 0, 0);
-        if (c < KC && b < M) {
-          xh[i][g][b] = *reinterpret_cast<const uint4*>(a.act + (size_t)b * a.act_ld + k);
-          if (a.act_lo) xl[i][g][b] = *reinterpret_cast<const uint4*>(a.act_lo + (size_t)b * a.act_ld + k);
-        }
-      }
-    }
-  }
-
-  float acc[MP];
-#pragma unroll
-  for (int b = 0; b < MP; ++b) acc[b] = 0.f;
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    if (!I8) {
-#pragma unroll
-      for (int b = 0; b < MP; ++b) acc[b] = dot8(w[i], xl[i][0][b], dot8(w[i], xh[i][0][b], acc[b]));
-    } else {
-      uint4 wa, wb;
-      wa.x = i8pair_to_bf16x2(w[i].x, 0);
-      wa.y = i8pair_to_bf16x2(w[i].x, 1);
-      wa.z = i8pair_to_bf16x2(w[i].y, 0);
-      wa.w = i8pair_to_bf16x2(w[i].y, 1);
-      wb.x = i8pair_to_bf16x2(w[i].z, 0);
-      wb.y = i8pair_to_bf16x2(w[i].z, 1);
-      wb.z = i8pair_to_bf16x2(w[i].w, 0);
-      wb.w = i8pair_to_bf16x2(w[i].w, 1);
-#pragma unroll
-      for (int b = 0; b < MP; ++b) {
-        float t = dot8(wa, xh[i][0][b], acc[b]);
-        t = dot8(wa, xl[i][0][b], t);
-        t = dot8(wb, xh[i][G - 1][b], t);
-        acc[b] = dot8(wb, xl[i][G - 1][b], t);
-      }
-    }
-  }
-  constexpr int P = Log2<MP>::value;
-  const float tot = transpose_reduce<MP>(acc, lane);
-  if ((lane & ((64 >> P) - 1)) == 0) tile[wave * MP + (lane >> (6 - P))] = tot;
-  if (a.ss_in && wave < MP) ss_finish(a, wave, 4, ssr, ss_per_lane, s_inv);
-  __syncthreads();
-  gemm_epilogue(a, 4, n0, tile, MP, s_inv);
+// Eight int8 weights (bytes 8*sb .. 8*sb+7 of w) as a bf16x8 operand (exact).
+__device__ __forceinline__ uint4 i8_to_bf16x8(const uint4& w, int sb) {
+  const uint32_t a = sb ? w.z : w.x, b = sb ? w.w : w.y;
+  return make_uint4(i8pair_to_bf16x2(a, 0), i8pair_to_bf16x2(a, 1), i8pair_to_bf16x2(b, 0),
+                    i8pair_to_bf16x2(b, 1));
 }
 
-// ------------------------------------------------------------------ MFMA path
-constexpr int kMfmaWaves = 8;
-
-template <int MT, int SPW, bool I8>
-__global__ __launch_bounds__(512) void k_gemm_mfma(GemmArgs a) {
-  constexpr int TLD = 64;  // tile columns (activation rows)
-  constexpr int NW = kMfmaWaves;
-  __shared__ float red[NW][16 * TLD];
-  __shared__ float tile[16 * TLD];
+// One block: weight rows [n0, n0+16) over all of K.  NW waves, MT 16-row MFMA
+// activation tiles (MT == 0: VALU form for M <= 2), G K steps per load group.
+template <int NW, int MT, int G, bool I8>
+__global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs a) {
+  constexpr int TLD = MT ? 16 * MT : 2;  // tile columns (activation rows)
+  constexpr int SUB = I8 ? 2 : 1;        // 32-wide MFMA K substeps per packed K step
+  constexpr int MV = MT ? 16 * MT : 2;   // activation rows held per lane group
+  __shared__ float red[NW][kGemmRows * TLD];
   __shared__ float s_inv[64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i = lane & 15, q = lane >> 4;
-  const int n0 = a.row0 + blockIdx.x * 16;
-  const int n = n0 + i;
-  const int M = a.M;
-  const int nsteps = a.K / 128;
+  const int rt = (a.row0 >> 4) + blockIdx.x;
+  const int n0 = rt * kGemmRows;
+  const int M = a.M, ld = a.act_ld;
+  const int ksteps = a.K / (32 * SUB);
+  const uint4* W = reinterpret_cast<const uint4*>(a.W) + (size_t)rt * ksteps * 64 + lane;
+  const uint4* H = reinterpret_cast<const uint4*>(a.act);
+  const uint4* L = reinterpret_cast<const uint4*>(a.act_lo);
+  const bool has_lo = a.act_lo != nullptr;
 
   float ssr[kSsRegs];
   int ss_per_lane = 0;
   if (a.ss_in) ss_prefetch(a, wave, NW, ssr, ss_per_lane);
 
-  const int passes = (M + 16 * MT - 1) / (16 * MT);
-  for (int pass = 0; pass < passes; ++pass) {
+  // activation row m of chunk c: 16 bytes at H[c * ld + m]
+  if constexpr (MT > 0) {
     f32x4 acc[MT];
 #pragma unroll
     for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int st0 = wave; st0 < nsteps; st0 += NW * SPW) {
-      // ---- issue every load of this group of steps
-      uint4 wr[SPW][4];
-      uint4 bh[SPW][MT][4], bl[SPW][MT][4];
+    for (int j0 = wave; j0 < ksteps; j0 += NW * G) {
+      uint4 w[G], h[G][SUB][MT], l[G][SUB][MT];
 #pragma unroll
-      for (int j = 0; j < SPW; ++j) {
-        const int st = st0 + NW * j;
-        const bool ok = st < nsteps;
-        const int kb = st * 128 + 8 * q;  // piece s of this lane: [kb + 32 s, +8)
-        if (!I8) {
-          const uint16_t* p = reinterpret_cast<const uint16_t*>(a.W) + (size_t)n * a.K + kb;
+      for (int g = 0; g < G; ++g) {
+        const int j = j0 + NW * g;
+        const bool ok = j < ksteps;
+        w[g] = ok ? W[(size_t)j * 64] : make_uint4(0, 0, 0, 0);
 #pragma unroll
-          for (int s = 0; s < 4; ++s)
-            wr[j][s] = ok ? *reinterpret_cast<const uint4*>(p + 32 * s) : make_uint4(0, 0, 0, 0);
-        } else {
-          const int8_t* p = reinterpret_cast<const int8_t*>(a.W) + (size_t)n * a.K + kb;
+        for (int sb = 0; sb < SUB; ++sb) {
+          const size_t c = (size_t)(j * SUB + sb) * 4 + q;
 #pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            const uint2 v = ok ? *reinterpret_cast<const uint2*>(p + 32 * s) : make_uint2(0, 0);
-            wr[j][s] = make_uint4(v.x, v.y, 0, 0);
-          }
-        }
-#pragma unroll
-        for (int t = 0; t < MT; ++t) {
-          const int m = (pass * MT + t) * 16 + i;
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            uint4 h = make_uint4(0, 0, 0, 0), l = make_uint4(0, 0, 0, 0);
-            if (ok && m < M) {
-              const size_t off = (size_t)m * a.act_ld + kb + 32 * s;
-              h = *reinterpret_cast<const uint4*>(a.act + off);
-              if (a.act_lo) l = *reinterpret_cast<const uint4*>(a.act_lo + off);
-            }
-            bh[j][t][s] = h;
-            bl[j][t][s] = l;
+          for (int t = 0; t < MT; ++t) {
+            const int m = 16 * t + i;
+            const bool in = ok && m < M;
+            h[g][sb][t] = in ? H[c * ld + m] : make_uint4(0, 0, 0, 0);
+            l[g][sb][t] = in && has_lo ? L[c * ld + m] : make_uint4(0, 0, 0, 0);
           }
         }
       }
-      // ---- multiply
 #pragma unroll
-      for (int j = 0; j < SPW; ++j) {
+      for (int g = 0; g < G; ++g) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          bf16x8 aop;
-          if (!I8) {
-            aop = __builtin_bit_cast(bf16x8, wr[j][s]);
-          } else {
-            uint4 c;
-            c.x = i8pair_to_bf16x2(wr[j][s].x, 0);
-            c.y = i8pair_to_bf16x2(wr[j][s].x, 1);
-            c.z = i8pair_to_bf16x2(wr[j][s].y, 0);
-            c.w = i8pair_to_bf16x2(wr[j][s].y, 1);
-            aop = __builtin_bit_cast(bf16x8, c);
-          }
+        for (int sb = 0; sb < SUB; ++sb) {
+          const bf16x8 A = __builtin_bit_cast(bf16x8, I8 ? i8_to_bf16x8(w[g], sb) : w[g]);
 #pragma unroll
           for (int t = 0; t < MT; ++t) {
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, __builtin_bit_cast(bf16x8, bh[j][t][s]), acc[t], 0, 0, 0);
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, __builtin_bit_cast(bf16x8, bl[j][t][s]), acc[t], 0, 0, 0);
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                A, __builtin_bit_cast(bf16x8, h[g][sb][t]), acc[t], 0, 0, 0);
+            if (has_lo)
+              acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  A, __builtin_bit_cast(bf16x8, l[g][sb][t]), acc[t], 0, 0, 0);
           }
         }
       }
     }
-    // D layout of a 16x16 tile: lane l, element j -> weight row 4*(l>>4)+j, activation column l&15
+    // D layout of a 16x16 tile: lane l, element e -> weight row 4*(l>>4)+e, column l&15
 #pragma unroll
     for (int t = 0; t < MT; ++t)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) red[wave][(4 * q + j) * TLD + (pass * MT + t) * 16 + i] = acc[t][j];
+      for (int e = 0; e < 4; ++e) red[wave][(4 * q + e) * TLD + 16 * t + i] = acc[t][e];
+  } else {
+    float acc[MV];
+#pragma unroll
+    for (int m = 0; m < MV; ++m) acc[m] = 0.f;
+    for (int j0 = wave; j0 < ksteps; j0 += NW * G) {
+      uint4 w[G], h[G][SUB][MV], l[G][SUB][MV];
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        const int j = j0 + NW * g;
+        const bool ok = j < ksteps;
+        w[g] = ok ? W[(size_t)j * 64] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int sb = 0; sb < SUB; ++sb) {
+          const size_t c = (size_t)(j * SUB + sb) * 4 + q;
+#pragma unroll
+          for (int m = 0; m < MV; ++m) {
+            const bool in = ok && m < M;
+            h[g][sb][m] = in ? H[c * ld + m] : make_uint4(0, 0, 0, 0);
+            l[g][sb][m] = in && has_lo ? L[c * ld + m] : make_uint4(0, 0, 0, 0);
+          }
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+#pragma unroll
+        for (int sb = 0; sb < SUB; ++sb) {
+          const uint4 A = I8 ? i8_to_bf16x8(w[g], sb) : w[g];
+#pragma unroll
+          for (int m = 0; m < MV; ++m) acc[m] = dot8(A, l[g][sb][m], dot8(A, h[g][sb][m], acc[m]));
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < MV; ++m) {
+      float v = acc[m];
+      v += __shfl_xor(v, 16);
+      v += __shfl_xor(v, 32);
+      if (q == 0) red[wave][i * TLD + m] = v;
+    }
   }
   if (a.ss_in) ss_finish(a, wave, NW, ssr, ss_per_lane, s_inv);
   __syncthreads();
-  for (int e = tid; e < 16 * M; e += NW * 64) {
-    const int r = e / M, m = e - r * M;
+  for (int e = tid; e < kGemmRows * M; e += NW * 64) {
+    const int m = e >> 4, r = e & 15;
     float s = 0.f;
 #pragma unroll
     for (int v = 0; v < NW; ++v) s += red[v][r * TLD + m];
-    tile[r * TLD + m] = s;
+    red[0][r * TLD + m] = s;
   }
   __syncthreads();
-  gemm_epilogue(a, 16, n0, tile, TLD, s_inv);
-}
-
-// NI = 16-byte chunks per lane over K (up to K = 6144: 12 bf16, 6 int8).
-template <int MP, bool I8>
-hipError_t valu_ni(const GemmArgs& a, int ni, hipStream_t s) {
-  const dim3 grid(a.nrows / 4);
-  switch (ni) {
-    case 1: launch_kernel((k_gemm_valu<MP, 1, I8>), grid, dim3(256), s, a); break;
-    case 2: launch_kernel((k_gemm_valu<MP, 2, I8>), grid, dim3(256), s, a); break;
-    case 3: launch_kernel((k_gemm_valu<MP, 3, I8>), grid, dim3(256), s, a); break;
-    case 4: launch_kernel((k_gemm_valu<MP, 4, I8>), grid, dim3(256), s, a); break;
-    default:
-      if constexpr (I8) {
-        launch_kernel((k_gemm_valu<MP, 6, I8>), grid, dim3(256), s, a);
-      } else {
-        if (ni <= 6)
-          launch_kernel((k_gemm_valu<MP, 6, I8>), grid, dim3(256), s, a);
-        else
-          launch_kernel((k_gemm_valu<MP, 12, I8>), grid, dim3(256), s, a);
-      }
-      break;
-  }
-  return hipGetLastError();
+  gemm_epilogue(a, n0, red[0], TLD, s_inv);
 }
 
 template <bool I8>
 hipError_t gemm_dispatch(const GemmArgs& a, const GemmPlan& p, hipStream_t s) {
-  if (p.mfma) {
-    const dim3 grid(a.nrows / 16), block(64 * kMfmaWaves);
-    if (p.mt == 1)
-      launch_kernel((k_gemm_mfma<1, 2, I8>), grid, block, s, a);
-    else
-      launch_kernel((k_gemm_mfma<2, 2, I8>), grid, block, s, a);
-    return hipGetLastError();
+  const dim3 grid(p.row_blocks), block(64 * p.nw);
+  switch (p.mt) {
+    case 0: launch_kernel((k_gemm<16, 0, 2, I8>), grid, block, s, a); break;
+    case 1: launch_kernel((k_gemm<8, 1, 2, I8>), grid, block, s, a); break;
+    case 2: launch_kernel((k_gemm<8, 2, 2, I8>), grid, block, s, a); break;
+    default: launch_kernel((k_gemm<8, 4, 1, I8>), grid, block, s, a); break;
   }
-  return p.mp == 1 ? valu_ni<1, I8>(a, p.ni, s) : valu_ni<2, I8>(a, p.ni, s);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ packing
+// Source rows [rows][K] bf16 -> rows row0 + r*step of a tiled [N][K] matrix.
+__global__ __launch_bounds__(256) void k_pack_tiled(const uint16_t* src, int rows, int K,
+                                                    uint16_t* dst, int row0, int step) {
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;  // one 8-wide chunk
+  const int kc = K >> 3;
+  if (e >= (long long)rows * kc) return;
+  const int r = (int)(e / kc), k = (int)(e - (long long)r * kc) << 3;
+  const uint4 v = *reinterpret_cast<const uint4*>(src + (size_t)r * K + k);
+  *reinterpret_cast<uint4*>(dst + tiled_bf16(row0 + r * step, k, K)) = v;
+}
+
+// Rows row0 + r*step of a tiled int8 [N][K] matrix -> row-major [rows][K].
+__global__ __launch_bounds__(256) void k_untile_i8(const int8_t* tiled, int rows, int K, int row0,
+                                                   int step, int8_t* out) {
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
+  const int kc = K >> 3;
+  if (e >= (long long)rows * kc) return;
+  const int r = (int)(e / kc), k = (int)(e - (long long)r * kc) << 3;
+  const uint2 v = *reinterpret_cast<const uint2*>(tiled + tiled_i8(row0 + r * step, k, K));
+  *reinterpret_cast<uint2*>(out + (size_t)r * K + k) = v;
 }
 
 }  // namespace
 
 // Launch shape for nrows weight rows, K columns, M activation rows.
 GemmPlan plan_gemm(int nrows, int K, int M, bool i8) {
+  (void)K;
+  (void)i8;
   GemmPlan p{};
-  if (M >= 3) {
-    p.mfma = true;
-    p.mt = M <= 16 ? 1 : 2;
-    p.nw = kMfmaWaves;
-    p.rows_per_block = 16;
+  if (M <= 2) {
+    p.nw = 16, p.mt = 0, p.g = 2;
+  } else if (M <= 16) {
+    p.nw = 8, p.mt = 1, p.g = 2;
+  } else if (M <= 32) {
+    p.nw = 8, p.mt = 2, p.g = 2;
   } else {
-    p.mfma = false;
-    p.mp = M == 1 ? 1 : 2;
-    p.rw = 1;
-    const int chunks = (K / (i8 ? 16 : 8) + 63) / 64;  // 16-byte chunks per lane
-    p.ni = chunks <= 4 ? chunks : (chunks <= 6 ? 6 : 12);
-    p.rows_per_block = 4;
+    p.nw = 8, p.mt = 4, p.g = 1;
   }
-  p.row_blocks = nrows / p.rows_per_block;
+  p.rows_per_block = kGemmRows;
+  p.row_blocks = nrows / kGemmRows;
   return p;
 }
 
 void gemm_kernel_name(const GemmArgs& a, char* buf, int len) {
   const bool i8 = a.scale != nullptr;
   const GemmPlan p = plan_gemm(a.nrows, a.K, a.M, i8);
-  if (p.mfma)
-    snprintf(buf, len, "k_gemm_mfma<%d,2,%s>", p.mt, i8 ? "true" : "false");
-  else
-    snprintf(buf, len, "k_gemm_valu<%d,%d,%s>", p.mp, p.ni, i8 ? "true" : "false");
+  snprintf(buf, len, "k_gemm<%d,%d,%d,%s>", p.nw, p.mt, p.g, i8 ? "true" : "false");
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
-  if (a.M < 1 || a.M > 64 || a.nrows <= 0 || (a.nrows % 64) || (a.K % 512) ||
-      (a.epi == EPI_SWIGLU && (a.row0 & 1)))
+  if (a.M < 1 || a.M > 64 || a.nrows <= 0 || (a.nrows % kGemmRows) || (a.row0 % kGemmRows) ||
+      a.row0 + a.nrows > a.N || a.K <= 0 || (a.K % 64) || a.act_ld < a.M)
     return hipErrorInvalidValue;
+  if (a.ss_in && a.ss_in_slots < 1) return hipErrorInvalidValue;
+  if (a.epi == EPI_HEAD && ((a.n_logits % kGemmRows) || (a.argmax_range > a.n_logits)))
+    return hipErrorInvalidValue;
+  if ((a.epi == EPI_RESID || a.epi == EPI_HEAD) && a.u_gain && !a.ss_out) return hipErrorInvalidValue;
   const bool i8 = a.scale != nullptr;
   const GemmPlan p = plan_gemm(a.nrows, a.K, a.M, i8);
-  if (!p.mfma && (a.K / (i8 ? 16 : 8) + 63) / 64 > (i8 ? 6 : 12)) return hipErrorInvalidValue;
-  if (a.ss_in && a.ss_in_slots < 1) return hipErrorInvalidValue;
   return i8 ? gemm_dispatch<true>(a, p, s) : gemm_dispatch<false>(a, p, s);
+}
+
+hipError_t launch_pack_tiled(const uint16_t* src, int rows, int K, uint16_t* dst, int row0,
+                             int step, hipStream_t s) {
+  if (rows <= 0 || K <= 0 || (K % 32) || row0 < 0 || step < 1) return hipErrorInvalidValue;
+  const long long n = (long long)rows * (K / 8);
+  launch_kernel(k_pack_tiled, dim3((unsigned)((n + 255) / 256)), dim3(256), s, src, rows, K, dst,
+                row0, step);
+  return hipGetLastError();
+}
+
+hipError_t launch_untile_i8(const int8_t* tiled, int rows, int K, int row0, int step, int8_t* out,
+                            hipStream_t s) {
+  if (rows <= 0 || K <= 0 || (K % 64) || row0 < 0 || step < 1) return hipErrorInvalidValue;
+  const long long n = (long long)rows * (K / 8);
+  launch_kernel(k_untile_i8, dim3((unsigned)((n + 255) / 256)), dim3(256), s, tiled, rows, K, row0,
+                step, out);
+  return hipGetLastError();
 }
 
 }  // namespace qt

@@ -17,24 +17,52 @@ constexpr int kMaxPagesPerSplit = 8;
 // and lo = bf16(x - hi), so that hi + lo keeps ~16 significant bits of the fp32
 // value; each weight operand is multiplied by both.  Weights stay bf16 / int8.
 //
+// Layouts (all chosen so that every GEMM load and store moves whole 16-byte
+// pieces of contiguous memory):
+//  * packed weights, bf16: W[n][k] of an [N][K] matrix sits in 1 KB tiles
+//    [N/16][K/32][64 lanes][8]; lane q*16+i of tile (n/16, k/32) holds
+//    W[16*(n/16)+i][32*(k/32) + 8q .. +8], the A operand of one
+//    16x16x32 MFMA.  tiled_bf16() gives the element offset.
+//  * packed weights, int8: 1 KB tiles [N/16][K/64][64][16 bytes]; lane q*16+i
+//    holds W[16*(n/16)+i][64j + 8q .. +8] in bytes 0..7 and
+//    W[..][64j + 32 + 8q .. +8] in bytes 8..15 (j = k/64).  tiled_i8().
+//  * activations ("chunked"): element (m, k) of a [rows][K] activation is at
+//    ((k/8)*ld + m)*8 + k%8, i.e. [K/8][ld][8]; ld is the buffer's row count.
+//    Sixteen consecutive rows of one 8-column chunk are 256 contiguous bytes.
+__host__ __device__ inline size_t tiled_bf16(int n, int k, int K) {
+  return ((((size_t)(n >> 4) * (K >> 5) + (k >> 5)) * 64 + ((k >> 3) & 3) * 16 + (n & 15)) << 3) +
+         (k & 7);
+}
+__host__ __device__ inline size_t tiled_i8(int n, int k, int K) {
+  return ((((size_t)(n >> 4) * (K >> 6) + (k >> 6)) * 64 + ((k >> 3) & 3) * 16 + (n & 15)) << 4) +
+         (((k >> 5) & 1) << 3) + (k & 7);
+}
+__host__ __device__ inline size_t chunked(int m, int k, int ld) {
+  return (((size_t)(k >> 3) * ld + m) << 3) + (k & 7);
+}
+
+constexpr int kGemmRows = 16;   // weight rows per GEMM block (one MFMA A tile)
+constexpr int kKeyBlock = 16;   // logits rows per greedy-key candidate
+
 // GEMM epilogues.  y[m][n] = sum_k W[n][k] * act[m][k] (times scale[n] in INT8 mode).
 enum Epi : int {
   EPI_STORE = 0,   // out_f32[m*out_ld + n] = y
   EPI_RESID = 1,   // out_f32[m*out_ld + n] += y
   EPI_SWIGLU = 2,  // rows interleaved (gate n, up n) at (2n, 2n+1):
-                   // out_bf16[m*out_ld + n] = bf16(silu(gate) * up)
-  EPI_HEAD = 3,    // n < n_logits: logits[m*logits_ld + n] = y, greedy key over n < argmax_range;
-                   // n >= n_logits: out_f32[m*out_ld + n - n_logits] = y (projection rows)
+                   // u (chunked, no gain) column n = silu(gate) * up
+  EPI_HEAD = 3,    // n < n_logits: logits[m*logits_ld + n] = y, greedy-key candidates over
+                   // n < argmax_range; n >= n_logits: out_f32[m*out_ld + n - n_logits] = y
+                   // (projection rows)
 };
 
 struct GemmArgs {
-  const void* W;          // bf16 [N][K] or int8 [N][K]
+  const void* W;          // packed tiles (see above) of a bf16 or int8 [N][K] matrix
   const float* scale;     // [N] when INT8, else nullptr
   int N, K;               // full matrix
-  int row0, nrows;        // rows [row0, row0+nrows) are computed
-  const uint16_t* act;    // bf16 [M][act_ld]: high part of the activations
-  const uint16_t* act_lo; // bf16 [M][act_ld]: low part, or nullptr
-  int act_ld, M;
+  int row0, nrows;        // rows [row0, row0+nrows) are computed (multiples of 16)
+  const uint16_t* act;    // chunked bf16 [K/8][act_ld][8]: high part of the activations
+  const uint16_t* act_lo; // low part, or nullptr
+  int act_ld, M;          // rows 0..M-1 of the chunked arrays are used
   // Consumer of an RMSNorm: the activations are x * gain (left by the producer of
   // x), so every output is multiplied by inv[m] = 1/sqrt(sum_s ss_in[s*ss_in_ld+m]/K
   // + eps), the producer's per-row-block sums of squares.  ss_in == nullptr: none.
@@ -42,19 +70,18 @@ struct GemmArgs {
   int ss_in_ld, ss_in_slots;
   float norm_eps;
   int epi;
-  float* out_f32;
+  float* out_f32;         // row-major f32 [M][out_ld]
   int out_ld;
-  uint16_t* out_bf16;     // EPI_SWIGLU: high part
-  uint16_t* out_bf16_lo;  // EPI_SWIGLU: low part
   float* logits;
   int logits_ld, n_logits, argmax_range;
-  unsigned long long* keys;  // greedy keys, one per m, stride keys_ld
-  int keys_ld;
+  // greedy-key candidates: cand[m*cand_ld + n/16] = best key of rows n..n+15
+  unsigned long long* cand;
+  int cand_ld;
   uint32_t* status;
-  // Producer of an RMSNorm input (EPI_RESID rows, EPI_HEAD projection rows): for
-  // every written value v at output column c, u_hi/u_lo[m*u_ld + c] = hi/lo of
-  // v * u_gain[c] (the next norm's gain), and per row block the sum of squares of
-  // the block's values in ss_out[slot*ss_out_ld + m].  u_gain == nullptr: none.
+  // Chunked bf16 output pair: EPI_SWIGLU writes the SwiGLU activations here; a
+  // producer of an RMSNorm input (EPI_RESID rows, EPI_HEAD projection rows) writes
+  // hi/lo of v * u_gain[c] for every value v at output column c, and per 16-row
+  // block the sum of squares of the block's values in ss_out[slot*ss_out_ld + m].
   const uint16_t* u_gain;
   uint16_t* u_hi;
   uint16_t* u_lo;
@@ -80,10 +107,11 @@ inline void launch_kernel(Kernel kernel, dim3 grid, dim3 block, hipStream_t s, A
     hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
 }
 
-// Launch shape chosen for one GEMM (see plan_gemm).
+// Launch shape chosen for one GEMM (see plan_gemm): 16 weight rows per block, nw
+// waves splitting K; mt > 0: MFMA over mt 16-row activation tiles, mt == 0: VALU
+// dot products (M <= 2); g = K steps per load group.
 struct GemmPlan {
-  bool mfma;
-  int mt, mp, rw, ni, rt, nw;
+  int nw, mt, g;
   int rows_per_block, row_blocks;
 };
 
@@ -102,9 +130,9 @@ struct AttnPagedArgs {
   int pages_per_split, n_splits;
   float* part;            // [B][n_q][n_splits][128 + 2]
   unsigned* counters;     // [B][n_kv]
-  uint16_t* o;            // [B][o_ld] bf16 high part of the attention output
+  uint16_t* o;            // chunked bf16 [q_dim/8][o_ld][8]: high part of the attention output
   uint16_t* o_lo;         // low part
-  int o_ld;
+  int o_ld;               // rows of the chunked output (>= B)
   uint32_t* status;
 };
 
@@ -118,9 +146,9 @@ struct AttnPredArgs {
   uint16_t* v_cache;
   long long sess_stride;  // elements between sessions
   int pos0, n_new;
-  uint16_t* o;            // [n_new*B][o_ld] high part
+  uint16_t* o;            // chunked [q_dim/8][o_ld][8]; row i*B + b: new position pos0+i of session b
   uint16_t* o_lo;         // low part
-  int o_ld;
+  int o_ld;               // rows of the chunked output (>= n_new*B)
 };
 
 struct FrameBeginArgs {
@@ -129,12 +157,14 @@ struct FrameBeginArgs {
   const uint16_t* talker_in;
   const int32_t* tok0_in;
   const int32_t* kv_len;
+  const uint16_t* h_in;     // [B][Ht] bf16 post-norm hidden (predictor mode)
   float* x_t;              // [B][Ht] f32
   float* ss_t;             // [B]: sum of squares of the talker input rows (one slot)
   const uint16_t* gain;    // [Ht]: gain of the first Talker norm
-  uint16_t* u_hi;          // [B][Ht]: hi/lo of x * gain
+  uint16_t* u_hi;          // chunked [Ht/8][B][8]: hi/lo of x * gain (predictor mode: h_in, 0)
   uint16_t* u_lo;
-  unsigned long long* keys;  // [B][ncb]
+  unsigned long long* cand;  // [ncb][B][cand_ld] greedy-key candidates
+  int cand_ld;
   unsigned* counters;        // [B][n_kv] attention counters, zeroed
   uint32_t* status;
 };
@@ -143,21 +173,24 @@ struct EmbedArgs {
   int B, H, vocab, ncb, step;   // step k >= 1 embeds the token of codebook k-1
   float eps;
   const uint16_t* table;        // [vocab][H]
-  const unsigned long long* keys;
+  const unsigned long long* cand;  // candidates of codebook step-1: [B][cand_ld], n_cand used
+  int cand_ld, n_cand;
   const int32_t* forced;        // [B][ncb] or nullptr
   float* x;                     // [rows][H]
   float* ss;                    // sums of squares: slot 0 of the written rows, other slots zero
   int ss_ld, ss_slots;
   const uint16_t* gain;         // [H]: gain of the first predictor norm
-  uint16_t* u_hi;               // [rows][H]: hi/lo of x * gain
+  uint16_t* u_hi;               // chunked [H/8][u_ld][8]: hi/lo of x * gain
   uint16_t* u_lo;
+  int u_ld;
   int row_off;
   uint32_t* status;
 };
 
 struct FrameEndArgs {
   int mode, B, ncb, capacity;
-  const unsigned long long* keys;
+  const unsigned long long* cand;  // [ncb][B][cand_ld]
+  int cand_ld, n_cand0, n_cand;    // candidates of codebook 0 / of the others
   int32_t* tokens;  // [B][ncb]
   int32_t* kv_len;
 };
@@ -172,8 +205,16 @@ hipError_t launch_attn_pred(const AttnPredArgs& a, float theta, hipStream_t s);
 hipError_t launch_frame_begin(const FrameBeginArgs& a, hipStream_t s);
 hipError_t launch_embed(const EmbedArgs& a, hipStream_t s);
 hipError_t launch_frame_end(const FrameEndArgs& a, hipStream_t s);
+// Pack bf16 source rows [rows][K] as rows row0 + i*step of a tiled [N][K] matrix.
+hipError_t launch_pack_tiled(const uint16_t* src, int rows, int K, uint16_t* dst, int row0, int step,
+                             hipStream_t s);
+// Copy rows row0 + i*step (i < rows) of a tiled int8 [N][K] matrix out row-major.
+hipError_t launch_untile_i8(const int8_t* tiled, int rows, int K, int row0, int step, int8_t* out,
+                            hipStream_t s);
+// INT8 quantizer.  tiled_K == 0: q row r at q + r*q_row_stride; tiled_K > 0: source row r
+// becomes row row0 + r*q_row_stride of a tiled int8 [N][tiled_K] matrix at q.
 hipError_t launch_quantize(const uint16_t* w, long long rows, long long cols, int8_t* q,
                            long long q_row_stride, float* scale, long long scale_stride,
-                           hipStream_t s);
+                           int tiled_K, long long row0, hipStream_t s);
 
 }  // namespace qt

@@ -68,7 +68,7 @@ __global__ __launch_bounds__(256) void k_attn_paged(AttnPagedArgs a, float theta
   const int p = a.kv_len[b];
   const int j0 = 2 * h;
   const int jj = tid >> 7, d = tid & 127;
-  const size_t orow = (size_t)b * a.o_ld + (j0 + jj) * 128 + d;
+  const size_t orow = chunked(b, (j0 + jj) * 128 + d, a.o_ld);
   if (p < 0 || p >= cap) {
     if (s == 0) a.o[orow] = a.o_lo[orow] = 0;
     return;
@@ -369,13 +369,15 @@ __global__ __launch_bounds__(256) void k_attn_pred(AttnPredArgs a, float theta_l
   __syncthreads();
   for (int i = 0; i < a.n_new; ++i) {
     const float out = red[0][i][jj][d] + red[1][i][jj][d] + red[2][i][jj][d] + red[3][i][jj][d];
-    split_bf16(out / lsum[i][jj], a.o, a.o_lo, (size_t)(i * a.B + b) * a.o_ld + (j0 + jj) * 128 + d);
+    split_bf16(out / lsum[i][jj], a.o, a.o_lo, chunked(i * a.B + b, (j0 + jj) * 128 + d, a.o_ld));
   }
 }
 
 // ---------------------------------------------------------------------------
-// Frame entry: Talker input rows to fp32 with their sums of squares, capacity
-// check, greedy keys and attention counters cleared.
+// Frame entry: Talker input rows to fp32 with their sums of squares and the first
+// norm's hi/lo input (predictor mode: the given post-norm hidden as the projection
+// input), capacity check, codebook-0 candidates of predictor mode, attention
+// counters cleared.
 __global__ __launch_bounds__(256) void k_frame_begin(FrameBeginArgs a) {
   __shared__ float part[4];
   const int b = blockIdx.x, tid = threadIdx.x;
@@ -385,7 +387,7 @@ __global__ __launch_bounds__(256) void k_frame_begin(FrameBeginArgs a) {
       const size_t e = (size_t)b * a.Ht + i;
       const float v = bf2f(a.talker_in[e]);
       a.x_t[e] = v;
-      split_bf16(v * bf2f(a.gain[i]), a.u_hi, a.u_lo, e);
+      split_bf16(v * bf2f(a.gain[i]), a.u_hi, a.u_lo, chunked(b, i, a.B));
       ss = fmaf(v, v, ss);
     }
     ss = wave_sum(ss);
@@ -396,52 +398,72 @@ __global__ __launch_bounds__(256) void k_frame_begin(FrameBeginArgs a) {
       const int p = a.kv_len[b];
       if (p < 0 || p + 1 > a.capacity) atomicOr(a.status, QT_STATUS_KV_OVERFLOW);
     }
-  }
-  for (int k = tid; k < a.ncb; k += 256) {
-    unsigned long long key = 0;
-    if (a.mode == QT_MODE_PREDICTOR && k == 0) key = greedy_key(0.0f, a.tok0_in[b]);
-    a.keys[(size_t)b * a.ncb + k] = key;
+  } else {
+    for (int i = tid; i < a.Ht; i += 256) a.u_hi[chunked(b, i, a.B)] = a.h_in[(size_t)b * a.Ht + i];
+    unsigned long long* c0 = a.cand + (size_t)b * a.cand_ld;
+    for (int k = tid; k < a.cand_ld; k += 256) c0[k] = k == 0 ? greedy_key(0.0f, a.tok0_in[b]) : 0ull;
   }
   if (tid < a.n_kv) a.counters[(size_t)b * a.n_kv + tid] = 0u;
 }
 
+// Best of n greedy-key candidates, reduced by the 64 lanes of a wave.
+__device__ __forceinline__ unsigned long long best_key_wave(const unsigned long long* c, int n) {
+  const int lane = threadIdx.x & 63;
+  unsigned long long best = 0;
+  for (int k = lane; k < n; k += 64) best = c[k] > best ? c[k] : best;
+  return wave_max_u64(best);
+}
+
 // Predictor step input: row E_step[token] (token = forced, or the previous step's
-// greedy token) to fp32, with its sum of squares.
+// greedy token) to fp32, with its sum of squares and the first norm's hi/lo input.
 __global__ __launch_bounds__(256) void k_embed(EmbedArgs a) {
   __shared__ float part[4];
+  __shared__ int s_tok;
   const int b = blockIdx.x, tid = threadIdx.x;
-  int tok = a.forced ? a.forced[(size_t)b * a.ncb + a.step - 1]
-                     : key_index(a.keys[(size_t)b * a.ncb + a.step - 1]);
+  if (a.forced) {
+    if (tid == 0) s_tok = a.forced[(size_t)b * a.ncb + a.step - 1];
+  } else if (tid < 64) {
+    const unsigned long long k =
+        best_key_wave(a.cand + ((size_t)(a.step - 1) * a.B + b) * a.cand_ld, a.n_cand);
+    if (tid == 0) s_tok = key_index(k);
+  }
+  __syncthreads();
+  int tok = s_tok;
   if (tok < 0 || tok >= a.vocab) {
     if (tid == 0) atomicOr(a.status, QT_STATUS_BAD_TOKEN);
     tok = 0;
   }
   const uint16_t* src = a.table + (size_t)tok * a.H;
-  float* dst = a.x + (size_t)(a.row_off + b) * a.H;
+  const int m = a.row_off + b;
+  float* dst = a.x + (size_t)m * a.H;
   float ss = 0.f;
-  const size_t ub = (size_t)(a.row_off + b) * a.H;
   for (int i = tid; i < a.H; i += 256) {
     const float v = bf2f(src[i]);
     dst[i] = v;
-    split_bf16(v * bf2f(a.gain[i]), a.u_hi, a.u_lo, ub + i);
+    split_bf16(v * bf2f(a.gain[i]), a.u_hi, a.u_lo, chunked(m, i, a.u_ld));
     ss = fmaf(v, v, ss);
   }
   ss = wave_sum(ss);
   if ((tid & 63) == 0) part[tid >> 6] = ss;
   __syncthreads();
-  const int m = a.row_off + b;
   for (int sl = tid; sl < a.ss_slots; sl += 256)
     a.ss[(size_t)sl * a.ss_ld + m] = sl == 0 ? part[0] + part[1] + part[2] + part[3] : 0.f;
 }
 
+// Frame exit, one block per session: each codebook's candidates reduced to its
+// greedy token, and the session's cache length advanced.
 __global__ __launch_bounds__(256) void k_frame_end(FrameEndArgs a) {
-  const int e = blockIdx.x * 256 + threadIdx.x;
-  if (e >= a.B * a.ncb) return;
-  const int b = e / a.ncb, k = e - b * a.ncb;
-  int tok = key_index(a.keys[e]);
-  if (a.mode == QT_MODE_TALKER && k > 0) tok = -1;
-  a.tokens[e] = tok;
-  if (k == 0 && a.mode != QT_MODE_PREDICTOR) {
+  const int b = blockIdx.x, tid = threadIdx.x, wave = tid >> 6;
+  for (int k = wave; k < a.ncb; k += 4) {
+    const unsigned long long best = best_key_wave(
+        a.cand + ((size_t)k * a.B + b) * a.cand_ld, k == 0 ? a.n_cand0 : a.n_cand);
+    if ((tid & 63) == 0) {
+      int tok = key_index(best);
+      if (a.mode == QT_MODE_TALKER && k > 0) tok = -1;
+      a.tokens[(size_t)b * a.ncb + k] = tok;
+    }
+  }
+  if (tid == 0 && a.mode != QT_MODE_PREDICTOR) {
     const int p = a.kv_len[b];
     if (p >= 0 && p + 1 <= a.capacity) a.kv_len[b] = p + 1;
   }
@@ -451,7 +473,7 @@ __global__ __launch_bounds__(256) void k_frame_end(FrameEndArgs a) {
 // Per-row symmetric INT8: s = max|w| / 127 (IEEE divide), q = clamp(rint(w / s), +-127).
 __global__ __launch_bounds__(256) void k_quantize(const uint16_t* w, long long cols, int8_t* q,
                                                   long long q_stride, float* scale,
-                                                  long long s_stride) {
+                                                  long long s_stride, int tiled_K, long long row0) {
   __shared__ float part[4];
   const long long r = blockIdx.x;
   const int tid = threadIdx.x;
@@ -464,14 +486,15 @@ __global__ __launch_bounds__(256) void k_quantize(const uint16_t* w, long long c
   amax = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
   const float sc = __fdiv_rn(amax, 127.0f);
   if (tid == 0) scale[r * s_stride] = sc;
-  int8_t* qr = q + r * q_stride;
   for (long long k = tid; k < cols; k += 256) {
     float v = 0.f;
     if (sc != 0.f) {
       v = rintf(__fdiv_rn(bf2f(row[k]), sc));
       v = fminf(fmaxf(v, -127.f), 127.f);
     }
-    qr[k] = (int8_t)(int)v;
+    const size_t o = tiled_K ? tiled_i8((int)(row0 + r * q_stride), (int)k, tiled_K)
+                             : (size_t)(r * q_stride + k);
+    q[o] = (int8_t)(int)v;
   }
 }
 
@@ -505,16 +528,17 @@ hipError_t launch_embed(const EmbedArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_frame_end(const FrameEndArgs& a, hipStream_t s) {
-  launch_kernel(k_frame_end, dim3((a.B * a.ncb + 255) / 256), dim3(256), s, a);
+  launch_kernel(k_frame_end, dim3(a.B), dim3(256), s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_quantize(const uint16_t* w, long long rows, long long cols, int8_t* q,
                            long long q_row_stride, float* scale, long long scale_stride,
-                           hipStream_t s) {
+                           int tiled_K, long long row0, hipStream_t s) {
   if (rows <= 0 || cols <= 0 || rows > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (tiled_K && (cols != tiled_K || tiled_K % 64 || row0 < 0)) return hipErrorInvalidValue;
   launch_kernel(k_quantize, dim3((unsigned)rows), dim3(256), s, w, cols, q, q_row_stride,
-                     scale, scale_stride);
+                     scale, scale_stride, tiled_K, row0);
   return hipGetLastError();
 }
 
