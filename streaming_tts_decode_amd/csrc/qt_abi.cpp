@@ -545,7 +545,8 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
   GemmArgs head = gemm_act(m, m->plan.t_head, ut, nullptr, ld_t, B, out->status);
 
   if (talker) {
-    const int pps_raw = (B * T.n_kv_heads * max_pages + 2047) / 2048;
+    // pages per split: about 1024 blocks over the page table, at most 8 pages each
+    const int pps_raw = (B * T.n_kv_heads * max_pages + 1023) / 1024;
     const int pps = pps_raw < 1 ? 1 : (pps_raw > kMaxPagesPerSplit ? kMaxPagesPerSplit : pps_raw);
     const int n_splits = (max_pages + pps - 1) / pps;
     const size_t layer_elems = (size_t)kv->num_pages * T.n_kv_heads * kPage * kHeadDim;

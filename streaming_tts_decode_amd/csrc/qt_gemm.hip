@@ -90,18 +90,46 @@ __device__ __forceinline__ void split8(const float (&v)[8], uint4& hi, uint4& lo
   lo = make_uint4(l[0], l[1], l[2], l[3]);
 }
 
+// Operands of the epilogue that live in memory, loaded at kernel start so that
+// their latency overlaps the main loads: the residual values this thread adds to
+// (elements e = tid + k*nthr of the 16 x M tile, e -> (m = e/16, r = e%16)), the
+// INT8 scale of row n0 + tid%16 and the next norm's gains of the block's columns.
+constexpr int kMaxResid = 2;  // 16 * 64 tile elements over >= 512 threads
+struct EpiPrefetch {
+  float x[kMaxResid];
+  float scale;
+  float gain;  // column c0 + tid (tid < 16)
+};
+
+__device__ __forceinline__ void epi_prefetch(const GemmArgs& a, int n0, EpiPrefetch& p) {
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int M = a.M;
+#pragma unroll
+  for (int k = 0; k < kMaxResid; ++k) {
+    const int e = tid + k * nthr;
+    p.x[k] = (a.epi == EPI_RESID && e < kGemmRows * M)
+                 ? a.out_f32[(size_t)(e >> 4) * a.out_ld + n0 + (e & 15)]
+                 : 0.f;
+  }
+  p.scale = a.scale ? a.scale[n0 + (tid & 15)] : 1.f;
+  const int base = a.epi == EPI_RESID ? 0 : a.n_logits;
+  p.gain = (a.u_gain && (a.epi == EPI_RESID || a.epi == EPI_HEAD) && n0 >= base && tid < kGemmRows)
+               ? bf2f(a.u_gain[n0 - base + tid])
+               : 0.f;
+}
+
 // Epilogue over the block's tile: tile[r * tld + m] is weight row n0 + r (r < 16),
-// activation row m, before the INT8 scale and the RMSNorm factor.
+// activation row m, before the INT8 scale and the RMSNorm factor.  s_gain: LDS
+// copy of the prefetched gains.
 __device__ void gemm_epilogue(const GemmArgs& a, int n0, float* tile, int tld,
-                              const float* s_inv) {
+                              const float* s_inv, const EpiPrefetch& pf, const float* s_gain) {
   constexpr int R = kGemmRows;
   const int M = a.M;
   const int tid = threadIdx.x, nthr = blockDim.x;
   if (a.scale || a.ss_in) {
     for (int e = tid; e < R * M; e += nthr) {
       const int m = e >> 4, r = e & 15;
-      float y = tile[r * tld + m];
-      if (a.scale) y *= a.scale[n0 + r];
+      float y = tile[r * tld + m] * pf.scale;
       if (a.ss_in) y *= s_inv[m];
       tile[r * tld + m] = y;
     }
@@ -156,12 +184,14 @@ __device__ void gemm_epilogue(const GemmArgs& a, int n0, float* tile, int tld,
   // residual rows (EPI_RESID: x += y) or projection rows (EPI_HEAD: x = y)
   const int base = a.epi == EPI_RESID ? 0 : a.n_logits;
   const int c0 = n0 - base;
-  for (int e = tid; e < R * M; e += nthr) {
+#pragma unroll
+  for (int k = 0; k < kMaxResid; ++k) {
+    const int e = tid + k * nthr;
+    if (e >= R * M) break;
     const int m = e >> 4, r = e & 15;
-    float* p = a.out_f32 + (size_t)m * a.out_ld + c0 + r;
     float v = tile[r * tld + m];
-    if (a.epi == EPI_RESID) v += *p;
-    *p = v;
+    if (a.epi == EPI_RESID) v += pf.x[k];
+    a.out_f32[(size_t)m * a.out_ld + c0 + r] = v;
     tile[r * tld + m] = v;
   }
   if (!a.u_gain) return;
@@ -176,7 +206,7 @@ __device__ void gemm_epilogue(const GemmArgs& a, int n0, float* tile, int tld,
       for (int j = 0; j < 8; ++j) {
         const float x = tile[(8 * h + j) * tld + m];
         ss = fmaf(x, x, ss);
-        v[j] = x * bf2f(a.u_gain[c0 + 8 * h + j]);
+        v[j] = x * s_gain[8 * h + j];
       }
       uint4 hi, lo;
       split8(v, hi, lo);
@@ -204,6 +234,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs a) {
   constexpr int MV = MT ? 16 * MT : 2;   // activation rows held per lane group
   __shared__ float red[NW][kGemmRows * TLD];
   __shared__ float s_inv[64];
+  __shared__ float s_gain[kGemmRows];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i = lane & 15, q = lane >> 4;
   const int rt = (a.row0 >> 4) + blockIdx.x;
@@ -218,6 +249,8 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs a) {
   float ssr[kSsRegs];
   int ss_per_lane = 0;
   if (a.ss_in) ss_prefetch(a, wave, NW, ssr, ss_per_lane);
+  EpiPrefetch pf;
+  epi_prefetch(a, n0, pf);
 
   // activation row m of chunk c: 16 bytes at H[c * ld + m]
   if constexpr (MT > 0) {
@@ -305,6 +338,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs a) {
     }
   }
   if (a.ss_in) ss_finish(a, wave, NW, ssr, ss_per_lane, s_inv);
+  if (tid < kGemmRows) s_gain[tid] = pf.gain;
   __syncthreads();
   for (int e = tid; e < kGemmRows * M; e += NW * 64) {
     const int m = e >> 4, r = e & 15;
@@ -314,7 +348,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs a) {
     red[0][r * TLD + m] = s;
   }
   __syncthreads();
-  gemm_epilogue(a, n0, red[0], TLD, s_inv);
+  gemm_epilogue(a, n0, red[0], TLD, s_inv, pf, s_gain);
 }
 
 template <bool I8>

@@ -51,6 +51,11 @@ __device__ __forceinline__ float norm_rope_128(float v, int d, const uint16_t* g
 // unnormalised output) partials; the last block to arrive merges them in split
 // order (deterministic), writes the bf16 attention output and resets the
 // counter.
+//
+// Memory round trips are kept to two before the arithmetic: the cache length,
+// this split's page-table entries and the raw q / k / v values are loaded
+// together; then all of the split's K/V loads are issued, and the q and k
+// normalisation and rotation run while they are in flight.
 __global__ __launch_bounds__(256) void k_attn_paged(AttnPagedArgs a, float theta_log2) {
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -62,42 +67,75 @@ __global__ __launch_bounds__(256) void k_attn_paged(AttnPagedArgs a, float theta
   __shared__ float ssq[2][2];
   __shared__ float stat[2][2];
   __shared__ float mstat[2], lstat[2];
+  __shared__ float mred[2][2];
   __shared__ int s_last;
 
   const int cap = a.max_pages * kPage;
-  const int p = a.kv_len[b];
+  const int pps = a.pages_per_split;
   const int j0 = 2 * h;
   const int jj = tid >> 7, d = tid & 127;
+  const float* qrow = a.qkv + (size_t)b * a.qkv_ld;
+  const int q_dim = a.n_q * 128, kv_dim = a.n_kv * 128;
+  const int* ptab = a.page_table + (size_t)b * a.max_pages;
+
+  // ---- round trip 1: nothing here depends on the cache length
+  const int p = a.kv_len[b];
+  int pg[kMaxPagesPerSplit];
+#pragma unroll
+  for (int g = 0; g < kMaxPagesPerSplit; ++g) {
+    const int pidx = s * pps + g;
+    pg[g] = (g < pps && pidx < a.max_pages) ? ptab[pidx] : -1;
+  }
+  const float qraw = qrow[(j0 + jj) * 128 + d];
+  const float kvraw = qrow[q_dim + (jj ? kv_dim : 0) + h * 128 + d];
+
   const size_t orow = chunked(b, (j0 + jj) * 128 + d, a.o_ld);
   if (p < 0 || p >= cap) {
     if (s == 0) a.o[orow] = a.o_lo[orow] = 0;
     return;
   }
-  const int S = a.pages_per_split * kPage;
+  const int S = pps * kPage;
   const int n_active = p / S + 1;
   if (s >= n_active) return;
   const int t0 = s * S, t1 = min(t0 + S, p + 1);
   const bool has_new = (s == n_active - 1);
-  const float* qrow = a.qkv + (size_t)b * a.qkv_ld;
-  const int q_dim = a.n_q * 128, kv_dim = a.n_kv * 128;
 
-  // q heads j0 (threads 0..127) and j0+1 (128..255)
+  // ---- round trip 2: the split's K/V; thread (pi = tid>>4, c = tid&15) covers
+  // positions t0 + 16g + pi, dims 8c..8c+7
+  const int pi = tid >> 4, c = tid & 15;
+  uint4 kk[kMaxPagesPerSplit], vv[kMaxPagesPerSplit];
+  bool bad = false;
+#pragma unroll
+  for (int g = 0; g < kMaxPagesPerSplit; ++g) {
+    kk[g] = make_uint4(0, 0, 0, 0);
+    vv[g] = make_uint4(0, 0, 0, 0);
+    const int t = t0 + g * kPage + pi;
+    if (g < pps && t < t1 && t != p) {
+      if (pg[g] >= 0 && pg[g] < a.num_pages) {
+        const size_t off = ((size_t)pg[g] * a.n_kv + h) * (kPage * 128) + (size_t)pi * 128 + 8 * c;
+        kk[g] = *reinterpret_cast<const uint4*>(a.k_pool + off);
+        vv[g] = *reinterpret_cast<const uint4*>(a.v_pool + off);
+      } else {
+        bad = true;
+      }
+    }
+  }
+  if (bad && c == 0) atomicOr(a.status, QT_STATUS_BAD_PAGE);
+
+  // q heads j0 (threads 0..127) and j0+1 (128..255), while the K/V loads fly
   {
-    const float v = qrow[(j0 + jj) * 128 + d];
-    const float r = norm_rope_128(v, d, a.q_norm, a.eps, p, theta_log2, rb[jj], ssq[jj]);
+    const float r = norm_rope_128(qraw, d, a.q_norm, a.eps, p, theta_log2, rb[jj], ssq[jj]);
     qs[jj][d] = r * kInvSqrtHd;
   }
-  const int* ptab = a.page_table + (size_t)b * a.max_pages;
   if (has_new) {
     // threads 0..127: key of KV head h (normalised and rotated); threads 128..255:
     // value (taken raw; the normalisation both halves run keeps barriers uniform)
-    const float raw = qrow[q_dim + (jj ? kv_dim : 0) + h * 128 + d];
-    const float kr = norm_rope_128(raw, d, a.k_norm, a.eps, p, theta_log2, rb[jj], ssq[jj]);
-    const float kv = jj ? raw : kr;
+    const float kr = norm_rope_128(kvraw, d, a.k_norm, a.eps, p, theta_log2, rb[jj], ssq[jj]);
+    const float kv = jj ? kvraw : kr;
     const uint16_t bits = f2bf(kv);
-    const int pg = ptab[p / kPage];
-    if (pg >= 0 && pg < a.num_pages) {
-      const size_t off = ((size_t)pg * a.n_kv + h) * (kPage * 128) + (size_t)(p % kPage) * 128 + d;
+    const int pgn = ptab[p / kPage];
+    if (pgn >= 0 && pgn < a.num_pages) {
+      const size_t off = ((size_t)pgn * a.n_kv + h) * (kPage * 128) + (size_t)(p % kPage) * 128 + d;
       (jj == 0 ? a.k_pool : a.v_pool)[off] = bits;
     } else if (d == 0 && jj == 0) {
       atomicOr(a.status, QT_STATUS_BAD_PAGE);
@@ -106,34 +144,15 @@ __global__ __launch_bounds__(256) void k_attn_paged(AttnPagedArgs a, float theta
   }
   __syncthreads();
 
-  // scores: thread (pi = tid>>4, c = tid&15) covers position t0+16g+pi, dims 8c..8c+7
-  const int pi = tid >> 4, c = tid & 15;
   float q0[8], q1[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     q0[e] = qs[0][8 * c + e];
     q1[e] = qs[1][8 * c + e];
   }
-  uint4 kk[kMaxPagesPerSplit], vv[kMaxPagesPerSplit];
 #pragma unroll
   for (int g = 0; g < kMaxPagesPerSplit; ++g) {
-    kk[g] = make_uint4(0, 0, 0, 0);
-    vv[g] = make_uint4(0, 0, 0, 0);
-    const int t = t0 + g * kPage + pi;
-    if (g < a.pages_per_split && t < t1 && t != p) {
-      const int pg = ptab[t / kPage];
-      if (pg >= 0 && pg < a.num_pages) {
-        const size_t off = ((size_t)pg * a.n_kv + h) * (kPage * 128) + (size_t)pi * 128 + 8 * c;
-        kk[g] = *reinterpret_cast<const uint4*>(a.k_pool + off);
-        vv[g] = *reinterpret_cast<const uint4*>(a.v_pool + off);
-      } else if (c == 0) {
-        atomicOr(a.status, QT_STATUS_BAD_PAGE);
-      }
-    }
-  }
-#pragma unroll
-  for (int g = 0; g < kMaxPagesPerSplit; ++g) {
-    if (g >= a.pages_per_split) break;
+    if (g >= pps) break;
     const int t = t0 + g * kPage + pi;
     float kf[8];
     if (t == p) {
@@ -188,7 +207,7 @@ __global__ __launch_bounds__(256) void k_attn_paged(AttnPagedArgs a, float theta
   for (int e = 0; e < 8; ++e) a0[e] = a1[e] = 0.f;
 #pragma unroll
   for (int g = 0; g < kMaxPagesPerSplit; ++g) {
-    if (g >= a.pages_per_split) break;
+    if (g >= pps) break;
     const int t = t0 + g * kPage + pi;
     if (t < t1) {
       const float w0 = sc[0][g * kPage + pi], w1 = sc[1][g * kPage + pi];
@@ -249,14 +268,22 @@ __global__ __launch_bounds__(256) void k_attn_paged(AttnPagedArgs a, float theta
   }
   __syncthreads();
   if (!s_last) return;
+  // merge: the running maximum over splits (threads of a head split the splits
+  // between them), then every thread sums its dimension over the splits in order
   const float* pb = a.part + ((size_t)b * a.n_q + j0 + jj) * a.n_splits * 130;
   float M = -INFINITY;
-  for (int ss = 0; ss < n_active; ++ss) M = fmaxf(M, dev_load(pb + ss * 130));
+  for (int ss = d; ss < n_active; ss += 128) M = fmaxf(M, dev_load(pb + ss * 130));
+  M = wave_max(M);
+  if (lane == 0) mred[jj][wave & 1] = M;
+  __syncthreads();
+  M = fmaxf(mred[jj][0], mred[jj][1]);
   float L = 0.f, O = 0.f;
+#pragma unroll 8
   for (int ss = 0; ss < n_active; ++ss) {
-    const float w = expf(dev_load(pb + ss * 130) - M);
-    L = fmaf(dev_load(pb + ss * 130 + 1), w, L);
-    O = fmaf(dev_load(pb + ss * 130 + 2 + d), w, O);
+    const float* ps = pb + ss * 130;
+    const float w = expf(dev_load(ps) - M);
+    L = fmaf(dev_load(ps + 1), w, L);
+    O = fmaf(dev_load(ps + 2 + d), w, O);
   }
   split_bf16(O / L, a.o, a.o_lo, orow);
   if (tid == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -283,16 +310,31 @@ __global__ __launch_bounds__(256) void k_attn_pred(AttnPredArgs a, float theta_l
   uint16_t* kbase = a.k_cache + (size_t)b * a.sess_stride;
   uint16_t* vbase = a.v_cache + (size_t)b * a.sess_stride;
 
+  // one round trip: the raw new rows and every cached position (thread group
+  // t = tid>>4 holds position t, dims 8c..8c+7)
+  const int t = tid >> 4, c = tid & 15;
+  uint4 kq = make_uint4(0, 0, 0, 0), vq = make_uint4(0, 0, 0, 0);
+  if (t < a.pos0) {
+    const size_t off = ((size_t)t * a.n_kv + h) * 128 + 8 * c;
+    kq = *reinterpret_cast<const uint4*>(kbase + off);
+    vq = *reinterpret_cast<const uint4*>(vbase + off);
+  }
+  float qraw[2] = {0.f, 0.f}, kvraw[2] = {0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    if (i < a.n_new) {
+      const float* row = a.qkv + (size_t)(i * a.B + b) * a.qkv_ld;
+      qraw[i] = row[(j0 + jj) * 128 + d];
+      kvraw[i] = row[q_dim + (jj ? kv_dim : 0) + h * 128 + d];
+    }
+  }
   for (int i = 0; i < a.n_new; ++i) {
-    const float* row = a.qkv + (size_t)(i * a.B + b) * a.qkv_ld;
     const int pos = a.pos0 + i;
-    const float r = norm_rope_128(row[(j0 + jj) * 128 + d], d, a.q_norm, a.eps, pos, theta_log2,
-                                  rb[jj], ssq[jj]);
+    const float r = norm_rope_128(qraw[i], d, a.q_norm, a.eps, pos, theta_log2, rb[jj], ssq[jj]);
     qs[i][jj][d] = r * kInvSqrtHd;
     __syncthreads();
-    const float raw = row[q_dim + (jj ? kv_dim : 0) + h * 128 + d];
-    const float kr = norm_rope_128(raw, d, a.k_norm, a.eps, pos, theta_log2, rb[jj], ssq[jj]);
-    const float kv = jj ? raw : kr;
+    const float kr = norm_rope_128(kvraw[i], d, a.k_norm, a.eps, pos, theta_log2, rb[jj], ssq[jj]);
+    const float kv = jj ? kvraw[i] : kr;
     const uint16_t bits = f2bf(kv);
     const size_t off = ((size_t)pos * a.n_kv + h) * 128 + d;
     (jj == 0 ? kbase : vbase)[off] = bits;
@@ -301,7 +343,6 @@ __global__ __launch_bounds__(256) void k_attn_pred(AttnPredArgs a, float theta_l
   }
 
   const int n_pos = a.pos0 + a.n_new;
-  const int t = tid >> 4, c = tid & 15;
   float kf[8], vf[8];
   if (t < n_pos) {
     if (t >= a.pos0) {
@@ -311,9 +352,6 @@ __global__ __launch_bounds__(256) void k_attn_pred(AttnPredArgs a, float theta_l
         vf[e] = vn[t - a.pos0][8 * c + e];
       }
     } else {
-      const size_t off = ((size_t)t * a.n_kv + h) * 128 + 8 * c;
-      const uint4 kq = *reinterpret_cast<const uint4*>(kbase + off);
-      const uint4 vq = *reinterpret_cast<const uint4*>(vbase + off);
       kf[0] = bf_lo(kq.x); kf[1] = bf_hi(kq.x); kf[2] = bf_lo(kq.y); kf[3] = bf_hi(kq.y);
       kf[4] = bf_lo(kq.z); kf[5] = bf_hi(kq.z); kf[6] = bf_lo(kq.w); kf[7] = bf_hi(kq.w);
       vf[0] = bf_lo(vq.x); vf[1] = bf_hi(vq.x); vf[2] = bf_lo(vq.y); vf[3] = bf_hi(vq.y);
