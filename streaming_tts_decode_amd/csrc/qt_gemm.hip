@@ -36,185 +36,159 @@ namespace qt {
 namespace {
 using namespace dev;
 
-// Registers for prefetched sum-of-squares slots, per wave.
-constexpr int kSsRegs = 16;
+// ---- RMSNorm statistics of the input rows (consumer side)
+// The producer of x left per-16-column sums of squares in ss_in[slot][m]
+// (slot < ss_in_slots).  Thread t of the block handles row m = t % M and slots
+// g, g + G, ... with g = t / M, G = min(nthr / M, slots): the loads are
+// coalesced over m and issued before the main loads; after the main loop the G
+// partials of a row are added in a fixed order.
+constexpr int kSsPer = 16;  // slot loads per thread kept in registers
 
-// Issue the sum-of-squares loads of rows m = first + step*j before the main loads,
-// so that waiting on them later does not wait on the main loads.
-__device__ __forceinline__ void ss_prefetch(const GemmArgs& a, int first, int step,
-                                            float (&r)[kSsRegs], int& per_lane) {
-  const int lane = threadIdx.x & 63;
-  per_lane = (a.ss_in_slots + 63) / 64;
-  int idx = 0;
+struct SsPrefetch {
+  float v[kSsPer];
+  int G;     // slot groups
+  bool on;   // this thread holds a partial
+};
+
+__device__ __forceinline__ void ss_prefetch(const GemmArgs& a, SsPrefetch& p) {
+  const int tid = threadIdx.x, nthr = blockDim.x, M = a.M;
+  int G = nthr / M;
+  if (G > a.ss_in_slots) G = a.ss_in_slots;
+  p.G = G;
+  const int g = tid / M, m = tid - g * M;
+  p.on = g < G;
 #pragma unroll
-  for (int j = 0; j < kSsRegs; ++j) r[j] = 0.f;
-  for (int m = first; m < a.M; m += step)
-    for (int s = 0; s < per_lane && idx < kSsRegs; ++s, ++idx) {
-      const int slot = lane + 64 * s;
-      r[idx] = slot < a.ss_in_slots ? a.ss_in[(size_t)slot * a.ss_in_ld + m] : 0.f;
-    }
-}
-
-// Finish the inverse RMS of the prefetched rows into s_inv (slots that did not fit
-// in the registers are summed directly).
-__device__ __forceinline__ void ss_finish(const GemmArgs& a, int first, int step,
-                                          const float (&r)[kSsRegs], int per_lane, float* s_inv) {
-  const int lane = threadIdx.x & 63;
-  int idx = 0;
-  for (int m = first; m < a.M; m += step) {
-    float ss = 0.f;
-    for (int s = 0; s < per_lane; ++s, ++idx) {
-      if (idx < kSsRegs) {
-        ss += r[idx];
-      } else {
-        const int slot = lane + 64 * s;
-        if (slot < a.ss_in_slots) ss += a.ss_in[(size_t)slot * a.ss_in_ld + m];
-      }
-    }
-    ss = wave_sum(ss);
-    if (lane == 0) s_inv[m] = 1.0f / sqrtf(ss / (float)a.K + a.norm_eps);
+  for (int k = 0; k < kSsPer; ++k) {
+    const int slot = g + k * G;
+    p.v[k] = (p.on && slot < a.ss_in_slots) ? a.ss_in[(size_t)slot * a.ss_in_ld + m] : 0.f;
   }
 }
 
-// Eight values to chunked hi/lo bf16 pieces (16 bytes each).
-__device__ __forceinline__ void split8(const float (&v)[8], uint4& hi, uint4& lo) {
-  uint32_t h[4], l[4];
+// Partial of this thread (slots beyond the registered ones are loaded now).
+__device__ __forceinline__ float ss_partial(const GemmArgs& a, const SsPrefetch& p) {
+  const int tid = threadIdx.x, M = a.M;
+  const int g = tid / M, m = tid - g * M;
+  float s = 0.f;
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const uint16_t h0 = f2bf(v[2 * p]), h1 = f2bf(v[2 * p + 1]);
-    const uint16_t l0 = f2bf(v[2 * p] - bf2f(h0)), l1 = f2bf(v[2 * p + 1] - bf2f(h1));
-    h[p] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-    l[p] = (uint32_t)l0 | ((uint32_t)l1 << 16);
-  }
-  hi = make_uint4(h[0], h[1], h[2], h[3]);
-  lo = make_uint4(l[0], l[1], l[2], l[3]);
+  for (int k = 0; k < kSsPer; ++k) s += p.v[k];
+  for (int slot = g + kSsPer * p.G; slot < a.ss_in_slots; slot += p.G)
+    s += a.ss_in[(size_t)slot * a.ss_in_ld + m];
+  return s;
+}
+
+// Nontemporal 16-byte load (weights are streamed once per call).
+__device__ __forceinline__ uint4 load_stream(const uint4* p) {
+  typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
 }
 
 // Operands of the epilogue that live in memory, loaded at kernel start so that
-// their latency overlaps the main loads: the residual values this thread adds to
-// (elements e = tid + k*nthr of the 16 x M tile, e -> (m = e/16, r = e%16)), the
-// INT8 scale of row n0 + tid%16 and the next norm's gains of the block's columns.
-constexpr int kMaxResid = 2;  // 16 * 64 tile elements over >= 512 threads
+// their latency overlaps the main loads.  Epilogue thread mapping: element
+// e = tid + k*nthr of the 16 x M tile is row r = e % 16, activation row m = e / 16
+// (so r = tid % 16 for every k): the residual value it adds to, the INT8 scale of
+// its row and the next norm's gain of its column.
+constexpr int kMaxElem = 2;  // 16 * 64 tile elements over >= 512 threads
 struct EpiPrefetch {
-  float x[kMaxResid];
+  float x[kMaxElem];
   float scale;
-  float gain;  // column c0 + tid (tid < 16)
+  float gain;
 };
 
 __device__ __forceinline__ void epi_prefetch(const GemmArgs& a, int n0, EpiPrefetch& p) {
   const int tid = threadIdx.x, nthr = blockDim.x;
-  const int M = a.M;
+  const int M = a.M, r = tid & 15;
 #pragma unroll
-  for (int k = 0; k < kMaxResid; ++k) {
+  for (int k = 0; k < kMaxElem; ++k) {
     const int e = tid + k * nthr;
     p.x[k] = (a.epi == EPI_RESID && e < kGemmRows * M)
-                 ? a.out_f32[(size_t)(e >> 4) * a.out_ld + n0 + (e & 15)]
+                 ? a.out_f32[(size_t)(e >> 4) * a.out_ld + n0 + r]
                  : 0.f;
   }
-  p.scale = a.scale ? a.scale[n0 + (tid & 15)] : 1.f;
+  p.scale = a.scale ? a.scale[n0 + r] : 1.f;
   const int base = a.epi == EPI_RESID ? 0 : a.n_logits;
-  p.gain = (a.u_gain && (a.epi == EPI_RESID || a.epi == EPI_HEAD) && n0 >= base && tid < kGemmRows)
-               ? bf2f(a.u_gain[n0 - base + tid])
+  p.gain = (a.u_gain && (a.epi == EPI_RESID || a.epi == EPI_HEAD) && n0 >= base)
+               ? bf2f(a.u_gain[n0 - base + r])
                : 0.f;
 }
 
-// Epilogue over the block's tile: tile[r * tld + m] is weight row n0 + r (r < 16),
-// activation row m, before the INT8 scale and the RMSNorm factor.  s_gain: LDS
-// copy of the prefetched gains.
-__device__ void gemm_epilogue(const GemmArgs& a, int n0, float* tile, int tld,
-                              const float* s_inv, const EpiPrefetch& pf, const float* s_gain) {
-  constexpr int R = kGemmRows;
-  const int M = a.M;
-  const int tid = threadIdx.x, nthr = blockDim.x;
-  if (a.scale || a.ss_in) {
-    for (int e = tid; e < R * M; e += nthr) {
-      const int m = e >> 4, r = e & 15;
-      float y = tile[r * tld + m] * pf.scale;
-      if (a.ss_in) y *= s_inv[m];
-      tile[r * tld + m] = y;
-    }
-    __syncthreads();
-  }
-  if (a.epi == EPI_STORE) {
-    for (int e = tid; e < R * M; e += nthr) {
-      const int m = e >> 4, r = e & 15;
-      a.out_f32[(size_t)m * a.out_ld + n0 + r] = tile[r * tld + m];
-    }
-    return;
-  }
-  if (a.epi == EPI_SWIGLU) {
-    // rows 2p (gate) and 2p+1 (up) -> output column n0/2 + p: one 8-wide chunk per m
-    for (int m = tid; m < M; m += nthr) {
-      float v[8];
+// Sum over the 16 lanes of a row group (lanes with the same tid / 16).
+__device__ __forceinline__ float sum16(float v) {
 #pragma unroll
-      for (int p = 0; p < 8; ++p) v[p] = silu(tile[(2 * p) * tld + m]) * tile[(2 * p + 1) * tld + m];
-      uint4 hi, lo;
-      split8(v, hi, lo);
-      const size_t o = chunked(m, n0 >> 1, a.u_ld);
-      *reinterpret_cast<uint4*>(a.u_hi + o) = hi;
-      *reinterpret_cast<uint4*>(a.u_lo + o) = lo;
+  for (int o = 8; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ unsigned long long max16(unsigned long long v) {
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) {
+    const unsigned long long w = __shfl_xor(v, o);
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+// Epilogue, one thread per output element.  y(r, m): the block's finished value
+// of weight row n0 + r for activation row m (waves summed in order, INT8 scale and
+// RMSNorm factor applied).  s_scale: the 16 rows' scales (for SwiGLU, whose
+// threads need two rows).
+template <int NW, int TLD>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, int n0,
+                                              const float (*red)[kGemmRows * TLD],
+                                              const float* s_inv, const float* s_scale,
+                                              const EpiPrefetch& pf) {
+  const int M = a.M;
+  const int tid = threadIdx.x;
+  constexpr int nthr = NW * 64;
+  auto y = [&](int r, int m) -> float {
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) v += red[w][r * TLD + m];
+    if (a.scale) v *= s_scale[r];
+    if (a.ss_in) v *= s_inv[m];
+    return v;
+  };
+  if (a.epi == EPI_SWIGLU) {
+    // rows 2p (gate) and 2p+1 (up) -> output column n0/2 + p; eight threads per chunk
+    for (int e = tid; e < 8 * M; e += nthr) {
+      const int m = e >> 3, p = e & 7;
+      const float v = silu(y(2 * p, m)) * y(2 * p + 1, m);
+      split_bf16(v, a.u_hi, a.u_lo, chunked(m, (n0 >> 1) + p, a.u_ld));
     }
     return;
   }
-  if (a.epi == EPI_HEAD && n0 < a.n_logits) {
-    for (int e = tid; e < R * M; e += nthr) {
-      const int m = e >> 4, r = e & 15;
-      a.logits[(size_t)m * a.logits_ld + n0 + r] = tile[r * tld + m];
-    }
-    if (n0 < a.argmax_range) {
-      // greedy-key candidate of these 16 rows (lowest index wins ties; NaN flagged)
-      for (int m = tid; m < M; m += nthr) {
-        unsigned long long best = 0;
-        bool nan = false;
-        for (int r = 0; r < R && n0 + r < a.argmax_range; ++r) {
-          const float y = tile[r * tld + m];
-          if (y != y) {
-            nan = true;
-            continue;
-          }
-          const unsigned long long k = greedy_key(y, n0 + r);
-          best = k > best ? k : best;
-        }
-        a.cand[(size_t)m * a.cand_ld + n0 / kKeyBlock] = best;
-        if (nan) atomicOr(a.status, QT_STATUS_NAN);
-      }
-    }
-    return;
-  }
-  // residual rows (EPI_RESID: x += y) or projection rows (EPI_HEAD: x = y)
+  const bool logits = a.epi == EPI_HEAD && n0 < a.n_logits;
   const int base = a.epi == EPI_RESID ? 0 : a.n_logits;
   const int c0 = n0 - base;
 #pragma unroll
-  for (int k = 0; k < kMaxResid; ++k) {
+  for (int k = 0; k < kMaxElem; ++k) {
     const int e = tid + k * nthr;
-    if (e >= R * M) break;
+    if (e >= kGemmRows * M) break;  // whole 16-lane groups leave together
     const int m = e >> 4, r = e & 15;
-    float v = tile[r * tld + m];
-    if (a.epi == EPI_RESID) v += pf.x[k];
-    a.out_f32[(size_t)m * a.out_ld + c0 + r] = v;
-    tile[r * tld + m] = v;
-  }
-  if (!a.u_gain) return;
-  __syncthreads();
-  // the next norm's input (two 8-wide chunks) and this block's sum of squares
-  for (int m = tid; m < M; m += nthr) {
-    float ss = 0.f;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      float v[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float x = tile[(8 * h + j) * tld + m];
-        ss = fmaf(x, x, ss);
-        v[j] = x * s_gain[8 * h + j];
+    float v = y(r, m);
+    if (a.epi == EPI_STORE) {
+      a.out_f32[(size_t)m * a.out_ld + n0 + r] = v;
+    } else if (logits) {
+      a.logits[(size_t)m * a.logits_ld + n0 + r] = v;
+      if (n0 < a.argmax_range) {
+        // greedy-key candidate of the 16 rows (lowest index wins ties; NaN flagged)
+        const bool valid = n0 + r < a.argmax_range;
+        const bool nan = valid && v != v;
+        unsigned long long key = (valid && !nan) ? greedy_key(v, n0 + r) : 0ull;
+        key = max16(key);
+        if (nan) atomicOr(a.status, QT_STATUS_NAN);
+        if (r == 0) a.cand[(size_t)m * a.cand_ld + n0 / kKeyBlock] = key;
       }
-      uint4 hi, lo;
-      split8(v, hi, lo);
-      const size_t o = chunked(m, c0 + 8 * h, a.u_ld);
-      *reinterpret_cast<uint4*>(a.u_hi + o) = hi;
-      *reinterpret_cast<uint4*>(a.u_lo + o) = lo;
+    } else {
+      // residual rows (EPI_RESID: x += y) or projection rows (EPI_HEAD: x = y), then
+      // the next norm's input and the 16 columns' sum of squares
+      if (a.epi == EPI_RESID) v += pf.x[k];
+      a.out_f32[(size_t)m * a.out_ld + c0 + r] = v;
+      if (a.u_gain) {
+        split_bf16(v * pf.gain, a.u_hi, a.u_lo, chunked(m, c0 + r, a.u_ld));
+        const float ss = sum16(v * v);
+        if (r == 0) a.ss_out[(size_t)(c0 / kGemmRows) * a.ss_out_ld + m] = ss;
+      }
     }
-    a.ss_out[(size_t)(c0 / R) * a.ss_out_ld + m] = ss;
   }
 }
 
@@ -233,8 +207,9 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs a) {
   constexpr int SUB = I8 ? 2 : 1;        // 32-wide MFMA K substeps per packed K step
   constexpr int MV = MT ? 16 * MT : 2;   // activation rows held per lane group
   __shared__ float red[NW][kGemmRows * TLD];
+  __shared__ float s_ssp[NW * 64];
   __shared__ float s_inv[64];
-  __shared__ float s_gain[kGemmRows];
+  __shared__ float s_scale[kGemmRows];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i = lane & 15, q = lane >> 4;
   const int rt = (a.row0 >> 4) + blockIdx.x;
@@ -246,9 +221,8 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs a) {
   const uint4* L = reinterpret_cast<const uint4*>(a.act_lo);
   const bool has_lo = a.act_lo != nullptr;
 
-  float ssr[kSsRegs];
-  int ss_per_lane = 0;
-  if (a.ss_in) ss_prefetch(a, wave, NW, ssr, ss_per_lane);
+  SsPrefetch ssp;
+  if (a.ss_in) ss_prefetch(a, ssp);
   EpiPrefetch pf;
   epi_prefetch(a, n0, pf);
 
@@ -263,7 +237,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs a) {
       for (int g = 0; g < G; ++g) {
         const int j = j0 + NW * g;
         const bool ok = j < ksteps;
-        w[g] = ok ? W[(size_t)j * 64] : make_uint4(0, 0, 0, 0);
+        w[g] = ok ? load_stream(W + (size_t)j * 64) : make_uint4(0, 0, 0, 0);
 #pragma unroll
         for (int sb = 0; sb < SUB; ++sb) {
           const size_t c = (size_t)(j * SUB + sb) * 4 + q;
@@ -307,7 +281,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs a) {
       for (int g = 0; g < G; ++g) {
         const int j = j0 + NW * g;
         const bool ok = j < ksteps;
-        w[g] = ok ? W[(size_t)j * 64] : make_uint4(0, 0, 0, 0);
+        w[g] = ok ? load_stream(W + (size_t)j * 64) : make_uint4(0, 0, 0, 0);
 #pragma unroll
         for (int sb = 0; sb < SUB; ++sb) {
           const size_t c = (size_t)(j * SUB + sb) * 4 + q;
@@ -337,18 +311,29 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs a) {
       if (q == 0) red[wave][i * TLD + m] = v;
     }
   }
-  if (a.ss_in) ss_finish(a, wave, NW, ssr, ss_per_lane, s_inv);
-  if (tid < kGemmRows) s_gain[tid] = pf.gain;
+  if (a.ss_in) s_ssp[tid] = ssp.on ? ss_partial(a, ssp) : 0.f;
+  if (tid < kGemmRows) s_scale[tid] = pf.scale;
   __syncthreads();
-  for (int e = tid; e < kGemmRows * M; e += NW * 64) {
-    const int m = e >> 4, r = e & 15;
-    float s = 0.f;
-#pragma unroll
-    for (int v = 0; v < NW; ++v) s += red[v][r * TLD + m];
-    red[0][r * TLD + m] = s;
+  if (a.ss_in) {
+    // row m's G partials, summed in a fixed order: by one thread when there are
+    // few of them (many rows), else by a wave (tree sum over its lanes)
+    if (ssp.G <= 32) {
+      if (tid < M) {
+        float ss = 0.f;
+        for (int g = 0; g < ssp.G; ++g) ss += s_ssp[g * M + tid];
+        s_inv[tid] = 1.0f / sqrtf(ss / (float)a.K + a.norm_eps);
+      }
+    } else {
+      for (int m = wave; m < M; m += NW) {
+        float ss = 0.f;
+        for (int g = lane; g < ssp.G; g += 64) ss += s_ssp[g * M + m];
+        ss = wave_sum(ss);
+        if (lane == 0) s_inv[m] = 1.0f / sqrtf(ss / (float)a.K + a.norm_eps);
+      }
+    }
+    __syncthreads();
   }
-  __syncthreads();
-  gemm_epilogue(a, n0, red[0], TLD, s_inv, pf, s_gain);
+  gemm_epilogue<NW, TLD>(a, n0, red, s_inv, s_scale, pf);
 }
 
 template <bool I8>
