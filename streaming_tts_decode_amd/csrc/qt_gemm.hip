@@ -130,7 +130,8 @@ __device__ __forceinline__ unsigned long long max16(unsigned long long v) {
 // Epilogue, one thread per output element.  y(r, m): the block's finished value
 // of weight row n0 + r for activation row m (waves summed in order, INT8 scale and
 // RMSNorm factor applied).  s_scale: the 16 rows' scales (for SwiGLU, whose
-// threads need two rows).
+// threads need two rows).  TLD: row stride of the partial tiles in LDS, odd so
+// that the 16 rows a thread group reads fall in distinct banks.
 template <int NW, int TLD>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, int n0,
                                               const float (*red)[kGemmRows * TLD],
@@ -202,8 +203,8 @@ __device__ __forceinline__ uint4 i8_to_bf16x8(const uint4& w, int sb) {
 // One block: weight rows [n0, n0+16) over all of K.  NW waves, MT 16-row MFMA
 // activation tiles (MT == 0: VALU form for M <= 2), G K steps per load group.
 template <int NW, int MT, int G, bool I8>
-__global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs a) {
-  constexpr int TLD = MT ? 16 * MT : 2;  // tile columns (activation rows)
+__global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs args, int msplit) {
+  constexpr int TLD = (MT ? 16 * MT : 2) + 1;  // tile row stride: activation rows + 1 (odd)
   constexpr int SUB = I8 ? 2 : 1;        // 32-wide MFMA K substeps per packed K step
   constexpr int MV = MT ? 16 * MT : 2;   // activation rows held per lane group
   __shared__ float red[NW][kGemmRows * TLD];
@@ -212,7 +213,32 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs a) {
   __shared__ float s_scale[kGemmRows];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i = lane & 15, q = lane >> 4;
-  const int rt = (a.row0 >> 4) + blockIdx.x;
+  // block -> (weight tile, activation-row part).  With msplit > 1, blocks b and
+  // b + 8, b + 16, ... (the same XCD under round-robin dispatch) share a tile.
+  int rtl = blockIdx.x, mh = 0;
+  if (msplit > 1) {
+    const int x = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    mh = slot % msplit;
+    rtl = (slot / msplit) * 8 + x;
+  }
+  // this block's rows m0 .. m0 + M-1 of the activations, as a shifted view
+  GemmArgs a = args;
+  {
+    const int m0 = mh * (MT ? 16 * MT : 2);
+    a.M = min(args.M - m0, MT ? 16 * MT : 2);
+    const size_t c8 = (size_t)m0 * 8;
+    a.act += c8;
+    if (a.act_lo) a.act_lo += c8;
+    if (a.ss_in) a.ss_in += m0;
+    a.out_f32 += (size_t)m0 * a.out_ld;
+    if (a.logits) a.logits += (size_t)m0 * a.logits_ld;
+    if (a.cand) a.cand += (size_t)m0 * a.cand_ld;
+    if (a.u_hi) a.u_hi += c8;
+    if (a.u_lo) a.u_lo += c8;
+    if (a.ss_out) a.ss_out += m0;
+  }
+  if (a.M <= 0) return;  // (plan_gemm never makes an empty part; whole block leaves)
+  const int rt = (a.row0 >> 4) + rtl;
   const int n0 = rt * kGemmRows;
   const int M = a.M, ld = a.act_ld;
   const int ksteps = a.K / (32 * SUB);
@@ -338,12 +364,13 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs a) {
 
 template <bool I8>
 hipError_t gemm_dispatch(const GemmArgs& a, const GemmPlan& p, hipStream_t s) {
-  const dim3 grid(p.row_blocks), block(64 * p.nw);
+  const dim3 grid(p.row_blocks * p.msplit), block(64 * p.nw);
+  const int ms = p.msplit;
   switch (p.mt) {
-    case 0: launch_kernel((k_gemm<16, 0, 2, I8>), grid, block, s, a); break;
-    case 1: launch_kernel((k_gemm<8, 1, 2, I8>), grid, block, s, a); break;
-    case 2: launch_kernel((k_gemm<8, 2, 2, I8>), grid, block, s, a); break;
-    default: launch_kernel((k_gemm<8, 4, 1, I8>), grid, block, s, a); break;
+    case 0: launch_kernel((k_gemm<16, 0, 2, I8>), grid, block, s, a, ms); break;
+    case 1: launch_kernel((k_gemm<8, 1, 2, I8>), grid, block, s, a, ms); break;
+    case 2: launch_kernel((k_gemm<8, 2, 2, I8>), grid, block, s, a, ms); break;
+    default: launch_kernel((k_gemm<8, 4, 1, I8>), grid, block, s, a, ms); break;
   }
   return hipGetLastError();
 }
@@ -373,22 +400,27 @@ __global__ __launch_bounds__(256) void k_untile_i8(const int8_t* tiled, int rows
 
 }  // namespace
 
-// Launch shape for nrows weight rows, K columns, M activation rows.
+// Launch shape for nrows weight rows, K columns, M activation rows.  Small weight
+// matrices with many activation rows split the rows over 2 or 4 blocks per tile,
+// aiming at >= 256 blocks.
 GemmPlan plan_gemm(int nrows, int K, int M, bool i8) {
   (void)K;
   (void)i8;
   GemmPlan p{};
-  if (M <= 2) {
-    p.nw = 16, p.mt = 0, p.g = 2;
-  } else if (M <= 16) {
-    p.nw = 8, p.mt = 1, p.g = 2;
-  } else if (M <= 32) {
-    p.nw = 8, p.mt = 2, p.g = 2;
-  } else {
-    p.nw = 8, p.mt = 4, p.g = 1;
-  }
   p.rows_per_block = kGemmRows;
   p.row_blocks = nrows / kGemmRows;
+  p.msplit = 1;
+  if (M <= 2) {
+    p.nw = 16, p.mt = 0, p.g = 2;
+    return p;
+  }
+  const int tiles = (M + 15) / 16;
+  if (tiles > 1 && p.row_blocks % 8 == 0)
+    while (p.msplit * 2 <= tiles && p.row_blocks * p.msplit < 256) p.msplit *= 2;
+  const int mt = (tiles + p.msplit - 1) / p.msplit;
+  p.nw = 8;
+  p.mt = mt <= 1 ? 1 : (mt <= 2 ? 2 : 4);
+  p.g = p.mt == 4 ? 1 : 2;
   return p;
 }
 

@@ -109,9 +109,12 @@ inline void launch_kernel(Kernel kernel, dim3 grid, dim3 block, hipStream_t s, A
 
 // Launch shape chosen for one GEMM (see plan_gemm): 16 weight rows per block, nw
 // waves splitting K; mt > 0: MFMA over mt 16-row activation tiles, mt == 0: VALU
-// dot products (M <= 2); g = K steps per load group.
+// dot products (M <= 2); g = K steps per load group.  msplit > 1: the activation
+// rows are split over msplit blocks per weight tile (more blocks for GEMMs with
+// few weight rows); the blocks sharing a tile run on one XCD, so the tile is read
+// from HBM once.
 struct GemmPlan {
-  int nw, mt, g;
+  int nw, mt, g, msplit;
   int rows_per_block, row_blocks;
 };
 
