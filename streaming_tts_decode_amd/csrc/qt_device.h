@@ -66,56 +66,83 @@ __device__ __forceinline__ int key_index(unsigned long long k) {
   return (int)(0xffffffffu - (uint32_t)(k & 0xffffffffull));
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+// ---- cross-lane reductions (every participating lane must be active)
+// DPP row steps within 16-lane rows: quad_perm [1,0,3,2], quad_perm [2,3,0,1],
+// row_half_mirror, row_mirror.  After the four steps every lane of a row holds the
+// row's total, with the same bits in every lane (each step adds a lane's value to
+// its mirror's, a commutative pair).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v)));
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp_f32<kDppXor1>(v);
+  v += dpp_f32<kDppXor2>(v);
+  v += dpp_f32<kDppHalfMirror>(v);
+  v += dpp_f32<kDppMirror>(v);
   return v;
+}
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, dpp_f32<kDppXor1>(v));
+  v = fmaxf(v, dpp_f32<kDppXor2>(v));
+  v = fmaxf(v, dpp_f32<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_f32<kDppMirror>(v));
+  return v;
+}
+template <int CTRL>
+__device__ __forceinline__ void max_u64_step(uint32_t& hi, uint32_t& lo) {
+  const uint32_t oh = dpp_u32<CTRL>(hi), ol = dpp_u32<CTRL>(lo);
+  const bool take = oh > hi || (oh == hi && ol > lo);
+  hi = take ? oh : hi;
+  lo = take ? ol : lo;
+}
+__device__ __forceinline__ unsigned long long row_max16_u64(unsigned long long k) {
+  uint32_t hi = (uint32_t)(k >> 32), lo = (uint32_t)k;
+  max_u64_step<kDppXor1>(hi, lo);
+  max_u64_step<kDppXor2>(hi, lo);
+  max_u64_step<kDppHalfMirror>(hi, lo);
+  max_u64_step<kDppMirror>(hi, lo);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+// Sum over lanes l, l^16, l^32 and l^48 with the gfx950 lane-swap instructions;
+// all four lanes receive the same total.
+__device__ __forceinline__ float sum_q4(float v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
+  v = __int_as_float(p[0]) + __int_as_float(p[1]);
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+  return __int_as_float(q[0]) + __int_as_float(q[1]);
+}
+
+__device__ __forceinline__ float lane_f32(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+// Wave-wide reductions: row totals, then the four rows combined as uniform values.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row_sum16(v);
+  return (lane_f32(v, 0) + lane_f32(v, 16)) + (lane_f32(v, 32) + lane_f32(v, 48));
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  v = row_max16(v);
+  return fmaxf(fmaxf(lane_f32(v, 0), lane_f32(v, 16)), fmaxf(lane_f32(v, 32), lane_f32(v, 48)));
 }
 __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
+  v = row_max16_u64(v);
+  unsigned long long best = 0;
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    unsigned long long w = __shfl_xor(v, o);
-    v = w > v ? w : v;
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 16 * r);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 16 * r);
+    const unsigned long long k = ((unsigned long long)hi << 32) | lo;
+    best = k > best ? k : best;
   }
-  return v;
-}
-
-template <int V>
-struct Log2 {
-  static constexpr int value = 1 + Log2<V / 2>::value;
-};
-template <>
-struct Log2<1> {
-  static constexpr int value = 0;
-};
-
-// Sum V values held by every lane over the 64 lanes of the wave.  After the
-// call, lane l holds the total of value index (l >> (6 - log2 V)).  Halving
-// exchange: each step sends half of the remaining values to the partner lane.
-template <int V>
-__device__ __forceinline__ float transpose_reduce(float (&v)[V], int lane) {
-  constexpr int P = Log2<V>::value;
-#pragma unroll
-  for (int s = 0; s < P; ++s) {
-    const int h = (V >> s) >> 1;
-    const int o = 32 >> s;
-    const bool up = (lane & o) != 0;
-#pragma unroll
-    for (int i = 0; i < h; ++i) {
-      const float send = up ? v[i] : v[i + h];
-      const float keep = up ? v[i + h] : v[i];
-      v[i] = keep + __shfl_xor(send, o);
-    }
-  }
-  float r = v[0];
-#pragma unroll
-  for (int o = 32 >> P; o >= 1; o >>= 1) r += __shfl_xor(r, o);
-  return r;
+  return best;
 }
 
 // Device-coherent (agent-scope) store / load: performed at the point where all

@@ -112,21 +112,6 @@ __device__ __forceinline__ void epi_prefetch(const GemmArgs& a, int n0, EpiPrefe
                : 0.f;
 }
 
-// Sum over the 16 lanes of a row group (lanes with the same tid / 16).
-__device__ __forceinline__ float sum16(float v) {
-#pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-__device__ __forceinline__ unsigned long long max16(unsigned long long v) {
-#pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) {
-    const unsigned long long w = __shfl_xor(v, o);
-    v = w > v ? w : v;
-  }
-  return v;
-}
-
 // Epilogue, one thread per output element.  y(r, m): the block's finished value
 // of weight row n0 + r for activation row m (waves summed in order, INT8 scale and
 // RMSNorm factor applied).  s_scale: the 16 rows' scales (for SwiGLU, whose
@@ -175,7 +160,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, int n0,
         const bool valid = n0 + r < a.argmax_range;
         const bool nan = valid && v != v;
         unsigned long long key = (valid && !nan) ? greedy_key(v, n0 + r) : 0ull;
-        key = max16(key);
+        key = row_max16_u64(key);
         if (nan) atomicOr(a.status, QT_STATUS_NAN);
         if (r == 0) a.cand[(size_t)m * a.cand_ld + n0 / kKeyBlock] = key;
       }
@@ -186,7 +171,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, int n0,
       a.out_f32[(size_t)m * a.out_ld + c0 + r] = v;
       if (a.u_gain) {
         split_bf16(v * pf.gain, a.u_hi, a.u_lo, chunked(m, c0 + r, a.u_ld));
-        const float ss = sum16(v * v);
+        const float ss = row_sum16(v * v);
         if (r == 0) a.ss_out[(size_t)(c0 / kGemmRows) * a.ss_out_ld + m] = ss;
       }
     }
@@ -331,9 +316,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs args, int msplit) {
     }
 #pragma unroll
     for (int m = 0; m < MV; ++m) {
-      float v = acc[m];
-      v += __shfl_xor(v, 16);
-      v += __shfl_xor(v, 32);
+      const float v = sum_q4(acc[m]);
       if (q == 0) red[wave][i * TLD + m] = v;
     }
   }

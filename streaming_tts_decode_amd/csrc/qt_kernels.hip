@@ -170,11 +170,8 @@ __global__ __launch_bounds__(256) void k_attn_paged(AttnPagedArgs a, float theta
       s0 = fmaf(q0[e], kf[e], s0);
       s1 = fmaf(q1[e], kf[e], s1);
     }
-#pragma unroll
-    for (int o = 8; o >= 1; o >>= 1) {
-      s0 += __shfl_xor(s0, o);
-      s1 += __shfl_xor(s1, o);
-    }
+    s0 = row_sum16(s0);
+    s1 = row_sum16(s1);
     if (c == 0) {
       sc[0][g * kPage + pi] = (t < t1) ? s0 : -INFINITY;
       sc[1][g * kPage + pi] = (t < t1) ? s1 : -INFINITY;
@@ -231,10 +228,8 @@ __global__ __launch_bounds__(256) void k_attn_paged(AttnPagedArgs a, float theta
   // reduce over the 4 positions of the wave (lanes c, c+16, c+32, c+48)
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    a0[e] += __shfl_xor(a0[e], 16);
-    a1[e] += __shfl_xor(a1[e], 16);
-    a0[e] += __shfl_xor(a0[e], 32);
-    a1[e] += __shfl_xor(a1[e], 32);
+    a0[e] = sum_q4(a0[e]);
+    a1[e] = sum_q4(a1[e]);
   }
   if (lane < 16) {
 #pragma unroll
@@ -368,8 +363,7 @@ __global__ __launch_bounds__(256) void k_attn_pred(AttnPredArgs a, float theta_l
       float s = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) s = fmaf(qs[i][hh][8 * c + e], kf[e], s);
-#pragma unroll
-      for (int o = 8; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+      s = row_sum16(s);
       if (c == 0) sc[i][hh][t] = (t <= a.pos0 + i) ? s : -INFINITY;
     }
   }
@@ -395,8 +389,7 @@ __global__ __launch_bounds__(256) void k_attn_pred(AttnPredArgs a, float theta_l
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         acc[e] = w * vf[e];
-        acc[e] += __shfl_xor(acc[e], 16);
-        acc[e] += __shfl_xor(acc[e], 32);
+        acc[e] = sum_q4(acc[e]);
       }
       if (lane < 16) {
 #pragma unroll
