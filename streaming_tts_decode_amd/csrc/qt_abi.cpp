@@ -238,7 +238,7 @@ qt_status check_cfg(const qt_model_cfg* c) {
 
 // ------------------------------------------------------------------ workspace layout
 struct Ws {
-  size_t x_t, x_p, ss_t, ss_p, ut, ut_lo, up, up_lo, qkv, o, o_lo, ffn, ffn_lo, pk, pv, part, cnt,
+  size_t x_t, x_p, ss_t, ss_p, ut, up, qkv, o, ffn, pk, pv, part, cnt,
       cand, total;
   int qkv_ld, o_ld, f_ld;
   int cand_ld;        // greedy-key candidates per (codebook, session)
@@ -271,14 +271,10 @@ Ws make_ws(const qt_model_cfg& c, int B, int max_pages) {
   w.ss_t = take((size_t)(t.hidden / kGemmRows) * B * 4);
   w.ss_p = take((size_t)(p.hidden / kGemmRows) * M * 4);
   w.ut = take((size_t)B * t.hidden * 2);
-  w.ut_lo = take((size_t)B * t.hidden * 2);
   w.up = take((size_t)M * p.hidden * 2);
-  w.up_lo = take((size_t)M * p.hidden * 2);
   w.qkv = take((size_t)M * w.qkv_ld * 4);
   w.o = take((size_t)M * w.o_ld * 2);
-  w.o_lo = take((size_t)M * w.o_ld * 2);
   w.ffn = take((size_t)M * w.f_ld * 2);
-  w.ffn_lo = take((size_t)M * w.f_ld * 2);
   w.pk_sess = (long long)p.layers * c.n_codebooks * p.n_kv_heads * p.head_dim;
   w.pk = take((size_t)B * w.pk_sess * 2);
   w.pv = take((size_t)B * w.pk_sess * 2);
@@ -312,9 +308,9 @@ namespace {
 
 const uint16_t* vp(const qt_model* m, size_t off) { return (const uint16_t*)(m->base + off); }
 
-// GEMM over a packed matrix with hi/lo bf16 activations (act_lo may be null).
-GemmArgs gemm_act(const qt_model* m, const MatSlot& s, const uint16_t* act,
-                  const uint16_t* act_lo, int act_ld, int M, uint32_t* status) {
+// GEMM over a packed matrix with chunked half activations of act_ld rows.
+GemmArgs gemm_act(const qt_model* m, const MatSlot& s, const uint16_t* act, int act_ld, int M,
+                  uint32_t* status) {
   GemmArgs a{};
   a.W = m->base + s.w;
   a.scale = m->i8 ? (const float*)(m->base + s.s) : nullptr;
@@ -323,19 +319,17 @@ GemmArgs gemm_act(const qt_model* m, const MatSlot& s, const uint16_t* act,
   a.row0 = 0;
   a.nrows = s.N;
   a.act = act;
-  a.act_lo = act_lo;
   a.act_ld = act_ld;
   a.M = M;
   a.status = status;
   return a;
 }
 
-// GEMM whose input is an RMSNorm: u = hi/lo(x * gain) as left by the producer of x,
+// GEMM whose input is an RMSNorm: u = half(x * gain) as left by the producer of x,
 // whose sums of squares sit in `slots` slots of ss (stride ss_ld).
-GemmArgs gemm_norm(const qt_model* m, const MatSlot& s, const uint16_t* u, const uint16_t* u_lo,
-                   int u_ld, const float* ss, int ss_ld, int slots, float eps, int M,
-                   uint32_t* status) {
-  GemmArgs a = gemm_act(m, s, u, u_lo, u_ld, M, status);
+GemmArgs gemm_norm(const qt_model* m, const MatSlot& s, const uint16_t* u, int u_ld,
+                   const float* ss, int ss_ld, int slots, float eps, int M, uint32_t* status) {
+  GemmArgs a = gemm_act(m, s, u, u_ld, M, status);
   a.ss_in = ss;
   a.ss_in_ld = ss_ld;
   a.ss_in_slots = slots;
@@ -409,14 +403,10 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
   float* ss_t = (float*)(ws + w.ss_t);
   float* ss_p = (float*)(ws + w.ss_p);
   uint16_t* ut = (uint16_t*)(ws + w.ut);
-  uint16_t* ut_lo = (uint16_t*)(ws + w.ut_lo);
   uint16_t* up = (uint16_t*)(ws + w.up);
-  uint16_t* up_lo = (uint16_t*)(ws + w.up_lo);
   float* qkv = (float*)(ws + w.qkv);
   uint16_t* o = (uint16_t*)(ws + w.o);
-  uint16_t* o_lo = (uint16_t*)(ws + w.o_lo);
   uint16_t* ffn = (uint16_t*)(ws + w.ffn);
-  uint16_t* ffn_lo = (uint16_t*)(ws + w.ffn_lo);
   unsigned long long* cand = (unsigned long long*)(ws + w.cand);
   const int cand_ld = w.cand_ld;
   const int ld_t = B, ld_p = 2 * B;  // rows of the chunked activation buffers
@@ -476,8 +466,7 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
   fb.x_t = x_t;
   fb.ss_t = ss_t;
   fb.gain = vp(m, m->plan.tl[0].in_norm);
-  fb.u_hi = ut;
-  fb.u_lo = ut_lo;
+  fb.u = ut;
   fb.h_in = (const uint16_t*)in->h_in;
   fb.cand = cand;
   fb.cand_ld = cand_ld;
@@ -491,58 +480,56 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
     QT_LAUNCH(launch_gemm(g, st));
     return ok();
   };
-  // A GEMM that writes residual / projection rows v also writes u = hi/lo(v * gain)
+  // A GEMM that writes residual / projection rows v also writes u = half(v * gain)
   // for the next RMSNorm and one sum-of-squares slot per row block; returns the
   // number of rows per block.
-  auto produce = [&](GemmArgs& g, const uint16_t* gain, uint16_t* u, uint16_t* u_lo, int u_ld,
-                     float* ss, int ss_ld) -> int {
+  auto produce = [&](GemmArgs& g, const uint16_t* gain, uint16_t* u, int u_ld, float* ss,
+                     int ss_ld) -> int {
     g.u_gain = gain;
-    g.u_hi = u;
-    g.u_lo = u_lo;
+    g.u = u;
     g.u_ld = u_ld;
     g.ss_out = ss;
     g.ss_out_ld = ss_ld;
     return plan_gemm(g.nrows, g.K, g.M, g.scale != nullptr).rows_per_block;
   };
 
-  // One decoder layer over M rows of residual x (row stride = hidden).  u / u_lo:
-  // the normalised-input buffer of the stack; ld: rows of the stack's chunked
+  // One decoder layer over M rows of residual x (row stride = hidden).  u: the
+  // normalised-input buffer of the stack; ld: rows of the stack's chunked
   // activation buffers; ss / ss_ld: sums of squares of x; *slots: how many slots
   // the last producer of x left; next_gain: gain of the norm that follows the layer.
-  auto layer = [&](const qt_decoder_cfg& d, const LayerSlots& L, float* x, uint16_t* u,
-                   uint16_t* u_lo, int ld, float* ss, int ss_ld, int* slots,
-                   const uint16_t* next_gain, int M, auto&& attention) -> qt_status {
+  auto layer = [&](const qt_decoder_cfg& d, const LayerSlots& L, float* x, uint16_t* u, int ld,
+                   float* ss, int ss_ld, int* slots, const uint16_t* next_gain, int M,
+                   auto&& attention) -> qt_status {
     qt_status r;
-    GemmArgs g = gemm_norm(m, L.qkv, u, u_lo, ld, ss, ss_ld, *slots, d.rms_eps, M, out->status);
+    GemmArgs g = gemm_norm(m, L.qkv, u, ld, ss, ss_ld, *slots, d.rms_eps, M, out->status);
     g.epi = EPI_STORE;
     g.out_f32 = qkv;
     g.out_ld = w.qkv_ld;
     if ((r = run(g))) return r;
     if ((r = attention())) return r;
-    g = gemm_act(m, L.o, o, o_lo, ld, M, out->status);
+    g = gemm_act(m, L.o, o, ld, M, out->status);
     g.epi = EPI_RESID;
     g.out_f32 = x;
     g.out_ld = d.hidden;
-    *slots = d.hidden / produce(g, vp(m, L.post_norm), u, u_lo, ld, ss, ss_ld);
+    *slots = d.hidden / produce(g, vp(m, L.post_norm), u, ld, ss, ss_ld);
     if ((r = run(g))) return r;
-    g = gemm_norm(m, L.gu, u, u_lo, ld, ss, ss_ld, *slots, d.rms_eps, M, out->status);
+    g = gemm_norm(m, L.gu, u, ld, ss, ss_ld, *slots, d.rms_eps, M, out->status);
     g.epi = EPI_SWIGLU;
-    g.u_hi = ffn;
-    g.u_lo = ffn_lo;
+    g.u = ffn;
     g.u_ld = ld;
     if ((r = run(g))) return r;
-    g = gemm_act(m, L.down, ffn, ffn_lo, ld, M, out->status);
+    g = gemm_act(m, L.down, ffn, ld, M, out->status);
     g.epi = EPI_RESID;
     g.out_f32 = x;
     g.out_ld = d.hidden;
-    *slots = d.hidden / produce(g, next_gain, u, u_lo, ld, ss, ss_ld);
+    *slots = d.hidden / produce(g, next_gain, u, ld, ss, ss_ld);
     return run(g);
   };
   int t_slots = 1, p_slots = 1;
   const int ss_t_ld = B, ss_p_ld = 2 * B;
 
   // predictor mode: the entry kernel copies h_in into ut (no lo part, no norm)
-  GemmArgs head = gemm_act(m, m->plan.t_head, ut, nullptr, ld_t, B, out->status);
+  GemmArgs head = gemm_act(m, m->plan.t_head, ut, ld_t, B, out->status);
 
   if (talker) {
     // pages per split: about 1024 blocks over the page table, at most 8 pages each
@@ -555,7 +542,7 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
       const LayerSlots& L = m->plan.tl[l];
       const uint16_t* next_gain =
           vp(m, l + 1 < T.layers ? m->plan.tl[l + 1].in_norm : m->plan.t_final);
-      qt_status s = layer(T, L, x_t, ut, ut_lo, ld_t, ss_t, ss_t_ld, &t_slots, next_gain, B,
+      qt_status s = layer(T, L, x_t, ut, ld_t, ss_t, ss_t_ld, &t_slots, next_gain, B,
                           [&]() -> qt_status {
         AttnPagedArgs a{};
         a.qkv = qkv;
@@ -576,7 +563,6 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
         a.part = (float*)(ws + w.part);
         a.counters = cnt;
         a.o = o;
-        a.o_lo = o_lo;
         a.o_ld = ld_t;
         a.status = out->status;
         QT_MARK(QT_KERNEL_ATTN_PAGED, "k_attn_paged", B, nullptr);
@@ -586,7 +572,7 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
       if (s) return s;
     }
     cur_layer = -1;
-    head = gemm_norm(m, m->plan.t_head, ut, ut_lo, ld_t, ss_t, ss_t_ld, t_slots, T.rms_eps, B,
+    head = gemm_norm(m, m->plan.t_head, ut, ld_t, ss_t, ss_t_ld, t_slots, T.rms_eps, B,
                      out->status);
     head.nrows = mode == QT_MODE_TALKER ? c.talker_vocab : c.talker_vocab + Pd.hidden;
   } else {
@@ -604,8 +590,7 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
   head.out_f32 = x_p;  // projection rows land in predictor rows [0, B)
   head.out_ld = Pd.hidden;
   if (mode != QT_MODE_TALKER)
-    p_slots = Pd.hidden / produce(head, vp(m, m->plan.pl[0].in_norm), up, up_lo, ld_p, ss_p,
-                                  ss_p_ld);
+    p_slots = Pd.hidden / produce(head, vp(m, m->plan.pl[0].in_norm), up, ld_p, ss_p, ss_p_ld);
   {
     qt_status s = run(head);
     if (s) return s;
@@ -633,8 +618,7 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
       if (k > 1) p_slots = 1;  // rows [0, B) are all new
       e.ss_slots = p_slots;
       e.gain = vp(m, m->plan.pl[0].in_norm);
-      e.u_hi = up;
-      e.u_lo = up_lo;
+      e.u = up;
       e.u_ld = ld_p;
       e.row_off = emb_row;
       e.status = out->status;
@@ -647,7 +631,7 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
         const LayerSlots& L = m->plan.pl[l];
         const uint16_t* next_gain =
             vp(m, l + 1 < Pd.layers ? m->plan.pl[l + 1].in_norm : m->plan.p_final);
-        qt_status s = layer(Pd, L, x_p, up, up_lo, ld_p, ss_p, ss_p_ld, &p_slots, next_gain, M,
+        qt_status s = layer(Pd, L, x_p, up, ld_p, ss_p, ss_p_ld, &p_slots, next_gain, M,
                             [&]() -> qt_status {
           AttnPredArgs a{};
           a.qkv = qkv;
@@ -665,7 +649,6 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
           a.pos0 = (k == 1) ? 0 : k;
           a.n_new = (k == 1) ? 2 : 1;
           a.o = o;
-          a.o_lo = o_lo;
           a.o_ld = ld_p;
           QT_MARK(QT_KERNEL_ATTN_PRED, "k_attn_pred", B, nullptr);
           QT_LAUNCH(launch_attn_pred(a, Pd.rope_theta, st));
@@ -675,9 +658,8 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
       }
       cur_layer = -1;
       // the step's head reads the last position: rows [emb_row, emb_row + B)
-      GemmArgs g = gemm_norm(m, m->plan.heads[k - 1], up + (size_t)emb_row * 8,
-                             up_lo + (size_t)emb_row * 8, ld_p, ss_p + emb_row, ss_p_ld, p_slots,
-                             Pd.rms_eps, B, out->status);
+      GemmArgs g = gemm_norm(m, m->plan.heads[k - 1], up + (size_t)emb_row * 8, ld_p,
+                             ss_p + emb_row, ss_p_ld, p_slots, Pd.rms_eps, B, out->status);
       g.epi = EPI_HEAD;
       g.logits = out->logits_pred + (size_t)(k - 1) * c.code_vocab;
       g.logits_ld = (ncb - 1) * c.code_vocab;

@@ -1,4 +1,4 @@
-// Device-side helpers shared by the gfx950 kernels (bf16 conversions, dot
+// Device-side helpers shared by the gfx950 kernels (bf16 / fp16 conversions, dot
 // products, wave reductions, device-coherent loads/stores, greedy keys).
 #pragma once
 #include <hip/hip_runtime.h>
@@ -10,6 +10,8 @@ namespace dev {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kInvSqrtHd = 0.08838834764831845f;  // 1/sqrt(128)
@@ -26,31 +28,27 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
   return (uint16_t)(u >> 16);
 }
 
-// x ~ hi + lo with both parts bfloat16 (x - hi is exact in fp32).
-__device__ __forceinline__ void split_bf16(float x, uint16_t* hi, uint16_t* lo, size_t i) {
-  const uint16_t h = f2bf(x);
-  hi[i] = h;
-  lo[i] = f2bf(x - bf2f(h));
+// float <-> IEEE half bits (round to nearest even; out of range -> inf).
+__device__ __forceinline__ uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+__device__ __forceinline__ float h2f(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+
+// fp16 dot products with fp32 accumulation (v_dot2_f32_f16).
+__device__ __forceinline__ float dot2h(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c, false);
+}
+__device__ __forceinline__ float dot8h(const uint4& w, const uint4& x, float c) {
+  c = dot2h(w.x, x.x, c);
+  c = dot2h(w.y, x.y, c);
+  c = dot2h(w.z, x.z, c);
+  return dot2h(w.w, x.w, c);
 }
 
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
-                                         __builtin_bit_cast(bf16x2, b), c, false);
-}
-
-__device__ __forceinline__ float dot8(const uint4& w, const uint4& x, float c) {
-  c = dot2(w.x, x.x, c);
-  c = dot2(w.y, x.y, c);
-  c = dot2(w.z, x.z, c);
-  return dot2(w.w, x.w, c);
-}
-
-// Two signed int8 (bytes 2i, 2i+1 of word) -> packed bf16 pair.  |q| <= 127 is
-// exact in bfloat16, so taking the high half of the float is exact.
-__device__ __forceinline__ uint32_t i8pair_to_bf16x2(uint32_t word, int i) {
+// Two signed int8 (bytes 2i, 2i+1 of word) -> packed fp16 pair (exact: integers
+// up to 2048 are exact in fp16, so rounding toward zero changes nothing).
+__device__ __forceinline__ uint32_t i8pair_to_f16x2(uint32_t word, int i) {
   const float lo = (float)(int)(int8_t)(word >> (16 * i));
   const float hi = (float)(int)(int8_t)(word >> (16 * i + 8));
-  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
 }
 
 // Greedy key: order-preserving float bits in the high word, (~index) in the low

@@ -11,22 +11,21 @@
 //
 // Memory layouts (see qt_internal.h) make every load a contiguous piece:
 //  * weights are packed in 1 KB tiles holding exactly the 16x32 A operand of a
-//    v_mfma_f32_16x16x32_bf16 (bf16) or of two of them (int8), so one wave load
+//    v_mfma_f32_16x16x32_f16 (half) or of two of them (int8), so one wave load
 //    instruction reads 1 KB of contiguous memory;
 //  * activations are "chunked", [K/8][rows][8], so the 16 rows of an 8-wide K
 //    chunk that one MFMA B operand needs are 256 contiguous bytes.
 // Lane (i, q) (i = lane & 15, q = lane >> 4) holds weight row i, K elements
 // [8q, 8q+8) of each 32-wide step.
 //  * MFMA form (M >= 3): the activation rows are the 16-column B operand tiles.
-//  * VALU form (M <= 2): each lane forms v_dot2_f32_bf16 products of its weight
+//  * VALU form (M <= 2): each lane forms v_dot2_f32_f16 products of its weight
 //    piece with the (broadcast) activation piece of the same K range; the four
 //    lanes of a row are summed with cross-lane adds.
 //
-// Activations are a bf16 hi/lo pair (hi + lo carries ~16 bits of the fp32 value),
-// each multiplied by the weights.  RMSNorm is split between producer and consumer:
-// the GEMM (or kernel) that writes a residual row v also writes hi/lo(v * gain)
-// and the 16-row block's sum of squares; the consuming GEMM multiplies its
-// outputs by 1/rms from those sums.
+// Activations and packed weights are IEEE half, accumulation fp32.  RMSNorm is
+// split between producer and consumer: the GEMM (or kernel) that writes a
+// residual row v also writes half(v * gain) and the 16-row block's sum of
+// squares; the consuming GEMM multiplies its outputs by 1/rms from those sums.
 #include <stdio.h>
 
 #include "qt_device.h"
@@ -138,7 +137,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, int n0,
     for (int e = tid; e < 8 * M; e += nthr) {
       const int m = e >> 3, p = e & 7;
       const float v = silu(y(2 * p, m)) * y(2 * p + 1, m);
-      split_bf16(v, a.u_hi, a.u_lo, chunked(m, (n0 >> 1) + p, a.u_ld));
+      a.u[chunked(m, (n0 >> 1) + p, a.u_ld)] = f2h(v);
     }
     return;
   }
@@ -170,7 +169,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, int n0,
       if (a.epi == EPI_RESID) v += pf.x[k];
       a.out_f32[(size_t)m * a.out_ld + c0 + r] = v;
       if (a.u_gain) {
-        split_bf16(v * pf.gain, a.u_hi, a.u_lo, chunked(m, c0 + r, a.u_ld));
+        a.u[chunked(m, c0 + r, a.u_ld)] = f2h(v * pf.gain);
         const float ss = row_sum16(v * v);
         if (r == 0) a.ss_out[(size_t)(c0 / kGemmRows) * a.ss_out_ld + m] = ss;
       }
@@ -178,11 +177,11 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, int n0,
   }
 }
 
-// Eight int8 weights (bytes 8*sb .. 8*sb+7 of w) as a bf16x8 operand (exact).
-__device__ __forceinline__ uint4 i8_to_bf16x8(const uint4& w, int sb) {
+// Eight int8 weights (bytes 8*sb .. 8*sb+7 of w) as a half x 8 operand (exact).
+__device__ __forceinline__ uint4 i8_to_f16x8(const uint4& w, int sb) {
   const uint32_t a = sb ? w.z : w.x, b = sb ? w.w : w.y;
-  return make_uint4(i8pair_to_bf16x2(a, 0), i8pair_to_bf16x2(a, 1), i8pair_to_bf16x2(b, 0),
-                    i8pair_to_bf16x2(b, 1));
+  return make_uint4(i8pair_to_f16x2(a, 0), i8pair_to_f16x2(a, 1), i8pair_to_f16x2(b, 0),
+                    i8pair_to_f16x2(b, 1));
 }
 
 // One block: weight rows [n0, n0+16) over all of K.  NW waves, MT 16-row MFMA
@@ -213,13 +212,11 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs args, int msplit) {
     a.M = min(args.M - m0, MT ? 16 * MT : 2);
     const size_t c8 = (size_t)m0 * 8;
     a.act += c8;
-    if (a.act_lo) a.act_lo += c8;
     if (a.ss_in) a.ss_in += m0;
     a.out_f32 += (size_t)m0 * a.out_ld;
     if (a.logits) a.logits += (size_t)m0 * a.logits_ld;
     if (a.cand) a.cand += (size_t)m0 * a.cand_ld;
-    if (a.u_hi) a.u_hi += c8;
-    if (a.u_lo) a.u_lo += c8;
+    if (a.u) a.u += c8;
     if (a.ss_out) a.ss_out += m0;
   }
   if (a.M <= 0) return;  // (plan_gemm never makes an empty part; whole block leaves)
@@ -229,8 +226,6 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs args, int msplit) {
   const int ksteps = a.K / (32 * SUB);
   const uint4* W = reinterpret_cast<const uint4*>(a.W) + (size_t)rt * ksteps * 64 + lane;
   const uint4* H = reinterpret_cast<const uint4*>(a.act);
-  const uint4* L = reinterpret_cast<const uint4*>(a.act_lo);
-  const bool has_lo = a.act_lo != nullptr;
 
   SsPrefetch ssp;
   if (a.ss_in) ss_prefetch(a, ssp);
@@ -243,7 +238,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs args, int msplit) {
 #pragma unroll
     for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int j0 = wave; j0 < ksteps; j0 += NW * G) {
-      uint4 w[G], h[G][SUB][MT], l[G][SUB][MT];
+      uint4 w[G], h[G][SUB][MT];
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         const int j = j0 + NW * g;
@@ -255,9 +250,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs args, int msplit) {
 #pragma unroll
           for (int t = 0; t < MT; ++t) {
             const int m = 16 * t + i;
-            const bool in = ok && m < M;
-            h[g][sb][t] = in ? H[c * ld + m] : make_uint4(0, 0, 0, 0);
-            l[g][sb][t] = in && has_lo ? L[c * ld + m] : make_uint4(0, 0, 0, 0);
+            h[g][sb][t] = ok && m < M ? H[c * ld + m] : make_uint4(0, 0, 0, 0);
           }
         }
       }
@@ -265,15 +258,11 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs args, int msplit) {
       for (int g = 0; g < G; ++g) {
 #pragma unroll
         for (int sb = 0; sb < SUB; ++sb) {
-          const bf16x8 A = __builtin_bit_cast(bf16x8, I8 ? i8_to_bf16x8(w[g], sb) : w[g]);
+          const f16x8 A = __builtin_bit_cast(f16x8, I8 ? i8_to_f16x8(w[g], sb) : w[g]);
 #pragma unroll
-          for (int t = 0; t < MT; ++t) {
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                A, __builtin_bit_cast(bf16x8, h[g][sb][t]), acc[t], 0, 0, 0);
-            if (has_lo)
-              acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  A, __builtin_bit_cast(bf16x8, l[g][sb][t]), acc[t], 0, 0, 0);
-          }
+          for (int t = 0; t < MT; ++t)
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                A, __builtin_bit_cast(f16x8, h[g][sb][t]), acc[t], 0, 0, 0);
         }
       }
     }
@@ -287,7 +276,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs args, int msplit) {
 #pragma unroll
     for (int m = 0; m < MV; ++m) acc[m] = 0.f;
     for (int j0 = wave; j0 < ksteps; j0 += NW * G) {
-      uint4 w[G], h[G][SUB][MV], l[G][SUB][MV];
+      uint4 w[G], h[G][SUB][MV];
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         const int j = j0 + NW * g;
@@ -297,20 +286,17 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs args, int msplit) {
         for (int sb = 0; sb < SUB; ++sb) {
           const size_t c = (size_t)(j * SUB + sb) * 4 + q;
 #pragma unroll
-          for (int m = 0; m < MV; ++m) {
-            const bool in = ok && m < M;
-            h[g][sb][m] = in ? H[c * ld + m] : make_uint4(0, 0, 0, 0);
-            l[g][sb][m] = in && has_lo ? L[c * ld + m] : make_uint4(0, 0, 0, 0);
-          }
+          for (int m = 0; m < MV; ++m)
+            h[g][sb][m] = ok && m < M ? H[c * ld + m] : make_uint4(0, 0, 0, 0);
         }
       }
 #pragma unroll
       for (int g = 0; g < G; ++g) {
 #pragma unroll
         for (int sb = 0; sb < SUB; ++sb) {
-          const uint4 A = I8 ? i8_to_bf16x8(w[g], sb) : w[g];
+          const uint4 A = I8 ? i8_to_f16x8(w[g], sb) : w[g];
 #pragma unroll
-          for (int m = 0; m < MV; ++m) acc[m] = dot8(A, l[g][sb][m], dot8(A, h[g][sb][m], acc[m]));
+          for (int m = 0; m < MV; ++m) acc[m] = dot8h(A, h[g][sb][m], acc[m]);
         }
       }
     }
@@ -359,7 +345,7 @@ hipError_t gemm_dispatch(const GemmArgs& a, const GemmPlan& p, hipStream_t s) {
 }
 
 // ------------------------------------------------------------------ packing
-// Source rows [rows][K] bf16 -> rows row0 + r*step of a tiled [N][K] matrix.
+// Source rows [rows][K] bf16 -> half rows row0 + r*step of a tiled [N][K] matrix.
 __global__ __launch_bounds__(256) void k_pack_tiled(const uint16_t* src, int rows, int K,
                                                     uint16_t* dst, int row0, int step) {
   const long long e = (long long)blockIdx.x * 256 + threadIdx.x;  // one 8-wide chunk
@@ -367,7 +353,12 @@ __global__ __launch_bounds__(256) void k_pack_tiled(const uint16_t* src, int row
   if (e >= (long long)rows * kc) return;
   const int r = (int)(e / kc), k = (int)(e - (long long)r * kc) << 3;
   const uint4 v = *reinterpret_cast<const uint4*>(src + (size_t)r * K + k);
-  *reinterpret_cast<uint4*>(dst + tiled_bf16(row0 + r * step, k, K)) = v;
+  const uint32_t in[4] = {v.x, v.y, v.z, v.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    o[j] = (uint32_t)f2h(bf_lo(in[j])) | ((uint32_t)f2h(bf_hi(in[j])) << 16);
+  *reinterpret_cast<uint4*>(dst + tiled_bf16(row0 + r * step, k, K)) = make_uint4(o[0], o[1], o[2], o[3]);
 }
 
 // Rows row0 + r*step of a tiled int8 [N][K] matrix -> row-major [rows][K].

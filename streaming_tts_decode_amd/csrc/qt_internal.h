@@ -13,16 +13,19 @@ constexpr int kHeadDim = 128;   // head dimension the attention kernels are writ
 constexpr int kPage = 16;       // Talker KV page size in positions
 constexpr int kMaxPagesPerSplit = 8;
 
-// Activations that feed a GEMM are carried as two bfloat16 arrays, hi = bf16(x)
-// and lo = bf16(x - hi), so that hi + lo keeps ~16 significant bits of the fp32
-// value; each weight operand is multiplied by both.  Weights stay bf16 / int8.
+// Activations that feed a GEMM are IEEE half (11-bit significand: about eight
+// times finer than bfloat16, which the 28-layer stack amplifies past the logit
+// tolerance), and the GEMM weights are packed as half too so that both MFMA
+// operands share the type: converting a bfloat16 weight to half is exact for
+// |w| >= 2^-14 and within 2^-25 below.  INT8 weights become exact halves in
+// registers.  Accumulation is fp32; residual streams are fp32.
 //
 // Layouts (all chosen so that every GEMM load and store moves whole 16-byte
 // pieces of contiguous memory):
-//  * packed weights, bf16: W[n][k] of an [N][K] matrix sits in 1 KB tiles
+//  * packed weights, half: W[n][k] of an [N][K] matrix sits in 1 KB tiles
 //    [N/16][K/32][64 lanes][8]; lane q*16+i of tile (n/16, k/32) holds
 //    W[16*(n/16)+i][32*(k/32) + 8q .. +8], the A operand of one
-//    16x16x32 MFMA.  tiled_bf16() gives the element offset.
+//    16x16x32 MFMA.  tiled_bf16() gives the element offset (2-byte elements).
 //  * packed weights, int8: 1 KB tiles [N/16][K/64][64][16 bytes]; lane q*16+i
 //    holds W[16*(n/16)+i][64j + 8q .. +8] in bytes 0..7 and
 //    W[..][64j + 32 + 8q .. +8] in bytes 8..15 (j = k/64).  tiled_i8().
@@ -56,13 +59,12 @@ enum Epi : int {
 };
 
 struct GemmArgs {
-  const void* W;          // packed tiles (see above) of a bf16 or int8 [N][K] matrix
+  const void* W;          // packed tiles (see above) of a half or int8 [N][K] matrix
   const float* scale;     // [N] when INT8, else nullptr
   int N, K;               // full matrix
   int row0, nrows;        // rows [row0, row0+nrows) are computed (multiples of 16)
-  const uint16_t* act;    // chunked bf16 [K/8][act_ld][8]: high part of the activations
-  const uint16_t* act_lo; // low part, or nullptr
-  int act_ld, M;          // rows 0..M-1 of the chunked arrays are used
+  const uint16_t* act;    // chunked half [K/8][act_ld][8] activations
+  int act_ld, M;          // rows 0..M-1 of the chunked array are used
   // Consumer of an RMSNorm: the activations are x * gain (left by the producer of
   // x), so every output is multiplied by inv[m] = 1/sqrt(sum_s ss_in[s*ss_in_ld+m]/K
   // + eps), the producer's per-row-block sums of squares.  ss_in == nullptr: none.
@@ -78,13 +80,12 @@ struct GemmArgs {
   unsigned long long* cand;
   int cand_ld;
   uint32_t* status;
-  // Chunked bf16 output pair: EPI_SWIGLU writes the SwiGLU activations here; a
-  // producer of an RMSNorm input (EPI_RESID rows, EPI_HEAD projection rows) writes
-  // hi/lo of v * u_gain[c] for every value v at output column c, and per 16-row
-  // block the sum of squares of the block's values in ss_out[slot*ss_out_ld + m].
+  // Chunked half output: EPI_SWIGLU writes the SwiGLU activations here; a producer
+  // of an RMSNorm input (EPI_RESID rows, EPI_HEAD projection rows) writes
+  // v * u_gain[c] for every value v at output column c, and per 16-row block the
+  // sum of squares of the block's values in ss_out[slot*ss_out_ld + m].
   const uint16_t* u_gain;
-  uint16_t* u_hi;
-  uint16_t* u_lo;
+  uint16_t* u;
   int u_ld;
   float* ss_out;
   int ss_out_ld;
@@ -133,8 +134,7 @@ struct AttnPagedArgs {
   int pages_per_split, n_splits;
   float* part;            // [B][n_q][n_splits][128 + 2]
   unsigned* counters;     // [B][n_kv]
-  uint16_t* o;            // chunked bf16 [q_dim/8][o_ld][8]: high part of the attention output
-  uint16_t* o_lo;         // low part
+  uint16_t* o;            // chunked half [q_dim/8][o_ld][8]: the attention output
   int o_ld;               // rows of the chunked output (>= B)
   uint32_t* status;
 };
@@ -149,8 +149,7 @@ struct AttnPredArgs {
   uint16_t* v_cache;
   long long sess_stride;  // elements between sessions
   int pos0, n_new;
-  uint16_t* o;            // chunked [q_dim/8][o_ld][8]; row i*B + b: new position pos0+i of session b
-  uint16_t* o_lo;         // low part
+  uint16_t* o;            // chunked half [q_dim/8][o_ld][8]; row i*B + b: position pos0+i of session b
   int o_ld;               // rows of the chunked output (>= n_new*B)
 };
 
@@ -164,8 +163,7 @@ struct FrameBeginArgs {
   float* x_t;              // [B][Ht] f32
   float* ss_t;             // [B]: sum of squares of the talker input rows (one slot)
   const uint16_t* gain;    // [Ht]: gain of the first Talker norm
-  uint16_t* u_hi;          // chunked [Ht/8][B][8]: hi/lo of x * gain (predictor mode: h_in, 0)
-  uint16_t* u_lo;
+  uint16_t* u;             // chunked half [Ht/8][B][8]: x * gain (predictor mode: h_in)
   unsigned long long* cand;  // [ncb][B][cand_ld] greedy-key candidates
   int cand_ld;
   unsigned* counters;        // [B][n_kv] attention counters, zeroed
@@ -183,8 +181,7 @@ struct EmbedArgs {
   float* ss;                    // sums of squares: slot 0 of the written rows, other slots zero
   int ss_ld, ss_slots;
   const uint16_t* gain;         // [H]: gain of the first predictor norm
-  uint16_t* u_hi;               // chunked [H/8][u_ld][8]: hi/lo of x * gain
-  uint16_t* u_lo;
+  uint16_t* u;                  // chunked half [H/8][u_ld][8]: x * gain
   int u_ld;
   int row_off;
   uint32_t* status;
@@ -208,7 +205,7 @@ hipError_t launch_attn_pred(const AttnPredArgs& a, float theta, hipStream_t s);
 hipError_t launch_frame_begin(const FrameBeginArgs& a, hipStream_t s);
 hipError_t launch_embed(const EmbedArgs& a, hipStream_t s);
 hipError_t launch_frame_end(const FrameEndArgs& a, hipStream_t s);
-// Pack bf16 source rows [rows][K] as rows row0 + i*step of a tiled [N][K] matrix.
+// Pack bf16 source rows [rows][K] as half rows row0 + i*step of a tiled [N][K] matrix.
 hipError_t launch_pack_tiled(const uint16_t* src, int rows, int K, uint16_t* dst, int row0, int step,
                              hipStream_t s);
 // Copy rows row0 + i*step (i < rows) of a tiled int8 [N][K] matrix out row-major.

@@ -91,7 +91,7 @@ __global__ __launch_bounds__(256) void k_attn_paged(AttnPagedArgs a, float theta
 
   const size_t orow = chunked(b, (j0 + jj) * 128 + d, a.o_ld);
   if (p < 0 || p >= cap) {
-    if (s == 0) a.o[orow] = a.o_lo[orow] = 0;
+    if (s == 0) a.o[orow] = 0;
     return;
   }
   const int S = pps * kPage;
@@ -241,7 +241,7 @@ __global__ __launch_bounds__(256) void k_attn_paged(AttnPagedArgs a, float theta
   __syncthreads();
   const float out = red[0][jj][d] + red[1][jj][d] + red[2][jj][d] + red[3][jj][d];
   if (n_active == 1) {
-    split_bf16(out / lstat[jj], a.o, a.o_lo, orow);
+    a.o[orow] = f2h(out / lstat[jj]);
     return;
   }
   // Publish this split's partial with device-coherent stores, wait until they
@@ -280,7 +280,7 @@ __global__ __launch_bounds__(256) void k_attn_paged(AttnPagedArgs a, float theta
     L = fmaf(dev_load(ps + 1), w, L);
     O = fmaf(dev_load(ps + 2 + d), w, O);
   }
-  split_bf16(O / L, a.o, a.o_lo, orow);
+  a.o[orow] = f2h(O / L);
   if (tid == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -400,13 +400,13 @@ __global__ __launch_bounds__(256) void k_attn_pred(AttnPredArgs a, float theta_l
   __syncthreads();
   for (int i = 0; i < a.n_new; ++i) {
     const float out = red[0][i][jj][d] + red[1][i][jj][d] + red[2][i][jj][d] + red[3][i][jj][d];
-    split_bf16(out / lsum[i][jj], a.o, a.o_lo, chunked(i * a.B + b, (j0 + jj) * 128 + d, a.o_ld));
+    a.o[chunked(i * a.B + b, (j0 + jj) * 128 + d, a.o_ld)] = f2h(out / lsum[i][jj]);
   }
 }
 
 // ---------------------------------------------------------------------------
 // Frame entry: Talker input rows to fp32 with their sums of squares and the first
-// norm's hi/lo input (predictor mode: the given post-norm hidden as the projection
+// norm's half input (predictor mode: the given post-norm hidden as the projection
 // input), capacity check, codebook-0 candidates of predictor mode, attention
 // counters cleared.
 __global__ __launch_bounds__(256) void k_frame_begin(FrameBeginArgs a) {
@@ -418,7 +418,7 @@ __global__ __launch_bounds__(256) void k_frame_begin(FrameBeginArgs a) {
       const size_t e = (size_t)b * a.Ht + i;
       const float v = bf2f(a.talker_in[e]);
       a.x_t[e] = v;
-      split_bf16(v * bf2f(a.gain[i]), a.u_hi, a.u_lo, chunked(b, i, a.B));
+      a.u[chunked(b, i, a.B)] = f2h(v * bf2f(a.gain[i]));
       ss = fmaf(v, v, ss);
     }
     ss = wave_sum(ss);
@@ -430,7 +430,8 @@ __global__ __launch_bounds__(256) void k_frame_begin(FrameBeginArgs a) {
       if (p < 0 || p + 1 > a.capacity) atomicOr(a.status, QT_STATUS_KV_OVERFLOW);
     }
   } else {
-    for (int i = tid; i < a.Ht; i += 256) a.u_hi[chunked(b, i, a.B)] = a.h_in[(size_t)b * a.Ht + i];
+    for (int i = tid; i < a.Ht; i += 256)
+      a.u[chunked(b, i, a.B)] = f2h(bf2f(a.h_in[(size_t)b * a.Ht + i]));
     unsigned long long* c0 = a.cand + (size_t)b * a.cand_ld;
     for (int k = tid; k < a.cand_ld; k += 256) c0[k] = k == 0 ? greedy_key(0.0f, a.tok0_in[b]) : 0ull;
   }
@@ -446,7 +447,7 @@ __device__ __forceinline__ unsigned long long best_key_wave(const unsigned long 
 }
 
 // Predictor step input: row E_step[token] (token = forced, or the previous step's
-// greedy token) to fp32, with its sum of squares and the first norm's hi/lo input.
+// greedy token) to fp32, with its sum of squares and the first norm's half input.
 __global__ __launch_bounds__(256) void k_embed(EmbedArgs a) {
   __shared__ float part[4];
   __shared__ int s_tok;
@@ -471,7 +472,7 @@ __global__ __launch_bounds__(256) void k_embed(EmbedArgs a) {
   for (int i = tid; i < a.H; i += 256) {
     const float v = bf2f(src[i]);
     dst[i] = v;
-    split_bf16(v * bf2f(a.gain[i]), a.u_hi, a.u_lo, chunked(m, i, a.u_ld));
+    a.u[chunked(m, i, a.u_ld)] = f2h(v * bf2f(a.gain[i]));
     ss = fmaf(v, v, ss);
   }
   ss = wave_sum(ss);

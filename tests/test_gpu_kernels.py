@@ -1,5 +1,6 @@
 """GPU tests on the reduced model and the INT8 quantizer: batch sizes across the
-VALU (M <= 8) and MFMA (M > 8) GEMM paths, ragged and boundary KV lengths,
+VALU (M <= 2) and MFMA (M >= 3, with the activation-row split) GEMM forms, ragged
+and boundary KV lengths, long contexts at full batch,
 determinism, graph replay, paging invariance, device status bits, and the
 bit-exact INT8 quantizer on every decode weight of the full model."""
 import numpy as np
@@ -41,6 +42,15 @@ def test_small_long_context_many_splits(small_pm, orc_small):
     """B=2 with ~1.5k positions: the split-KV partials and their merge."""
     w = small_w("Slong", batch=2, frames=2, lens=[1500, 700])
     run_frames(small_pm, orc_small, w, check=[0, 1])
+
+
+@pytest.mark.parametrize("lo,hi", [(1900, 2000), (3600, 4000)])
+def test_small_long_context_full_batch(small_pm, orc_small, lo, hi):
+    """B=32 with 2k and 4k contexts: many sessions with 16+ attention splits each,
+    all merged by their last block."""
+    w = small_w(f"Sgrp{hi}", batch=32, frames=1, lo=lo, hi=hi)
+    L = w.lengths()
+    run_frames(small_pm, orc_small, w, check=[int(np.argmax(L)), int(np.argmin(L))])
 
 
 def test_small_graph_replay(small_pm, orc_small):
