@@ -475,7 +475,10 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
   QT_MARK(QT_KERNEL_FRAME_BEGIN, "k_frame_begin", B, nullptr);
   QT_LAUNCH(launch_frame_begin(fb, st));
 
+  // predictor matrices are read once per step: keep them in the caches
+  bool keep_w = false;
   auto run = [&](GemmArgs& g) -> qt_status {
+    g.keep_w = keep_w ? 1 : 0;
     QT_MARK(QT_KERNEL_GEMM, nullptr, g.M, &g);
     QT_LAUNCH(launch_gemm(g, st));
     return ok();
@@ -597,6 +600,7 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
   }
 
   if (mode != QT_MODE_TALKER) {
+    keep_w = true;
     for (int k = 1; k < ncb; ++k) {
       const int M = (k == 1) ? 2 * B : B;
       const int emb_row = (k == 1) ? B : 0;

@@ -154,5 +154,13 @@ __device__ __forceinline__ float dev_load(const float* p) {
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
+// Non-temporal 16-byte load, for data read once per frame (streamed weights,
+// the Talker KV cache): it then does not displace what later steps re-read.
+__device__ __forceinline__ uint4 load_nt(const uint4* p) {
+  typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 }  // namespace dev
 }  // namespace qt

@@ -75,11 +75,12 @@ __device__ __forceinline__ float ss_partial(const GemmArgs& a, const SsPrefetch&
   return s;
 }
 
-// Nontemporal 16-byte load (weights are streamed once per call).
-__device__ __forceinline__ uint4 load_stream(const uint4* p) {
-  typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
+// 16-byte weight load: non-temporal for matrices streamed once per frame, a
+// plain (cached) load for matrices that later steps of the frame read again
+// (the predictor's layers fit in the memory-side cache and stay there).
+template <bool KEEP>
+__device__ __forceinline__ uint4 load_w(const uint4* p) {
+  return KEEP ? *p : load_nt(p);
 }
 
 // Operands of the epilogue that live in memory, loaded at kernel start so that
@@ -91,7 +92,7 @@ constexpr int kMaxElem = 2;  // 16 * 64 tile elements over >= 512 threads
 struct EpiPrefetch {
   float x[kMaxElem];
   float scale;
-  float gain;
+  uint32_t gain_bits;  // raw bfloat16: converted at use, so no wait is forced here
 };
 
 __device__ __forceinline__ void epi_prefetch(const GemmArgs& a, int n0, EpiPrefetch& p) {
@@ -106,9 +107,9 @@ __device__ __forceinline__ void epi_prefetch(const GemmArgs& a, int n0, EpiPrefe
   }
   p.scale = a.scale ? a.scale[n0 + r] : 1.f;
   const int base = a.epi == EPI_RESID ? 0 : a.n_logits;
-  p.gain = (a.u_gain && (a.epi == EPI_RESID || a.epi == EPI_HEAD) && n0 >= base)
-               ? bf2f(a.u_gain[n0 - base + r])
-               : 0.f;
+  p.gain_bits = (a.u_gain && (a.epi == EPI_RESID || a.epi == EPI_HEAD) && n0 >= base)
+                    ? (uint32_t)a.u_gain[n0 - base + r]
+                    : 0u;
 }
 
 // Epilogue, one thread per output element.  y(r, m): the block's finished value
@@ -169,7 +170,11 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, int n0,
       if (a.epi == EPI_RESID) v += pf.x[k];
       a.out_f32[(size_t)m * a.out_ld + c0 + r] = v;
       if (a.u_gain) {
-        a.u[chunked(m, c0 + r, a.u_ld)] = f2h(v * pf.gain);
+        // the conversion stays here: folded into the prefetch's branch it would make
+        // the kernel wait for that load before its main loop
+        uint32_t gb = pf.gain_bits;
+        asm volatile("" : "+v"(gb));
+        a.u[chunked(m, c0 + r, a.u_ld)] = f2h(v * bf2f((uint16_t)gb));
         const float ss = row_sum16(v * v);
         if (r == 0) a.ss_out[(size_t)(c0 / kGemmRows) * a.ss_out_ld + m] = ss;
       }
@@ -186,7 +191,7 @@ __device__ __forceinline__ uint4 i8_to_f16x8(const uint4& w, int sb) {
 
 // One block: weight rows [n0, n0+16) over all of K.  NW waves, MT 16-row MFMA
 // activation tiles (MT == 0: VALU form for M <= 2), G K steps per load group.
-template <int NW, int MT, int G, bool I8>
+template <int NW, int MT, int G, bool I8, bool KEEP>
 __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs args, int msplit) {
   constexpr int TLD = (MT ? 16 * MT : 2) + 1;  // tile row stride: activation rows + 1 (odd)
   constexpr int SUB = I8 ? 2 : 1;        // 32-wide MFMA K substeps per packed K step
@@ -243,7 +248,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs args, int msplit) {
       for (int g = 0; g < G; ++g) {
         const int j = j0 + NW * g;
         const bool ok = j < ksteps;
-        w[g] = ok ? load_stream(W + (size_t)j * 64) : make_uint4(0, 0, 0, 0);
+        w[g] = ok ? load_w<KEEP>(W + (size_t)j * 64) : make_uint4(0, 0, 0, 0);
 #pragma unroll
         for (int sb = 0; sb < SUB; ++sb) {
           const size_t c = (size_t)(j * SUB + sb) * 4 + q;
@@ -281,7 +286,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs args, int msplit) {
       for (int g = 0; g < G; ++g) {
         const int j = j0 + NW * g;
         const bool ok = j < ksteps;
-        w[g] = ok ? load_stream(W + (size_t)j * 64) : make_uint4(0, 0, 0, 0);
+        w[g] = ok ? load_w<KEEP>(W + (size_t)j * 64) : make_uint4(0, 0, 0, 0);
 #pragma unroll
         for (int sb = 0; sb < SUB; ++sb) {
           const size_t c = (size_t)(j * SUB + sb) * 4 + q;
@@ -331,15 +336,15 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs args, int msplit) {
   gemm_epilogue<NW, TLD>(a, n0, red, s_inv, s_scale, pf);
 }
 
-template <bool I8>
+template <bool I8, bool KEEP>
 hipError_t gemm_dispatch(const GemmArgs& a, const GemmPlan& p, hipStream_t s) {
   const dim3 grid(p.row_blocks * p.msplit), block(64 * p.nw);
   const int ms = p.msplit;
   switch (p.mt) {
-    case 0: launch_kernel((k_gemm<16, 0, 2, I8>), grid, block, s, a, ms); break;
-    case 1: launch_kernel((k_gemm<8, 1, 2, I8>), grid, block, s, a, ms); break;
-    case 2: launch_kernel((k_gemm<8, 2, 2, I8>), grid, block, s, a, ms); break;
-    default: launch_kernel((k_gemm<8, 4, 1, I8>), grid, block, s, a, ms); break;
+    case 0: launch_kernel((k_gemm<16, 0, 2, I8, KEEP>), grid, block, s, a, ms); break;
+    case 1: launch_kernel((k_gemm<8, 1, 2, I8, KEEP>), grid, block, s, a, ms); break;
+    case 2: launch_kernel((k_gemm<8, 2, 2, I8, KEEP>), grid, block, s, a, ms); break;
+    default: launch_kernel((k_gemm<8, 4, 1, I8, KEEP>), grid, block, s, a, ms); break;
   }
   return hipGetLastError();
 }
@@ -401,7 +406,8 @@ GemmPlan plan_gemm(int nrows, int K, int M, bool i8) {
 void gemm_kernel_name(const GemmArgs& a, char* buf, int len) {
   const bool i8 = a.scale != nullptr;
   const GemmPlan p = plan_gemm(a.nrows, a.K, a.M, i8);
-  snprintf(buf, len, "k_gemm<%d,%d,%d,%s>", p.nw, p.mt, p.g, i8 ? "true" : "false");
+  snprintf(buf, len, "k_gemm<%d,%d,%d,%s,%s>", p.nw, p.mt, p.g, i8 ? "true" : "false",
+           a.keep_w ? "true" : "false");
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
@@ -414,7 +420,8 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
   if ((a.epi == EPI_RESID || a.epi == EPI_HEAD) && a.u_gain && !a.ss_out) return hipErrorInvalidValue;
   const bool i8 = a.scale != nullptr;
   const GemmPlan p = plan_gemm(a.nrows, a.K, a.M, i8);
-  return i8 ? gemm_dispatch<true>(a, p, s) : gemm_dispatch<false>(a, p, s);
+  if (a.keep_w) return i8 ? gemm_dispatch<true, true>(a, p, s) : gemm_dispatch<false, true>(a, p, s);
+  return i8 ? gemm_dispatch<true, false>(a, p, s) : gemm_dispatch<false, false>(a, p, s);
 }
 
 hipError_t launch_pack_tiled(const uint16_t* src, int rows, int K, uint16_t* dst, int row0,

@@ -61,6 +61,8 @@ enum Epi : int {
 struct GemmArgs {
   const void* W;          // packed tiles (see above) of a half or int8 [N][K] matrix
   const float* scale;     // [N] when INT8, else nullptr
+  int keep_w;             // 1: the matrix is read again within the frame (predictor
+                          // steps), so its loads go through the caches; 0: streamed
   int N, K;               // full matrix
   int row0, nrows;        // rows [row0, row0+nrows) are computed (multiples of 16)
   const uint16_t* act;    // chunked half [K/8][act_ld][8] activations

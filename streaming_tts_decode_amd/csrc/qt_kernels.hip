@@ -113,8 +113,10 @@ __global__ __launch_bounds__(256) void k_attn_paged(AttnPagedArgs a, float theta
     if (g < pps && t < t1 && t != p) {
       if (pg[g] >= 0 && pg[g] < a.num_pages) {
         const size_t off = ((size_t)pg[g] * a.n_kv + h) * (kPage * 128) + (size_t)pi * 128 + 8 * c;
-        kk[g] = *reinterpret_cast<const uint4*>(a.k_pool + off);
-        vv[g] = *reinterpret_cast<const uint4*>(a.v_pool + off);
+        // non-temporal: the cache is streamed once per frame and should not
+        // displace the predictor weights that every step re-reads
+        kk[g] = load_nt(reinterpret_cast<const uint4*>(a.k_pool + off));
+        vv[g] = load_nt(reinterpret_cast<const uint4*>(a.v_pool + off));
       } else {
         bad = true;
       }
