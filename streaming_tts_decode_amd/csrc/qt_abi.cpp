@@ -493,7 +493,7 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
     g.u_ld = u_ld;
     g.ss_out = ss;
     g.ss_out_ld = ss_ld;
-    return plan_gemm(g.nrows, g.K, g.M, g.scale != nullptr).rows_per_block;
+    return plan_gemm(g.nrows, g.K, g.M, g.scale != nullptr, keep_w).rows_per_block;
   };
 
   // One decoder layer over M rows of residual x (row stride = hidden).  u: the

@@ -340,11 +340,12 @@ template <bool I8, bool KEEP>
 hipError_t gemm_dispatch(const GemmArgs& a, const GemmPlan& p, hipStream_t s) {
   const dim3 grid(p.row_blocks * p.msplit), block(64 * p.nw);
   const int ms = p.msplit;
+  // (the group sizes here and in plan_gemm agree)
   switch (p.mt) {
     case 0: launch_kernel((k_gemm<16, 0, 2, I8, KEEP>), grid, block, s, a, ms); break;
-    case 1: launch_kernel((k_gemm<8, 1, 2, I8, KEEP>), grid, block, s, a, ms); break;
-    case 2: launch_kernel((k_gemm<8, 2, 2, I8, KEEP>), grid, block, s, a, ms); break;
-    default: launch_kernel((k_gemm<8, 4, 1, I8, KEEP>), grid, block, s, a, ms); break;
+    case 1: launch_kernel((k_gemm<8, 1, 4, I8, KEEP>), grid, block, s, a, ms); break;
+    case 2: launch_kernel((k_gemm<8, 2, KEEP ? 4 : 2, I8, KEEP>), grid, block, s, a, ms); break;
+    default: launch_kernel((k_gemm<8, 4, KEEP ? 2 : 1, I8, KEEP>), grid, block, s, a, ms); break;
   }
   return hipGetLastError();
 }
@@ -382,7 +383,7 @@ __global__ __launch_bounds__(256) void k_untile_i8(const int8_t* tiled, int rows
 // Launch shape for nrows weight rows, K columns, M activation rows.  Small weight
 // matrices with many activation rows split the rows over 2 or 4 blocks per tile,
 // aiming at >= 256 blocks.
-GemmPlan plan_gemm(int nrows, int K, int M, bool i8) {
+GemmPlan plan_gemm(int nrows, int K, int M, bool i8, bool keep) {
   (void)K;
   (void)i8;
   GemmPlan p{};
@@ -399,13 +400,16 @@ GemmPlan plan_gemm(int nrows, int K, int M, bool i8) {
   const int mt = (tiles + p.msplit - 1) / p.msplit;
   p.nw = 8;
   p.mt = mt <= 1 ? 1 : (mt <= 2 ? 2 : 4);
-  p.g = p.mt == 4 ? 1 : 2;
+  // K steps per load group (measured on the frame): larger groups keep more
+  // bytes in flight, until the registers they take cost a block per CU, which
+  // the streamed Talker matrices with two activation tiles feel
+  p.g = p.mt == 1 ? 4 : (p.mt == 2 ? (keep ? 4 : 2) : (keep ? 2 : 1));
   return p;
 }
 
 void gemm_kernel_name(const GemmArgs& a, char* buf, int len) {
   const bool i8 = a.scale != nullptr;
-  const GemmPlan p = plan_gemm(a.nrows, a.K, a.M, i8);
+  const GemmPlan p = plan_gemm(a.nrows, a.K, a.M, i8, a.keep_w != 0);
   snprintf(buf, len, "k_gemm<%d,%d,%d,%s,%s>", p.nw, p.mt, p.g, i8 ? "true" : "false",
            a.keep_w ? "true" : "false");
 }
@@ -419,7 +423,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
     return hipErrorInvalidValue;
   if ((a.epi == EPI_RESID || a.epi == EPI_HEAD) && a.u_gain && !a.ss_out) return hipErrorInvalidValue;
   const bool i8 = a.scale != nullptr;
-  const GemmPlan p = plan_gemm(a.nrows, a.K, a.M, i8);
+  const GemmPlan p = plan_gemm(a.nrows, a.K, a.M, i8, a.keep_w != 0);
   if (a.keep_w) return i8 ? gemm_dispatch<true, true>(a, p, s) : gemm_dispatch<false, true>(a, p, s);
   return i8 ? gemm_dispatch<true, false>(a, p, s) : gemm_dispatch<false, false>(a, p, s);
 }

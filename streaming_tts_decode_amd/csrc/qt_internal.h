@@ -198,7 +198,7 @@ struct FrameEndArgs {
 };
 
 // launchers (enqueue only; shapes are validated by the caller)
-GemmPlan plan_gemm(int nrows, int K, int M, bool i8);
+GemmPlan plan_gemm(int nrows, int K, int M, bool i8, bool keep);
 // Kernel symbol (with template arguments) that launch_gemm picks for these arguments.
 void gemm_kernel_name(const GemmArgs& a, char* buf, int len);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
