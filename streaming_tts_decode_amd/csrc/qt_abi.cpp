@@ -535,9 +535,11 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
   GemmArgs head = gemm_act(m, m->plan.t_head, ut, ld_t, B, out->status);
 
   if (talker) {
-    // pages per split: about 1024 blocks over the page table, at most 8 pages each
+    // pages per split: about 1024 blocks over the page table, 4 to 8 pages each
+    // (fewer pages per split leave the last block of a session-head too many
+    // partials to merge: at B = 1, 4 pages per split took 8.3 us a layer, 1 page 12.2)
     const int pps_raw = (B * T.n_kv_heads * max_pages + 1023) / 1024;
-    const int pps = pps_raw < 1 ? 1 : (pps_raw > kMaxPagesPerSplit ? kMaxPagesPerSplit : pps_raw);
+    const int pps = pps_raw < 4 ? 4 : (pps_raw > kMaxPagesPerSplit ? kMaxPagesPerSplit : pps_raw);
     const int n_splits = (max_pages + pps - 1) / pps;
     const size_t layer_elems = (size_t)kv->num_pages * T.n_kv_heads * kPage * kHeadDim;
     for (int l = 0; l < T.layers; ++l) {
