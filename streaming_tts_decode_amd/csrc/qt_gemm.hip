@@ -95,7 +95,7 @@ struct EpiPrefetch {
   uint32_t gain_bits;  // raw bfloat16: converted at use, so no wait is forced here
 };
 
-__device__ __forceinline__ void epi_prefetch(const GemmArgs& a, int n0, EpiPrefetch& p) {
+__device__ __forceinline__ void epi_prefetch(const GemmArgs& a, int n0, int rows, EpiPrefetch& p) {
   const int tid = threadIdx.x, nthr = blockDim.x;
   const int M = a.M, r = tid & 15;
 #pragma unroll
@@ -105,7 +105,7 @@ __device__ __forceinline__ void epi_prefetch(const GemmArgs& a, int n0, EpiPrefe
                  ? a.out_f32[(size_t)(e >> 4) * a.out_ld + n0 + r]
                  : 0.f;
   }
-  p.scale = a.scale ? a.scale[n0 + r] : 1.f;
+  p.scale = a.scale ? a.scale[n0 + tid % rows] : 1.f;  // row tid % rows of the block
   const int base = a.epi == EPI_RESID ? 0 : a.n_logits;
   p.gain_bits = (a.u_gain && (a.epi == EPI_RESID || a.epi == EPI_HEAD) && n0 >= base)
                     ? (uint32_t)a.u_gain[n0 - base + r]
@@ -117,9 +117,9 @@ __device__ __forceinline__ void epi_prefetch(const GemmArgs& a, int n0, EpiPrefe
 // RMSNorm factor applied).  s_scale: the 16 rows' scales (for SwiGLU, whose
 // threads need two rows).  TLD: row stride of the partial tiles in LDS, odd so
 // that the 16 rows a thread group reads fall in distinct banks.
-template <int NW, int TLD>
+template <int NW, int TLD, int R>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, int n0,
-                                              const float (*red)[kGemmRows * TLD],
+                                              const float (*red)[kGemmRows * R * TLD],
                                               const float* s_inv, const float* s_scale,
                                               const EpiPrefetch& pf) {
   const int M = a.M;
@@ -134,9 +134,9 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, int n0,
     return v;
   };
   if (a.epi == EPI_SWIGLU) {
-    // rows 2p (gate) and 2p+1 (up) -> output column n0/2 + p; eight threads per chunk
-    for (int e = tid; e < 8 * M; e += nthr) {
-      const int m = e >> 3, p = e & 7;
+    // rows 2p (gate) and 2p+1 (up) of the block's 16R -> output column n0/2 + p
+    for (int e = tid; e < 8 * R * M; e += nthr) {
+      const int m = e / (8 * R), p = e - m * (8 * R);
       const float v = silu(y(2 * p, m)) * y(2 * p + 1, m);
       a.u[chunked(m, (n0 >> 1) + p, a.u_ld)] = f2h(v);
     }
@@ -191,15 +191,15 @@ __device__ __forceinline__ uint4 i8_to_f16x8(const uint4& w, int sb) {
 
 // One block: weight rows [n0, n0+16) over all of K.  NW waves, MT 16-row MFMA
 // activation tiles (MT == 0: VALU form for M <= 2), G K steps per load group.
-template <int NW, int MT, int G, bool I8, bool KEEP>
+template <int NW, int MT, int G, bool I8, bool KEEP, int R>
 __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs args, int msplit) {
   constexpr int TLD = (MT ? 16 * MT : 2) + 1;  // tile row stride: activation rows + 1 (odd)
   constexpr int SUB = I8 ? 2 : 1;        // 32-wide MFMA K substeps per packed K step
   constexpr int MV = MT ? 16 * MT : 2;   // activation rows held per lane group
-  __shared__ float red[NW][kGemmRows * TLD];
+  __shared__ float red[NW][kGemmRows * R * TLD];
   __shared__ float s_ssp[NW * 64];
   __shared__ float s_inv[64];
-  __shared__ float s_scale[kGemmRows];
+  __shared__ float s_scale[kGemmRows * R];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i = lane & 15, q = lane >> 4;
   // block -> (weight tile, activation-row part).  With msplit > 1, blocks b and
@@ -225,7 +225,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs args, int msplit) {
     if (a.ss_out) a.ss_out += m0;
   }
   if (a.M <= 0) return;  // (plan_gemm never makes an empty part; whole block leaves)
-  const int rt = (a.row0 >> 4) + rtl;
+  const int rt = (a.row0 >> 4) + rtl * R;  // first of the block's R row tiles
   const int n0 = rt * kGemmRows;
   const int M = a.M, ld = a.act_ld;
   const int ksteps = a.K / (32 * SUB);
@@ -235,20 +235,24 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs args, int msplit) {
   SsPrefetch ssp;
   if (a.ss_in) ss_prefetch(a, ssp);
   EpiPrefetch pf;
-  epi_prefetch(a, n0, pf);
+  epi_prefetch(a, n0, kGemmRows * R, pf);
 
   // activation row m of chunk c: 16 bytes at H[c * ld + m]
   if constexpr (MT > 0) {
-    f32x4 acc[MT];
+    f32x4 acc[R][MT];
 #pragma unroll
-    for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+      for (int t = 0; t < MT; ++t) acc[rr][t] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int j0 = wave; j0 < ksteps; j0 += NW * G) {
-      uint4 w[G], h[G][SUB][MT];
+      uint4 w[G][R], h[G][SUB][MT];
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         const int j = j0 + NW * g;
         const bool ok = j < ksteps;
-        w[g] = ok ? load_w<KEEP>(W + (size_t)j * 64) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr)
+          w[g][rr] = ok ? load_w<KEEP>(W + ((size_t)rr * ksteps + j) * 64) : make_uint4(0, 0, 0, 0);
 #pragma unroll
         for (int sb = 0; sb < SUB; ++sb) {
           const size_t c = (size_t)(j * SUB + sb) * 4 + q;
@@ -263,30 +267,40 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs args, int msplit) {
       for (int g = 0; g < G; ++g) {
 #pragma unroll
         for (int sb = 0; sb < SUB; ++sb) {
-          const f16x8 A = __builtin_bit_cast(f16x8, I8 ? i8_to_f16x8(w[g], sb) : w[g]);
 #pragma unroll
-          for (int t = 0; t < MT; ++t)
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                A, __builtin_bit_cast(f16x8, h[g][sb][t]), acc[t], 0, 0, 0);
+          for (int rr = 0; rr < R; ++rr) {
+            const f16x8 A = __builtin_bit_cast(f16x8, I8 ? i8_to_f16x8(w[g][rr], sb) : w[g][rr]);
+#pragma unroll
+            for (int t = 0; t < MT; ++t)
+              acc[rr][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                  A, __builtin_bit_cast(f16x8, h[g][sb][t]), acc[rr][t], 0, 0, 0);
+          }
         }
       }
     }
     // D layout of a 16x16 tile: lane l, element e -> weight row 4*(l>>4)+e, column l&15
 #pragma unroll
-    for (int t = 0; t < MT; ++t)
+    for (int rr = 0; rr < R; ++rr)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) red[wave][(4 * q + e) * TLD + 16 * t + i] = acc[t][e];
+      for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          red[wave][(16 * rr + 4 * q + e) * TLD + 16 * t + i] = acc[rr][t][e];
   } else {
-    float acc[MV];
+    float acc[R][MV];
 #pragma unroll
-    for (int m = 0; m < MV; ++m) acc[m] = 0.f;
+    for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+      for (int m = 0; m < MV; ++m) acc[rr][m] = 0.f;
     for (int j0 = wave; j0 < ksteps; j0 += NW * G) {
-      uint4 w[G], h[G][SUB][MV];
+      uint4 w[G][R], h[G][SUB][MV];
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         const int j = j0 + NW * g;
         const bool ok = j < ksteps;
-        w[g] = ok ? load_w<KEEP>(W + (size_t)j * 64) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr)
+          w[g][rr] = ok ? load_w<KEEP>(W + ((size_t)rr * ksteps + j) * 64) : make_uint4(0, 0, 0, 0);
 #pragma unroll
         for (int sb = 0; sb < SUB; ++sb) {
           const size_t c = (size_t)(j * SUB + sb) * 4 + q;
@@ -299,20 +313,25 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs args, int msplit) {
       for (int g = 0; g < G; ++g) {
 #pragma unroll
         for (int sb = 0; sb < SUB; ++sb) {
-          const uint4 A = I8 ? i8_to_f16x8(w[g], sb) : w[g];
 #pragma unroll
-          for (int m = 0; m < MV; ++m) acc[m] = dot8h(A, h[g][sb][m], acc[m]);
+          for (int rr = 0; rr < R; ++rr) {
+            const uint4 A = I8 ? i8_to_f16x8(w[g][rr], sb) : w[g][rr];
+#pragma unroll
+            for (int m = 0; m < MV; ++m) acc[rr][m] = dot8h(A, h[g][sb][m], acc[rr][m]);
+          }
         }
       }
     }
 #pragma unroll
-    for (int m = 0; m < MV; ++m) {
-      const float v = sum_q4(acc[m]);
-      if (q == 0) red[wave][i * TLD + m] = v;
-    }
+    for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+      for (int m = 0; m < MV; ++m) {
+        const float v = sum_q4(acc[rr][m]);
+        if (q == 0) red[wave][(16 * rr + i) * TLD + m] = v;
+      }
   }
   if (a.ss_in) s_ssp[tid] = ssp.on ? ss_partial(a, ssp) : 0.f;
-  if (tid < kGemmRows) s_scale[tid] = pf.scale;
+  if (tid < kGemmRows * R) s_scale[tid] = pf.scale;
   __syncthreads();
   if (a.ss_in) {
     // row m's G partials, summed in a fixed order: by one thread when there are
@@ -333,7 +352,7 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs args, int msplit) {
     }
     __syncthreads();
   }
-  gemm_epilogue<NW, TLD>(a, n0, red, s_inv, s_scale, pf);
+  gemm_epilogue<NW, TLD, R>(a, n0, red, s_inv, s_scale, pf);
 }
 
 template <bool I8, bool KEEP>
@@ -341,11 +360,24 @@ hipError_t gemm_dispatch(const GemmArgs& a, const GemmPlan& p, hipStream_t s) {
   const dim3 grid(p.row_blocks * p.msplit), block(64 * p.nw);
   const int ms = p.msplit;
   // (the group sizes here and in plan_gemm agree)
+  if (p.tiles == 3) {  // (streamed matrices only)
+    if constexpr (KEEP) {
+      return hipErrorInvalidConfiguration;
+    } else {
+      switch (p.mt) {
+        case 0: launch_kernel((k_gemm<16, 0, 2, I8, false, 3>), grid, block, s, a, ms); break;
+        case 1: launch_kernel((k_gemm<8, 1, 4, I8, false, 3>), grid, block, s, a, ms); break;
+        case 2: launch_kernel((k_gemm<8, 2, 2, I8, false, 3>), grid, block, s, a, ms); break;
+        default: return hipErrorInvalidConfiguration;
+      }
+      return hipGetLastError();
+    }
+  }
   switch (p.mt) {
-    case 0: launch_kernel((k_gemm<16, 0, 2, I8, KEEP>), grid, block, s, a, ms); break;
-    case 1: launch_kernel((k_gemm<8, 1, 4, I8, KEEP>), grid, block, s, a, ms); break;
-    case 2: launch_kernel((k_gemm<8, 2, KEEP ? 4 : 2, I8, KEEP>), grid, block, s, a, ms); break;
-    default: launch_kernel((k_gemm<8, 4, KEEP ? 2 : 1, I8, KEEP>), grid, block, s, a, ms); break;
+    case 0: launch_kernel((k_gemm<16, 0, 2, I8, KEEP, 1>), grid, block, s, a, ms); break;
+    case 1: launch_kernel((k_gemm<8, 1, 4, I8, KEEP, 1>), grid, block, s, a, ms); break;
+    case 2: launch_kernel((k_gemm<8, 2, KEEP ? 4 : 2, I8, KEEP, 1>), grid, block, s, a, ms); break;
+    default: launch_kernel((k_gemm<8, 4, KEEP ? 2 : 1, I8, KEEP, 1>), grid, block, s, a, ms); break;
   }
   return hipGetLastError();
 }
@@ -383,19 +415,28 @@ __global__ __launch_bounds__(256) void k_untile_i8(const int8_t* tiled, int rows
 // Launch shape for nrows weight rows, K columns, M activation rows.  Small weight
 // matrices with many activation rows split the rows over 2 or 4 blocks per tile,
 // aiming at >= 256 blocks.
-GemmPlan plan_gemm(int nrows, int K, int M, bool i8, bool keep) {
+GemmPlan plan_gemm(int nrows, int K, int M, bool i8, bool keep, bool swiglu) {
   (void)K;
   (void)i8;
   GemmPlan p{};
   p.rows_per_block = kGemmRows;
   p.row_blocks = nrows / kGemmRows;
   p.msplit = 1;
+  p.tiles = 1;
+  // A streamed SwiGLU matrix with three times more row tiles than CUs: three
+  // tiles per block, so every block re-reads the activations a third as often
+  // and keeps three tiles' weight loads in flight (at most two 16-row
+  // activation tiles: the Talker's own batch).
+  if (swiglu && !keep && p.row_blocks >= 768 && p.row_blocks % 3 == 0 && M <= 32) {
+    p.tiles = 3;
+    p.row_blocks /= 3;
+  }
   if (M <= 2) {
     p.nw = 16, p.mt = 0, p.g = 2;
     return p;
   }
   const int tiles = (M + 15) / 16;
-  if (tiles > 1 && p.row_blocks % 8 == 0)
+  if (tiles > 1 && p.row_blocks % 8 == 0 && p.tiles == 1)
     while (p.msplit * 2 <= tiles && p.row_blocks * p.msplit < 256) p.msplit *= 2;
   const int mt = (tiles + p.msplit - 1) / p.msplit;
   p.nw = 8;
@@ -409,9 +450,9 @@ GemmPlan plan_gemm(int nrows, int K, int M, bool i8, bool keep) {
 
 void gemm_kernel_name(const GemmArgs& a, char* buf, int len) {
   const bool i8 = a.scale != nullptr;
-  const GemmPlan p = plan_gemm(a.nrows, a.K, a.M, i8, a.keep_w != 0);
-  snprintf(buf, len, "k_gemm<%d,%d,%d,%s,%s>", p.nw, p.mt, p.g, i8 ? "true" : "false",
-           a.keep_w ? "true" : "false");
+  const GemmPlan p = plan_gemm(a.nrows, a.K, a.M, i8, a.keep_w != 0, a.epi == EPI_SWIGLU);
+  snprintf(buf, len, "k_gemm<%d,%d,%d,%s,%s,%d>", p.nw, p.mt, p.g, i8 ? "true" : "false",
+           a.keep_w ? "true" : "false", p.tiles);
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
@@ -423,7 +464,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
     return hipErrorInvalidValue;
   if ((a.epi == EPI_RESID || a.epi == EPI_HEAD) && a.u_gain && !a.ss_out) return hipErrorInvalidValue;
   const bool i8 = a.scale != nullptr;
-  const GemmPlan p = plan_gemm(a.nrows, a.K, a.M, i8, a.keep_w != 0);
+  const GemmPlan p = plan_gemm(a.nrows, a.K, a.M, i8, a.keep_w != 0, a.epi == EPI_SWIGLU);
   if (a.keep_w) return i8 ? gemm_dispatch<true, true>(a, p, s) : gemm_dispatch<false, true>(a, p, s);
   return i8 ? gemm_dispatch<true, false>(a, p, s) : gemm_dispatch<false, false>(a, p, s);
 }

@@ -110,7 +110,8 @@ inline void launch_kernel(Kernel kernel, dim3 grid, dim3 block, hipStream_t s, A
     hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
 }
 
-// Launch shape chosen for one GEMM (see plan_gemm): 16 weight rows per block, nw
+// Launch shape chosen for one GEMM (see plan_gemm): 16 weight rows (one tile, or
+// three for large SwiGLU matrices) per block, nw
 // waves splitting K; mt > 0: MFMA over mt 16-row activation tiles, mt == 0: VALU
 // dot products (M <= 2); g = K steps per load group.  msplit > 1: the activation
 // rows are split over msplit blocks per weight tile (more blocks for GEMMs with
@@ -118,7 +119,9 @@ inline void launch_kernel(Kernel kernel, dim3 grid, dim3 block, hipStream_t s, A
 // from HBM once.
 struct GemmPlan {
   int nw, mt, g, msplit;
-  int rows_per_block, row_blocks;
+  int rows_per_block;  // rows per sum-of-squares slot of a producing epilogue (16)
+  int row_blocks;      // blocks along the weight rows
+  int tiles;           // 16-row weight tiles per block (1, or 3 for large SwiGLU matrices)
 };
 
 struct AttnPagedArgs {
@@ -198,7 +201,7 @@ struct FrameEndArgs {
 };
 
 // launchers (enqueue only; shapes are validated by the caller)
-GemmPlan plan_gemm(int nrows, int K, int M, bool i8, bool keep);
+GemmPlan plan_gemm(int nrows, int K, int M, bool i8, bool keep, bool swiglu = false);
 // Kernel symbol (with template arguments) that launch_gemm picks for these arguments.
 void gemm_kernel_name(const GemmArgs& a, char* buf, int len);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
