@@ -49,8 +49,8 @@ struct SsPrefetch {
   bool on;   // this thread holds a partial
 };
 
-__device__ __forceinline__ void ss_prefetch(const GemmArgs& a, SsPrefetch& p) {
-  const int tid = threadIdx.x, nthr = blockDim.x, M = a.M;
+__device__ __forceinline__ void ss_prefetch(const GemmArgs& a, int nthr, SsPrefetch& p) {
+  const int tid = threadIdx.x, M = a.M;
   int G = nthr / M;
   if (G > a.ss_in_slots) G = a.ss_in_slots;
   p.G = G;
@@ -95,8 +95,9 @@ struct EpiPrefetch {
   uint32_t gain_bits;  // raw bfloat16: converted at use, so no wait is forced here
 };
 
-__device__ __forceinline__ void epi_prefetch(const GemmArgs& a, int n0, int rows, EpiPrefetch& p) {
-  const int tid = threadIdx.x, nthr = blockDim.x;
+__device__ __forceinline__ void epi_prefetch(const GemmArgs& a, int nthr, int n0, int rows,
+                                             EpiPrefetch& p) {
+  const int tid = threadIdx.x;
   const int M = a.M, r = tid & 15;
 #pragma unroll
   for (int k = 0; k < kMaxElem; ++k) {
@@ -189,10 +190,27 @@ __device__ __forceinline__ uint4 i8_to_f16x8(const uint4& w, int sb) {
                     i8pair_to_f16x2(b, 1));
 }
 
+// Every kernel argument is a scalar load, and the compiler issues each one where
+// its value is first needed, often inside a branch: the prologue became a chain
+// of five or six dependent round trips before the first weight load.  Taking
+// every field through an empty asm at entry issues the loads together and waits
+// for them once.
+__device__ __forceinline__ void fetch_args(const GemmArgs& a, int msplit) {
+  asm volatile("" ::"s"(a.W), "s"(a.scale), "s"(a.act), "s"(a.ss_in), "s"(a.out_f32),
+               "s"(a.logits), "s"(a.cand), "s"(a.status), "s"(a.u_gain), "s"(a.u),
+               "s"(a.ss_out), "s"(msplit));
+  asm volatile("" ::"s"(a.N), "s"(a.K), "s"(a.row0), "s"(a.nrows), "s"(a.act_ld), "s"(a.M),
+               "s"(a.ss_in_ld), "s"(a.ss_in_slots), "s"(a.norm_eps), "s"(a.epi), "s"(a.out_ld),
+               "s"(a.logits_ld), "s"(a.n_logits), "s"(a.argmax_range), "s"(a.cand_ld),
+               "s"(a.u_ld), "s"(a.ss_out_ld), "s"(a.keep_w));
+}
+
 // One block: weight rows [n0, n0+16) over all of K.  NW waves, MT 16-row MFMA
 // activation tiles (MT == 0: VALU form for M <= 2), G K steps per load group.
 template <int NW, int MT, int G, bool I8, bool KEEP, int R>
-__global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs args, int msplit) {
+__global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs args_in, int msplit) {
+  const GemmArgs& args = args_in;
+  fetch_args(args, msplit);
   constexpr int TLD = (MT ? 16 * MT : 2) + 1;  // tile row stride: activation rows + 1 (odd)
   constexpr int SUB = I8 ? 2 : 1;        // 32-wide MFMA K substeps per packed K step
   constexpr int MV = MT ? 16 * MT : 2;   // activation rows held per lane group
@@ -233,9 +251,9 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs args, int msplit) {
   const uint4* H = reinterpret_cast<const uint4*>(a.act);
 
   SsPrefetch ssp;
-  if (a.ss_in) ss_prefetch(a, ssp);
+  if (a.ss_in) ss_prefetch(a, NW * 64, ssp);
   EpiPrefetch pf;
-  epi_prefetch(a, n0, kGemmRows * R, pf);
+  epi_prefetch(a, NW * 64, n0, kGemmRows * R, pf);
 
   // activation row m of chunk c: 16 bytes at H[c * ld + m]
   if constexpr (MT > 0) {
