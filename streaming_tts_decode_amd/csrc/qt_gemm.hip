@@ -37,41 +37,41 @@ using namespace dev;
 
 // ---- RMSNorm statistics of the input rows (consumer side)
 // The producer of x left per-16-column sums of squares in ss_in[slot][m]
-// (slot < ss_in_slots).  Thread t of the block handles row m = t % M and slots
-// g, g + G, ... with g = t / M, G = min(nthr / M, slots): the loads are
-// coalesced over m and issued before the main loads; after the main loop the G
-// partials of a row are added in a fixed order.
-constexpr int kSsPer = 16;  // slot loads per thread kept in registers
-
+// (slot < ss_in_slots).  Thread t of the block handles row m = t % MP and slots
+// g, g + G, ... with g = t / MP, G = NTHR / MP, where MP is the block's padded
+// row count: a constant, so the mapping costs no division (rows m >= M load
+// nothing).  The loads are coalesced over m and issued before the main loads;
+// after the main loop the G partials of a row are added in a fixed order.
+template <int MP, int NTHR>
 struct SsPrefetch {
-  float v[kSsPer];
-  int G;     // slot groups
-  bool on;   // this thread holds a partial
+  static constexpr int G = NTHR / MP;
+  static constexpr int PER = (128 + G - 1) / G;  // slots per thread held in registers
+  float v[PER];
 };
 
-__device__ __forceinline__ void ss_prefetch(const GemmArgs& a, int nthr, SsPrefetch& p) {
-  const int tid = threadIdx.x, M = a.M;
-  int G = nthr / M;
-  if (G > a.ss_in_slots) G = a.ss_in_slots;
-  p.G = G;
-  const int g = tid / M, m = tid - g * M;
-  p.on = g < G;
+template <int MP, int NTHR>
+__device__ __forceinline__ void ss_prefetch(const GemmArgs& a, SsPrefetch<MP, NTHR>& p) {
+  using S = SsPrefetch<MP, NTHR>;
+  const int tid = threadIdx.x, g = tid / MP, m = tid % MP;
+  const bool on = m < a.M;
 #pragma unroll
-  for (int k = 0; k < kSsPer; ++k) {
-    const int slot = g + k * G;
-    p.v[k] = (p.on && slot < a.ss_in_slots) ? a.ss_in[(size_t)slot * a.ss_in_ld + m] : 0.f;
+  for (int k = 0; k < S::PER; ++k) {
+    const int slot = g + k * S::G;
+    p.v[k] = (on && slot < a.ss_in_slots) ? a.ss_in[(size_t)slot * a.ss_in_ld + m] : 0.f;
   }
 }
 
 // Partial of this thread (slots beyond the registered ones are loaded now).
-__device__ __forceinline__ float ss_partial(const GemmArgs& a, const SsPrefetch& p) {
-  const int tid = threadIdx.x, M = a.M;
-  const int g = tid / M, m = tid - g * M;
+template <int MP, int NTHR>
+__device__ __forceinline__ float ss_partial(const GemmArgs& a, const SsPrefetch<MP, NTHR>& p) {
+  using S = SsPrefetch<MP, NTHR>;
+  const int tid = threadIdx.x, g = tid / MP, m = tid % MP;
   float s = 0.f;
 #pragma unroll
-  for (int k = 0; k < kSsPer; ++k) s += p.v[k];
-  for (int slot = g + kSsPer * p.G; slot < a.ss_in_slots; slot += p.G)
-    s += a.ss_in[(size_t)slot * a.ss_in_ld + m];
+  for (int k = 0; k < S::PER; ++k) s += p.v[k];
+  if (m < a.M)
+    for (int slot = g + S::PER * S::G; slot < a.ss_in_slots; slot += S::G)
+      s += a.ss_in[(size_t)slot * a.ss_in_ld + m];
   return s;
 }
 
@@ -223,10 +223,10 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs args_in, int msplit) 
   // block -> (weight tile, activation-row part).  With msplit > 1, blocks b and
   // b + 8, b + 16, ... (the same XCD under round-robin dispatch) share a tile.
   int rtl = blockIdx.x, mh = 0;
-  if (msplit > 1) {
-    const int x = blockIdx.x & 7, slot = blockIdx.x >> 3;
-    mh = slot % msplit;
-    rtl = (slot / msplit) * 8 + x;
+  if (msplit > 1) {  // (a power of two)
+    const int x = blockIdx.x & 7, slot = blockIdx.x >> 3, sh = __builtin_ctz(msplit);
+    mh = slot & (msplit - 1);
+    rtl = (slot >> sh) * 8 + x;
   }
   // this block's rows m0 .. m0 + M-1 of the activations, as a shifted view
   GemmArgs a = args;
@@ -250,8 +250,8 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs args_in, int msplit) 
   const uint4* W = reinterpret_cast<const uint4*>(a.W) + (size_t)rt * ksteps * 64 + lane;
   const uint4* H = reinterpret_cast<const uint4*>(a.act);
 
-  SsPrefetch ssp;
-  if (a.ss_in) ss_prefetch(a, NW * 64, ssp);
+  SsPrefetch<MV, NW * 64> ssp;
+  if (a.ss_in) ss_prefetch(a, ssp);
   EpiPrefetch pf;
   epi_prefetch(a, NW * 64, n0, kGemmRows * R, pf);
 
@@ -348,22 +348,24 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs args_in, int msplit) 
         if (q == 0) red[wave][(16 * rr + i) * TLD + m] = v;
       }
   }
-  if (a.ss_in) s_ssp[tid] = ssp.on ? ss_partial(a, ssp) : 0.f;
+  if (a.ss_in) s_ssp[tid] = ss_partial(a, ssp);
   if (tid < kGemmRows * R) s_scale[tid] = pf.scale;
   __syncthreads();
   if (a.ss_in) {
     // row m's G partials, summed in a fixed order: by one thread when there are
     // few of them (many rows), else by a wave (tree sum over its lanes)
-    if (ssp.G <= 32) {
+    constexpr int SG = SsPrefetch<MV, NW * 64>::G;
+    if constexpr (SG <= 32) {
       if (tid < M) {
         float ss = 0.f;
-        for (int g = 0; g < ssp.G; ++g) ss += s_ssp[g * M + tid];
+#pragma unroll
+        for (int g = 0; g < SG; ++g) ss += s_ssp[g * MV + tid];
         s_inv[tid] = 1.0f / sqrtf(ss / (float)a.K + a.norm_eps);
       }
     } else {
       for (int m = wave; m < M; m += NW) {
         float ss = 0.f;
-        for (int g = lane; g < ssp.G; g += 64) ss += s_ssp[g * M + m];
+        for (int g = lane; g < SG; g += 64) ss += s_ssp[g * MV + m];
         ss = wave_sum(ss);
         if (lane == 0) s_inv[m] = 1.0f / sqrtf(ss / (float)a.K + a.norm_eps);
       }
