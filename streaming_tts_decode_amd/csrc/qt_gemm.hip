@@ -118,27 +118,41 @@ __device__ __forceinline__ void epi_prefetch(const GemmArgs& a, int nthr, int n0
 // RMSNorm factor applied).  s_scale: the 16 rows' scales (for SwiGLU, whose
 // threads need two rows).  TLD: row stride of the partial tiles in LDS, odd so
 // that the 16 rows a thread group reads fall in distinct banks.
-template <int NW, int TLD, int R>
+// s_ssp: the statistics partials ([SG][MV], summed here per row when SG <= 32, so
+// that no second barrier is needed); s_inv: the rows' norm factors otherwise.
+template <int NW, int TLD, int R, int MV, int SG>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, int n0,
                                               const float (*red)[kGemmRows * R * TLD],
-                                              const float* s_inv, const float* s_scale,
-                                              const EpiPrefetch& pf) {
+                                              const float* s_inv, const float* s_ssp,
+                                              const float* s_scale, const EpiPrefetch& pf) {
   const int M = a.M;
   const int tid = threadIdx.x;
   constexpr int nthr = NW * 64;
-  auto y = [&](int r, int m) -> float {
+  auto inv_row = [&](int m) -> float {
+    if (!a.ss_in) return 1.f;
+    if constexpr (SG <= 32) {
+      float ss = 0.f;
+#pragma unroll
+      for (int g = 0; g < SG; ++g) ss += s_ssp[g * MV + m];
+      return 1.0f / sqrtf(ss / (float)a.K + a.norm_eps);
+    } else {
+      return s_inv[m];
+    }
+  };
+  auto y = [&](int r, int m, float inv) -> float {
     float v = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) v += red[w][r * TLD + m];
     if (a.scale) v *= s_scale[r];
-    if (a.ss_in) v *= s_inv[m];
+    if (a.ss_in) v *= inv;
     return v;
   };
   if (a.epi == EPI_SWIGLU) {
     // rows 2p (gate) and 2p+1 (up) of the block's 16R -> output column n0/2 + p
     for (int e = tid; e < 8 * R * M; e += nthr) {
       const int m = e / (8 * R), p = e - m * (8 * R);
-      const float v = silu(y(2 * p, m)) * y(2 * p + 1, m);
+      const float inv = inv_row(m);
+      const float v = silu(y(2 * p, m, inv)) * y(2 * p + 1, m, inv);
       a.u[chunked(m, (n0 >> 1) + p, a.u_ld)] = f2h(v);
     }
     return;
@@ -151,7 +165,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, int n0,
     const int e = tid + k * nthr;
     if (e >= kGemmRows * M) break;  // whole 16-lane groups leave together
     const int m = e >> 4, r = e & 15;
-    float v = y(r, m);
+    float v = y(r, m, inv_row(m));
     if (a.epi == EPI_STORE) {
       a.out_f32[(size_t)m * a.out_ld + n0 + r] = v;
     } else if (logits) {
@@ -351,28 +365,22 @@ __global__ __launch_bounds__(NW * 64) void k_gemm(GemmArgs args_in, int msplit) 
   if (a.ss_in) s_ssp[tid] = ss_partial(a, ssp);
   if (tid < kGemmRows * R) s_scale[tid] = pf.scale;
   __syncthreads();
-  if (a.ss_in) {
-    // row m's G partials, summed in a fixed order: by one thread when there are
-    // few of them (many rows), else by a wave (tree sum over its lanes)
-    constexpr int SG = SsPrefetch<MV, NW * 64>::G;
-    if constexpr (SG <= 32) {
-      if (tid < M) {
-        float ss = 0.f;
-#pragma unroll
-        for (int g = 0; g < SG; ++g) ss += s_ssp[g * MV + tid];
-        s_inv[tid] = 1.0f / sqrtf(ss / (float)a.K + a.norm_eps);
-      }
-    } else {
+  // row m's SG statistics partials are summed in a fixed order: few of them (many
+  // rows) by every epilogue thread of the row itself, else by a wave (tree sum
+  // over its lanes) before a second barrier
+  constexpr int SG = SsPrefetch<MV, NW * 64>::G;
+  if constexpr (SG > 32) {
+    if (a.ss_in) {
       for (int m = wave; m < M; m += NW) {
         float ss = 0.f;
         for (int g = lane; g < SG; g += 64) ss += s_ssp[g * MV + m];
         ss = wave_sum(ss);
         if (lane == 0) s_inv[m] = 1.0f / sqrtf(ss / (float)a.K + a.norm_eps);
       }
+      __syncthreads();
     }
-    __syncthreads();
   }
-  gemm_epilogue<NW, TLD, R>(a, n0, red, s_inv, s_scale, pf);
+  gemm_epilogue<NW, TLD, R, MV, SG>(a, n0, red, s_inv, s_ssp, s_scale, pf);
 }
 
 template <bool I8, bool KEEP>
