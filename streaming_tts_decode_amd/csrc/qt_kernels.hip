@@ -32,13 +32,13 @@ __device__ __forceinline__ float norm_rope_128(float v, int d, float gain, float
   buf[d] = nv;
   __syncthreads();
   const int i = d & 63;
-  // angle = pos * theta^(-2i/128), reduced mod 2*pi in double before the float sincos
-  const double inv_freq = exp2(-(double)(2 * i) * (double)theta_log2 / 128.0);
-  double ang = (double)pos * inv_freq;
-  const double two_pi = 6.283185307179586476925286766559;
-  ang -= two_pi * floor(ang / two_pi);
-  float sn, cs;
-  sincosf((float)ang, &sn, &cs);
+  // angle = pos * theta^(-2i/128), in revolutions and reduced to [0, 1) in double;
+  // the hardware sine and cosine (arguments in revolutions) take it from there
+  const double inv_rev = exp2(-(double)(2 * i) * (double)theta_log2 / 128.0) *
+                         0.15915494309189533576888376337251;  // 1 / (2 pi)
+  double rev = (double)pos * inv_rev;
+  rev -= floor(rev);
+  const float sn = __builtin_amdgcn_sinf((float)rev), cs = __builtin_amdgcn_cosf((float)rev);
   const float partner = buf[d ^ 64];
   return (d < 64) ? nv * cs - partner * sn : nv * cs + partner * sn;
 }
