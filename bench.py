@@ -31,7 +31,7 @@ HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 # change, the entry no longer applies and `traffic` is reported as null.
 PMC_TRAFFIC = {
     # profiles/gemm_attention_C4_pmc_traffic.md
-    ("C4", "k_attn_paged"): {"digest": "8d83d0c9b2274dbb", "bytes_per_launch": 168137178},
+    ("C4", "k_attn_paged"): {"digest": "a3b7fbcddbdd7624", "bytes_per_launch": 168113969},
 }
 KERNEL_SOURCES = ["qt_gemm.hip", "qt_kernels.hip", "qt_device.h", "qt_internal.h"]
 
