@@ -73,7 +73,6 @@ __global__ __launch_bounds__(256) void k_attn_paged(AttnPagedArgs a, float theta
   __shared__ float ssq[2][2];
   __shared__ float stat[2][2];
   __shared__ float mstat[2], lstat[2];
-  __shared__ float mred[2][2];
   __shared__ int s_last;
 
   const int cap = a.max_pages * kPage;
@@ -276,22 +275,37 @@ __global__ __launch_bounds__(256) void k_attn_paged(AttnPagedArgs a, float theta
   }
   __syncthreads();
   if (!s_last) return;
-  // merge: the running maximum over splits (threads of a head split the splits
-  // between them), then every thread sums its dimension over the splits in order
+  // merge, 16 splits per round trip: every thread loads the splits' (max, sum)
+  // and its own dimension of their outputs at once (indices past the last split
+  // repeat it and are masked), then folds them into a running (max, sum, output)
+  // in split order
   const float* pb = a.part + ((size_t)b * a.n_q + j0 + jj) * a.n_splits * 130;
-  float M = -INFINITY;
-  for (int ss = d; ss < n_active; ss += 128) M = fmaxf(M, dev_load(pb + ss * 130));
-  M = wave_max(M);
-  if (lane == 0) mred[jj][wave & 1] = M;
-  __syncthreads();
-  M = fmaxf(mred[jj][0], mred[jj][1]);
-  float L = 0.f, O = 0.f;
-#pragma unroll 8
-  for (int ss = 0; ss < n_active; ++ss) {
-    const float* ps = pb + ss * 130;
-    const float w = expf(dev_load(ps) - M);
-    L = fmaf(dev_load(ps + 1), w, L);
-    O = fmaf(dev_load(ps + 2 + d), w, O);
+  float M = -INFINITY, L = 0.f, O = 0.f;
+  for (int c0 = 0; c0 < n_active; c0 += 16) {
+    float mv[16], lv[16], ov[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const float* ps = pb + (size_t)min(c0 + k, n_active - 1) * 130;
+      mv[k] = dev_load(ps);
+      lv[k] = dev_load(ps + 1);
+      ov[k] = dev_load(ps + 2 + d);
+    }
+    float Mc = M;
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      if (c0 + k < n_active) Mc = fmaxf(Mc, mv[k]);
+    const float r = expf(M - Mc);  // 0 on the first chunk (M = -inf, Mc finite)
+    L *= r;
+    O *= r;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      if (c0 + k < n_active) {
+        const float w = expf(mv[k] - Mc);
+        L = fmaf(lv[k], w, L);
+        O = fmaf(ov[k], w, O);
+      }
+    }
+    M = Mc;
   }
   a.o[orow] = f2h(O / L);
   if (tid == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
