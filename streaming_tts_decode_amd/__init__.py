@@ -26,7 +26,14 @@ EXPORTED = ["qt_last_error", "qt_abi_version", "qt_validate_cfg", "qt_packed_byt
             "qt_workspace_bytes", "qt_load_weights", "qt_quantize_int8", "qt_model_export_int8",
             "qt_frame_decode", "qt_frame_graph_create", "qt_frame_graph_launch",
             "qt_graph_destroy", "qt_model_destroy", "qt_trace_create", "qt_frame_launch_count",
-            "qt_frame_trace", "qt_trace_read", "qt_trace_destroy"]
+            "qt_frame_trace", "qt_trace_read", "qt_trace_destroy",
+            # qt_sched.h
+            "qt_sched_bytes", "qt_sched_create", "qt_sched_open", "qt_sched_submit",
+            "qt_sched_step", "qt_sched_outputs", "qt_sched_state", "qt_sched_length",
+            "qt_sched_status_word", "qt_sched_free_pages", "qt_sched_close", "qt_sched_plan",
+            "qt_sched_destroy"]
+SCHED_MAX_BUCKETS, SCHED_MAX_BATCH, SCHED_MAX_SESSIONS = 8, 32, 4096
+SESSION_FREE, SESSION_RUNNING, SESSION_ENDED_EOS, SESSION_ENDED_MAX = 0, 1, 2, 3
 KERNEL_KINDS = {0: "frame_begin", 1: "gemm", 2: "attn_paged", 3: "attn_pred", 4: "embed",
                 5: "frame_end"}
 
@@ -77,6 +84,19 @@ class LaunchInfo(C.Structure):
     _fields_ = [("kind", C.c_int32), ("step", C.c_int32), ("layer", C.c_int32), ("m", C.c_int32),
                 ("n", C.c_int32), ("k", C.c_int32), ("int8", C.c_int32), ("n_logits", C.c_int32),
                 ("name", C.c_char * 40)]
+
+
+class SchedCfg(C.Structure):
+    _fields_ = [("n_buckets", C.c_int32), ("buckets", C.c_int32 * SCHED_MAX_BUCKETS),
+                ("max_sessions", C.c_int32), ("max_pages", C.c_int32), ("eos_index", C.c_int32)]
+
+
+def make_sched_cfg(buckets, max_sessions: int, max_pages: int, eos_index: int = -1) -> SchedCfg:
+    """n_buckets is len(buckets) even beyond SCHED_MAX_BUCKETS, which the library rejects."""
+    buckets = list(buckets)
+    kept = buckets[:SCHED_MAX_BUCKETS]
+    arr = (C.c_int32 * SCHED_MAX_BUCKETS)(*(kept + [0] * (SCHED_MAX_BUCKETS - len(kept))))
+    return SchedCfg(len(buckets), arr, max_sessions, max_pages, eos_index)
 
 
 _lib = None
@@ -132,6 +152,36 @@ def lib():
                                     C.POINTER(C.c_int32)]
         L.qt_trace_destroy.restype = None
         L.qt_trace_destroy.argtypes = [_P]
+        i32p = C.POINTER(C.c_int32)
+        L.qt_sched_bytes.restype = st
+        L.qt_sched_bytes.argtypes = [C.POINTER(ModelCfg), C.POINTER(SchedCfg),
+                                     C.POINTER(C.c_uint64), C.POINTER(C.c_uint64)]
+        L.qt_sched_create.restype = st
+        L.qt_sched_create.argtypes = [_P, C.POINTER(SchedCfg), C.POINTER(KvCaches), _P, C.c_uint64,
+                                      _P, C.c_uint64, _P, C.POINTER(_P)]
+        L.qt_sched_open.restype = st
+        L.qt_sched_open.argtypes = [_P, C.c_int32, C.c_int32, C.c_int32, i32p, i32p]
+        L.qt_sched_submit.restype = st
+        L.qt_sched_submit.argtypes = [_P, C.c_int32, _P, _P]
+        L.qt_sched_step.restype = st
+        L.qt_sched_step.argtypes = [_P, i32p]
+        L.qt_sched_outputs.restype = st
+        L.qt_sched_outputs.argtypes = [_P, C.c_int32, C.POINTER(_P), C.POINTER(_P), C.POINTER(_P),
+                                       i32p]
+        L.qt_sched_state.restype = st
+        L.qt_sched_state.argtypes = [_P, C.c_int32, i32p, i32p]
+        L.qt_sched_length.restype = st
+        L.qt_sched_length.argtypes = [_P, C.c_int32, i32p]
+        L.qt_sched_status_word.restype = st
+        L.qt_sched_status_word.argtypes = [_P, C.POINTER(_P)]
+        L.qt_sched_free_pages.restype = st
+        L.qt_sched_free_pages.argtypes = [_P, i32p]
+        L.qt_sched_close.restype = st
+        L.qt_sched_close.argtypes = [_P, C.c_int32]
+        L.qt_sched_plan.restype = st
+        L.qt_sched_plan.argtypes = [i32p, C.c_int32, i32p, C.c_int32, i32p, i32p, i32p]
+        L.qt_sched_destroy.restype = None
+        L.qt_sched_destroy.argtypes = [_P]
         _lib = L
     return _lib
 
@@ -262,3 +312,96 @@ def qt_trace_read(trace: int, max_launches: int):
 
 def qt_trace_destroy(trace: int) -> None:
     lib().qt_trace_destroy(trace)
+
+
+# --------------------------------------------------------------------------- scheduler (qt_sched.h)
+def qt_sched_bytes(cfg: ModelCfg, scfg: SchedCfg):
+    """(device_bytes, host_bytes) the scheduler needs."""
+    d, h = C.c_uint64(), C.c_uint64()
+    _check(lib().qt_sched_bytes(C.byref(cfg), C.byref(scfg), C.byref(d), C.byref(h)),
+           "qt_sched_bytes")
+    return d.value, h.value
+
+
+def qt_sched_create(model: int, scfg: SchedCfg, kv: KvCaches, device_ptr: int, device_bytes: int,
+                    host_ptr: int, host_bytes: int, stream: int = 0) -> int:
+    out = _P()
+    _check(lib().qt_sched_create(model, C.byref(scfg), C.byref(kv), device_ptr, device_bytes,
+                                 host_ptr, host_bytes, stream, C.byref(out)), "qt_sched_create")
+    return out.value
+
+
+def qt_sched_open(sched: int, length: int, min_frames: int, max_frames: int,
+                  page_size: int = 16):
+    """Returns (session id, list of the page ids that hold positions [0, length))."""
+    n = -(-length // page_size) if length > 0 else 0
+    pages = (C.c_int32 * max(n, 1))()
+    sid = C.c_int32()
+    _check(lib().qt_sched_open(sched, length, min_frames, max_frames, pages, C.byref(sid)),
+           "qt_sched_open")
+    return sid.value, list(pages)[:n]
+
+
+def qt_sched_submit(sched: int, session: int, talker_in_ptr: int, forced_ptr: int | None = None):
+    _check(lib().qt_sched_submit(sched, session, talker_in_ptr, forced_ptr), "qt_sched_submit")
+
+
+def qt_sched_step(sched: int) -> int:
+    ng = C.c_int32()
+    _check(lib().qt_sched_step(sched, C.byref(ng)), "qt_sched_step")
+    return ng.value
+
+
+def qt_sched_outputs(sched: int, session: int):
+    """(logits0_ptr, logits_pred_ptr, tokens_ptr, frames)."""
+    a, b, c, f = _P(), _P(), _P(), C.c_int32()
+    _check(lib().qt_sched_outputs(sched, session, C.byref(a), C.byref(b), C.byref(c), C.byref(f)),
+           "qt_sched_outputs")
+    return a.value, b.value, c.value, f.value
+
+
+def qt_sched_state(sched: int, session: int):
+    """(qt_session_state, end_frame)."""
+    st, ef = C.c_int32(), C.c_int32()
+    _check(lib().qt_sched_state(sched, session, C.byref(st), C.byref(ef)), "qt_sched_state")
+    return st.value, ef.value
+
+
+def qt_sched_length(sched: int, session: int) -> int:
+    n = C.c_int32()
+    _check(lib().qt_sched_length(sched, session, C.byref(n)), "qt_sched_length")
+    return n.value
+
+
+def qt_sched_status_word(sched: int) -> int:
+    p = _P()
+    _check(lib().qt_sched_status_word(sched, C.byref(p)), "qt_sched_status_word")
+    return p.value
+
+
+def qt_sched_free_pages(sched: int) -> int:
+    n = C.c_int32()
+    _check(lib().qt_sched_free_pages(sched, C.byref(n)), "qt_sched_free_pages")
+    return n.value
+
+
+def qt_sched_close(sched: int, session: int) -> None:
+    _check(lib().qt_sched_close(sched, session), "qt_sched_close")
+
+
+def qt_sched_plan(cls, buckets):
+    """(group_of list, group_bucket list) for ready sessions of classes `cls`."""
+    cls = list(cls)
+    buckets = list(buckets)
+    n = len(cls)
+    c_cls = (C.c_int32 * max(n, 1))(*cls)
+    c_b = (C.c_int32 * max(len(buckets), 1))(*buckets)
+    g_of = (C.c_int32 * max(n, 1))()
+    g_b = (C.c_int32 * max(n, 1))()
+    ng = C.c_int32()
+    _check(lib().qt_sched_plan(c_cls, n, c_b, len(buckets), g_of, g_b, C.byref(ng)), "qt_sched_plan")
+    return list(g_of)[:n], list(g_b)[:ng.value]
+
+
+def qt_sched_destroy(sched: int) -> None:
+    lib().qt_sched_destroy(sched)

@@ -699,6 +699,20 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
 
 }  // namespace
 
+namespace qt {
+const qt_model_cfg* model_cfg(const qt_model* m) { return &m->cfg; }
+
+qt_status report(qt_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+}  // namespace qt
+
 // ------------------------------------------------------------------ exported
 extern "C" {
 

@@ -200,6 +200,49 @@ struct FrameEndArgs {
   int32_t* kv_len;
 };
 
+// Scheduler helpers (qt_sched.cpp): per-group batch tables in, per-session results out.
+constexpr int kSchedMaxBatch = 32;
+
+struct SchedSetupArgs {
+  int B, H, ncb, max_pages, pad_page;
+  const int32_t* host_pages;     // pinned host [max_sessions][max_pages]: rows at open
+  int32_t* sess_pages;           // device [max_sessions][max_pages]
+  int32_t* kv_len;               // batch [B]
+  int32_t* page_table;           // batch [B][max_pages]
+  uint16_t* talker_in;           // batch [B][H]
+  int32_t* forced;               // batch [B][ncb] (nullptr: the group is not teacher-forced)
+  int32_t* flags;                // device [max_sessions]: frame that ended the session, or 0
+  int32_t slot_session[kSchedMaxBatch];  // -1: padding slot
+  int32_t slot_len[kSchedMaxBatch];      // cached positions before this frame
+  int32_t slot_first[kSchedMaxBatch];    // pages held at open if this is the first frame, else -1
+  int32_t new_index[kSchedMaxBatch];     // page appended this frame at this row index, or -1
+  int32_t new_page[kSchedMaxBatch];
+  const uint16_t* in_ptr[kSchedMaxBatch];
+  const int32_t* forced_ptr[kSchedMaxBatch];
+};
+
+struct SchedCollectArgs {
+  int B, talker_vocab, cb0_range, pred_elems, ncb, eos_index;
+  const float* logits0;          // batch outputs
+  const float* logits_pred;
+  const int32_t* tokens;
+  float* res_logits0;            // per session
+  float* res_pred;
+  int32_t* res_tokens;
+  int32_t* flags;                // device [max_sessions]
+  int32_t* host_flags;           // pinned host [max_sessions]
+  int32_t slot_session[kSchedMaxBatch];
+  int32_t slot_check[kSchedMaxBatch];    // frame number to record at end of speech, or 0
+};
+
+hipError_t launch_sched_setup(const SchedSetupArgs& a, hipStream_t s);
+hipError_t launch_sched_collect(const SchedCollectArgs& a, hipStream_t s);
+
+// Configuration of a loaded model, and the thread-local error text behind
+// qt_last_error() (qt_abi.cpp).
+const qt_model_cfg* model_cfg(const qt_model* m);
+qt_status report(qt_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+
 // launchers (enqueue only; shapes are validated by the caller)
 GemmPlan plan_gemm(int nrows, int K, int M, bool i8, bool keep, bool swiglu = false);
 // Kernel symbol (with template arguments) that launch_gemm picks for these arguments.

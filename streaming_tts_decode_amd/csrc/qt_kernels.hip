@@ -558,6 +558,84 @@ __global__ __launch_bounds__(256) void k_quantize(const uint16_t* w, long long c
   }
 }
 
+// ---------------------------------------------------------------------------
+// Scheduler helpers, one block per batch slot.
+// Setup: the slot's cache length, page-table row, Talker input row and forced tokens.
+// On a session's first frame its row comes from the host mirror written at open
+// (read at system scope, so no stale cache line is used); a page appended this
+// frame is also stored into the session's device row.  Padding slots get length 0,
+// the padding page and a zero input.
+// Collect: the slot's outputs copied to its session's result rows and, where asked,
+// the end-of-speech decision: the entry wins the codebook-0 choice (lowest index
+// wins ties) -> the frame number goes to the device flag and the host buffer.
+__global__ __launch_bounds__(256) void k_sched_setup(SchedSetupArgs a) {
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int sess = a.slot_session[b];
+  int32_t* row = a.page_table + (size_t)b * a.max_pages;
+  uint4* in_row = reinterpret_cast<uint4*>(a.talker_in + (size_t)b * a.H);
+  if (sess < 0) {
+    for (int i = tid; i < a.max_pages; i += 256) row[i] = a.pad_page;
+    for (int i = tid; i < a.H / 8; i += 256) in_row[i] = make_uint4(0, 0, 0, 0);
+    if (a.forced)
+      for (int i = tid; i < a.ncb; i += 256) a.forced[(size_t)b * a.ncb + i] = 0;
+    if (tid == 0) a.kv_len[b] = 0;
+    return;
+  }
+  int32_t* dev_row = a.sess_pages + (size_t)sess * a.max_pages;
+  const int first = a.slot_first[b];
+  for (int i = tid; i < a.max_pages; i += 256) {
+    int32_t v;
+    if (i == a.new_index[b]) {
+      v = a.new_page[b];
+    } else if (first >= 0) {
+      v = i < first ? __hip_atomic_load(a.host_pages + (size_t)sess * a.max_pages + i,
+                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM)
+                    : a.pad_page;
+    } else {
+      v = dev_row[i];
+    }
+    row[i] = v;
+    if (first >= 0 || i == a.new_index[b]) dev_row[i] = v;
+  }
+  const uint4* in = reinterpret_cast<const uint4*>(a.in_ptr[b]);
+  for (int i = tid; i < a.H / 8; i += 256) in_row[i] = in[i];
+  if (a.forced) {
+    const int32_t* f = a.forced_ptr[b];
+    for (int i = tid; i < a.ncb; i += 256) a.forced[(size_t)b * a.ncb + i] = f ? f[i] : 0;
+  }
+  if (tid == 0) {
+    a.kv_len[b] = a.slot_len[b];
+    if (first >= 0) a.flags[sess] = 0;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_sched_collect(SchedCollectArgs a) {
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int sess = a.slot_session[b];
+  if (sess < 0) return;
+  const float4* l0 = reinterpret_cast<const float4*>(a.logits0 + (size_t)b * a.talker_vocab);
+  float4* r0 = reinterpret_cast<float4*>(a.res_logits0 + (size_t)sess * a.talker_vocab);
+  for (int i = tid; i < a.talker_vocab / 4; i += 256) r0[i] = l0[i];
+  const float4* lp = reinterpret_cast<const float4*>(a.logits_pred + (size_t)b * a.pred_elems);
+  float4* rp = reinterpret_cast<float4*>(a.res_pred + (size_t)sess * a.pred_elems);
+  for (int i = tid; i < a.pred_elems / 4; i += 256) rp[i] = lp[i];
+  for (int i = tid; i < a.ncb; i += 256)
+    a.res_tokens[(size_t)sess * a.ncb + i] = a.tokens[(size_t)b * a.ncb + i];
+  if (tid == 0 && a.eos_index >= 0 && a.slot_check[b] > 0 && a.flags[sess] == 0) {
+    const float* lg = a.logits0 + (size_t)b * a.talker_vocab;
+    const int t0 = a.tokens[(size_t)b * a.ncb];
+    const int e = a.eos_index;
+    bool end = false;
+    if (t0 >= 0 && t0 < a.cb0_range)
+      end = e == t0 || (e < t0 ? lg[e] >= lg[t0] : lg[e] > lg[t0]);
+    if (end) {
+      a.flags[sess] = a.slot_check[b];
+      __hip_atomic_store(a.host_flags + sess, a.slot_check[b], __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+  }
+}
+
 }  // namespace
 
 // --------------------------------------------------------------------------- launchers
@@ -612,4 +690,19 @@ hipError_t launch_quantize(const uint16_t* w, long long rows, long long cols, in
   return hipGetLastError();
 }
 
+}  // namespace qt
+
+namespace qt {
+hipError_t launch_sched_setup(const SchedSetupArgs& a, hipStream_t s) {
+  if (a.B < 1 || a.B > kSchedMaxBatch || (a.H % 8)) return hipErrorInvalidValue;
+  launch_kernel(k_sched_setup, dim3(a.B), dim3(256), s, a);
+  return hipGetLastError();
+}
+hipError_t launch_sched_collect(const SchedCollectArgs& a, hipStream_t s) {
+  if (a.B < 1 || a.B > kSchedMaxBatch || (a.talker_vocab % 4) || (a.pred_elems % 4) ||
+      a.eos_index < -1 || a.eos_index >= a.talker_vocab)
+    return hipErrorInvalidValue;
+  launch_kernel(k_sched_collect, dim3(a.B), dim3(256), s, a);
+  return hipGetLastError();
+}
 }  // namespace qt

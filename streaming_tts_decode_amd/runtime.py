@@ -10,10 +10,13 @@ from __future__ import annotations
 import numpy as np
 
 from . import (KERNEL_KINDS, FrameInputs, FrameOutputs, KvCaches, MODES, QT_BF16, Sessions,
-               make_cfg, qt_frame_decode, qt_frame_graph_create, qt_frame_graph_launch,
-               qt_frame_launch_count, qt_frame_trace, qt_graph_destroy, qt_load_weights,
-               qt_model_destroy, qt_packed_bytes, qt_trace_create, qt_trace_destroy,
-               qt_trace_read, qt_workspace_bytes)
+               make_cfg, make_sched_cfg, qt_frame_decode, qt_frame_graph_create,
+               qt_frame_graph_launch, qt_frame_launch_count, qt_frame_trace, qt_graph_destroy,
+               qt_load_weights, qt_model_destroy, qt_packed_bytes, qt_sched_bytes, qt_sched_close,
+               qt_sched_create, qt_sched_destroy, qt_sched_free_pages, qt_sched_length,
+               qt_sched_open, qt_sched_outputs, qt_sched_state, qt_sched_status_word,
+               qt_sched_step, qt_sched_submit, qt_trace_create, qt_trace_destroy, qt_trace_read,
+               qt_workspace_bytes)
 
 PAGE = 16
 
@@ -26,6 +29,22 @@ def _aligned(torch, nbytes: int, device, align: int = 256):
 
 def _bits(torch, a: np.ndarray, device):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)).to(device)
+
+
+def _write_pages(torch, k_pool, v_pool, pages, k_bits: np.ndarray, v_bits: np.ndarray):
+    """Store a prefilled cache ([layers, L, n_kv, hd] bf16 bits) into `pages` (page
+    ids in position order) of the pools [layers][num_pages][n_kv][PAGE][hd]."""
+    layers, L, nkv, hd = k_bits.shape
+    npg = len(pages)
+    if npg == 0:
+        return
+    dev = k_pool.device
+    idx = torch.from_numpy(np.asarray(pages, dtype=np.int64)).to(dev)
+    for src, pool in ((k_bits, k_pool), (v_bits, v_pool)):
+        x = np.zeros((layers, npg * PAGE, nkv, hd), dtype=np.uint16)
+        x[:, :L] = src
+        t = _bits(torch, x, dev).view(layers, npg, PAGE, nkv, hd).permute(0, 1, 3, 2, 4)
+        pool[:, idx] = t
 
 
 class PackedModel:
@@ -124,13 +143,7 @@ class Decoder:
         npg = -(-L // PAGE)
         if npg > self.max_pages:
             raise ValueError(f"session {b}: {L} positions need {npg} pages > {self.max_pages}")
-        if npg:
-            pages = torch.from_numpy(self.page_table_np[b, :npg].astype(np.int64)).to(self.dev)
-            for src, pool in ((k_bits, self.k_pages), (v_bits, self.v_pages)):
-                x = np.zeros((layers, npg * PAGE, nkv, hd), dtype=np.uint16)
-                x[:, :L] = src
-                t = _bits(torch, x, self.dev).view(layers, npg, PAGE, nkv, hd).permute(0, 1, 3, 2, 4)
-                pool[:, pages] = t
+        _write_pages(torch, self.k_pages, self.v_pages, self.page_table_np[b, :npg], k_bits, v_bits)
         self.kv_len[b] = L
 
     def set_lengths(self, lengths):
@@ -220,3 +233,97 @@ def setup_workload(w, model: PackedModel, kv_pool=None):
                 dec.load_session_kv(b, kb, vb)
     dec.torch.cuda.synchronize(dec.dev)
     return dec, lengths
+
+
+class Scheduler:
+    """The library's lockstep scheduler (qt_sched.h) with its buffers: a Talker KV
+    pool of num_pages pages, the scheduler's device buffer and its pinned host
+    buffer.  Every step enqueues on the stream current at construction."""
+
+    def __init__(self, model: PackedModel, buckets=(1, 2, 4, 8, 16, 32), max_sessions: int = 32,
+                 max_pages: int = 8, num_pages: int | None = None, eos_index: int = -1):
+        import torch
+        self.torch = torch
+        self.pm = model
+        self.dims = model.dims
+        self.dev = model.dev
+        t = self.dims.talker
+        self.num_pages = num_pages if num_pages is not None else max_sessions * max_pages + 1
+        self.max_pages = max_pages
+        self.scfg = make_sched_cfg(buckets, max_sessions, max_pages, eos_index)
+        dev_bytes, host_bytes = qt_sched_bytes(model.cfg, self.scfg)
+        self._dev_buf, self.dev_ptr = _aligned(torch, dev_bytes, self.dev)
+        self._dev_off = self.dev_ptr - self._dev_buf.data_ptr()
+        self._host_buf = torch.empty(host_bytes + 256, dtype=torch.uint8, pin_memory=True)
+        self.host_ptr = self._host_buf.data_ptr() + (-self._host_buf.data_ptr()) % 256
+        shape = (t.layers, self.num_pages, t.n_kv, PAGE, t.head_dim)
+        self.k_pages = torch.zeros(shape, dtype=torch.int16, device=self.dev)
+        self.v_pages = torch.zeros(shape, dtype=torch.int16, device=self.dev)
+        self.kv = KvCaches(self.k_pages.data_ptr(), self.v_pages.data_ptr(), self.num_pages)
+        self.stream = torch.cuda.current_stream(self.dev)
+        self.handle = qt_sched_create(model.handle, self.scfg, self.kv, self.dev_ptr, dev_bytes,
+                                      self.host_ptr, host_bytes, self.stream.cuda_stream)
+        self._held = []
+
+    def _view(self, ptr: int, dtype, shape):
+        torch = self.torch
+        esize = torch.tensor([], dtype=dtype).element_size()
+        off = ptr - self._dev_buf.data_ptr()
+        n = int(np.prod(shape))
+        return self._dev_buf[off:off + n * esize].view(dtype).view(*shape)
+
+    def open(self, length: int, k_bits=None, v_bits=None, min_frames: int = 1,
+             max_frames: int = 1 << 30) -> int:
+        """Open a session with `length` prefilled positions (K/V bits [layers, length,
+        n_kv, hd]), written into the pages the scheduler hands out."""
+        sid, pages = qt_sched_open(self.handle, length, min_frames, max_frames, PAGE)
+        if length:
+            _write_pages(self.torch, self.k_pages, self.v_pages, pages, k_bits, v_bits)
+        return sid
+
+    def submit(self, sid: int, talker_in, forced=None):
+        """talker_in: device int16 [talker hidden] (bf16 bits); forced: device int32
+        [n_codebooks] or None.  Both are kept alive until the next step is enqueued."""
+        qt_sched_submit(self.handle, sid, talker_in.data_ptr(),
+                        forced.data_ptr() if forced is not None else None)
+        self._held.append((talker_in, forced))
+
+    def step(self) -> int:
+        n = qt_sched_step(self.handle)
+        self._held = []
+        return n
+
+    def outputs(self, sid: int):
+        """(logits0 [talker_vocab], logits_pred [n_codebooks-1, code_vocab], tokens
+        [n_codebooks], frames) as views of the scheduler's device buffer."""
+        torch, d = self.torch, self.dims
+        l0, lp, tok, frames = qt_sched_outputs(self.handle, sid)
+        return (self._view(l0, torch.float32, (d.talker_vocab,)),
+                self._view(lp, torch.float32, (d.n_steps, d.code_vocab)),
+                self._view(tok, torch.int32, (d.n_codebooks,)), frames)
+
+    def state(self, sid: int):
+        return qt_sched_state(self.handle, sid)
+
+    def length(self, sid: int) -> int:
+        return qt_sched_length(self.handle, sid)
+
+    def free_pages(self) -> int:
+        return qt_sched_free_pages(self.handle)
+
+    def close_session(self, sid: int):
+        qt_sched_close(self.handle, sid)
+
+    def status(self) -> int:
+        return int(self._view(qt_sched_status_word(self.handle), self.torch.int32, (1,)).item())
+
+    def close(self):
+        if self.handle:
+            qt_sched_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
