@@ -124,7 +124,58 @@ def trace_frames(dec, d, lengths, n, int8, log):
     return per, total / n
 
 
-def run_workload(pm, w, steps, warmup, log, n_trace=0):
+def run_scheduler(pm, w, dec, lengths, steps, warmup, log):
+    """The same workload decoded through the library's lockstep scheduler
+    (qt_sched.h): every session submits its Talker input row and one qt_sched_step
+    per frame decodes them all (captured sizes 1..32, so B=32 is one call).  The
+    prefilled caches are copied device to device from `dec`'s pages into the pages
+    the scheduler hands out.  GPU time is taken with events on the scheduler's
+    stream around `steps` frames; host time is the loop's wall clock per frame."""
+    import numpy as np
+    import torch
+
+    import synth
+    from streaming_tts_decode_amd.runtime import PAGE, Scheduler
+    frames = steps + warmup
+    max_pages = int(max(-(-(int(L) + frames + 1) // PAGE) for L in lengths))
+    sch = Scheduler(pm, buckets=(1, 2, 4, 8, 16, 32), max_sessions=w.batch, max_pages=max_pages,
+                    num_pages=w.batch * max_pages + 1)
+    sids = [sch.open(int(lengths[b]), copy_from=(dec.k_pages, dec.v_pages, dec.page_table_np[b]))
+            for b in range(w.batch)]
+    ins = synth.frame_inputs(w)["talker_in"]
+    talker_all = torch.from_numpy(ins.view(np.int16)).to(dec.dev)
+    for f in range(warmup):
+        for b, sid in enumerate(sids):
+            sch.submit(sid, talker_all[f % w.frames, b])
+        sch.step()
+    torch.cuda.synchronize()
+    stream = sch.stream
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    t0 = time.perf_counter()
+    groups = 0
+    for f in range(steps):
+        for b, sid in enumerate(sids):
+            sch.submit(sid, talker_all[(warmup + f) % w.frames, b])
+        groups += sch.step()
+    host = time.perf_counter() - t0
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1)
+    status = sch.status()
+    if status:
+        raise RuntimeError(f"scheduler {w.name}: device status {status:#x}")
+    sch.close()
+    res = {"codec_frames_per_s": w.batch * steps / (ms / 1e3), "ms_per_frame": ms / steps,
+           "host_ms_per_frame": 1e3 * host / steps, "calls_per_step": groups / steps,
+           "pages": "handed out by the scheduler's free list: consecutive in a fresh pool "
+                    "(the headline frame uses a shuffled pool)"}
+    log(f"[bench] scheduler {w.name}: {res}")
+    return res
+
+
+def run_workload(pm, w, steps, warmup, log, n_trace=0, sched=False):
     import numpy as np
     import torch
 
@@ -172,6 +223,12 @@ def run_workload(pm, w, steps, warmup, log, n_trace=0):
     res["hbm_frac"] = res["hbm_gbs_algorithmic"] / HBM_PEAK_GBS
     log(f"[bench] { {k: v for k, v in res.items() if k != 'kernels'} }")
     dec.close()
+    if sched:
+        s = run_scheduler(pm, w, dec, lengths, steps, warmup, log)
+        s["vs_graph"] = s["codec_frames_per_s"] / res["codec_frames_per_s"]
+        res["scheduler"] = s
+    del dec
+    torch.cuda.empty_cache()
     return res, lengths
 
 
@@ -245,6 +302,8 @@ def main():
     ap.add_argument("--int8", action="store_true", help="INT8 weight-only decode")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-scheduler", action="store_true",
+                    help="skip timing the headline workload through the lockstep scheduler")
     ap.add_argument("--trace-frames", type=int, default=5,
                     help="eager frames timed launch by launch for the roofline")
     args = ap.parse_args()
@@ -275,7 +334,8 @@ def main():
     W = synth.gen_weights(d)
     pm = PackedModel(d, W, int8=head.int8)
     main_res, lengths = run_workload(pm, head, args.steps, args.warmup, log,
-                                     n_trace=max(1, args.trace_frames))
+                                     n_trace=max(1, args.trace_frames),
+                                     sched=not args.no_scheduler)
     extra = {}
     for name in [x for x in args.also.split(",") if x]:
         w = dataclasses.replace(synth.WORKLOADS[name], int8=head.int8)
@@ -307,6 +367,7 @@ def main():
         "frame_hbm_frac": main_res["hbm_frac"],
         "bytes_per_frame": main_res["bytes_per_frame"],
         "other_batches": extra,
+        "scheduler": main_res.get("scheduler"),
         "roofline": roofline(main_res, max(1, args.trace_frames)),
         "cpu_baseline": cpu,
     }

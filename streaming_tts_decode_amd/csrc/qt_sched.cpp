@@ -140,9 +140,11 @@ qt_status check_session(qt_sched* s, int32_t id) {
   return QT_OK;
 }
 
+// Pages go back in reverse so that the stack hands them out again in ascending
+// order: a session's consecutive pages keep its attention reads local in HBM.
 void release(qt_sched* s, int id) {
   Session& q = s->sess[id];
-  for (int32_t p : q.pages) s->free_pages.push_back(p);
+  for (auto it = q.pages.rbegin(); it != q.pages.rend(); ++it) s->free_pages.push_back(*it);
   q = Session();
   s->free_ids.push_back(id);
 }

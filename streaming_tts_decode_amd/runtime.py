@@ -273,11 +273,21 @@ class Scheduler:
         return self._dev_buf[off:off + n * esize].view(dtype).view(*shape)
 
     def open(self, length: int, k_bits=None, v_bits=None, min_frames: int = 1,
-             max_frames: int = 1 << 30) -> int:
-        """Open a session with `length` prefilled positions (K/V bits [layers, length,
-        n_kv, hd]), written into the pages the scheduler hands out."""
+             max_frames: int = 1 << 30, copy_from=None) -> int:
+        """Open a session with `length` prefilled positions, written into the pages the
+        scheduler hands out: from K/V bits [layers, length, n_kv, hd], or copied on
+        the device from copy_from = (k_pool, v_pool, page ids in position order) of
+        another pool with the same layout."""
         sid, pages = qt_sched_open(self.handle, length, min_frames, max_frames, PAGE)
-        if length:
+        if length and copy_from is not None:
+            torch = self.torch
+            k_src, v_src, src_pages = copy_from
+            dst = torch.as_tensor(np.asarray(pages, dtype=np.int64), device=self.dev)
+            src = torch.as_tensor(np.asarray(src_pages[:len(pages)], dtype=np.int64),
+                                  device=self.dev)
+            self.k_pages[:, dst] = k_src[:, src]
+            self.v_pages[:, dst] = v_src[:, src]
+        elif length:
             _write_pages(self.torch, self.k_pages, self.v_pages, pages, k_bits, v_bits)
         return sid
 
