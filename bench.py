@@ -213,12 +213,37 @@ def run_workload(pm, w, steps, warmup, log, n_trace=0, sched=False):
     nbytes = sum(frame_bytes(w.dims, lengths + f, pm.int8) for f in range(steps))
     per, traced_ms = (trace_frames(dec, w.dims, lengths + steps, n_trace, pm.int8, log)
                       if n_trace else (None, None))
+    sampled = None
+    if sched:
+        # the same frames drawing every codebook (qt_sampling) instead of the argmax
+        dec.set_sampling((0.9, 1.0, 1.05, 50), (0.9, 1.0, 1.0, 50), list(range(1, w.batch + 1)))
+        gs = dec.capture("full", forced=False, sampling=True)
+        for f in range(warmup):
+            dec.talker_in.copy_(talker_all[f % w.frames], non_blocking=True)
+            dec.replay(gs)
+        dec.kv_len.copy_(L0)
+        dec.status.zero_()
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for f in range(steps):
+            dec.talker_in.copy_(talker_all[f % w.frames], non_blocking=True)
+            dec.replay(gs)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        ms_s = ev0.elapsed_time(ev1)
+        if int(dec.status.item()):
+            raise RuntimeError(f"{w.name} sampled: device status {int(dec.status.item()):#x}")
+        sampled = {"codec_frames_per_s": w.batch * steps / (ms_s / 1e3), "ms_per_frame": ms_s / steps,
+                   "vs_greedy": ms / ms_s,
+                   "params": "codebook 0: T 0.9, top_k 50, top_p 1.0, penalty 1.05; "
+                             "predictor: T 0.9, top_k 50, top_p 1.0"}
+        log(f"[bench] sampled {w.name}: {sampled}")
     res = {
         "workload": w.name, "batch": w.batch, "frames": steps,
         "ms_per_frame": ms / steps, "codec_frames_per_s": w.batch * steps / (ms / 1e3),
         "hbm_gbs_algorithmic": nbytes / (ms / 1e3) / 1e9,
         "bytes_per_frame": nbytes / steps, "wall_s": wall,
-        "kernels": per, "traced_ms_per_frame": traced_ms,
+        "kernels": per, "traced_ms_per_frame": traced_ms, "sampled": sampled,
     }
     res["hbm_frac"] = res["hbm_gbs_algorithmic"] / HBM_PEAK_GBS
     log(f"[bench] { {k: v for k, v in res.items() if k != 'kernels'} }")
@@ -368,6 +393,7 @@ def main():
         "bytes_per_frame": main_res["bytes_per_frame"],
         "other_batches": extra,
         "scheduler": main_res.get("scheduler"),
+        "sampled": main_res.get("sampled"),
         "roofline": roofline(main_res, max(1, args.trace_frames)),
         "cpu_baseline": cpu,
     }

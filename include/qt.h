@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define QT_ABI_VERSION 1
+#define QT_ABI_VERSION 2
 
 typedef enum {
   QT_OK = 0,
@@ -81,6 +81,7 @@ typedef enum {
 #define QT_STATUS_BAD_PAGE 2u    /* a page id outside [0, num_pages): that page is read as zeros */
 #define QT_STATUS_BAD_TOKEN 4u   /* a forced / input token outside the code vocabulary: 0 used */
 #define QT_STATUS_NAN 8u         /* a NaN logit was produced */
+#define QT_STATUS_BAD_SAMPLER 16u /* sampler parameters out of range: that draw was greedy */
 
 /* One decoder stack (Qwen3-style: pre-norm, q/k RMSNorm, rotate-half RoPE,
  * grouped-query attention, SwiGLU).  This build supports head_dim = 128,
@@ -128,6 +129,44 @@ typedef struct {
   int32_t num_pages;
 } qt_kv_caches;
 
+/* ------------------------------------------------------------------ sampling
+ * Codec tokens drawn instead of taken greedily ("Qwen3-TTS PR 5", Graph: two
+ * samplers, the codebook-0 one with a repetition penalty; "Qwen3-TTS Native v0.3.0",
+ * What changed: sampling state, seen-token histories and random states stay per
+ * request, and seeded runs repeat exactly).  For one row of logits x over the
+ * draw range (codebook 0: [0, cb0_range) of logits0; predictor step k: its
+ * code_vocab logits), in float32:
+ *   1. codebook 0 only: an entry already in the session's seen set becomes
+ *      x / penalty if x > 0, else x * penalty;
+ *   2. z = x / temperature (a NaN z is never drawn);
+ *   3. the top_k largest z, ties to the lower index, ordered by (z descending,
+ *      index ascending), with weights w_j = exp(z_j - z_0);
+ *   4. the shortest prefix whose weight sum reaches top_p times the top_k total
+ *      is kept (at least one entry);
+ *   5. with r = u * (kept total), the token is the first kept entry whose running
+ *      weight sum exceeds r.
+ * u is the top 24 bits of word 0 of Philox4x64-10 (Salmon et al., SC 2011) with
+ * key (seed[b], 0) and counter ((uint32) counter[b], codebook, 0, 0), times 2^-24.
+ * Drawn tokens are what `tokens` reports; with `forced`, the predictor still
+ * embeds the forced tokens.  Codebook 0's drawn token is added to the seen set. */
+#define QT_SAMPLER_MAX_TOP_K 64
+
+typedef struct {
+  float temperature;        /* > 0 */
+  float top_p;              /* (0, 1] */
+  float repetition_penalty; /* >= 1, codebook 0 only (1: none) */
+  int32_t top_k;            /* 1 .. QT_SAMPLER_MAX_TOP_K */
+} qt_sampler_params;
+
+typedef struct {
+  const qt_sampler_params* params; /* device [B][2]: [b][0] codebook 0, [b][1] the predictor's codebooks */
+  const uint64_t* seed;            /* device [B]: per-session Philox key */
+  const int32_t* counter;          /* device [B]: per-session draw counter, e.g. kv_len (read before
+                                      the frame advances kv_len) */
+  uint32_t* seen0;                 /* device [B][(cb0_range + 31) / 32] bit sets of codebook-0 tokens
+                                      already emitted, or NULL (no penalty, no update) */
+} qt_sampling;
+
 typedef struct {
   int32_t mode;            /* qt_mode */
   const void* talker_in;   /* device bf16 [B][talker hidden]: the Talker input (FULL, TALKER) */
@@ -135,13 +174,15 @@ typedef struct {
   const int32_t* tok0_in;  /* device int32 [B]: codebook-0 tokens (PREDICTOR) */
   const int32_t* forced;   /* device int32 [B][n_codebooks] or NULL: teacher forcing; predictor
                               step k embeds forced[b][k-1] instead of the frame's own token */
+  const qt_sampling* sampling; /* host descriptor or NULL (greedy); its arrays are device memory */
 } qt_frame_inputs;
 
 typedef struct {
   float* logits0;      /* device f32 [B][talker_vocab] (FULL, TALKER) */
   float* logits_pred;  /* device f32 [B][n_codebooks-1][code_vocab] (FULL, PREDICTOR) */
-  int32_t* tokens;     /* device int32 [B][n_codebooks]: the frame's greedy tokens (lowest index
-                          wins ties); TALKER fills column 0, PREDICTOR copies tok0_in into it */
+  int32_t* tokens;     /* device int32 [B][n_codebooks]: the frame's tokens, greedy (lowest index
+                          wins ties) or drawn (qt_sampling); TALKER fills column 0, PREDICTOR
+                          copies tok0_in into it */
   uint32_t* status;    /* device uint32 [1]: QT_STATUS_* bits are OR-ed in; the caller clears it */
 } qt_frame_outputs;
 

@@ -21,6 +21,8 @@ QT_BF16, QT_F32, QT_I8, QT_I32 = 0, 1, 2, 3
 MODE_FULL, MODE_TALKER, MODE_PREDICTOR = 0, 1, 2
 MODES = {"full": MODE_FULL, "talker": MODE_TALKER, "predictor": MODE_PREDICTOR}
 STATUS_KV_OVERFLOW, STATUS_BAD_PAGE, STATUS_BAD_TOKEN, STATUS_NAN = 1, 2, 4, 8
+STATUS_BAD_SAMPLER = 16
+SAMPLER_MAX_TOP_K = 64
 
 EXPORTED = ["qt_last_error", "qt_abi_version", "qt_validate_cfg", "qt_packed_bytes",
             "qt_workspace_bytes", "qt_load_weights", "qt_quantize_int8", "qt_model_export_int8",
@@ -70,9 +72,20 @@ class KvCaches(C.Structure):
     _fields_ = [("k_pages", C.c_void_p), ("v_pages", C.c_void_p), ("num_pages", C.c_int32)]
 
 
+class SamplerParams(C.Structure):
+    _fields_ = [("temperature", C.c_float), ("top_p", C.c_float),
+                ("repetition_penalty", C.c_float), ("top_k", C.c_int32)]
+
+
+class Sampling(C.Structure):
+    _fields_ = [("params", C.c_void_p), ("seed", C.c_void_p), ("counter", C.c_void_p),
+                ("seen0", C.c_void_p)]
+
+
 class FrameInputs(C.Structure):
     _fields_ = [("mode", C.c_int32), ("talker_in", C.c_void_p), ("h_in", C.c_void_p),
-                ("tok0_in", C.c_void_p), ("forced", C.c_void_p)]
+                ("tok0_in", C.c_void_p), ("forced", C.c_void_p),
+                ("sampling", C.POINTER(Sampling))]
 
 
 class FrameOutputs(C.Structure):

@@ -372,6 +372,18 @@ qt_status check_frame_args(const qt_model* m, const qt_sessions* ss, const qt_kv
   }
   if (in->mode != QT_MODE_TALKER && !out->logits_pred)
     return fail(QT_E_INVALID_ARG, "outputs.logits_pred is NULL");
+  if (in->sampling) {
+    const qt_sampling& sp = *in->sampling;
+    if (!sp.params || !sp.seed || !sp.counter)
+      return fail(QT_E_INVALID_ARG, "sampling.params/seed/counter is NULL");
+    if (((uintptr_t)sp.params & 15) || ((uintptr_t)sp.seed & 7) || ((uintptr_t)sp.counter & 3) ||
+        ((uintptr_t)sp.seen0 & 3))
+      return fail(QT_E_INVALID_ARG, "sampling arrays are not aligned to their element size");
+    if (m->cfg.cb0_range > 4096 || m->cfg.code_vocab > 4096)
+      return fail(QT_E_UNSUPPORTED, "sampling draws over at most 4096 entries per row");
+    if (in->mode == QT_MODE_TALKER && !out->logits0)
+      return fail(QT_E_INVALID_ARG, "outputs.logits0 is NULL");
+  }
   if ((uintptr_t)ws & (kAlign - 1)) return fail(QT_E_INVALID_ARG, "workspace must be 256-byte aligned");
   const int mp = talker ? ss->max_pages : 1;
   const Ws w = make_ws(m->cfg, ss->batch, mp);
@@ -379,6 +391,16 @@ qt_status check_frame_args(const qt_model* m, const qt_sessions* ss, const qt_kv
     return fail(QT_E_CAPACITY, "workspace has %llu bytes, this call needs %llu",
                 (unsigned long long)ws_bytes, (unsigned long long)w.total);
   return ok();
+}
+
+SamplerArgs sampler_args(const qt_model_cfg& c, const qt_sampling& sp) {
+  SamplerArgs a{};
+  a.params = sp.params;
+  a.seed = sp.seed;
+  a.counter = sp.counter;
+  a.seen0 = sp.seen0;
+  a.seen_ld = (c.cb0_range + 31) / 32;
+  return a;
 }
 
 // Enqueue one frame.  Arguments are validated by the caller.
@@ -628,6 +650,14 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
       e.u_ld = ld_p;
       e.row_off = emb_row;
       e.status = out->status;
+      e.tokens = out->tokens;
+      if (in->sampling && !(k == 1 && mode == QT_MODE_PREDICTOR)) {
+        e.sample = 1;
+        e.smp = sampler_args(c, *in->sampling);
+        e.row = k == 1 ? SampleRow{out->logits0, c.talker_vocab, c.cb0_range, 0, 0}
+                       : SampleRow{out->logits_pred + (size_t)(k - 2) * c.code_vocab,
+                                   (long long)(ncb - 1) * c.code_vocab, c.code_vocab, 1, k - 1};
+      }
       cur_step = k;
       cur_layer = -1;
       QT_MARK(QT_KERNEL_EMBED, "k_embed", B, nullptr);
@@ -689,6 +719,15 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
   fe.n_cand = key_blocks(c.code_vocab);
   fe.tokens = out->tokens;
   fe.kv_len = ss->kv_len;
+  fe.status = out->status;
+  if (in->sampling) {
+    fe.sample = 1;
+    fe.smp = sampler_args(c, *in->sampling);
+    fe.row = mode == QT_MODE_TALKER
+                 ? SampleRow{out->logits0, c.talker_vocab, c.cb0_range, 0, 0}
+                 : SampleRow{out->logits_pred + (size_t)(ncb - 2) * c.code_vocab,
+                             (long long)(ncb - 1) * c.code_vocab, c.code_vocab, 1, ncb - 1};
+  }
   cur_step = 0;
   cur_layer = -1;
   QT_MARK(QT_KERNEL_FRAME_END, "k_frame_end", B, nullptr);

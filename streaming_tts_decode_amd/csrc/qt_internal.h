@@ -175,6 +175,24 @@ struct FrameBeginArgs {
   uint32_t* status;
 };
 
+// Drawing codec tokens instead of taking the argmax (qt_sampling in qt.h).
+struct SamplerArgs {
+  const qt_sampler_params* params;  // [B][2]; nullptr: greedy
+  const uint64_t* seed;             // [B]
+  const int32_t* counter;           // [B]
+  uint32_t* seen0;                  // [B][seen_ld] or nullptr
+  int seen_ld;
+};
+
+// The row a draw reads: session b's logits at logits + b * ld, entries [0, V).
+struct SampleRow {
+  const float* logits;
+  long long ld;
+  int V;
+  int group;     // 0: codebook 0 (params [b][0], penalty, seen update); 1: predictor
+  int codebook;  // Philox counter word 1 and the tokens column written
+};
+
 struct EmbedArgs {
   int B, H, vocab, ncb, step;   // step k >= 1 embeds the token of codebook k-1
   float eps;
@@ -190,6 +208,10 @@ struct EmbedArgs {
   int u_ld;
   int row_off;
   uint32_t* status;
+  int sample;                   // 1: draw codebook step-1 from `row` instead of the argmax keys
+  SamplerArgs smp;
+  SampleRow row;
+  int32_t* tokens;              // [B][ncb]: the drawn token is written to column step-1
 };
 
 struct FrameEndArgs {
@@ -198,6 +220,10 @@ struct FrameEndArgs {
   int cand_ld, n_cand0, n_cand;    // candidates of codebook 0 / of the others
   int32_t* tokens;  // [B][ncb]
   int32_t* kv_len;
+  int sample;       // 1: the frame draws tokens; this kernel draws `row` (the last draw)
+  SamplerArgs smp;
+  SampleRow row;
+  uint32_t* status;
 };
 
 // Scheduler helpers (qt_sched.cpp): per-group batch tables in, per-session results out.

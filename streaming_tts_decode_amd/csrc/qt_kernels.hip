@@ -474,13 +474,222 @@ __device__ __forceinline__ unsigned long long best_key_wave(const unsigned long 
   return wave_max_u64(best);
 }
 
+// ---------------------------------------------------------------------------
+// Token draws (qt_sampling).  Philox4x64-10 as defined by Salmon, Moraes, Dror and
+// Shaw (SC 2011): per round, words 0 and 2 are multiplied by two 64-bit constants
+// and the new words are (hi(M1 c2) ^ c1 ^ k0, lo(M1 c2), hi(M0 c0) ^ c3 ^ k1,
+// lo(M0 c0)); the key advances by the Weyl increments (golden ratio, sqrt 3 - 1).
+// Only the first output word of a block is used.
+__device__ __forceinline__ uint64_t philox4x64_word0(uint64_t c0, uint64_t c1, uint64_t k0) {
+  constexpr uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  constexpr uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+  uint64_t c2 = 0, c3 = 0, k1 = 0;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t hi0 = __umul64hi(M0, c0), lo0 = M0 * c0;
+    const uint64_t hi1 = __umul64hi(M1, c2), lo1 = M1 * c2;
+    c0 = hi1 ^ c1 ^ k0;
+    c1 = lo1;
+    c2 = hi0 ^ c3 ^ k1;
+    c3 = lo0;
+    k0 += W0;
+    k1 += W1;
+  }
+  return c0;
+}
+
+// Float -> unsigned key with the same order (larger float, larger key).
+__device__ __forceinline__ uint32_t order_key(float x) {
+  const uint32_t b = __float_as_uint(x);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+constexpr int kSampleSlots = 16;  // row entries per thread: rows up to 4096 entries
+
+struct SampleSmem {
+  uint32_t hist[256];
+  float cval[QT_SAMPLER_MAX_TOP_K];
+  int cidx[QT_SAMPLER_MAX_TOP_K];
+  int eq[kSampleSlots][4];
+  uint32_t digit;
+  int above;
+  int n_cand;
+  int token;
+};
+
+// One draw over row[0, V) by the 256 threads of a block (every thread returns the
+// token).  1. penalty and temperature; 2. the top_k-th largest score by a 4-pass
+// radix select over order keys (8 bits per pass), entries equal to it ranked by
+// index; 3. the candidates sorted by one wave (bitonic, (score desc, index asc));
+// 4. weights, running sums (wave scan), the top-p cut and the draw.
+__device__ int sample_row(const float* row, int V, float temperature, float top_p,
+                          float penalty, int top_k, const uint32_t* seen, float u,
+                          SampleSmem& sm) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ne = (V + 255) >> 8;
+  uint32_t key[kSampleSlots];
+#pragma unroll
+  for (int e = 0; e < kSampleSlots; ++e) {
+    const int i = tid + 256 * e;
+    key[e] = 0u;  // below every score: entries past V and NaN scores
+    if (e < ne && i < V) {
+      float x = row[i];
+      if (seen && ((seen[i >> 5] >> (i & 31)) & 1u)) x = x > 0.f ? x / penalty : x * penalty;
+      const float z = x / temperature;
+      if (z == z) key[e] = order_key(z);
+    }
+  }
+  const int k = top_k < V ? top_k : V;
+  uint32_t prefix = 0, pmask = 0;
+  int kr = k;
+  if (tid == 0) sm.n_cand = 0;
+#pragma unroll 1
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    sm.hist[tid] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < kSampleSlots; ++e)
+      if (e < ne && (key[e] & pmask) == prefix) atomicAdd(&sm.hist[(key[e] >> shift) & 255u], 1u);
+    __syncthreads();
+    if (wave == 0) {
+      // lane l owns bins 4l..4l+3; "above" counts the keys in higher bins
+      const uint32_t h0 = sm.hist[4 * lane], h1 = sm.hist[4 * lane + 1];
+      const uint32_t h2 = sm.hist[4 * lane + 2], h3 = sm.hist[4 * lane + 3];
+      const uint32_t own = h0 + h1 + h2 + h3;
+      uint32_t suf = own;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t t = __shfl_down(suf, off);
+        if (lane + off < 64) suf += t;
+      }
+      uint32_t above = suf - own;
+      const uint32_t hs[4] = {h3, h2, h1, h0};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (above < (uint32_t)kr && (uint32_t)kr <= above + hs[q]) {
+          sm.digit = 4 * lane + 3 - q;
+          sm.above = (int)above;
+        }
+        above += hs[q];
+      }
+    }
+    __syncthreads();
+    prefix |= sm.digit << shift;
+    pmask |= 255u << shift;
+    kr -= sm.above;
+  }
+  // candidates: every key above the threshold, and the kr lowest-index keys equal to it
+  int rank_base = 0;
+  {
+    uint64_t masks[kSampleSlots];
+#pragma unroll
+    for (int e = 0; e < kSampleSlots; ++e) {
+      masks[e] = __ballot(e < ne && key[e] == prefix);
+      if (lane == 0 && e < ne) sm.eq[e][wave] = __popcll(masks[e]);
+    }
+    __syncthreads();
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+    for (int e = 0; e < kSampleSlots; ++e) {
+      if (e < ne) {
+        const int i = tid + 256 * e;
+        bool take = key[e] > prefix;
+        if (key[e] == prefix) {
+          int rank = rank_base + __popcll(masks[e] & below);
+          for (int w = 0; w < wave; ++w) rank += sm.eq[e][w];
+          take = rank < kr;
+        }
+        if (take) {
+          const int slot = atomicAdd(&sm.n_cand, 1);
+          sm.cval[slot] = key[e] ? key_value(key[e]) : -INFINITY;
+          sm.cidx[slot] = i;
+        }
+        rank_base += sm.eq[e][0] + sm.eq[e][1] + sm.eq[e][2] + sm.eq[e][3];
+      }
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    float v = lane < k ? sm.cval[lane] : -INFINITY;
+    int idx = lane < k ? sm.cidx[lane] : 0x7fffffff;
+#pragma unroll
+    for (int size = 2; size <= 64; size <<= 1) {
+#pragma unroll
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        const float ov = __shfl_xor(v, stride);
+        const int oi = __shfl_xor(idx, stride);
+        const bool desc = (lane & size) == 0 || size == 64;
+        const bool lower = (lane & stride) == 0;
+        const bool greater = v > ov || (v == ov && idx < oi);
+        if (greater != (lower == desc)) {
+          v = ov;
+          idx = oi;
+        }
+      }
+    }
+    const float vmax = __shfl(v, 0);
+    float w = 0.f;
+    if (lane < k) w = vmax == -INFINITY ? (lane == 0 ? 1.f : 0.f) : expf(v - vmax);
+    float cum = w;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float t = __shfl_up(cum, off);
+      if (lane >= off) cum += t;
+    }
+    const float total = __shfl(cum, k - 1);
+    int m = __popcll(__ballot(lane < k && cum < top_p * total)) + 1;
+    m = m < k ? m : k;
+    const float r = u * __shfl(cum, m - 1);
+    const uint64_t hit = __ballot(lane < m && cum > r);
+    const int j = hit ? __ffsll((unsigned long long)hit) - 1 : m - 1;
+    const int tok = __shfl(idx, j);
+    if (lane == 0) sm.token = (tok >= 0 && tok < V) ? tok : 0;
+  }
+  __syncthreads();
+  return sm.token;
+}
+
+// Session b's draw of `row` with its parameters and random stream; thread 0 writes
+// the token to tokens[b][codebook] and, for codebook 0, adds it to the seen set.
+__device__ int sample_session(const SamplerArgs& s, const SampleRow& row, int b, int ncb,
+                              int32_t* tokens, uint32_t* status, SampleSmem& sm) {
+  const qt_sampler_params p = s.params[2 * b + row.group];
+  const uint64_t seed = s.seed[b];
+  const uint32_t ctr = (uint32_t)s.counter[b];
+  float T = p.temperature, tp = p.top_p, pen = p.repetition_penalty;
+  int tk = p.top_k;
+  const bool ok = T > 0.f && T < INFINITY && tp > 0.f && tp <= 1.f && pen >= 1.f &&
+                  pen < INFINITY && tk >= 1 && tk <= QT_SAMPLER_MAX_TOP_K;
+  if (!ok) {
+    if (threadIdx.x == 0) atomicOr(status, QT_STATUS_BAD_SAMPLER);
+    T = 1.f, tp = 1.f, pen = 1.f, tk = 1;
+  }
+  const uint64_t x = philox4x64_word0(ctr, (uint64_t)row.codebook, seed);
+  const float u = (float)(uint32_t)(x >> 40) * 0x1p-24f;
+  uint32_t* seen = (row.group == 0 && s.seen0) ? s.seen0 + (size_t)b * s.seen_ld : nullptr;
+  const int tok = sample_row(row.logits + (size_t)b * row.ld, row.V, T, tp, pen, tk, seen, u, sm);
+  if (threadIdx.x == 0) {
+    tokens[(size_t)b * ncb + row.codebook] = tok;
+    if (seen) seen[tok >> 5] |= 1u << (tok & 31);
+  }
+  return tok;
+}
+
 // Predictor step input: row E_step[token] (token = forced, or the previous step's
 // greedy token) to fp32, with its sum of squares and the first norm's half input.
 __global__ __launch_bounds__(256) void k_embed(EmbedArgs a) {
   __shared__ float part[4];
   __shared__ int s_tok;
+  __shared__ SampleSmem sm;
   const int b = blockIdx.x, tid = threadIdx.x;
-  if (a.forced) {
+  if (a.sample) {
+    const int drawn = sample_session(a.smp, a.row, b, a.ncb, a.tokens, a.status, sm);
+    if (tid == 0) s_tok = a.forced ? a.forced[(size_t)b * a.ncb + a.step - 1] : drawn;
+  } else if (a.forced) {
     if (tid == 0) s_tok = a.forced[(size_t)b * a.ncb + a.step - 1];
   } else if (tid < 64) {
     const unsigned long long k =
@@ -514,6 +723,22 @@ __global__ __launch_bounds__(256) void k_embed(EmbedArgs a) {
 // greedy token, and the session's cache length advanced.
 __global__ __launch_bounds__(256) void k_frame_end(FrameEndArgs a) {
   const int b = blockIdx.x, tid = threadIdx.x, wave = tid >> 6;
+  if (a.sample) {
+    // the predictor's draws were written by the embedding gathers; this block draws
+    // the last one (codebook 0 in Talker mode), then advances the cache length
+    __shared__ SampleSmem sm;
+    if (a.mode == QT_MODE_PREDICTOR && wave == 0) {
+      const unsigned long long best = best_key_wave(a.cand + (size_t)b * a.cand_ld, a.n_cand0);
+      if (tid == 0) a.tokens[(size_t)b * a.ncb] = key_index(best);
+    }
+    if (a.mode == QT_MODE_TALKER && tid >= 1 && tid < a.ncb) a.tokens[(size_t)b * a.ncb + tid] = -1;
+    sample_session(a.smp, a.row, b, a.ncb, a.tokens, a.status, sm);
+    if (tid == 0 && a.mode != QT_MODE_PREDICTOR) {
+      const int p = a.kv_len[b];
+      if (p >= 0 && p + 1 <= a.capacity) a.kv_len[b] = p + 1;
+    }
+    return;
+  }
   for (int k = wave; k < a.ncb; k += 4) {
     const unsigned long long best = best_key_wave(
         a.cand + ((size_t)k * a.B + b) * a.cand_ld, k == 0 ? a.n_cand0 : a.n_cand);

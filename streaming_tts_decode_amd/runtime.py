@@ -7,9 +7,12 @@ fills descriptors; all decoding happens inside libqt.so.
 """
 from __future__ import annotations
 
+import ctypes as C
+
 import numpy as np
 
-from . import (KERNEL_KINDS, FrameInputs, FrameOutputs, KvCaches, MODES, QT_BF16, Sessions,
+from . import (KERNEL_KINDS, FrameInputs, FrameOutputs, KvCaches, MODES, QT_BF16, Sampling,
+               Sessions,
                make_cfg, make_sched_cfg, qt_frame_decode, qt_frame_graph_create,
                qt_frame_graph_launch, qt_frame_launch_count, qt_frame_trace, qt_graph_destroy,
                qt_load_weights, qt_model_destroy, qt_packed_bytes, qt_sched_bytes, qt_sched_close,
@@ -131,6 +134,13 @@ class Decoder:
                                        device=self.dev)
         self.tokens = torch.zeros((batch, dims.n_codebooks), dtype=torch.int32, device=self.dev)
         self.status = torch.zeros(1, dtype=torch.int32, device=self.dev)
+        # sampling state: [b][0] codebook-0 and [b][1] predictor parameters (16 bytes
+        # each: temperature, top_p, repetition_penalty as f32, top_k as i32), seeds,
+        # and the seen sets of codebook-0 tokens; the draw counter is kv_len
+        self.sampler_params = torch.zeros((batch, 2, 4), dtype=torch.int32, device=self.dev)
+        self.seed = torch.zeros(batch, dtype=torch.int64, device=self.dev)
+        self.seen0 = torch.zeros((batch, (dims.cb0_range + 31) // 32), dtype=torch.int32,
+                                 device=self.dev)
         self.graphs = []
         self._trace = None
 
@@ -160,20 +170,42 @@ class Decoder:
         if forced is not None:
             self.forced.copy_(torch.as_tensor(np.asarray(forced, dtype=np.int32)))
 
+    def set_sampling(self, talker, predictor, seeds):
+        """talker / predictor: per-session (temperature, top_p, repetition_penalty,
+        top_k) tuples (or one tuple for all); seeds: per-session integers."""
+        def rows(p):
+            p = list(p) if isinstance(p[0], (tuple, list)) else [p] * self.B
+            return p
+        rec = np.zeros((self.B, 2), dtype=[("t", "<f4"), ("p", "<f4"), ("r", "<f4"), ("k", "<i4")])
+        for g, ps in enumerate((rows(talker), rows(predictor))):
+            for b, (t, p, r, k) in enumerate(ps):
+                rec[b, g] = (t, p, r, k)
+        self.sampler_params.copy_(self.torch.from_numpy(rec.view(np.int32).reshape(self.B, 2, 4)))
+        self.seed.copy_(self.torch.as_tensor(np.asarray(seeds, dtype=np.uint64).view(np.int64)))
+
     # ------------------------------------------------------------------ descriptors
-    def _descs(self, mode: str, forced: bool, batch: int | None = None):
+    def _descs(self, mode: str, forced: bool, batch: int | None = None, sampling: bool = False,
+               seen: bool = True):
         B = batch or self.B
         ss = Sessions(B, self.kv_len.data_ptr(), self.page_table.data_ptr(), self.max_pages)
         kv = KvCaches(self.k_pages.data_ptr(), self.v_pages.data_ptr(), self.num_pages)
         fi = FrameInputs(MODES[mode], self.talker_in.data_ptr(), self.h_in.data_ptr(),
                          self.tok0_in.data_ptr(), self.forced.data_ptr() if forced else None)
+        if sampling:
+            self._sampling = Sampling(self.sampler_params.data_ptr(), self.seed.data_ptr(),
+                                      self.kv_len.data_ptr(),
+                                      self.seen0.data_ptr() if seen else None)
+            fi.sampling = C.pointer(self._sampling)
         fo = FrameOutputs(self.logits0.data_ptr(), self.logits_pred.data_ptr(),
                           self.tokens.data_ptr(), self.status.data_ptr())
         return ss, kv, fi, fo
 
-    def decode(self, mode: str = "full", forced: bool = False, batch: int | None = None):
-        """Enqueue one frame on the current stream (no host synchronisation)."""
-        ss, kv, fi, fo = self._descs(mode, forced, batch)
+    def decode(self, mode: str = "full", forced: bool = False, batch: int | None = None,
+               sampling: bool = False, seen: bool = True):
+        """Enqueue one frame on the current stream (no host synchronisation).  With
+        sampling, tokens are drawn with the parameters of set_sampling and kv_len as
+        the draw counter."""
+        ss, kv, fi, fo = self._descs(mode, forced, batch, sampling, seen)
         qt_frame_decode(self.model, ss, kv, fi, fo, self.ws_ptr, self.ws_bytes,
                         self.torch.cuda.current_stream(self.dev).cuda_stream)
 
@@ -189,8 +221,8 @@ class Decoder:
         return [(li.name.decode(), KERNEL_KINDS[li.kind], li, ms)
                 for li, ms in qt_trace_read(self._trace, self._trace_n)]
 
-    def capture(self, mode: str = "full", forced: bool = False) -> int:
-        ss, kv, fi, fo = self._descs(mode, forced)
+    def capture(self, mode: str = "full", forced: bool = False, sampling: bool = False) -> int:
+        ss, kv, fi, fo = self._descs(mode, forced, sampling=sampling)
         g = qt_frame_graph_create(self.model, ss, kv, fi, fo, self.ws_ptr, self.ws_bytes)
         self.graphs.append(g)
         return g
