@@ -293,8 +293,29 @@ class OracleModel:
         return {"logits0": logits0, "logits_pred": logits_pred, "tokens": tokens,
                 "h": h_out}, L.value
 
+    def prefill(self, embeds_bits, capacity: int = 0):
+        """The Talker over a prompt: positions 0..T-1 of one session from an empty
+        cache ("Qwen3-TTS PR 5", What changed: prefill replays a graph over token
+        buckets; "Qwen3-TTS PR 5", Graph: the prefill feeds the decode loop's KV).
+        embeds_bits: bf16 bits [T, talker hidden], the Talker's inputs.  Returns
+        h [T, hidden] (final-normed outputs), logits0 [talker_vocab] of the codec
+        head at the last position, tok0 (its argmax over [0, cb0_range)) and the
+        cache kc, vc [layers, max(T, capacity), n_kv, hd] holding positions 0..T-1."""
+        x = bf16_to_f64(np.asarray(embeds_bits))
+        T = x.shape[0]
+        kc, vc = self.new_cache(max(T, capacity))
+        h = self.stack_forward("talker", x, 0, kc, vc)
+        W = self._keep[0]
+        if self.int8:
+            q, sc = self.quantized["talker.codec_head"]
+            logits0 = linear(W["talker.codec_head"], h[-1], q, sc)
+        else:
+            logits0 = linear(W["talker.codec_head"], h[-1])
+        return {"h": h, "logits0": logits0, "tok0": argmax(logits0[:self.dims.cb0_range]),
+                "kc": kc, "vc": vc}
+
     def run_session(self, mode: str, frames: int, talker_in=None, k_bits=None, v_bits=None,
-                    length: int = 0, h_in=None, tok0=None, forced=None):
+                    length: int = 0, h_in=None, tok0=None, forced=None, cache=None):
         """Run `frames` consecutive frames of one session (free-running unless
         `forced` [frames, n_codebooks] is given).  Inputs are bf16 bits:
         talker_in / h_in [frames, talker hidden]; k_bits / v_bits
@@ -303,6 +324,9 @@ class OracleModel:
         kc = vc = None
         if mode != "predictor":
             kc, vc = self.new_cache(length + frames, k_bits, v_bits)
+            if cache is not None:  # float64 contents of positions 0..length-1
+                kc[:, :length] = cache[0][:, :length]
+                vc[:, :length] = cache[1][:, :length]
         outs = {"logits0": [], "logits_pred": [], "tokens": [], "h": []}
         L = length
         for f in range(frames):

@@ -387,3 +387,34 @@ def test_capacity_overflow_is_an_error(tiny_model):
     kc, vc = m.new_cache(4)
     with pytest.raises(ValueError):
         m.stack_forward("talker", np.zeros((1, d.talker.hidden)), 4, kc, vc)
+
+
+# ---------------------------------------------------------------- prefill
+@pytest.mark.parametrize("T", [1, 5, 13])
+def test_prefill_matches_brute_force(tiny_model, T):
+    """The prompt prefill (all T positions through the stack at once, from an empty
+    cache) against the brute-force full-sequence forward with an explicit causal
+    mask, position by position; the codec head at the last position."""
+    d, W, m = tiny_model
+    X = synth.normal_bf16(f"pin.prefill.T{T}", (T, d.talker.hidden))
+    out = m.prefill(X)
+    h = bf.stack_forward(W, "talker", d.talker, bf.f64(X), np.arange(T))
+    np.testing.assert_allclose(out["h"], h, rtol=1e-9, atol=1e-12)
+    lg = bf.Lin(W, "talker.codec_head")(h[-1:])[0]
+    np.testing.assert_allclose(out["logits0"], lg, rtol=1e-9, atol=1e-12)
+    assert out["tok0"] == int(np.argmax(lg[: d.cb0_range]))
+
+
+def test_prefill_then_decode_equals_decoding_the_prompt(tiny_model):
+    """Decode frames after a prefill of T positions see the same cache as decode
+    frames after feeding the prompt one position at a time (brute force on the
+    whole sequence of prompt + frame inputs)."""
+    d, W, m = tiny_model
+    T, F = 7, 3
+    X = synth.normal_bf16("pin.prefill.cont", (T + F, d.talker.hidden))
+    pre = m.prefill(X[:T], capacity=T + F)
+    out = m.run_session("talker", F, talker_in=X[T:], length=T, cache=(pre["kc"], pre["vc"]))
+    for f in range(F):
+        h = bf.stack_forward(W, "talker", d.talker, bf.f64(X[:T + f + 1]), np.arange(T + f + 1))
+        lg = bf.Lin(W, "talker.codec_head")(h[-1:])[0]
+        np.testing.assert_allclose(out["logits0"][f], lg, rtol=1e-9, atol=1e-12)
