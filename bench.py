@@ -23,6 +23,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 / bf16 matrix peak, published
 
 # HBM bytes per launch of a kernel, from two rocprofv3 --pmc runs of this script
 # (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by 1 GiB / the same
@@ -173,6 +174,66 @@ def run_scheduler(pm, w, dec, lengths, steps, warmup, log):
                     "(the headline frame uses a shuffled pool)"}
     log(f"[bench] scheduler {w.name}: {res}")
     return res
+
+
+def prefill_flops(d, lengths) -> float:
+    """Multiply-adds x 2 of a prefill: every Talker projection for every row, causal
+    attention (q.k and p.v over positions 0..p for each row), the codec head at each
+    sequence's last row."""
+    t = d.talker
+    per_row = 2 * t.layers * ((t.q_dim + 2 * t.kv_dim) * t.hidden + t.hidden * t.q_dim
+                              + 2 * t.ffn * t.hidden + t.hidden * t.ffn)
+    flops = 0.0
+    for L in lengths:
+        flops += L * per_row + 2 * d.talker_vocab * t.hidden
+        flops += t.layers * 4.0 * t.head_dim * t.n_q * L * (L + 1) / 2
+    return flops
+
+
+def run_prefill(pm, d, log, rows=1024, packings=((1024,), (256, 256, 256, 256)), reps=10):
+    """Prompt prefill from a graph captured for `rows` rows, per packing of prompts:
+    milliseconds per call, prompt tokens per second and achieved TFLOP/s against the
+    dense fp16 MFMA peak (the projections run as fp16 x fp16 with f32 accumulation)."""
+    import numpy as np
+    import torch
+
+    import synth
+    from streaming_tts_decode_amd.runtime import Decoder
+    out = {}
+    for packing in packings:
+        S = len(packing)
+        max_pages = max(-(-L // 16) for L in packing)
+        dec = Decoder(pm, batch=S, max_pages=max_pages)
+        dec.prefill_setup(rows)
+        prompts = [synth.normal_bf16(f"bench.prefill.{S}.{i}", (L, d.talker.hidden))
+                   for i, L in enumerate(packing)]
+        dec.prefill_inputs(prompts)
+        g = dec.prefill_capture()
+        stream = torch.cuda.current_stream()
+        for _ in range(2):
+            dec.replay(g)
+        dec.status.zero_()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            dec.replay(g)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        if int(dec.status.item()):
+            raise RuntimeError(f"prefill: device status {int(dec.status.item()):#x}")
+        fl = prefill_flops(d, packing)
+        res = {"rows": rows, "sequences": list(packing), "ms": ms,
+               "tokens_per_s": sum(packing) / (ms / 1e3), "tflops": fl / (ms / 1e3) / 1e12,
+               "mfma_frac": fl / (ms / 1e3) / 1e12 / MFMA_F16_PEAK_TFLOPS}
+        log(f"[bench] prefill {res}")
+        out["x".join(str(L) for L in packing)] = res
+        dec.close()
+        del dec
+        torch.cuda.empty_cache()
+    return out
 
 
 def run_workload(pm, w, steps, warmup, log, n_trace=0, sched=False):
@@ -327,6 +388,8 @@ def main():
     ap.add_argument("--int8", action="store_true", help="INT8 weight-only decode")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip timing the prompt prefill (1024 rows)")
     ap.add_argument("--no-scheduler", action="store_true",
                     help="skip timing the headline workload through the lockstep scheduler")
     ap.add_argument("--trace-frames", type=int, default=5,
@@ -367,6 +430,7 @@ def main():
         r, _ = run_workload(pm, w, args.steps, args.warmup, log)
         extra[f"B{w.batch}"] = {k: r[k] for k in ("codec_frames_per_s", "ms_per_frame",
                                                   "hbm_gbs_algorithmic", "hbm_frac")}
+    prefill = None if args.no_prefill else run_prefill(pm, d, log)
     pm.close()
     calibration_copy(log)
     cpu = None if args.no_cpu_baseline else cpu_baseline(head, W, args.cpu_seconds, log)
@@ -394,6 +458,7 @@ def main():
         "other_batches": extra,
         "scheduler": main_res.get("scheduler"),
         "sampled": main_res.get("sampled"),
+        "prefill": prefill,
         "roofline": roofline(main_res, max(1, args.trace_frames)),
         "cpu_baseline": cpu,
     }

@@ -258,6 +258,57 @@ qt_status qt_frame_graph_launch(qt_graph* graph, void* stream);
 void qt_graph_destroy(qt_graph* graph);
 void qt_model_destroy(qt_model* model);
 
+/* ------------------------------------------------------------------ prefill
+ * The Talker over prompt positions, before the decode loop ("Qwen3-TTS PR 5", What
+ * changed: the Talker prefill replays a packed graph over token buckets 32..1024).
+ * Several sequences are packed into one call: sequence s holds rows
+ * [seq_start[s], seq_start[s+1]) of `embeds`, its positions 0, 1, ... from an
+ * empty cache, and every row runs the same decoder layers as a decode step
+ * (q/k-norm before RoPE, grouped-query attention causal within its sequence).
+ * The keys and values of every position go to the sequence's pages, so decode
+ * frames can follow with kv_len = the sequence length.  At each sequence's last
+ * row the codec head gives logits0 (and its greedy codebook-0 token), and the
+ * final-normed hidden state is what a PREDICTOR-mode frame takes as h_in.
+ * Rows past seq_start[max_seqs] are padding: they write no keys or values.  A
+ * graph captured for one `rows` (a bucket) serves every packing of at most that
+ * many rows, since the boundaries are read from device memory. */
+#define QT_PREFILL_MAX_SEQS 32
+#define QT_PREFILL_MAX_ROWS 4096
+
+typedef struct {
+  int32_t rows;              /* R: rows of the call, a multiple of 16; above 64, a multiple of 64;
+                                at most QT_PREFILL_MAX_ROWS */
+  int32_t max_seqs;          /* 1..QT_PREFILL_MAX_SEQS */
+  const int32_t* seq_start;  /* device int32 [max_seqs + 1], non-decreasing, seq_start[0] = 0,
+                                seq_start[max_seqs] <= rows */
+  const void* embeds;        /* device bf16 [rows][talker hidden]: the Talker input of each row */
+  const int32_t* page_table; /* device int32 [max_seqs][max_pages]: page of positions
+                                [i*page_size, (i+1)*page_size) of sequence s */
+  int32_t max_pages;
+  int32_t* kv_len;           /* device int32 [max_seqs]: set to each sequence's length */
+  float* logits0;            /* device f32 [max_seqs][talker_vocab]: codec head at the last row
+                                (all zero for an empty sequence) */
+  int32_t* tok0;             /* device int32 [max_seqs] or NULL: greedy codebook-0 token there */
+  void* h_last;              /* device bf16 [max_seqs][talker hidden] or NULL: final-normed hidden */
+  uint32_t* status;          /* device uint32 [1]: QT_STATUS_* bits are OR-ed in */
+} qt_prefill_args;
+
+/* Bytes of the prefill workspace for `rows` rows and max_seqs sequences. */
+qt_status qt_prefill_workspace_bytes(const qt_model_cfg* cfg, int32_t rows, int32_t max_seqs,
+                                     uint64_t* bytes);
+
+/* Enqueue a prefill on `stream` (no host synchronisation).  `workspace`: at least
+ * qt_prefill_workspace_bytes, 256-byte aligned, not shared with a call in flight.
+ * A sequence longer than max_pages * page_size sets QT_STATUS_KV_OVERFLOW and its
+ * positions past the capacity are not stored. */
+qt_status qt_prefill(qt_model* model, const qt_prefill_args* args, const qt_kv_caches* kv,
+                     void* workspace, uint64_t workspace_bytes, void* stream);
+
+/* Capture the same prefill into a graph (see qt_frame_graph_create for ownership). */
+qt_status qt_prefill_graph_create(qt_model* model, const qt_prefill_args* args,
+                                  const qt_kv_caches* kv, void* workspace,
+                                  uint64_t workspace_bytes, qt_graph** out_graph);
+
 /* ------------------------------------------------------------------ tracing
  * Per-kernel timing of one frame, for measuring each kernel against the memory
  * roofline.  A frame is launched as a sequence of kernels; qt_frame_trace enqueues

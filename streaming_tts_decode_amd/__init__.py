@@ -29,6 +29,7 @@ EXPORTED = ["qt_last_error", "qt_abi_version", "qt_validate_cfg", "qt_packed_byt
             "qt_frame_decode", "qt_frame_graph_create", "qt_frame_graph_launch",
             "qt_graph_destroy", "qt_model_destroy", "qt_trace_create", "qt_frame_launch_count",
             "qt_frame_trace", "qt_trace_read", "qt_trace_destroy",
+            "qt_prefill_workspace_bytes", "qt_prefill", "qt_prefill_graph_create",
             # qt_sched.h
             "qt_sched_bytes", "qt_sched_create", "qt_sched_open", "qt_sched_submit",
             "qt_sched_step", "qt_sched_outputs", "qt_sched_state", "qt_sched_length",
@@ -91,6 +92,16 @@ class FrameInputs(C.Structure):
 class FrameOutputs(C.Structure):
     _fields_ = [("logits0", C.c_void_p), ("logits_pred", C.c_void_p), ("tokens", C.c_void_p),
                 ("status", C.c_void_p)]
+
+
+class PrefillArgs(C.Structure):
+    _fields_ = [("rows", C.c_int32), ("max_seqs", C.c_int32), ("seq_start", C.c_void_p),
+                ("embeds", C.c_void_p), ("page_table", C.c_void_p), ("max_pages", C.c_int32),
+                ("kv_len", C.c_void_p), ("logits0", C.c_void_p), ("tok0", C.c_void_p),
+                ("h_last", C.c_void_p), ("status", C.c_void_p)]
+
+
+PREFILL_MAX_SEQS, PREFILL_MAX_ROWS = 32, 4096
 
 
 class LaunchInfo(C.Structure):
@@ -165,6 +176,14 @@ def lib():
                                     C.POINTER(C.c_int32)]
         L.qt_trace_destroy.restype = None
         L.qt_trace_destroy.argtypes = [_P]
+        L.qt_prefill_workspace_bytes.restype = st
+        L.qt_prefill_workspace_bytes.argtypes = [C.POINTER(ModelCfg), C.c_int32, C.c_int32,
+                                                 C.POINTER(C.c_uint64)]
+        L.qt_prefill.restype = st
+        L.qt_prefill.argtypes = [_P, C.POINTER(PrefillArgs), C.POINTER(KvCaches), _P, C.c_uint64, _P]
+        L.qt_prefill_graph_create.restype = st
+        L.qt_prefill_graph_create.argtypes = [_P, C.POINTER(PrefillArgs), C.POINTER(KvCaches), _P,
+                                              C.c_uint64, C.POINTER(_P)]
         i32p = C.POINTER(C.c_int32)
         L.qt_sched_bytes.restype = st
         L.qt_sched_bytes.argtypes = [C.POINTER(ModelCfg), C.POINTER(SchedCfg),
@@ -325,6 +344,27 @@ def qt_trace_read(trace: int, max_launches: int):
 
 def qt_trace_destroy(trace: int) -> None:
     lib().qt_trace_destroy(trace)
+
+
+def qt_prefill_workspace_bytes(cfg: ModelCfg, rows: int, max_seqs: int) -> int:
+    n = C.c_uint64()
+    _check(lib().qt_prefill_workspace_bytes(C.byref(cfg), rows, max_seqs, C.byref(n)),
+           "qt_prefill_workspace_bytes")
+    return n.value
+
+
+def qt_prefill(model: int, args: PrefillArgs, kv: KvCaches, workspace_ptr: int, workspace_bytes: int,
+               stream: int = 0) -> None:
+    _check(lib().qt_prefill(model, C.byref(args), C.byref(kv), workspace_ptr, workspace_bytes, stream),
+           "qt_prefill")
+
+
+def qt_prefill_graph_create(model: int, args: PrefillArgs, kv: KvCaches, workspace_ptr: int,
+                            workspace_bytes: int) -> int:
+    g = _P()
+    _check(lib().qt_prefill_graph_create(model, C.byref(args), C.byref(kv), workspace_ptr,
+                                         workspace_bytes, C.byref(g)), "qt_prefill_graph_create")
+    return g.value
 
 
 # --------------------------------------------------------------------------- scheduler (qt_sched.h)

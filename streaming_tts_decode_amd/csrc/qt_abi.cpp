@@ -736,6 +736,255 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
 #undef QT_MARK
 }
 
+// Capture what `enqueue` puts on a fresh stream into an instantiated graph.
+template <typename F>
+qt_status capture_graph(qt_graph** out_graph, F&& enqueue) {
+  hipStream_t cs;
+  QT_HIP(hipStreamCreateWithFlags(&cs, hipStreamNonBlocking));
+  hipError_t e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) {
+    (void)hipStreamDestroy(cs);
+    return fail(QT_E_HIP, "hipStreamBeginCapture failed: %s", hipGetErrorString(e));
+  }
+  qt_status st = enqueue(cs);
+  hipGraph_t g = nullptr;
+  e = hipStreamEndCapture(cs, &g);
+  (void)hipStreamDestroy(cs);
+  if (st) {
+    if (g) (void)hipGraphDestroy(g);
+    return st;
+  }
+  if (e != hipSuccess) return fail(QT_E_HIP, "hipStreamEndCapture failed: %s", hipGetErrorString(e));
+  hipGraphExec_t ex;
+  e = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0);
+  if (e != hipSuccess) {
+    (void)hipGraphDestroy(g);
+    return fail(QT_E_HIP, "hipGraphInstantiate failed: %s", hipGetErrorString(e));
+  }
+  qt_graph* gr = new qt_graph();
+  gr->graph = g;
+  gr->exec = ex;
+  *out_graph = gr;
+  return ok();
+}
+
+// ------------------------------------------------------------------ prompt prefill
+struct PrefillWs {
+  size_t x, ss, u, qkv, o, ffn, rowinfo, ul, ssl, cand, total;
+  int qkv_ld, cand_ld;
+};
+
+PrefillWs make_prefill_ws(const qt_model_cfg& c, int R, int S) {
+  const qt_decoder_cfg& t = c.talker;
+  PrefillWs w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  w.qkv_ld = (t.n_q_heads + 2 * t.n_kv_heads) * t.head_dim;
+  w.cand_ld = key_blocks(c.cb0_range);
+  w.x = take((size_t)R * t.hidden * 4);
+  w.ss = take((size_t)(t.hidden / kGemmRows) * R * 4);
+  w.u = take((size_t)R * t.hidden * 2);
+  w.qkv = take((size_t)R * w.qkv_ld * 4);
+  w.o = take((size_t)R * t.n_q_heads * t.head_dim * 2);
+  w.ffn = take((size_t)R * t.ffn * 2);
+  w.rowinfo = take((size_t)R * 2 * 4);
+  w.ul = take((size_t)S * t.hidden * 2);
+  w.ssl = take((size_t)S * 4);
+  w.cand = take((size_t)S * w.cand_ld * 8);
+  w.total = off;
+  return w;
+}
+
+qt_status check_prefill_rows(int R, int S) {
+  if (R < 16 || R > QT_PREFILL_MAX_ROWS || (R % 16) || (R > 64 && (R % 64)))
+    return fail(QT_E_SHAPE, "rows = %d: expected a multiple of 16 (of 64 above 64), at most %d", R,
+                QT_PREFILL_MAX_ROWS);
+  if (S < 1 || S > QT_PREFILL_MAX_SEQS)
+    return fail(QT_E_INVALID_ARG, "max_seqs = %d: expected 1..%d", S, QT_PREFILL_MAX_SEQS);
+  return ok();
+}
+
+qt_status check_prefill_args(const qt_model* m, const qt_prefill_args* a, const qt_kv_caches* kv,
+                             void* ws, uint64_t ws_bytes) {
+  if (!m || !a || !kv) return fail(QT_E_INVALID_ARG, "model, args or kv is NULL");
+  qt_status st = check_prefill_rows(a->rows, a->max_seqs);
+  if (st) return st;
+  if (!a->seq_start || !a->embeds || !a->page_table || !a->kv_len || !a->logits0 || !a->status)
+    return fail(QT_E_INVALID_ARG, "a prefill array is NULL");
+  if (a->max_pages < 1) return fail(QT_E_INVALID_ARG, "max_pages = %d", a->max_pages);
+  if (!kv->k_pages || !kv->v_pages || kv->num_pages < 1)
+    return fail(QT_E_INVALID_ARG, "kv pages are NULL or empty");
+  if (((uintptr_t)kv->k_pages | (uintptr_t)kv->v_pages) & 15)
+    return fail(QT_E_INVALID_ARG, "kv pages must be 16-byte aligned");
+  if (!ws) return fail(QT_E_INVALID_ARG, "workspace is NULL");
+  if ((uintptr_t)ws & (kAlign - 1)) return fail(QT_E_INVALID_ARG, "workspace must be 256-byte aligned");
+  const PrefillWs w = make_prefill_ws(m->cfg, a->rows, a->max_seqs);
+  if (ws_bytes < w.total)
+    return fail(QT_E_CAPACITY, "workspace has %llu bytes, this prefill needs %llu",
+                (unsigned long long)ws_bytes, (unsigned long long)w.total);
+  return ok();
+}
+
+// Enqueue a prefill.  Per Talker layer: the four projections as GEMMs over slices
+// of at most 64 rows (the decode GEMM, its weights kept in the caches across the
+// slices), [q/k-norm, RoPE, K/V to pages] and [causal attention] over all rows.
+// Then the last row of each sequence: final norm, codec head, greedy token.
+qt_status enqueue_prefill(const qt_model* m, const qt_prefill_args* a, const qt_kv_caches* kv,
+                          void* wsp, hipStream_t st) {
+  const qt_model_cfg& c = m->cfg;
+  const qt_decoder_cfg& T = c.talker;
+  const int R = a->rows, S = a->max_seqs;
+  const int chunk = R < 64 ? R : 64;
+  const PrefillWs w = make_prefill_ws(c, R, S);
+  char* ws = (char*)wsp;
+  float* x = (float*)(ws + w.x);
+  float* ss = (float*)(ws + w.ss);
+  uint16_t* u = (uint16_t*)(ws + w.u);
+  float* qkv = (float*)(ws + w.qkv);
+  uint16_t* o = (uint16_t*)(ws + w.o);
+  uint16_t* ffn = (uint16_t*)(ws + w.ffn);
+  int32_t* rowinfo = (int32_t*)(ws + w.rowinfo);
+
+  PrefillBeginArgs b{};
+  b.R = R;
+  b.H = T.hidden;
+  b.max_seqs = S;
+  b.seq_start = a->seq_start;
+  b.embeds = (const uint16_t*)a->embeds;
+  b.gain = vp(m, m->plan.tl[0].in_norm);
+  b.x = x;
+  b.u = u;
+  b.ss = ss;
+  b.rowinfo = rowinfo;
+  QT_LAUNCH(launch_prefill_begin(b, st));
+
+  auto run = [&](GemmArgs& g) -> qt_status {
+    g.keep_w = 1;  // every slice reads the same matrix again
+    QT_LAUNCH(launch_gemm(g, st));
+    return ok();
+  };
+  const size_t layer_elems = (size_t)kv->num_pages * T.n_kv_heads * kPage * kHeadDim;
+  int slots = 1;
+  for (int l = 0; l < T.layers; ++l) {
+    const LayerSlots& L = m->plan.tl[l];
+    const uint16_t* next_gain =
+        vp(m, l + 1 < T.layers ? m->plan.tl[l + 1].in_norm : m->plan.t_final);
+    qt_status r;
+    for (int r0 = 0; r0 < R; r0 += chunk) {
+      GemmArgs g = gemm_norm(m, L.qkv, u + (size_t)r0 * 8, R, ss + r0, R, slots, T.rms_eps, chunk,
+                             a->status);
+      g.epi = EPI_STORE;
+      g.out_f32 = qkv + (size_t)r0 * w.qkv_ld;
+      g.out_ld = w.qkv_ld;
+      if ((r = run(g))) return r;
+    }
+    PrefillQkArgs q{};
+    q.qkv = qkv;
+    q.qkv_ld = w.qkv_ld;
+    q.n_q = T.n_q_heads;
+    q.n_kv = T.n_kv_heads;
+    q.q_norm = vp(m, L.q_norm);
+    q.k_norm = vp(m, L.k_norm);
+    q.eps = T.rms_eps;
+    q.k_pool = (uint16_t*)kv->k_pages + (size_t)l * layer_elems;
+    q.v_pool = (uint16_t*)kv->v_pages + (size_t)l * layer_elems;
+    q.num_pages = kv->num_pages;
+    q.page_table = a->page_table;
+    q.max_pages = a->max_pages;
+    q.rowinfo = rowinfo;
+    q.status = a->status;
+    QT_LAUNCH(launch_prefill_qk(q, R, T.rope_theta, st));
+    PrefillAttnArgs at{};
+    at.qkv = qkv;
+    at.qkv_ld = w.qkv_ld;
+    at.n_q = T.n_q_heads;
+    at.n_kv = T.n_kv_heads;
+    at.R = R;
+    at.k_pool = q.k_pool;
+    at.v_pool = q.v_pool;
+    at.num_pages = kv->num_pages;
+    at.page_table = a->page_table;
+    at.max_pages = a->max_pages;
+    at.rowinfo = rowinfo;
+    at.o = o;
+    QT_LAUNCH(launch_prefill_attn(at, st));
+    int o_slots = 1;
+    for (int r0 = 0; r0 < R; r0 += chunk) {
+      GemmArgs g = gemm_act(m, L.o, o + (size_t)r0 * 8, R, chunk, a->status);
+      g.epi = EPI_RESID;
+      g.out_f32 = x + (size_t)r0 * T.hidden;
+      g.out_ld = T.hidden;
+      g.u_gain = vp(m, L.post_norm);
+      g.u = u + (size_t)r0 * 8;
+      g.u_ld = R;
+      g.ss_out = ss + r0;
+      g.ss_out_ld = R;
+      o_slots = T.hidden / plan_gemm(g.nrows, g.K, g.M, g.scale != nullptr, true).rows_per_block;
+      if ((r = run(g))) return r;
+    }
+    for (int r0 = 0; r0 < R; r0 += chunk) {
+      GemmArgs g = gemm_norm(m, L.gu, u + (size_t)r0 * 8, R, ss + r0, R, o_slots, T.rms_eps, chunk,
+                             a->status);
+      g.epi = EPI_SWIGLU;
+      g.u = ffn + (size_t)r0 * 8;
+      g.u_ld = R;
+      if ((r = run(g))) return r;
+    }
+    for (int r0 = 0; r0 < R; r0 += chunk) {
+      GemmArgs g = gemm_act(m, L.down, ffn + (size_t)r0 * 8, R, chunk, a->status);
+      g.epi = EPI_RESID;
+      g.out_f32 = x + (size_t)r0 * T.hidden;
+      g.out_ld = T.hidden;
+      g.u_gain = next_gain;
+      g.u = u + (size_t)r0 * 8;
+      g.u_ld = R;
+      g.ss_out = ss + r0;
+      g.ss_out_ld = R;
+      slots = T.hidden / plan_gemm(g.nrows, g.K, g.M, g.scale != nullptr, true).rows_per_block;
+      if ((r = run(g))) return r;
+    }
+  }
+
+  PrefillLastArgs pl{};
+  pl.max_seqs = S;
+  pl.H = T.hidden;
+  pl.R = R;
+  pl.seq_start = a->seq_start;
+  pl.x = x;
+  pl.gain = vp(m, m->plan.t_final);
+  pl.eps = T.rms_eps;
+  pl.u = (uint16_t*)(ws + w.ul);
+  pl.ss = (float*)(ws + w.ssl);
+  pl.h_last = (uint16_t*)a->h_last;
+  pl.kv_len = a->kv_len;
+  QT_LAUNCH(launch_prefill_last(pl, st));
+  GemmArgs head = gemm_norm(m, m->plan.t_head, pl.u, S, pl.ss, S, 1, T.rms_eps, S, a->status);
+  head.nrows = c.talker_vocab;
+  head.epi = EPI_HEAD;
+  head.logits = a->logits0;
+  head.logits_ld = c.talker_vocab;
+  head.n_logits = c.talker_vocab;
+  head.argmax_range = c.cb0_range;
+  head.cand = (unsigned long long*)(ws + w.cand);
+  head.cand_ld = w.cand_ld;
+  head.keep_w = 0;
+  QT_LAUNCH(launch_gemm(head, st));
+  if (a->tok0) {
+    PrefillEndArgs pe{};
+    pe.max_seqs = S;
+    pe.cand_ld = w.cand_ld;
+    pe.n_cand = key_blocks(c.cb0_range);
+    pe.cand = head.cand;
+    pe.tok0 = a->tok0;
+    QT_LAUNCH(launch_prefill_end(pe, st));
+  }
+  return ok();
+}
+
 }  // namespace
 
 namespace qt {
@@ -915,33 +1164,39 @@ qt_status qt_frame_graph_create(qt_model* model, const qt_sessions* sessions, co
   *out_graph = nullptr;
   qt_status st = check_frame_args(model, sessions, kv, in, out, workspace, workspace_bytes);
   if (st) return st;
-  hipStream_t cs;
-  QT_HIP(hipStreamCreateWithFlags(&cs, hipStreamNonBlocking));
-  hipError_t e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
-  if (e != hipSuccess) {
-    (void)hipStreamDestroy(cs);
-    return fail(QT_E_HIP, "hipStreamBeginCapture failed: %s", hipGetErrorString(e));
-  }
-  st = enqueue_frame(model, sessions, kv, in, out, workspace, cs);
-  hipGraph_t g = nullptr;
-  e = hipStreamEndCapture(cs, &g);
-  (void)hipStreamDestroy(cs);
-  if (st) {
-    if (g) (void)hipGraphDestroy(g);
-    return st;
-  }
-  if (e != hipSuccess) return fail(QT_E_HIP, "hipStreamEndCapture failed: %s", hipGetErrorString(e));
-  hipGraphExec_t ex;
-  e = hipGraphInstantiate(&ex, g, nullptr, nullptr, 0);
-  if (e != hipSuccess) {
-    (void)hipGraphDestroy(g);
-    return fail(QT_E_HIP, "hipGraphInstantiate failed: %s", hipGetErrorString(e));
-  }
-  qt_graph* gr = new qt_graph();
-  gr->graph = g;
-  gr->exec = ex;
-  *out_graph = gr;
+  return capture_graph(out_graph, [&](hipStream_t cs) {
+    return enqueue_frame(model, sessions, kv, in, out, workspace, cs);
+  });
+}
+
+
+qt_status qt_prefill_workspace_bytes(const qt_model_cfg* cfg, int32_t rows, int32_t max_seqs,
+                                     uint64_t* bytes) {
+  qt_status st = check_cfg(cfg);
+  if (st) return st;
+  if (!bytes) return fail(QT_E_INVALID_ARG, "bytes is NULL");
+  if ((st = check_prefill_rows(rows, max_seqs))) return st;
+  *bytes = make_prefill_ws(*cfg, rows, max_seqs).total;
   return ok();
+}
+
+qt_status qt_prefill(qt_model* model, const qt_prefill_args* args, const qt_kv_caches* kv,
+                     void* workspace, uint64_t workspace_bytes, void* stream) {
+  qt_status st = check_prefill_args(model, args, kv, workspace, workspace_bytes);
+  if (st) return st;
+  return enqueue_prefill(model, args, kv, workspace, (hipStream_t)stream);
+}
+
+qt_status qt_prefill_graph_create(qt_model* model, const qt_prefill_args* args,
+                                  const qt_kv_caches* kv, void* workspace,
+                                  uint64_t workspace_bytes, qt_graph** out_graph) {
+  if (!out_graph) return fail(QT_E_INVALID_ARG, "out_graph is NULL");
+  *out_graph = nullptr;
+  qt_status st = check_prefill_args(model, args, kv, workspace, workspace_bytes);
+  if (st) return st;
+  return capture_graph(out_graph, [&](hipStream_t cs) {
+    return enqueue_prefill(model, args, kv, workspace, cs);
+  });
 }
 
 qt_status qt_frame_graph_launch(qt_graph* graph, void* stream) {

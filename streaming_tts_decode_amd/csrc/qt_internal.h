@@ -226,6 +226,70 @@ struct FrameEndArgs {
   uint32_t* status;
 };
 
+// Prompt prefill (qt_prefill): rows of packed sequences; rowinfo[2r] = sequence
+// of row r (-1: padding), rowinfo[2r+1] = its position.
+struct PrefillBeginArgs {
+  int R, H, max_seqs;
+  const int32_t* seq_start;
+  const uint16_t* embeds;   // [R][H] bf16
+  const uint16_t* gain;     // first input norm
+  float* x;                 // [R][H]
+  uint16_t* u;              // chunked half [H/8][R][8]
+  float* ss;                // slot 0: [R]
+  int32_t* rowinfo;         // [R][2]
+};
+
+struct PrefillQkArgs {
+  float* qkv;               // [R][qkv_ld]: q is replaced by its normalised, rotated, scaled form
+  int qkv_ld, n_q, n_kv;
+  const uint16_t* q_norm;
+  const uint16_t* k_norm;
+  float eps;
+  uint16_t* k_pool;         // this layer's pages
+  uint16_t* v_pool;
+  int num_pages;
+  const int32_t* page_table;
+  int max_pages;
+  const int32_t* rowinfo;
+  uint32_t* status;
+};
+
+struct PrefillAttnArgs {
+  const float* qkv;
+  int qkv_ld, n_q, n_kv, R;
+  const uint16_t* k_pool;
+  const uint16_t* v_pool;
+  int num_pages;
+  const int32_t* page_table;
+  int max_pages;
+  const int32_t* rowinfo;
+  uint16_t* o;              // chunked half [q_dim/8][R][8]
+};
+
+struct PrefillLastArgs {
+  int max_seqs, H, R;
+  const int32_t* seq_start;
+  const float* x;
+  const uint16_t* gain;     // final norm
+  float eps;
+  uint16_t* u;              // chunked half [H/8][max_seqs][8]
+  float* ss;                // [max_seqs]
+  uint16_t* h_last;         // [max_seqs][H] bf16 or nullptr
+  int32_t* kv_len;
+};
+
+struct PrefillEndArgs {
+  int max_seqs, cand_ld, n_cand;
+  const unsigned long long* cand;
+  int32_t* tok0;
+};
+
+hipError_t launch_prefill_begin(const PrefillBeginArgs& a, hipStream_t s);
+hipError_t launch_prefill_qk(const PrefillQkArgs& a, int R, float theta, hipStream_t s);
+hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t s);
+hipError_t launch_prefill_last(const PrefillLastArgs& a, hipStream_t s);
+hipError_t launch_prefill_end(const PrefillEndArgs& a, hipStream_t s);
+
 // Scheduler helpers (qt_sched.cpp): per-group batch tables in, per-session results out.
 constexpr int kSchedMaxBatch = 32;
 

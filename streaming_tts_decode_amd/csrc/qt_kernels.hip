@@ -861,6 +861,217 @@ __global__ __launch_bounds__(256) void k_sched_collect(SchedCollectArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Prompt prefill.  Entry, one block per row: the row's sequence and position
+// (sequences are packed in order; rows past the last one are padding, set to
+// zero), the residual x, the first norm's half input and its sum of squares.
+__global__ __launch_bounds__(256) void k_prefill_begin(PrefillBeginArgs a) {
+  __shared__ float part[4];
+  __shared__ int s_seq;
+  const int r = blockIdx.x, tid = threadIdx.x;
+  if (tid == 0) {
+    int seq = -1, pos = 0;
+    for (int q = 0; q < a.max_seqs; ++q) {
+      const int lo = a.seq_start[q], hi = a.seq_start[q + 1];
+      if (lo <= r && r < hi) {
+        seq = q;
+        pos = r - lo;
+        break;
+      }
+    }
+    s_seq = seq;
+    a.rowinfo[2 * r] = seq;
+    a.rowinfo[2 * r + 1] = pos;
+  }
+  __syncthreads();
+  const bool live = s_seq >= 0;
+  float ss = 0.f;
+  for (int i = tid; i < a.H; i += 256) {
+    const float v = live ? bf2f(a.embeds[(size_t)r * a.H + i]) : 0.f;
+    a.x[(size_t)r * a.H + i] = v;
+    a.u[chunked(r, i, a.R)] = f2h(v * bf2f(a.gain[i]));
+    ss = fmaf(v, v, ss);
+  }
+  ss = wave_sum(ss);
+  if ((tid & 63) == 0) part[tid >> 6] = ss;
+  __syncthreads();
+  if (tid == 0) a.ss[r] = part[0] + part[1] + part[2] + part[3];
+}
+
+// Per (row, KV head h): query heads 2h, 2h+1 and key head h normalised and rotated at
+// the row's position (the same arithmetic as a decode step); q is stored back
+// scaled by 1/sqrt(128), the key (bf16) and the raw value go to the page slot.
+__global__ __launch_bounds__(256) void k_prefill_qk(PrefillQkArgs a, float theta_log2) {
+  __shared__ float rb[2][128];
+  __shared__ float ssq[2][2];
+  const int r = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int jj = tid >> 7, d = tid & 127;
+  const int seq = a.rowinfo[2 * r], p = seq >= 0 ? a.rowinfo[2 * r + 1] : 0;
+  float* row = a.qkv + (size_t)r * a.qkv_ld;
+  const int q_dim = a.n_q * 128, kv_dim = a.n_kv * 128;
+  const float qraw = row[(2 * h + jj) * 128 + d];
+  const float kvraw = row[q_dim + (jj ? kv_dim : 0) + h * 128 + d];
+  const float gq = bf2f(a.q_norm[d]), gk = bf2f(a.k_norm[d]);
+  const float qr = norm_rope_128(qraw, d, gq, a.eps, p, theta_log2, rb[jj], ssq[jj]);
+  const float kr = norm_rope_128(kvraw, d, gk, a.eps, p, theta_log2, rb[jj], ssq[jj]);
+  row[(2 * h + jj) * 128 + d] = qr * kInvSqrtHd;
+  if (seq < 0) return;
+  if (p >= a.max_pages * kPage) {
+    if (tid == 0) atomicOr(a.status, QT_STATUS_KV_OVERFLOW);
+    return;
+  }
+  const int pg = a.page_table[(size_t)seq * a.max_pages + p / kPage];
+  if (pg < 0 || pg >= a.num_pages) {
+    if (tid == 0) atomicOr(a.status, QT_STATUS_BAD_PAGE);
+    return;
+  }
+  const size_t off = ((size_t)pg * a.n_kv + h) * (kPage * 128) + (size_t)(p % kPage) * 128 + d;
+  (jj == 0 ? a.k_pool : a.v_pool)[off] = f2bf(jj ? kvraw : kr);
+}
+
+// Causal attention over packed sequences.  Block (16-row tile, KV head h): thread
+// t serves (row t/16, query head 2h + (t/8)%2) and dims 16*(t%8) .. +15.  For each
+// sequence present in the tile, its pages (one 4 KB piece per page for head h, K
+// and V) are staged through LDS in position order; each page updates a running
+// max, sum and output (online softmax), keys after the row's position masked.
+__global__ __launch_bounds__(256) void k_prefill_attn(PrefillAttnArgs a) {
+  __shared__ __align__(16) uint16_t Ks[kPage * 128];
+  __shared__ __align__(16) uint16_t Vs[kPage * 128];
+  __shared__ int t_seq[16], t_pos[16];
+  const int tid = threadIdx.x, h = blockIdx.y;
+  const int r0 = 16 * blockIdx.x;
+  const int pair = tid >> 3, sub = tid & 7, rl = pair >> 1, qh = 2 * h + (pair & 1);
+  const int row = r0 + rl;
+  if (tid < 16) {
+    t_seq[tid] = a.rowinfo[2 * (r0 + tid)];
+    t_pos[tid] = a.rowinfo[2 * (r0 + tid) + 1];
+  }
+  __syncthreads();
+  const int my_seq = t_seq[rl], my_pos = t_pos[rl];
+  float q[16], acc[16];
+  const float* qp = a.qkv + (size_t)row * a.qkv_ld + qh * 128 + 16 * sub;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    q[e] = qp[e];
+    acc[e] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+  int seq_lo = 0x7fffffff, seq_hi = -1;
+  for (int i = 0; i < 16; ++i)
+    if (t_seq[i] >= 0) {
+      seq_lo = t_seq[i] < seq_lo ? t_seq[i] : seq_lo;
+      seq_hi = t_seq[i] > seq_hi ? t_seq[i] : seq_hi;
+    }
+  const size_t head_off = (size_t)h * (kPage * 128);
+  for (int seq = seq_lo; seq <= seq_hi; ++seq) {
+    int pmax = -1;
+    for (int i = 0; i < 16; ++i)
+      if (t_seq[i] == seq && t_pos[i] > pmax) pmax = t_pos[i];
+    if (pmax < 0) continue;
+    int npg = pmax / kPage + 1;
+    npg = npg < a.max_pages ? npg : a.max_pages;
+    for (int pi = 0; pi < npg; ++pi) {
+      const int pg = a.page_table[(size_t)seq * a.max_pages + pi];
+      const bool ok = pg >= 0 && pg < a.num_pages;
+      const size_t base = (size_t)(ok ? pg : 0) * a.n_kv * (kPage * 128) + head_off;
+      uint4 kq = *reinterpret_cast<const uint4*>(a.k_pool + base + 8 * tid);
+      uint4 vq = *reinterpret_cast<const uint4*>(a.v_pool + base + 8 * tid);
+      if (!ok) kq = vq = make_uint4(0, 0, 0, 0);
+      __syncthreads();  // the previous page is consumed
+      reinterpret_cast<uint4*>(Ks)[tid] = kq;
+      reinterpret_cast<uint4*>(Vs)[tid] = vq;
+      __syncthreads();
+      if (my_seq == seq) {
+        float sc[kPage];
+#pragma unroll
+        for (int j = 0; j < kPage; ++j) {
+          const uint4 k0 = reinterpret_cast<const uint4*>(Ks + j * 128 + 16 * sub)[0];
+          const uint4 k1 = reinterpret_cast<const uint4*>(Ks + j * 128 + 16 * sub)[1];
+          const uint32_t kw[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+          float dot = 0.f;
+#pragma unroll
+          for (int w = 0; w < 8; ++w) {
+            dot = fmaf(q[2 * w], bf_lo(kw[w]), dot);
+            dot = fmaf(q[2 * w + 1], bf_hi(kw[w]), dot);
+          }
+          dot += __shfl_xor(dot, 1);
+          dot += __shfl_xor(dot, 2);
+          dot += __shfl_xor(dot, 4);
+          sc[j] = (pi * kPage + j <= my_pos) ? dot : -INFINITY;
+        }
+        float mt = sc[0];
+#pragma unroll
+        for (int j = 1; j < kPage; ++j) mt = fmaxf(mt, sc[j]);
+        const float mn = fmaxf(m, mt);
+        const float scale = expf(m - mn);
+        l *= scale;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[e] *= scale;
+#pragma unroll
+        for (int j = 0; j < kPage; ++j) {
+          const float pj = expf(sc[j] - mn);
+          l += pj;
+          const uint4 v0 = reinterpret_cast<const uint4*>(Vs + j * 128 + 16 * sub)[0];
+          const uint4 v1 = reinterpret_cast<const uint4*>(Vs + j * 128 + 16 * sub)[1];
+          const uint32_t vw[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+          for (int w = 0; w < 8; ++w) {
+            acc[2 * w] = fmaf(pj, bf_lo(vw[w]), acc[2 * w]);
+            acc[2 * w + 1] = fmaf(pj, bf_hi(vw[w]), acc[2 * w + 1]);
+          }
+        }
+        m = mn;
+      }
+    }
+  }
+  const float inv = (my_seq >= 0 && l > 0.f) ? 1.f / l : 0.f;
+  uint32_t packed[8];
+#pragma unroll
+  for (int w = 0; w < 8; ++w)
+    packed[w] = (uint32_t)f2h(acc[2 * w] * inv) | ((uint32_t)f2h(acc[2 * w + 1] * inv) << 16);
+  const int col = qh * 128 + 16 * sub;
+  *reinterpret_cast<uint4*>(a.o + chunked(row, col, a.R)) =
+      make_uint4(packed[0], packed[1], packed[2], packed[3]);
+  *reinterpret_cast<uint4*>(a.o + chunked(row, col + 8, a.R)) =
+      make_uint4(packed[4], packed[5], packed[6], packed[7]);
+}
+
+// One block per sequence: its length into kv_len, and from its last row the head's
+// input (half x * final gain, sum of squares) and the final-normed hidden state.
+__global__ __launch_bounds__(256) void k_prefill_last(PrefillLastArgs a) {
+  __shared__ float part[4];
+  const int q = blockIdx.x, tid = threadIdx.x;
+  const int lo = a.seq_start[q], hi = a.seq_start[q + 1];
+  const int len = (hi > lo && hi <= a.R) ? hi - lo : 0;
+  const float* x = a.x + (size_t)(len ? hi - 1 : 0) * a.H;
+  float ss = 0.f;
+  for (int i = tid; i < a.H; i += 256) {
+    const float v = len ? x[i] : 0.f;
+    a.u[chunked(q, i, a.max_seqs)] = f2h(v * bf2f(a.gain[i]));
+    ss = fmaf(v, v, ss);
+  }
+  ss = wave_sum(ss);
+  if ((tid & 63) == 0) part[tid >> 6] = ss;
+  __syncthreads();
+  const float tot = part[0] + part[1] + part[2] + part[3];
+  if (tid == 0) {
+    a.ss[q] = tot;
+    a.kv_len[q] = len;
+  }
+  if (a.h_last) {
+    const float inv = 1.0f / sqrtf(tot / (float)a.H + a.eps);
+    for (int i = tid; i < a.H; i += 256)
+      a.h_last[(size_t)q * a.H + i] = f2bf(len ? x[i] * inv * bf2f(a.gain[i]) : 0.f);
+  }
+}
+
+// Greedy codebook-0 token of each sequence's last row from the head's keys.
+__global__ __launch_bounds__(64) void k_prefill_end(PrefillEndArgs a) {
+  const int q = blockIdx.x;
+  const unsigned long long best = best_key_wave(a.cand + (size_t)q * a.cand_ld, a.n_cand);
+  if (threadIdx.x == 0) a.tok0[q] = key_index(best);
+}
+
 }  // namespace
 
 // --------------------------------------------------------------------------- launchers
@@ -928,6 +1139,32 @@ hipError_t launch_sched_collect(const SchedCollectArgs& a, hipStream_t s) {
       a.eos_index < -1 || a.eos_index >= a.talker_vocab)
     return hipErrorInvalidValue;
   launch_kernel(k_sched_collect, dim3(a.B), dim3(256), s, a);
+  return hipGetLastError();
+}
+}  // namespace qt
+
+namespace qt {
+hipError_t launch_prefill_begin(const PrefillBeginArgs& a, hipStream_t s) {
+  if (a.R < 1 || a.max_seqs < 1) return hipErrorInvalidValue;
+  launch_kernel(k_prefill_begin, dim3(a.R), dim3(256), s, a);
+  return hipGetLastError();
+}
+hipError_t launch_prefill_qk(const PrefillQkArgs& a, int R, float theta, hipStream_t s) {
+  if (R < 1 || a.n_q != 2 * a.n_kv) return hipErrorInvalidValue;
+  launch_kernel(k_prefill_qk, dim3(R, a.n_kv), dim3(256), s, a, (float)log2((double)theta));
+  return hipGetLastError();
+}
+hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t s) {
+  if (a.R < 16 || (a.R % 16) || a.n_q != 2 * a.n_kv) return hipErrorInvalidValue;
+  launch_kernel(k_prefill_attn, dim3(a.R / 16, a.n_kv), dim3(256), s, a);
+  return hipGetLastError();
+}
+hipError_t launch_prefill_last(const PrefillLastArgs& a, hipStream_t s) {
+  launch_kernel(k_prefill_last, dim3(a.max_seqs), dim3(256), s, a);
+  return hipGetLastError();
+}
+hipError_t launch_prefill_end(const PrefillEndArgs& a, hipStream_t s) {
+  launch_kernel(k_prefill_end, dim3(a.max_seqs), dim3(64), s, a);
   return hipGetLastError();
 }
 }  // namespace qt

@@ -11,8 +11,8 @@ import ctypes as C
 
 import numpy as np
 
-from . import (KERNEL_KINDS, FrameInputs, FrameOutputs, KvCaches, MODES, QT_BF16, Sampling,
-               Sessions,
+from . import (KERNEL_KINDS, FrameInputs, FrameOutputs, KvCaches, MODES, QT_BF16, PrefillArgs,
+               Sampling, Sessions, qt_prefill, qt_prefill_graph_create, qt_prefill_workspace_bytes,
                make_cfg, make_sched_cfg, qt_frame_decode, qt_frame_graph_create,
                qt_frame_graph_launch, qt_frame_launch_count, qt_frame_trace, qt_graph_destroy,
                qt_load_weights, qt_model_destroy, qt_packed_bytes, qt_sched_bytes, qt_sched_close,
@@ -209,13 +209,63 @@ class Decoder:
         qt_frame_decode(self.model, ss, kv, fi, fo, self.ws_ptr, self.ws_bytes,
                         self.torch.cuda.current_stream(self.dev).cuda_stream)
 
-    def trace(self, mode: str = "full", forced: bool = False):
+    # ------------------------------------------------------------------ prompt prefill
+    def prefill_setup(self, rows: int):
+        """Buffers for prefills of up to `rows` packed rows into this decoder's
+        sessions (sequence s = session s, its pages from the page table)."""
+        torch, d = self.torch, self.dims
+        self.pf_rows = rows
+        self.pf_ws_bytes = qt_prefill_workspace_bytes(self.cfg, rows, self.B)
+        self._pf_ws_buf, self.pf_ws_ptr = _aligned(torch, self.pf_ws_bytes, self.dev)
+        self.pf_seq_start = torch.zeros(self.B + 1, dtype=torch.int32, device=self.dev)
+        self.pf_embeds = torch.zeros((rows, d.talker.hidden), dtype=torch.int16, device=self.dev)
+        self.pf_logits0 = torch.zeros((self.B, d.talker_vocab), dtype=torch.float32, device=self.dev)
+        self.pf_tok0 = torch.zeros(self.B, dtype=torch.int32, device=self.dev)
+        self.pf_h = torch.zeros((self.B, d.talker.hidden), dtype=torch.int16, device=self.dev)
+
+    def _pf_args(self):
+        return PrefillArgs(self.pf_rows, self.B, self.pf_seq_start.data_ptr(),
+                           self.pf_embeds.data_ptr(), self.page_table.data_ptr(), self.max_pages,
+                           self.kv_len.data_ptr(), self.pf_logits0.data_ptr(),
+                           self.pf_tok0.data_ptr(), self.pf_h.data_ptr(), self.status.data_ptr())
+
+    def prefill_inputs(self, prompts):
+        """Pack prompts (per session: bf16 bits [T_s, hidden], or None) into the rows."""
+        torch = self.torch
+        starts = [0]
+        rows = np.zeros((self.pf_rows, self.dims.talker.hidden), dtype=np.uint16)
+        for b in range(self.B):
+            p = prompts[b] if b < len(prompts) and prompts[b] is not None else None
+            n = 0 if p is None else p.shape[0]
+            if starts[-1] + n > self.pf_rows:
+                raise ValueError("prompts exceed the prefill rows")
+            if n:
+                rows[starts[-1]:starts[-1] + n] = p
+            starts.append(starts[-1] + n)
+        self.pf_seq_start.copy_(torch.as_tensor(np.asarray(starts, dtype=np.int32)))
+        self.pf_embeds.copy_(_bits(torch, rows, self.dev))
+
+    def prefill(self):
+        """Enqueue a prefill of the packed prompts on the current stream."""
+        qt_prefill(self.model, self._pf_args(), self._kv(), self.pf_ws_ptr, self.pf_ws_bytes,
+                   self.torch.cuda.current_stream(self.dev).cuda_stream)
+
+    def prefill_capture(self) -> int:
+        g = qt_prefill_graph_create(self.model, self._pf_args(), self._kv(), self.pf_ws_ptr,
+                                    self.pf_ws_bytes)
+        self.graphs.append(g)
+        return g
+
+    def _kv(self):
+        return KvCaches(self.k_pages.data_ptr(), self.v_pages.data_ptr(), self.num_pages)
+
+    def trace(self, mode: str = "full", forced: bool = False, sampling: bool = False):
         """Run one frame as decode() does with an event around every launch; waits for
         it and returns [(kernel name, kind, info, ms)] in launch order."""
         if self._trace is None:
             self._trace_n = qt_frame_launch_count(self.cfg, MODES["full"])
             self._trace = qt_trace_create(self._trace_n)
-        ss, kv, fi, fo = self._descs(mode, forced)
+        ss, kv, fi, fo = self._descs(mode, forced, sampling=sampling)
         qt_frame_trace(self.model, ss, kv, fi, fo, self.ws_ptr, self.ws_bytes,
                        self.torch.cuda.current_stream(self.dev).cuda_stream, self._trace)
         return [(li.name.decode(), KERNEL_KINDS[li.kind], li, ms)

@@ -1,0 +1,150 @@
+"""GPU checks of the prompt prefill (qt_prefill in include/qt.h) against the oracle's
+prefill (oracle/__init__.py: the Talker over positions 0..T-1 from an empty
+cache), through the C ABI.
+
+For every sequence of a packed call: the codec-head logits at its last row
+(parity bound: 1e-2 of the largest |logit|), the greedy codebook-0 token where the
+oracle's top-2 margin is wide, the final-normed hidden state, every key and value
+it stored in its pages, and decode frames that continue from the prefilled cache
+(against the oracle continuing from its own prefilled cache).
+"""
+import numpy as np
+import pytest
+
+import synth
+from tests.gpu_cases import log
+from tests.parity import compare
+
+pytestmark = pytest.mark.gpu
+
+
+def _bf16(bits):
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def _check_cache(dec, b, L, pre, label, dims):
+    """Keys and values of session b's first L positions against the oracle's cache
+    (bf16 storage: a few bf16 ulps of the per-head scale)."""
+    t = dims.talker
+    pages = dec.page_table_np[b, :-(-L // 16)]
+    k = dec.k_pages[:, pages].cpu().numpy()  # [layers, npg, n_kv, 16, hd]
+    v = dec.v_pages[:, pages].cpu().numpy()
+    for name, pool, ref in (("K", k, pre["kc"]), ("V", v, pre["vc"])):
+        got = _bf16(pool.view(np.uint16)).transpose(0, 1, 3, 2, 4).reshape(t.layers, -1, t.n_kv, t.head_dim)[:, :L]
+        want = ref[:, :L]
+        scale = np.abs(want).max(axis=(1, 3), keepdims=True)
+        err = np.abs(got - want) / scale
+        assert err.max() <= 2e-2, f"{label} {name}: max error {err.max():.3g} of the head scale"
+
+
+def _run(pm, orc, dims, lengths, rows, max_pages, tag, frames_after=0):
+    from streaming_tts_decode_amd.runtime import Decoder
+    torch = pm.torch
+    B = len(lengths)
+    t = dims.talker
+    prompts = [synth.normal_bf16(f"{tag}.prompt.s{b}", (L, t.hidden)) if L else None
+               for b, L in enumerate(lengths)]
+    log(f"[prefill] {tag}: lengths={lengths} rows={rows} max_pages={max_pages}")
+    dec = Decoder(pm, batch=B, max_pages=max_pages)
+    dec.prefill_setup(rows)
+    dec.prefill_inputs(prompts)
+    dec.status.zero_()
+    dec.prefill()
+    torch.cuda.synchronize()
+    assert int(dec.status.item()) == 0
+    np.testing.assert_array_equal(dec.kv_len.cpu().numpy(), lengths)
+    logits = dec.pf_logits0.cpu().numpy()
+    tok0 = dec.pf_tok0.cpu().numpy()
+    h = _bf16(dec.pf_h.cpu().numpy().view(np.uint16))
+    pres = {}
+    for b, L in enumerate(lengths):
+        if not L:
+            assert np.all(logits[b] == 0) and np.all(h[b] == 0)
+            continue
+        pre = orc.prefill(prompts[b], capacity=L + frames_after)
+        pres[b] = pre
+        compare(logits[b][None], pre["logits0"][None], dims.cb0_range, gpu_tokens=tok0[b:b + 1],
+                label=f"{tag} s{b} logits0")
+        herr = np.abs(h[b] - pre["h"][-1]).max() / np.abs(pre["h"][-1]).max()
+        assert herr <= 2e-2, f"{tag} s{b}: h_last error {herr:.3g}"
+        _check_cache(dec, b, L, pre, f"{tag} s{b}", dims)
+    if frames_after:
+        x = synth.normal_bf16(f"{tag}.after", (frames_after, B, t.hidden))
+        got = []
+        for f in range(frames_after):
+            dec.set_inputs(talker_in=x[f])
+            dec.decode("talker")
+            torch.cuda.synchronize()
+            got.append(dec.logits0.cpu().numpy().copy())
+        assert int(dec.status.item()) == 0
+        for b, pre in pres.items():
+            L = lengths[b]
+            ref = orc.run_session("talker", frames_after, talker_in=x[:, b], length=L,
+                                  cache=(pre["kc"], pre["vc"]))
+            compare(np.stack([g[b] for g in got]), ref["logits0"], dims.cb0_range,
+                    label=f"{tag} s{b} decode after prefill")
+    return dec, prompts, logits
+
+
+def test_prefill_single_sequence_and_decode_after(small_pm, orc_small):
+    dec, _, _ = _run(small_pm, orc_small, synth.SMALL, [37], rows=48, max_pages=4, tag="pf1",
+                     frames_after=3)
+    dec.close()
+
+
+def test_prefill_packed_ragged_sequences(small_pm, orc_small):
+    # rows of one 16-row tile belong to two sequences (50 is not a multiple of 16),
+    # an empty sequence, a sequence filling several pages, and padding rows
+    dec, _, _ = _run(small_pm, orc_small, synth.SMALL, [50, 0, 77, 3], rows=192, max_pages=6,
+                     tag="pf2", frames_after=2)
+    dec.close()
+
+
+def test_prefill_graph_replays_other_packings(small_pm):
+    torch = small_pm.torch
+    from streaming_tts_decode_amd.runtime import Decoder
+    t = synth.SMALL.talker
+    dec = Decoder(small_pm, batch=3, max_pages=8)  # 128 positions per session
+    dec.prefill_setup(128)
+    g = dec.prefill_capture()
+    for packing in ([40, 70, 1], [0, 128, 0], [16, 16, 16]):
+        prompts = [synth.normal_bf16(f"pfg.{i}.{L}", (L, t.hidden)) if L else None
+                   for i, L in enumerate(packing)]
+        outs = []
+        for use_graph in (False, True):
+            dec.prefill_inputs(prompts)
+            dec.status.zero_()
+            if use_graph:
+                dec.replay(g)
+            else:
+                dec.prefill()
+            torch.cuda.synchronize()  # host work between the replays
+            assert int(dec.status.item()) == 0
+            outs.append((dec.pf_logits0.cpu().numpy().copy(), dec.kv_len.cpu().numpy().copy(),
+                         dec.k_pages.cpu().numpy().copy()))
+        for a, b in zip(*outs):
+            np.testing.assert_array_equal(a, b)
+        np.testing.assert_array_equal(outs[0][1], packing)
+    dec.close()
+
+
+def test_prefill_overflow_sets_status(small_pm):
+    torch = small_pm.torch
+    from streaming_tts_decode_amd import STATUS_KV_OVERFLOW
+    from streaming_tts_decode_amd.runtime import Decoder
+    t = synth.SMALL.talker
+    dec = Decoder(small_pm, batch=1, max_pages=2)  # 32 positions
+    dec.prefill_setup(48)
+    dec.prefill_inputs([synth.normal_bf16("pfo", (40, t.hidden))])
+    dec.status.zero_()
+    dec.prefill()
+    torch.cuda.synchronize()
+    assert int(dec.status.item()) & STATUS_KV_OVERFLOW
+    assert np.all(np.isfinite(dec.pf_logits0.cpu().numpy()))
+    dec.close()
+
+
+def test_prefill_full_model(full_pm, orc_full):
+    dec, _, _ = _run(full_pm, orc_full, synth.FULL, [45, 19], rows=64, max_pages=8, tag="pffull",
+                     frames_after=1)
+    dec.close()
