@@ -929,111 +929,165 @@ __global__ __launch_bounds__(256) void k_prefill_qk(PrefillQkArgs a, float theta
   (jj == 0 ? a.k_pool : a.v_pool)[off] = f2bf(jj ? kvraw : kr);
 }
 
-// Causal attention over packed sequences.  Block (16-row tile, KV head h): thread
-// t serves (row t/16, query head 2h + (t/8)%2) and dims 16*(t%8) .. +15.  For each
-// sequence present in the tile, its pages (one 4 KB piece per page for head h, K
-// and V) are staged through LDS in position order; each page updates a running
-// max, sum and output (online softmax), keys after the row's position masked.
-__global__ __launch_bounds__(256) void k_prefill_attn(PrefillAttnArgs a) {
-  __shared__ __align__(16) uint16_t Ks[kPage * 128];
-  __shared__ __align__(16) uint16_t Vs[kPage * 128];
+// Causal attention over packed sequences on the matrix cores.  Block (16-row
+// tile, KV head h), two waves: wave w serves query head 2h + w for the tile's 16
+// rows.  For each sequence present in the tile, keys come in blocks of 32 (two
+// pages): K staged through LDS as half [key][dim], V as half [dim][key]; the next
+// block's loads are in flight while the current one is used.  Per block of keys:
+//   S = Q K^T   (v_mfma_f32_16x16x32_f16: 2 key tiles x 4 dim steps), masked to
+//               keys at or before the row's position;
+//   online softmax in the accumulator layout (lane l, element e: row 4(l>>4)+e,
+//               key l&15), row max and sum over 16 lanes;
+//   P -> per-wave LDS tile -> A operand; O += P V (8 dim tiles, one 32-key step).
+// Key slots past the sequence's last row are staged as zeros.
+constexpr int kKsLd = 136;  // half elements per staged key row (bank spread)
+constexpr int kVtLd = 40;   // half elements per staged dim row of V^T / per P row
+
+__global__ __launch_bounds__(128) void k_prefill_attn(PrefillAttnArgs a) {
+  __shared__ __align__(16) _Float16 Ks[32 * kKsLd];
+  __shared__ __align__(16) _Float16 Vt[128 * kVtLd];
+  __shared__ __align__(16) _Float16 Ps[2][16 * kVtLd];
   __shared__ int t_seq[16], t_pos[16];
-  const int tid = threadIdx.x, h = blockIdx.y;
-  const int r0 = 16 * blockIdx.x;
-  const int pair = tid >> 3, sub = tid & 7, rl = pair >> 1, qh = 2 * h + (pair & 1);
-  const int row = r0 + rl;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int i = lane & 15, qg = lane >> 4;
+  const int h = blockIdx.y, r0 = 16 * blockIdx.x, qh = 2 * h + wave;
   if (tid < 16) {
     t_seq[tid] = a.rowinfo[2 * (r0 + tid)];
     t_pos[tid] = a.rowinfo[2 * (r0 + tid) + 1];
   }
-  __syncthreads();
-  const int my_seq = t_seq[rl], my_pos = t_pos[rl];
-  float q[16], acc[16];
-  const float* qp = a.qkv + (size_t)row * a.qkv_ld + qh * 128 + 16 * sub;
+  // Q operand: row i of the tile, dims [32 ks + 8 qg, +8), already scaled
+  f16x8 qf[4];
+  {
+    const float* qp = a.qkv + (size_t)(r0 + i) * a.qkv_ld + qh * 128 + 8 * qg;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    q[e] = qp[e];
-    acc[e] = 0.f;
+    for (int ks = 0; ks < 4; ++ks) {
+      const float4 x0 = *reinterpret_cast<const float4*>(qp + 32 * ks);
+      const float4 x1 = *reinterpret_cast<const float4*>(qp + 32 * ks + 4);
+      qf[ks] = f16x8{(_Float16)x0.x, (_Float16)x0.y, (_Float16)x0.z, (_Float16)x0.w,
+                     (_Float16)x1.x, (_Float16)x1.y, (_Float16)x1.z, (_Float16)x1.w};
+    }
   }
-  float m = -INFINITY, l = 0.f;
+  __syncthreads();
+  int row_seq[4], row_pos[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    row_seq[e] = t_seq[4 * qg + e];
+    row_pos[e] = t_pos[4 * qg + e];
+  }
+  f32x4 O[8];
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) O[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m[4], l[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    m[e] = -INFINITY;
+    l[e] = 0.f;
+  }
   int seq_lo = 0x7fffffff, seq_hi = -1;
-  for (int i = 0; i < 16; ++i)
-    if (t_seq[i] >= 0) {
-      seq_lo = t_seq[i] < seq_lo ? t_seq[i] : seq_lo;
-      seq_hi = t_seq[i] > seq_hi ? t_seq[i] : seq_hi;
+  for (int r = 0; r < 16; ++r)
+    if (t_seq[r] >= 0) {
+      seq_lo = t_seq[r] < seq_lo ? t_seq[r] : seq_lo;
+      seq_hi = t_seq[r] > seq_hi ? t_seq[r] : seq_hi;
     }
   const size_t head_off = (size_t)h * (kPage * 128);
-  for (int seq = seq_lo; seq <= seq_hi; ++seq) {
-    int pmax = -1;
-    for (int i = 0; i < 16; ++i)
-      if (t_seq[i] == seq && t_pos[i] > pmax) pmax = t_pos[i];
-    if (pmax < 0) continue;
-    int npg = pmax / kPage + 1;
-    npg = npg < a.max_pages ? npg : a.max_pages;
-    for (int pi = 0; pi < npg; ++pi) {
-      const int pg = a.page_table[(size_t)seq * a.max_pages + pi];
-      const bool ok = pg >= 0 && pg < a.num_pages;
-      const size_t base = (size_t)(ok ? pg : 0) * a.n_kv * (kPage * 128) + head_off;
-      uint4 kq = *reinterpret_cast<const uint4*>(a.k_pool + base + 8 * tid);
-      uint4 vq = *reinterpret_cast<const uint4*>(a.v_pool + base + 8 * tid);
-      if (!ok) kq = vq = make_uint4(0, 0, 0, 0);
-      __syncthreads();  // the previous page is consumed
-      reinterpret_cast<uint4*>(Ks)[tid] = kq;
-      reinterpret_cast<uint4*>(Vs)[tid] = vq;
-      __syncthreads();
-      if (my_seq == seq) {
-        float sc[kPage];
+  const size_t page_elems = (size_t)a.n_kv * (kPage * 128);
+  // thread t stages 16-byte pieces u = t + 128 j: key u >> 4 (0..31), dims 8 (u & 15)
+  auto fetch = [&](int seq, int kb, int pmax, uint4* kr, uint4* vr) {
 #pragma unroll
-        for (int j = 0; j < kPage; ++j) {
-          const uint4 k0 = reinterpret_cast<const uint4*>(Ks + j * 128 + 16 * sub)[0];
-          const uint4 k1 = reinterpret_cast<const uint4*>(Ks + j * 128 + 16 * sub)[1];
-          const uint32_t kw[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
-          float dot = 0.f;
-#pragma unroll
-          for (int w = 0; w < 8; ++w) {
-            dot = fmaf(q[2 * w], bf_lo(kw[w]), dot);
-            dot = fmaf(q[2 * w + 1], bf_hi(kw[w]), dot);
-          }
-          dot += __shfl_xor(dot, 1);
-          dot += __shfl_xor(dot, 2);
-          dot += __shfl_xor(dot, 4);
-          sc[j] = (pi * kPage + j <= my_pos) ? dot : -INFINITY;
+    for (int j = 0; j < 4; ++j) {
+      const int u = tid + 128 * j, key = u >> 4, d8 = u & 15;
+      const int kpos = 32 * kb + key, pi = kpos >> 4;
+      kr[j] = vr[j] = make_uint4(0, 0, 0, 0);
+      if (kpos <= pmax && pi < a.max_pages) {
+        const int pg = a.page_table[(size_t)seq * a.max_pages + pi];
+        if (pg >= 0 && pg < a.num_pages) {
+          const size_t off = (size_t)pg * page_elems + head_off + (size_t)(kpos & 15) * 128 + 8 * d8;
+          kr[j] = *reinterpret_cast<const uint4*>(a.k_pool + off);
+          vr[j] = *reinterpret_cast<const uint4*>(a.v_pool + off);
         }
-        float mt = sc[0];
-#pragma unroll
-        for (int j = 1; j < kPage; ++j) mt = fmaxf(mt, sc[j]);
-        const float mn = fmaxf(m, mt);
-        const float scale = expf(m - mn);
-        l *= scale;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[e] *= scale;
-#pragma unroll
-        for (int j = 0; j < kPage; ++j) {
-          const float pj = expf(sc[j] - mn);
-          l += pj;
-          const uint4 v0 = reinterpret_cast<const uint4*>(Vs + j * 128 + 16 * sub)[0];
-          const uint4 v1 = reinterpret_cast<const uint4*>(Vs + j * 128 + 16 * sub)[1];
-          const uint32_t vw[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-#pragma unroll
-          for (int w = 0; w < 8; ++w) {
-            acc[2 * w] = fmaf(pj, bf_lo(vw[w]), acc[2 * w]);
-            acc[2 * w + 1] = fmaf(pj, bf_hi(vw[w]), acc[2 * w + 1]);
-          }
-        }
-        m = mn;
       }
     }
-  }
-  const float inv = (my_seq >= 0 && l > 0.f) ? 1.f / l : 0.f;
-  uint32_t packed[8];
+  };
+  for (int seq = seq_lo; seq <= seq_hi; ++seq) {
+    int pmax = -1;
+    for (int r = 0; r < 16; ++r)
+      if (t_seq[r] == seq && t_pos[r] > pmax) pmax = t_pos[r];
+    if (pmax < 0) continue;
+    const int nblk = pmax / 32 + 1;
+    uint4 kr[4], vr[4];
+    fetch(seq, 0, pmax, kr, vr);
+    for (int kb = 0; kb < nblk; ++kb) {
+      __syncthreads();  // the previous block of keys is consumed
 #pragma unroll
-  for (int w = 0; w < 8; ++w)
-    packed[w] = (uint32_t)f2h(acc[2 * w] * inv) | ((uint32_t)f2h(acc[2 * w + 1] * inv) << 16);
-  const int col = qh * 128 + 16 * sub;
-  *reinterpret_cast<uint4*>(a.o + chunked(row, col, a.R)) =
-      make_uint4(packed[0], packed[1], packed[2], packed[3]);
-  *reinterpret_cast<uint4*>(a.o + chunked(row, col + 8, a.R)) =
-      make_uint4(packed[4], packed[5], packed[6], packed[7]);
+      for (int j = 0; j < 4; ++j) {
+        const int u = tid + 128 * j, key = u >> 4, d8 = u & 15;
+        const uint32_t kw[4] = {kr[j].x, kr[j].y, kr[j].z, kr[j].w};
+        const uint32_t vw[4] = {vr[j].x, vr[j].y, vr[j].z, vr[j].w};
+        f16x8 kh;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          kh[2 * w] = (_Float16)bf_lo(kw[w]);
+          kh[2 * w + 1] = (_Float16)bf_hi(kw[w]);
+          Vt[(8 * d8 + 2 * w) * kVtLd + key] = (_Float16)bf_lo(vw[w]);
+          Vt[(8 * d8 + 2 * w + 1) * kVtLd + key] = (_Float16)bf_hi(vw[w]);
+        }
+        *reinterpret_cast<f16x8*>(Ks + key * kKsLd + 8 * d8) = kh;
+      }
+      __syncthreads();
+      if (kb + 1 < nblk) fetch(seq, kb + 1, pmax, kr, vr);
+      f32x4 S0 = f32x4{0.f, 0.f, 0.f, 0.f}, S1 = S0;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const f16x8 b0 = *reinterpret_cast<const f16x8*>(Ks + i * kKsLd + 32 * ks + 8 * qg);
+        const f16x8 b1 = *reinterpret_cast<const f16x8*>(Ks + (16 + i) * kKsLd + 32 * ks + 8 * qg);
+        S0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qf[ks], b0, S0, 0, 0, 0);
+        S1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qf[ks], b1, S1, 0, 0, 0);
+      }
+      const int k0 = 32 * kb + i, k1 = k0 + 16;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool live = row_seq[e] == seq;
+        const float s0 = (live && k0 <= row_pos[e]) ? S0[e] : -INFINITY;
+        const float s1 = (live && k1 <= row_pos[e]) ? S1[e] : -INFINITY;
+        float mx = fmaxf(s0, s1);
+        mx = fmaxf(mx, __shfl_xor(mx, 1));
+        mx = fmaxf(mx, __shfl_xor(mx, 2));
+        mx = fmaxf(mx, __shfl_xor(mx, 4));
+        mx = fmaxf(mx, __shfl_xor(mx, 8));
+        const float mn = fmaxf(m[e], mx);
+        const float scale = mn == -INFINITY ? 1.f : expf(m[e] - mn);
+        const float p0 = s0 == -INFINITY ? 0.f : expf(s0 - mn);
+        const float p1 = s1 == -INFINITY ? 0.f : expf(s1 - mn);
+        float rs = p0 + p1;
+        rs += __shfl_xor(rs, 1);
+        rs += __shfl_xor(rs, 2);
+        rs += __shfl_xor(rs, 4);
+        rs += __shfl_xor(rs, 8);
+        l[e] = l[e] * scale + rs;
+        m[e] = mn;
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) O[nb][e] *= scale;
+        Ps[wave][(4 * qg + e) * kVtLd + i] = (_Float16)p0;
+        Ps[wave][(4 * qg + e) * kVtLd + 16 + i] = (_Float16)p1;
+      }
+      __builtin_amdgcn_wave_barrier();
+      const f16x8 pa = *reinterpret_cast<const f16x8*>(&Ps[wave][i * kVtLd + 8 * qg]);
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        const f16x8 vb = *reinterpret_cast<const f16x8*>(Vt + (16 * nb + i) * kVtLd + 8 * qg);
+        O[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vb, O[nb], 0, 0, 0);
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int row = r0 + 4 * qg + e;
+    const float inv = (row_seq[e] >= 0 && l[e] > 0.f) ? 1.f / l[e] : 0.f;
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb)
+      a.o[chunked(row, qh * 128 + 16 * nb + i, a.R)] = f2h(O[nb][e] * inv);
+  }
 }
 
 // One block per sequence: its length into kv_len, and from its last row the head's
@@ -1156,7 +1210,7 @@ hipError_t launch_prefill_qk(const PrefillQkArgs& a, int R, float theta, hipStre
 }
 hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t s) {
   if (a.R < 16 || (a.R % 16) || a.n_q != 2 * a.n_kv) return hipErrorInvalidValue;
-  launch_kernel(k_prefill_attn, dim3(a.R / 16, a.n_kv), dim3(256), s, a);
+  launch_kernel(k_prefill_attn, dim3(a.R / 16, a.n_kv), dim3(128), s, a);
   return hipGetLastError();
 }
 hipError_t launch_prefill_last(const PrefillLastArgs& a, hipStream_t s) {
