@@ -770,9 +770,14 @@ qt_status capture_graph(qt_graph** out_graph, F&& enqueue) {
 
 // ------------------------------------------------------------------ prompt prefill
 struct PrefillWs {
-  size_t x, ss, u, qkv, o, ffn, rowinfo, ul, ssl, cand, total;
+  size_t x, ss, u, qkv, o, ffn, rowinfo, ul, ssl, cand, part, total;
   int qkv_ld, cand_ld;
 };
+
+// Key splits of the prefill attention: a 16-row tile's blocks of 32 keys are
+// dealt over this many blocks (4 x the blocks of one split; at 1024 rows the last
+// tile's 32 key blocks become 8 per split).
+constexpr int kPrefillSplits = 4;
 
 PrefillWs make_prefill_ws(const qt_model_cfg& c, int R, int S) {
   const qt_decoder_cfg& t = c.talker;
@@ -795,6 +800,7 @@ PrefillWs make_prefill_ws(const qt_model_cfg& c, int R, int S) {
   w.ul = take((size_t)S * t.hidden * 2);
   w.ssl = take((size_t)S * 4);
   w.cand = take((size_t)S * w.cand_ld * 8);
+  w.part = take((size_t)R * t.n_q_heads * kPrefillSplits * (kHeadDim + 2) * 4);
   w.total = off;
   return w;
 }
@@ -829,16 +835,14 @@ qt_status check_prefill_args(const qt_model* m, const qt_prefill_args* a, const 
   return ok();
 }
 
-// Enqueue a prefill.  Per Talker layer: the four projections as GEMMs over slices
-// of at most 64 rows (the decode GEMM, its weights kept in the caches across the
-// slices), [q/k-norm, RoPE, K/V to pages] and [causal attention] over all rows.
+// Enqueue a prefill.  Per Talker layer: the four projections as many-row GEMMs
+// over all rows, [q/k-norm, RoPE, K/V to pages] and [causal attention].
 // Then the last row of each sequence: final norm, codec head, greedy token.
 qt_status enqueue_prefill(const qt_model* m, const qt_prefill_args* a, const qt_kv_caches* kv,
                           void* wsp, hipStream_t st) {
   const qt_model_cfg& c = m->cfg;
   const qt_decoder_cfg& T = c.talker;
   const int R = a->rows, S = a->max_seqs;
-  const int chunk = R < 64 ? R : 64;
   const PrefillWs w = make_prefill_ws(c, R, S);
   char* ws = (char*)wsp;
   float* x = (float*)(ws + w.x);
@@ -863,25 +867,22 @@ qt_status enqueue_prefill(const qt_model* m, const qt_prefill_args* a, const qt_
   QT_LAUNCH(launch_prefill_begin(b, st));
 
   auto run = [&](GemmArgs& g) -> qt_status {
-    g.keep_w = 1;  // every slice reads the same matrix again
-    QT_LAUNCH(launch_gemm(g, st));
+    QT_LAUNCH(launch_gemm_rows(g, st));
     return ok();
   };
   const size_t layer_elems = (size_t)kv->num_pages * T.n_kv_heads * kPage * kHeadDim;
+  const int resid_slots = T.hidden / kGemmRows;  // one per 16 weight rows of a residual GEMM
   int slots = 1;
   for (int l = 0; l < T.layers; ++l) {
     const LayerSlots& L = m->plan.tl[l];
     const uint16_t* next_gain =
         vp(m, l + 1 < T.layers ? m->plan.tl[l + 1].in_norm : m->plan.t_final);
     qt_status r;
-    for (int r0 = 0; r0 < R; r0 += chunk) {
-      GemmArgs g = gemm_norm(m, L.qkv, u + (size_t)r0 * 8, R, ss + r0, R, slots, T.rms_eps, chunk,
-                             a->status);
-      g.epi = EPI_STORE;
-      g.out_f32 = qkv + (size_t)r0 * w.qkv_ld;
-      g.out_ld = w.qkv_ld;
-      if ((r = run(g))) return r;
-    }
+    GemmArgs g = gemm_norm(m, L.qkv, u, R, ss, R, slots, T.rms_eps, R, a->status);
+    g.epi = EPI_STORE;
+    g.out_f32 = qkv;
+    g.out_ld = w.qkv_ld;
+    if ((r = run(g))) return r;
     PrefillQkArgs q{};
     q.qkv = qkv;
     q.qkv_ld = w.qkv_ld;
@@ -911,42 +912,35 @@ qt_status enqueue_prefill(const qt_model* m, const qt_prefill_args* a, const qt_
     at.max_pages = a->max_pages;
     at.rowinfo = rowinfo;
     at.o = o;
+    at.part = (float*)(ws + w.part);
+    at.n_splits = kPrefillSplits;
     QT_LAUNCH(launch_prefill_attn(at, st));
-    int o_slots = 1;
-    for (int r0 = 0; r0 < R; r0 += chunk) {
-      GemmArgs g = gemm_act(m, L.o, o + (size_t)r0 * 8, R, chunk, a->status);
-      g.epi = EPI_RESID;
-      g.out_f32 = x + (size_t)r0 * T.hidden;
-      g.out_ld = T.hidden;
-      g.u_gain = vp(m, L.post_norm);
-      g.u = u + (size_t)r0 * 8;
-      g.u_ld = R;
-      g.ss_out = ss + r0;
-      g.ss_out_ld = R;
-      o_slots = T.hidden / plan_gemm(g.nrows, g.K, g.M, g.scale != nullptr, true).rows_per_block;
-      if ((r = run(g))) return r;
-    }
-    for (int r0 = 0; r0 < R; r0 += chunk) {
-      GemmArgs g = gemm_norm(m, L.gu, u + (size_t)r0 * 8, R, ss + r0, R, o_slots, T.rms_eps, chunk,
-                             a->status);
-      g.epi = EPI_SWIGLU;
-      g.u = ffn + (size_t)r0 * 8;
-      g.u_ld = R;
-      if ((r = run(g))) return r;
-    }
-    for (int r0 = 0; r0 < R; r0 += chunk) {
-      GemmArgs g = gemm_act(m, L.down, ffn + (size_t)r0 * 8, R, chunk, a->status);
-      g.epi = EPI_RESID;
-      g.out_f32 = x + (size_t)r0 * T.hidden;
-      g.out_ld = T.hidden;
-      g.u_gain = next_gain;
-      g.u = u + (size_t)r0 * 8;
-      g.u_ld = R;
-      g.ss_out = ss + r0;
-      g.ss_out_ld = R;
-      slots = T.hidden / plan_gemm(g.nrows, g.K, g.M, g.scale != nullptr, true).rows_per_block;
-      if ((r = run(g))) return r;
-    }
+    g = gemm_act(m, L.o, o, R, R, a->status);
+    g.epi = EPI_RESID;
+    g.out_f32 = x;
+    g.out_ld = T.hidden;
+    g.u_gain = vp(m, L.post_norm);
+    g.u = u;
+    g.u_ld = R;
+    g.ss_out = ss;
+    g.ss_out_ld = R;
+    if ((r = run(g))) return r;
+    g = gemm_norm(m, L.gu, u, R, ss, R, resid_slots, T.rms_eps, R, a->status);
+    g.epi = EPI_SWIGLU;
+    g.u = ffn;
+    g.u_ld = R;
+    if ((r = run(g))) return r;
+    g = gemm_act(m, L.down, ffn, R, R, a->status);
+    g.epi = EPI_RESID;
+    g.out_f32 = x;
+    g.out_ld = T.hidden;
+    g.u_gain = next_gain;
+    g.u = u;
+    g.u_ld = R;
+    g.ss_out = ss;
+    g.ss_out_ld = R;
+    if ((r = run(g))) return r;
+    slots = resid_slots;
   }
 
   PrefillLastArgs pl{};

@@ -410,6 +410,127 @@ hipError_t gemm_dispatch(const GemmArgs& a, const GemmPlan& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ many-row GEMM
+// The same products for M in the hundreds or thousands (a prompt's rows): a block
+// computes 128 weight rows x 128 activation rows, each of its four waves a 64 x 64
+// quarter as 4 x 4 tiles of v_mfma_f32_16x16x32_f16, reading the weight tiles and
+// the chunked activations straight into operand registers (the next K step's
+// loads are issued before this step's products).  Blocks that share weight rows
+// are adjacent in launch order, so a weight tile is fetched from HBM about once
+// and the other row blocks find it in L2.  Outputs match the epilogues above:
+// EPI_STORE, EPI_RESID (x += y; half(x * gain) and per-16-row sums of squares)
+// and EPI_SWIGLU (rows 2p, 2p+1 -> column p), with the INT8 scale and the RMSNorm
+// factor 1/sqrt(sum ss / K + eps) of each activation row.
+template <bool I8>
+__global__ __launch_bounds__(256) void k_gemm_rows(GemmArgs a) {
+  constexpr int SUB = I8 ? 2 : 1;
+  __shared__ float s_inv[128];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int i = lane & 15, q = lane >> 4;
+  const int mb = 128 * blockIdx.x;
+  const int n0 = a.row0 + 128 * blockIdx.y + 64 * (wave & 1);
+  const int m0 = mb + 64 * (wave >> 1);
+  const int M = a.M, ld = a.act_ld;
+  const int ksteps = a.K / (32 * SUB);
+  if (tid < 128) {
+    float inv = 1.f;
+    const int m = mb + tid;
+    if (a.ss_in && m < M) {
+      float ss = 0.f;
+      for (int slot = 0; slot < a.ss_in_slots; ++slot) ss += a.ss_in[(size_t)slot * a.ss_in_ld + m];
+      inv = 1.0f / sqrtf(ss / (float)a.K + a.norm_eps);
+    }
+    s_inv[tid] = inv;
+  }
+  const uint4* W = reinterpret_cast<const uint4*>(a.W) + (size_t)(n0 >> 4) * ksteps * 64 + lane;
+  const uint4* H = reinterpret_cast<const uint4*>(a.act);
+  bool mrow[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) mrow[u] = m0 + 16 * u + i < M;
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc[t][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  uint4 cw[4], ch[SUB][4];
+  auto load = [&](int j, uint4* w, uint4 (*h)[4]) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) w[t] = W[((size_t)t * ksteps + j) * 64];
+#pragma unroll
+    for (int sb = 0; sb < SUB; ++sb) {
+      const size_t c = (size_t)(j * SUB + sb) * 4 + q;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        h[sb][u] = mrow[u] ? H[c * ld + m0 + 16 * u + i] : make_uint4(0, 0, 0, 0);
+    }
+  };
+  load(0, cw, ch);
+  for (int j = 0; j < ksteps; ++j) {
+    uint4 nw[4], nh[SUB][4];
+    if (j + 1 < ksteps) load(j + 1, nw, nh);
+#pragma unroll
+    for (int sb = 0; sb < SUB; ++sb)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const f16x8 A = __builtin_bit_cast(f16x8, I8 ? i8_to_f16x8(cw[t], sb) : cw[t]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          acc[t][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+              A, __builtin_bit_cast(f16x8, ch[sb][u]), acc[t][u], 0, 0, 0);
+      }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) cw[t] = nw[t];
+#pragma unroll
+    for (int sb = 0; sb < SUB; ++sb)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) ch[sb][u] = nh[sb][u];
+  }
+  __syncthreads();
+  // accumulator (t, u), lane (i, q), element e: weight row n0 + 16t + 4q + e,
+  // activation row m0 + 16u + i
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int nb = n0 + 16 * t + 4 * q;
+    float sc[4] = {1.f, 1.f, 1.f, 1.f};
+    if (a.scale)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sc[e] = a.scale[nb + e];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int m = m0 + 16 * u + i;
+      if (!mrow[u]) continue;  // (the four lanes of a row leave together)
+      const float inv = s_inv[m - mb];
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = acc[t][u][e] * sc[e] * inv;
+      if (a.epi == EPI_STORE) {
+        *reinterpret_cast<float4*>(a.out_f32 + (size_t)m * a.out_ld + nb) =
+            make_float4(v[0], v[1], v[2], v[3]);
+      } else if (a.epi == EPI_SWIGLU) {
+        const uint32_t pk = (uint32_t)f2h(silu(v[0]) * v[1]) | ((uint32_t)f2h(silu(v[2]) * v[3]) << 16);
+        *reinterpret_cast<uint32_t*>(a.u + chunked(m, nb >> 1, a.u_ld)) = pk;
+      } else {  // EPI_RESID
+        float* xp = a.out_f32 + (size_t)m * a.out_ld + nb;
+        const float4 x0 = *reinterpret_cast<const float4*>(xp);
+        const float x[4] = {x0.x + v[0], x0.y + v[1], x0.z + v[2], x0.w + v[3]};
+        *reinterpret_cast<float4*>(xp) = make_float4(x[0], x[1], x[2], x[3]);
+        if (a.u_gain) {
+          uint32_t h2[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e)
+            h2[e] = (uint32_t)f2h(x[2 * e] * bf2f(a.u_gain[nb + 2 * e])) |
+                    ((uint32_t)f2h(x[2 * e + 1] * bf2f(a.u_gain[nb + 2 * e + 1])) << 16);
+          *reinterpret_cast<uint2*>(a.u + chunked(m, nb, a.u_ld)) = make_uint2(h2[0], h2[1]);
+          float ss = x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+          ss += __shfl_xor(ss, 16);
+          ss += __shfl_xor(ss, 32);
+          if (q == 0) a.ss_out[(size_t)((n0 + 16 * t) >> 4) * a.ss_out_ld + m] = ss;
+        }
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ packing
 // Source rows [rows][K] bf16 -> half rows row0 + r*step of a tiled [N][K] matrix.
 __global__ __launch_bounds__(256) void k_pack_tiled(const uint16_t* src, int rows, int K,
@@ -481,6 +602,19 @@ void gemm_kernel_name(const GemmArgs& a, char* buf, int len) {
   const GemmPlan p = plan_gemm(a.nrows, a.K, a.M, i8, a.keep_w != 0, a.epi == EPI_SWIGLU);
   snprintf(buf, len, "k_gemm<%d,%d,%d,%s,%s,%d>", p.nw, p.mt, p.g, i8 ? "true" : "false",
            a.keep_w ? "true" : "false", p.tiles);
+}
+
+hipError_t launch_gemm_rows(const GemmArgs& a, hipStream_t s) {
+  if (a.M < 1 || a.nrows <= 0 || (a.nrows % 128) || (a.row0 % kGemmRows) ||
+      a.row0 + a.nrows > a.N || a.K <= 0 || (a.K % 64) || a.act_ld < a.M || (a.M % 16))
+    return hipErrorInvalidValue;
+  if (a.epi != EPI_STORE && a.epi != EPI_RESID && a.epi != EPI_SWIGLU) return hipErrorInvalidValue;
+  if (a.ss_in && a.ss_in_slots < 1) return hipErrorInvalidValue;
+  if (a.epi == EPI_RESID && a.u_gain && !a.ss_out) return hipErrorInvalidValue;
+  const dim3 grid((a.M + 127) / 128, a.nrows / 128);
+  if (a.scale) launch_kernel(k_gemm_rows<true>, grid, dim3(256), s, a);
+  else launch_kernel(k_gemm_rows<false>, grid, dim3(256), s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {

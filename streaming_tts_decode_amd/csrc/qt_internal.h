@@ -264,6 +264,8 @@ struct PrefillAttnArgs {
   int max_pages;
   const int32_t* rowinfo;
   uint16_t* o;              // chunked half [q_dim/8][R][8]
+  float* part;              // [R][n_q][n_splits][128 + 2]: split outputs, max and sum
+  int n_splits;             // key blocks of a tile are dealt round-robin over the splits
 };
 
 struct PrefillLastArgs {
@@ -338,6 +340,9 @@ GemmPlan plan_gemm(int nrows, int K, int M, bool i8, bool keep, bool swiglu = fa
 // Kernel symbol (with template arguments) that launch_gemm picks for these arguments.
 void gemm_kernel_name(const GemmArgs& a, char* buf, int len);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+// Many activation rows (M a multiple of 16; nrows a multiple of 128): EPI_STORE,
+// EPI_RESID and EPI_SWIGLU, one 16-row statistics slot per 16 weight rows.
+hipError_t launch_gemm_rows(const GemmArgs& a, hipStream_t s);
 hipError_t launch_attn_paged(const AttnPagedArgs& a, int B, float theta, hipStream_t s);
 hipError_t launch_attn_pred(const AttnPredArgs& a, float theta, hipStream_t s);
 hipError_t launch_frame_begin(const FrameBeginArgs& a, hipStream_t s);

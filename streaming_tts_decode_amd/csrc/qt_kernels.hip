@@ -929,36 +929,45 @@ __global__ __launch_bounds__(256) void k_prefill_qk(PrefillQkArgs a, float theta
   (jj == 0 ? a.k_pool : a.v_pool)[off] = f2bf(jj ? kvraw : kr);
 }
 
-// Causal attention over packed sequences on the matrix cores.  Block (16-row
-// tile, KV head h), two waves: wave w serves query head 2h + w for the tile's 16
-// rows.  For each sequence present in the tile, keys come in blocks of 32 (two
-// pages): K staged through LDS as half [key][dim], V as half [dim][key]; the next
-// block's loads are in flight while the current one is used.  Per block of keys:
+// Causal attention over packed sequences on the matrix cores.  Block (64-row
+// tile, KV head h, split z), eight waves: wave w serves rows 16(w/2) .. +15 of the
+// tile for query head 2h + w%2, so every staged key block serves 128 query rows.
+// For each sequence present in the tile, keys come in blocks of 32 (two pages),
+// blocks z, z + n_splits, ... to this split: K staged through LDS as half
+// [key][dim], V as half [dim][key] (a wave's lanes take consecutive keys, so the
+// transposing stores spread over the banks); the next block's loads are in flight
+// while the current one is used.  The split writes its unnormalised output, max
+// and sum per (row, head); k_prefill_attn_merge combines the splits in order.
+// Per block of keys:
 //   S = Q K^T   (v_mfma_f32_16x16x32_f16: 2 key tiles x 4 dim steps), masked to
 //               keys at or before the row's position;
 //   online softmax in the accumulator layout (lane l, element e: row 4(l>>4)+e,
 //               key l&15), row max and sum over 16 lanes;
 //   P -> per-wave LDS tile -> A operand; O += P V (8 dim tiles, one 32-key step).
-// Key slots past the sequence's last row are staged as zeros.
+// Key slots past the tile's last position are staged as zeros.
 constexpr int kKsLd = 136;  // half elements per staged key row (bank spread)
 constexpr int kVtLd = 40;   // half elements per staged dim row of V^T / per P row
+constexpr int kAttnRows = 64;
 
-__global__ __launch_bounds__(128) void k_prefill_attn(PrefillAttnArgs a) {
+__global__ __launch_bounds__(512) void k_prefill_attn(PrefillAttnArgs a) {
   __shared__ __align__(16) _Float16 Ks[32 * kKsLd];
   __shared__ __align__(16) _Float16 Vt[128 * kVtLd];
-  __shared__ __align__(16) _Float16 Ps[2][16 * kVtLd];
-  __shared__ int t_seq[16], t_pos[16];
+  __shared__ __align__(16) _Float16 Ps[8][16 * kVtLd];
+  __shared__ int t_seq[kAttnRows], t_pos[kAttnRows];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int i = lane & 15, qg = lane >> 4;
-  const int h = blockIdx.y, r0 = 16 * blockIdx.x, qh = 2 * h + wave;
-  if (tid < 16) {
-    t_seq[tid] = a.rowinfo[2 * (r0 + tid)];
-    t_pos[tid] = a.rowinfo[2 * (r0 + tid) + 1];
+  const int i = lane & 15, qg = lane >> 4, rg = wave >> 1;
+  const int h = blockIdx.y, r0 = kAttnRows * blockIdx.x, qh = 2 * h + (wave & 1);
+  const int z = blockIdx.z, nz = a.n_splits;
+  if (tid < kAttnRows) {
+    const int r = r0 + tid;
+    t_seq[tid] = r < a.R ? a.rowinfo[2 * r] : -1;
+    t_pos[tid] = r < a.R ? a.rowinfo[2 * r + 1] : 0;
   }
-  // Q operand: row i of the tile, dims [32 ks + 8 qg, +8), already scaled
+  // Q operand: row 16 rg + i of the tile, dims [32 ks + 8 qg, +8), already scaled
   f16x8 qf[4];
   {
-    const float* qp = a.qkv + (size_t)(r0 + i) * a.qkv_ld + qh * 128 + 8 * qg;
+    const int r = r0 + 16 * rg + i;
+    const float* qp = a.qkv + (size_t)(r < a.R ? r : 0) * a.qkv_ld + qh * 128 + 8 * qg;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const float4 x0 = *reinterpret_cast<const float4*>(qp + 32 * ks);
@@ -971,8 +980,8 @@ __global__ __launch_bounds__(128) void k_prefill_attn(PrefillAttnArgs a) {
   int row_seq[4], row_pos[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    row_seq[e] = t_seq[4 * qg + e];
-    row_pos[e] = t_pos[4 * qg + e];
+    row_seq[e] = t_seq[16 * rg + 4 * qg + e];
+    row_pos[e] = t_pos[16 * rg + 4 * qg + e];
   }
   f32x4 O[8];
 #pragma unroll
@@ -984,57 +993,53 @@ __global__ __launch_bounds__(128) void k_prefill_attn(PrefillAttnArgs a) {
     l[e] = 0.f;
   }
   int seq_lo = 0x7fffffff, seq_hi = -1;
-  for (int r = 0; r < 16; ++r)
+  for (int r = 0; r < kAttnRows; ++r)
     if (t_seq[r] >= 0) {
       seq_lo = t_seq[r] < seq_lo ? t_seq[r] : seq_lo;
       seq_hi = t_seq[r] > seq_hi ? t_seq[r] : seq_hi;
     }
   const size_t head_off = (size_t)h * (kPage * 128);
   const size_t page_elems = (size_t)a.n_kv * (kPage * 128);
-  // thread t stages 16-byte pieces u = t + 128 j: key u >> 4 (0..31), dims 8 (u & 15)
-  auto fetch = [&](int seq, int kb, int pmax, uint4* kr, uint4* vr) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int u = tid + 128 * j, key = u >> 4, d8 = u & 15;
-      const int kpos = 32 * kb + key, pi = kpos >> 4;
-      kr[j] = vr[j] = make_uint4(0, 0, 0, 0);
-      if (kpos <= pmax && pi < a.max_pages) {
-        const int pg = a.page_table[(size_t)seq * a.max_pages + pi];
-        if (pg >= 0 && pg < a.num_pages) {
-          const size_t off = (size_t)pg * page_elems + head_off + (size_t)(kpos & 15) * 128 + 8 * d8;
-          kr[j] = *reinterpret_cast<const uint4*>(a.k_pool + off);
-          vr[j] = *reinterpret_cast<const uint4*>(a.v_pool + off);
-        }
-      }
-    }
+  // staging pieces of 16 bytes: K piece (key tid >> 4, dims 8 (tid & 15)), V piece
+  // (key tid & 31, dims 8 (tid >> 5))
+  const int kkey = tid >> 4, kd8 = tid & 15, vkey = tid & 31, vd8 = tid >> 5;
+  auto piece = [&](int seq, int kb, int pmax, int key, int d8, const uint16_t* pool) -> uint4 {
+    const int kpos = 32 * kb + key, pi = kpos >> 4;
+    if (kpos > pmax || pi >= a.max_pages) return make_uint4(0, 0, 0, 0);
+    const int pg = a.page_table[(size_t)seq * a.max_pages + pi];
+    if (pg < 0 || pg >= a.num_pages) return make_uint4(0, 0, 0, 0);
+    return *reinterpret_cast<const uint4*>(pool + (size_t)pg * page_elems + head_off +
+                                           (size_t)(kpos & 15) * 128 + 8 * d8);
   };
   for (int seq = seq_lo; seq <= seq_hi; ++seq) {
     int pmax = -1;
-    for (int r = 0; r < 16; ++r)
+    for (int r = 0; r < kAttnRows; ++r)
       if (t_seq[r] == seq && t_pos[r] > pmax) pmax = t_pos[r];
     if (pmax < 0) continue;
     const int nblk = pmax / 32 + 1;
-    uint4 kr[4], vr[4];
-    fetch(seq, 0, pmax, kr, vr);
-    for (int kb = 0; kb < nblk; ++kb) {
+    if (z >= nblk) continue;
+    uint4 kr = piece(seq, z, pmax, kkey, kd8, a.k_pool);
+    uint4 vr = piece(seq, z, pmax, vkey, vd8, a.v_pool);
+    for (int kb = z; kb < nblk; kb += nz) {
       __syncthreads();  // the previous block of keys is consumed
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int u = tid + 128 * j, key = u >> 4, d8 = u & 15;
-        const uint32_t kw[4] = {kr[j].x, kr[j].y, kr[j].z, kr[j].w};
-        const uint32_t vw[4] = {vr[j].x, vr[j].y, vr[j].z, vr[j].w};
+      {
+        const uint32_t kw[4] = {kr.x, kr.y, kr.z, kr.w};
+        const uint32_t vw[4] = {vr.x, vr.y, vr.z, vr.w};
         f16x8 kh;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
           kh[2 * w] = (_Float16)bf_lo(kw[w]);
           kh[2 * w + 1] = (_Float16)bf_hi(kw[w]);
-          Vt[(8 * d8 + 2 * w) * kVtLd + key] = (_Float16)bf_lo(vw[w]);
-          Vt[(8 * d8 + 2 * w + 1) * kVtLd + key] = (_Float16)bf_hi(vw[w]);
+          Vt[(8 * vd8 + 2 * w) * kVtLd + vkey] = (_Float16)bf_lo(vw[w]);
+          Vt[(8 * vd8 + 2 * w + 1) * kVtLd + vkey] = (_Float16)bf_hi(vw[w]);
         }
-        *reinterpret_cast<f16x8*>(Ks + key * kKsLd + 8 * d8) = kh;
+        *reinterpret_cast<f16x8*>(Ks + kkey * kKsLd + 8 * kd8) = kh;
       }
       __syncthreads();
-      if (kb + 1 < nblk) fetch(seq, kb + 1, pmax, kr, vr);
+      if (kb + nz < nblk) {
+        kr = piece(seq, kb + nz, pmax, kkey, kd8, a.k_pool);
+        vr = piece(seq, kb + nz, pmax, vkey, vd8, a.v_pool);
+      }
       f32x4 S0 = f32x4{0.f, 0.f, 0.f, 0.f}, S1 = S0;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
@@ -1082,12 +1087,48 @@ __global__ __launch_bounds__(128) void k_prefill_attn(PrefillAttnArgs a) {
   }
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const int row = r0 + 4 * qg + e;
-    const float inv = (row_seq[e] >= 0 && l[e] > 0.f) ? 1.f / l[e] : 0.f;
+    const int row = r0 + 16 * rg + 4 * qg + e;
+    if (row >= a.R) continue;
+    float* pp = a.part + ((size_t)(row * a.n_q + qh) * nz + z) * 130;
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb)
-      a.o[chunked(row, qh * 128 + 16 * nb + i, a.R)] = f2h(O[nb][e] * inv);
+    for (int nb = 0; nb < 8; ++nb) pp[16 * nb + i] = O[nb][e];
+    if (i == 0) {
+      pp[128] = m[e];
+      pp[129] = l[e];
+    }
   }
+}
+
+// Split merge, block (16-row tile, KV head h): thread t serves (row t/16, query
+// head 2h + (t/8)%2), dims 16(t%8) .. +15; splits combined in order with weights
+// exp(m_z - max_z m), the half output written chunked for the o projection.
+__global__ __launch_bounds__(256) void k_prefill_attn_merge(PrefillAttnArgs a) {
+  const int tid = threadIdx.x, h = blockIdx.y, r0 = 16 * blockIdx.x;
+  const int pair = tid >> 3, sub = tid & 7, row = r0 + (pair >> 1), qh = 2 * h + (pair & 1);
+  const int nz = a.n_splits;
+  const float* pp = a.part + (size_t)(row * a.n_q + qh) * nz * 130;
+  float M = -INFINITY;
+  for (int z = 0; z < nz; ++z) M = fmaxf(M, pp[z * 130 + 128]);
+  float acc[16], L = 0.f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+  for (int z = 0; z < nz; ++z) {
+    const float mz = pp[z * 130 + 128];
+    const float w = mz == -INFINITY ? 0.f : expf(mz - M);
+    L = fmaf(w, pp[z * 130 + 129], L);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = fmaf(w, pp[z * 130 + 16 * sub + e], acc[e]);
+  }
+  const float inv = (a.rowinfo[2 * row] >= 0 && L > 0.f) ? 1.f / L : 0.f;
+  uint32_t packed[8];
+#pragma unroll
+  for (int w = 0; w < 8; ++w)
+    packed[w] = (uint32_t)f2h(acc[2 * w] * inv) | ((uint32_t)f2h(acc[2 * w + 1] * inv) << 16);
+  const int col = qh * 128 + 16 * sub;
+  *reinterpret_cast<uint4*>(a.o + chunked(row, col, a.R)) =
+      make_uint4(packed[0], packed[1], packed[2], packed[3]);
+  *reinterpret_cast<uint4*>(a.o + chunked(row, col + 8, a.R)) =
+      make_uint4(packed[4], packed[5], packed[6], packed[7]);
 }
 
 // One block per sequence: its length into kv_len, and from its last row the head's
@@ -1210,7 +1251,10 @@ hipError_t launch_prefill_qk(const PrefillQkArgs& a, int R, float theta, hipStre
 }
 hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t s) {
   if (a.R < 16 || (a.R % 16) || a.n_q != 2 * a.n_kv) return hipErrorInvalidValue;
-  launch_kernel(k_prefill_attn, dim3(a.R / 16, a.n_kv), dim3(128), s, a);
+  if (a.n_splits < 1 || a.n_splits > 64) return hipErrorInvalidValue;
+  launch_kernel(k_prefill_attn, dim3((a.R + kAttnRows - 1) / kAttnRows, a.n_kv, a.n_splits),
+                dim3(512), s, a);
+  launch_kernel(k_prefill_attn_merge, dim3(a.R / 16, a.n_kv), dim3(256), s, a);
   return hipGetLastError();
 }
 hipError_t launch_prefill_last(const PrefillLastArgs& a, hipStream_t s) {

@@ -148,3 +148,9 @@ def test_prefill_full_model(full_pm, orc_full):
     dec, _, _ = _run(full_pm, orc_full, synth.FULL, [45, 19], rows=64, max_pages=8, tag="pffull",
                      frames_after=1)
     dec.close()
+
+
+def test_prefill_full_model_int8(full_pm_i8, orc_full_i8):
+    dec, _, _ = _run(full_pm_i8, orc_full_i8, synth.FULL, [33], rows=64, max_pages=4, tag="pfi8",
+                     frames_after=1)
+    dec.close()
