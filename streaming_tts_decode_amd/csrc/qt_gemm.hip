@@ -421,18 +421,22 @@ hipError_t gemm_dispatch(const GemmArgs& a, const GemmPlan& p, hipStream_t s) {
 // EPI_STORE, EPI_RESID (x += y; half(x * gain) and per-16-row sums of squares)
 // and EPI_SWIGLU (rows 2p, 2p+1 -> column p), with the INT8 scale and the RMSNorm
 // factor 1/sqrt(sum ss / K + eps) of each activation row.
-template <bool I8>
+// TN x TM: 16-row weight tiles x 16-row activation tiles per wave (4 x 4, or
+// smaller when the big tiles would leave CUs idle); the block's four waves cover
+// 2 TN x 2 TM tiles.
+template <bool I8, int TN, int TM>
 __global__ __launch_bounds__(256) void k_gemm_rows(GemmArgs a) {
   constexpr int SUB = I8 ? 2 : 1;
-  __shared__ float s_inv[128];
+  constexpr int BM = 32 * TM;  // activation rows per block
+  __shared__ float s_inv[BM];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i = lane & 15, q = lane >> 4;
-  const int mb = 128 * blockIdx.x;
-  const int n0 = a.row0 + 128 * blockIdx.y + 64 * (wave & 1);
-  const int m0 = mb + 64 * (wave >> 1);
+  const int mb = BM * blockIdx.x;
+  const int n0 = a.row0 + 32 * TN * blockIdx.y + 16 * TN * (wave & 1);
+  const int m0 = mb + 16 * TM * (wave >> 1);
   const int M = a.M, ld = a.act_ld;
   const int ksteps = a.K / (32 * SUB);
-  if (tid < 128) {
+  if (tid < BM) {
     float inv = 1.f;
     const int m = mb + tid;
     if (a.ss_in && m < M) {
@@ -444,59 +448,59 @@ __global__ __launch_bounds__(256) void k_gemm_rows(GemmArgs a) {
   }
   const uint4* W = reinterpret_cast<const uint4*>(a.W) + (size_t)(n0 >> 4) * ksteps * 64 + lane;
   const uint4* H = reinterpret_cast<const uint4*>(a.act);
-  bool mrow[4];
+  bool mrow[TM];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) mrow[u] = m0 + 16 * u + i < M;
-  f32x4 acc[4][4];
+  for (int u = 0; u < TM; ++u) mrow[u] = m0 + 16 * u + i < M;
+  f32x4 acc[TN][TM];
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+  for (int t = 0; t < TN; ++t)
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc[t][u] = f32x4{0.f, 0.f, 0.f, 0.f};
-  uint4 cw[4], ch[SUB][4];
-  auto load = [&](int j, uint4* w, uint4 (*h)[4]) {
+    for (int u = 0; u < TM; ++u) acc[t][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  uint4 cw[TN], ch[SUB][TM];
+  auto load = [&](int j, uint4* w, uint4 (*h)[TM]) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) w[t] = W[((size_t)t * ksteps + j) * 64];
+    for (int t = 0; t < TN; ++t) w[t] = W[((size_t)t * ksteps + j) * 64];
 #pragma unroll
     for (int sb = 0; sb < SUB; ++sb) {
       const size_t c = (size_t)(j * SUB + sb) * 4 + q;
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < TM; ++u)
         h[sb][u] = mrow[u] ? H[c * ld + m0 + 16 * u + i] : make_uint4(0, 0, 0, 0);
     }
   };
   load(0, cw, ch);
   for (int j = 0; j < ksteps; ++j) {
-    uint4 nw[4], nh[SUB][4];
+    uint4 nw[TN], nh[SUB][TM];
     if (j + 1 < ksteps) load(j + 1, nw, nh);
 #pragma unroll
     for (int sb = 0; sb < SUB; ++sb)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
+      for (int t = 0; t < TN; ++t) {
         const f16x8 A = __builtin_bit_cast(f16x8, I8 ? i8_to_f16x8(cw[t], sb) : cw[t]);
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < TM; ++u)
           acc[t][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
               A, __builtin_bit_cast(f16x8, ch[sb][u]), acc[t][u], 0, 0, 0);
       }
 #pragma unroll
-    for (int t = 0; t < 4; ++t) cw[t] = nw[t];
+    for (int t = 0; t < TN; ++t) cw[t] = nw[t];
 #pragma unroll
     for (int sb = 0; sb < SUB; ++sb)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) ch[sb][u] = nh[sb][u];
+      for (int u = 0; u < TM; ++u) ch[sb][u] = nh[sb][u];
   }
   __syncthreads();
   // accumulator (t, u), lane (i, q), element e: weight row n0 + 16t + 4q + e,
   // activation row m0 + 16u + i
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
+  for (int t = 0; t < TN; ++t) {
     const int nb = n0 + 16 * t + 4 * q;
     float sc[4] = {1.f, 1.f, 1.f, 1.f};
     if (a.scale)
 #pragma unroll
       for (int e = 0; e < 4; ++e) sc[e] = a.scale[nb + e];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < TM; ++u) {
       const int m = m0 + 16 * u + i;
       if (!mrow[u]) continue;  // (the four lanes of a row leave together)
       const float inv = s_inv[m - mb];
@@ -611,9 +615,24 @@ hipError_t launch_gemm_rows(const GemmArgs& a, hipStream_t s) {
   if (a.epi != EPI_STORE && a.epi != EPI_RESID && a.epi != EPI_SWIGLU) return hipErrorInvalidValue;
   if (a.ss_in && a.ss_in_slots < 1) return hipErrorInvalidValue;
   if (a.epi == EPI_RESID && a.u_gain && !a.ss_out) return hipErrorInvalidValue;
-  const dim3 grid((a.M + 127) / 128, a.nrows / 128);
-  if (a.scale) launch_kernel(k_gemm_rows<true>, grid, dim3(256), s, a);
-  else launch_kernel(k_gemm_rows<false>, grid, dim3(256), s, a);
+  // 128 x 128 blocks unless they leave fewer than two blocks per CU: then 64 weight
+  // rows, then 64 x 64
+  const long long big = (long long)((a.M + 127) / 128) * (a.nrows / 128);
+  const long long mid = (long long)((a.M + 127) / 128) * (a.nrows / 64);
+  const bool i8 = a.scale != nullptr;
+  if (big >= 512) {
+    const dim3 grid((a.M + 127) / 128, a.nrows / 128);
+    if (i8) launch_kernel((k_gemm_rows<true, 4, 4>), grid, dim3(256), s, a);
+    else launch_kernel((k_gemm_rows<false, 4, 4>), grid, dim3(256), s, a);
+  } else if (mid >= 512) {
+    const dim3 grid((a.M + 127) / 128, a.nrows / 64);
+    if (i8) launch_kernel((k_gemm_rows<true, 2, 4>), grid, dim3(256), s, a);
+    else launch_kernel((k_gemm_rows<false, 2, 4>), grid, dim3(256), s, a);
+  } else {
+    const dim3 grid((a.M + 63) / 64, a.nrows / 64);
+    if (i8) launch_kernel((k_gemm_rows<true, 2, 2>), grid, dim3(256), s, a);
+    else launch_kernel((k_gemm_rows<false, 2, 2>), grid, dim3(256), s, a);
+  }
   return hipGetLastError();
 }
 
