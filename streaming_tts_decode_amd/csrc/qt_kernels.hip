@@ -834,16 +834,21 @@ __global__ __launch_bounds__(256) void k_sched_setup(SchedSetupArgs a) {
   }
 }
 
+// Grid (slot, part): the slot's rows are copied by kSchedCollectParts blocks.
+constexpr int kSchedCollectParts = 16;
+
 __global__ __launch_bounds__(256) void k_sched_collect(SchedCollectArgs a) {
-  const int b = blockIdx.x, tid = threadIdx.x;
+  const int b = blockIdx.x, part = blockIdx.y, tid = threadIdx.x;
   const int sess = a.slot_session[b];
   if (sess < 0) return;
+  const int t = part * 256 + tid, stride = kSchedCollectParts * 256;
   const float4* l0 = reinterpret_cast<const float4*>(a.logits0 + (size_t)b * a.talker_vocab);
   float4* r0 = reinterpret_cast<float4*>(a.res_logits0 + (size_t)sess * a.talker_vocab);
-  for (int i = tid; i < a.talker_vocab / 4; i += 256) r0[i] = l0[i];
+  for (int i = t; i < a.talker_vocab / 4; i += stride) r0[i] = l0[i];
   const float4* lp = reinterpret_cast<const float4*>(a.logits_pred + (size_t)b * a.pred_elems);
   float4* rp = reinterpret_cast<float4*>(a.res_pred + (size_t)sess * a.pred_elems);
-  for (int i = tid; i < a.pred_elems / 4; i += 256) rp[i] = lp[i];
+  for (int i = t; i < a.pred_elems / 4; i += stride) rp[i] = lp[i];
+  if (part != 0) return;
   for (int i = tid; i < a.ncb; i += 256)
     a.res_tokens[(size_t)sess * a.ncb + i] = a.tokens[(size_t)b * a.ncb + i];
   if (tid == 0 && a.eos_index >= 0 && a.slot_check[b] > 0 && a.flags[sess] == 0) {
@@ -1233,7 +1238,7 @@ hipError_t launch_sched_collect(const SchedCollectArgs& a, hipStream_t s) {
   if (a.B < 1 || a.B > kSchedMaxBatch || (a.talker_vocab % 4) || (a.pred_elems % 4) ||
       a.eos_index < -1 || a.eos_index >= a.talker_vocab)
     return hipErrorInvalidValue;
-  launch_kernel(k_sched_collect, dim3(a.B), dim3(256), s, a);
+  launch_kernel(k_sched_collect, dim3(a.B, kSchedCollectParts), dim3(256), s, a);
   return hipGetLastError();
 }
 }  // namespace qt
