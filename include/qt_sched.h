@@ -14,7 +14,8 @@
  *
  * Behaviour
  *  - Grouping: ready sessions fall into classes (first frame or not, teacher-forced
- *    or not); classes never share a batched call, first-frame classes run first.
+ *    or not, sampling or not); classes never share a batched call, first-frame
+ *    classes run first.
  *    Each class is cut into groups of the largest captured size plus one remainder
  *    group, and each group replays the graph of the smallest captured size that
  *    holds it; the extra slots (padding) decode a zero input into a reserved page
@@ -103,6 +104,16 @@ qt_status qt_sched_create(qt_model* model, const qt_sched_cfg* cfg, const qt_kv_
  * done with them) or too few pages are free. */
 qt_status qt_sched_open(qt_sched* s, int32_t length, int32_t min_frames, int32_t max_frames,
                         int32_t* pages, int32_t* session);
+
+/* Draw the session's tokens (qt_sampling in qt.h) from its next submitted frame on:
+ * params (host [2]: codebook 0, then the predictor's codebooks) and seed are copied
+ * now; params = NULL returns the session to greedy tokens.  The draw counter is the
+ * session's cache length before each frame, and its seen set of codebook-0 tokens
+ * starts empty at open.  Sampling and greedy sessions are decoded in separate
+ * batched calls.  End of speech is still decided against the greedy codebook-0
+ * choice.  QT_E_INVALID_ARG for parameters out of range. */
+qt_status qt_sched_set_sampling(qt_sched* s, int32_t session, const qt_sampler_params* params,
+                                uint64_t seed);
 
 /* Queue the next frame of a running session.  talker_in: device bf16 [talker hidden];
  * forced: device int32 [n_codebooks] or NULL (teacher forcing as in qt_frame_inputs).

@@ -34,7 +34,7 @@ EXPORTED = ["qt_last_error", "qt_abi_version", "qt_validate_cfg", "qt_packed_byt
             "qt_sched_bytes", "qt_sched_create", "qt_sched_open", "qt_sched_submit",
             "qt_sched_step", "qt_sched_outputs", "qt_sched_state", "qt_sched_length",
             "qt_sched_status_word", "qt_sched_free_pages", "qt_sched_close", "qt_sched_plan",
-            "qt_sched_destroy"]
+            "qt_sched_destroy", "qt_sched_set_sampling"]
 SCHED_MAX_BUCKETS, SCHED_MAX_BATCH, SCHED_MAX_SESSIONS = 8, 32, 4096
 SESSION_FREE, SESSION_RUNNING, SESSION_ENDED_EOS, SESSION_ENDED_MAX = 0, 1, 2, 3
 KERNEL_KINDS = {0: "frame_begin", 1: "gemm", 2: "attn_paged", 3: "attn_pred", 4: "embed",
@@ -193,6 +193,8 @@ def lib():
                                       _P, C.c_uint64, _P, C.POINTER(_P)]
         L.qt_sched_open.restype = st
         L.qt_sched_open.argtypes = [_P, C.c_int32, C.c_int32, C.c_int32, i32p, i32p]
+        L.qt_sched_set_sampling.restype = st
+        L.qt_sched_set_sampling.argtypes = [_P, C.c_int32, C.POINTER(SamplerParams), C.c_uint64]
         L.qt_sched_submit.restype = st
         L.qt_sched_submit.argtypes = [_P, C.c_int32, _P, _P]
         L.qt_sched_step.restype = st
@@ -393,6 +395,15 @@ def qt_sched_open(sched: int, length: int, min_frames: int, max_frames: int,
     _check(lib().qt_sched_open(sched, length, min_frames, max_frames, pages, C.byref(sid)),
            "qt_sched_open")
     return sid.value, list(pages)[:n]
+
+
+def qt_sched_set_sampling(sched: int, session: int, params=None, seed: int = 0):
+    """params: (codebook-0, predictor) pair of (temperature, top_p, repetition_penalty,
+    top_k) tuples, or None for greedy tokens."""
+    arr = None
+    if params is not None:
+        arr = (SamplerParams * 2)(*(SamplerParams(*p) for p in params))
+    _check(lib().qt_sched_set_sampling(sched, session, arr, seed), "qt_sched_set_sampling")
 
 
 def qt_sched_submit(sched: int, session: int, talker_in_ptr: int, forced_ptr: int | None = None):

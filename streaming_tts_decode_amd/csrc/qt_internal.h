@@ -311,6 +311,15 @@ struct SchedSetupArgs {
   int32_t new_page[kSchedMaxBatch];
   const uint16_t* in_ptr[kSchedMaxBatch];
   const int32_t* forced_ptr[kSchedMaxBatch];
+  // sampling groups: per-slot parameters and seed into the batch tables, and the
+  // session's seen set (cleared on its first frame) into the batch seen table
+  qt_sampler_params* params;     // batch [B][2], or nullptr
+  uint64_t* seed;                // batch [B]
+  uint32_t* seen;                // batch [B][seen_ld]
+  uint32_t* sess_seen;           // [max_sessions][seen_ld]
+  int seen_ld;
+  qt_sampler_params slot_params[kSchedMaxBatch][2];
+  uint64_t slot_seed[kSchedMaxBatch];
 };
 
 struct SchedCollectArgs {
@@ -325,6 +334,12 @@ struct SchedCollectArgs {
   int32_t* host_flags;           // pinned host [max_sessions]
   int32_t slot_session[kSchedMaxBatch];
   int32_t slot_check[kSchedMaxBatch];    // frame number to record at end of speech, or 0
+  // sampling groups: tokens[b][0] is a draw, so the end-of-speech test takes the
+  // greedy choice from logits0 itself; the batch seen rows go back to the sessions
+  int sampled;
+  const uint32_t* seen;          // batch [B][seen_ld]
+  uint32_t* sess_seen;           // [max_sessions][seen_ld]
+  int seen_ld;
 };
 
 hipError_t launch_sched_setup(const SchedSetupArgs& a, hipStream_t s);

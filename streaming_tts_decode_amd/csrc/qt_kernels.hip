@@ -803,6 +803,11 @@ __global__ __launch_bounds__(256) void k_sched_setup(SchedSetupArgs a) {
     for (int i = tid; i < a.H / 8; i += 256) in_row[i] = make_uint4(0, 0, 0, 0);
     if (a.forced)
       for (int i = tid; i < a.ncb; i += 256) a.forced[(size_t)b * a.ncb + i] = 0;
+    if (a.params) {
+      for (int i = tid; i < a.seen_ld; i += 256) a.seen[(size_t)b * a.seen_ld + i] = 0u;
+      if (tid < 2) a.params[2 * b + tid] = qt_sampler_params{1.f, 1.f, 1.f, 1};
+      if (tid == 2) a.seed[b] = 0;
+    }
     if (tid == 0) a.kv_len[b] = 0;
     return;
   }
@@ -828,6 +833,13 @@ __global__ __launch_bounds__(256) void k_sched_setup(SchedSetupArgs a) {
     const int32_t* f = a.forced_ptr[b];
     for (int i = tid; i < a.ncb; i += 256) a.forced[(size_t)b * a.ncb + i] = f ? f[i] : 0;
   }
+  if (a.params) {
+    uint32_t* dst = a.seen + (size_t)b * a.seen_ld;
+    const uint32_t* src = a.sess_seen + (size_t)sess * a.seen_ld;
+    for (int i = tid; i < a.seen_ld; i += 256) dst[i] = first >= 0 ? 0u : src[i];
+    if (tid < 2) a.params[2 * b + tid] = a.slot_params[b][tid];
+    if (tid == 2) a.seed[b] = a.slot_seed[b];
+  }
   if (tid == 0) {
     a.kv_len[b] = a.slot_len[b];
     if (first >= 0) a.flags[sess] = 0;
@@ -851,9 +863,34 @@ __global__ __launch_bounds__(256) void k_sched_collect(SchedCollectArgs a) {
   if (part != 0) return;
   for (int i = tid; i < a.ncb; i += 256)
     a.res_tokens[(size_t)sess * a.ncb + i] = a.tokens[(size_t)b * a.ncb + i];
-  if (tid == 0 && a.eos_index >= 0 && a.slot_check[b] > 0 && a.flags[sess] == 0) {
+  if (a.sampled)
+    for (int i = tid; i < a.seen_ld; i += 256)
+      a.sess_seen[(size_t)sess * a.seen_ld + i] = a.seen[(size_t)b * a.seen_ld + i];
+  const bool check = a.eos_index >= 0 && a.slot_check[b] > 0 && a.flags[sess] == 0;
+  __shared__ int s_greedy;
+  if (a.sampled && check) {
+    // the greedy codebook-0 choice (lowest index wins ties; NaN never chosen)
+    __shared__ unsigned long long best[4];
     const float* lg = a.logits0 + (size_t)b * a.talker_vocab;
-    const int t0 = a.tokens[(size_t)b * a.ncb];
+    unsigned long long k = 0ull;
+    for (int v = tid; v < a.cb0_range; v += 256) {
+      const float x = lg[v];
+      const unsigned long long c = x == x ? greedy_key(x, v) : 0ull;
+      k = c > k ? c : k;
+    }
+    k = wave_max_u64(k);
+    if ((tid & 63) == 0) best[tid >> 6] = k;
+    __syncthreads();
+    if (tid == 0) {
+      unsigned long long m = best[0];
+      for (int w = 1; w < 4; ++w) m = best[w] > m ? best[w] : m;
+      s_greedy = key_index(m);
+    }
+    __syncthreads();
+  }
+  if (tid == 0 && check) {
+    const float* lg = a.logits0 + (size_t)b * a.talker_vocab;
+    const int t0 = a.sampled ? s_greedy : a.tokens[(size_t)b * a.ncb];
     const int e = a.eos_index;
     bool end = false;
     if (t0 >= 0 && t0 < a.cb0_range)

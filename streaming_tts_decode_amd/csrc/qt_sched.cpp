@@ -2,6 +2,7 @@
 // grouping into captured batch sizes, and the per-group setup / graph replay /
 // collect sequence.  The behaviour is specified in qt_sched.h.
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <string.h>
 
 #include <algorithm>
@@ -30,7 +31,8 @@ size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 // Byte offsets of the scheduler's part of the device buffer (Bm = largest bucket).
 struct Layout {
   size_t ws, ws_bytes, kv_len, page_table, talker_in, forced, logits0, logits_pred, tokens,
-      status, sess_pages, flags, res_l0, res_lp, res_tok, total;
+      status, sess_pages, flags, res_l0, res_lp, res_tok, params, seed, seen, sess_seen, total;
+  int seen_ld;
   size_t host_flags, host_pages, host_total;
 };
 
@@ -86,6 +88,11 @@ qt_status make_layout(const qt_model_cfg& m, const qt_sched_cfg& c, Layout* L) {
   L->res_l0 = take(S * m.talker_vocab * 4);
   L->res_lp = take(S * pred * 4);
   L->res_tok = take(S * m.n_codebooks * 4);
+  L->seen_ld = (m.cb0_range + 31) / 32;
+  L->params = take((size_t)Bm * 2 * sizeof(qt_sampler_params));
+  L->seed = take((size_t)Bm * 8);
+  L->seen = take((size_t)Bm * L->seen_ld * 4);
+  L->sess_seen = take(S * L->seen_ld * 4);
   L->total = off;
   L->host_flags = 0;
   L->host_pages = align_up(S * 4);
@@ -105,6 +112,9 @@ struct Session {
   const int32_t* forced = nullptr;
   long long last_seq = 0;  // step that last decoded it (0: none)
   std::vector<int32_t> pages;
+  bool sampling = false;
+  qt_sampler_params params[2] = {};
+  uint64_t seed = 0;
 };
 
 }  // namespace
@@ -122,7 +132,7 @@ struct qt_sched {
   int32_t* host_flags_dev;
   hipStream_t stream;
   int pad_page;
-  qt_graph* graphs[QT_SCHED_MAX_BUCKETS][2];
+  qt_graph* graphs[QT_SCHED_MAX_BUCKETS][2][2];  // [bucket][forced][sampling]
   std::vector<Session> sess;
   std::vector<int32_t> free_pages;  // stack: popped from the back
   std::vector<int32_t> free_ids;
@@ -200,10 +210,10 @@ int bucket_index(const qt_sched* s, int size) {
   return -1;
 }
 
-// Capture (once) the frame of batch size buckets[bi], teacher-forced or not, over
-// the scheduler's batch tables.
-qt_status ensure_graph(qt_sched* s, int bi, int forced) {
-  if (s->graphs[bi][forced]) return QT_OK;
+// Capture (once) the frame of batch size buckets[bi], teacher-forced or not, drawing
+// tokens or not, over the scheduler's batch tables.
+qt_status ensure_graph(qt_sched* s, int bi, int forced, int sampled) {
+  if (s->graphs[bi][forced][sampled]) return QT_OK;
   const Layout& L = s->L;
   qt_sessions ss{};
   ss.batch = s->cfg.buckets[bi];
@@ -219,8 +229,22 @@ qt_status ensure_graph(qt_sched* s, int bi, int forced) {
   out.logits_pred = (float*)(s->dev + L.logits_pred);
   out.tokens = (int32_t*)(s->dev + L.tokens);
   out.status = (uint32_t*)(s->dev + L.status);
+  qt_sampling smp{};
+  if (sampled) {
+    smp.params = (const qt_sampler_params*)(s->dev + L.params);
+    smp.seed = (const uint64_t*)(s->dev + L.seed);
+    smp.counter = ss.kv_len;  // each slot's cache length before the frame
+    smp.seen0 = (uint32_t*)(s->dev + L.seen);
+    in.sampling = &smp;
+  }
   return qt_frame_graph_create(s->model, &ss, &s->kv, &in, &out, s->dev + L.ws, L.ws_bytes,
-                               &s->graphs[bi][forced]);
+                               &s->graphs[bi][forced][sampled]);
+}
+
+bool params_ok(const qt_sampler_params& p) {
+  return p.temperature > 0.f && p.temperature < INFINITY && p.top_p > 0.f && p.top_p <= 1.f &&
+         p.repetition_penalty >= 1.f && p.repetition_penalty < INFINITY && p.top_k >= 1 &&
+         p.top_k <= QT_SAMPLER_MAX_TOP_K;
 }
 
 }  // namespace
@@ -344,6 +368,27 @@ qt_status qt_sched_open(qt_sched* s, int32_t length, int32_t min_frames, int32_t
   return QT_OK;
 }
 
+qt_status qt_sched_set_sampling(qt_sched* s, int32_t session, const qt_sampler_params* params,
+                                uint64_t seed) {
+  qt_status st = check_session(s, session);
+  if (st) return st;
+  Session& q = s->sess[session];
+  if (!params) {
+    q.sampling = false;
+    return QT_OK;
+  }
+  for (int g = 0; g < 2; ++g)
+    if (!params_ok(params[g]))
+      return report(QT_E_INVALID_ARG,
+                    "sampler params[%d] out of range (temperature > 0, 0 < top_p <= 1, penalty >= 1, "
+                    "top_k 1..%d)", g, QT_SAMPLER_MAX_TOP_K);
+  q.sampling = true;
+  q.params[0] = params[0];
+  q.params[1] = params[1];
+  q.seed = seed;
+  return QT_OK;
+}
+
 qt_status qt_sched_submit(qt_sched* s, int32_t session, const void* talker_in,
                           const int32_t* forced) {
   qt_status st = check_session(s, session);
@@ -373,7 +418,7 @@ qt_status qt_sched_step(qt_sched* s, int32_t* n_groups) {
       return report(QT_E_CAPACITY, "session %d: %d positions fill its %d pages", id, q.length, mp);
     if (q.length == (int)q.pages.size() * ps) ++new_pages;
     ready.push_back(id);
-    cls.push_back((q.frames == 0 ? 0 : 2) + (q.forced ? 1 : 0));
+    cls.push_back((q.frames == 0 ? 0 : 4) + (q.forced ? 2 : 0) + (q.sampling ? 1 : 0));
   }
   if (ready.empty()) return QT_OK;
   if (new_pages > (int)s->free_pages.size())
@@ -385,10 +430,10 @@ qt_status qt_sched_step(qt_sched* s, int32_t* n_groups) {
   plan_groups(cls.data(), n, s->cfg.buckets, s->cfg.n_buckets, group_of.data(),
               group_bucket.data(), &ng);
   for (int g = 0; g < ng; ++g) {
-    int forced = 0;
+    int c = 0;
     for (int i = 0; i < n; ++i)
-      if (group_of[i] == g) forced = cls[i] & 1;
-    qt_status st = ensure_graph(s, bucket_index(s, group_bucket[g]), forced);
+      if (group_of[i] == g) c = cls[i];
+    qt_status st = ensure_graph(s, bucket_index(s, group_bucket[g]), (c >> 1) & 1, c & 1);
     if (st) return st;
   }
 
@@ -434,13 +479,17 @@ qt_status qt_sched_step(qt_sched* s, int32_t* n_groups) {
       a.new_index[b] = -1;
       c.slot_session[b] = -1;
     }
-    int forced = 0, slot = 0;
+    int forced = 0, sampled = 0, slot = 0;
     for (int i = 0; i < n; ++i) {
       if (group_of[i] != g) continue;
       const int id = ready[i];
       Session& q = s->sess[id];
       const int b = slot++;
-      forced = cls[i] & 1;
+      forced = (cls[i] >> 1) & 1;
+      sampled = cls[i] & 1;
+      a.slot_params[b][0] = q.params[0];
+      a.slot_params[b][1] = q.params[1];
+      a.slot_seed[b] = q.seed;
       a.slot_session[b] = id;
       a.slot_len[b] = q.length;
       a.slot_first[b] = q.frames == 0 ? (int)q.pages.size() : -1;
@@ -457,8 +506,19 @@ qt_status qt_sched_step(qt_sched* s, int32_t* n_groups) {
       c.slot_check[b] = frame >= q.min_frames ? frame : 0;
     }
     a.forced = forced ? (int32_t*)(s->dev + L.forced) : nullptr;
+    a.seen_ld = L.seen_ld;
+    a.sess_seen = (uint32_t*)(s->dev + L.sess_seen);
+    if (sampled) {
+      a.params = (qt_sampler_params*)(s->dev + L.params);
+      a.seed = (uint64_t*)(s->dev + L.seed);
+      a.seen = (uint32_t*)(s->dev + L.seen);
+    }
+    c.sampled = sampled;
+    c.seen = (const uint32_t*)(s->dev + L.seen);
+    c.sess_seen = (uint32_t*)(s->dev + L.sess_seen);
+    c.seen_ld = L.seen_ld;
     SCHED_HIP(launch_sched_setup(a, s->stream));
-    qt_status st = qt_frame_graph_launch(s->graphs[bucket_index(s, B)][forced], s->stream);
+    qt_status st = qt_frame_graph_launch(s->graphs[bucket_index(s, B)][forced][sampled], s->stream);
     if (st) return st;
     SCHED_HIP(launch_sched_collect(c, s->stream));
   }
@@ -566,7 +626,8 @@ void qt_sched_destroy(qt_sched* s) {
   if (!s) return;
   if (s->seq_issued > s->seq_done) (void)hipEventSynchronize(s->ev[s->seq_issued % kRing]);
   for (auto& row : s->graphs)
-    for (qt_graph* g : row) qt_graph_destroy(g);
+    for (auto& pair : row)
+      for (qt_graph* g : pair) qt_graph_destroy(g);
   for (hipEvent_t e : s->ev) (void)hipEventDestroy(e);
   delete s;
 }

@@ -17,6 +17,7 @@ from . import (KERNEL_KINDS, FrameInputs, FrameOutputs, KvCaches, MODES, QT_BF16
                qt_frame_graph_launch, qt_frame_launch_count, qt_frame_trace, qt_graph_destroy,
                qt_load_weights, qt_model_destroy, qt_packed_bytes, qt_sched_bytes, qt_sched_close,
                qt_sched_create, qt_sched_destroy, qt_sched_free_pages, qt_sched_length,
+               qt_sched_set_sampling,
                qt_sched_open, qt_sched_outputs, qt_sched_state, qt_sched_status_word,
                qt_sched_step, qt_sched_submit, qt_trace_create, qt_trace_destroy, qt_trace_read,
                qt_workspace_bytes)
@@ -372,6 +373,11 @@ class Scheduler:
         elif length:
             _write_pages(self.torch, self.k_pages, self.v_pages, pages, k_bits, v_bits)
         return sid
+
+    def set_sampling(self, sid: int, params=None, seed: int = 0):
+        """params: (codebook-0, predictor) (temperature, top_p, penalty, top_k) pair, or
+        None for greedy."""
+        qt_sched_set_sampling(self.handle, sid, params, seed)
 
     def submit(self, sid: int, talker_in, forced=None):
         """talker_in: device int16 [talker hidden] (bf16 bits); forced: device int32
