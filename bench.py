@@ -388,6 +388,8 @@ def main():
     ap.add_argument("--int8", action="store_true", help="INT8 weight-only decode")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-int8", action="store_true",
+                    help="skip timing the INT8 weight-only frames (C4, B=1)")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip timing the prompt prefill (1024 rows)")
     ap.add_argument("--no-scheduler", action="store_true",
@@ -432,6 +434,17 @@ def main():
                                                   "hbm_gbs_algorithmic", "hbm_frac")}
     prefill = None if args.no_prefill else run_prefill(pm, d, log)
     pm.close()
+    int8 = None
+    if not args.int8 and not args.no_int8:
+        # the INT8 weight-only frame (quantized at load from the same bf16 tensors)
+        pm8 = PackedModel(d, W, int8=True)
+        int8 = {}
+        for name in ("C4", "B1"):
+            w = dataclasses.replace(synth.WORKLOADS[name], int8=True)
+            r, _ = run_workload(pm8, w, args.steps, args.warmup, log)
+            int8[name] = {k: r[k] for k in ("codec_frames_per_s", "ms_per_frame",
+                                             "hbm_gbs_algorithmic", "hbm_frac", "bytes_per_frame")}
+        pm8.close()
     calibration_copy(log)
     cpu = None if args.no_cpu_baseline else cpu_baseline(head, W, args.cpu_seconds, log)
 
@@ -459,6 +472,7 @@ def main():
         "scheduler": main_res.get("scheduler"),
         "sampled": main_res.get("sampled"),
         "prefill": prefill,
+        "int8": int8,
         "roofline": roofline(main_res, max(1, args.trace_frames)),
         "cpu_baseline": cpu,
     }
