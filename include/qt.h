@@ -167,6 +167,19 @@ typedef struct {
                                       already emitted, or NULL (no penalty, no update) */
 } qt_sampling;
 
+/* Draw one token per row of caller-given logits with the frame's sampler (the
+ * same steps 1-5 and Philox draw as above), e.g. for logits computed elsewhere.
+ * logits: device f32 [rows][ld], entries [0, V) drawn over, V <= 4096;
+ * params: device [rows]; seed, counter: device [rows]; codebook: the Philox
+ * counter's second word; seen: device [rows][(V + 31) / 32] bit sets or NULL (the
+ * penalty applies to their entries, and each row's draw is added); tokens: device
+ * int32 [rows]; status: device uint32 [1] (QT_STATUS_BAD_SAMPLER for a row whose
+ * parameters are out of range: that row is drawn greedily).  Enqueued on `stream`. */
+qt_status qt_sample(const float* logits, int32_t rows, int32_t ld, int32_t V,
+                    const qt_sampler_params* params, const uint64_t* seed, const int32_t* counter,
+                    int32_t codebook, uint32_t* seen, int32_t* tokens, uint32_t* status,
+                    void* stream);
+
 typedef struct {
   int32_t mode;            /* qt_mode */
   const void* talker_in;   /* device bf16 [B][talker hidden]: the Talker input (FULL, TALKER) */

@@ -29,7 +29,7 @@ EXPORTED = ["qt_last_error", "qt_abi_version", "qt_validate_cfg", "qt_packed_byt
             "qt_frame_decode", "qt_frame_graph_create", "qt_frame_graph_launch",
             "qt_graph_destroy", "qt_model_destroy", "qt_trace_create", "qt_frame_launch_count",
             "qt_frame_trace", "qt_trace_read", "qt_trace_destroy",
-            "qt_prefill_workspace_bytes", "qt_prefill", "qt_prefill_graph_create",
+            "qt_prefill_workspace_bytes", "qt_prefill", "qt_prefill_graph_create", "qt_sample",
             # qt_sched.h
             "qt_sched_bytes", "qt_sched_create", "qt_sched_open", "qt_sched_submit",
             "qt_sched_step", "qt_sched_outputs", "qt_sched_state", "qt_sched_length",
@@ -176,6 +176,9 @@ def lib():
                                     C.POINTER(C.c_int32)]
         L.qt_trace_destroy.restype = None
         L.qt_trace_destroy.argtypes = [_P]
+        L.qt_sample.restype = st
+        L.qt_sample.argtypes = [_P, C.c_int32, C.c_int32, C.c_int32, _P, _P, _P, C.c_int32, _P, _P,
+                                _P, _P]
         L.qt_prefill_workspace_bytes.restype = st
         L.qt_prefill_workspace_bytes.argtypes = [C.POINTER(ModelCfg), C.c_int32, C.c_int32,
                                                  C.POINTER(C.c_uint64)]
@@ -346,6 +349,13 @@ def qt_trace_read(trace: int, max_launches: int):
 
 def qt_trace_destroy(trace: int) -> None:
     lib().qt_trace_destroy(trace)
+
+
+def qt_sample(logits_ptr: int, rows: int, ld: int, V: int, params_ptr: int, seed_ptr: int,
+              counter_ptr: int, codebook: int, seen_ptr: int | None, tokens_ptr: int,
+              status_ptr: int, stream: int = 0) -> None:
+    _check(lib().qt_sample(logits_ptr, rows, ld, V, params_ptr, seed_ptr, counter_ptr, codebook,
+                           seen_ptr, tokens_ptr, status_ptr, stream), "qt_sample")
 
 
 def qt_prefill_workspace_bytes(cfg: ModelCfg, rows: int, max_seqs: int) -> int:

@@ -1164,6 +1164,32 @@ qt_status qt_frame_graph_create(qt_model* model, const qt_sessions* sessions, co
 }
 
 
+qt_status qt_sample(const float* logits, int32_t rows, int32_t ld, int32_t V,
+                    const qt_sampler_params* params, const uint64_t* seed, const int32_t* counter,
+                    int32_t codebook, uint32_t* seen, int32_t* tokens, uint32_t* status,
+                    void* stream) {
+  if (!logits || !params || !seed || !counter || !tokens || !status)
+    return fail(QT_E_INVALID_ARG, "a qt_sample array is NULL");
+  if (rows < 1 || V < 1 || ld < V) return fail(QT_E_INVALID_ARG, "rows = %d, V = %d, ld = %d", rows, V, ld);
+  if (V > 4096) return fail(QT_E_UNSUPPORTED, "V = %d: draws cover at most 4096 entries", V);
+  if (codebook < 0) return fail(QT_E_INVALID_ARG, "codebook = %d", codebook);
+  SampleRowsArgs a{};
+  a.rows = rows;
+  a.V = V;
+  a.ld = ld;
+  a.codebook = codebook;
+  a.seen_ld = (V + 31) / 32;
+  a.logits = logits;
+  a.params = params;
+  a.seed = seed;
+  a.counter = counter;
+  a.seen = seen;
+  a.tokens = tokens;
+  a.status = status;
+  QT_LAUNCH(launch_sample_rows(a, (hipStream_t)stream));
+  return ok();
+}
+
 qt_status qt_prefill_workspace_bytes(const qt_model_cfg* cfg, int32_t rows, int32_t max_seqs,
                                      uint64_t* bytes) {
   qt_status st = check_cfg(cfg);

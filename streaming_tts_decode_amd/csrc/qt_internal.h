@@ -286,6 +286,20 @@ struct PrefillEndArgs {
   int32_t* tok0;
 };
 
+// qt_sample: one block per row.
+struct SampleRowsArgs {
+  int rows, V, codebook, seen_ld;
+  long long ld;
+  const float* logits;
+  const qt_sampler_params* params;  // [rows]
+  const uint64_t* seed;
+  const int32_t* counter;
+  uint32_t* seen;                   // [rows][seen_ld] or nullptr
+  int32_t* tokens;
+  uint32_t* status;
+};
+hipError_t launch_sample_rows(const SampleRowsArgs& a, hipStream_t s);
+
 hipError_t launch_prefill_begin(const PrefillBeginArgs& a, hipStream_t s);
 hipError_t launch_prefill_qk(const PrefillQkArgs& a, int R, float theta, hipStream_t s);
 hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t s);

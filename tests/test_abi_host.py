@@ -180,3 +180,39 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     monkeypatch.setattr(qt, "LIB_PATH", str(tmp_path / "libqt.so"))
     with pytest.raises(RuntimeError):
         qt.lib()
+
+
+def test_prefill_workspace_and_argument_errors(qt):
+    import ctypes as C
+    cfg = qt.make_cfg(synth.FULL)
+    small = qt.qt_prefill_workspace_bytes(cfg, 64, 1)
+    big = qt.qt_prefill_workspace_bytes(cfg, 1024, 4)
+    assert small > 0 and big > 8 * small
+    assert qt.qt_prefill_workspace_bytes(cfg, 1024, 32) > big
+    # rows: multiples of 16, of 64 above 64, at most QT_PREFILL_MAX_ROWS
+    for rows in (0, 8, 40, 80, 4096 + 64):
+        with pytest.raises(qt.QtError) as e:
+            qt.qt_prefill_workspace_bytes(cfg, rows, 1)
+        assert e.value.status == 2, rows
+    for seqs in (0, 33):
+        with pytest.raises(qt.QtError) as e:
+            qt.qt_prefill_workspace_bytes(cfg, 64, seqs)
+        assert e.value.status == 1
+    L = qt.lib()
+    args = qt.PrefillArgs(64, 1, None, None, None, 4, None, None, None, None, None)
+    kv = qt.KvCaches(None, None, 4)
+    assert L.qt_prefill(None, C.byref(args), C.byref(kv), None, 0, None) == 1
+    g = C.c_void_p()
+    assert L.qt_prefill_graph_create(None, C.byref(args), C.byref(kv), None, 0, C.byref(g)) == 1
+    assert g.value is None
+
+
+def test_sampling_descriptor_layout(qt):
+    """The ctypes mirror of qt_sampler_params / qt_sampling / qt_frame_inputs matches
+    the C layout the header declares (16-byte parameters, four pointers, the
+    sampling pointer last in the inputs)."""
+    import ctypes as C
+    assert C.sizeof(qt.SamplerParams) == 16
+    assert C.sizeof(qt.Sampling) == 32
+    assert qt.FrameInputs.sampling.offset == 40 and C.sizeof(qt.FrameInputs) == 48
+    assert C.sizeof(qt.PrefillArgs) == 80

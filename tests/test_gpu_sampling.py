@@ -262,3 +262,124 @@ def test_sampled_graph_replays_match_eager(small_pm):
     for f in range(frames):
         np.testing.assert_array_equal(res[0][f][0], res[1][f][0])
         np.testing.assert_array_equal(res[0][f][1], res[1][f][1])
+
+
+def _sample_rows(torch, logits, params, seeds, counters, codebook=0, seen=None):
+    """qt_sample on host arrays; returns (tokens, seen after, status)."""
+    import streaming_tts_decode_amd as qt
+    R, V = logits.shape
+    dev = torch.device("cuda")
+    lg = torch.from_numpy(np.ascontiguousarray(logits, dtype=np.float32)).to(dev)
+    rec = np.zeros(R, dtype=[("t", "<f4"), ("p", "<f4"), ("r", "<f4"), ("k", "<i4")])
+    for i, (t, p, r, k) in enumerate(params):
+        rec[i] = (t, p, r, k)
+    pr = torch.from_numpy(rec.view(np.int32).reshape(R, 4).copy()).to(dev)
+    sd = torch.from_numpy(np.asarray(seeds, dtype=np.uint64).view(np.int64)).to(dev)
+    ct = torch.from_numpy(np.asarray(counters, dtype=np.int32)).to(dev)
+    words = (V + 31) // 32
+    sn = None
+    if seen is not None:
+        packed = np.zeros((R, words * 32), dtype=bool)
+        packed[:, :V] = seen
+        sn = torch.from_numpy(np.packbits(packed, axis=1, bitorder="little").view(np.int32).copy()).to(dev)
+    tok = torch.zeros(R, dtype=torch.int32, device=dev)
+    st = torch.zeros(1, dtype=torch.int32, device=dev)
+    qt.qt_sample(lg.data_ptr(), R, V, V, pr.data_ptr(), sd.data_ptr(), ct.data_ptr(), codebook,
+                 sn.data_ptr() if sn is not None else None, tok.data_ptr(), st.data_ptr(),
+                 torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    after = None
+    if sn is not None:
+        after = np.unpackbits(sn.cpu().numpy().view(np.uint8), axis=1, bitorder="little")[:, :V].astype(bool)
+    return tok.cpu().numpy(), after, int(st.item())
+
+
+def _check_rows(logits, toks, params, seeds, counters, codebook, seen, label):
+    stats = {"n": 0, "exact": 0, "tied": 0}
+    for r in range(logits.shape[0]):
+        u = sampler.uniform(seeds[r], int(counters[r]), codebook)
+        _check_draw(logits[r], int(toks[r]), u, params[r], None if seen is None else seen[r],
+                    f"{label} row {r}", stats)
+    return stats
+
+
+def test_sampler_rows_edge_cases(gpu):
+    """Rows chosen to take both selection paths: random rows (the threshold path),
+    all-equal rows (zero spread), rows of three distinct values (massive ties at the
+    k-th value, more than 128 candidates above every threshold), NaN and -inf
+    entries, rows shorter than top_k, a huge-scale row, the longest row (4096)."""
+    import torch
+    rng = np.random.default_rng(21)
+    cases = []
+    V = 2048
+    cases.append(("normal", rng.normal(scale=1.5, size=(24, V)).astype(np.float32)))
+    cases.append(("equal", np.full((6, V), 0.37, dtype=np.float32)))
+    cases.append(("three values", rng.integers(0, 3, size=(8, V)).astype(np.float32)))
+    x = rng.normal(size=(6, V)).astype(np.float32)
+    x[:, ::7] = np.nan
+    x[:, 3::11] = -np.inf
+    cases.append(("nan and -inf", x))
+    cases.append(("huge scale", (rng.normal(size=(4, V)) * 1e4).astype(np.float32)))
+    cases.append(("short rows", rng.normal(size=(6, 40)).astype(np.float32)))
+    cases.append(("longest rows", rng.normal(size=(4, 4096)).astype(np.float32)))
+    total = {"n": 0, "exact": 0, "tied": 0}
+    for label, lg in cases:
+        R = lg.shape[0]
+        params = [(float(rng.choice([0.5, 1.0, 1.7])), float(rng.choice([1.0, 0.9, 0.5])), 1.0,
+                   int(rng.choice([1, 7, 50, 64]))) for _ in range(R)]
+        seeds = [int(s) for s in rng.integers(0, 2 ** 62, size=R)]
+        counters = rng.integers(0, 10000, size=R).astype(np.int32)
+        toks, _, status = _sample_rows(torch, lg, params, seeds, counters, codebook=3)
+        assert status == 0, label
+        st = _check_rows(lg, toks, params, seeds, counters, 3, None, label)
+        for k in total:
+            total[k] += st[k]
+    log(f"[sampling] edge-case rows {total}")
+    assert total["exact"] >= total["n"] - 2
+
+
+def test_sampler_rows_many_draws_and_penalty(gpu):
+    """One row drawn under 2000 counters matches the oracle draw by draw (so its
+    frequencies are the oracle's distribution); a repetition penalty over a seen set
+    changes the draws as the oracle's does, and each row's draw joins its set."""
+    import torch
+    rng = np.random.default_rng(5)
+    V = 256
+    row = rng.normal(scale=2.0, size=V).astype(np.float32)
+    n = 2000
+    lg = np.tile(row, (n, 1))
+    params = [(0.8, 0.9, 1.0, 20)] * n
+    seeds = [77] * n
+    counters = np.arange(n, dtype=np.int32)
+    toks, _, status = _sample_rows(torch, lg, params, seeds, counters)
+    assert status == 0
+    st = _check_rows(lg, toks, params, seeds, counters, 0, None, "draws")
+    assert st["exact"] >= n - 2
+    p = sampler.distribution(row, temperature=0.8, top_k=20, top_p=0.9)
+    freq = np.bincount(toks, minlength=V) / n
+    assert np.abs(freq - p).max() < 0.05
+    # penalty over a seen set that holds the most probable entries
+    seen = np.zeros((n, V), dtype=bool)
+    seen[:, np.argsort(-row)[:5]] = True
+    params = [(0.8, 1.0, 3.0, 20)] * n
+    toks2, after, status = _sample_rows(torch, lg, params, seeds, counters, seen=seen)
+    assert status == 0
+    st = _check_rows(lg, toks2, params, seeds, counters, 0, seen, "penalty")
+    assert st["exact"] >= n - 2
+    assert np.mean(toks2 != toks) > 0.2
+    want = seen.copy()
+    want[np.arange(n), toks2] = True
+    np.testing.assert_array_equal(after, want)
+
+
+def test_sampler_rows_bad_parameters(gpu):
+    import torch
+    from streaming_tts_decode_amd import STATUS_BAD_SAMPLER
+    rng = np.random.default_rng(8)
+    lg = rng.normal(size=(3, 512)).astype(np.float32)
+    lg[2, 100] = lg[2, 200] = lg[2].max() + 1.0  # tie: the lower index wins
+    params = [(0.0, 1.0, 1.0, 5), (1.0, 1.0, 1.0, 65), (1.0, 0.0, 1.0, 5)]
+    toks, _, status = _sample_rows(torch, lg, params, [1, 2, 3], [0, 0, 0])
+    assert status == STATUS_BAD_SAMPLER
+    np.testing.assert_array_equal(toks, np.argmax(lg, axis=1))
+    assert toks[2] == 100
