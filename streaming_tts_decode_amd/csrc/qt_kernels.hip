@@ -508,249 +508,129 @@ __device__ __forceinline__ float key_value(uint32_t k) {
 }
 
 constexpr int kSampleSlots = 16;  // row entries per thread: rows up to 4096 entries
-constexpr int kFastCands = 128;   // candidates the threshold path sorts (one wave, 2 per lane)
-constexpr int kThresholds = 16;
-
-// threshold j of the fast path: max - spread * 2^(j/2 - 6) (literal, so that the
-// counting and the gathering compute the same floats)
-__constant__ float kThrMult[kThresholds] = {0.015625f, 0.02209708691207961f, 0.03125f, 0.04419417382415922f, 0.0625f, 0.08838834764831845f, 0.125f, 0.1767766952966369f, 0.25f, 0.3535533905932738f, 0.5f, 0.7071067811865476f, 1.0f, 1.4142135623730951f, 2.0f, 2.8284271247461903f};
 
 struct SampleSmem {
   uint32_t hist[256];
-  float cval[kFastCands];
-  int cidx[kFastCands];
+  float cval[QT_SAMPLER_MAX_TOP_K];
+  int cidx[QT_SAMPLER_MAX_TOP_K];
   int eq[kSampleSlots][4];
-  float red[4][2];
-  int cnt[4][kThresholds];
   uint32_t digit;
   int above;
   int n_cand;
   int token;
 };
 
-__device__ __forceinline__ bool cand_greater(float v, int i, float ov, int oi) {
-  return v > ov || (v == ov && i < oi);
-}
-
 // One draw over row[0, V) by the 256 threads of a block (every thread returns the
-// token).  1. penalty and temperature; 2. the top_k largest scores, ties to the
-// lower index, in order: usually by a threshold found from the row's maximum and
-// mean (16 candidate thresholds counted with ballots; the first that keeps between
-// top_k and 128 entries is taken, its entries sorted by one wave), otherwise by a
-// 4-pass radix select over order keys (8 bits per pass, entries equal to the
-// k-th ranked by index) and a one-wave sort; 3. weights, running sums (wave
-// scan), the top-p cut and the draw.  Both ways give the same candidates.
+// token).  1. penalty and temperature; 2. the top_k-th largest score by a 4-pass
+// radix select over order keys (8 bits per pass), entries equal to it ranked by
+// index; 3. the candidates sorted by one wave (bitonic, (score desc, index asc));
+// 4. weights, running sums (wave scan), the top-p cut and the draw.
 __device__ int sample_row(const float* row, int V, float temperature, float top_p,
                           float penalty, int top_k, const uint32_t* seen, float u,
                           SampleSmem& sm) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ne = (V + 255) >> 8;
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   uint32_t key[kSampleSlots];
-  float zv[kSampleSlots];
-  float zmax = -INFINITY, zsum = 0.f;
 #pragma unroll
   for (int e = 0; e < kSampleSlots; ++e) {
     const int i = tid + 256 * e;
     key[e] = 0u;  // below every score: entries past V and NaN scores
-    zv[e] = -INFINITY;
     if (e < ne && i < V) {
       float x = row[i];
       if (seen && ((seen[i >> 5] >> (i & 31)) & 1u)) x = x > 0.f ? x / penalty : x * penalty;
       const float z = x / temperature;
-      if (z == z) {
-        key[e] = order_key(z);
-        zv[e] = z;
-        zmax = fmaxf(zmax, z);
-        zsum += z;  // (an infinite score only makes the threshold path fall back)
-      }
+      if (z == z) key[e] = order_key(z);
     }
   }
   const int k = top_k < V ? top_k : V;
-  zmax = wave_max(zmax);
-  zsum = wave_sum(zsum);
-  if (lane == 0) {
-    sm.red[wave][0] = zmax;
-    sm.red[wave][1] = zsum;
-  }
+  uint32_t prefix = 0, pmask = 0;
+  int kr = k;
   if (tid == 0) sm.n_cand = 0;
-  __syncthreads();
-  const float M = fmaxf(fmaxf(sm.red[0][0], sm.red[1][0]), fmaxf(sm.red[2][0], sm.red[3][0]));
-  const float mean = (sm.red[0][1] + sm.red[1][1] + sm.red[2][1] + sm.red[3][1]) / (float)V;
-  const float spread = M - mean;
-  // thresholds M - spread * 2^(j/2 - 6), j = 0..15
-  bool fast = M > -INFINITY && M < INFINITY && spread > 0.f && spread < INFINITY;
-  if (fast) {
+#pragma unroll 1
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    sm.hist[tid] = 0u;
+    __syncthreads();
 #pragma unroll
-    for (int j = 0; j < kThresholds; ++j) {
-      const float thr = fmaf(-spread, kThrMult[j], M);
-      int c = 0;
+    for (int e = 0; e < kSampleSlots; ++e)
+      if (e < ne && (key[e] & pmask) == prefix) atomicAdd(&sm.hist[(key[e] >> shift) & 255u], 1u);
+    __syncthreads();
+    if (wave == 0) {
+      // lane l owns bins 4l..4l+3; "above" counts the keys in higher bins
+      const uint32_t h0 = sm.hist[4 * lane], h1 = sm.hist[4 * lane + 1];
+      const uint32_t h2 = sm.hist[4 * lane + 2], h3 = sm.hist[4 * lane + 3];
+      const uint32_t own = h0 + h1 + h2 + h3;
+      uint32_t suf = own;
 #pragma unroll
-      for (int e = 0; e < kSampleSlots; ++e)
-        if (e < ne) c += __popcll(__ballot(zv[e] >= thr));
-      if (lane == 0) sm.cnt[wave][j] = c;
-    }
-  }
-  __syncthreads();
-  float thr = 0.f;
-  if (fast) {
-    int jstar = -1, cstar = 0;
-    for (int j = 0; j < kThresholds && jstar < 0; ++j) {
-      const int c = sm.cnt[0][j] + sm.cnt[1][j] + sm.cnt[2][j] + sm.cnt[3][j];
-      if (c >= k) {
-        jstar = j;
-        cstar = c;
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t t = __shfl_down(suf, off);
+        if (lane + off < 64) suf += t;
+      }
+      uint32_t above = suf - own;
+      const uint32_t hs[4] = {h3, h2, h1, h0};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (above < (uint32_t)kr && (uint32_t)kr <= above + hs[q]) {
+          sm.digit = 4 * lane + 3 - q;
+          sm.above = (int)above;
+        }
+        above += hs[q];
       }
     }
-    fast = jstar >= 0 && cstar <= kFastCands;
-    if (fast) thr = fmaf(-spread, kThrMult[jstar], M);
+    __syncthreads();
+    prefix |= sm.digit << shift;
+    pmask |= 255u << shift;
+    kr -= sm.above;
   }
-  float v0 = -INFINITY;  // wave 0, lane l: the l-th candidate in order (l < k)
-  int i0 = 0x7fffffff;
-  if (fast) {
+  // candidates: every key above the threshold, and the kr lowest-index keys equal to it
+  int rank_base = 0;
+  {
+    uint64_t masks[kSampleSlots];
+#pragma unroll
+    for (int e = 0; e < kSampleSlots; ++e) {
+      masks[e] = __ballot(e < ne && key[e] == prefix);
+      if (lane == 0 && e < ne) sm.eq[e][wave] = __popcll(masks[e]);
+    }
+    __syncthreads();
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
     for (int e = 0; e < kSampleSlots; ++e) {
       if (e < ne) {
-        const bool take = zv[e] >= thr;
-        const uint64_t mask = __ballot(take);
-        int base = 0;
-        if (lane == 0 && mask) base = atomicAdd(&sm.n_cand, __popcll(mask));
-        base = __shfl(base, 0);
-        const int pos = base + __popcll(mask & below);
-        if (take && pos < kFastCands) {
-          sm.cval[pos] = zv[e];
-          sm.cidx[pos] = tid + 256 * e;
+        const int i = tid + 256 * e;
+        bool take = key[e] > prefix;
+        if (key[e] == prefix) {
+          int rank = rank_base + __popcll(masks[e] & below);
+          for (int w = 0; w < wave; ++w) rank += sm.eq[e][w];
+          take = rank < kr;
         }
-      }
-    }
-    __syncthreads();
-    if (wave == 0) {
-      const int c = sm.n_cand < kFastCands ? sm.n_cand : kFastCands;
-      float a0 = lane < c ? sm.cval[lane] : -INFINITY, a1 = lane + 64 < c ? sm.cval[lane + 64] : -INFINITY;
-      int b0 = lane < c ? sm.cidx[lane] : 0x7fffffff, b1 = lane + 64 < c ? sm.cidx[lane + 64] : 0x7fffffff;
-      // bitonic sort of 128 entries, entry n = 64 s + lane in slot s, descending
-#pragma unroll
-      for (int size = 2; size <= 128; size <<= 1) {
-#pragma unroll
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-          if (stride == 64) {
-            if (!cand_greater(a0, b0, a1, b1)) {
-              const float t = a0; a0 = a1; a1 = t;
-              const int ti = b0; b0 = b1; b1 = ti;
-            }
-          } else {
-            const bool lower = (lane & stride) == 0;
-            {
-              const float ov = __shfl_xor(a0, stride);
-              const int oi = __shfl_xor(b0, stride);
-              const bool desc = (lane & size) == 0;  // entry n = lane
-              if (cand_greater(a0, b0, ov, oi) != (lower == desc)) { a0 = ov; b0 = oi; }
-            }
-            {
-              const float ov = __shfl_xor(a1, stride);
-              const int oi = __shfl_xor(b1, stride);
-              const bool desc = ((64 + lane) & size) == 0;  // entry n = 64 + lane
-              if (cand_greater(a1, b1, ov, oi) != (lower == desc)) { a1 = ov; b1 = oi; }
-            }
-          }
+        if (take) {
+          const int slot = atomicAdd(&sm.n_cand, 1);
+          sm.cval[slot] = key[e] ? key_value(key[e]) : -INFINITY;
+          sm.cidx[slot] = i;
         }
+        rank_base += sm.eq[e][0] + sm.eq[e][1] + sm.eq[e][2] + sm.eq[e][3];
       }
-      v0 = a0;
-      i0 = b0;
-    }
-  } else {
-    uint32_t prefix = 0, pmask = 0;
-    int kr = k;
-#pragma unroll 1
-    for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
-      sm.hist[tid] = 0u;
-      __syncthreads();
-#pragma unroll
-      for (int e = 0; e < kSampleSlots; ++e)
-        if (e < ne && (key[e] & pmask) == prefix) atomicAdd(&sm.hist[(key[e] >> shift) & 255u], 1u);
-      __syncthreads();
-      if (wave == 0) {
-        // lane l owns bins 4l..4l+3; "above" counts the keys in higher bins
-        const uint32_t h0 = sm.hist[4 * lane], h1 = sm.hist[4 * lane + 1];
-        const uint32_t h2 = sm.hist[4 * lane + 2], h3 = sm.hist[4 * lane + 3];
-        const uint32_t own = h0 + h1 + h2 + h3;
-        uint32_t suf = own;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const uint32_t t = __shfl_down(suf, off);
-          if (lane + off < 64) suf += t;
-        }
-        uint32_t above = suf - own;
-        const uint32_t hs[4] = {h3, h2, h1, h0};
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-          if (above < (uint32_t)kr && (uint32_t)kr <= above + hs[qq]) {
-            sm.digit = 4 * lane + 3 - qq;
-            sm.above = (int)above;
-          }
-          above += hs[qq];
-        }
-      }
-      __syncthreads();
-      prefix |= sm.digit << shift;
-      pmask |= 255u << shift;
-      kr -= sm.above;
-    }
-    // candidates: every key above the threshold, and the kr lowest-index keys equal to it
-    int rank_base = 0;
-    {
-      uint64_t masks[kSampleSlots];
-#pragma unroll
-      for (int e = 0; e < kSampleSlots; ++e) {
-        masks[e] = __ballot(e < ne && key[e] == prefix);
-        if (lane == 0 && e < ne) sm.eq[e][wave] = __popcll(masks[e]);
-      }
-      __syncthreads();
-#pragma unroll
-      for (int e = 0; e < kSampleSlots; ++e) {
-        if (e < ne) {
-          const int i = tid + 256 * e;
-          bool take = key[e] > prefix;
-          if (key[e] == prefix) {
-            int rank = rank_base + __popcll(masks[e] & below);
-            for (int w = 0; w < wave; ++w) rank += sm.eq[e][w];
-            take = rank < kr;
-          }
-          if (take) {
-            const int slot = atomicAdd(&sm.n_cand, 1);
-            sm.cval[slot] = key[e] ? key_value(key[e]) : -INFINITY;
-            sm.cidx[slot] = i;
-          }
-          rank_base += sm.eq[e][0] + sm.eq[e][1] + sm.eq[e][2] + sm.eq[e][3];
-        }
-      }
-    }
-    __syncthreads();
-    if (wave == 0) {
-      float v = lane < k ? sm.cval[lane] : -INFINITY;
-      int idx = lane < k ? sm.cidx[lane] : 0x7fffffff;
-#pragma unroll
-      for (int size = 2; size <= 64; size <<= 1) {
-#pragma unroll
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-          const float ov = __shfl_xor(v, stride);
-          const int oi = __shfl_xor(idx, stride);
-          const bool desc = (lane & size) == 0 || size == 64;
-          const bool lower = (lane & stride) == 0;
-          if (cand_greater(v, idx, ov, oi) != (lower == desc)) {
-            v = ov;
-            idx = oi;
-          }
-        }
-      }
-      v0 = v;
-      i0 = idx;
     }
   }
+  __syncthreads();
   if (wave == 0) {
-    const float v = v0;
-    const int idx = i0;
+    float v = lane < k ? sm.cval[lane] : -INFINITY;
+    int idx = lane < k ? sm.cidx[lane] : 0x7fffffff;
+#pragma unroll
+    for (int size = 2; size <= 64; size <<= 1) {
+#pragma unroll
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        const float ov = __shfl_xor(v, stride);
+        const int oi = __shfl_xor(idx, stride);
+        const bool desc = (lane & size) == 0 || size == 64;
+        const bool lower = (lane & stride) == 0;
+        const bool greater = v > ov || (v == ov && idx < oi);
+        if (greater != (lower == desc)) {
+          v = ov;
+          idx = oi;
+        }
+      }
+    }
     const float vmax = __shfl(v, 0);
     float w = 0.f;
     if (lane < k) w = vmax == -INFINITY ? (lane == 0 ? 1.f : 0.f) : expf(v - vmax);

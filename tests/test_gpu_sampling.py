@@ -304,10 +304,10 @@ def _check_rows(logits, toks, params, seeds, counters, codebook, seen, label):
 
 
 def test_sampler_rows_edge_cases(gpu):
-    """Rows chosen to take both selection paths: random rows (the threshold path),
-    all-equal rows (zero spread), rows of three distinct values (massive ties at the
-    k-th value, more than 128 candidates above every threshold), NaN and -inf
-    entries, rows shorter than top_k, a huge-scale row, the longest row (4096)."""
+    """Rows that stress the top-k selection: random rows, all-equal rows (every entry
+    ties with the k-th), rows of three distinct values (massive ties at the k-th
+    value, ranked by index), NaN and -inf entries, rows shorter than top_k, a
+    huge-scale row, the longest row (4096)."""
     import torch
     rng = np.random.default_rng(21)
     cases = []
