@@ -53,9 +53,11 @@ def pmc_traffic(workload: str, kernel: str):
     return e["bytes_per_launch"]
 
 
-def weight_bytes(d, int8: bool) -> int:
+def weight_bytes(d, int8: bool, distinct: bool = False) -> int:
     """Logical weight bytes one frame streams: every decode GEMM weight once per
-    use for the whole batch (predictor layers once per predictor step)."""
+    use for the whole batch (predictor layers once per predictor step).  With
+    distinct=True, every matrix once per frame: the predictor's layers, which all
+    15 steps share, are counted once (the stricter lower bound)."""
     def mat(n, k):
         return n * k + 4 * n if int8 else 2 * n * k
 
@@ -65,11 +67,12 @@ def weight_bytes(d, int8: bool) -> int:
                 + 2 * (2 * x.hidden + 2 * x.head_dim))
     t, p = d.talker, d.predictor
     talker = t.layers * layer(t) + mat(d.talker_vocab + p.hidden, t.hidden) + 2 * t.hidden
-    pred_step = p.layers * layer(p) + mat(d.code_vocab, p.hidden) + 2 * p.hidden
-    return talker + d.n_steps * pred_step
+    pred_layers = p.layers * layer(p)
+    pred_own = mat(d.code_vocab, p.hidden) + 2 * p.hidden  # each step's head and final gain
+    return talker + (1 if distinct else d.n_steps) * pred_layers + d.n_steps * pred_own
 
 
-def frame_bytes(d, lengths, int8: bool) -> int:
+def frame_bytes(d, lengths, int8: bool, distinct: bool = False) -> int:
     """Algorithmic bytes of one frame: weights (above) plus, per session, the
     Talker K/V read over positions 0..L (L = cached length before the frame), the
     appended K/V, the embedding rows, the input and the fp32 logits and tokens."""
@@ -80,7 +83,7 @@ def frame_bytes(d, lengths, int8: bool) -> int:
         per_sess += kv_pos * (int(L) + 1) + kv_pos
         per_sess += d.n_steps * d.predictor.hidden * 2 + t.hidden * 2
         per_sess += 4 * (d.talker_vocab + d.n_steps * d.code_vocab) + 4 * d.n_codebooks
-    return weight_bytes(d, int8) + per_sess
+    return weight_bytes(d, int8, distinct) + per_sess
 
 
 def launch_bytes(d, kind, li, lengths, int8: bool) -> int:
@@ -272,6 +275,7 @@ def run_workload(pm, w, steps, warmup, log, n_trace=0, sched=False):
     if status:
         raise RuntimeError(f"{w.name}: device status {status:#x}")
     nbytes = sum(frame_bytes(w.dims, lengths + f, pm.int8) for f in range(steps))
+    nbytes_distinct = sum(frame_bytes(w.dims, lengths + f, pm.int8, distinct=True) for f in range(steps))
     per, traced_ms = (trace_frames(dec, w.dims, lengths + steps, n_trace, pm.int8, log)
                       if n_trace else (None, None))
     sampled = None
@@ -307,6 +311,8 @@ def run_workload(pm, w, steps, warmup, log, n_trace=0, sched=False):
         "kernels": per, "traced_ms_per_frame": traced_ms, "sampled": sampled,
     }
     res["hbm_frac"] = res["hbm_gbs_algorithmic"] / HBM_PEAK_GBS
+    # the stricter figure: each matrix once per frame (the shared predictor layers once)
+    res["hbm_frac_distinct"] = nbytes_distinct / (ms / 1e3) / 1e9 / HBM_PEAK_GBS
     log(f"[bench] { {k: v for k, v in res.items() if k != 'kernels'} }")
     dec.close()
     if sched:
@@ -431,7 +437,7 @@ def main():
         w = dataclasses.replace(synth.WORKLOADS[name], int8=head.int8)
         r, _ = run_workload(pm, w, args.steps, args.warmup, log)
         extra[f"B{w.batch}"] = {k: r[k] for k in ("codec_frames_per_s", "ms_per_frame",
-                                                  "hbm_gbs_algorithmic", "hbm_frac")}
+                                                  "hbm_gbs_algorithmic", "hbm_frac", "hbm_frac_distinct")}
     prefill = None if args.no_prefill else run_prefill(pm, d, log)
     pm.close()
     int8 = None
@@ -443,7 +449,8 @@ def main():
             w = dataclasses.replace(synth.WORKLOADS[name], int8=True)
             r, _ = run_workload(pm8, w, args.steps, args.warmup, log)
             int8[name] = {k: r[k] for k in ("codec_frames_per_s", "ms_per_frame",
-                                             "hbm_gbs_algorithmic", "hbm_frac", "bytes_per_frame")}
+                                             "hbm_gbs_algorithmic", "hbm_frac", "hbm_frac_distinct",
+                                             "bytes_per_frame")}
         pm8.close()
     calibration_copy(log)
     cpu = None if args.no_cpu_baseline else cpu_baseline(head, W, args.cpu_seconds, log)
@@ -467,6 +474,7 @@ def main():
                    "parallelism": "single GPU"},
         "frame_hbm_gbs": main_res["hbm_gbs_algorithmic"],
         "frame_hbm_frac": main_res["hbm_frac"],
+        "frame_hbm_frac_distinct": main_res["hbm_frac_distinct"],
         "bytes_per_frame": main_res["bytes_per_frame"],
         "other_batches": extra,
         "scheduler": main_res.get("scheduler"),
