@@ -154,3 +154,17 @@ def test_prefill_full_model_int8(full_pm_i8, orc_full_i8):
     dec, _, _ = _run(full_pm_i8, orc_full_i8, synth.FULL, [33], rows=64, max_pages=4, tag="pfi8",
                      frames_after=1)
     dec.close()
+
+
+def test_prefill_largest_call(small_pm, orc_small):
+    # QT_PREFILL_MAX_SEQS sequences filling QT_PREFILL_MAX_ROWS rows exactly: ragged
+    # lengths, one empty sequence, one single-token sequence, and a decode frame after
+    from streaming_tts_decode_amd import PREFILL_MAX_ROWS, PREFILL_MAX_SEQS
+    rng = np.random.default_rng(32)
+    lengths = [int(x) for x in rng.integers(16, 224, size=PREFILL_MAX_SEQS - 1)]
+    lengths[5], lengths[17] = 0, 1
+    lengths.append(PREFILL_MAX_ROWS - sum(lengths))
+    assert 1 <= lengths[-1] < 32 * 16 and sum(lengths) == PREFILL_MAX_ROWS
+    dec, _, _ = _run(small_pm, orc_small, synth.SMALL, lengths, rows=PREFILL_MAX_ROWS, max_pages=32,
+                     tag="pfmax", frames_after=1)
+    dec.close()
