@@ -239,7 +239,7 @@ def run_prefill(pm, d, log, rows=1024, packings=((1024,), (256, 256, 256, 256)),
     return out
 
 
-def run_workload(pm, w, steps, warmup, log, n_trace=0, sched=False):
+def run_workload(pm, w, steps, warmup, log, n_trace=0, extras=False):
     import numpy as np
     import torch
 
@@ -278,8 +278,26 @@ def run_workload(pm, w, steps, warmup, log, n_trace=0, sched=False):
     nbytes_distinct = sum(frame_bytes(w.dims, lengths + f, pm.int8, distinct=True) for f in range(steps))
     per, traced_ms = (trace_frames(dec, w.dims, lengths + steps, n_trace, pm.int8, log)
                       if n_trace else (None, None))
+    # repeated sequences (outside the timed region above): the workload's own frame
+    # count from the same starting lengths, each timed alone; min and median
+    seq_ms = []
+    for rep in range(5 if extras else 0):
+        dec.kv_len.copy_(L0)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for f in range(w.frames):
+            dec.talker_in.copy_(talker_all[f % w.frames], non_blocking=True)
+            dec.replay(g)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        seq_ms.append(ev0.elapsed_time(ev1) / w.frames)
+    if int(dec.status.item()):
+        raise RuntimeError(f"{w.name} sequences: device status {int(dec.status.item()):#x}")
+    sequences = ({"reps": len(seq_ms), "frames": w.frames, "min_ms_per_frame": min(seq_ms),
+                  "median_ms_per_frame": float(np.median(seq_ms)),
+                  "max_codec_frames_per_s": w.batch / (min(seq_ms) / 1e3)} if seq_ms else None)
     sampled = None
-    if sched:
+    if extras:
         # the same frames drawing every codebook (qt_sampling) instead of the argmax
         dec.set_sampling((0.9, 1.0, 1.05, 50), (0.9, 1.0, 1.0, 50), list(range(1, w.batch + 1)))
         gs = dec.capture("full", forced=False, sampling=True)
@@ -308,14 +326,14 @@ def run_workload(pm, w, steps, warmup, log, n_trace=0, sched=False):
         "ms_per_frame": ms / steps, "codec_frames_per_s": w.batch * steps / (ms / 1e3),
         "hbm_gbs_algorithmic": nbytes / (ms / 1e3) / 1e9,
         "bytes_per_frame": nbytes / steps, "wall_s": wall,
-        "kernels": per, "traced_ms_per_frame": traced_ms, "sampled": sampled,
+        "kernels": per, "traced_ms_per_frame": traced_ms, "sampled": sampled, "sequences": sequences,
     }
     res["hbm_frac"] = res["hbm_gbs_algorithmic"] / HBM_PEAK_GBS
     # the stricter figure: each matrix once per frame (the shared predictor layers once)
     res["hbm_frac_distinct"] = nbytes_distinct / (ms / 1e3) / 1e9 / HBM_PEAK_GBS
     log(f"[bench] { {k: v for k, v in res.items() if k != 'kernels'} }")
     dec.close()
-    if sched:
+    if extras:
         s = run_scheduler(pm, w, dec, lengths, steps, warmup, log)
         s["vs_graph"] = s["codec_frames_per_s"] / res["codec_frames_per_s"]
         res["scheduler"] = s
@@ -399,7 +417,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip timing the prompt prefill (1024 rows)")
     ap.add_argument("--no-scheduler", action="store_true",
-                    help="skip timing the headline workload through the lockstep scheduler")
+                    help="skip the headline workload's extra timings: through the lockstep "
+                         "scheduler, with every codebook drawn, and as repeated sequences")
     ap.add_argument("--trace-frames", type=int, default=5,
                     help="eager frames timed launch by launch for the roofline")
     args = ap.parse_args()
@@ -431,7 +450,7 @@ def main():
     pm = PackedModel(d, W, int8=head.int8)
     main_res, lengths = run_workload(pm, head, args.steps, args.warmup, log,
                                      n_trace=max(1, args.trace_frames),
-                                     sched=not args.no_scheduler)
+                                     extras=not args.no_scheduler)
     extra = {}
     for name in [x for x in args.also.split(",") if x]:
         w = dataclasses.replace(synth.WORKLOADS[name], int8=head.int8)
@@ -479,6 +498,7 @@ def main():
         "other_batches": extra,
         "scheduler": main_res.get("scheduler"),
         "sampled": main_res.get("sampled"),
+        "sequences": main_res.get("sequences"),
         "prefill": prefill,
         "int8": int8,
         "roofline": roofline(main_res, max(1, args.trace_frames)),
