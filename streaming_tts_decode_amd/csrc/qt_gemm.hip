@@ -535,6 +535,8 @@ __global__ __launch_bounds__(256) void k_gemm_rows(GemmArgs a) {
   }
 }
 
+constexpr int kPipeKU = 2;  // K steps of 32 per stage of the copy-pipelined form
+
 // 16-byte LDS read at a byte offset, hidden from the compiler's wait insertion
 // (which would otherwise wait for every copy in flight before any LDS read); the
 // caller waits with lds_wait before using the values.
@@ -545,22 +547,24 @@ __device__ __forceinline__ u32x4 lds_read16(uint32_t off) {
   return v;
 }
 
-// Pipelined form for half weights: the block's operands for one 32-wide K step
-// (its 2 TN weight tiles in lane order, its activation rows of the step's 4
-// chunks) are copied global -> LDS by the load unit itself (global_load_lds,
-// 16 bytes per lane at the wave's LDS base + 16 x lane), NS steps in flight.
-// Before a step is used, each wave waits until at most the younger steps' copies
-// are outstanding, and one barrier both publishes the step and frees the buffer
-// the next copies overwrite.  Activation rows past M are copied from row M - 1
-// (their products are never stored).
-template <int TN, int TM, int NS>
+// Pipelined form for half weights: the block's operands for a stage of KU
+// 32-wide K steps (per step its 2 TN weight tiles in lane order and its
+// activation rows of the step's 4 chunks) are copied global -> LDS by the load
+// unit itself (global_load_lds, 16 bytes per lane at the wave's LDS base +
+// 16 x lane), NS stages in flight.  Before a stage is used, each wave waits until
+// at most the younger stages' copies are outstanding, and one barrier both
+// publishes the stage and frees the buffer the next copies overwrite; all of the
+// stage's operand reads are issued before one wait.  Activation rows past M are
+// copied from row M - 1 (their products are never stored).
+template <int TN, int TM, int NS, int KU>
 __global__ __launch_bounds__(256) void k_gemm_rows_pipe(GemmArgs a) {
   constexpr int BM = 32 * TM;
-  constexpr int WT = 2 * TN;                   // weight tiles per step
-  constexpr int AP = 4 * (BM / 64);            // 64-row activation pieces per step
-  constexpr int PER = (WT + AP) / 4;           // copies per wave per step
-  constexpr int STAGE = WT * 64 + 4 * BM;      // uint4 per step
-  static_assert((WT + AP) % 4 == 0, "copies must divide over the four waves");
+  constexpr int WT = 2 * TN;                   // weight tiles per K step
+  constexpr int AP = 4 * (BM / 64);            // 64-row activation pieces per K step
+  constexpr int PER = KU * (WT + AP) / 4;      // copies per wave per stage
+  constexpr int STEP = WT * 64 + 4 * BM;       // uint4 per K step
+  constexpr int STAGE = KU * STEP;             // uint4 per stage (KU K steps)
+  static_assert((KU * (WT + AP)) % 4 == 0, "copies must divide over the four waves");
   __shared__ uint4 lds[NS * STAGE];
   __shared__ float s_inv[BM];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -571,6 +575,7 @@ __global__ __launch_bounds__(256) void k_gemm_rows_pipe(GemmArgs a) {
   const int n0 = nb0 + wn, m0 = mb + wm;
   const int M = a.M, ld = a.act_ld;
   const int ksteps = a.K / 32;
+  const int nst = ksteps / KU;  // stages (the launcher checks that KU divides the K steps)
   if (tid < BM) {
     float inv = 1.f;
     const int m = mb + tid;
@@ -583,21 +588,25 @@ __global__ __launch_bounds__(256) void k_gemm_rows_pipe(GemmArgs a) {
   }
   const uint4* W = reinterpret_cast<const uint4*>(a.W) + (size_t)(nb0 >> 4) * ksteps * 64;
   const uint4* H = reinterpret_cast<const uint4*>(a.act);
-  auto issue = [&](int j, int buf) {
+  // copy stage g (K steps g*KU .. g*KU+KU-1) into buffer buf: piece p of the stage
+  // is K step kk = p / (WT + AP), within it weight tile x < WT or activation piece
+  auto issue = [&](int g, int buf) {
 #pragma unroll
     for (int r = 0; r < PER; ++r) {
-      const int p = wave + 4 * r;  // piece of the step (wave-uniform)
+      const int p = wave + 4 * r;  // (wave-uniform)
+      const int kk = p / (WT + AP), x = p % (WT + AP);
+      const int j = g * KU + kk;
       const uint4* src;
       uint4* dst;
-      if (p < WT) {
-        src = W + ((size_t)p * ksteps + j) * 64 + lane;
-        dst = lds + buf * STAGE + p * 64;
+      if (x < WT) {
+        src = W + ((size_t)x * ksteps + j) * 64 + lane;
+        dst = lds + buf * STAGE + kk * STEP + x * 64;
       } else {
-        const int x = p - WT, c = x / (BM / 64), h = x % (BM / 64);
+        const int y = x - WT, c = y / (BM / 64), h = y % (BM / 64);
         int row = mb + 64 * h + lane;
         row = row < M ? row : M - 1;
         src = H + (size_t)(4 * j + c) * ld + row;
-        dst = lds + buf * STAGE + WT * 64 + c * BM + 64 * h;
+        dst = lds + buf * STAGE + kk * STEP + WT * 64 + c * BM + 64 * h;
       }
       __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
                                        (void __attribute__((address_space(3)))*)dst, 16, 0, 0);
@@ -610,33 +619,41 @@ __global__ __launch_bounds__(256) void k_gemm_rows_pipe(GemmArgs a) {
     for (int u = 0; u < TM; ++u) acc[t][u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int st = 0; st < NS - 1; ++st)
-    if (st < ksteps) issue(st, st);
+    if (st < nst) issue(st, st);
   // s_inv is in LDS before the first barrier (a full one, with its fence)
   __syncthreads();
   const uint32_t lds0 = (uint32_t)(uintptr_t)lds;  // byte offset of the array in LDS
-  for (int j = 0; j < ksteps; ++j) {
-    if (j + NS - 2 < ksteps) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PER * (NS - 2)) : "memory");
+  for (int g = 0; g < nst; ++g) {
+    if (g + NS - 2 < nst) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PER * (NS - 2)) : "memory");
     else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();  // every wave's copies of step j have landed
-    if (j + NS - 1 < ksteps) issue(j + NS - 1, (j + NS - 1) % NS);
-    const uint32_t sw = lds0 + (uint32_t)((j % NS) * STAGE) * 16;
-    const uint32_t sa = sw + WT * 64 * 16;
-    u32x4 av[TN], bv[TM];
+    __builtin_amdgcn_s_barrier();  // every wave's copies of stage g have landed
+    if (g + NS - 1 < nst) issue(g + NS - 1, (g + NS - 1) % NS);
+    u32x4 av[KU][TN], bv[KU][TM];
 #pragma unroll
-    for (int t = 0; t < TN; ++t) av[t] = lds_read16(sw + (((wave & 1) * TN + t) * 64 + lane) * 16);
+    for (int kk = 0; kk < KU; ++kk) {
+      const uint32_t sw = lds0 + (uint32_t)((g % NS) * STAGE + kk * STEP) * 16;
+      const uint32_t sa = sw + WT * 64 * 16;
 #pragma unroll
-    for (int u = 0; u < TM; ++u) bv[u] = lds_read16(sa + (q * BM + wm + 16 * u + i) * 16);
+      for (int t = 0; t < TN; ++t) av[kk][t] = lds_read16(sw + (((wave & 1) * TN + t) * 64 + lane) * 16);
+#pragma unroll
+      for (int u = 0; u < TM; ++u) bv[kk][u] = lds_read16(sa + (q * BM + wm + 16 * u + i) * 16);
+    }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-    for (int t = 0; t < TN; ++t) asm volatile("" : "+v"(av[t]));
+    for (int kk = 0; kk < KU; ++kk) {
 #pragma unroll
-    for (int u = 0; u < TM; ++u) asm volatile("" : "+v"(bv[u]));
+      for (int t = 0; t < TN; ++t) asm volatile("" : "+v"(av[kk][t]));
 #pragma unroll
-    for (int t = 0; t < TN; ++t)
+      for (int u = 0; u < TM; ++u) asm volatile("" : "+v"(bv[kk][u]));
+    }
 #pragma unroll
-      for (int u = 0; u < TM; ++u)
-        acc[t][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-            __builtin_bit_cast(f16x8, av[t]), __builtin_bit_cast(f16x8, bv[u]), acc[t][u], 0, 0, 0);
+    for (int kk = 0; kk < KU; ++kk)
+#pragma unroll
+      for (int t = 0; t < TN; ++t)
+#pragma unroll
+        for (int u = 0; u < TM; ++u)
+          acc[t][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+              __builtin_bit_cast(f16x8, av[kk][t]), __builtin_bit_cast(f16x8, bv[kk][u]), acc[t][u], 0, 0, 0);
   }
   bool mrow[TM];
 #pragma unroll
@@ -766,7 +783,8 @@ hipError_t launch_gemm_rows(const GemmArgs& a, hipStream_t s) {
   const long long mid = (long long)((a.M + 127) / 128) * (a.nrows / 64);
   const bool i8 = a.scale != nullptr;
   // (measured at 1024 rows: the direct form is faster for 128 x 128 blocks, the
-  // copy-pipelined form for 64 x 128 and 64 x 64)
+  // copy-pipelined form for 64 x 128 and 64 x 64; stages of two K steps, three in
+  // flight for 64 x 128 (72 KB of LDS, two blocks per CU) and four for 64 x 64)
   if (big >= 512) {
     const dim3 grid((a.M + 127) / 128, a.nrows / 128);
     if (i8) launch_kernel((k_gemm_rows<true, 4, 4>), grid, dim3(256), s, a);
@@ -774,11 +792,11 @@ hipError_t launch_gemm_rows(const GemmArgs& a, hipStream_t s) {
   } else if (mid >= 512) {
     const dim3 grid((a.M + 127) / 128, a.nrows / 64);
     if (i8) launch_kernel((k_gemm_rows<true, 2, 4>), grid, dim3(256), s, a);
-    else launch_kernel((k_gemm_rows_pipe<2, 4, 4>), grid, dim3(256), s, a);
+    else launch_kernel((k_gemm_rows_pipe<2, 4, 3, kPipeKU>), grid, dim3(256), s, a);
   } else {
     const dim3 grid((a.M + 63) / 64, a.nrows / 64);
     if (i8) launch_kernel((k_gemm_rows<true, 2, 2>), grid, dim3(256), s, a);
-    else launch_kernel((k_gemm_rows_pipe<2, 2, 4>), grid, dim3(256), s, a);
+    else launch_kernel((k_gemm_rows_pipe<2, 2, 4, kPipeKU>), grid, dim3(256), s, a);
   }
   return hipGetLastError();
 }
