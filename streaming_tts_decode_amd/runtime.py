@@ -374,6 +374,53 @@ class Scheduler:
             _write_pages(self.torch, self.k_pages, self.v_pages, pages, k_bits, v_bits)
         return sid
 
+    def open_pages(self, length: int, min_frames: int = 1, max_frames: int = 1 << 30):
+        """Open a session with `length` positions to be prefilled and return (id, its
+        pages in position order) without writing them: the caller fills them, e.g.
+        with prefill() below, before the session's first step."""
+        sid, pages = qt_sched_open(self.handle, length, min_frames, max_frames, PAGE)
+        return sid, [int(p) for p in pages]
+
+    def prefill(self, sessions, prompts):
+        """qt_prefill of prompts[i] (bf16 bits [T_i, talker hidden], T_i the length the
+        session was opened with) into the pages of sessions[i] = (id, pages) from
+        open_pages, on this scheduler's stream.  Returns device tensors (logits0
+        [n, talker_vocab], tok0 [n], h_last bf16 bits [n, talker hidden], status [1]),
+        valid once the stream has reached them."""
+        torch, d = self.torch, self.dims
+        n = len(sessions)
+        lens = [int(p.shape[0]) for p in prompts]
+        rows = max(16, -(-sum(lens) // 16) * 16)
+        if rows > 64:
+            rows = -(-rows // 64) * 64
+        starts = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        emb = np.zeros((rows, d.talker.hidden), dtype=np.uint16)
+        table = np.zeros((n, self.max_pages), dtype=np.int32)
+        for i, ((_, pages), p) in enumerate(zip(sessions, prompts)):
+            emb[starts[i]:starts[i + 1]] = p
+            table[i, :len(pages)] = pages
+            table[i, len(pages):] = pages[-1] if pages else 0  # (past the prompt: never used)
+        dev = self.dev
+        bufs = {
+            "seq_start": torch.from_numpy(starts).to(dev),
+            "embeds": torch.from_numpy(emb.view(np.int16)).to(dev),
+            "page_table": torch.from_numpy(table).to(dev),
+            "kv_len": torch.zeros(n, dtype=torch.int32, device=dev),
+            "logits0": torch.zeros((n, d.talker_vocab), dtype=torch.float32, device=dev),
+            "tok0": torch.zeros(n, dtype=torch.int32, device=dev),
+            "h_last": torch.zeros((n, d.talker.hidden), dtype=torch.int16, device=dev),
+            "status": torch.zeros(1, dtype=torch.int32, device=dev),
+        }
+        ws_bytes = qt_prefill_workspace_bytes(self.pm.cfg, rows, n)
+        ws_buf, ws_ptr = _aligned(torch, ws_bytes, dev)
+        args = PrefillArgs(rows, n, bufs["seq_start"].data_ptr(), bufs["embeds"].data_ptr(),
+                           bufs["page_table"].data_ptr(), self.max_pages, bufs["kv_len"].data_ptr(),
+                           bufs["logits0"].data_ptr(), bufs["tok0"].data_ptr(),
+                           bufs["h_last"].data_ptr(), bufs["status"].data_ptr())
+        qt_prefill(self.pm.handle, args, self.kv, ws_ptr, ws_bytes, self.stream.cuda_stream)
+        self._held.append((bufs, ws_buf))  # alive until the next step is enqueued
+        return bufs["logits0"], bufs["tok0"], bufs["h_last"], bufs["status"]
+
     def set_sampling(self, sid: int, params=None, seed: int = 0):
         """params: (codebook-0, predictor) (temperature, top_p, penalty, top_k) pair, or
         None for greedy."""

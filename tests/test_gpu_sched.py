@@ -430,3 +430,46 @@ def test_sched_sampling_is_bit_identical_to_plain_frames(small_pm):
     dec.close()
     log(f"[sched] sampled scheduler frames bit-identical to plain frames; "
         f"frames whose codebook-0 draws moved off the first frame's: {changed}")
+
+
+def test_prefill_into_scheduler_pages_then_steps(small_pm, orc_small):
+    """Prompts prefilled (qt_prefill) straight into the pages the scheduler hands out,
+    then teacher-forced frames through qt_sched_step: every session's codec-head
+    logits after the prefill and every frame's logits match the oracle continuing
+    from its own prefill ("Qwen3-TTS PR 5", What changed: the Talker prefill, then
+    decode from its cache)."""
+    from streaming_tts_decode_amd.runtime import Scheduler
+    from tests.parity import compare
+    torch = small_pm.torch
+    lengths = [37, 16, 1, 60, 33]  # a page boundary, one token, several pages
+    F = 3
+    S = len(lengths)
+    x, forced = _inputs("sched.pf", F, S)
+    prompts = [synth.normal_bf16(f"sched.pf.prompt{s}", (L, D.talker.hidden)) for s, L in enumerate(lengths)]
+    sch = Scheduler(small_pm, buckets=(1, 2, 4), max_sessions=8, max_pages=8)
+    try:
+        sess = [sch.open_pages(L) for L in lengths]
+        assert [len(p) for _, p in sess] == [-(-L // PS) for L in lengths]
+        l0, tok0, _, st = sch.prefill(sess, prompts)
+        torch.cuda.synchronize()
+        assert int(st.item()) == 0
+        got, groups = _run_sched(sch, [sid for sid, _ in sess], x, forced, F)
+        assert sch.status() == 0
+        for s, sid in enumerate(sess):
+            assert sch.length(sid[0]) == lengths[s] + F
+        log(f"[sched] prefill then steps: lengths {lengths}, groups per step {groups}")
+        worst = 0.0
+        for s, L in enumerate(lengths):
+            pre = orc_small.prefill(prompts[s], capacity=L + F)
+            st0 = compare(l0[s].cpu().numpy()[None], pre["logits0"][None], D.cb0_range,
+                          gpu_tokens=tok0[s:s + 1].cpu().numpy(), label=f"sched prefill s{s}")
+            ref = orc_small.run_session("full", F, talker_in=x[:, s], length=L,
+                                        forced=forced[:, s], cache=(pre["kc"], pre["vc"]))
+            a = compare(got[s]["l0"], ref["logits0"], D.cb0_range, gpu_tokens=got[s]["tok"][:, 0],
+                        label=f"sched after prefill s{s} logits0")
+            b = compare(got[s]["lp"], ref["logits_pred"], D.code_vocab, gpu_tokens=got[s]["tok"][:, 1:],
+                        label=f"sched after prefill s{s} predictor")
+            worst = max(worst, st0["rel_max"], a["rel_max"], b["rel_max"])
+        log(f"[sched] prefill then steps: worst relative logit error {worst:.3g}")
+    finally:
+        sch.close()
