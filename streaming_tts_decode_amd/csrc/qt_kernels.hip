@@ -316,14 +316,17 @@ __global__ __launch_bounds__(256) void k_attn_paged(AttnPagedArgs a, float theta
 // Grid (kv head, session).  n_new (1 or 2) new positions pos0 .. pos0+n_new-1
 // are normalised, rotated, appended, and each attends causally to positions
 // 0 .. its own.  At most 16 positions: one thread group of 16 per position.
+// The new vectors go one per wave (waves 0, 1: query heads 2h, 2h+1; wave 2: the
+// key; wave 3: the value), lane l holding dimensions l and l + 64, the two halves
+// of each RoPE pair: the norm is one wave reduction and the rotation stays in the
+// lane, with no block barrier.  The softmax of all (new position, head) rows is
+// one wave's work, a row of 16 lanes per row.
 __global__ __launch_bounds__(256) void k_attn_pred(AttnPredArgs a, float theta_log2) {
   const int h = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int jj = tid >> 7, d = tid & 127;
   __shared__ float qs[2][2][128];
   __shared__ float kn[2][128], vn[2][128];
-  __shared__ float rb[2][128];
-  __shared__ float ssq[2][2];
   __shared__ float sc[2][2][16];
   __shared__ float red[4][2][2][128];
   __shared__ float lsum[2][2];
@@ -332,38 +335,60 @@ __global__ __launch_bounds__(256) void k_attn_pred(AttnPredArgs a, float theta_l
   uint16_t* kbase = a.k_cache + (size_t)b * a.sess_stride;
   uint16_t* vbase = a.v_cache + (size_t)b * a.sess_stride;
 
-  // one round trip: the raw new rows and every cached position (thread group
-  // t = tid>>4 holds position t, dims 8c..8c+7)
+  // one round trip: every cached position (thread group t = tid>>4 holds position
+  // t, dims 8c..8c+7), this wave's vector of every new position and its gain
   const int t = tid >> 4, c = tid & 15;
-  const uint16_t gq_bits = a.q_norm[d], gk_bits = a.k_norm[d];
   uint4 kq = make_uint4(0, 0, 0, 0), vq = make_uint4(0, 0, 0, 0);
   if (t < a.pos0) {
     const size_t off = ((size_t)t * a.n_kv + h) * 128 + 8 * c;
     kq = *reinterpret_cast<const uint4*>(kbase + off);
     vq = *reinterpret_cast<const uint4*>(vbase + off);
   }
-  float qraw[2] = {0.f, 0.f}, kvraw[2] = {0.f, 0.f};
+  const int col = wave < 2 ? (j0 + wave) * 128 : q_dim + (wave == 3 ? kv_dim : 0) + h * 128;
+  float x0[2] = {0.f, 0.f}, x1[2] = {0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     if (i < a.n_new) {
-      const float* row = a.qkv + (size_t)(i * a.B + b) * a.qkv_ld;
-      qraw[i] = row[(j0 + jj) * 128 + d];
-      kvraw[i] = row[q_dim + (jj ? kv_dim : 0) + h * 128 + d];
+      const float* row = a.qkv + (size_t)(i * a.B + b) * a.qkv_ld + col;
+      x0[i] = row[lane];
+      x1[i] = row[lane + 64];
     }
   }
+  const uint16_t* gain = wave < 2 ? a.q_norm : a.k_norm;
+  const float g0 = bf2f(gain[lane]), g1 = bf2f(gain[lane + 64]);
+  // angle of pair `lane` = pos * theta^(-2 lane/128), in revolutions and reduced to
+  // [0, 1) in double; the hardware sine and cosine take it from there
+  const double inv_rev = exp2(-(double)(2 * lane) * (double)theta_log2 / 128.0) *
+                         0.15915494309189533576888376337251;  // 1 / (2 pi)
   for (int i = 0; i < a.n_new; ++i) {
     const int pos = a.pos0 + i;
-    const float r = norm_rope_128(qraw[i], d, bf2f(gq_bits), a.eps, pos, theta_log2, rb[jj], ssq[jj]);
-    qs[i][jj][d] = r * kInvSqrtHd;
-    __syncthreads();
-    const float kr = norm_rope_128(kvraw[i], d, bf2f(gk_bits), a.eps, pos, theta_log2, rb[jj], ssq[jj]);
-    const float kv = jj ? kvraw[i] : kr;
-    const uint16_t bits = f2bf(kv);
-    const size_t off = ((size_t)pos * a.n_kv + h) * 128 + d;
-    (jj == 0 ? kbase : vbase)[off] = bits;
-    (jj == 0 ? kn[i] : vn[i])[d] = bf2f(bits);
-    __syncthreads();
+    float v0 = x0[i], v1 = x1[i];
+    if (wave < 3) {  // q heads and the key: RMSNorm with the gain, then RoPE
+      const float f = 1.0f / sqrtf(wave_sum(v0 * v0 + v1 * v1) * (1.0f / 128.0f) + a.eps);
+      v0 = v0 * f * g0;
+      v1 = v1 * f * g1;
+      double rev = (double)pos * inv_rev;
+      rev -= floor(rev);
+      const float sn = __builtin_amdgcn_sinf((float)rev), cs = __builtin_amdgcn_cosf((float)rev);
+      const float r0 = v0 * cs - v1 * sn, r1 = v1 * cs + v0 * sn;
+      v0 = r0;
+      v1 = r1;
+    }
+    if (wave < 2) {
+      qs[i][wave][lane] = v0 * kInvSqrtHd;
+      qs[i][wave][lane + 64] = v1 * kInvSqrtHd;
+    } else {
+      const uint16_t b0 = f2bf(v0), b1 = f2bf(v1);
+      const size_t off = ((size_t)pos * a.n_kv + h) * 128;
+      uint16_t* dst = wave == 2 ? kbase : vbase;
+      dst[off + lane] = b0;
+      dst[off + lane + 64] = b1;
+      float* nb = wave == 2 ? kn[i] : vn[i];
+      nb[lane] = bf2f(b0);
+      nb[lane + 64] = bf2f(b1);
+    }
   }
+  __syncthreads();
 
   const int n_pos = a.pos0 + a.n_new;
   float kf[8], vf[8];
@@ -384,7 +409,7 @@ __global__ __launch_bounds__(256) void k_attn_pred(AttnPredArgs a, float theta_l
 #pragma unroll
     for (int e = 0; e < 8; ++e) kf[e] = vf[e] = 0.f;
   }
-  // scores for every (new position i, head jj)
+  // scores for every (new position i, head hh)
   for (int i = 0; i < a.n_new; ++i) {
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
@@ -396,17 +421,18 @@ __global__ __launch_bounds__(256) void k_attn_pred(AttnPredArgs a, float theta_l
     }
   }
   __syncthreads();
-  if (tid < 2 * a.n_new) {
-    const int i = tid >> 1, hh = tid & 1;
-    float m = -INFINITY;
-    for (int u = 0; u <= a.pos0 + i; ++u) m = fmaxf(m, sc[i][hh][u]);
-    float l = 0.f;
-    for (int u = 0; u < 16; ++u) {
-      const float e = (u <= a.pos0 + i) ? expf(sc[i][hh][u] - m) : 0.f;
+  // softmax: wave 0, lane (i, hh, u) = (lane >> 5, (lane >> 4) & 1, lane & 15)
+  if (wave == 0) {
+    const int i = lane >> 5, hh = (lane >> 4) & 1, u = lane & 15;
+    if (i < a.n_new) {  // (rows of 16 lanes: uniform within each row)
+      const bool in = u <= a.pos0 + i;
+      const float v = in ? sc[i][hh][u] : -INFINITY;
+      const float m = row_max16(v);
+      const float e = in ? expf(v - m) : 0.f;
+      const float l = row_sum16(e);
       sc[i][hh][u] = e;
-      l += e;
+      if (u == 0) lsum[i][hh] = l;
     }
-    lsum[i][hh] = l;
   }
   __syncthreads();
   for (int i = 0; i < a.n_new; ++i) {
