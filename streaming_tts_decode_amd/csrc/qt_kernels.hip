@@ -15,32 +15,29 @@ namespace {
 
 using namespace dev;
 
-// Per-head RMSNorm + rotate-half RoPE of one 128-vector held by 128 threads
-// (thread d of the group holds element d).  `buf` is a 128-float LDS slot used
-// for the pair exchange; `ss_slot` two floats for the sum of squares of the two
-// waves of the group.  `gain` is element d of the norm gain, loaded by the caller
-// ahead of its other loads (loads complete in order, so a gain loaded here would
-// wait for all of them).  Returns the rotated element d.
-__device__ __forceinline__ float norm_rope_128(float v, int d, float gain, float eps, int pos,
-                                               float theta_log2, float* buf, float* ss_slot) {
-  const int lane = threadIdx.x & 63;
-  float ss = wave_sum(v * v);
-  if (lane == 0) ss_slot[(d >> 6)] = ss;
-  __syncthreads();
-  const float tot = ss_slot[0] + ss_slot[1];
-  const float nv = v * (1.0f / sqrtf(tot * (1.0f / 128.0f) + eps)) * gain;
-  buf[d] = nv;
-  __syncthreads();
-  const int i = d & 63;
-  // angle = pos * theta^(-2i/128), in revolutions and reduced to [0, 1) in double;
-  // the hardware sine and cosine (arguments in revolutions) take it from there
-  const double inv_rev = exp2(-(double)(2 * i) * (double)theta_log2 / 128.0) *
-                         0.15915494309189533576888376337251;  // 1 / (2 pi)
+// The inverse frequency of RoPE pair l (dimensions l and l + 64) in revolutions
+// per position, theta^(-2l/128) / (2 pi), in double.
+__device__ __forceinline__ double rope_inv_rev(int l, float theta_log2) {
+  return exp2(-(double)(2 * l) * (double)theta_log2 / 128.0) *
+         0.15915494309189533576888376337251;  // 1 / (2 pi)
+}
+
+// Per-head RMSNorm + rotate-half RoPE of one 128-vector held by one wave, lane l
+// holding elements l (v0) and l + 64 (v1), the two halves of its RoPE pair: the
+// norm is one wave reduction and the rotation stays in the lane, so no block
+// barrier is needed.  The angle pos * inv_rev is reduced to [0, 1) revolutions
+// in double; the hardware sine and cosine take it from there.
+__device__ __forceinline__ void norm_rope_pair(float& v0, float& v1, float g0, float g1, float eps,
+                                               double inv_rev, int pos) {
+  const float f = 1.0f / sqrtf(wave_sum(v0 * v0 + v1 * v1) * (1.0f / 128.0f) + eps);
+  v0 = v0 * f * g0;
+  v1 = v1 * f * g1;
   double rev = (double)pos * inv_rev;
   rev -= floor(rev);
   const float sn = __builtin_amdgcn_sinf((float)rev), cs = __builtin_amdgcn_cosf((float)rev);
-  const float partner = buf[d ^ 64];
-  return (d < 64) ? nv * cs - partner * sn : nv * cs + partner * sn;
+  const float r0 = v0 * cs - v1 * sn, r1 = v1 * cs + v0 * sn;
+  v0 = r0;
+  v1 = r1;
 }
 
 // ---------------------------------------------------------------------------
@@ -66,11 +63,9 @@ __global__ __launch_bounds__(256) void k_attn_paged(AttnPagedArgs a, float theta
   const int h = blockIdx.x, b = blockIdx.y, s = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   __shared__ float qs[2][128];
-  __shared__ float rb[2][128];
   __shared__ float knew[128], vnew[128];
   __shared__ float sc[2][PPS * kPage];
   __shared__ float red[4][2][128];
-  __shared__ float ssq[2][2];
   __shared__ float stat[2][2];
   __shared__ float mstat[2], lstat[2];
   __shared__ int s_last;
@@ -90,9 +85,12 @@ __global__ __launch_bounds__(256) void k_attn_paged(AttnPagedArgs a, float theta
     const int pidx = s * PPS + g;
     pg[g] = ptab[pidx < a.max_pages ? pidx : a.max_pages - 1];
   }
-  const float qraw = qrow[(j0 + jj) * 128 + d];
-  const float kvraw = qrow[q_dim + (jj ? kv_dim : 0) + h * 128 + d];
-  const uint16_t gq_bits = a.q_norm[d], gk_bits = a.k_norm[d];
+  // this wave's vector (waves 0, 1: query heads j0, j0+1; wave 2: the new key;
+  // wave 3: the new value), lane l holding dimensions l and l + 64, and its gain
+  const int col = wave < 2 ? (j0 + wave) * 128 : q_dim + (wave == 3 ? kv_dim : 0) + h * 128;
+  const float x0 = qrow[col + lane], x1 = qrow[col + lane + 64];
+  const uint16_t* gain = wave < 2 ? a.q_norm : a.k_norm;
+  const uint16_t g0_bits = gain[lane], g1_bits = gain[lane + 64];
 
   const size_t orow = chunked(b, (j0 + jj) * 128 + d, a.o_ld);
   if (p < 0 || p >= cap) {
@@ -135,24 +133,29 @@ __global__ __launch_bounds__(256) void k_attn_paged(AttnPagedArgs a, float theta
     vv[g] = load_nt(reinterpret_cast<const uint4*>(a.v_pool + koff[g]));
   if (bad && c == 0) atomicOr(a.status, QT_STATUS_BAD_PAGE);
 
-  // q heads j0 (threads 0..127) and j0+1 (128..255), while the K/V loads fly
-  {
-    const float r = norm_rope_128(qraw, d, bf2f(gq_bits), a.eps, p, theta_log2, rb[jj], ssq[jj]);
-    qs[jj][d] = r * kInvSqrtHd;
-  }
-  if (has_new) {
-    // threads 0..127: key of KV head h (normalised and rotated); threads 128..255:
-    // value (taken raw; the normalisation both halves run keeps barriers uniform)
-    const float kr = norm_rope_128(kvraw, d, bf2f(gk_bits), a.eps, p, theta_log2, rb[jj], ssq[jj]);
-    const float kv = jj ? kvraw : kr;
-    const uint16_t bits = f2bf(kv);
-    if (pgn >= 0 && pgn < a.num_pages) {
-      const size_t off = ((size_t)pgn * a.n_kv + h) * (kPage * 128) + (size_t)(p % kPage) * 128 + d;
-      (jj == 0 ? a.k_pool : a.v_pool)[off] = bits;
-    } else if (d == 0 && jj == 0) {
-      atomicOr(a.status, QT_STATUS_BAD_PAGE);
+  // q heads, and in the split holding p the new key and value, while the K/V
+  // loads fly: one vector per wave, no block barrier until all are in LDS
+  if (wave < 2 || has_new) {
+    float v0 = x0, v1 = x1;
+    if (wave < 3)  // the value is taken raw
+      norm_rope_pair(v0, v1, bf2f(g0_bits), bf2f(g1_bits), a.eps, rope_inv_rev(lane, theta_log2), p);
+    if (wave < 2) {
+      qs[wave][lane] = v0 * kInvSqrtHd;
+      qs[wave][lane + 64] = v1 * kInvSqrtHd;
+    } else {
+      const uint16_t b0 = f2bf(v0), b1 = f2bf(v1);
+      if (pgn >= 0 && pgn < a.num_pages) {
+        const size_t off = ((size_t)pgn * a.n_kv + h) * (kPage * 128) + (size_t)(p % kPage) * 128;
+        uint16_t* dst = wave == 2 ? a.k_pool : a.v_pool;
+        dst[off + lane] = b0;
+        dst[off + lane + 64] = b1;
+      } else if (wave == 2 && lane == 0) {
+        atomicOr(a.status, QT_STATUS_BAD_PAGE);
+      }
+      float* nb = wave == 2 ? knew : vnew;
+      nb[lane] = bf2f(b0);
+      nb[lane + 64] = bf2f(b1);
     }
-    (jj == 0 ? knew : vnew)[d] = bf2f(bits);
   }
   __syncthreads();
 
@@ -356,24 +359,12 @@ __global__ __launch_bounds__(256) void k_attn_pred(AttnPredArgs a, float theta_l
   }
   const uint16_t* gain = wave < 2 ? a.q_norm : a.k_norm;
   const float g0 = bf2f(gain[lane]), g1 = bf2f(gain[lane + 64]);
-  // angle of pair `lane` = pos * theta^(-2 lane/128), in revolutions and reduced to
-  // [0, 1) in double; the hardware sine and cosine take it from there
-  const double inv_rev = exp2(-(double)(2 * lane) * (double)theta_log2 / 128.0) *
-                         0.15915494309189533576888376337251;  // 1 / (2 pi)
+  const double inv_rev = rope_inv_rev(lane, theta_log2);
   for (int i = 0; i < a.n_new; ++i) {
     const int pos = a.pos0 + i;
     float v0 = x0[i], v1 = x1[i];
-    if (wave < 3) {  // q heads and the key: RMSNorm with the gain, then RoPE
-      const float f = 1.0f / sqrtf(wave_sum(v0 * v0 + v1 * v1) * (1.0f / 128.0f) + a.eps);
-      v0 = v0 * f * g0;
-      v1 = v1 * f * g1;
-      double rev = (double)pos * inv_rev;
-      rev -= floor(rev);
-      const float sn = __builtin_amdgcn_sinf((float)rev), cs = __builtin_amdgcn_cosf((float)rev);
-      const float r0 = v0 * cs - v1 * sn, r1 = v1 * cs + v0 * sn;
-      v0 = r0;
-      v1 = r1;
-    }
+    // q heads and the key: RMSNorm with the gain, then RoPE (the value is taken raw)
+    if (wave < 3) norm_rope_pair(v0, v1, g0, g1, a.eps, inv_rev, pos);
     if (wave < 2) {
       qs[i][wave][lane] = v0 * kInvSqrtHd;
       qs[i][wave][lane + 64] = v1 * kInvSqrtHd;
@@ -982,34 +973,41 @@ __global__ __launch_bounds__(256) void k_prefill_begin(PrefillBeginArgs a) {
 }
 
 // Per (row, KV head h): query heads 2h, 2h+1 and key head h normalised and rotated at
-// the row's position (the same arithmetic as a decode step); q is stored back
-// scaled by 1/sqrt(128), the key (bf16) and the raw value go to the page slot.
+// the row's position (the same arithmetic as a decode step), one vector per wave
+// (waves 0, 1: the query heads; wave 2: the key; wave 3: the value), lane l holding
+// dimensions l and l + 64; q is stored back scaled by 1/sqrt(128), the key (bf16)
+// and the raw value go to the page slot.
 __global__ __launch_bounds__(256) void k_prefill_qk(PrefillQkArgs a, float theta_log2) {
-  __shared__ float rb[2][128];
-  __shared__ float ssq[2][2];
   const int r = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
-  const int jj = tid >> 7, d = tid & 127;
+  const int lane = tid & 63, wave = tid >> 6;
   const int seq = a.rowinfo[2 * r], p = seq >= 0 ? a.rowinfo[2 * r + 1] : 0;
   float* row = a.qkv + (size_t)r * a.qkv_ld;
   const int q_dim = a.n_q * 128, kv_dim = a.n_kv * 128;
-  const float qraw = row[(2 * h + jj) * 128 + d];
-  const float kvraw = row[q_dim + (jj ? kv_dim : 0) + h * 128 + d];
-  const float gq = bf2f(a.q_norm[d]), gk = bf2f(a.k_norm[d]);
-  const float qr = norm_rope_128(qraw, d, gq, a.eps, p, theta_log2, rb[jj], ssq[jj]);
-  const float kr = norm_rope_128(kvraw, d, gk, a.eps, p, theta_log2, rb[jj], ssq[jj]);
-  row[(2 * h + jj) * 128 + d] = qr * kInvSqrtHd;
+  const int col = wave < 2 ? (2 * h + wave) * 128 : q_dim + (wave == 3 ? kv_dim : 0) + h * 128;
+  float v0 = row[col + lane], v1 = row[col + lane + 64];
+  const uint16_t* gain = wave < 2 ? a.q_norm : a.k_norm;
+  if (wave < 3)  // the value is taken raw
+    norm_rope_pair(v0, v1, bf2f(gain[lane]), bf2f(gain[lane + 64]), a.eps,
+                   rope_inv_rev(lane, theta_log2), p);
+  if (wave < 2) {
+    row[col + lane] = v0 * kInvSqrtHd;
+    row[col + lane + 64] = v1 * kInvSqrtHd;
+    return;
+  }
   if (seq < 0) return;
   if (p >= a.max_pages * kPage) {
-    if (tid == 0) atomicOr(a.status, QT_STATUS_KV_OVERFLOW);
+    if (wave == 2 && lane == 0) atomicOr(a.status, QT_STATUS_KV_OVERFLOW);
     return;
   }
   const int pg = a.page_table[(size_t)seq * a.max_pages + p / kPage];
   if (pg < 0 || pg >= a.num_pages) {
-    if (tid == 0) atomicOr(a.status, QT_STATUS_BAD_PAGE);
+    if (wave == 2 && lane == 0) atomicOr(a.status, QT_STATUS_BAD_PAGE);
     return;
   }
-  const size_t off = ((size_t)pg * a.n_kv + h) * (kPage * 128) + (size_t)(p % kPage) * 128 + d;
-  (jj == 0 ? a.k_pool : a.v_pool)[off] = f2bf(jj ? kvraw : kr);
+  const size_t off = ((size_t)pg * a.n_kv + h) * (kPage * 128) + (size_t)(p % kPage) * 128;
+  uint16_t* dst = wave == 2 ? a.k_pool : a.v_pool;
+  dst[off + lane] = f2bf(v0);
+  dst[off + lane + 64] = f2bf(v1);
 }
 
 // Causal attention over packed sequences on the matrix cores.  Block (64-row
