@@ -66,7 +66,6 @@ __global__ __launch_bounds__(256) void k_attn_paged(AttnPagedArgs a, float theta
   __shared__ float knew[128], vnew[128];
   __shared__ float sc[2][PPS * kPage];
   __shared__ float red[4][2][128];
-  __shared__ float stat[2][2];
   __shared__ float mstat[2], lstat[2];
   __shared__ int s_last;
 
@@ -194,22 +193,22 @@ __global__ __launch_bounds__(256) void k_attn_paged(AttnPagedArgs a, float theta
   }
   __syncthreads();
 
-  // softmax statistics per head over this split (threads 0..127 head 0, 128..255 head 1)
+  // softmax statistics per head over this split: wave w < 2 takes head w, lane l
+  // its positions l and l + 64 (wave reductions only, one barrier)
   const int n = t1 - t0;
-  {
-    const float v = (d < n) ? sc[jj][d] : -INFINITY;
-    const float mx = wave_max(v);
-    if (lane == 0) stat[jj][wave & 1] = mx;
-    __syncthreads();
-    const float m = fmaxf(stat[jj][0], stat[jj][1]);
-    const float e = (d < n) ? expf(v - m) : 0.f;
-    const float sm = wave_sum(e);
-    __syncthreads();
-    if (d < n) sc[jj][d] = e;
-    if (lane == 0) stat[jj][wave & 1] = sm;
-    if (d == 0) mstat[jj] = m;
-    __syncthreads();
-    if (d == 0) lstat[jj] = stat[jj][0] + stat[jj][1];
+  if (wave < 2) {
+    const int u0 = lane, u1 = lane + 64;
+    const float v0 = u0 < n ? sc[wave][u0] : -INFINITY;
+    const float v1 = u1 < n ? sc[wave][u1] : -INFINITY;
+    const float m = wave_max(fmaxf(v0, v1));
+    const float e0 = u0 < n ? expf(v0 - m) : 0.f, e1 = u1 < n ? expf(v1 - m) : 0.f;
+    const float sm = wave_sum(e0 + e1);
+    if (u0 < n) sc[wave][u0] = e0;
+    if (u1 < n) sc[wave][u1] = e1;
+    if (lane == 0) {
+      mstat[wave] = m;
+      lstat[wave] = sm;
+    }
   }
   __syncthreads();
 
