@@ -362,16 +362,17 @@ class Scheduler:
         the device from copy_from = (k_pool, v_pool, page ids in position order) of
         another pool with the same layout."""
         sid, pages = qt_sched_open(self.handle, length, min_frames, max_frames, PAGE)
-        if length and copy_from is not None:
-            torch = self.torch
-            k_src, v_src, src_pages = copy_from
-            dst = torch.as_tensor(np.asarray(pages, dtype=np.int64), device=self.dev)
-            src = torch.as_tensor(np.asarray(src_pages[:len(pages)], dtype=np.int64),
-                                  device=self.dev)
-            self.k_pages[:, dst] = k_src[:, src]
-            self.v_pages[:, dst] = v_src[:, src]
-        elif length:
-            _write_pages(self.torch, self.k_pages, self.v_pages, pages, k_bits, v_bits)
+        torch = self.torch
+        with torch.cuda.stream(self.stream):  # ordered before the session's first step
+            if length and copy_from is not None:
+                k_src, v_src, src_pages = copy_from
+                dst = torch.as_tensor(np.asarray(pages, dtype=np.int64), device=self.dev)
+                src = torch.as_tensor(np.asarray(src_pages[:len(pages)], dtype=np.int64),
+                                      device=self.dev)
+                self.k_pages[:, dst] = k_src[:, src]
+                self.v_pages[:, dst] = v_src[:, src]
+            elif length:
+                _write_pages(torch, self.k_pages, self.v_pages, pages, k_bits, v_bits)
         return sid
 
     def open_pages(self, length: int, min_frames: int = 1, max_frames: int = 1 << 30):
@@ -401,23 +402,25 @@ class Scheduler:
             table[i, :len(pages)] = pages
             table[i, len(pages):] = pages[-1] if pages else 0  # (past the prompt: never used)
         dev = self.dev
-        bufs = {
-            "seq_start": torch.from_numpy(starts).to(dev),
-            "embeds": torch.from_numpy(emb.view(np.int16)).to(dev),
-            "page_table": torch.from_numpy(table).to(dev),
-            "kv_len": torch.zeros(n, dtype=torch.int32, device=dev),
-            "logits0": torch.zeros((n, d.talker_vocab), dtype=torch.float32, device=dev),
-            "tok0": torch.zeros(n, dtype=torch.int32, device=dev),
-            "h_last": torch.zeros((n, d.talker.hidden), dtype=torch.int16, device=dev),
-            "status": torch.zeros(1, dtype=torch.int32, device=dev),
-        }
-        ws_bytes = qt_prefill_workspace_bytes(self.pm.cfg, rows, n)
-        ws_buf, ws_ptr = _aligned(torch, ws_bytes, dev)
-        args = PrefillArgs(rows, n, bufs["seq_start"].data_ptr(), bufs["embeds"].data_ptr(),
-                           bufs["page_table"].data_ptr(), self.max_pages, bufs["kv_len"].data_ptr(),
-                           bufs["logits0"].data_ptr(), bufs["tok0"].data_ptr(),
-                           bufs["h_last"].data_ptr(), bufs["status"].data_ptr())
-        qt_prefill(self.pm.handle, args, self.kv, ws_ptr, ws_bytes, self.stream.cuda_stream)
+        with torch.cuda.stream(self.stream):  # the copies, the call and its steps share one stream
+            bufs = {
+                "seq_start": torch.from_numpy(starts).to(dev),
+                "embeds": torch.from_numpy(emb.view(np.int16)).to(dev),
+                "page_table": torch.from_numpy(table).to(dev),
+                "kv_len": torch.zeros(n, dtype=torch.int32, device=dev),
+                "logits0": torch.zeros((n, d.talker_vocab), dtype=torch.float32, device=dev),
+                "tok0": torch.zeros(n, dtype=torch.int32, device=dev),
+                "h_last": torch.zeros((n, d.talker.hidden), dtype=torch.int16, device=dev),
+                "status": torch.zeros(1, dtype=torch.int32, device=dev),
+            }
+            ws_bytes = qt_prefill_workspace_bytes(self.pm.cfg, rows, n)
+            ws_buf, ws_ptr = _aligned(torch, ws_bytes, dev)
+            args = PrefillArgs(rows, n, bufs["seq_start"].data_ptr(), bufs["embeds"].data_ptr(),
+                               bufs["page_table"].data_ptr(), self.max_pages,
+                               bufs["kv_len"].data_ptr(), bufs["logits0"].data_ptr(),
+                               bufs["tok0"].data_ptr(), bufs["h_last"].data_ptr(),
+                               bufs["status"].data_ptr())
+            qt_prefill(self.pm.handle, args, self.kv, ws_ptr, ws_bytes, self.stream.cuda_stream)
         self._held.append((bufs, ws_buf))  # alive until the next step is enqueued
         return bufs["logits0"], bufs["tok0"], bufs["h_last"], bufs["status"]
 
