@@ -424,8 +424,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build runs on exactly one GPU (sessions shard across GPUs with no "
-              "communication; multi-GPU runs are not part of it)", file=sys.stderr)
+        print("bench.py: runs on exactly one GPU (sessions would shard across GPUs with no "
+              "communication; runs on several GPUs are not implemented)", file=sys.stderr)
         sys.exit(2)
 
     import torch

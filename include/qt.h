@@ -65,7 +65,7 @@ typedef enum {
   QT_E_CAPACITY = 6,          /* a buffer smaller than required, or a batch above the workspace's */
   QT_E_STATE = 7,             /* the handle is not usable for this call */
   QT_E_HIP = 8,               /* a HIP runtime call failed; see qt_last_error() */
-  QT_E_UNSUPPORTED = 9        /* a valid request this build does not implement */
+  QT_E_UNSUPPORTED = 9        /* a valid request the library does not implement */
 } qt_status;
 
 typedef enum { QT_BF16 = 0, QT_F32 = 1, QT_I8 = 2, QT_I32 = 3 } qt_dtype;
@@ -98,7 +98,7 @@ typedef struct {
   int32_t code_vocab;   /* rows of each predictor embedding and head (2048) */
   int32_t cb0_range;    /* codebook-0 argmax runs over [0, cb0_range) (2048) */
   int32_t n_codebooks;  /* 1 Talker codebook + (n_codebooks - 1) predictor steps, 2..16 */
-  int32_t page_size;    /* Talker KV page size in positions; this build: 16 */
+  int32_t page_size;    /* Talker KV page size in positions; the library supports 16 */
 } qt_model_cfg;
 
 /* A named source tensor for qt_load_weights: device pointer, bf16, [rows, cols];

@@ -203,7 +203,7 @@ qt_status check_decoder(const qt_decoder_cfg& d, const char* which) {
   if (d.layers < 1 || d.layers > 256)
     return fail(QT_E_SHAPE, "%s.layers = %d: expected 1..256", which, d.layers);
   if (d.head_dim != kHeadDim)
-    return fail(QT_E_SHAPE, "%s.head_dim = %d: this build supports 128", which, d.head_dim);
+    return fail(QT_E_SHAPE, "%s.head_dim = %d: the library supports 128", which, d.head_dim);
   if (d.n_kv_heads < 1 || d.n_q_heads != 2 * d.n_kv_heads)
     return fail(QT_E_SHAPE, "%s: n_q_heads (%d) must be 2 * n_kv_heads (%d)", which, d.n_q_heads,
                 d.n_kv_heads);
@@ -232,7 +232,7 @@ qt_status check_cfg(const qt_model_cfg* c) {
   if (c->n_codebooks < 2 || c->n_codebooks > 16)
     return fail(QT_E_SHAPE, "n_codebooks = %d: expected 2..16", c->n_codebooks);
   if (c->page_size != kPage)
-    return fail(QT_E_SHAPE, "page_size = %d: this build supports 16", c->page_size);
+    return fail(QT_E_SHAPE, "page_size = %d: the library supports 16", c->page_size);
   return ok();
 }
 
@@ -354,7 +354,7 @@ qt_status check_frame_args(const qt_model* m, const qt_sessions* ss, const qt_kv
     return fail(QT_E_INVALID_ARG, "mode = %d is not a qt_mode", in->mode);
   if (ss->batch < 1) return fail(QT_E_INVALID_ARG, "batch = %d: expected >= 1", ss->batch);
   if (ss->batch > kMaxBatch)
-    return fail(QT_E_UNSUPPORTED, "batch = %d: this build decodes at most %d sessions per call",
+    return fail(QT_E_UNSUPPORTED, "batch = %d: the library decodes at most %d sessions per call",
                 ss->batch, kMaxBatch);
   if (!out->tokens || !out->status) return fail(QT_E_INVALID_ARG, "outputs.tokens/status is NULL");
   const bool talker = in->mode != QT_MODE_PREDICTOR;
@@ -1021,7 +1021,7 @@ qt_status qt_workspace_bytes(const qt_model_cfg* cfg, int32_t max_batch, int32_t
   if (max_batch < 1 || max_pages < 1)
     return fail(QT_E_INVALID_ARG, "max_batch and max_pages must be >= 1");
   if (max_batch > kMaxBatch)
-    return fail(QT_E_UNSUPPORTED, "max_batch = %d: this build decodes at most %d sessions per call",
+    return fail(QT_E_UNSUPPORTED, "max_batch = %d: the library decodes at most %d sessions per call",
                 max_batch, kMaxBatch);
   *bytes = make_ws(*cfg, max_batch, max_pages).total;
   return ok();
