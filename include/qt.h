@@ -84,7 +84,7 @@ typedef enum {
 #define QT_STATUS_BAD_SAMPLER 16u /* sampler parameters out of range: that draw was greedy */
 
 /* One decoder stack (Qwen3-style: pre-norm, q/k RMSNorm, rotate-half RoPE,
- * grouped-query attention, SwiGLU).  This build supports head_dim = 128,
+ * grouped-query attention, SwiGLU).  The library supports head_dim = 128,
  * n_q_heads = 2 * n_kv_heads, hidden, n_q_heads*head_dim and ffn multiples
  * of 512. */
 typedef struct {
