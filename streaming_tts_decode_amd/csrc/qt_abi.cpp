@@ -247,6 +247,24 @@ struct Ws {
 
 int key_blocks(int range) { return (range + kKeyBlock - 1) / kKeyBlock; }
 
+// Split-KV shape of the Talker attention: about 1024 blocks over the page table,
+// 4 to 8 pages each (fewer pages per split leave the last block of a session-head
+// too many partials to merge: at B = 1, 4 pages per split took 8.3 us a layer,
+// 1 page 12.2).  The workspace holds partials for the most splits any batch size
+// can take (4 pages each), so a workspace sized for B sessions serves every
+// smaller batch too.
+constexpr int kMinPagesPerSplit = 4;
+struct AttnSplit {
+  int pps, n_splits;
+};
+AttnSplit attn_split(int B, int n_kv, int max_pages) {
+  const int raw = (B * n_kv * max_pages + 1023) / 1024;
+  AttnSplit s;
+  s.pps = raw < kMinPagesPerSplit ? kMinPagesPerSplit : (raw > kMaxPagesPerSplit ? kMaxPagesPerSplit : raw);
+  s.n_splits = (max_pages + s.pps - 1) / s.pps;
+  return s;
+}
+
 // Residual rows carry sums of squares per producing 16-row block, so hidden/16
 // slots per row.  Activation buffers are chunked [cols/8][rows][8] with rows = B
 // (Talker) or 2B (predictor, whose step 1 carries two positions per session).
@@ -278,7 +296,8 @@ Ws make_ws(const qt_model_cfg& c, int B, int max_pages) {
   w.pk_sess = (long long)p.layers * c.n_codebooks * p.n_kv_heads * p.head_dim;
   w.pk = take((size_t)B * w.pk_sess * 2);
   w.pv = take((size_t)B * w.pk_sess * 2);
-  w.part = take((size_t)B * t.n_q_heads * (size_t)max_pages * (kHeadDim + 2) * 4);
+  const int max_splits = (max_pages + kMinPagesPerSplit - 1) / kMinPagesPerSplit;
+  w.part = take((size_t)B * t.n_q_heads * (size_t)max_splits * (kHeadDim + 2) * 4);
   w.cnt = take((size_t)B * t.n_kv_heads * 4);
   w.cand_ld = key_blocks(c.cb0_range) > key_blocks(c.code_vocab) ? key_blocks(c.cb0_range)
                                                                   : key_blocks(c.code_vocab);
@@ -557,12 +576,8 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
   GemmArgs head = gemm_act(m, m->plan.t_head, ut, ld_t, B, out->status);
 
   if (talker) {
-    // pages per split: about 1024 blocks over the page table, 4 to 8 pages each
-    // (fewer pages per split leave the last block of a session-head too many
-    // partials to merge: at B = 1, 4 pages per split took 8.3 us a layer, 1 page 12.2)
-    const int pps_raw = (B * T.n_kv_heads * max_pages + 1023) / 1024;
-    const int pps = pps_raw < 4 ? 4 : (pps_raw > kMaxPagesPerSplit ? kMaxPagesPerSplit : pps_raw);
-    const int n_splits = (max_pages + pps - 1) / pps;
+    const AttnSplit split = attn_split(B, T.n_kv_heads, max_pages);
+    const int pps = split.pps, n_splits = split.n_splits;
     const size_t layer_elems = (size_t)kv->num_pages * T.n_kv_heads * kPage * kHeadDim;
     for (int l = 0; l < T.layers; ++l) {
       cur_layer = l;
