@@ -53,11 +53,13 @@ def pmc_traffic(workload: str, kernel: str):
     return e["bytes_per_launch"]
 
 
-def weight_bytes(d, int8: bool, distinct: bool = False) -> int:
+def weight_bytes(d, int8: bool, distinct: bool = False, mode: str = "full") -> int:
     """Logical weight bytes one frame streams: every decode GEMM weight once per
     use for the whole batch (predictor layers once per predictor step).  With
     distinct=True, every matrix once per frame: the predictor's layers, which all
-    15 steps share, are counted once (the stricter lower bound)."""
+    15 steps share, are counted once (the stricter lower bound).
+    mode "talker": the Talker layers, its final gain and the codec head only;
+    mode "predictor": the projection and the predictor steps only."""
     def mat(n, k):
         return n * k + 4 * n if int8 else 2 * n * k
 
@@ -66,13 +68,19 @@ def weight_bytes(d, int8: bool, distinct: bool = False) -> int:
                 + mat(2 * x.ffn, x.hidden) + mat(x.hidden, x.ffn)
                 + 2 * (2 * x.hidden + 2 * x.head_dim))
     t, p = d.talker, d.predictor
-    talker = t.layers * layer(t) + mat(d.talker_vocab + p.hidden, t.hidden) + 2 * t.hidden
-    pred_layers = p.layers * layer(p)
-    pred_own = mat(d.code_vocab, p.hidden) + 2 * p.hidden  # each step's head and final gain
-    return talker + (1 if distinct else d.n_steps) * pred_layers + d.n_steps * pred_own
+    head_rows = {"full": d.talker_vocab + p.hidden, "talker": d.talker_vocab,
+                 "predictor": p.hidden}[mode]
+    total = mat(head_rows, t.hidden)  # codec head and / or projection rows
+    if mode != "predictor":
+        total += t.layers * layer(t) + 2 * t.hidden
+    if mode != "talker":
+        pred_layers = p.layers * layer(p)
+        pred_own = mat(d.code_vocab, p.hidden) + 2 * p.hidden  # each step's head and final gain
+        total += (1 if distinct else d.n_steps) * pred_layers + d.n_steps * pred_own
+    return total
 
 
-def frame_bytes(d, lengths, int8: bool, distinct: bool = False) -> int:
+def frame_bytes(d, lengths, int8: bool, distinct: bool = False, mode: str = "full") -> int:
     """Algorithmic bytes of one frame: weights (above) plus, per session, the
     Talker K/V read over positions 0..L (L = cached length before the frame), the
     appended K/V, the embedding rows, the input and the fp32 logits and tokens."""
@@ -80,10 +88,12 @@ def frame_bytes(d, lengths, int8: bool, distinct: bool = False) -> int:
     kv_pos = t.layers * t.n_kv * t.head_dim * 2 * 2  # K and V, bf16, all layers
     per_sess = 0
     for L in lengths:
-        per_sess += kv_pos * (int(L) + 1) + kv_pos
-        per_sess += d.n_steps * d.predictor.hidden * 2 + t.hidden * 2
-        per_sess += 4 * (d.talker_vocab + d.n_steps * d.code_vocab) + 4 * d.n_codebooks
-    return weight_bytes(d, int8, distinct) + per_sess
+        per_sess += 4 * d.n_codebooks + t.hidden * 2  # tokens; Talker input or h_in
+        if mode != "predictor":
+            per_sess += kv_pos * (int(L) + 1) + kv_pos + 4 * d.talker_vocab
+        if mode != "talker":
+            per_sess += d.n_steps * (d.predictor.hidden * 2 + 4 * d.code_vocab)
+    return weight_bytes(d, int8, distinct, mode) + per_sess
 
 
 def launch_bytes(d, kind, li, lengths, int8: bool) -> int:
@@ -248,13 +258,24 @@ def run_workload(pm, w, steps, warmup, log, n_trace=0, extras=False):
     frames = max(w.frames, steps + warmup + n_trace)
     wcap = dataclasses.replace(w, frames=frames)
     dec, lengths = setup_workload(wcap, pm)
-    ins = synth.frame_inputs(w)["talker_in"]  # [w.frames, B, H]
-    talker_all = torch.from_numpy(ins.view(np.int16)).to(dec.dev)
-    g = dec.capture("full", forced=False)
+    fin = synth.frame_inputs(w)
+    if w.mode == "predictor":  # the post-norm Talker hidden and codebook-0 token per frame
+        h_all = torch.from_numpy(fin["h_in"].view(np.int16)).to(dec.dev)
+        tok_all = torch.from_numpy(fin["tok0"]).to(dec.dev)
+
+        def feed(f):
+            dec.h_in.copy_(h_all[f % w.frames], non_blocking=True)
+            dec.tok0_in.copy_(tok_all[f % w.frames], non_blocking=True)
+    else:
+        talker_all = torch.from_numpy(fin["talker_in"].view(np.int16)).to(dec.dev)  # [frames, B, H]
+
+        def feed(f):
+            dec.talker_in.copy_(talker_all[f % w.frames], non_blocking=True)
+    g = dec.capture(w.mode, forced=False)
     L0 = dec.kv_len.clone()
     stream = torch.cuda.current_stream()
     for f in range(warmup):
-        dec.talker_in.copy_(talker_all[f % w.frames], non_blocking=True)
+        feed(f)
         dec.replay(g)
     torch.cuda.synchronize()
     dec.kv_len.copy_(L0)
@@ -265,7 +286,7 @@ def run_workload(pm, w, steps, warmup, log, n_trace=0, extras=False):
     t0 = time.perf_counter()
     ev0.record(stream)
     for f in range(steps):
-        dec.talker_in.copy_(talker_all[f % w.frames], non_blocking=True)
+        feed(f)
         dec.replay(g)
     ev1.record(stream)
     torch.cuda.synchronize()
@@ -274,8 +295,10 @@ def run_workload(pm, w, steps, warmup, log, n_trace=0, extras=False):
     status = int(dec.status.item())
     if status:
         raise RuntimeError(f"{w.name}: device status {status:#x}")
-    nbytes = sum(frame_bytes(w.dims, lengths + f, pm.int8) for f in range(steps))
-    nbytes_distinct = sum(frame_bytes(w.dims, lengths + f, pm.int8, distinct=True) for f in range(steps))
+    adv = 0 if w.mode == "predictor" else 1  # cached lengths advance once per frame
+    nbytes = sum(frame_bytes(w.dims, lengths + adv * f, pm.int8, mode=w.mode) for f in range(steps))
+    nbytes_distinct = sum(frame_bytes(w.dims, lengths + adv * f, pm.int8, distinct=True, mode=w.mode)
+                          for f in range(steps))
     per, traced_ms = (trace_frames(dec, w.dims, lengths + steps, n_trace, pm.int8, log)
                       if n_trace else (None, None))
     # repeated sequences (outside the timed region above): the workload's own frame
@@ -376,11 +399,33 @@ def calibration_copy(log):
     del src, dst
 
 
+def host_cpu() -> dict:
+    """The host's CPU model name (first "model name" of /proc/cpuinfo), the logical
+    CPUs it has and the ones this process may run on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count(), "affinity": len(os.sched_getaffinity(0))}
+
+
 def cpu_baseline(w, weights, seconds: float, log):
-    """The oracle, as it stands, on the host cores: session 0 of the workload,
-    consecutive frames until `seconds` of CPU work have run."""
+    """The oracle, as it stands, on the host cores, compiled for this host
+    (gcc -O3 -march=native -fopenmp, no fast-math or contraction: the same results
+    as the portable build the tests use):
+      * session 0 of the workload, consecutive full frames until `seconds` of
+        wall time have run, with every OpenMP thread (the headline baseline);
+      * on one thread: one predictor-only frame (the C1 workload) and one Talker
+        step over 256 cached positions (the C2 workload), the per-core rates."""
     import oracle
     import synth
+    flags = oracle.use_native_build()
+    threads = oracle.max_threads()
     d = w.dims
     t = d.talker
     orc = oracle.OracleModel(d, weights, int8=w.int8)
@@ -394,10 +439,29 @@ def cpu_baseline(w, weights, seconds: float, log):
         _, length = orc.frame("full", kc, vc, length, talker_in=oracle.bf16_to_f64(ins[n]))
         n += 1
     el = time.perf_counter() - t0
-    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    res = {"value": n / el, "unit": "codec frames/s", "cores": cores, "kind": "oracle",
-           "sample": f"{w.name} session 0 (L={L}), {n} consecutive full frames, float64 C oracle, "
-                     f"{el:.1f} s"}
+    one = {}
+    oracle.set_threads(1)
+    try:
+        c1 = synth.WORKLOADS["C1"]
+        f1 = synth.frame_inputs(c1)
+        t1 = time.perf_counter()
+        orc.frame("predictor", h_in=oracle.bf16_to_f64(f1["h_in"][0, 0]), tok0=int(f1["tok0"][0, 0]))
+        one["C1_predictor_frames_per_s"] = 1.0 / (time.perf_counter() - t1)
+        c2 = synth.WORKLOADS["C2"]
+        L2 = int(c2.lengths()[0])
+        kb2, vb2 = synth.gen_kv(c2.name, 0, t.layers, L2, t.n_kv, t.head_dim)
+        kc2, vc2 = orc.new_cache(L2 + 1, kb2, vb2)
+        x2 = synth.frame_inputs(c2)["talker_in"][0, 0]
+        t2 = time.perf_counter()
+        orc.frame("talker", kc2, vc2, L2, talker_in=oracle.bf16_to_f64(x2))
+        one["C2_talker_steps_per_s"] = 1.0 / (time.perf_counter() - t2)
+    finally:
+        oracle.set_threads(threads)
+    res = {"value": n / el, "unit": "codec frames/s", "cores": threads, "kind": "oracle",
+           "sample": f"{w.name} session 0 (L={L}), {n} consecutive full frames on {threads} "
+                     f"threads, float64 C oracle, {el:.1f} s",
+           "threads": threads, **host_cpu(), "compiler": "gcc " + " ".join(flags),
+           "one_thread": one}
     log(f"[cpu] {res}")
     return res
 
@@ -409,6 +473,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="C4")
     ap.add_argument("--also", default="B1,C3", help="extra workloads reported beside the headline")
+    ap.add_argument("--parts", default="C1,C2",
+                    help="the predictor-only frame and the Talker step, timed on their own")
     ap.add_argument("--int8", action="store_true", help="INT8 weight-only decode")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -457,6 +523,17 @@ def main():
         r, _ = run_workload(pm, w, args.steps, args.warmup, log)
         extra[f"B{w.batch}"] = {k: r[k] for k in ("codec_frames_per_s", "ms_per_frame",
                                                   "hbm_gbs_algorithmic", "hbm_frac", "hbm_frac_distinct")}
+    # the predictor-only frame (C1) and the Talker step (C2), each at B = 1 from its
+    # own graph: frames (or Talker steps) per second and their algorithmic HBM rate
+    parts = {}
+    for name in [x for x in args.parts.split(",") if x]:
+        w = dataclasses.replace(synth.WORKLOADS[name], int8=head.int8)
+        r, _ = run_workload(pm, w, args.steps, args.warmup, log)
+        unit = "Talker steps/s" if w.mode == "talker" else "predictor frames/s"
+        parts[name] = {"note": w.note, "per_s": r["codec_frames_per_s"], "unit": unit,
+                       "ms_per_call": r["ms_per_frame"], "bytes_per_call": r["bytes_per_frame"],
+                       "hbm_gbs_algorithmic": r["hbm_gbs_algorithmic"], "hbm_frac": r["hbm_frac"],
+                       "hbm_frac_distinct": r["hbm_frac_distinct"]}
     prefill = None if args.no_prefill else run_prefill(pm, d, log)
     pm.close()
     int8 = None
@@ -485,7 +562,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8" if head.int8 else "bf16",
+        "dtype": ("int8 source weights quantized per row, fp16 operands, fp32 accumulate"
+                  if head.int8 else "bf16 source weights, fp16 operands, fp32 accumulate"),
         "data": "synthetic: seeded N(0,0.02) bf16 weights, N(0,1) inputs and prefilled KV",
         "config": {"workload": f"{head.name}: {head.note}", "batch": head.batch,
                    "kv_len": f"{head.len_lo}..{head.len_hi} (ragged, 16-token pages)",
@@ -496,6 +574,7 @@ def main():
         "frame_hbm_frac_distinct": main_res["hbm_frac_distinct"],
         "bytes_per_frame": main_res["bytes_per_frame"],
         "other_batches": extra,
+        "parts": parts,
         "scheduler": main_res.get("scheduler"),
         "sampled": main_res.get("sampled"),
         "sequences": main_res.get("sequences"),

@@ -25,15 +25,43 @@ MODE_FULL, MODE_TALKER, MODE_PREDICTOR = 0, 1, 2
 _MODES = {"full": MODE_FULL, "talker": MODE_TALKER, "predictor": MODE_PREDICTOR}
 
 
-def build(force: bool = True) -> str:
-    """Compile the oracle with gcc (portable x86-64 code, no fast-math)."""
-    if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp"
-        cmd = ["gcc", "-std=c99", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall",
-               "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp, "-lm"]
+# The portable build (tests, smoke) and the timing build of the CPU baseline, which
+# is compiled for the host it runs on.  Neither contracts or reorders floating-point
+# operations (-ffp-contract=off, no fast-math), so both give the same results.
+FLAGS = ["-std=c99", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall", "-fno-fast-math",
+         "-ffp-contract=off"]
+NATIVE_FLAGS = ["-std=c99", "-O3", "-march=native", "-fopenmp", "-fPIC", "-shared", "-Wall",
+                "-fno-fast-math", "-ffp-contract=off"]
+_NATIVE_LIB = os.path.join(_HERE, "liborc_native.so")
+
+
+def build(force: bool = True, native: bool = False) -> str:
+    """Compile the oracle with gcc (no fast-math): portable x86-64 code, or with
+    native=True the timing build for this host (-O3 -march=native)."""
+    out = _NATIVE_LIB if native else _LIB
+    if force or not os.path.exists(out):
+        tmp = out + ".tmp"
+        cmd = ["gcc"] + (NATIVE_FLAGS if native else FLAGS) + [_SRC, "-o", tmp, "-lm"]
         subprocess.run(cmd, check=True)
-        os.replace(tmp, _LIB)
-    return _LIB
+        os.replace(tmp, out)
+    return out
+
+
+def use_native_build() -> list:
+    """Build the timing oracle for this host and route every later oracle call
+    through it (the CPU baseline of the benchmark).  Returns its gcc flags."""
+    global _LIB, _lib
+    _LIB = build(force=True, native=True)
+    _lib = None
+    return NATIVE_FLAGS
+
+
+def max_threads() -> int:
+    return int(lib().orc_max_threads())
+
+
+def set_threads(n: int) -> None:
+    lib().orc_set_threads(int(n))
 
 
 # ---------------------------------------------------------------- ctypes types
@@ -76,6 +104,10 @@ def lib():
         if not os.path.exists(_LIB):
             build(force=False)
         L = C.CDLL(_LIB)
+        L.orc_max_threads.restype = C.c_int32
+        L.orc_max_threads.argtypes = []
+        L.orc_set_threads.restype = None
+        L.orc_set_threads.argtypes = [C.c_int32]
         L.orc_bf16_to_f64.restype = C.c_double
         L.orc_bf16_to_f64.argtypes = [C.c_uint16]
         L.orc_rmsnorm.argtypes = [_dp, C.c_void_p, C.c_int32, C.c_double, _dp]

@@ -25,8 +25,14 @@
 #include "qt_oracle.h"
 
 #include <math.h>
+#include <omp.h>
 #include <stdlib.h>
 #include <string.h>
+
+/* Thread count of the OpenMP loops, for timing the oracle (results do not depend
+ * on it: every dot product is summed by one thread in index order). */
+int32_t orc_max_threads(void) { return (int32_t)omp_get_max_threads(); }
+void orc_set_threads(int32_t n) { omp_set_num_threads(n > 0 ? n : 1); }
 
 double orc_bf16_to_f64(uint16_t h) {
   uint32_t u = (uint32_t)h << 16;
