@@ -256,6 +256,23 @@ qt_status qt_frame_decode(qt_model* model, const qt_sessions* sessions, const qt
                           const qt_frame_inputs* in, const qt_frame_outputs* out, void* workspace,
                           uint64_t workspace_bytes, void* stream);
 
+/* The same frame as qt_frame_decode, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the per-frame scratch is a static array of QT_NOALLOC_SCRATCH_BYTES
+ * bytes inside the library, one per GPU, held until the process ends, instead of a
+ * caller workspace.  Nothing is allocated or freed by this call.  A batch whose
+ * workspace (qt_workspace_bytes(cfg, batch, max_pages)) exceeds that size is refused
+ * with QT_E_CAPACITY before anything is enqueued: 32 sessions with page tables of up
+ * to 256 pages (4096 positions) fit.  Every call on one GPU shares that GPU's array:
+ * calls whose frames overlap on the device (other streams, or other threads) race
+ * and give wrong results; calls enqueued in order on one stream do not.  The frame
+ * clears what it needs cleared itself, so nothing from an earlier call leaks in.
+ * Arguments, outputs and errors are otherwise those of qt_frame_decode. */
+#define QT_NOALLOC_SCRATCH_BYTES (32u << 20)
+qt_status qt_frame_decode_noalloc(qt_model* model, const qt_sessions* sessions,
+                                  const qt_kv_caches* kv, const qt_frame_inputs* in,
+                                  const qt_frame_outputs* out, void* stream);
+
 /* Capture the same frame as qt_frame_decode into a HIP graph and instantiate it.  The
  * graph bakes in every pointer and the batch size: the caller keeps all buffers alive
  * and at the same addresses until qt_graph_destroy, and changes per-frame data only by

@@ -22,11 +22,13 @@ MODE_FULL, MODE_TALKER, MODE_PREDICTOR = 0, 1, 2
 MODES = {"full": MODE_FULL, "talker": MODE_TALKER, "predictor": MODE_PREDICTOR}
 STATUS_KV_OVERFLOW, STATUS_BAD_PAGE, STATUS_BAD_TOKEN, STATUS_NAN = 1, 2, 4, 8
 STATUS_BAD_SAMPLER = 16
+NOALLOC_SCRATCH_BYTES = 32 << 20
 SAMPLER_MAX_TOP_K = 64
 
 EXPORTED = ["qt_last_error", "qt_abi_version", "qt_validate_cfg", "qt_packed_bytes",
             "qt_workspace_bytes", "qt_load_weights", "qt_quantize_int8", "qt_model_export_int8",
-            "qt_frame_decode", "qt_frame_graph_create", "qt_frame_graph_launch",
+            "qt_frame_decode", "qt_frame_decode_noalloc", "qt_frame_graph_create",
+            "qt_frame_graph_launch",
             "qt_graph_destroy", "qt_model_destroy", "qt_trace_create", "qt_frame_launch_count",
             "qt_frame_trace", "qt_trace_read", "qt_trace_destroy",
             "qt_prefill_workspace_bytes", "qt_prefill", "qt_prefill_graph_create", "qt_sample",
@@ -157,6 +159,8 @@ def lib():
                       C.POINTER(FrameOutputs), _P, C.c_uint64]
         L.qt_frame_decode.restype = st
         L.qt_frame_decode.argtypes = frame_args + [_P]
+        L.qt_frame_decode_noalloc.restype = st
+        L.qt_frame_decode_noalloc.argtypes = frame_args[:5] + [_P]
         L.qt_frame_graph_create.restype = st
         L.qt_frame_graph_create.argtypes = frame_args + [C.POINTER(_P)]
         L.qt_frame_graph_launch.restype = st
@@ -295,6 +299,13 @@ def qt_frame_decode(model: int, sessions: Sessions, kv: KvCaches, inputs: FrameI
     _check(lib().qt_frame_decode(model, C.byref(sessions), C.byref(kv), C.byref(inputs),
                                  C.byref(outputs), workspace_ptr, workspace_bytes, stream),
            "qt_frame_decode")
+
+
+def qt_frame_decode_noalloc(model: int, sessions: Sessions, kv: KvCaches, inputs: FrameInputs,
+                            outputs: FrameOutputs, stream: int = 0) -> None:
+    """qt_frame_decode with the library's static scratch instead of a workspace."""
+    _check(lib().qt_frame_decode_noalloc(model, C.byref(sessions), C.byref(kv), C.byref(inputs),
+                                         C.byref(outputs), stream), "qt_frame_decode_noalloc")
 
 
 def qt_frame_graph_create(model: int, sessions: Sessions, kv: KvCaches, inputs: FrameInputs,

@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include <map>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -1010,6 +1011,40 @@ qt_status report(qt_status st, const char* fmt, ...) {
 }
 }  // namespace qt
 
+// ------------------------------------------------------------------ allocation-free frames
+// qt_frame_decode_noalloc runs the frame in this file-scope device array instead of
+// a caller workspace.  Every GPU the library runs on holds its own copy, at its own
+// address, until the process ends.  In host code `scratch` only names a host-side
+// stand-in: its device address comes from hipGetSymbolAddress, taken once per device
+// with that device current, and only that address is ever passed on.
+constexpr size_t kNoallocScratchBytes = QT_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kNoallocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices] = {};
+
+qt_status noalloc_scratch(void** out) {
+  int dev = -1;
+  QT_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(QT_E_UNSUPPORTED, "device %d: the allocation-free frame supports devices 0..%d", dev,
+                kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(QT_E_HIP, "hipGetSymbolAddress(scratch) on device %d failed: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return ok();
+}
+}  // namespace
+
 // ------------------------------------------------------------------ exported
 extern "C" {
 
@@ -1164,6 +1199,31 @@ qt_status qt_frame_decode(qt_model* model, const qt_sessions* sessions, const qt
   qt_status st = check_frame_args(model, sessions, kv, in, out, workspace, workspace_bytes);
   if (st) return st;
   return enqueue_frame(model, sessions, kv, in, out, workspace, (hipStream_t)stream);
+}
+
+qt_status qt_frame_decode_noalloc(qt_model* model, const qt_sessions* sessions,
+                                  const qt_kv_caches* kv, const qt_frame_inputs* in,
+                                  const qt_frame_outputs* out, void* stream) {
+  void* ws = nullptr;
+  qt_status st = noalloc_scratch(&ws);
+  if (st) return st;
+  if (model && sessions && in && sessions->batch >= 1 && sessions->batch <= kMaxBatch &&
+      in->mode >= QT_MODE_FULL && in->mode <= QT_MODE_PREDICTOR) {
+    const int mp = in->mode != QT_MODE_PREDICTOR ? sessions->max_pages : 1;
+    if (mp >= 1) {
+      const size_t need = make_ws(model->cfg, sessions->batch, mp).total;
+      if (need > kNoallocScratchBytes)
+        return fail(QT_E_CAPACITY,
+                    "qt_frame_decode_noalloc: %d sessions with %d-page tables need %llu bytes of "
+                    "scratch; the library's static scratch holds %llu (qt_frame_decode takes a "
+                    "caller workspace of any size)",
+                    sessions->batch, mp, (unsigned long long)need,
+                    (unsigned long long)kNoallocScratchBytes);
+    }
+  }
+  st = check_frame_args(model, sessions, kv, in, out, ws, kNoallocScratchBytes);
+  if (st) return st;
+  return enqueue_frame(model, sessions, kv, in, out, ws, (hipStream_t)stream);
 }
 
 qt_status qt_frame_graph_create(qt_model* model, const qt_sessions* sessions, const qt_kv_caches* kv,

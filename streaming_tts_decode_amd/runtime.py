@@ -13,7 +13,8 @@ import numpy as np
 
 from . import (KERNEL_KINDS, FrameInputs, FrameOutputs, KvCaches, MODES, QT_BF16, PrefillArgs,
                Sampling, Sessions, qt_prefill, qt_prefill_graph_create, qt_prefill_workspace_bytes,
-               make_cfg, make_sched_cfg, qt_frame_decode, qt_frame_graph_create,
+               make_cfg, make_sched_cfg, qt_frame_decode, qt_frame_decode_noalloc,
+               qt_frame_graph_create,
                qt_frame_graph_launch, qt_frame_launch_count, qt_frame_trace, qt_graph_destroy,
                qt_load_weights, qt_model_destroy, qt_packed_bytes, qt_sched_bytes, qt_sched_close,
                qt_sched_create, qt_sched_destroy, qt_sched_free_pages, qt_sched_length,
@@ -209,6 +210,13 @@ class Decoder:
         ss, kv, fi, fo = self._descs(mode, forced, batch, sampling, seen)
         qt_frame_decode(self.model, ss, kv, fi, fo, self.ws_ptr, self.ws_bytes,
                         self.torch.cuda.current_stream(self.dev).cuda_stream)
+
+    def decode_noalloc(self, mode: str = "full", forced: bool = False, batch: int | None = None):
+        """The same frame through qt_frame_decode_noalloc: the library's static
+        scratch instead of this decoder's workspace."""
+        ss, kv, fi, fo = self._descs(mode, forced, batch)
+        qt_frame_decode_noalloc(self.model, ss, kv, fi, fo,
+                                self.torch.cuda.current_stream(self.dev).cuda_stream)
 
     # ------------------------------------------------------------------ prompt prefill
     def prefill_setup(self, rows: int):
