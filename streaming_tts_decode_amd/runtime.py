@@ -439,9 +439,15 @@ class Scheduler:
 
     def submit(self, sid: int, talker_in, forced=None):
         """talker_in: device int16 [talker hidden] (bf16 bits); forced: device int32
-        [n_codebooks] or None.  Both are kept alive until the next step is enqueued."""
+        [n_codebooks] or None.  The step reads them on the scheduler's stream, so they
+        are recorded as in use there: the caching allocator does not hand their memory
+        out again until the step that reads them has run, whatever stream the caller
+        allocated them on."""
         qt_sched_submit(self.handle, sid, talker_in.data_ptr(),
                         forced.data_ptr() if forced is not None else None)
+        talker_in.record_stream(self.stream)
+        if forced is not None:
+            forced.record_stream(self.stream)
         self._held.append((talker_in, forced))
 
     def step(self) -> int:

@@ -473,3 +473,49 @@ def test_prefill_into_scheduler_pages_then_steps(small_pm, orc_small):
         log(f"[sched] prefill then steps: worst relative logit error {worst:.3g}")
     finally:
         sch.close()
+
+
+def test_sched_inputs_from_another_stream(small_pm):
+    """Inputs allocated on another stream and dropped by the caller right after
+    submit are still intact when the scheduler's stream reads them: the step is
+    held back behind a busy kernel while the other stream allocates and fills new
+    tensors of the same size, which the caching allocator would otherwise place in
+    the dropped inputs' memory."""
+    from streaming_tts_decode_amd.runtime import Scheduler
+    torch = small_pm.torch
+    lengths = [13, 40]
+    frames, max_pages = 3, 5
+    x, forced = _inputs("sched.stream", frames, len(lengths))
+    kvs = _kv("sched.stream", lengths)
+    sch = Scheduler(small_pm, buckets=(2,), max_sessions=2, max_pages=max_pages)
+    sids = [sch.open(L, *kvs[s]) for s, L in enumerate(lengths)]
+    side = torch.cuda.Stream()
+    got = {s: {"l0": [], "lp": [], "tok": []} for s in range(len(sids))}
+    for f in range(frames):
+        with torch.cuda.stream(sch.stream):
+            torch.cuda._sleep(20_000_000)  # holds the step back (bounded busy loop)
+        with torch.cuda.stream(side):
+            xs = torch.from_numpy(x[f].view(np.int16)).to(sch.dev)
+            fs = torch.from_numpy(forced[f]).to(sch.dev)
+        side.synchronize()
+        for s, sid in enumerate(sids):
+            sch.submit(sid, xs[s], fs[s])
+        del xs, fs
+        sch.step()
+        with torch.cuda.stream(side):  # same sizes, garbage contents
+            junk_x = torch.full((len(lengths), D.talker.hidden), 0x7bff, dtype=torch.int16, device=sch.dev)
+            junk_f = torch.full((len(lengths), D.n_codebooks), 7, dtype=torch.int32, device=sch.dev)
+        torch.cuda.synchronize()
+        del junk_x, junk_f
+        for s, sid in enumerate(sids):
+            l0, lp, tok, n = sch.outputs(sid)
+            assert n == f + 1
+            got[s]["l0"].append(l0.cpu().numpy().copy())
+            got[s]["lp"].append(lp.cpu().numpy().copy())
+            got[s]["tok"].append(tok.cpu().numpy().copy())
+    assert sch.status() == 0
+    sch.close()
+    for s in range(len(lengths)):
+        ref = _plain(small_pm, kvs[s], lengths[s], x[:, s], forced[:, s], max_pages)
+        _agree({k: np.stack(v) for k, v in got[s].items()}, ref, f"session {s}")
+    log("[sched] inputs from another stream intact")
