@@ -83,6 +83,11 @@ int64_t orc_quantize_int8(const uint16_t* w, int64_t rows, int64_t cols, int8_t*
 int32_t orc_stack_forward(const orc_stack* st, double* x, int32_t n_new, int32_t pos0,
                           double* kc, double* vc, int32_t capacity);
 
+/* OpenMP thread count of the oracle's loops (for timing only; results do not
+ * depend on it). */
+int32_t orc_max_threads(void);
+void orc_set_threads(int32_t n);
+
 /* One decode frame for one session.
  *   mode FULL:      talker_in -> Talker at position *len -> logits0, tok0 ->
  *                   projection -> predictor steps 1..n_codebooks-1.
@@ -95,11 +100,6 @@ int32_t orc_stack_forward(const orc_stack* st, double* x, int32_t n_new, int32_t
  *   (FULL/PREDICTOR), tokens [n_cb] (own argmaxes; PREDICTOR copies tok0_in to [0]),
  *   h_out [talker hidden] (optional, FULL/TALKER: the post-norm Talker output).
  * *len is advanced by one in FULL/TALKER mode.  Returns 0 or a negative error. */
-/* OpenMP thread count of the oracle's loops (for timing only; results do not
- * depend on it). */
-int32_t orc_max_threads(void);
-void orc_set_threads(int32_t n);
-
 int32_t orc_frame(const orc_model* m, int32_t mode, const double* talker_in,
                   const double* h_in, int32_t tok0_in, double* kc, double* vc,
                   int32_t capacity, int32_t* len, const int32_t* forced,

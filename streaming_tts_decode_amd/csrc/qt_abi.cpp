@@ -1124,10 +1124,11 @@ qt_status qt_load_weights(const qt_model_cfg* cfg, const qt_tensor* tensors, int
       return fail(QT_E_DTYPE, "tensor '%s' has dtype %d, expected bf16", t.name, t.dtype);
     }
     if (t.rows != it->second.rows || t.cols != it->second.cols) {
+      // (the expected shape lives in the model's table: read it before the model goes)
+      const long long er = (long long)it->second.rows, ec = (long long)it->second.cols;
       delete m;
       return fail(QT_E_SHAPE, "tensor '%s' is [%lld, %lld], expected [%lld, %lld]", t.name,
-                  (long long)t.rows, (long long)t.cols, (long long)it->second.rows,
-                  (long long)it->second.cols);
+                  (long long)t.rows, (long long)t.cols, er, ec);
     }
     if (!t.data) {
       delete m;
