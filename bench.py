@@ -105,6 +105,8 @@ def launch_bytes(d, kind, li, lengths, int8: bool) -> int:
       attn_paged:  per session, this layer's K and V over positions 0..L_b (the cache
                    plus the new one) and the appended pair: 4 * n_kv * head_dim * (L_b + 2).
       embed:       one bf16 embedding row per session.
+      predictor:   the one-launch predictor: every step's layer and head weights, and per
+                   session its embedding rows and f32 logits.
       others:      0 (predictor K/V is frame-local and could stay on chip)."""
     if kind == "gemm":
         w = li.n * li.k + 4 * li.n if li.int8 else 2 * li.n * li.k
@@ -114,6 +116,11 @@ def launch_bytes(d, kind, li, lengths, int8: bool) -> int:
         return int(sum(4 * t.n_kv * t.head_dim * (int(L) + 2) for L in lengths))
     if kind == "embed":
         return li.m * d.predictor.hidden * 2
+    if kind == "predictor":  # every predictor step in one launch: layers and heads per step,
+        p = d.predictor      # each session's embedding rows and logits
+        proj = (p.hidden * d.talker.hidden + 4 * p.hidden) if int8 else 2 * p.hidden * d.talker.hidden
+        return (weight_bytes(d, int8, mode="predictor") - proj
+                + li.m * d.n_steps * (p.hidden * 2 + 4 * d.code_vocab))
     return 0
 
 

@@ -82,6 +82,13 @@ typedef enum {
 #define QT_STATUS_BAD_TOKEN 4u   /* a forced / input token outside the code vocabulary: 0 used */
 #define QT_STATUS_NAN 8u         /* a NaN logit was produced */
 #define QT_STATUS_BAD_SAMPLER 16u /* sampler parameters out of range: that draw was greedy */
+#define QT_STATUS_FP16_RANGE 32u  /* a GEMM input held a finite value beyond the IEEE half range
+                                     (|v| >= 65520): it became +-inf.  GEMM inputs are half(x * gain)
+                                     of the residual rows (before the RMS factor), the SwiGLU
+                                     output and the attention output */
+#define QT_STATUS_SYNC 64u        /* the one-launch code predictor could not synchronise its blocks
+                                     (they were not all resident, or not on the expected XCDs):
+                                     that frame's predictor outputs are not valid */
 
 /* One decoder stack (Qwen3-style: pre-norm, q/k RMSNorm, rotate-half RoPE,
  * grouped-query attention, SwiGLU).  The library supports head_dim = 128,
@@ -203,7 +210,9 @@ typedef struct {
 const char* qt_last_error(void);
 int32_t qt_abi_version(void);
 
-/* Check that the configuration is one the kernels support.  QT_E_SHAPE otherwise. */
+/* Check that the configuration is one the kernels support.  QT_E_SHAPE otherwise.
+ * (This and the two sizing calls below are the library's own memory plan; the pages
+ * describe the engine, not its buffers.) */
 qt_status qt_validate_cfg(const qt_model_cfg* cfg);
 
 /* Bytes of the packed-weight buffer for this configuration (int8_mode 0: bf16, 1: INT8). */
@@ -214,7 +223,10 @@ qt_status qt_packed_bytes(const qt_model_cfg* cfg, int32_t int8_mode, uint64_t* 
 qt_status qt_workspace_bytes(const qt_model_cfg* cfg, int32_t max_batch, int32_t max_pages,
                              uint64_t* bytes);
 
-/* Validate and pack the model weights into the caller's device buffer `packed`
+/* Load the weights ("Qwen3-TTS PR 5", What changed: weight loading checks coverage
+ * in both directions; "Qwen3-TTS Native v0.3.0", What changed: INT8 weight-only decode
+ * is chosen when the engine loads and is quantized from the BF16 weights).
+ * Validate and pack the model weights into the caller's device buffer `packed`
  * (at least qt_packed_bytes bytes, 256-byte aligned).  `tensors` (host array of
  * n_tensors entries) must name every expected weight exactly once with the
  * expected shape and dtype bf16, and nothing else (checked in both directions:
@@ -226,7 +238,13 @@ qt_status qt_workspace_bytes(const qt_model_cfg* cfg, int32_t max_batch, int32_t
  * int8_mode 1 quantizes every decode GEMM weight (attention, FFN, projection, codec
  * head and predictor heads) with qt_quantize_int8's arithmetic; embeddings and norm
  * gains stay bf16.  Packing is enqueued on `stream`; the source tensors may be
- * freed once it has completed.  *out receives a handle for qt_frame_decode. */
+ * freed once it has completed.  *out receives a handle for qt_frame_decode.
+ * Range: in bf16 mode the GEMM weights are packed as IEEE half (exact for
+ * |w| >= 2^-14, within 2^-25 below), so a weight matrix holding a finite entry with
+ * |w| > 65504 is refused with QT_E_UNSUPPORTED naming it; to find out, the call waits
+ * for the packing to finish on `stream` in bf16 mode.  INT8 mode takes any finite
+ * weights.  At decode time the GEMM inputs are half too: a residual row value x with
+ * |x * gain| >= 65520 sets QT_STATUS_FP16_RANGE (see the status bits). */
 qt_status qt_load_weights(const qt_model_cfg* cfg, const qt_tensor* tensors, int32_t n_tensors,
                           int32_t int8_mode, void* packed, uint64_t packed_bytes, void* stream,
                           qt_model** out);
@@ -247,7 +265,18 @@ qt_status qt_quantize_int8(const void* w_bf16, int64_t rows, int64_t cols, int8_
 qt_status qt_model_export_int8(const qt_model* model, const char* name, int8_t* q, float* scale,
                                void* stream);
 
-/* Decode one frame for all sessions (see qt_mode).  Enqueues every kernel of the frame
+/* One lockstep frame ("Qwen3-TTS Native v0.3.0", What changed: one batched call runs
+ * the Talker step and the 15-step code predictor for every active session, every
+ * shared weight read once per frame, per-session state kept request-local;
+ * decomputer.nl article, parts 3 and 5: the predictor always runs its fixed steps on
+ * a preallocated cache, and the decode loop avoids CPU-GPU synchronisation;
+ * qwen.lukaloehr.com llms.txt: the codebook-0 token goes from Talker to predictor on
+ * the device).  The predictor runs as a chain of launches; with QT_PREDICTOR=persistent
+ * in the environment when the model is loaded, greedy and teacher-forced frames of a
+ * model whose predictor has the full-size shapes (hidden 1024, 16 / 8 heads, FFN 3072,
+ * vocabulary 2048) run every predictor step in one launch on a 256-CU device
+ * (QT_KERNEL_PREDICTOR).  Both compute the same definition.
+ * Decode one frame for all sessions (see qt_mode).  Enqueues every kernel of the frame
  * on `stream` and returns without synchronising.  `workspace` is a device buffer of at
  * least qt_workspace_bytes(cfg, B, max_pages) bytes; the caller must not touch it while
  * a frame that uses it is in flight, and concurrent frames need separate workspaces.
@@ -268,12 +297,15 @@ qt_status qt_frame_decode(qt_model* model, const qt_sessions* sessions, const qt
  * and give wrong results; calls enqueued in order on one stream do not.  The frame
  * clears what it needs cleared itself, so nothing from an earlier call leaks in.
  * Arguments, outputs and errors are otherwise those of qt_frame_decode. */
-#define QT_NOALLOC_SCRATCH_BYTES (32u << 20)
+#define QT_NOALLOC_SCRATCH_BYTES (48u << 20)
 qt_status qt_frame_decode_noalloc(qt_model* model, const qt_sessions* sessions,
                                   const qt_kv_caches* kv, const qt_frame_inputs* in,
                                   const qt_frame_outputs* out, void* stream);
 
-/* Capture the same frame as qt_frame_decode into a HIP graph and instantiate it.  The
+/* Frames as graphs ("Qwen3-TTS Native v0.3.0", What changed: the frame is captured
+ * once per session tuple and replayed; decomputer.nl article, part 5: graphs for a
+ * fixed set of batch sizes).
+ * Capture the same frame as qt_frame_decode into a HIP graph and instantiate it.  The
  * graph bakes in every pointer and the batch size: the caller keeps all buffers alive
  * and at the same addresses until qt_graph_destroy, and changes per-frame data only by
  * rewriting buffer contents (inputs, forced tokens, kv_len). */
@@ -282,7 +314,7 @@ qt_status qt_frame_graph_create(qt_model* model, const qt_sessions* sessions,
                                 const qt_frame_outputs* out, void* workspace,
                                 uint64_t workspace_bytes, qt_graph** out_graph);
 
-/* Replay a captured frame on `stream` (enqueue only). */
+/* Replay a captured frame or prefill on `stream` (enqueue only). */
 qt_status qt_frame_graph_launch(qt_graph* graph, void* stream);
 
 void qt_graph_destroy(qt_graph* graph);
@@ -352,7 +384,11 @@ typedef enum {
   QT_KERNEL_ATTN_PAGED = 2,  /* k_attn_paged: Talker q/k-norm, RoPE, KV append, paged attention */
   QT_KERNEL_ATTN_PRED = 3,   /* k_attn_pred: the same over the predictor's frame-local KV */
   QT_KERNEL_EMBED = 4,       /* k_embed: codebook-embedding gather of a predictor step */
-  QT_KERNEL_FRAME_END = 5    /* k_frame_end: tokens out, kv_len advance */
+  QT_KERNEL_FRAME_END = 5,   /* k_frame_end: tokens out, kv_len advance */
+  QT_KERNEL_PREDICTOR = 6    /* k_pred_persist: every code-predictor step of the frame in one
+                                launch (QT_PREDICTOR=persistent; see qt_frame_decode); by
+                                default the predictor runs as QT_KERNEL_EMBED / GEMM /
+                                ATTN_PRED launches */
 } qt_kernel_kind;
 
 typedef struct {

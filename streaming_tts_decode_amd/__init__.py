@@ -22,7 +22,9 @@ MODE_FULL, MODE_TALKER, MODE_PREDICTOR = 0, 1, 2
 MODES = {"full": MODE_FULL, "talker": MODE_TALKER, "predictor": MODE_PREDICTOR}
 STATUS_KV_OVERFLOW, STATUS_BAD_PAGE, STATUS_BAD_TOKEN, STATUS_NAN = 1, 2, 4, 8
 STATUS_BAD_SAMPLER = 16
-NOALLOC_SCRATCH_BYTES = 32 << 20
+STATUS_FP16_RANGE = 32
+STATUS_SYNC = 64
+NOALLOC_SCRATCH_BYTES = 48 << 20
 SAMPLER_MAX_TOP_K = 64
 
 EXPORTED = ["qt_last_error", "qt_abi_version", "qt_validate_cfg", "qt_packed_bytes",
@@ -40,7 +42,7 @@ EXPORTED = ["qt_last_error", "qt_abi_version", "qt_validate_cfg", "qt_packed_byt
 SCHED_MAX_BUCKETS, SCHED_MAX_BATCH, SCHED_MAX_SESSIONS = 8, 32, 4096
 SESSION_FREE, SESSION_RUNNING, SESSION_ENDED_EOS, SESSION_ENDED_MAX = 0, 1, 2, 3
 KERNEL_KINDS = {0: "frame_begin", 1: "gemm", 2: "attn_paged", 3: "attn_pred", 4: "embed",
-                5: "frame_end"}
+                5: "frame_end", 6: "predictor"}
 
 
 class QtError(RuntimeError):

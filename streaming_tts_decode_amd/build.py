@@ -5,7 +5,8 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libqt.so")
-SOURCES = [os.path.join(HERE, "csrc", f) for f in ("qt_kernels.hip", "qt_gemm.hip", "qt_abi.cpp", "qt_sched.cpp")]
+SOURCES = [os.path.join(HERE, "csrc", f) for f in ("qt_kernels.hip", "qt_gemm.hip", "qt_pred.hip", "qt_abi.cpp",
+                                                    "qt_sched.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -5,6 +5,7 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <map>
@@ -84,6 +85,8 @@ struct Plan {
   MatSlot t_head;  // codec head rows [0, talker_vocab) then projection rows
   std::vector<size_t> embeds;
   std::vector<MatSlot> heads;
+  size_t range_flags = 0;  // one word per source GEMM weight: set if it exceeds the half range
+  int n_mats = 0;
   size_t total = 0;
 };
 
@@ -137,6 +140,10 @@ Plan make_plan(const qt_model_cfg& c, bool i8) {
     plan.embeds.push_back(P.vec(c.code_vocab * c.predictor.hidden));
     plan.heads.push_back(P.mat(c.code_vocab, c.predictor.hidden));
   }
+  // q, k, v, o, gate, up, down per layer; codec head, projection, one head per step
+  plan.n_mats = 7 * (c.talker.layers + c.predictor.layers) + 2 + (c.n_codebooks - 1);
+  plan.range_flags = P.off;
+  P.off = align_up(P.off + (size_t)plan.n_mats * 4);
   plan.total = P.off;
   return plan;
 }
@@ -241,6 +248,9 @@ qt_status check_cfg(const qt_model_cfg* c) {
 struct Ws {
   size_t x_t, x_p, ss_t, ss_p, ut, up, qkv, o, ffn, pk, pv, part, cnt,
       cand, total;
+  // the one-launch predictor (pp_ldm > 0): per-XCD rows, partial sums, sync words
+  size_t pp_x, pp_u, pp_ss, pp_qkv, pp_o, pp_f, pp_po, pp_pd, pp_sync;
+  int pp_ldm;
   int qkv_ld, o_ld, f_ld;
   int cand_ld;        // greedy-key candidates per (codebook, session)
   long long pk_sess;  // elements per session in the predictor cache
@@ -264,6 +274,16 @@ AttnSplit attn_split(int B, int n_kv, int max_pages) {
   s.pps = raw < kMinPagesPerSplit ? kMinPagesPerSplit : (raw > kMaxPagesPerSplit ? kMaxPagesPerSplit : raw);
   s.n_splits = (max_pages + s.pps - 1) / s.pps;
   return s;
+}
+
+// Whether a model's predictor has the shapes the one-launch predictor is written
+// for (qt_pred.hip): hidden 1024, 16 query / 8 KV heads of 128, FFN 3072, code
+// vocabulary 2048, at most kPredMaxLayers layers and kPredMaxSteps steps.
+bool pred_persist_shapes(const qt_model_cfg& c) {
+  const qt_decoder_cfg& p = c.predictor;
+  return p.hidden == 1024 && p.n_q_heads == 16 && p.n_kv_heads == 8 && p.head_dim == kHeadDim &&
+         p.ffn == 3072 && c.code_vocab == 2048 && p.layers <= kPredMaxLayers &&
+         c.n_codebooks - 1 <= kPredMaxSteps;
 }
 
 // Residual rows carry sums of squares per producing 16-row block, so hidden/16
@@ -303,6 +323,21 @@ Ws make_ws(const qt_model_cfg& c, int B, int max_pages) {
   w.cand_ld = key_blocks(c.cb0_range) > key_blocks(c.code_vocab) ? key_blocks(c.cb0_range)
                                                                   : key_blocks(c.code_vocab);
   w.cand = take((size_t)c.n_codebooks * B * w.cand_ld * 8);
+  w.pp_ldm = 0;
+  if (pred_persist_shapes(c)) {
+    const int ldm = (2 * B + 15) / 16 * 16;
+    const size_t H = 1024, X = 8;
+    w.pp_ldm = ldm;
+    w.pp_x = take(X * ldm * H * 4);
+    w.pp_u = take(X * ldm * H * 2);
+    w.pp_ss = take(X * 32 * ldm * 4);
+    w.pp_qkv = take(X * ldm * 512 * 4);
+    w.pp_o = take(X * ldm * 256 * 2);
+    w.pp_f = take(X * ldm * 384 * 2);
+    w.pp_po = take(X * ldm * H * 4);
+    w.pp_pd = take(X * ldm * H * 4);
+    w.pp_sync = take((size_t)kPredSyncWords * 4);
+  }
   w.total = off;
   return w;
 }
@@ -313,6 +348,7 @@ Ws make_ws(const qt_model_cfg& c, int B, int max_pages) {
 struct qt_model {
   qt_model_cfg cfg;
   int i8;
+  int pred_persist;  // frames may run the predictor as one launch (shapes, 256 CUs)
   Plan plan;
   std::map<std::string, Dest> dests;
   char* base;  // packed buffer (device)
@@ -514,6 +550,9 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
   fb.cand_ld = cand_ld;
   fb.counters = cnt;
   fb.status = out->status;
+  // the one-launch predictor: greedy or teacher-forced frames of a supported model
+  const bool pp = m->pred_persist && mode != QT_MODE_TALKER && !in->sampling && w.pp_ldm > 0;
+  fb.pred_sync = pp ? (unsigned*)(ws + w.pp_sync) : nullptr;
   QT_MARK(QT_KERNEL_FRAME_BEGIN, "k_frame_begin", B, nullptr);
   QT_LAUNCH(launch_frame_begin(fb, st));
 
@@ -639,7 +678,61 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
     if (s) return s;
   }
 
-  if (mode != QT_MODE_TALKER) {
+  if (pp) {
+    PredPersistArgs a{};
+    a.B = B;
+    a.layers = Pd.layers;
+    a.n_steps = ncb - 1;
+    a.ncb = ncb;
+    a.ldm = w.pp_ldm;
+    a.eps = Pd.rms_eps;
+    a.theta_log2 = (float)log2((double)Pd.rope_theta);
+    for (int l = 0; l < Pd.layers; ++l) {
+      const LayerSlots& L = m->plan.pl[l];
+      a.w_qkv[l] = m->base + L.qkv.w;
+      a.w_o[l] = m->base + L.o.w;
+      a.w_gu[l] = m->base + L.gu.w;
+      a.w_dn[l] = m->base + L.down.w;
+      if (m->i8) {
+        a.s_qkv[l] = (const float*)(m->base + L.qkv.s);
+        a.s_o[l] = (const float*)(m->base + L.o.s);
+        a.s_gu[l] = (const float*)(m->base + L.gu.s);
+        a.s_dn[l] = (const float*)(m->base + L.down.s);
+      }
+      a.g_in[l] = vp(m, L.in_norm);
+      a.g_q[l] = vp(m, L.q_norm);
+      a.g_k[l] = vp(m, L.k_norm);
+      a.g_post[l] = vp(m, L.post_norm);
+    }
+    a.g_final = vp(m, m->plan.p_final);
+    for (int k = 0; k < ncb - 1; ++k) {
+      a.w_head[k] = m->base + m->plan.heads[k].w;
+      a.s_head[k] = m->i8 ? (const float*)(m->base + m->plan.heads[k].s) : nullptr;
+      a.embed[k] = vp(m, m->plan.embeds[k]);
+    }
+    a.x_p = x_p;
+    a.cand = cand;
+    a.cand_ld = cand_ld;
+    a.forced = in->forced;
+    a.logits = out->logits_pred;
+    a.status = out->status;
+    a.kc = (uint16_t*)(ws + w.pk);
+    a.vc = (uint16_t*)(ws + w.pv);
+    a.sess_stride = w.pk_sess;
+    a.x_loc = (float*)(ws + w.pp_x);
+    a.u_loc = (uint16_t*)(ws + w.pp_u);
+    a.ss_loc = (float*)(ws + w.pp_ss);
+    a.qkv_loc = (float*)(ws + w.pp_qkv);
+    a.o_loc = (uint16_t*)(ws + w.pp_o);
+    a.f_loc = (uint16_t*)(ws + w.pp_f);
+    a.p_o = (float*)(ws + w.pp_po);
+    a.p_d = (float*)(ws + w.pp_pd);
+    a.sync = (unsigned*)(ws + w.pp_sync);
+    cur_step = 1;
+    cur_layer = -1;
+    QT_MARK(QT_KERNEL_PREDICTOR, "k_pred_persist", B, nullptr);
+    QT_LAUNCH(launch_pred_persist(a, m->i8 != 0, st));
+  } else if (mode != QT_MODE_TALKER) {
     keep_w = true;
     for (int k = 1; k < ncb; ++k) {
       const int M = (k == 1) ? 2 * B : B;
@@ -702,6 +795,7 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
           a.n_new = (k == 1) ? 2 : 1;
           a.o = o;
           a.o_ld = ld_p;
+          a.status = out->status;
           QT_MARK(QT_KERNEL_ATTN_PRED, "k_attn_pred", B, nullptr);
           QT_LAUNCH(launch_attn_pred(a, Pd.rope_theta, st));
           return ok();
@@ -880,6 +974,7 @@ qt_status enqueue_prefill(const qt_model* m, const qt_prefill_args* a, const qt_
   b.u = u;
   b.ss = ss;
   b.rowinfo = rowinfo;
+  b.status = a->status;
   QT_LAUNCH(launch_prefill_begin(b, st));
 
   auto run = [&](GemmArgs& g) -> qt_status {
@@ -930,6 +1025,7 @@ qt_status enqueue_prefill(const qt_model* m, const qt_prefill_args* a, const qt_
     at.o = o;
     at.part = (float*)(ws + w.part);
     at.n_splits = kPrefillSplits;
+    at.status = a->status;
     QT_LAUNCH(launch_prefill_attn(at, st));
     g = gemm_act(m, L.o, o, R, R, a->status);
     g.epi = EPI_RESID;
@@ -971,6 +1067,7 @@ qt_status enqueue_prefill(const qt_model* m, const qt_prefill_args* a, const qt_
   pl.ss = (float*)(ws + w.ssl);
   pl.h_last = (uint16_t*)a->h_last;
   pl.kv_len = a->kv_len;
+  pl.status = a->status;
   QT_LAUNCH(launch_prefill_last(pl, st));
   GemmArgs head = gemm_norm(m, m->plan.t_head, pl.u, S, pl.ss, S, 1, T.rms_eps, S, a->status);
   head.nrows = c.talker_vocab;
@@ -1100,6 +1197,21 @@ qt_status qt_load_weights(const qt_model_cfg* cfg, const qt_tensor* tensors, int
   m->dests = make_dests(*cfg, m->plan);
   m->base = (char*)packed;
   m->bytes = packed_bytes;
+  // The one-launch predictor (qt_pred.hip) is chosen with QT_PREDICTOR=persistent in
+  // the environment when the model is loaded; it needs its 256 blocks resident
+  // together, one per CU of a 256-CU device.  By default the predictor runs as a
+  // chain of launches, which measured faster (its barriers cost what the kernel
+  // boundaries they replace cost, and it has more dependent stages).
+  {
+    int dev = 0, cus = 0;
+    const char* env = getenv("QT_PREDICTOR");
+    const bool persistent = env && strcmp(env, "persistent") == 0;
+    m->pred_persist = 0;
+    if (persistent && pred_persist_shapes(*cfg) && hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        cus == kPredBlocks && prepare_pred_persist(i8) == hipSuccess)
+      m->pred_persist = 1;
+  }
 
   // coverage in both directions, shapes and dtypes, before any copy is enqueued
   std::map<std::string, const qt_tensor*> seen;
@@ -1144,6 +1256,17 @@ qt_status qt_load_weights(const qt_model_cfg* cfg, const qt_tensor* tensors, int
   }
 
   hipStream_t s = (hipStream_t)stream;
+  // bf16 mode packs the GEMM weights as IEEE half: one flag per source matrix records
+  // a finite weight beyond the half range, read back once packing has finished
+  uint32_t* range_flags = (uint32_t*)(m->base + m->plan.range_flags);
+  std::vector<std::string> mat_names;
+  if (!i8) {
+    const hipError_t e = hipMemsetAsync(range_flags, 0, (size_t)m->plan.n_mats * 4, s);
+    if (e != hipSuccess) {
+      delete m;
+      return fail(QT_E_HIP, "clearing the range flags failed: %s", hipGetErrorString(e));
+    }
+  }
   for (const auto& kvp : seen) {
     const Dest& d = m->dests[kvp.first];
     const qt_tensor& t = *kvp.second;
@@ -1152,8 +1275,14 @@ qt_status qt_load_weights(const qt_model_cfg* cfg, const qt_tensor* tensors, int
       e = hipMemcpyAsync(m->base + d.vec_off, t.data, (size_t)t.rows * t.cols * 2,
                          hipMemcpyDeviceToDevice, s);
     } else if (!i8) {
+      if ((int)mat_names.size() >= m->plan.n_mats) {
+        delete m;
+        return fail(QT_E_STATE, "more GEMM weights than the plan counts");
+      }
       e = launch_pack_tiled((const uint16_t*)t.data, (int)d.rows, (int)d.cols,
-                            (uint16_t*)(m->base + d.mat->w), d.row0, d.step, s);
+                            (uint16_t*)(m->base + d.mat->w), d.row0, d.step,
+                            range_flags + mat_names.size(), s);
+      mat_names.push_back(kvp.first);
     } else {
       float* sc = (float*)(m->base + d.mat->s) + d.row0;
       e = launch_quantize((const uint16_t*)t.data, d.rows, d.cols, (int8_t*)(m->base + d.mat->w),
@@ -1163,6 +1292,26 @@ qt_status qt_load_weights(const qt_model_cfg* cfg, const qt_tensor* tensors, int
       delete m;
       return fail(QT_E_HIP, "packing '%s' failed: %s", kvp.first.c_str(), hipGetErrorString(e));
     }
+  }
+  if (!i8) {
+    std::vector<uint32_t> flags(mat_names.size(), 0u);
+    hipError_t e = flags.empty() ? hipSuccess
+                                 : hipMemcpyAsync(flags.data(), range_flags, flags.size() * 4,
+                                                  hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) {
+      delete m;
+      return fail(QT_E_HIP, "reading the range flags failed: %s", hipGetErrorString(e));
+    }
+    for (size_t i = 0; i < flags.size(); ++i)
+      if (flags[i]) {
+        std::string name = mat_names[i];
+        delete m;
+        return fail(QT_E_UNSUPPORTED,
+                    "weight '%s' holds values beyond the IEEE half range (|w| > 65504): the "
+                    "GEMMs take half operands (INT8 mode scales every row and accepts it)",
+                    name.c_str());
+      }
   }
   *out = m;
   return ok();

@@ -32,6 +32,16 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
 __device__ __forceinline__ uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
 __device__ __forceinline__ float h2f(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
 
+// Half of v that also notes in `over` a finite v that half cannot hold (|v| >= 65520
+// rounds to infinity).  Producers of GEMM inputs write half(x * gain) of residual rows
+// before the RMS factor is applied, so a large residual would otherwise become inf
+// without a trace; the caller ORs QT_STATUS_FP16_RANGE into the status word.
+__device__ __forceinline__ uint16_t f2h_chk(float v, bool& over) {
+  const uint16_t h = f2h(v);
+  over = over || (((h & 0x7fffu) == 0x7c00u) && !(fabsf(v) == INFINITY));
+  return h;
+}
+
 // fp16 dot products with fp32 accumulation (v_dot2_f32_f16).
 __device__ __forceinline__ float dot2h(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), c, false);

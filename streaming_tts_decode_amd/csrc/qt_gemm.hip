@@ -147,14 +147,16 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, int n0,
     if (a.ss_in) v *= inv;
     return v;
   };
+  bool over = false;  // a half input out of range (QT_STATUS_FP16_RANGE)
   if (a.epi == EPI_SWIGLU) {
     // rows 2p (gate) and 2p+1 (up) of the block's 16R -> output column n0/2 + p
     for (int e = tid; e < 8 * R * M; e += nthr) {
       const int m = e / (8 * R), p = e - m * (8 * R);
       const float inv = inv_row(m);
       const float v = silu(y(2 * p, m, inv)) * y(2 * p + 1, m, inv);
-      a.u[chunked(m, (n0 >> 1) + p, a.u_ld)] = f2h(v);
+      a.u[chunked(m, (n0 >> 1) + p, a.u_ld)] = f2h_chk(v, over);
     }
+    if (over) atomicOr(a.status, QT_STATUS_FP16_RANGE);
     return;
   }
   const bool logits = a.epi == EPI_HEAD && n0 < a.n_logits;
@@ -189,12 +191,13 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, int n0,
         // the kernel wait for that load before its main loop
         uint32_t gb = pf.gain_bits;
         asm volatile("" : "+v"(gb));
-        a.u[chunked(m, c0 + r, a.u_ld)] = f2h(v * bf2f((uint16_t)gb));
+        a.u[chunked(m, c0 + r, a.u_ld)] = f2h_chk(v * bf2f((uint16_t)gb), over);
         const float ss = row_sum16(v * v);
         if (r == 0) a.ss_out[(size_t)(c0 / kGemmRows) * a.ss_out_ld + m] = ss;
       }
     }
   }
+  if (over) atomicOr(a.status, QT_STATUS_FP16_RANGE);
 }
 
 // Eight int8 weights (bytes 8*sb .. 8*sb+7 of w) as a half x 8 operand (exact).
@@ -492,6 +495,7 @@ __global__ __launch_bounds__(256) void k_gemm_rows(GemmArgs a) {
   __syncthreads();
   // accumulator (t, u), lane (i, q), element e: weight row n0 + 16t + 4q + e,
   // activation row m0 + 16u + i
+  bool over = false;
 #pragma unroll
   for (int t = 0; t < TN; ++t) {
     const int nb = n0 + 16 * t + 4 * q;
@@ -511,7 +515,8 @@ __global__ __launch_bounds__(256) void k_gemm_rows(GemmArgs a) {
         *reinterpret_cast<float4*>(a.out_f32 + (size_t)m * a.out_ld + nb) =
             make_float4(v[0], v[1], v[2], v[3]);
       } else if (a.epi == EPI_SWIGLU) {
-        const uint32_t pk = (uint32_t)f2h(silu(v[0]) * v[1]) | ((uint32_t)f2h(silu(v[2]) * v[3]) << 16);
+        const uint32_t pk = (uint32_t)f2h_chk(silu(v[0]) * v[1], over) |
+                            ((uint32_t)f2h_chk(silu(v[2]) * v[3], over) << 16);
         *reinterpret_cast<uint32_t*>(a.u + chunked(m, nb >> 1, a.u_ld)) = pk;
       } else {  // EPI_RESID
         float* xp = a.out_f32 + (size_t)m * a.out_ld + nb;
@@ -522,8 +527,8 @@ __global__ __launch_bounds__(256) void k_gemm_rows(GemmArgs a) {
           uint32_t h2[2];
 #pragma unroll
           for (int e = 0; e < 2; ++e)
-            h2[e] = (uint32_t)f2h(x[2 * e] * bf2f(a.u_gain[nb + 2 * e])) |
-                    ((uint32_t)f2h(x[2 * e + 1] * bf2f(a.u_gain[nb + 2 * e + 1])) << 16);
+            h2[e] = (uint32_t)f2h_chk(x[2 * e] * bf2f(a.u_gain[nb + 2 * e]), over) |
+                    ((uint32_t)f2h_chk(x[2 * e + 1] * bf2f(a.u_gain[nb + 2 * e + 1]), over) << 16);
           *reinterpret_cast<uint2*>(a.u + chunked(m, nb, a.u_ld)) = make_uint2(h2[0], h2[1]);
           float ss = x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
           ss += __shfl_xor(ss, 16);
@@ -533,6 +538,7 @@ __global__ __launch_bounds__(256) void k_gemm_rows(GemmArgs a) {
       }
     }
   }
+  if (over) atomicOr(a.status, QT_STATUS_FP16_RANGE);
 }
 
 constexpr int kPipeKU = 2;  // K steps of 32 per stage of the copy-pipelined form
@@ -658,6 +664,7 @@ __global__ __launch_bounds__(256) void k_gemm_rows_pipe(GemmArgs a) {
   bool mrow[TM];
 #pragma unroll
   for (int u = 0; u < TM; ++u) mrow[u] = m0 + 16 * u + i < M;
+  bool over = false;
 #pragma unroll
   for (int t = 0; t < TN; ++t) {
     const int nb = n0 + 16 * t + 4 * q;
@@ -673,7 +680,8 @@ __global__ __launch_bounds__(256) void k_gemm_rows_pipe(GemmArgs a) {
         *reinterpret_cast<float4*>(a.out_f32 + (size_t)m * a.out_ld + nb) =
             make_float4(v[0], v[1], v[2], v[3]);
       } else if (a.epi == EPI_SWIGLU) {
-        const uint32_t pk = (uint32_t)f2h(silu(v[0]) * v[1]) | ((uint32_t)f2h(silu(v[2]) * v[3]) << 16);
+        const uint32_t pk = (uint32_t)f2h_chk(silu(v[0]) * v[1], over) |
+                            ((uint32_t)f2h_chk(silu(v[2]) * v[3], over) << 16);
         *reinterpret_cast<uint32_t*>(a.u + chunked(m, nb >> 1, a.u_ld)) = pk;
       } else {  // EPI_RESID
         float* xp = a.out_f32 + (size_t)m * a.out_ld + nb;
@@ -684,8 +692,8 @@ __global__ __launch_bounds__(256) void k_gemm_rows_pipe(GemmArgs a) {
           uint32_t h2[2];
 #pragma unroll
           for (int e = 0; e < 2; ++e)
-            h2[e] = (uint32_t)f2h(x[2 * e] * bf2f(a.u_gain[nb + 2 * e])) |
-                    ((uint32_t)f2h(x[2 * e + 1] * bf2f(a.u_gain[nb + 2 * e + 1])) << 16);
+            h2[e] = (uint32_t)f2h_chk(x[2 * e] * bf2f(a.u_gain[nb + 2 * e]), over) |
+                    ((uint32_t)f2h_chk(x[2 * e + 1] * bf2f(a.u_gain[nb + 2 * e + 1]), over) << 16);
           *reinterpret_cast<uint2*>(a.u + chunked(m, nb, a.u_ld)) = make_uint2(h2[0], h2[1]);
           float ss = x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
           ss += __shfl_xor(ss, 16);
@@ -695,12 +703,15 @@ __global__ __launch_bounds__(256) void k_gemm_rows_pipe(GemmArgs a) {
       }
     }
   }
+  if (over) atomicOr(a.status, QT_STATUS_FP16_RANGE);
 }
 
 // ------------------------------------------------------------------ packing
 // Source rows [rows][K] bf16 -> half rows row0 + r*step of a tiled [N][K] matrix.
+// A finite bf16 weight beyond the half range (|w| > 65504) sets *range_flag.
 __global__ __launch_bounds__(256) void k_pack_tiled(const uint16_t* src, int rows, int K,
-                                                    uint16_t* dst, int row0, int step) {
+                                                    uint16_t* dst, int row0, int step,
+                                                    uint32_t* range_flag) {
   const long long e = (long long)blockIdx.x * 256 + threadIdx.x;  // one 8-wide chunk
   const int kc = K >> 3;
   if (e >= (long long)rows * kc) return;
@@ -708,10 +719,12 @@ __global__ __launch_bounds__(256) void k_pack_tiled(const uint16_t* src, int row
   const uint4 v = *reinterpret_cast<const uint4*>(src + (size_t)r * K + k);
   const uint32_t in[4] = {v.x, v.y, v.z, v.w};
   uint32_t o[4];
+  bool over = false;
 #pragma unroll
   for (int j = 0; j < 4; ++j)
-    o[j] = (uint32_t)f2h(bf_lo(in[j])) | ((uint32_t)f2h(bf_hi(in[j])) << 16);
+    o[j] = (uint32_t)f2h_chk(bf_lo(in[j]), over) | ((uint32_t)f2h_chk(bf_hi(in[j]), over) << 16);
   *reinterpret_cast<uint4*>(dst + tiled_bf16(row0 + r * step, k, K)) = make_uint4(o[0], o[1], o[2], o[3]);
+  if (over) atomicOr(range_flag, 1u);
 }
 
 // Rows row0 + r*step of a tiled int8 [N][K] matrix -> row-major [rows][K].
@@ -817,11 +830,12 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_pack_tiled(const uint16_t* src, int rows, int K, uint16_t* dst, int row0,
-                             int step, hipStream_t s) {
-  if (rows <= 0 || K <= 0 || (K % 32) || row0 < 0 || step < 1) return hipErrorInvalidValue;
+                             int step, uint32_t* range_flag, hipStream_t s) {
+  if (rows <= 0 || K <= 0 || (K % 32) || row0 < 0 || step < 1 || !range_flag)
+    return hipErrorInvalidValue;
   const long long n = (long long)rows * (K / 8);
   launch_kernel(k_pack_tiled, dim3((unsigned)((n + 255) / 256)), dim3(256), s, src, rows, K, dst,
-                row0, step);
+                row0, step, range_flag);
   return hipGetLastError();
 }
 

@@ -156,10 +156,12 @@ struct AttnPredArgs {
   int pos0, n_new;
   uint16_t* o;            // chunked half [q_dim/8][o_ld][8]; row i*B + b: position pos0+i of session b
   int o_ld;               // rows of the chunked output (>= n_new*B)
+  uint32_t* status;
 };
 
 struct FrameBeginArgs {
   int mode, B, Ht, ncb, n_kv, capacity;
+  unsigned* pred_sync;      // sync counters of the persistent predictor, cleared (or nullptr)
   float eps;
   const uint16_t* talker_in;
   const int32_t* tok0_in;
@@ -237,6 +239,7 @@ struct PrefillBeginArgs {
   uint16_t* u;              // chunked half [H/8][R][8]
   float* ss;                // slot 0: [R]
   int32_t* rowinfo;         // [R][2]
+  uint32_t* status;
 };
 
 struct PrefillQkArgs {
@@ -266,6 +269,7 @@ struct PrefillAttnArgs {
   uint16_t* o;              // chunked half [q_dim/8][R][8]
   float* part;              // [R][n_q][n_splits][128 + 2]: split outputs, max and sum
   int n_splits;             // key blocks of a tile are dealt round-robin over the splits
+  uint32_t* status;
 };
 
 struct PrefillLastArgs {
@@ -278,6 +282,7 @@ struct PrefillLastArgs {
   float* ss;                // [max_seqs]
   uint16_t* h_last;         // [max_seqs][H] bf16 or nullptr
   int32_t* kv_len;
+  uint32_t* status;
 };
 
 struct PrefillEndArgs {
@@ -359,6 +364,63 @@ struct SchedCollectArgs {
 hipError_t launch_sched_setup(const SchedSetupArgs& a, hipStream_t s);
 hipError_t launch_sched_collect(const SchedCollectArgs& a, hipStream_t s);
 
+// Persistent code predictor (qt_pred.hip): every predictor step of a frame in one
+// launch of 256 blocks, one per CU, 32 on each of the eight XCDs (a block reads its
+// XCD from the hardware; the launch stops with QT_STATUS_SYNC if the blocks are not
+// all resident or not 32 per XCD).  XCD x owns KV
+// head x (its QKV rows and attention), the K-slice [256x, 256x + 256) of the output
+// projection, FFN columns [384x, 384x + 384) (its gate/up rows and the matching
+// K-slice of down) and head rows [256x, 256x + 256).  Shapes: predictor hidden 1024,
+// 16 query / 8 KV heads of 128, FFN 3072, code vocabulary 2048, B <= 32.
+constexpr int kPredMaxLayers = 8;
+constexpr int kPredMaxSteps = 15;
+constexpr int kPredBlocks = 256;
+constexpr unsigned kPredSyncWords = 64 * 40;  // sync counters, one 256-byte line each
+
+struct PredPersistArgs {
+  int B, layers, n_steps, ncb, ldm;  // ldm: rows of the per-XCD buffers (>= 2B)
+  float eps, theta_log2;
+  const void* w_qkv[kPredMaxLayers];
+  const void* w_o[kPredMaxLayers];
+  const void* w_gu[kPredMaxLayers];
+  const void* w_dn[kPredMaxLayers];
+  const float* s_qkv[kPredMaxLayers];  // INT8 row scales (nullptr in bf16 mode)
+  const float* s_o[kPredMaxLayers];
+  const float* s_gu[kPredMaxLayers];
+  const float* s_dn[kPredMaxLayers];
+  const uint16_t* g_in[kPredMaxLayers];
+  const uint16_t* g_q[kPredMaxLayers];
+  const uint16_t* g_k[kPredMaxLayers];
+  const uint16_t* g_post[kPredMaxLayers];
+  const uint16_t* g_final;
+  const void* w_head[kPredMaxSteps];
+  const float* s_head[kPredMaxSteps];
+  const uint16_t* embed[kPredMaxSteps];  // [2048][1024] bf16
+  const float* x_p;               // [B][1024]: projection rows left by the Talker's head GEMM
+  unsigned long long* cand;       // [ncb][B][cand_ld] greedy keys (codebook 0 from the head GEMM)
+  int cand_ld;
+  const int32_t* forced;          // [B][ncb] or nullptr
+  float* logits;                  // [B][ncb-1][2048]
+  uint32_t* status;
+  uint16_t* kc;                   // predictor cache [B][layers][ncb][8][128] bf16
+  uint16_t* vc;
+  long long sess_stride;          // elements per session of the cache
+  // workspace: per-XCD buffers and the cross-XCD partial sums
+  float* x_loc;                   // [8][ldm][1024] residual rows
+  uint16_t* u_loc;                // [8][128][ldm][8] half: next GEMM's normalised input
+  float* ss_loc;                  // [8][32][ldm] sums of squares per 32-column slice
+  float* qkv_loc;                 // [8][ldm][512]: q heads 2x, 2x+1, key x, value x
+  uint16_t* o_loc;                // [8][32][ldm][8] half: attention output of heads 2x, 2x+1
+  uint16_t* f_loc;                // [8][48][ldm][8] half: SwiGLU output, FFN slice x
+  float* p_o;                     // [8][ldm][1024] output-projection partial of XCD x
+  float* p_d;                     // [8][ldm][1024] down-projection partial of XCD x
+  unsigned* sync;                 // kPredSyncWords, zero at launch (k_frame_begin clears it)
+};
+hipError_t launch_pred_persist(const PredPersistArgs& a, bool i8, hipStream_t s);
+// Per process and device, before the first launch (not under stream capture): the
+// kernel's 96 KB of dynamic LDS (which also keeps it to one block per CU).
+hipError_t prepare_pred_persist(bool i8);
+
 // Configuration of a loaded model, and the thread-local error text behind
 // qt_last_error() (qt_abi.cpp).
 const qt_model_cfg* model_cfg(const qt_model* m);
@@ -377,9 +439,10 @@ hipError_t launch_attn_pred(const AttnPredArgs& a, float theta, hipStream_t s);
 hipError_t launch_frame_begin(const FrameBeginArgs& a, hipStream_t s);
 hipError_t launch_embed(const EmbedArgs& a, hipStream_t s);
 hipError_t launch_frame_end(const FrameEndArgs& a, hipStream_t s);
-// Pack bf16 source rows [rows][K] as half rows row0 + i*step of a tiled [N][K] matrix.
+// Pack bf16 source rows [rows][K] as half rows row0 + i*step of a tiled [N][K] matrix;
+// a finite weight beyond the half range sets *range_flag (device word).
 hipError_t launch_pack_tiled(const uint16_t* src, int rows, int K, uint16_t* dst, int row0, int step,
-                             hipStream_t s);
+                             uint32_t* range_flag, hipStream_t s);
 // Copy rows row0 + i*step (i < rows) of a tiled int8 [N][K] matrix out row-major.
 hipError_t launch_untile_i8(const int8_t* tiled, int rows, int K, int row0, int step, int8_t* out,
                             hipStream_t s);

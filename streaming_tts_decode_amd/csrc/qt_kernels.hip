@@ -3,8 +3,9 @@
 // Every kernel here is launched by qt_abi.cpp on the caller's stream; shapes
 // are validated on the host before launch (see the launchers at the end).
 //
-// Data types: weights bf16 or int8 (+ fp32 per-row scale), GEMM activations
-// bf16, accumulation fp32, residual streams fp32, KV caches bf16.
+// Data types: GEMM weights packed as IEEE half (from the bf16 source weights) or
+// int8 (+ fp32 per-row scale), GEMM activations half, accumulation fp32, residual
+// streams fp32, embeddings, norm gains and KV caches bf16.
 #include <math.h>
 
 #include "qt_device.h"
@@ -255,7 +256,9 @@ __global__ __launch_bounds__(256) void k_attn_paged(AttnPagedArgs a, float theta
   __syncthreads();
   const float out = red[0][jj][d] + red[1][jj][d] + red[2][jj][d] + red[3][jj][d];
   if (n_active == 1) {
-    a.o[orow] = f2h(out / lstat[jj]);
+    bool over = false;
+    a.o[orow] = f2h_chk(out / lstat[jj], over);
+    if (over) atomicOr(a.status, QT_STATUS_FP16_RANGE);
     return;
   }
   // Publish this split's partial with device-coherent stores, wait until they
@@ -309,7 +312,9 @@ __global__ __launch_bounds__(256) void k_attn_paged(AttnPagedArgs a, float theta
     }
     M = Mc;
   }
-  a.o[orow] = f2h(O / L);
+  bool over = false;
+  a.o[orow] = f2h_chk(O / L, over);
+  if (over) atomicOr(a.status, QT_STATUS_FP16_RANGE);
   if (tid == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -442,10 +447,12 @@ __global__ __launch_bounds__(256) void k_attn_pred(AttnPredArgs a, float theta_l
     }
   }
   __syncthreads();
+  bool over = false;
   for (int i = 0; i < a.n_new; ++i) {
     const float out = red[0][i][jj][d] + red[1][i][jj][d] + red[2][i][jj][d] + red[3][i][jj][d];
-    a.o[chunked(i * a.B + b, (j0 + jj) * 128 + d, a.o_ld)] = f2h(out / lsum[i][jj]);
+    a.o[chunked(i * a.B + b, (j0 + jj) * 128 + d, a.o_ld)] = f2h_chk(out / lsum[i][jj], over);
   }
+  if (over) atomicOr(a.status, QT_STATUS_FP16_RANGE);
 }
 
 // ---------------------------------------------------------------------------
@@ -456,13 +463,14 @@ __global__ __launch_bounds__(256) void k_attn_pred(AttnPredArgs a, float theta_l
 __global__ __launch_bounds__(256) void k_frame_begin(FrameBeginArgs a) {
   __shared__ float part[4];
   const int b = blockIdx.x, tid = threadIdx.x;
+  bool over = false;
   if (a.mode != QT_MODE_PREDICTOR) {
     float ss = 0.f;
     for (int i = tid; i < a.Ht; i += 256) {
       const size_t e = (size_t)b * a.Ht + i;
       const float v = bf2f(a.talker_in[e]);
       a.x_t[e] = v;
-      a.u[chunked(b, i, a.B)] = f2h(v * bf2f(a.gain[i]));
+      a.u[chunked(b, i, a.B)] = f2h_chk(v * bf2f(a.gain[i]), over);
       ss = fmaf(v, v, ss);
     }
     ss = wave_sum(ss);
@@ -475,11 +483,14 @@ __global__ __launch_bounds__(256) void k_frame_begin(FrameBeginArgs a) {
     }
   } else {
     for (int i = tid; i < a.Ht; i += 256)
-      a.u[chunked(b, i, a.B)] = f2h(bf2f(a.h_in[(size_t)b * a.Ht + i]));
+      a.u[chunked(b, i, a.B)] = f2h_chk(bf2f(a.h_in[(size_t)b * a.Ht + i]), over);
     unsigned long long* c0 = a.cand + (size_t)b * a.cand_ld;
     for (int k = tid; k < a.cand_ld; k += 256) c0[k] = k == 0 ? greedy_key(0.0f, a.tok0_in[b]) : 0ull;
   }
+  if (over) atomicOr(a.status, QT_STATUS_FP16_RANGE);
   if (tid < a.n_kv) a.counters[(size_t)b * a.n_kv + tid] = 0u;
+  if (a.pred_sync && b == 0)
+    for (unsigned i = tid; i < kPredSyncWords; i += 256) a.pred_sync[i] = 0u;
 }
 
 // Best of n greedy-key candidates, reduced by the 64 lanes of a wave.
@@ -737,12 +748,14 @@ __global__ __launch_bounds__(256) void k_embed(EmbedArgs a) {
   const int m = a.row_off + b;
   float* dst = a.x + (size_t)m * a.H;
   float ss = 0.f;
+  bool over = false;
   for (int i = tid; i < a.H; i += 256) {
     const float v = bf2f(src[i]);
     dst[i] = v;
-    a.u[chunked(m, i, a.u_ld)] = f2h(v * bf2f(a.gain[i]));
+    a.u[chunked(m, i, a.u_ld)] = f2h_chk(v * bf2f(a.gain[i]), over);
     ss = fmaf(v, v, ss);
   }
+  if (over) atomicOr(a.status, QT_STATUS_FP16_RANGE);
   ss = wave_sum(ss);
   if ((tid & 63) == 0) part[tid >> 6] = ss;
   __syncthreads();
@@ -959,12 +972,14 @@ __global__ __launch_bounds__(256) void k_prefill_begin(PrefillBeginArgs a) {
   __syncthreads();
   const bool live = s_seq >= 0;
   float ss = 0.f;
+  bool over = false;
   for (int i = tid; i < a.H; i += 256) {
     const float v = live ? bf2f(a.embeds[(size_t)r * a.H + i]) : 0.f;
     a.x[(size_t)r * a.H + i] = v;
-    a.u[chunked(r, i, a.R)] = f2h(v * bf2f(a.gain[i]));
+    a.u[chunked(r, i, a.R)] = f2h_chk(v * bf2f(a.gain[i]), over);
     ss = fmaf(v, v, ss);
   }
+  if (over) atomicOr(a.status, QT_STATUS_FP16_RANGE);
   ss = wave_sum(ss);
   if ((tid & 63) == 0) part[tid >> 6] = ss;
   __syncthreads();
@@ -1201,9 +1216,12 @@ __global__ __launch_bounds__(256) void k_prefill_attn_merge(PrefillAttnArgs a) {
   }
   const float inv = (a.rowinfo[2 * row] >= 0 && L > 0.f) ? 1.f / L : 0.f;
   uint32_t packed[8];
+  bool over = false;
 #pragma unroll
   for (int w = 0; w < 8; ++w)
-    packed[w] = (uint32_t)f2h(acc[2 * w] * inv) | ((uint32_t)f2h(acc[2 * w + 1] * inv) << 16);
+    packed[w] = (uint32_t)f2h_chk(acc[2 * w] * inv, over) |
+                ((uint32_t)f2h_chk(acc[2 * w + 1] * inv, over) << 16);
+  if (over) atomicOr(a.status, QT_STATUS_FP16_RANGE);
   const int col = qh * 128 + 16 * sub;
   *reinterpret_cast<uint4*>(a.o + chunked(row, col, a.R)) =
       make_uint4(packed[0], packed[1], packed[2], packed[3]);
@@ -1220,11 +1238,13 @@ __global__ __launch_bounds__(256) void k_prefill_last(PrefillLastArgs a) {
   const int len = (hi > lo && hi <= a.R) ? hi - lo : 0;
   const float* x = a.x + (size_t)(len ? hi - 1 : 0) * a.H;
   float ss = 0.f;
+  bool over = false;
   for (int i = tid; i < a.H; i += 256) {
     const float v = len ? x[i] : 0.f;
-    a.u[chunked(q, i, a.max_seqs)] = f2h(v * bf2f(a.gain[i]));
+    a.u[chunked(q, i, a.max_seqs)] = f2h_chk(v * bf2f(a.gain[i]), over);
     ss = fmaf(v, v, ss);
   }
+  if (over) atomicOr(a.status, QT_STATUS_FP16_RANGE);
   ss = wave_sum(ss);
   if ((tid & 63) == 0) part[tid >> 6] = ss;
   __syncthreads();

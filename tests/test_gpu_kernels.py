@@ -320,3 +320,50 @@ def test_int8_model_uses_quantizer_output(full_pm_i8, orc_full_i8):
         np.testing.assert_array_equal(q.cpu().numpy(), qo, err_msg=name)
         np.testing.assert_array_equal(s.cpu().numpy().view(np.uint32), so.view(np.uint32),
                                       err_msg=name)
+
+
+# ----------------------------------------------------------------- fp16 range
+def test_weight_beyond_half_range_is_refused(small_weights):
+    """bf16 mode packs the GEMM weights as IEEE half: a weight matrix with a finite
+    entry above 65504 is refused at load, naming it; INT8 mode scales every row and
+    takes it."""
+    import streaming_tts_decode_amd as qt
+    from streaming_tts_decode_amd.runtime import PackedModel
+    W = dict(small_weights)
+    name = "talker.layers.1.down_proj"
+    w = W[name].copy()
+    w[3, 17] = 0x47C3  # bf16 99840
+    W[name] = w
+    with pytest.raises(qt.QtError) as e:
+        PackedModel(S, W, int8=False)
+    assert e.value.status == 9 and name in str(e.value)
+    pm8 = PackedModel(S, W, int8=True)
+    pm8.close()
+
+
+def test_activation_beyond_half_range_sets_status(small_pm):
+    """A Talker input row value whose half(x * gain) overflows sets
+    QT_STATUS_FP16_RANGE; the other sessions' outputs are unaffected (rows are
+    independent)."""
+    import streaming_tts_decode_amd as qt
+    from streaming_tts_decode_amd.runtime import setup_workload
+    torch = small_pm.torch
+    w = small_w("Srange", batch=3, frames=1, lens=[20, 7, 41])
+    x = synth.frame_inputs(w)["talker_in"][0].copy()
+    dec, _ = setup_workload(w, small_pm)
+    L0 = dec.kv_len.clone()
+    dec.set_inputs(talker_in=x)
+    dec.decode("full")
+    torch.cuda.synchronize()
+    assert int(dec.status.item()) == 0
+    ref = dec.logits0.cpu().numpy().copy()
+    x[1, 100] = 0x4843  # bf16 199680: half(199680 * gain) is inf for any gain above 0.33
+    dec.kv_len.copy_(L0)
+    dec.set_inputs(talker_in=x)
+    dec.decode("full")
+    torch.cuda.synchronize()
+    st = int(dec.status.item())
+    assert st & qt.STATUS_FP16_RANGE, f"status {st:#x}"
+    got = dec.logits0.cpu().numpy()
+    np.testing.assert_array_equal(got[[0, 2]], ref[[0, 2]])
+    dec.close()

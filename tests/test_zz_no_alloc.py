@@ -75,7 +75,7 @@ def test_noalloc_refuses_oversize(full_pm):
     cfg = full_pm.cfg
     # a batch whose workspace is larger than the static scratch: refused on the host,
     # before anything is enqueued (the descriptors' buffers are never touched)
-    mp = 320
+    mp = 512
     assert qt.qt_workspace_bytes(cfg, 32, mp) > qt.NOALLOC_SCRATCH_BYTES
     buf = torch.zeros(1 << 20, dtype=torch.int32, device="cuda")
     p = buf.data_ptr()
