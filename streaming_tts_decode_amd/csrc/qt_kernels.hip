@@ -1030,25 +1030,32 @@ __global__ __launch_bounds__(256) void k_prefill_qk(PrefillQkArgs a, float theta
 // For each sequence present in the tile, keys come in blocks of 32 (two pages),
 // blocks z, z + n_splits, ... to this split: K staged through LDS as half
 // [key][dim], V as half [dim][key] (a wave's lanes take consecutive keys, so the
-// transposing stores spread over the banks); the next block's loads are in flight
-// while the current one is used.  The split writes its unnormalised output, max
-// and sum per (row, head); k_prefill_attn_merge combines the splits in order.
+// transposing stores spread over the banks).  The sequence's page indices are
+// staged in LDS first (a prompt has fewer than 4096 positions, so at most 256
+// pages), and the K/V pieces of the next kPfRing key blocks are always in flight:
+// each is requested unconditionally (a block past the split's last re-reads the
+// last; positions past the tile's rows or on a bad page are zeroed when staged),
+// so that no wait for a page index or for a later block holds up the current one.
+// The split writes its unnormalised output, max and sum per (row, head);
+// k_prefill_attn_merge combines the splits in order.
 // Per block of keys:
 //   S = Q K^T   (v_mfma_f32_16x16x32_f16: 2 key tiles x 4 dim steps), masked to
 //               keys at or before the row's position;
 //   online softmax in the accumulator layout (lane l, element e: row 4(l>>4)+e,
-//               key l&15), row max and sum over 16 lanes;
+//               key l&15), row max and sum over the 16 lanes of a row (DPP);
 //   P -> per-wave LDS tile -> A operand; O += P V (8 dim tiles, one 32-key step).
-// Key slots past the tile's last position are staged as zeros.
 constexpr int kKsLd = 136;  // half elements per staged key row (bank spread)
 constexpr int kVtLd = 40;   // half elements per staged dim row of V^T / per P row
 constexpr int kAttnRows = 64;
+constexpr int kPfMaxPages = QT_PREFILL_MAX_ROWS / kPage;
+constexpr int kPfRing = 2;  // key blocks in flight
 
 __global__ __launch_bounds__(512) void k_prefill_attn(PrefillAttnArgs a) {
   __shared__ __align__(16) _Float16 Ks[32 * kKsLd];
   __shared__ __align__(16) _Float16 Vt[128 * kVtLd];
   __shared__ __align__(16) _Float16 Ps[8][16 * kVtLd];
   __shared__ int t_seq[kAttnRows], t_pos[kAttnRows];
+  __shared__ int s_pg[kPfMaxPages];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i = lane & 15, qg = lane >> 4, rg = wave >> 1;
   const int h = blockIdx.y, r0 = kAttnRows * blockIdx.x, qh = 2 * h + (wave & 1);
@@ -1098,14 +1105,6 @@ __global__ __launch_bounds__(512) void k_prefill_attn(PrefillAttnArgs a) {
   // staging pieces of 16 bytes: K piece (key tid >> 4, dims 8 (tid & 15)), V piece
   // (key tid & 31, dims 8 (tid >> 5))
   const int kkey = tid >> 4, kd8 = tid & 15, vkey = tid & 31, vd8 = tid >> 5;
-  auto piece = [&](int seq, int kb, int pmax, int key, int d8, const uint16_t* pool) -> uint4 {
-    const int kpos = 32 * kb + key, pi = kpos >> 4;
-    if (kpos > pmax || pi >= a.max_pages) return make_uint4(0, 0, 0, 0);
-    const int pg = a.page_table[(size_t)seq * a.max_pages + pi];
-    if (pg < 0 || pg >= a.num_pages) return make_uint4(0, 0, 0, 0);
-    return *reinterpret_cast<const uint4*>(pool + (size_t)pg * page_elems + head_off +
-                                           (size_t)(kpos & 15) * 128 + 8 * d8);
-  };
   for (int seq = seq_lo; seq <= seq_hi; ++seq) {
     int pmax = -1;
     for (int r = 0; r < kAttnRows; ++r)
@@ -1113,71 +1112,88 @@ __global__ __launch_bounds__(512) void k_prefill_attn(PrefillAttnArgs a) {
     if (pmax < 0) continue;
     const int nblk = pmax / 32 + 1;
     if (z >= nblk) continue;
-    uint4 kr = piece(seq, z, pmax, kkey, kd8, a.k_pool);
-    uint4 vr = piece(seq, z, pmax, vkey, vd8, a.v_pool);
-    for (int kb = z; kb < nblk; kb += nz) {
-      __syncthreads();  // the previous block of keys is consumed
-      {
-        const uint32_t kw[4] = {kr.x, kr.y, kr.z, kr.w};
-        const uint32_t vw[4] = {vr.x, vr.y, vr.z, vr.w};
-        f16x8 kh;
+    const int cnt = (nblk - z + nz - 1) / nz;  // key blocks z, z + nz, ... of this split
+    const int npg = min(min(2 * nblk, a.max_pages), kPfMaxPages);
+    __syncthreads();  // the previous sequence's page indices are no longer read
+    for (int pi = tid; pi < npg; pi += 512) {
+      const int pg = a.page_table[(size_t)seq * a.max_pages + pi];
+      s_pg[pi] = (pg >= 0 && pg < a.num_pages) ? pg : -1;
+    }
+    __syncthreads();
+    // element offset of the piece (key, d8) of the split's key block n (clamped to
+    // its last), and whether it holds a live key
+    auto piece = [&](int n, int key, int d8, bool& live) -> size_t {
+      const int kpos = 32 * (z + nz * min(n, cnt - 1)) + key, pi = kpos >> 4;
+      const int pg = pi < npg ? s_pg[pi] : -1;
+      live = n < cnt && kpos <= pmax && pg >= 0;
+      return (size_t)(pg >= 0 ? pg : 0) * page_elems + head_off + (size_t)(kpos & 15) * 128 + 8 * d8;
+    };
+    uint4 kr[kPfRing], vr[kPfRing];
+    bool klive[kPfRing], vlive[kPfRing];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          kh[2 * w] = (_Float16)bf_lo(kw[w]);
-          kh[2 * w + 1] = (_Float16)bf_hi(kw[w]);
-          Vt[(8 * vd8 + 2 * w) * kVtLd + vkey] = (_Float16)bf_lo(vw[w]);
-          Vt[(8 * vd8 + 2 * w + 1) * kVtLd + vkey] = (_Float16)bf_hi(vw[w]);
+    for (int d = 0; d < kPfRing; ++d) {
+      kr[d] = *reinterpret_cast<const uint4*>(a.k_pool + piece(d, kkey, kd8, klive[d]));
+      vr[d] = *reinterpret_cast<const uint4*>(a.v_pool + piece(d, vkey, vd8, vlive[d]));
+    }
+    for (int n0 = 0; n0 < cnt; n0 += kPfRing) {
+#pragma unroll
+      for (int d = 0; d < kPfRing; ++d) {
+        const int n = n0 + d, kb = z + nz * n;
+        __syncthreads();  // the previous block of keys is consumed
+        if (n < cnt) {
+          const uint4 kq = klive[d] ? kr[d] : make_uint4(0, 0, 0, 0);
+          const uint4 vq = vlive[d] ? vr[d] : make_uint4(0, 0, 0, 0);
+          const uint32_t kw[4] = {kq.x, kq.y, kq.z, kq.w};
+          const uint32_t vw[4] = {vq.x, vq.y, vq.z, vq.w};
+          f16x8 kh;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            kh[2 * w] = (_Float16)bf_lo(kw[w]);
+            kh[2 * w + 1] = (_Float16)bf_hi(kw[w]);
+            Vt[(8 * vd8 + 2 * w) * kVtLd + vkey] = (_Float16)bf_lo(vw[w]);
+            Vt[(8 * vd8 + 2 * w + 1) * kVtLd + vkey] = (_Float16)bf_hi(vw[w]);
+          }
+          *reinterpret_cast<f16x8*>(Ks + kkey * kKsLd + 8 * kd8) = kh;
         }
-        *reinterpret_cast<f16x8*>(Ks + kkey * kKsLd + 8 * kd8) = kh;
-      }
-      __syncthreads();
-      if (kb + nz < nblk) {
-        kr = piece(seq, kb + nz, pmax, kkey, kd8, a.k_pool);
-        vr = piece(seq, kb + nz, pmax, vkey, vd8, a.v_pool);
-      }
-      f32x4 S0 = f32x4{0.f, 0.f, 0.f, 0.f}, S1 = S0;
+        __syncthreads();
+        // the ring slot is free: key block n + kPfRing is requested now
+        kr[d] = *reinterpret_cast<const uint4*>(a.k_pool + piece(n + kPfRing, kkey, kd8, klive[d]));
+        vr[d] = *reinterpret_cast<const uint4*>(a.v_pool + piece(n + kPfRing, vkey, vd8, vlive[d]));
+        if (n >= cnt) continue;
+        f32x4 S0 = f32x4{0.f, 0.f, 0.f, 0.f}, S1 = S0;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const f16x8 b0 = *reinterpret_cast<const f16x8*>(Ks + i * kKsLd + 32 * ks + 8 * qg);
-        const f16x8 b1 = *reinterpret_cast<const f16x8*>(Ks + (16 + i) * kKsLd + 32 * ks + 8 * qg);
-        S0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qf[ks], b0, S0, 0, 0, 0);
-        S1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qf[ks], b1, S1, 0, 0, 0);
-      }
-      const int k0 = 32 * kb + i, k1 = k0 + 16;
+        for (int ks = 0; ks < 4; ++ks) {
+          const f16x8 b0 = *reinterpret_cast<const f16x8*>(Ks + i * kKsLd + 32 * ks + 8 * qg);
+          const f16x8 b1 = *reinterpret_cast<const f16x8*>(Ks + (16 + i) * kKsLd + 32 * ks + 8 * qg);
+          S0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qf[ks], b0, S0, 0, 0, 0);
+          S1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qf[ks], b1, S1, 0, 0, 0);
+        }
+        const int k0 = 32 * kb + i, k1 = k0 + 16;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool live = row_seq[e] == seq;
-        const float s0 = (live && k0 <= row_pos[e]) ? S0[e] : -INFINITY;
-        const float s1 = (live && k1 <= row_pos[e]) ? S1[e] : -INFINITY;
-        float mx = fmaxf(s0, s1);
-        mx = fmaxf(mx, __shfl_xor(mx, 1));
-        mx = fmaxf(mx, __shfl_xor(mx, 2));
-        mx = fmaxf(mx, __shfl_xor(mx, 4));
-        mx = fmaxf(mx, __shfl_xor(mx, 8));
-        const float mn = fmaxf(m[e], mx);
-        const float scale = mn == -INFINITY ? 1.f : expf(m[e] - mn);
-        const float p0 = s0 == -INFINITY ? 0.f : expf(s0 - mn);
-        const float p1 = s1 == -INFINITY ? 0.f : expf(s1 - mn);
-        float rs = p0 + p1;
-        rs += __shfl_xor(rs, 1);
-        rs += __shfl_xor(rs, 2);
-        rs += __shfl_xor(rs, 4);
-        rs += __shfl_xor(rs, 8);
-        l[e] = l[e] * scale + rs;
-        m[e] = mn;
+        for (int e = 0; e < 4; ++e) {
+          const bool live = row_seq[e] == seq;
+          const float s0 = (live && k0 <= row_pos[e]) ? S0[e] : -INFINITY;
+          const float s1 = (live && k1 <= row_pos[e]) ? S1[e] : -INFINITY;
+          const float mn = fmaxf(m[e], row_max16(fmaxf(s0, s1)));
+          const float scale = mn == -INFINITY ? 1.f : expf(m[e] - mn);
+          const float p0 = s0 == -INFINITY ? 0.f : expf(s0 - mn);
+          const float p1 = s1 == -INFINITY ? 0.f : expf(s1 - mn);
+          l[e] = l[e] * scale + row_sum16(p0 + p1);
+          m[e] = mn;
 #pragma unroll
-        for (int nb = 0; nb < 8; ++nb) O[nb][e] *= scale;
-        Ps[wave][(4 * qg + e) * kVtLd + i] = (_Float16)p0;
-        Ps[wave][(4 * qg + e) * kVtLd + 16 + i] = (_Float16)p1;
-      }
-      __builtin_amdgcn_wave_barrier();
-      const f16x8 pa = *reinterpret_cast<const f16x8*>(&Ps[wave][i * kVtLd + 8 * qg]);
+          for (int nb = 0; nb < 8; ++nb) O[nb][e] *= scale;
+          Ps[wave][(4 * qg + e) * kVtLd + i] = (_Float16)p0;
+          Ps[wave][(4 * qg + e) * kVtLd + 16 + i] = (_Float16)p1;
+        }
+        __builtin_amdgcn_wave_barrier();
+        const f16x8 pa = *reinterpret_cast<const f16x8*>(&Ps[wave][i * kVtLd + 8 * qg]);
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
-        const f16x8 vb = *reinterpret_cast<const f16x8*>(Vt + (16 * nb + i) * kVtLd + 8 * qg);
-        O[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vb, O[nb], 0, 0, 0);
+        for (int nb = 0; nb < 8; ++nb) {
+          const f16x8 vb = *reinterpret_cast<const f16x8*>(Vt + (16 * nb + i) * kVtLd + 8 * qg);
+          O[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vb, O[nb], 0, 0, 0);
+        }
+        __builtin_amdgcn_wave_barrier();
       }
-      __builtin_amdgcn_wave_barrier();
     }
   }
 #pragma unroll
