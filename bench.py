@@ -60,12 +60,16 @@ def weight_bytes(d, int8: bool, distinct: bool = False, mode: str = "full") -> i
     15 steps share, are counted once (the stricter lower bound).
     mode "talker": the Talker layers, its final gain and the codec head only;
     mode "predictor": the projection and the predictor steps only."""
-    def mat(n, k):
-        return n * k + 4 * n if int8 else 2 * n * k
+    def mat(n, k, narrow=True):
+        # INT8 mode: int8 values + f32 row scales for the Talker's matrices, the
+        # same values held as halves for the code predictor's (cache-resident)
+        if not int8:
+            return 2 * n * k
+        return (n * k if narrow else 2 * n * k) + 4 * n
 
-    def layer(x):
-        return (mat(x.q_dim + 2 * x.kv_dim, x.hidden) + mat(x.hidden, x.q_dim)
-                + mat(2 * x.ffn, x.hidden) + mat(x.hidden, x.ffn)
+    def layer(x, narrow=True):
+        return (mat(x.q_dim + 2 * x.kv_dim, x.hidden, narrow) + mat(x.hidden, x.q_dim, narrow)
+                + mat(2 * x.ffn, x.hidden, narrow) + mat(x.hidden, x.ffn, narrow)
                 + 2 * (2 * x.hidden + 2 * x.head_dim))
     t, p = d.talker, d.predictor
     head_rows = {"full": d.talker_vocab + p.hidden, "talker": d.talker_vocab,
@@ -74,8 +78,8 @@ def weight_bytes(d, int8: bool, distinct: bool = False, mode: str = "full") -> i
     if mode != "predictor":
         total += t.layers * layer(t) + 2 * t.hidden
     if mode != "talker":
-        pred_layers = p.layers * layer(p)
-        pred_own = mat(d.code_vocab, p.hidden) + 2 * p.hidden  # each step's head and final gain
+        pred_layers = p.layers * layer(p, narrow=False)
+        pred_own = mat(d.code_vocab, p.hidden, narrow=False) + 2 * p.hidden  # each step's head, final gain
         total += (1 if distinct else d.n_steps) * pred_layers + d.n_steps * pred_own
     return total
 
@@ -99,7 +103,8 @@ def frame_bytes(d, lengths, int8: bool, distinct: bool = False, mode: str = "ful
 def launch_bytes(d, kind, li, lengths, int8: bool) -> int:
     """Algorithmic bytes of one kernel launch of a frame whose sessions hold
     `lengths` cached Talker positions.
-      GEMM:        the weight [n, k] once (bf16: 2nk; INT8: nk + 4n of row scales), plus
+      GEMM:        the weight [n, k] once (bf16: 2nk; INT8: nk + 4n of row scales, or
+                   2nk + 4n where the quantised values are held as halves), plus
                    the f32 logits a head writes (4 * m * n_logits); activations are
                    not counted (they could stay on chip).
       attn_paged:  per session, this layer's K and V over positions 0..L_b (the cache
@@ -109,7 +114,7 @@ def launch_bytes(d, kind, li, lengths, int8: bool) -> int:
                    session its embedding rows and f32 logits.
       others:      0 (predictor K/V is frame-local and could stay on chip)."""
     if kind == "gemm":
-        w = li.n * li.k + 4 * li.n if li.int8 else 2 * li.n * li.k
+        w = {0: 2 * li.n * li.k, 1: li.n * li.k + 4 * li.n, 2: 2 * li.n * li.k + 4 * li.n}[li.int8]
         return w + 4 * li.m * li.n_logits
     if kind == "attn_paged":
         t = d.talker

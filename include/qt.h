@@ -237,7 +237,11 @@ qt_status qt_workspace_bytes(const qt_model_cfg* cfg, int32_t max_batch, int32_t
  * predictor.codec_embed.{i}, predictor.lm_head.{i} for i < n_codebooks-1.
  * int8_mode 1 quantizes every decode GEMM weight (attention, FFN, projection, codec
  * head and predictor heads) with qt_quantize_int8's arithmetic; embeddings and norm
- * gains stay bf16.  Packing is enqueued on `stream`; the source tensors may be
+ * gains stay bf16.  The Talker's quantized matrices (and the codec head with the
+ * projection) are stored as int8, the code predictor's as the same integers in half
+ * (exact: |q| <= 127), since its matrices stay cached across its steps and its
+ * launches are bound by latency rather than bytes; the products are the same.
+ * Packing is enqueued on `stream`; the source tensors may be
  * freed once it has completed.  *out receives a handle for qt_frame_decode.
  * Range: in bf16 mode the GEMM weights are packed as IEEE half (exact for
  * |w| >= 2^-14, within 2^-25 below), so a weight matrix holding a finite entry with
@@ -397,7 +401,9 @@ typedef struct {
   int32_t layer;    /* decoder layer of the launch, -1 if none */
   int32_t m;        /* GEMM: activation rows; other kernels: sessions */
   int32_t n, k;     /* GEMM: weight rows and columns streamed (W is [n, k]); else 0 */
-  int32_t int8;     /* GEMM: 1 if the weight is INT8 + f32 row scales, 0 if bf16 */
+  int32_t int8;     /* GEMM weight storage: 0 half (bf16 mode); 1 int8 tiles + f32 row
+                       scales; 2 INT8-quantised values held as half tiles + f32 row
+                       scales (the code predictor's matrices in INT8 mode) */
   int32_t n_logits; /* GEMM: f32 logits written per row (head GEMMs), else 0 */
   char name[40];    /* kernel symbol with its template arguments, e.g. "k_gemm_mfma<2,2,false>" */
 } qt_launch_info;

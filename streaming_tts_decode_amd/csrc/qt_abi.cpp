@@ -74,6 +74,7 @@ namespace {
 struct MatSlot {
   size_t w = 0, s = 0;  // byte offsets of the weight rows and (INT8) the scales
   int N = 0, K = 0;
+  bool w8 = false;      // int8 tiles (else half tiles)
 };
 struct LayerSlots {
   size_t in_norm = 0, q_norm = 0, k_norm = 0, post_norm = 0;
@@ -98,12 +99,18 @@ struct Planner {
     off = align_up(off + (size_t)n * 2);
     return o;
   }
-  MatSlot mat(int N, int K) {
+  // INT8 mode quantises every decode GEMM weight; `narrow` stores the values as
+  // int8 tiles (the Talker's matrices, streamed from HBM every frame, where the
+  // bytes are the cost), otherwise as exact halves (the code predictor's, which
+  // stay in the memory-side cache across its 15 steps and whose launches are
+  // latency-bound: there unpacking int8 costs time and saving bytes gains none).
+  MatSlot mat(int N, int K, bool narrow) {
     MatSlot m;
     m.N = N;
     m.K = K;
     m.w = off;
-    off = align_up(off + (size_t)N * K * (i8 ? 1 : 2));
+    m.w8 = i8 && narrow;
+    off = align_up(off + (size_t)N * K * (m.w8 ? 1 : 2));
     if (i8) {
       m.s = off;
       off = align_up(off + (size_t)N * 4);
@@ -116,7 +123,7 @@ Plan make_plan(const qt_model_cfg& c, bool i8) {
   Planner P;
   P.i8 = i8;
   Plan plan;
-  auto layers = [&](const qt_decoder_cfg& d, std::vector<LayerSlots>& v) {
+  auto layers = [&](const qt_decoder_cfg& d, std::vector<LayerSlots>& v, bool narrow) {
     const int qd = d.n_q_heads * d.head_dim, kvd = d.n_kv_heads * d.head_dim;
     for (int l = 0; l < d.layers; ++l) {
       LayerSlots L;
@@ -124,21 +131,21 @@ Plan make_plan(const qt_model_cfg& c, bool i8) {
       L.q_norm = P.vec(d.head_dim);
       L.k_norm = P.vec(d.head_dim);
       L.post_norm = P.vec(d.hidden);
-      L.qkv = P.mat(qd + 2 * kvd, d.hidden);
-      L.o = P.mat(d.hidden, qd);
-      L.gu = P.mat(2 * d.ffn, d.hidden);
-      L.down = P.mat(d.hidden, d.ffn);
+      L.qkv = P.mat(qd + 2 * kvd, d.hidden, narrow);
+      L.o = P.mat(d.hidden, qd, narrow);
+      L.gu = P.mat(2 * d.ffn, d.hidden, narrow);
+      L.down = P.mat(d.hidden, d.ffn, narrow);
       v.push_back(L);
     }
   };
-  layers(c.talker, plan.tl);
+  layers(c.talker, plan.tl, true);
   plan.t_final = P.vec(c.talker.hidden);
-  plan.t_head = P.mat(c.talker_vocab + c.predictor.hidden, c.talker.hidden);
-  layers(c.predictor, plan.pl);
+  plan.t_head = P.mat(c.talker_vocab + c.predictor.hidden, c.talker.hidden, true);
+  layers(c.predictor, plan.pl, false);
   plan.p_final = P.vec(c.predictor.hidden);
   for (int i = 0; i < c.n_codebooks - 1; ++i) {
     plan.embeds.push_back(P.vec(c.code_vocab * c.predictor.hidden));
-    plan.heads.push_back(P.mat(c.code_vocab, c.predictor.hidden));
+    plan.heads.push_back(P.mat(c.code_vocab, c.predictor.hidden, false));
   }
   // q, k, v, o, gate, up, down per layer; codec head, projection, one head per step
   plan.n_mats = 7 * (c.talker.layers + c.predictor.layers) + 2 + (c.n_codebooks - 1);
@@ -370,6 +377,7 @@ GemmArgs gemm_act(const qt_model* m, const MatSlot& s, const uint16_t* act, int 
   GemmArgs a{};
   a.W = m->base + s.w;
   a.scale = m->i8 ? (const float*)(m->base + s.s) : nullptr;
+  a.w8 = s.w8 ? 1 : 0;
   a.N = s.N;
   a.K = s.K;
   a.row0 = 0;
@@ -510,7 +518,7 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
     if (g) {
       li.n = g->nrows;
       li.k = g->K;
-      li.int8 = g->scale != nullptr;
+      li.int8 = g->scale == nullptr ? 0 : (g->w8 ? 1 : 2);
       if (g->epi == EPI_HEAD) {
         const int hi = g->row0 + g->nrows < g->n_logits ? g->row0 + g->nrows : g->n_logits;
         li.n_logits = hi > g->row0 ? hi - g->row0 : 0;
@@ -574,7 +582,7 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
     g.u_ld = u_ld;
     g.ss_out = ss;
     g.ss_out_ld = ss_ld;
-    return plan_gemm(g.nrows, g.K, g.M, g.scale != nullptr, keep_w).rows_per_block;
+    return plan_gemm(g.nrows, g.K, g.M, g.w8 != 0, keep_w).rows_per_block;
   };
 
   // One decoder layer over M rows of residual x (row stride = hidden).  u: the
@@ -731,7 +739,7 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
     cur_step = 1;
     cur_layer = -1;
     QT_MARK(QT_KERNEL_PREDICTOR, "k_pred_persist", B, nullptr);
-    QT_LAUNCH(launch_pred_persist(a, m->i8 != 0, st));
+    QT_LAUNCH(launch_pred_persist(a, false, st));  // (predictor tiles are halves in both modes)
   } else if (mode != QT_MODE_TALKER) {
     keep_w = true;
     for (int k = 1; k < ncb; ++k) {
@@ -1209,7 +1217,7 @@ qt_status qt_load_weights(const qt_model_cfg* cfg, const qt_tensor* tensors, int
     m->pred_persist = 0;
     if (persistent && pred_persist_shapes(*cfg) && hipGetDevice(&dev) == hipSuccess &&
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-        cus == kPredBlocks && prepare_pred_persist(i8) == hipSuccess)
+        cus == kPredBlocks && prepare_pred_persist(false) == hipSuccess)
       m->pred_persist = 1;
   }
 
@@ -1285,8 +1293,10 @@ qt_status qt_load_weights(const qt_model_cfg* cfg, const qt_tensor* tensors, int
       mat_names.push_back(kvp.first);
     } else {
       float* sc = (float*)(m->base + d.mat->s) + d.row0;
-      e = launch_quantize((const uint16_t*)t.data, d.rows, d.cols, (int8_t*)(m->base + d.mat->w),
-                          d.step, sc, d.step, (int)d.cols, d.row0, s);
+      int8_t* q8 = d.mat->w8 ? (int8_t*)(m->base + d.mat->w) : nullptr;
+      uint16_t* qh = d.mat->w8 ? nullptr : (uint16_t*)(m->base + d.mat->w);
+      e = launch_quantize((const uint16_t*)t.data, d.rows, d.cols, q8, qh, d.step, sc, d.step,
+                          (int)d.cols, d.row0, s);
     }
     if (e != hipSuccess) {
       delete m;
@@ -1322,7 +1332,7 @@ qt_status qt_quantize_int8(const void* w_bf16, int64_t rows, int64_t cols, int8_
   if (!w_bf16 || !q || !scale) return fail(QT_E_INVALID_ARG, "a pointer is NULL");
   if (rows < 1 || cols < 1) return fail(QT_E_INVALID_ARG, "rows and cols must be >= 1");
   if (rows > 0x7fffffffLL) return fail(QT_E_SHAPE, "rows = %lld: at most 2^31-1", (long long)rows);
-  QT_HIP(launch_quantize((const uint16_t*)w_bf16, rows, cols, q, cols, scale, 1, 0, 0,
+  QT_HIP(launch_quantize((const uint16_t*)w_bf16, rows, cols, q, nullptr, cols, scale, 1, 0, 0,
                          (hipStream_t)stream));
   return ok();
 }
@@ -1336,7 +1346,7 @@ qt_status qt_model_export_int8(const qt_model* m, const char* name, int8_t* q, f
     return fail(QT_E_INVALID_ARG, "'%s' is not a decode GEMM weight", name);
   const Dest& d = it->second;
   hipStream_t s = (hipStream_t)stream;
-  QT_HIP(launch_untile_i8((const int8_t*)(m->base + d.mat->w), (int)d.rows, (int)d.cols, d.row0,
+  QT_HIP(launch_untile_i8(m->base + d.mat->w, !d.mat->w8, (int)d.rows, (int)d.cols, d.row0,
                           d.step, q, s));
   QT_HIP(hipMemcpy2DAsync(scale, 4, m->base + d.mat->s + (size_t)d.row0 * 4, (size_t)4 * d.step, 4,
                           (size_t)d.rows, hipMemcpyDeviceToDevice, s));

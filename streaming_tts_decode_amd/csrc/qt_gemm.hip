@@ -715,6 +715,10 @@ __global__ __launch_bounds__(256) void k_gemm_rows_pipe(GemmArgs a) {
 #pragma unroll
   for (int t = 0; t < TN; ++t) {
     const int nb = n0 + 16 * t + 4 * q;
+    float sc[4] = {1.f, 1.f, 1.f, 1.f};
+    if (a.scale)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sc[e] = a.scale[nb + e];
 #pragma unroll
     for (int u = 0; u < TM; ++u) {
       const int m = m0 + 16 * u + i;
@@ -722,7 +726,7 @@ __global__ __launch_bounds__(256) void k_gemm_rows_pipe(GemmArgs a) {
       const float inv = s_inv[m - mb];
       float v[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = acc[t][u][e] * inv;
+      for (int e = 0; e < 4; ++e) v[e] = acc[t][u][e] * sc[e] * inv;
       if (a.epi == EPI_STORE) {
         *reinterpret_cast<float4*>(a.out_f32 + (size_t)m * a.out_ld + nb) =
             make_float4(v[0], v[1], v[2], v[3]);
@@ -774,14 +778,30 @@ __global__ __launch_bounds__(256) void k_pack_tiled(const uint16_t* src, int row
   if (over) atomicOr(range_flag, 1u);
 }
 
-// Rows row0 + r*step of a tiled int8 [N][K] matrix -> row-major [rows][K].
-__global__ __launch_bounds__(256) void k_untile_i8(const int8_t* tiled, int rows, int K, int row0,
-                                                   int step, int8_t* out) {
+// Rows row0 + r*step of a tiled INT8-quantised [N][K] matrix -> row-major int8
+// [rows][K], from int8 tiles or from half tiles holding the integer values.
+__global__ __launch_bounds__(256) void k_untile_i8(const void* tiled, int half_src, int rows, int K,
+                                                   int row0, int step, int8_t* out) {
   const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
   const int kc = K >> 3;
   if (e >= (long long)rows * kc) return;
   const int r = (int)(e / kc), k = (int)(e - (long long)r * kc) << 3;
-  const uint2 v = *reinterpret_cast<const uint2*>(tiled + tiled_i8(row0 + r * step, k, K));
+  uint2 v;
+  if (half_src) {
+    const uint4 h = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(tiled) +
+                                                    tiled_bf16(row0 + r * step, k, K));
+    const uint32_t hw[4] = {h.x, h.y, h.z, h.w};
+    uint32_t b[2] = {0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int q = (int)h2f((uint16_t)(hw[j >> 1] >> (16 * (j & 1))));
+      b[j >> 2] |= ((uint32_t)q & 0xffu) << (8 * (j & 3));
+    }
+    v = make_uint2(b[0], b[1]);
+  } else {
+    v = *reinterpret_cast<const uint2*>(reinterpret_cast<const int8_t*>(tiled) +
+                                        tiled_i8(row0 + r * step, k, K));
+  }
   *reinterpret_cast<uint2*>(out + (size_t)r * K + k) = v;
 }
 
@@ -825,7 +845,7 @@ GemmPlan plan_gemm(int nrows, int K, int M, bool i8, bool keep, bool swiglu) {
 }
 
 void gemm_kernel_name(const GemmArgs& a, char* buf, int len) {
-  const bool i8 = a.scale != nullptr;
+  const bool i8 = a.w8 != 0;
   const GemmPlan p = plan_gemm(a.nrows, a.K, a.M, i8, a.keep_w != 0, a.epi == EPI_SWIGLU);
   snprintf(buf, len, "k_gemm<%d,%d,%d,%s,%s,%d>", p.nw, p.mt, p.g, i8 ? "true" : "false",
            a.keep_w ? "true" : "false", p.tiles);
@@ -842,7 +862,7 @@ hipError_t launch_gemm_rows(const GemmArgs& a, hipStream_t s) {
   // rows, then 64 x 64
   const long long big = (long long)((a.M + 127) / 128) * (a.nrows / 128);
   const long long mid = (long long)((a.M + 127) / 128) * (a.nrows / 64);
-  const bool i8 = a.scale != nullptr;
+  const bool i8 = a.w8 != 0;
   // (measured at 1024 rows: the direct form is faster for 128 x 128 blocks, the
   // copy-pipelined form for 64 x 128 and 64 x 64; stages of two K steps, three in
   // flight for 64 x 128 (72 KB of LDS, two blocks per CU) and four for 64 x 64)
@@ -870,7 +890,7 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
   if (a.epi == EPI_HEAD && ((a.n_logits % kGemmRows) || (a.argmax_range > a.n_logits)))
     return hipErrorInvalidValue;
   if ((a.epi == EPI_RESID || a.epi == EPI_HEAD) && a.u_gain && !a.ss_out) return hipErrorInvalidValue;
-  const bool i8 = a.scale != nullptr;
+  const bool i8 = a.w8 != 0;
   const GemmPlan p = plan_gemm(a.nrows, a.K, a.M, i8, a.keep_w != 0, a.epi == EPI_SWIGLU);
   if (a.keep_w) return i8 ? gemm_dispatch<true, true>(a, p, s) : gemm_dispatch<false, true>(a, p, s);
   return i8 ? gemm_dispatch<true, false>(a, p, s) : gemm_dispatch<false, false>(a, p, s);
@@ -886,12 +906,12 @@ hipError_t launch_pack_tiled(const uint16_t* src, int rows, int K, uint16_t* dst
   return hipGetLastError();
 }
 
-hipError_t launch_untile_i8(const int8_t* tiled, int rows, int K, int row0, int step, int8_t* out,
-                            hipStream_t s) {
+hipError_t launch_untile_i8(const void* tiled, bool half_src, int rows, int K, int row0, int step,
+                            int8_t* out, hipStream_t s) {
   if (rows <= 0 || K <= 0 || (K % 64) || row0 < 0 || step < 1) return hipErrorInvalidValue;
   const long long n = (long long)rows * (K / 8);
-  launch_kernel(k_untile_i8, dim3((unsigned)((n + 255) / 256)), dim3(256), s, tiled, rows, K, row0,
-                step, out);
+  launch_kernel(k_untile_i8, dim3((unsigned)((n + 255) / 256)), dim3(256), s, tiled,
+                half_src ? 1 : 0, rows, K, row0, step, out);
   return hipGetLastError();
 }
 

@@ -60,7 +60,9 @@ enum Epi : int {
 
 struct GemmArgs {
   const void* W;          // packed tiles (see above) of a half or int8 [N][K] matrix
-  const float* scale;     // [N] when INT8, else nullptr
+  const float* scale;     // [N] per-row scales of an INT8-quantised matrix, else nullptr
+  int w8;                 // 1: W holds int8 tiles; 0: half tiles (in INT8 mode, the
+                          // quantised values of a cache-resident matrix as exact halves)
   int keep_w;             // 1: the matrix is read again within the frame (predictor
                           // steps), so its loads go through the caches; 0: streamed
   int N, K;               // full matrix
@@ -443,13 +445,15 @@ hipError_t launch_frame_end(const FrameEndArgs& a, hipStream_t s);
 // a finite weight beyond the half range sets *range_flag (device word).
 hipError_t launch_pack_tiled(const uint16_t* src, int rows, int K, uint16_t* dst, int row0, int step,
                              uint32_t* range_flag, hipStream_t s);
-// Copy rows row0 + i*step (i < rows) of a tiled int8 [N][K] matrix out row-major.
-hipError_t launch_untile_i8(const int8_t* tiled, int rows, int K, int row0, int step, int8_t* out,
-                            hipStream_t s);
+// Copy rows row0 + i*step (i < rows) of a tiled INT8-quantised [N][K] matrix out
+// row-major as int8: from int8 tiles, or (half_src) from half tiles holding the values.
+hipError_t launch_untile_i8(const void* tiled, bool half_src, int rows, int K, int row0, int step,
+                            int8_t* out, hipStream_t s);
 // INT8 quantizer.  tiled_K == 0: q row r at q + r*q_row_stride; tiled_K > 0: source row r
-// becomes row row0 + r*q_row_stride of a tiled int8 [N][tiled_K] matrix at q.
+// becomes row row0 + r*q_row_stride of a tiled [N][tiled_K] matrix: int8 tiles at q, or,
+// when q_half is given, half tiles at q_half holding the same integer values.
 hipError_t launch_quantize(const uint16_t* w, long long rows, long long cols, int8_t* q,
-                           long long q_row_stride, float* scale, long long scale_stride,
-                           int tiled_K, long long row0, hipStream_t s);
+                           uint16_t* q_half, long long q_row_stride, float* scale,
+                           long long scale_stride, int tiled_K, long long row0, hipStream_t s);
 
 }  // namespace qt

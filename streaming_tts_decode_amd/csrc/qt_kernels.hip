@@ -800,9 +800,11 @@ __global__ __launch_bounds__(256) void k_frame_end(FrameEndArgs a) {
 
 // ---------------------------------------------------------------------------
 // Per-row symmetric INT8: s = max|w| / 127 (IEEE divide), q = clamp(rint(w / s), +-127).
+// With q_half the integers go to half tiles instead (exact: |q| <= 127).
 __global__ __launch_bounds__(256) void k_quantize(const uint16_t* w, long long cols, int8_t* q,
-                                                  long long q_stride, float* scale,
-                                                  long long s_stride, int tiled_K, long long row0) {
+                                                  uint16_t* q_half, long long q_stride,
+                                                  float* scale, long long s_stride, int tiled_K,
+                                                  long long row0) {
   __shared__ float part[4];
   const long long r = blockIdx.x;
   const int tid = threadIdx.x;
@@ -821,9 +823,13 @@ __global__ __launch_bounds__(256) void k_quantize(const uint16_t* w, long long c
       v = rintf(__fdiv_rn(bf2f(row[k]), sc));
       v = fminf(fmaxf(v, -127.f), 127.f);
     }
-    const size_t o = tiled_K ? tiled_i8((int)(row0 + r * q_stride), (int)k, tiled_K)
-                             : (size_t)(r * q_stride + k);
-    q[o] = (int8_t)(int)v;
+    if (q_half) {
+      q_half[tiled_bf16((int)(row0 + r * q_stride), (int)k, tiled_K)] = f2h(v);
+    } else {
+      const size_t o = tiled_K ? tiled_i8((int)(row0 + r * q_stride), (int)k, tiled_K)
+                               : (size_t)(r * q_stride + k);
+      q[o] = (int8_t)(int)v;
+    }
   }
 }
 
@@ -1328,11 +1334,12 @@ hipError_t launch_frame_end(const FrameEndArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_quantize(const uint16_t* w, long long rows, long long cols, int8_t* q,
-                           long long q_row_stride, float* scale, long long scale_stride,
-                           int tiled_K, long long row0, hipStream_t s) {
+                           uint16_t* q_half, long long q_row_stride, float* scale,
+                           long long scale_stride, int tiled_K, long long row0, hipStream_t s) {
   if (rows <= 0 || cols <= 0 || rows > 0x7fffffffLL) return hipErrorInvalidValue;
   if (tiled_K && (cols != tiled_K || tiled_K % 64 || row0 < 0)) return hipErrorInvalidValue;
-  launch_kernel(k_quantize, dim3((unsigned)rows), dim3(256), s, w, cols, q, q_row_stride,
+  if (q_half && !tiled_K) return hipErrorInvalidValue;
+  launch_kernel(k_quantize, dim3((unsigned)rows), dim3(256), s, w, cols, q, q_half, q_row_stride,
                      scale, scale_stride, tiled_K, row0);
   return hipGetLastError();
 }

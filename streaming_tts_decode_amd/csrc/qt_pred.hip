@@ -422,7 +422,7 @@ __device__ __forceinline__ float gemm_value(const Gemm& g, const float* red, con
   float v = 0.f;
 #pragma unroll
   for (int w = 0; w < NW; ++w) v += red[((w * 2 + t) * 16 + r16) * RED_LD + m];
-  if (I8) v *= g.scale[16 * g.rt[t] + r16];
+  if (g.scale) v *= g.scale[16 * g.rt[t] + r16];  // INT8-quantised (int8 or half values)
   if (g.norm) v *= s_inv[m];
   return v;
 }
