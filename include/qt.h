@@ -240,14 +240,18 @@ qt_status qt_workspace_bytes(const qt_model_cfg* cfg, int32_t max_batch, int32_t
  * gains stay bf16.  The Talker's quantized matrices (and the codec head with the
  * projection) are stored as int8, the code predictor's as the same integers in half
  * (exact: |q| <= 127), since its matrices stay cached across its steps and its
- * launches are bound by latency rather than bytes; the products are the same.
+ * launches are bound by latency rather than bytes; the products are the same.  The
+ * prompt prefill stays BF16 (same passage): in INT8 mode the Talker's matrices keep
+ * an unquantised half copy that only qt_prefill reads.
  * Packing is enqueued on `stream`; the source tensors may be
  * freed once it has completed.  *out receives a handle for qt_frame_decode.
  * Range: in bf16 mode the GEMM weights are packed as IEEE half (exact for
  * |w| >= 2^-14, within 2^-25 below), so a weight matrix holding a finite entry with
  * |w| > 65504 is refused with QT_E_UNSUPPORTED naming it; to find out, the call waits
- * for the packing to finish on `stream` in bf16 mode.  INT8 mode takes any finite
- * weights.  At decode time the GEMM inputs are half too: a residual row value x with
+ * for the packing to finish on `stream`.  INT8 mode takes any finite weights for
+ * decoding; a Talker weight beyond the half range then makes qt_prefill and
+ * qt_prefill_graph_create return QT_E_UNSUPPORTED naming it.  At decode time the
+ * GEMM inputs are half too: a residual row value x with
  * |x * gain| >= 65520 sets QT_STATUS_FP16_RANGE (see the status bits). */
 qt_status qt_load_weights(const qt_model_cfg* cfg, const qt_tensor* tensors, int32_t n_tensors,
                           int32_t int8_mode, void* packed, uint64_t packed_bytes, void* stream,
@@ -366,7 +370,10 @@ qt_status qt_prefill_workspace_bytes(const qt_model_cfg* cfg, int32_t rows, int3
 /* Enqueue a prefill on `stream` (no host synchronisation).  `workspace`: at least
  * qt_prefill_workspace_bytes, 256-byte aligned, not shared with a call in flight.
  * A sequence longer than max_pages * page_size sets QT_STATUS_KV_OVERFLOW and its
- * positions past the capacity are not stored. */
+ * positions past the capacity are not stored.  The Talker runs on its unquantised
+ * weights in both modes ("Qwen3-TTS Native v0.3.0", What changed: prefill stays
+ * BF16); QT_E_UNSUPPORTED if an INT8-mode model holds a Talker weight beyond the
+ * half range (see qt_load_weights). */
 qt_status qt_prefill(qt_model* model, const qt_prefill_args* args, const qt_kv_caches* kv,
                      void* workspace, uint64_t workspace_bytes, void* stream);
 

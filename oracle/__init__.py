@@ -216,8 +216,10 @@ class OracleModel:
     """The oracle's view of one set of model weights.
 
     ``weights`` maps tensor name -> bfloat16 bits (np.uint16).  With
-    ``int8=True`` every linear weight is quantized by the oracle's own
-    quantizer at construction (embeddings and norm gains stay bf16)."""
+    ``int8=True`` every linear weight of the decode path is quantized by the
+    oracle's own quantizer at construction (embeddings and norm gains stay bf16);
+    the prompt prefill keeps the bf16 weights ("Qwen3-TTS Native v0.3.0", What
+    changed: INT8 applies to decode GEMM weights and prefill stays BF16)."""
 
     def __init__(self, dims, weights: dict, int8: bool = False):
         self.dims = dims
@@ -227,19 +229,19 @@ class OracleModel:
         W = {k: np.ascontiguousarray(v, dtype=np.uint16) for k, v in weights.items()}
         self._keep.append(W)
 
-        def mat(name):
+        def mat(name, quant=int8):
             w = W[name]
             m = Mat()
             m.rows, m.cols = w.shape
             m.w = w.ctypes.data
-            if int8:
+            if quant:
                 q, s = quantize_int8(w)
                 self.quantized[name] = (q, s)
                 self._keep += [q, s]
                 m.q, m.s = q.ctypes.data, s.ctypes.data
             return m
 
-        def stack(prefix, d):
+        def stack(prefix, d, quant=int8):
             arr = (Layer * d.layers)()
             for l in range(d.layers):
                 p = f"{prefix}.layers.{l}."
@@ -248,9 +250,11 @@ class OracleModel:
                 L.q_norm = W[p + "q_norm"].ctypes.data
                 L.k_norm = W[p + "k_norm"].ctypes.data
                 L.post_norm = W[p + "post_norm"].ctypes.data
-                L.q, L.k, L.v = mat(p + "q_proj"), mat(p + "k_proj"), mat(p + "v_proj")
-                L.o = mat(p + "o_proj")
-                L.gate, L.up, L.down = mat(p + "gate_proj"), mat(p + "up_proj"), mat(p + "down_proj")
+                L.q, L.k, L.v = (mat(p + "q_proj", quant), mat(p + "k_proj", quant),
+                                 mat(p + "v_proj", quant))
+                L.o = mat(p + "o_proj", quant)
+                L.gate, L.up, L.down = (mat(p + "gate_proj", quant), mat(p + "up_proj", quant),
+                                        mat(p + "down_proj", quant))
             self._keep.append(arr)
             s = Stack()
             s.dims = Dims(d.layers, d.hidden, d.n_q, d.n_kv, d.head_dim, d.ffn,
@@ -275,7 +279,8 @@ class OracleModel:
         m.talker_vocab, m.code_vocab = dims.talker_vocab, dims.code_vocab
         m.cb0_range, m.n_codebooks = dims.cb0_range, dims.n_codebooks
         self.model = m
-        self.stacks = {"talker": m.talker, "predictor": m.predictor}
+        self.stacks = {"talker": m.talker, "predictor": m.predictor,
+                       "talker_prefill": stack("talker", dims.talker, False) if int8 else m.talker}
 
     # -- a session's Talker cache, float64 [layers, cap, n_kv, hd]
     def new_cache(self, capacity: int, k_bits=None, v_bits=None, which="talker"):
@@ -336,13 +341,9 @@ class OracleModel:
         x = bf16_to_f64(np.asarray(embeds_bits))
         T = x.shape[0]
         kc, vc = self.new_cache(max(T, capacity))
-        h = self.stack_forward("talker", x, 0, kc, vc)
+        h = self.stack_forward("talker_prefill", x, 0, kc, vc)  # bf16 weights in both modes
         W = self._keep[0]
-        if self.int8:
-            q, sc = self.quantized["talker.codec_head"]
-            logits0 = linear(W["talker.codec_head"], h[-1], q, sc)
-        else:
-            logits0 = linear(W["talker.codec_head"], h[-1])
+        logits0 = linear(W["talker.codec_head"], h[-1])
         return {"h": h, "logits0": logits0, "tok0": argmax(logits0[:self.dims.cb0_range]),
                 "kc": kc, "vc": vc}
 

@@ -75,6 +75,7 @@ struct MatSlot {
   size_t w = 0, s = 0;  // byte offsets of the weight rows and (INT8) the scales
   int N = 0, K = 0;
   bool w8 = false;      // int8 tiles (else half tiles)
+  size_t wh = 0;        // half tiles of the unquantised weights, for the prompt prefill
 };
 struct LayerSlots {
   size_t in_norm = 0, q_norm = 0, k_norm = 0, post_norm = 0;
@@ -114,6 +115,13 @@ struct Planner {
     if (i8) {
       m.s = off;
       off = align_up(off + (size_t)N * 4);
+    }
+    // The prompt prefill runs on the bf16 weights in INT8 mode too ("Qwen3-TTS
+    // Native v0.3.0", What changed): the Talker's matrices keep a half copy for it.
+    m.wh = m.w;
+    if (m.w8) {
+      m.wh = off;
+      off = align_up(off + (size_t)N * K * 2);
     }
     return m;
   }
@@ -355,6 +363,7 @@ Ws make_ws(const qt_model_cfg& c, int B, int max_pages) {
 struct qt_model {
   qt_model_cfg cfg;
   int i8;
+  std::string prefill_refusal;  // INT8 mode: a Talker weight the prefill's half copy cannot hold
   int pred_persist;  // frames may run the predictor as one launch (shapes, 256 CUs)
   Plan plan;
   std::map<std::string, Dest> dests;
@@ -371,13 +380,15 @@ namespace {
 
 const uint16_t* vp(const qt_model* m, size_t off) { return (const uint16_t*)(m->base + off); }
 
-// GEMM over a packed matrix with chunked half activations of act_ld rows.
+// GEMM over a packed matrix with chunked half activations of act_ld rows.  The
+// prompt prefill (prefill = true) takes the unquantised half copy in INT8 mode.
 GemmArgs gemm_act(const qt_model* m, const MatSlot& s, const uint16_t* act, int act_ld, int M,
-                  uint32_t* status) {
+                  uint32_t* status, bool prefill = false) {
   GemmArgs a{};
-  a.W = m->base + s.w;
-  a.scale = m->i8 ? (const float*)(m->base + s.s) : nullptr;
-  a.w8 = s.w8 ? 1 : 0;
+  const bool q = m->i8 && !prefill;
+  a.W = m->base + (prefill ? s.wh : s.w);
+  a.scale = q ? (const float*)(m->base + s.s) : nullptr;
+  a.w8 = q && s.w8 ? 1 : 0;
   a.N = s.N;
   a.K = s.K;
   a.row0 = 0;
@@ -392,8 +403,9 @@ GemmArgs gemm_act(const qt_model* m, const MatSlot& s, const uint16_t* act, int 
 // GEMM whose input is an RMSNorm: u = half(x * gain) as left by the producer of x,
 // whose sums of squares sit in `slots` slots of ss (stride ss_ld).
 GemmArgs gemm_norm(const qt_model* m, const MatSlot& s, const uint16_t* u, int u_ld,
-                   const float* ss, int ss_ld, int slots, float eps, int M, uint32_t* status) {
-  GemmArgs a = gemm_act(m, s, u, u_ld, M, status);
+                   const float* ss, int ss_ld, int slots, float eps, int M, uint32_t* status,
+                   bool prefill = false) {
+  GemmArgs a = gemm_act(m, s, u, u_ld, M, status, prefill);
   a.ss_in = ss;
   a.ss_in_ld = ss_ld;
   a.ss_in_slots = slots;
@@ -958,6 +970,11 @@ qt_status check_prefill_args(const qt_model* m, const qt_prefill_args* a, const 
 // Then the last row of each sequence: final norm, codec head, greedy token.
 qt_status enqueue_prefill(const qt_model* m, const qt_prefill_args* a, const qt_kv_caches* kv,
                           void* wsp, hipStream_t st) {
+  if (!m->prefill_refusal.empty())
+    return fail(QT_E_UNSUPPORTED,
+                "weight '%s' holds values beyond the IEEE half range (|w| > 65504): the prompt "
+                "prefill runs on the unquantised weights as halves, also in INT8 mode",
+                m->prefill_refusal.c_str());
   const qt_model_cfg& c = m->cfg;
   const qt_decoder_cfg& T = c.talker;
   const int R = a->rows, S = a->max_seqs;
@@ -997,7 +1014,7 @@ qt_status enqueue_prefill(const qt_model* m, const qt_prefill_args* a, const qt_
     const uint16_t* next_gain =
         vp(m, l + 1 < T.layers ? m->plan.tl[l + 1].in_norm : m->plan.t_final);
     qt_status r;
-    GemmArgs g = gemm_norm(m, L.qkv, u, R, ss, R, slots, T.rms_eps, R, a->status);
+    GemmArgs g = gemm_norm(m, L.qkv, u, R, ss, R, slots, T.rms_eps, R, a->status, true);
     g.epi = EPI_STORE;
     g.out_f32 = qkv;
     g.out_ld = w.qkv_ld;
@@ -1035,7 +1052,7 @@ qt_status enqueue_prefill(const qt_model* m, const qt_prefill_args* a, const qt_
     at.n_splits = kPrefillSplits;
     at.status = a->status;
     QT_LAUNCH(launch_prefill_attn(at, st));
-    g = gemm_act(m, L.o, o, R, R, a->status);
+    g = gemm_act(m, L.o, o, R, R, a->status, true);
     g.epi = EPI_RESID;
     g.out_f32 = x;
     g.out_ld = T.hidden;
@@ -1045,12 +1062,12 @@ qt_status enqueue_prefill(const qt_model* m, const qt_prefill_args* a, const qt_
     g.ss_out = ss;
     g.ss_out_ld = R;
     if ((r = run(g))) return r;
-    g = gemm_norm(m, L.gu, u, R, ss, R, resid_slots, T.rms_eps, R, a->status);
+    g = gemm_norm(m, L.gu, u, R, ss, R, resid_slots, T.rms_eps, R, a->status, true);
     g.epi = EPI_SWIGLU;
     g.u = ffn;
     g.u_ld = R;
     if ((r = run(g))) return r;
-    g = gemm_act(m, L.down, ffn, R, R, a->status);
+    g = gemm_act(m, L.down, ffn, R, R, a->status, true);
     g.epi = EPI_RESID;
     g.out_f32 = x;
     g.out_ld = T.hidden;
@@ -1077,7 +1094,8 @@ qt_status enqueue_prefill(const qt_model* m, const qt_prefill_args* a, const qt_
   pl.kv_len = a->kv_len;
   pl.status = a->status;
   QT_LAUNCH(launch_prefill_last(pl, st));
-  GemmArgs head = gemm_norm(m, m->plan.t_head, pl.u, S, pl.ss, S, 1, T.rms_eps, S, a->status);
+  GemmArgs head =
+      gemm_norm(m, m->plan.t_head, pl.u, S, pl.ss, S, 1, T.rms_eps, S, a->status, true);
   head.nrows = c.talker_vocab;
   head.epi = EPI_HEAD;
   head.logits = a->logits0;
@@ -1268,7 +1286,7 @@ qt_status qt_load_weights(const qt_model_cfg* cfg, const qt_tensor* tensors, int
   // a finite weight beyond the half range, read back once packing has finished
   uint32_t* range_flags = (uint32_t*)(m->base + m->plan.range_flags);
   std::vector<std::string> mat_names;
-  if (!i8) {
+  {
     const hipError_t e = hipMemsetAsync(range_flags, 0, (size_t)m->plan.n_mats * 4, s);
     if (e != hipSuccess) {
       delete m;
@@ -1297,13 +1315,23 @@ qt_status qt_load_weights(const qt_model_cfg* cfg, const qt_tensor* tensors, int
       uint16_t* qh = d.mat->w8 ? nullptr : (uint16_t*)(m->base + d.mat->w);
       e = launch_quantize((const uint16_t*)t.data, d.rows, d.cols, q8, qh, d.step, sc, d.step,
                           (int)d.cols, d.row0, s);
+      if (e == hipSuccess && d.mat->w8) {  // the prefill's half copy
+        if ((int)mat_names.size() >= m->plan.n_mats) {
+          delete m;
+          return fail(QT_E_STATE, "more GEMM weights than the plan counts");
+        }
+        e = launch_pack_tiled((const uint16_t*)t.data, (int)d.rows, (int)d.cols,
+                              (uint16_t*)(m->base + d.mat->wh), d.row0, d.step,
+                              range_flags + mat_names.size(), s);
+        mat_names.push_back(kvp.first);
+      }
     }
     if (e != hipSuccess) {
       delete m;
       return fail(QT_E_HIP, "packing '%s' failed: %s", kvp.first.c_str(), hipGetErrorString(e));
     }
   }
-  if (!i8) {
+  {
     std::vector<uint32_t> flags(mat_names.size(), 0u);
     hipError_t e = flags.empty() ? hipSuccess
                                  : hipMemcpyAsync(flags.data(), range_flags, flags.size() * 4,
@@ -1315,6 +1343,10 @@ qt_status qt_load_weights(const qt_model_cfg* cfg, const qt_tensor* tensors, int
     }
     for (size_t i = 0; i < flags.size(); ++i)
       if (flags[i]) {
+        if (i8) {  // decoding takes it (every row scaled); the prompt prefill refuses
+          if (m->prefill_refusal.empty()) m->prefill_refusal = mat_names[i];
+          continue;
+        }
         std::string name = mat_names[i];
         delete m;
         return fail(QT_E_UNSUPPORTED,

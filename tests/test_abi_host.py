@@ -78,12 +78,13 @@ def test_packed_bytes(qt):
     bf = qt.qt_packed_bytes(c, 0)
     assert raw <= bf <= raw + 256 * len(specs)
     i8 = qt.qt_packed_bytes(c, 1)
-    # INT8 mode: one byte per Talker / head / projection weight, the code predictor's
-    # quantized values as halves (two bytes), f32 scales for every weight row
+    # INT8 mode: one byte per Talker / head / projection weight plus its half copy
+    # for the prompt prefill, the code predictor's quantized values as halves (two
+    # bytes), f32 scales for every weight row
     w8 = sum(int(__import__("numpy").prod(s)) for n, s, k in specs
              if k == synth.WEIGHT and not n.startswith("predictor."))
     rows = sum(s[0] for _, s, k in specs if k == synth.WEIGHT)
-    assert raw - w8 + 4 * rows <= i8 <= raw - w8 + 4 * rows + 512 * len(specs)
+    assert raw + w8 + 4 * rows <= i8 <= raw + w8 + 4 * rows + 768 * len(specs)
     with pytest.raises(qt.QtError):
         qt.qt_packed_bytes(c, 2)
 

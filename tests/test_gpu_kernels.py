@@ -325,10 +325,11 @@ def test_int8_model_uses_quantizer_output(full_pm_i8, orc_full_i8):
 # ----------------------------------------------------------------- fp16 range
 def test_weight_beyond_half_range_is_refused(small_weights):
     """bf16 mode packs the GEMM weights as IEEE half: a weight matrix with a finite
-    entry above 65504 is refused at load, naming it; INT8 mode scales every row and
-    takes it."""
+    entry above 65504 is refused at load, naming it.  INT8 mode scales every row and
+    decodes with it, but its prompt prefill runs on the unquantised weights as
+    halves, so qt_prefill refuses, naming it."""
     import streaming_tts_decode_amd as qt
-    from streaming_tts_decode_amd.runtime import PackedModel
+    from streaming_tts_decode_amd.runtime import Decoder, PackedModel
     W = dict(small_weights)
     name = "talker.layers.1.down_proj"
     w = W[name].copy()
@@ -338,7 +339,15 @@ def test_weight_beyond_half_range_is_refused(small_weights):
         PackedModel(S, W, int8=False)
     assert e.value.status == 9 and name in str(e.value)
     pm8 = PackedModel(S, W, int8=True)
-    pm8.close()
+    try:
+        dec = Decoder(pm8, batch=1, max_pages=4)
+        dec.prefill_setup(16)
+        dec.prefill_inputs([synth.normal_bf16("range.prompt", (5, S.talker.hidden))])
+        with pytest.raises(qt.QtError) as e:
+            dec.prefill()
+        assert e.value.status == 9 and name in str(e.value)
+    finally:
+        pm8.close()
 
 
 def test_activation_beyond_half_range_sets_status(small_pm):

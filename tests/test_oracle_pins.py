@@ -405,6 +405,23 @@ def test_prefill_matches_brute_force(tiny_model, T):
     assert out["tok0"] == int(np.argmax(lg[: d.cb0_range]))
 
 
+def test_int8_mode_prefill_keeps_bf16_weights(tiny_model):
+    """INT8 quantizes the decode GEMM weights, while the prompt prefill stays BF16
+    ("Qwen3-TTS Native v0.3.0", What changed): an INT8 model's prefill equals the
+    bf16 model's exactly, and its decode frames do not."""
+    d, W, m16 = tiny_model
+    m8 = oracle.OracleModel(d, W, int8=True)
+    X = synth.normal_bf16("pin.prefill.int8", (5, d.talker.hidden))
+    a, b = m16.prefill(X, capacity=6), m8.prefill(X, capacity=6)
+    for k in ("h", "logits0", "kc", "vc"):
+        assert np.array_equal(a[k], b[k]), k
+    assert a["tok0"] == b["tok0"]
+    ti = synth.normal_bf16("pin.prefill.int8.next", (d.talker.hidden,))
+    fa, _ = m16.frame("full", a["kc"], a["vc"], 5, talker_in=ti)
+    fb, _ = m8.frame("full", b["kc"], b["vc"], 5, talker_in=ti)
+    assert not np.array_equal(fa["logits0"], fb["logits0"])
+
+
 def test_prefill_then_decode_equals_decoding_the_prompt(tiny_model):
     """Decode frames after a prefill of T positions see the same cache as decode
     frames after feeding the prompt one position at a time (brute force on the
