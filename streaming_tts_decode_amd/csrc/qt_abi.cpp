@@ -751,7 +751,7 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
     cur_step = 1;
     cur_layer = -1;
     QT_MARK(QT_KERNEL_PREDICTOR, "k_pred_persist", B, nullptr);
-    QT_LAUNCH(launch_pred_persist(a, false, st));  // (predictor tiles are halves in both modes)
+    QT_LAUNCH(launch_pred_persist(a, st));
   } else if (mode != QT_MODE_TALKER) {
     keep_w = true;
     for (int k = 1; k < ncb; ++k) {
@@ -1235,7 +1235,7 @@ qt_status qt_load_weights(const qt_model_cfg* cfg, const qt_tensor* tensors, int
     m->pred_persist = 0;
     if (persistent && pred_persist_shapes(*cfg) && hipGetDevice(&dev) == hipSuccess &&
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-        cus == kPredBlocks && prepare_pred_persist(false) == hipSuccess)
+        cus == kPredBlocks && prepare_pred_persist(cus) == hipSuccess)
       m->pred_persist = 1;
   }
 

@@ -418,10 +418,12 @@ struct PredPersistArgs {
   float* p_d;                     // [8][ldm][1024] down-projection partial of XCD x
   unsigned* sync;                 // kPredSyncWords, zero at launch (k_frame_begin clears it)
 };
-hipError_t launch_pred_persist(const PredPersistArgs& a, bool i8, hipStream_t s);
+hipError_t launch_pred_persist(const PredPersistArgs& a, hipStream_t s);
 // Per process and device, before the first launch (not under stream capture): the
-// kernel's 96 KB of dynamic LDS (which also keeps it to one block per CU).
-hipError_t prepare_pred_persist(bool i8);
+// kernel's 96 KB of dynamic LDS (which also keeps it to one block per CU), and a
+// check that the occupancy of that shape lets all kPredBlocks blocks be resident
+// on `cus` CUs at once (hipErrorInvalidConfiguration if not).
+hipError_t prepare_pred_persist(int cus);
 
 // Configuration of a loaded model, and the thread-local error text behind
 // qt_last_error() (qt_abi.cpp).

@@ -755,49 +755,49 @@ __global__ __launch_bounds__(NT) void k_pred_persist(PredPersistArgs a) {
   }
 }
 
+// The predictor's tiles are halves in both weight modes (INT8 mode holds its
+// quantised values as halves), so only the half form is instantiated.
 template <int MTX>
-hipError_t set_lds(bool i8) {
-  return i8 ? hipFuncSetAttribute((const void*)k_pred_persist<true, MTX>,
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds)
-            : hipFuncSetAttribute((const void*)k_pred_persist<false, MTX>,
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
+hipError_t prepare_one(int cus) {
+  const void* k = (const void*)k_pred_persist<false, MTX>;
+  hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLds);
+  if (e != hipSuccess) return e;
+  // every block waits on all the others at each stage: all of them must be
+  // resident at once, which the occupancy of this launch shape has to allow
+  int per_cu = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k, NT, kLds);
+  if (e != hipSuccess) return e;
+  return (long long)per_cu * cus >= kPredBlocks ? hipSuccess : hipErrorInvalidConfiguration;
 }
 
 template <int MTX>
-hipError_t pred_launch(const PredPersistArgs& a, bool i8, hipStream_t s) {
+hipError_t pred_launch(const PredPersistArgs& a, hipStream_t s) {
   const dim3 grid(kPredBlocks), block(NT);
-  if (g_launch_events.start) {
-    if (i8)
-      hipExtLaunchKernelGGL(k_pred_persist<true, MTX>, grid, block, kLds, s, g_launch_events.start,
-                            g_launch_events.stop, 0, a);
-    else
-      hipExtLaunchKernelGGL(k_pred_persist<false, MTX>, grid, block, kLds, s, g_launch_events.start,
-                            g_launch_events.stop, 0, a);
-  } else if (i8) {
-    hipLaunchKernelGGL((k_pred_persist<true, MTX>), grid, block, kLds, s, a);
-  } else {
+  if (g_launch_events.start)
+    hipExtLaunchKernelGGL(k_pred_persist<false, MTX>, grid, block, kLds, s, g_launch_events.start,
+                          g_launch_events.stop, 0, a);
+  else
     hipLaunchKernelGGL((k_pred_persist<false, MTX>), grid, block, kLds, s, a);
-  }
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t prepare_pred_persist(bool i8) {
-  hipError_t e = set_lds<1>(i8);
-  if (e == hipSuccess) e = set_lds<2>(i8);
-  if (e == hipSuccess) e = set_lds<4>(i8);
+hipError_t prepare_pred_persist(int cus) {
+  hipError_t e = prepare_one<1>(cus);
+  if (e == hipSuccess) e = prepare_one<2>(cus);
+  if (e == hipSuccess) e = prepare_one<4>(cus);
   return e;
 }
 
-hipError_t launch_pred_persist(const PredPersistArgs& a, bool i8, hipStream_t s) {
+hipError_t launch_pred_persist(const PredPersistArgs& a, hipStream_t s) {
   if (a.B < 1 || a.B > 32 || a.ldm < 2 * a.B || a.layers < 1 || a.layers > kPredMaxLayers ||
       a.n_steps < 1 || a.n_steps > kPredMaxSteps || a.ncb != a.n_steps + 1 || a.cand_ld < PV / 16)
     return hipErrorInvalidValue;
   // 16-row activation tiles of the largest step (step 1 carries 2B rows)
-  if (a.B <= 8) return pred_launch<1>(a, i8, s);
-  if (a.B <= 16) return pred_launch<2>(a, i8, s);
-  return pred_launch<4>(a, i8, s);
+  if (a.B <= 8) return pred_launch<1>(a, s);
+  if (a.B <= 16) return pred_launch<2>(a, s);
+  return pred_launch<4>(a, s);
 }
 
 }  // namespace qt
