@@ -904,10 +904,12 @@ struct PrefillWs {
   int qkv_ld, cand_ld;
 };
 
-// Key splits of the prefill attention: a 16-row tile's blocks of 32 keys are
-// dealt over this many blocks (4 x the blocks of one split; at 1024 rows the last
-// tile's 32 key blocks become 8 per split).
-constexpr int kPrefillSplits = 4;
+// Key splits of the prefill attention: a 64-row tile's blocks of 32 keys are
+// dealt over this many blocks (at 1024 rows the last tile's 32 key blocks become
+// 16 per split).  Measured on 1 x 1024 and 4 x 256 prompts: 2 splits 7.84 / 7.23
+// ms, 1 split 8.67 / 7.35, 4 splits 8.05 / 7.44, 8 splits 8.51 / 7.98 (with two
+// key blocks in flight, longer loops cost less than more partials to merge).
+constexpr int kPrefillSplits = 2;
 
 PrefillWs make_prefill_ws(const qt_model_cfg& c, int R, int S) {
   const qt_decoder_cfg& t = c.talker;
