@@ -863,9 +863,9 @@ hipError_t launch_gemm_rows(const GemmArgs& a, hipStream_t s) {
   const long long big = (long long)((a.M + 127) / 128) * (a.nrows / 128);
   const long long mid = (long long)((a.M + 127) / 128) * (a.nrows / 64);
   const bool i8 = a.w8 != 0;
-  // (measured at 1024 rows: the direct form is faster for 128 x 128 blocks, the
-  // copy-pipelined form for 64 x 128 and 64 x 64; stages of two K steps, three in
-  // flight for 64 x 128 (72 KB of LDS, two blocks per CU) and four for 64 x 64)
+  // (measured at 1024 rows: the direct form for 128 x 128 and 64 x 128 blocks, the
+  // copy-pipelined form for 64 x 64, with stages of two K steps, four in flight;
+  // splitting K in halves for twice the blocks gained nothing for the QKV shape)
   if (big >= 512) {
     const dim3 grid((a.M + 127) / 128, a.nrows / 128);
     if (i8) launch_kernel((k_gemm_rows<true, 4, 4>), grid, dim3(256), s, a);
