@@ -128,6 +128,14 @@ __device__ __forceinline__ float sum_q4(float v) {
   return __int_as_float(q[0]) + __int_as_float(q[1]);
 }
 
+// Maximum over the same four lanes, all four receiving it.
+__device__ __forceinline__ float max_q4(float v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_int(v), __float_as_int(v), false, false);
+  v = fmaxf(__int_as_float(p[0]), __int_as_float(p[1]));
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_int(v), __float_as_int(v), false, false);
+  return fmaxf(__int_as_float(q[0]), __int_as_float(q[1]));
+}
+
 __device__ __forceinline__ float lane_f32(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }

@@ -1034,32 +1034,41 @@ __global__ __launch_bounds__(256) void k_prefill_qk(PrefillQkArgs a, float theta
 // tile, KV head h, split z), eight waves: wave w serves rows 16(w/2) .. +15 of the
 // tile for query head 2h + w%2, so every staged key block serves 128 query rows.
 // For each sequence present in the tile, keys come in blocks of 32 (two pages),
-// blocks z, z + n_splits, ... to this split: K staged through LDS as half
-// [key][dim], V as half [dim][key] (a wave's lanes take consecutive keys, so the
-// transposing stores spread over the banks).  The sequence's page indices are
-// staged in LDS first (a prompt has fewer than 4096 positions, so at most 256
-// pages), and the K/V pieces of the next kPfRing key blocks are always in flight:
-// each is requested unconditionally (a block past the split's last re-reads the
-// last; positions past the tile's rows or on a bad page are zeroed when staged),
-// so that no wait for a page index or for a later block holds up the current one.
-// The split writes its unnormalised output, max and sum per (row, head);
-// k_prefill_attn_merge combines the splits in order.
-// Per block of keys:
-//   S = Q K^T   (v_mfma_f32_16x16x32_f16: 2 key tiles x 4 dim steps), masked to
-//               keys at or before the row's position;
-//   online softmax in the accumulator layout (lane l, element e: row 4(l>>4)+e,
-//               key l&15), row max and sum over the 16 lanes of a row (DPP);
-//   P -> per-wave LDS tile -> A operand; O += P V (8 dim tiles, one 32-key step).
+// blocks z, z + n_splits, ... to this split, staged through LDS: K as half
+// [key][dim], V as half [dim][key'] with the keys of each block in the order the
+// products below take them.  The sequence's page indices are staged in LDS first
+// (a prompt has fewer than 4096 positions, so at most 256 pages), and the K/V
+// pieces of the next kPfRing key blocks are always in flight: each is requested
+// unconditionally (a block past the split's last re-reads the last; positions past
+// the tile's rows or on a bad page are zeroed when staged), so that no wait for a
+// page index or for a later block holds up the current one.  The split writes its
+// unnormalised output, max and sum per (row, head); k_prefill_attn_merge combines
+// the splits in order.
+// The products are taken transposed, so that a lane holds one query row: lane l
+// (i = l & 15, g = l >> 4) owns row i of the wave's 16.  Per block of keys:
+//   S^T = K Q^T  (v_mfma_f32_16x16x32_f16, K from LDS as the A operand, the
+//                 row's Q as B; 2 key tiles x 4 dim steps): lane l holds the
+//                 scores of its row for keys 4g + e and 16 + 4g + e (e < 4);
+//   online softmax in the lane: max and sum over its 8 scores, then over the four
+//                 lanes of the row (lane swaps), one rescale factor per lane;
+//   O^T += V^T P^T: the lane's 8 probabilities, as halves, are the B operand
+//                 directly (MFMA K index 8g + j <-> key 4g + j, 16 + 4g + j - 4),
+//                 V^T staged in that key order is A; O^T's lane l holds row i,
+//                 dims 16 nb + 4g + e.
 constexpr int kKsLd = 136;  // half elements per staged key row (bank spread)
-constexpr int kVtLd = 40;   // half elements per staged dim row of V^T / per P row
+constexpr int kVtLd = 40;   // half elements per staged dim row of V^T
 constexpr int kAttnRows = 64;
 constexpr int kPfMaxPages = QT_PREFILL_MAX_ROWS / kPage;
 constexpr int kPfRing = 2;  // key blocks in flight
 
+// column of key k (0..31) of a block in the staged V^T: the order the products take
+__device__ __forceinline__ int vt_col(int k) {
+  return 8 * ((k & 15) >> 2) + 4 * (k >> 4) + (k & 3);
+}
+
 __global__ __launch_bounds__(512) void k_prefill_attn(PrefillAttnArgs a) {
   __shared__ __align__(16) _Float16 Ks[32 * kKsLd];
   __shared__ __align__(16) _Float16 Vt[128 * kVtLd];
-  __shared__ __align__(16) _Float16 Ps[8][16 * kVtLd];
   __shared__ int t_seq[kAttnRows], t_pos[kAttnRows];
   __shared__ int s_pg[kPfMaxPages];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1071,7 +1080,7 @@ __global__ __launch_bounds__(512) void k_prefill_attn(PrefillAttnArgs a) {
     t_seq[tid] = r < a.R ? a.rowinfo[2 * r] : -1;
     t_pos[tid] = r < a.R ? a.rowinfo[2 * r + 1] : 0;
   }
-  // Q operand: row 16 rg + i of the tile, dims [32 ks + 8 qg, +8), already scaled
+  // Q^T operand: row 16 rg + i of the tile, dims [32 ks + 8 qg, +8), already scaled
   f16x8 qf[4];
   {
     const int r = r0 + 16 * rg + i;
@@ -1085,21 +1094,11 @@ __global__ __launch_bounds__(512) void k_prefill_attn(PrefillAttnArgs a) {
     }
   }
   __syncthreads();
-  int row_seq[4], row_pos[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    row_seq[e] = t_seq[16 * rg + 4 * qg + e];
-    row_pos[e] = t_pos[16 * rg + 4 * qg + e];
-  }
+  const int row_seq = t_seq[16 * rg + i], row_pos = t_pos[16 * rg + i];
   f32x4 O[8];
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb) O[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m[4], l[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    m[e] = -INFINITY;
-    l[e] = 0.f;
-  }
+  float m = -INFINITY, l = 0.f;
   int seq_lo = 0x7fffffff, seq_hi = -1;
   for (int r = 0; r < kAttnRows; ++r)
     if (t_seq[r] >= 0) {
@@ -1111,6 +1110,7 @@ __global__ __launch_bounds__(512) void k_prefill_attn(PrefillAttnArgs a) {
   // staging pieces of 16 bytes: K piece (key tid >> 4, dims 8 (tid & 15)), V piece
   // (key tid & 31, dims 8 (tid >> 5))
   const int kkey = tid >> 4, kd8 = tid & 15, vkey = tid & 31, vd8 = tid >> 5;
+  const int vcol = vt_col(vkey);
   for (int seq = seq_lo; seq <= seq_hi; ++seq) {
     int pmax = -1;
     for (int r = 0; r < kAttnRows; ++r)
@@ -1141,6 +1141,7 @@ __global__ __launch_bounds__(512) void k_prefill_attn(PrefillAttnArgs a) {
       kr[d] = *reinterpret_cast<const uint4*>(a.k_pool + piece(d, kkey, kd8, klive[d]));
       vr[d] = *reinterpret_cast<const uint4*>(a.v_pool + piece(d, vkey, vd8, vlive[d]));
     }
+    const bool row_live = row_seq == seq;
     for (int n0 = 0; n0 < cnt; n0 += kPfRing) {
 #pragma unroll
       for (int d = 0; d < kPfRing; ++d) {
@@ -1156,8 +1157,8 @@ __global__ __launch_bounds__(512) void k_prefill_attn(PrefillAttnArgs a) {
           for (int w = 0; w < 4; ++w) {
             kh[2 * w] = (_Float16)bf_lo(kw[w]);
             kh[2 * w + 1] = (_Float16)bf_hi(kw[w]);
-            Vt[(8 * vd8 + 2 * w) * kVtLd + vkey] = (_Float16)bf_lo(vw[w]);
-            Vt[(8 * vd8 + 2 * w + 1) * kVtLd + vkey] = (_Float16)bf_hi(vw[w]);
+            Vt[(8 * vd8 + 2 * w) * kVtLd + vcol] = (_Float16)bf_lo(vw[w]);
+            Vt[(8 * vd8 + 2 * w + 1) * kVtLd + vcol] = (_Float16)bf_hi(vw[w]);
           }
           *reinterpret_cast<f16x8*>(Ks + kkey * kKsLd + 8 * kd8) = kh;
         }
@@ -1166,52 +1167,60 @@ __global__ __launch_bounds__(512) void k_prefill_attn(PrefillAttnArgs a) {
         kr[d] = *reinterpret_cast<const uint4*>(a.k_pool + piece(n + kPfRing, kkey, kd8, klive[d]));
         vr[d] = *reinterpret_cast<const uint4*>(a.v_pool + piece(n + kPfRing, vkey, vd8, vlive[d]));
         if (n >= cnt) continue;
+        // S^T for key tiles 0 and 1 of the block
         f32x4 S0 = f32x4{0.f, 0.f, 0.f, 0.f}, S1 = S0;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          const f16x8 b0 = *reinterpret_cast<const f16x8*>(Ks + i * kKsLd + 32 * ks + 8 * qg);
-          const f16x8 b1 = *reinterpret_cast<const f16x8*>(Ks + (16 + i) * kKsLd + 32 * ks + 8 * qg);
-          S0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qf[ks], b0, S0, 0, 0, 0);
-          S1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(qf[ks], b1, S1, 0, 0, 0);
+          const f16x8 a0 = *reinterpret_cast<const f16x8*>(Ks + i * kKsLd + 32 * ks + 8 * qg);
+          const f16x8 a1 = *reinterpret_cast<const f16x8*>(Ks + (16 + i) * kKsLd + 32 * ks + 8 * qg);
+          S0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, qf[ks], S0, 0, 0, 0);
+          S1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, qf[ks], S1, 0, 0, 0);
         }
-        const int k0 = 32 * kb + i, k1 = k0 + 16;
+        // the row's 8 scores: keys 32 kb + 4g + e and 32 kb + 16 + 4g + e
+        float sc[8];
+        float mx = -INFINITY;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const bool live = row_seq[e] == seq;
-          const float s0 = (live && k0 <= row_pos[e]) ? S0[e] : -INFINITY;
-          const float s1 = (live && k1 <= row_pos[e]) ? S1[e] : -INFINITY;
-          const float mn = fmaxf(m[e], row_max16(fmaxf(s0, s1)));
-          const float scale = mn == -INFINITY ? 1.f : expf(m[e] - mn);
-          const float p0 = s0 == -INFINITY ? 0.f : expf(s0 - mn);
-          const float p1 = s1 == -INFINITY ? 0.f : expf(s1 - mn);
-          l[e] = l[e] * scale + row_sum16(p0 + p1);
-          m[e] = mn;
-#pragma unroll
-          for (int nb = 0; nb < 8; ++nb) O[nb][e] *= scale;
-          Ps[wave][(4 * qg + e) * kVtLd + i] = (_Float16)p0;
-          Ps[wave][(4 * qg + e) * kVtLd + 16 + i] = (_Float16)p1;
+          const int k0 = 32 * kb + 4 * qg + e;
+          sc[e] = (row_live && k0 <= row_pos) ? S0[e] : -INFINITY;
+          sc[4 + e] = (row_live && k0 + 16 <= row_pos) ? S1[e] : -INFINITY;
         }
-        __builtin_amdgcn_wave_barrier();
-        const f16x8 pa = *reinterpret_cast<const f16x8*>(&Ps[wave][i * kVtLd + 8 * qg]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) mx = fmaxf(mx, sc[j]);
+        const float mn = fmaxf(m, max_q4(mx));
+        const float scale = mn == -INFINITY ? 1.f : expf(m - mn);
+        float rs = 0.f;
+        f16x8 pb;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float p = sc[j] == -INFINITY ? 0.f : expf(sc[j] - mn);
+          rs += p;
+          pb[j] = (_Float16)p;
+        }
+        l = l * scale + sum_q4(rs);
+        m = mn;
 #pragma unroll
         for (int nb = 0; nb < 8; ++nb) {
-          const f16x8 vb = *reinterpret_cast<const f16x8*>(Vt + (16 * nb + i) * kVtLd + 8 * qg);
-          O[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, vb, O[nb], 0, 0, 0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) O[nb][e] *= scale;
+          const f16x8 va = *reinterpret_cast<const f16x8*>(Vt + (16 * nb + i) * kVtLd + 8 * qg);
+          O[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, O[nb], 0, 0, 0);
         }
-        __builtin_amdgcn_wave_barrier();
       }
     }
   }
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int row = r0 + 16 * rg + 4 * qg + e;
-    if (row >= a.R) continue;
+  // O^T: lane l holds row 16 rg + i, dims 16 nb + 4g + e; the four lanes of a row
+  // hold the same max and sum
+  const int row = r0 + 16 * rg + i;
+  if (row < a.R) {
     float* pp = a.part + ((size_t)(row * a.n_q + qh) * nz + z) * 130;
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb) pp[16 * nb + i] = O[nb][e];
-    if (i == 0) {
-      pp[128] = m[e];
-      pp[129] = l[e];
+    for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pp[16 * nb + 4 * qg + e] = O[nb][e];  // (partials: 520-byte rows)
+    if (qg == 0) {
+      pp[128] = m;
+      pp[129] = l;
     }
   }
 }
