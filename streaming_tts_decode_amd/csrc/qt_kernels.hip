@@ -1081,16 +1081,20 @@ __global__ __launch_bounds__(512) void k_prefill_attn(PrefillAttnArgs a) {
     t_pos[tid] = r < a.R ? a.rowinfo[2 * r + 1] : 0;
   }
   // Q^T operand: row 16 rg + i of the tile, dims [32 ks + 8 qg, +8), already scaled
+  // by 1/sqrt(128), times log2(e): scores, maxima and the partials' max are in
+  // base-2 units, so every exponential is one exp2
   f16x8 qf[4];
   {
     const int r = r0 + 16 * rg + i;
     const float* qp = a.qkv + (size_t)(r < a.R ? r : 0) * a.qkv_ld + qh * 128 + 8 * qg;
+    constexpr float kLog2e = 1.4426950408889634f;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const float4 x0 = *reinterpret_cast<const float4*>(qp + 32 * ks);
       const float4 x1 = *reinterpret_cast<const float4*>(qp + 32 * ks + 4);
-      qf[ks] = f16x8{(_Float16)x0.x, (_Float16)x0.y, (_Float16)x0.z, (_Float16)x0.w,
-                     (_Float16)x1.x, (_Float16)x1.y, (_Float16)x1.z, (_Float16)x1.w};
+      qf[ks] = f16x8{(_Float16)(x0.x * kLog2e), (_Float16)(x0.y * kLog2e), (_Float16)(x0.z * kLog2e),
+                     (_Float16)(x0.w * kLog2e), (_Float16)(x1.x * kLog2e), (_Float16)(x1.y * kLog2e),
+                     (_Float16)(x1.z * kLog2e), (_Float16)(x1.w * kLog2e)};
     }
   }
   __syncthreads();
@@ -1188,12 +1192,12 @@ __global__ __launch_bounds__(512) void k_prefill_attn(PrefillAttnArgs a) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) mx = fmaxf(mx, sc[j]);
         const float mn = fmaxf(m, max_q4(mx));
-        const float scale = mn == -INFINITY ? 1.f : expf(m - mn);
+        const float scale = mn == -INFINITY ? 1.f : exp2f(m - mn);
         float rs = 0.f;
         f16x8 pb;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const float p = sc[j] == -INFINITY ? 0.f : expf(sc[j] - mn);
+          const float p = sc[j] == -INFINITY ? 0.f : exp2f(sc[j] - mn);
           rs += p;
           pb[j] = (_Float16)p;
         }
@@ -1240,7 +1244,7 @@ __global__ __launch_bounds__(256) void k_prefill_attn_merge(PrefillAttnArgs a) {
   for (int e = 0; e < 16; ++e) acc[e] = 0.f;
   for (int z = 0; z < nz; ++z) {
     const float mz = pp[z * 130 + 128];
-    const float w = mz == -INFINITY ? 0.f : expf(mz - M);
+    const float w = mz == -INFINITY ? 0.f : exp2f(mz - M);  // (maxima in base-2 units)
     L = fmaf(w, pp[z * 130 + 129], L);
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[e] = fmaf(w, pp[z * 130 + 16 * sub + e], acc[e]);
