@@ -1033,10 +1033,10 @@ __global__ __launch_bounds__(256) void k_prefill_qk(PrefillQkArgs a, float theta
 // Causal attention over packed sequences on the matrix cores.  Block (64-row
 // tile, KV head h, split z), eight waves: wave w serves rows 16(w/2) .. +15 of the
 // tile for query head 2h + w%2, so every staged key block serves 128 query rows.
-// For each sequence present in the tile, keys come in blocks of 32 (two pages),
-// blocks z, z + n_splits, ... to this split, staged through LDS: K as half
-// [key][dim], V as half [dim][key'] with the keys of each block in the order the
-// products below take them.  The sequence's page indices are staged in LDS first
+// For each sequence present in the tile, keys come in blocks of KB (64: four
+// pages), blocks z, z + n_splits, ... to this split, staged through LDS: K as half
+// [key][dim], V as half [dim][key'] with the keys of each 32-key group in the
+// order the products below take them.  The sequence's page indices are staged in LDS first
 // (a prompt has fewer than 4096 positions, so at most 256 pages), and the K/V
 // pieces of the next kPfRing key blocks are always in flight: each is requested
 // unconditionally (a block past the split's last re-reads the last; positions past
@@ -1047,28 +1047,33 @@ __global__ __launch_bounds__(256) void k_prefill_qk(PrefillQkArgs a, float theta
 // The products are taken transposed, so that a lane holds one query row: lane l
 // (i = l & 15, g = l >> 4) owns row i of the wave's 16.  Per block of keys:
 //   S^T = K Q^T  (v_mfma_f32_16x16x32_f16, K from LDS as the A operand, the
-//                 row's Q as B; 2 key tiles x 4 dim steps): lane l holds the
-//                 scores of its row for keys 4g + e and 16 + 4g + e (e < 4);
-//   online softmax in the lane: max and sum over its 8 scores, then over the four
-//                 lanes of the row (lane swaps), one rescale factor per lane;
-//   O^T += V^T P^T: the lane's 8 probabilities, as halves, are the B operand
-//                 directly (MFMA K index 8g + j <-> key 4g + j, 16 + 4g + j - 4),
-//                 V^T staged in that key order is A; O^T's lane l holds row i,
-//                 dims 16 nb + 4g + e.
+//                 row's Q as B; KB/16 key tiles x 4 dim steps): lane l holds the
+//                 scores of its row for keys 16 t + 4g + e (e < 4);
+//   online softmax in the lane: max and sum over its KB/4 scores, then over the
+//                 four lanes of the row (lane swaps), one rescale factor per lane;
+//   O^T += V^T P^T, one step per 32-key group: the lane's 8 probabilities of the
+//                 group, as halves, are the B operand directly (MFMA K index
+//                 8g + j <-> key 4g + j, 16 + 4g + j - 4 of the group), V^T staged
+//                 in that key order is A; O^T's lane l holds row i, dims
+//                 16 nb + 4g + e.
 constexpr int kKsLd = 136;  // half elements per staged key row (bank spread)
-constexpr int kVtLd = 40;   // half elements per staged dim row of V^T
 constexpr int kAttnRows = 64;
 constexpr int kPfMaxPages = QT_PREFILL_MAX_ROWS / kPage;
 constexpr int kPfRing = 2;  // key blocks in flight
+constexpr int kPfKeys = 64;  // keys per staged block
 
-// column of key k (0..31) of a block in the staged V^T: the order the products take
+// column of key k (0..31) of a 32-key group in the staged V^T: the order the
+// products take them
 __device__ __forceinline__ int vt_col(int k) {
   return 8 * ((k & 15) >> 2) + 4 * (k >> 4) + (k & 3);
 }
 
+template <int KB>
 __global__ __launch_bounds__(512) void k_prefill_attn(PrefillAttnArgs a) {
-  __shared__ __align__(16) _Float16 Ks[32 * kKsLd];
-  __shared__ __align__(16) _Float16 Vt[128 * kVtLd];
+  constexpr int NG = KB / 32;       // 32-key groups per block (one P.V step each)
+  constexpr int VLD = KB + 8;       // half elements per staged dim row of V^T
+  __shared__ __align__(16) _Float16 Ks[KB * kKsLd];
+  __shared__ __align__(16) _Float16 Vt[128 * VLD];
   __shared__ int t_seq[kAttnRows], t_pos[kAttnRows];
   __shared__ int s_pg[kPfMaxPages];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -1111,8 +1116,8 @@ __global__ __launch_bounds__(512) void k_prefill_attn(PrefillAttnArgs a) {
     }
   const size_t head_off = (size_t)h * (kPage * 128);
   const size_t page_elems = (size_t)a.n_kv * (kPage * 128);
-  // staging pieces of 16 bytes: K piece (key tid >> 4, dims 8 (tid & 15)), V piece
-  // (key tid & 31, dims 8 (tid >> 5))
+  // staging pieces of 16 bytes, NG of each per thread: K piece (key (tid >> 4) +
+  // 32 p, dims 8 (tid & 15)), V piece (key (tid & 31) + 32 p, dims 8 (tid >> 5))
   const int kkey = tid >> 4, kd8 = tid & 15, vkey = tid & 31, vd8 = tid >> 5;
   const int vcol = vt_col(vkey);
   for (int seq = seq_lo; seq <= seq_hi; ++seq) {
@@ -1120,10 +1125,10 @@ __global__ __launch_bounds__(512) void k_prefill_attn(PrefillAttnArgs a) {
     for (int r = 0; r < kAttnRows; ++r)
       if (t_seq[r] == seq && t_pos[r] > pmax) pmax = t_pos[r];
     if (pmax < 0) continue;
-    const int nblk = pmax / 32 + 1;
+    const int nblk = pmax / KB + 1;
     if (z >= nblk) continue;
     const int cnt = (nblk - z + nz - 1) / nz;  // key blocks z, z + nz, ... of this split
-    const int npg = min(min(2 * nblk, a.max_pages), kPfMaxPages);
+    const int npg = min(min(nblk * (KB / kPage), a.max_pages), kPfMaxPages);
     __syncthreads();  // the previous sequence's page indices are no longer read
     for (int pi = tid; pi < npg; pi += 512) {
       const int pg = a.page_table[(size_t)seq * a.max_pages + pi];
@@ -1133,18 +1138,22 @@ __global__ __launch_bounds__(512) void k_prefill_attn(PrefillAttnArgs a) {
     // element offset of the piece (key, d8) of the split's key block n (clamped to
     // its last), and whether it holds a live key
     auto piece = [&](int n, int key, int d8, bool& live) -> size_t {
-      const int kpos = 32 * (z + nz * min(n, cnt - 1)) + key, pi = kpos >> 4;
+      const int kpos = KB * (z + nz * min(n, cnt - 1)) + key, pi = kpos >> 4;
       const int pg = pi < npg ? s_pg[pi] : -1;
       live = n < cnt && kpos <= pmax && pg >= 0;
       return (size_t)(pg >= 0 ? pg : 0) * page_elems + head_off + (size_t)(kpos & 15) * 128 + 8 * d8;
     };
-    uint4 kr[kPfRing], vr[kPfRing];
-    bool klive[kPfRing], vlive[kPfRing];
+    uint4 kr[kPfRing][NG], vr[kPfRing][NG];
+    bool klive[kPfRing][NG], vlive[kPfRing][NG];
+    auto request = [&](int d, int n) {
 #pragma unroll
-    for (int d = 0; d < kPfRing; ++d) {
-      kr[d] = *reinterpret_cast<const uint4*>(a.k_pool + piece(d, kkey, kd8, klive[d]));
-      vr[d] = *reinterpret_cast<const uint4*>(a.v_pool + piece(d, vkey, vd8, vlive[d]));
-    }
+      for (int g = 0; g < NG; ++g) {
+        kr[d][g] = *reinterpret_cast<const uint4*>(a.k_pool + piece(n, kkey + 32 * g, kd8, klive[d][g]));
+        vr[d][g] = *reinterpret_cast<const uint4*>(a.v_pool + piece(n, vkey + 32 * g, vd8, vlive[d][g]));
+      }
+    };
+#pragma unroll
+    for (int d = 0; d < kPfRing; ++d) request(d, d);
     const bool row_live = row_seq == seq;
     for (int n0 = 0; n0 < cnt; n0 += kPfRing) {
 #pragma unroll
@@ -1152,54 +1161,57 @@ __global__ __launch_bounds__(512) void k_prefill_attn(PrefillAttnArgs a) {
         const int n = n0 + d, kb = z + nz * n;
         __syncthreads();  // the previous block of keys is consumed
         if (n < cnt) {
-          const uint4 kq = klive[d] ? kr[d] : make_uint4(0, 0, 0, 0);
-          const uint4 vq = vlive[d] ? vr[d] : make_uint4(0, 0, 0, 0);
-          const uint32_t kw[4] = {kq.x, kq.y, kq.z, kq.w};
-          const uint32_t vw[4] = {vq.x, vq.y, vq.z, vq.w};
-          f16x8 kh;
 #pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            kh[2 * w] = (_Float16)bf_lo(kw[w]);
-            kh[2 * w + 1] = (_Float16)bf_hi(kw[w]);
-            Vt[(8 * vd8 + 2 * w) * kVtLd + vcol] = (_Float16)bf_lo(vw[w]);
-            Vt[(8 * vd8 + 2 * w + 1) * kVtLd + vcol] = (_Float16)bf_hi(vw[w]);
+          for (int g = 0; g < NG; ++g) {
+            const uint4 kq = klive[d][g] ? kr[d][g] : make_uint4(0, 0, 0, 0);
+            const uint4 vq = vlive[d][g] ? vr[d][g] : make_uint4(0, 0, 0, 0);
+            const uint32_t kw[4] = {kq.x, kq.y, kq.z, kq.w};
+            const uint32_t vw[4] = {vq.x, vq.y, vq.z, vq.w};
+            f16x8 kh;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+              kh[2 * w] = (_Float16)bf_lo(kw[w]);
+              kh[2 * w + 1] = (_Float16)bf_hi(kw[w]);
+              Vt[(8 * vd8 + 2 * w) * VLD + 32 * g + vcol] = (_Float16)bf_lo(vw[w]);
+              Vt[(8 * vd8 + 2 * w + 1) * VLD + 32 * g + vcol] = (_Float16)bf_hi(vw[w]);
+            }
+            *reinterpret_cast<f16x8*>(Ks + (kkey + 32 * g) * kKsLd + 8 * kd8) = kh;
           }
-          *reinterpret_cast<f16x8*>(Ks + kkey * kKsLd + 8 * kd8) = kh;
         }
         __syncthreads();
-        // the ring slot is free: key block n + kPfRing is requested now
-        kr[d] = *reinterpret_cast<const uint4*>(a.k_pool + piece(n + kPfRing, kkey, kd8, klive[d]));
-        vr[d] = *reinterpret_cast<const uint4*>(a.v_pool + piece(n + kPfRing, vkey, vd8, vlive[d]));
+        request(d, n + kPfRing);  // the ring slot is free: key block n + kPfRing
         if (n >= cnt) continue;
-        // S^T for key tiles 0 and 1 of the block
-        f32x4 S0 = f32x4{0.f, 0.f, 0.f, 0.f}, S1 = S0;
+        // S^T for the block's 2 NG key tiles: lane l holds its row's scores for
+        // keys KB kb + 16 t + 4g + e
+        f32x4 S[2 * NG];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const f16x8 a0 = *reinterpret_cast<const f16x8*>(Ks + i * kKsLd + 32 * ks + 8 * qg);
-          const f16x8 a1 = *reinterpret_cast<const f16x8*>(Ks + (16 + i) * kKsLd + 32 * ks + 8 * qg);
-          S0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, qf[ks], S0, 0, 0, 0);
-          S1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, qf[ks], S1, 0, 0, 0);
-        }
-        // the row's 8 scores: keys 32 kb + 4g + e and 32 kb + 16 + 4g + e
-        float sc[8];
+        for (int t = 0; t < 2 * NG; ++t) S[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+          for (int t = 0; t < 2 * NG; ++t) {
+            const f16x8 ka = *reinterpret_cast<const f16x8*>(Ks + (16 * t + i) * kKsLd + 32 * ks + 8 * qg);
+            S[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qf[ks], S[t], 0, 0, 0);
+          }
+        float sc[8 * NG];
         float mx = -INFINITY;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int k0 = 32 * kb + 4 * qg + e;
-          sc[e] = (row_live && k0 <= row_pos) ? S0[e] : -INFINITY;
-          sc[4 + e] = (row_live && k0 + 16 <= row_pos) ? S1[e] : -INFINITY;
-        }
+        for (int t = 0; t < 2 * NG; ++t)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) mx = fmaxf(mx, sc[j]);
+          for (int e = 0; e < 4; ++e) {
+            const int k = KB * kb + 16 * t + 4 * qg + e;
+            sc[4 * t + e] = (row_live && k <= row_pos) ? S[t][e] : -INFINITY;
+            mx = fmaxf(mx, sc[4 * t + e]);
+          }
         const float mn = fmaxf(m, max_q4(mx));
         const float scale = mn == -INFINITY ? 1.f : exp2f(m - mn);
         float rs = 0.f;
-        f16x8 pb;
+        f16x8 pb[NG];  // 32-key group g: MFMA K index 8 qg + j <-> tile 2g + (j >> 2), e = j & 3
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < 8 * NG; ++j) {
           const float p = sc[j] == -INFINITY ? 0.f : exp2f(sc[j] - mn);
           rs += p;
-          pb[j] = (_Float16)p;
+          pb[j >> 3][j & 7] = (_Float16)p;
         }
         l = l * scale + sum_q4(rs);
         m = mn;
@@ -1207,8 +1219,11 @@ __global__ __launch_bounds__(512) void k_prefill_attn(PrefillAttnArgs a) {
         for (int nb = 0; nb < 8; ++nb) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) O[nb][e] *= scale;
-          const f16x8 va = *reinterpret_cast<const f16x8*>(Vt + (16 * nb + i) * kVtLd + 8 * qg);
-          O[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb, O[nb], 0, 0, 0);
+#pragma unroll
+          for (int g = 0; g < NG; ++g) {
+            const f16x8 va = *reinterpret_cast<const f16x8*>(Vt + (16 * nb + i) * VLD + 32 * g + 8 * qg);
+            O[nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, pb[g], O[nb], 0, 0, 0);
+          }
         }
       }
     }
@@ -1388,7 +1403,7 @@ hipError_t launch_prefill_qk(const PrefillQkArgs& a, int R, float theta, hipStre
 hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t s) {
   if (a.R < 16 || (a.R % 16) || a.n_q != 2 * a.n_kv) return hipErrorInvalidValue;
   if (a.n_splits < 1 || a.n_splits > 64) return hipErrorInvalidValue;
-  launch_kernel(k_prefill_attn, dim3((a.R + kAttnRows - 1) / kAttnRows, a.n_kv, a.n_splits),
+  launch_kernel(k_prefill_attn<kPfKeys>, dim3((a.R + kAttnRows - 1) / kAttnRows, a.n_kv, a.n_splits),
                 dim3(512), s, a);
   launch_kernel(k_prefill_attn_merge, dim3(a.R / 16, a.n_kv), dim3(256), s, a);
   return hipGetLastError();
