@@ -1023,6 +1023,7 @@ qt_status enqueue_prefill(const qt_model* m, const qt_prefill_args* a, const qt_
     if ((r = run(g))) return r;
     PrefillQkArgs q{};
     q.qkv = qkv;
+    q.R = R;
     q.qkv_ld = w.qkv_ld;
     q.n_q = T.n_q_heads;
     q.n_kv = T.n_kv_heads;

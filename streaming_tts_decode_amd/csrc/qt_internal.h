@@ -246,6 +246,7 @@ struct PrefillBeginArgs {
 
 struct PrefillQkArgs {
   float* qkv;               // [R][qkv_ld]: q is replaced by its normalised, rotated, scaled form
+  int R;                    // rows
   int qkv_ld, n_q, n_kv;
   const uint16_t* q_norm;
   const uint16_t* k_norm;

@@ -992,42 +992,67 @@ __global__ __launch_bounds__(256) void k_prefill_begin(PrefillBeginArgs a) {
   if (tid == 0) a.ss[r] = part[0] + part[1] + part[2] + part[3];
 }
 
-// Per (row, KV head h): query heads 2h, 2h+1 and key head h normalised and rotated at
-// the row's position (the same arithmetic as a decode step), one vector per wave
-// (waves 0, 1: the query heads; wave 2: the key; wave 3: the value), lane l holding
-// dimensions l and l + 64; q is stored back scaled by 1/sqrt(128), the key (bf16)
-// and the raw value go to the page slot.
+// Per (kQkRows rows, KV head h): query heads 2h, 2h+1 and key head h normalised and
+// rotated at each row's position (the same arithmetic as a decode step), one vector
+// per wave (waves 0, 1: the query heads; wave 2: the key; wave 3: the value), lane l
+// holding dimensions l and l + 64; q is stored back scaled by 1/sqrt(128), the key
+// (bf16) and the raw value go to the page slot.  All of the block's rows are loaded
+// before any is used, and the rotation's frequency is computed once per lane.
+constexpr int kQkRows = 4;
 __global__ __launch_bounds__(256) void k_prefill_qk(PrefillQkArgs a, float theta_log2) {
-  const int r = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int r0 = blockIdx.x * kQkRows, h = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int seq = a.rowinfo[2 * r], p = seq >= 0 ? a.rowinfo[2 * r + 1] : 0;
-  float* row = a.qkv + (size_t)r * a.qkv_ld;
   const int q_dim = a.n_q * 128, kv_dim = a.n_kv * 128;
   const int col = wave < 2 ? (2 * h + wave) * 128 : q_dim + (wave == 3 ? kv_dim : 0) + h * 128;
-  float v0 = row[col + lane], v1 = row[col + lane + 64];
+  int seq[kQkRows], pos[kQkRows];
+  float v0[kQkRows], v1[kQkRows];
+#pragma unroll
+  for (int rr = 0; rr < kQkRows; ++rr) {
+    const int r = r0 + rr;
+    const bool in = r < a.R;
+    const float* row = a.qkv + (size_t)(in ? r : 0) * a.qkv_ld;
+    seq[rr] = in ? a.rowinfo[2 * r] : -1;
+    pos[rr] = in ? a.rowinfo[2 * r + 1] : 0;
+    v0[rr] = row[col + lane];
+    v1[rr] = row[col + lane + 64];
+  }
   const uint16_t* gain = wave < 2 ? a.q_norm : a.k_norm;
-  if (wave < 3)  // the value is taken raw
-    norm_rope_pair(v0, v1, bf2f(gain[lane]), bf2f(gain[lane + 64]), a.eps,
-                   rope_inv_rev(lane, theta_log2), p);
+  const float g0 = bf2f(gain[lane]), g1 = bf2f(gain[lane + 64]);
+  const double inv_rev = rope_inv_rev(lane, theta_log2);
+#pragma unroll
+  for (int rr = 0; rr < kQkRows; ++rr) {
+    const int p = seq[rr] >= 0 ? pos[rr] : 0;
+    if (wave < 3)  // the value is taken raw
+      norm_rope_pair(v0[rr], v1[rr], g0, g1, a.eps, inv_rev, p);
+  }
   if (wave < 2) {
-    row[col + lane] = v0 * kInvSqrtHd;
-    row[col + lane + 64] = v1 * kInvSqrtHd;
+#pragma unroll
+    for (int rr = 0; rr < kQkRows; ++rr) {
+      if (r0 + rr >= a.R) break;
+      float* row = a.qkv + (size_t)(r0 + rr) * a.qkv_ld;
+      row[col + lane] = v0[rr] * kInvSqrtHd;
+      row[col + lane + 64] = v1[rr] * kInvSqrtHd;
+    }
     return;
   }
-  if (seq < 0) return;
-  if (p >= a.max_pages * kPage) {
-    if (wave == 2 && lane == 0) atomicOr(a.status, QT_STATUS_KV_OVERFLOW);
-    return;
-  }
-  const int pg = a.page_table[(size_t)seq * a.max_pages + p / kPage];
-  if (pg < 0 || pg >= a.num_pages) {
-    if (wave == 2 && lane == 0) atomicOr(a.status, QT_STATUS_BAD_PAGE);
-    return;
-  }
-  const size_t off = ((size_t)pg * a.n_kv + h) * (kPage * 128) + (size_t)(p % kPage) * 128;
   uint16_t* dst = wave == 2 ? a.k_pool : a.v_pool;
-  dst[off + lane] = f2bf(v0);
-  dst[off + lane + 64] = f2bf(v1);
+#pragma unroll
+  for (int rr = 0; rr < kQkRows; ++rr) {
+    const int sq = seq[rr], p = pos[rr];
+    if (sq < 0) continue;  // (also rows past R)
+    if (p >= a.max_pages * kPage) {
+      if (wave == 2 && lane == 0) atomicOr(a.status, QT_STATUS_KV_OVERFLOW);
+      continue;
+    }
+    const int pg = a.page_table[(size_t)sq * a.max_pages + p / kPage];
+    if (pg < 0 || pg >= a.num_pages) {
+      if (wave == 2 && lane == 0) atomicOr(a.status, QT_STATUS_BAD_PAGE);
+      continue;
+    }
+    const size_t off = ((size_t)pg * a.n_kv + h) * (kPage * 128) + (size_t)(p % kPage) * 128;
+    dst[off + lane] = f2bf(v0[rr]);
+    dst[off + lane + 64] = f2bf(v1[rr]);
+  }
 }
 
 // Causal attention over packed sequences on the matrix cores.  Block (64-row
@@ -1397,7 +1422,9 @@ hipError_t launch_prefill_begin(const PrefillBeginArgs& a, hipStream_t s) {
 }
 hipError_t launch_prefill_qk(const PrefillQkArgs& a, int R, float theta, hipStream_t s) {
   if (R < 1 || a.n_q != 2 * a.n_kv) return hipErrorInvalidValue;
-  launch_kernel(k_prefill_qk, dim3(R, a.n_kv), dim3(256), s, a, (float)log2((double)theta));
+  if (a.R != R) return hipErrorInvalidValue;
+  launch_kernel(k_prefill_qk, dim3((R + kQkRows - 1) / kQkRows, a.n_kv), dim3(256), s, a,
+                (float)log2((double)theta));
   return hipGetLastError();
 }
 hipError_t launch_prefill_attn(const PrefillAttnArgs& a, hipStream_t s) {
