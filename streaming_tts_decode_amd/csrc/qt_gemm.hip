@@ -444,11 +444,59 @@ __device__ __forceinline__ void rows_tile(int& mblk, int& nblk) {
   mblk = t - nblk * nM;
 }
 
+// Norm factors of a block's BM activation rows mb .. mb + BM - 1, the consumer side
+// of an RMSNorm: s_inv[r] = 1 / sqrt(sum of row mb + r's ss_in slots / K + eps), or 1
+// without a norm.  The slots are [slots][ss_in_ld] floats.  Each of the NT threads
+// takes four consecutive rows of every G-th slot (G = NT / (BM / 4)) and issues all
+// of its loads before adding any, so the sums cost one memory round trip rather
+// than one per slot; the G partials are then added in order through LDS.  (M is a
+// multiple of 16, so a group of four rows lies wholly before or wholly past M.)
+template <int BM, int NT>
+__device__ __forceinline__ void norm_factors(const GemmArgs& a, int mb, float* s_inv,
+                                             float (*s_part)[BM]) {
+  constexpr int TPS = BM / 4, G = NT / TPS, U = 8;
+  static_assert(NT % TPS == 0, "row groups must divide over the threads");
+  const int tid = threadIdx.x;
+  if (!a.ss_in) {
+    for (int r = tid; r < BM; r += NT) s_inv[r] = 1.f;
+    return;
+  }
+  const int g = tid / TPS, c = tid - g * TPS;
+  const int m = mb + 4 * c, S = a.ss_in_slots;
+  float4 part = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (m < a.M) {
+    for (int s0 = g; s0 < S; s0 += U * G) {
+      float4 v[U];
+#pragma unroll
+      for (int k = 0; k < U; ++k) {  // (slots past the end re-read the last one)
+        const int sl = min(s0 + k * G, S - 1);
+        v[k] = *reinterpret_cast<const float4*>(a.ss_in + (size_t)sl * a.ss_in_ld + m);
+      }
+#pragma unroll
+      for (int k = 0; k < U; ++k)
+        if (s0 + k * G < S) {
+          part.x += v[k].x;
+          part.y += v[k].y;
+          part.z += v[k].z;
+          part.w += v[k].w;
+        }
+    }
+  }
+  *reinterpret_cast<float4*>(&s_part[g][4 * c]) = part;
+  __syncthreads();
+  for (int r = tid; r < BM; r += NT) {
+    float ss = 0.f;
+    for (int q = 0; q < G; ++q) ss += s_part[q][r];
+    s_inv[r] = 1.0f / sqrtf(ss / (float)a.K + a.norm_eps);  // (rows past M: unused)
+  }
+}
+
 template <bool I8, int TN, int TM>
 __global__ __launch_bounds__(256) void k_gemm_rows(GemmArgs a) {
   constexpr int SUB = I8 ? 2 : 1;
   constexpr int BM = 32 * TM;  // activation rows per block
   __shared__ float s_inv[BM];
+  __shared__ __attribute__((aligned(16))) float s_part[256 / (BM / 4)][BM];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i = lane & 15, q = lane >> 4;
   int mblk, nblk;
@@ -458,16 +506,7 @@ __global__ __launch_bounds__(256) void k_gemm_rows(GemmArgs a) {
   const int m0 = mb + 16 * TM * (wave >> 1);
   const int M = a.M, ld = a.act_ld;
   const int ksteps = a.K / (32 * SUB);
-  if (tid < BM) {
-    float inv = 1.f;
-    const int m = mb + tid;
-    if (a.ss_in && m < M) {
-      float ss = 0.f;
-      for (int slot = 0; slot < a.ss_in_slots; ++slot) ss += a.ss_in[(size_t)slot * a.ss_in_ld + m];
-      inv = 1.0f / sqrtf(ss / (float)a.K + a.norm_eps);
-    }
-    s_inv[tid] = inv;
-  }
+  norm_factors<BM, 256>(a, mb, s_inv, s_part);
   const uint4* W = reinterpret_cast<const uint4*>(a.W) + (size_t)(n0 >> 4) * ksteps * 64 + lane;
   const uint4* Hq = reinterpret_cast<const uint4*>(a.act) + (size_t)q * ld;
   bool mrow[TM];
@@ -586,6 +625,7 @@ __global__ __launch_bounds__(256) void k_gemm_rows(GemmArgs a) {
   if (over) atomicOr(a.status, QT_STATUS_FP16_RANGE);
 }
 
+constexpr int kCUs = 256;    // compute units of a gfx950 (MI355X)
 constexpr int kPipeKU = 2;  // K steps of 32 per stage of the copy-pipelined form
 
 // 16-byte LDS read at a byte offset, hidden from the compiler's wait insertion
@@ -618,6 +658,7 @@ __global__ __launch_bounds__(256) void k_gemm_rows_pipe(GemmArgs a) {
   static_assert((KU * (WT + AP)) % 4 == 0, "copies must divide over the four waves");
   __shared__ uint4 lds[NS * STAGE];
   __shared__ float s_inv[BM];
+  __shared__ __attribute__((aligned(16))) float s_part[256 / (BM / 4)][BM];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int i = lane & 15, q = lane >> 4;
   int mblk, nblk;
@@ -629,16 +670,7 @@ __global__ __launch_bounds__(256) void k_gemm_rows_pipe(GemmArgs a) {
   const int M = a.M, ld = a.act_ld;
   const int ksteps = a.K / 32;
   const int nst = ksteps / KU;  // stages (the launcher checks that KU divides the K steps)
-  if (tid < BM) {
-    float inv = 1.f;
-    const int m = mb + tid;
-    if (a.ss_in && m < M) {
-      float ss = 0.f;
-      for (int slot = 0; slot < a.ss_in_slots; ++slot) ss += a.ss_in[(size_t)slot * a.ss_in_ld + m];
-      inv = 1.0f / sqrtf(ss / (float)a.K + a.norm_eps);
-    }
-    s_inv[tid] = inv;
-  }
+  norm_factors<BM, 256>(a, mb, s_inv, s_part);
   const uint4* W = reinterpret_cast<const uint4*>(a.W) + (size_t)(nb0 >> 4) * ksteps * 64;
   const uint4* H = reinterpret_cast<const uint4*>(a.act);
   // copy stage g (K steps g*KU .. g*KU+KU-1) into buffer buf: piece p of the stage
@@ -757,6 +789,221 @@ __global__ __launch_bounds__(256) void k_gemm_rows_pipe(GemmArgs a) {
   if (over) atomicOr(a.status, QT_STATUS_FP16_RANGE);
 }
 
+// Large-tile form for many activation rows (the prompt prefill), on the 32 x 32 x 16
+// matrix instruction.  Each wave owns a (32 TM activation rows) x (32 TN weight
+// rows) tile as TN x TM accumulators of 32 x 32; WGM x WGN waves make a block of
+// BM = 32 TM WGM rows by BN = 32 TN WGN weight rows.  Every operand byte is
+// copied once per block from global memory into LDS by the load unit
+// (global_load_lds, 16 bytes per lane at the wave's LDS base + 16 x lane), one
+// 32-wide K step per stage, NS stages in the ring; each wave then reads its
+// fragments from LDS.  Per K step the LDS holds the BN/16 weight tiles as packed
+// (1 KB each, lane order of the 16-row tile) and the activations as 4 chunks of
+// BM rows x 16 bytes.
+//
+// Fragment reads are conflict-free: for the weights, lane l takes row l & 31 of
+// the 32-row block (tile (l >> 4) & 1 of the two, row l & 15 in it) at chunk
+// 2h + (l >> 5) of the K step's half h, so each 16 lanes read 256 contiguous
+// bytes; for the activations lanes 0-31 and 32-63 each read 512 contiguous bytes.
+// Accumulator element e of lane l is weight row 8(e >> 2) + 4(l >> 5) + (e & 3) and
+// activation row l & 31 of the 32 x 32 tile, so a lane holds four consecutive
+// weight rows per group: the SwiGLU pairs (even, odd) and the 16-row sums of
+// squares (two groups and the lane 32 apart) stay within reach.
+template <int TM, int TN, int WGM, int WGN, int NS>
+__global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_mx(GemmArgs a) {
+  constexpr int NW = WGM * WGN;
+  constexpr int BM = 32 * TM * WGM, BN = 32 * TN * WGN;
+  constexpr int WT = BN / 16, AP = BM / 16;         // 1 KB pieces per K step
+  constexpr int P = WT + AP;
+  constexpr int PHI = (P + NW - 1) / NW, PLO = P / NW, NHI = P % NW;  // copies per wave
+  constexpr int STEP = 64 * (BN + BM);              // bytes per K step
+  static_assert(BM % 64 == 0, "activation pieces are 64 rows");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[NS * STEP];
+  __shared__ float s_inv[BM];
+  __shared__ __attribute__((aligned(16))) float s_part[64 * NW / (BM / 4)][BM];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wx = wave % WGN, wy = wave / WGN;
+  int mblk, nblk;
+  rows_tile(mblk, nblk);
+  const int mb = BM * mblk;
+  const int nb0 = a.row0 + BN * nblk;
+  const int M = a.M, ld = a.act_ld;
+  const int ksteps = a.K / 32;
+  norm_factors<BM, 64 * NW>(a, mb, s_inv, s_part);
+  const uint4* W = reinterpret_cast<const uint4*>(a.W) + (size_t)(nb0 >> 4) * ksteps * 64;
+  const uint4* H = reinterpret_cast<const uint4*>(a.act);
+  // copy K step j into ring slot j % NS: piece p < WT is weight tile p, else the
+  // activation rows 64 h .. 64 h + 63 of chunk c (rows past M re-read row M - 1;
+  // their products are never stored)
+  auto copy_one = [&](int j, int r) {  // this wave's r-th piece of step j
+    const int p = wave + NW * r;         // (wave-uniform)
+    if (r < PLO || p < P) {
+      uint8_t* base = lds + (j % NS) * STEP;
+      const uint4* src;
+      uint8_t* dst;
+      if (p < WT) {
+        src = W + ((size_t)p * ksteps + j) * 64 + lane;
+        dst = base + p * 1024;
+      } else {
+        const int y = p - WT, c = y / (BM / 64), h = y % (BM / 64);
+        const int row = min(mb + 64 * h + lane, M - 1);
+        src = H + (size_t)(4 * j + c) * ld + row;
+        dst = base + WT * 1024 + (c * BM + 64 * h) * 16;
+      }
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
+                                       (void __attribute__((address_space(3)))*)dst, 16, 0, 0);
+    }
+  };
+  auto issue = [&](int j) {
+#pragma unroll
+    for (int r = 0; r < PHI; ++r) copy_one(j, r);
+  };
+  f32x16 acc[TN][TM];
+#pragma unroll
+  for (int t = 0; t < TN; ++t)
+#pragma unroll
+    for (int u = 0; u < TM; ++u)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[t][u][e] = 0.f;
+  // this lane's fragment offsets within a K step, for half 0 (half 1: + 32 bytes
+  // for the weights' chunk pair, + 2 BM x 16 for the activations')
+  uint32_t offw[TN], offa[TM];
+#pragma unroll
+  for (int t = 0; t < TN; ++t)
+    offw[t] = (uint32_t)(((32 * TN * wx + 32 * t) / 16 + ((lane >> 4) & 1)) * 1024 +
+                         ((lane >> 5) * 16 + (lane & 15)) * 16);
+#pragma unroll
+  for (int u = 0; u < TM; ++u)
+    offa[u] = (uint32_t)(WT * 1024 + ((lane >> 5) * BM + 32 * TM * wy + 32 * u + (lane & 31)) * 16);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
+  // fragment r of step j: r < 2 TN the weights' (half r / TN, tile r % TN), then
+  // the activations' (half, tile) in the same order
+  auto read_one = [&](int j, int r, u32x4 (&wv)[2][TN], u32x4 (&av)[2][TM]) {
+    const uint32_t sb = lds0 + (uint32_t)((j % NS) * STEP);
+    if (r < 2 * TN) {
+      const int h = r / TN, t = r % TN;
+      wv[h][t] = lds_read16(sb + offw[t] + 32 * 16 * h);
+    } else {
+      const int h = (r - 2 * TN) / TM, u = (r - 2 * TN) % TM;
+      av[h][u] = lds_read16(sb + offa[u] + 2 * BM * 16 * h);
+    }
+  };
+  auto read = [&](int j, u32x4 (&wv)[2][TN], u32x4 (&av)[2][TM]) {
+#pragma unroll
+    for (int r = 0; r < 2 * (TN + TM); ++r) read_one(j, r, wv, av);
+  };
+  // Step j: its fragments were read during step j - 1.  Once they are in (and so
+  // this wave is done with slot j % NS) and this wave's copies of step j + 1 have
+  // landed, one barrier lets the slot be refilled with step j + NS and step j + 1
+  // be read.  Those reads and copies are interleaved with step j's products, one
+  // group after each product: a wave issues them while the matrix unit works,
+  // which it could not do with the products issued back to back (with one wave per
+  // SIMD, nothing else would keep the unit busy meanwhile).  The reads go with the
+  // first half of the products, so that they are in before the next step; the
+  // copies with the second half.
+  constexpr int NMF = 2 * TN * TM, HALF = NMF / 2, NRD = 2 * (TN + TM);
+  auto body = [&](int j, u32x4 (&wv)[2][TN], u32x4 (&av)[2][TM], u32x4 (&wn)[2][TN],
+                  u32x4 (&an)[2][TM]) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int t = 0; t < TN; ++t) asm volatile("" : "+v"(wv[h][t]));
+#pragma unroll
+      for (int u = 0; u < TM; ++u) asm volatile("" : "+v"(av[h][u]));
+    }
+    if (j + NS - 1 < ksteps) {  // younger issued steps than j + 1: NS - 2 of them
+      if (NHI == 0 || wave < NHI) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PHI * (NS - 2)) : "memory");
+      else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PLO * (NS - 2)) : "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    __builtin_amdgcn_s_barrier();
+    const bool more_reads = j + 1 < ksteps, more_copies = j + NS < ksteps;
+#pragma unroll
+    for (int f = 0; f < NMF; ++f) {
+      const int h = f / (TN * TM), t = (f / TM) % TN, u = f % TM;
+      acc[t][u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+          __builtin_bit_cast(f16x8, wv[h][t]), __builtin_bit_cast(f16x8, av[h][u]), acc[t][u], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int r = 0; r < NRD; ++r)
+        if (r * HALF / NRD == f && more_reads) read_one(j + 1, r, wn, an);
+#pragma unroll
+      for (int c = 0; c < PHI; ++c)
+        if (HALF + c * (NMF - HALF) / PHI == f && more_copies) copy_one(j + NS, c);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  __syncthreads();  // (s_inv; before any copy, so that this barrier waits for none)
+#pragma unroll
+  for (int st = 0; st < NS; ++st)
+    if (st < ksteps) issue(st);
+  // step 0 in: younger issued steps, min(NS, ksteps) - 1 of them
+  if (NS <= ksteps) {
+    if (NHI == 0 || wave < NHI) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PHI * (NS - 1)) : "memory");
+    else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PLO * (NS - 1)) : "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  __builtin_amdgcn_s_barrier();
+  u32x4 w0[2][TN], a0[2][TM], w1[2][TN], a1[2][TM];
+  read(0, w0, a0);
+  for (int j = 0; j < ksteps; j += 2) {  // (K is a multiple of 64: ksteps is even)
+    body(j, w0, a0, w1, a1);
+    body(j + 1, w1, a1, w0, a0);
+  }
+  bool over = false;
+#pragma unroll
+  for (int u = 0; u < TM; ++u) {
+    const int r = 32 * TM * wy + 32 * u + (lane & 31);
+    const int m = mb + r;
+    if (m >= M) continue;  // (lanes l and l ^ 32 hold the same row and leave together)
+    const float inv = s_inv[r];
+#pragma unroll
+    for (int t = 0; t < TN; ++t) {
+      const int nt = nb0 + 32 * TN * wx + 32 * t;  // first weight row of the 32 x 32 tile
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {  // 16-row halves of the tile
+        float ss = 0.f;
+#pragma unroll
+        for (int g = 2 * s; g < 2 * s + 2; ++g) {
+          const int nb = nt + 8 * g + 4 * (lane >> 5);
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = acc[t][u][4 * g + e] * inv;
+          if (a.epi == EPI_STORE) {
+            *reinterpret_cast<float4*>(a.out_f32 + (size_t)m * a.out_ld + nb) =
+                make_float4(v[0], v[1], v[2], v[3]);
+          } else if (a.epi == EPI_SWIGLU) {
+            const uint32_t pk = (uint32_t)f2h_chk(silu(v[0]) * v[1], over) |
+                                ((uint32_t)f2h_chk(silu(v[2]) * v[3], over) << 16);
+            *reinterpret_cast<uint32_t*>(a.u + chunked(m, nb >> 1, a.u_ld)) = pk;
+          } else {  // EPI_RESID
+            float* xp = a.out_f32 + (size_t)m * a.out_ld + nb;
+            const float4 x0 = *reinterpret_cast<const float4*>(xp);
+            const float x[4] = {x0.x + v[0], x0.y + v[1], x0.z + v[2], x0.w + v[3]};
+            *reinterpret_cast<float4*>(xp) = make_float4(x[0], x[1], x[2], x[3]);
+            if (a.u_gain) {
+              uint32_t h2[2];
+#pragma unroll
+              for (int e = 0; e < 2; ++e)
+                h2[e] = (uint32_t)f2h_chk(x[2 * e] * bf2f(a.u_gain[nb + 2 * e]), over) |
+                        ((uint32_t)f2h_chk(x[2 * e + 1] * bf2f(a.u_gain[nb + 2 * e + 1]), over) << 16);
+              *reinterpret_cast<uint2*>(a.u + chunked(m, nb, a.u_ld)) = make_uint2(h2[0], h2[1]);
+              ss += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+            }
+          }
+        }
+        if (a.epi == EPI_RESID && a.u_gain) {
+          ss += __shfl_xor(ss, 32);
+          if (lane < 32) a.ss_out[(size_t)((nt + 16 * s) >> 4) * a.ss_out_ld + m] = ss;
+        }
+      }
+    }
+  }
+  if (over) atomicOr(a.status, QT_STATUS_FP16_RANGE);
+}
+
 // ------------------------------------------------------------------ packing
 // Source rows [rows][K] bf16 -> half rows row0 + r*step of a tiled [N][K] matrix.
 // A finite bf16 weight beyond the half range (|w| > 65504) sets *range_flag.
@@ -860,9 +1107,26 @@ hipError_t launch_gemm_rows(const GemmArgs& a, hipStream_t s) {
   if (a.epi == EPI_RESID && a.u_gain && !a.ss_out) return hipErrorInvalidValue;
   // 128 x 128 blocks unless they leave fewer than two blocks per CU: then 64 weight
   // rows, then 64 x 64
+  const bool i8 = a.w8 != 0;
+  // Many rows: the large-tile LDS form, on the first shape whose blocks fill every
+  // CU at least once
+  if (!i8 && !a.scale) {
+    const long long m256 = (a.M + 255) / 256, m128 = (a.M + 127) / 128;
+    if (a.nrows % 192 == 0 && m256 * (a.nrows / 192) >= kCUs) {
+      launch_kernel((k_gemm_mx<2, 2, 4, 3, 5>), dim3((unsigned)m256, a.nrows / 192), dim3(768), s, a);
+      return hipGetLastError();
+    }
+    if (m128 * (a.nrows / 128) >= kCUs) {
+      launch_kernel((k_gemm_mx<2, 2, 2, 2, 8>), dim3((unsigned)m128, a.nrows / 128), dim3(256), s, a);
+      return hipGetLastError();
+    }
+    if (m128 * (a.nrows / 64) >= kCUs) {
+      launch_kernel((k_gemm_mx<2, 1, 2, 2, 10>), dim3((unsigned)m128, a.nrows / 64), dim3(256), s, a);
+      return hipGetLastError();
+    }
+  }
   const long long big = (long long)((a.M + 127) / 128) * (a.nrows / 128);
   const long long mid = (long long)((a.M + 127) / 128) * (a.nrows / 64);
-  const bool i8 = a.w8 != 0;
   // (measured at 1024 rows: the direct form for 128 x 128 and 64 x 128 blocks, the
   // copy-pipelined form for 64 x 64, with stages of two K steps, four in flight;
   // splitting K in halves for twice the blocks gained nothing for the QKV shape)

@@ -150,6 +150,27 @@ def test_prefill_full_model(full_pm, orc_full):
     dec.close()
 
 
+def test_prefill_full_model_many_rows(full_pm, orc_full):
+    # 1088 packed rows: every projection runs over 1088 activation rows at the full
+    # model's matrix sizes, which selects the large-tile forms (256 x 192 for the
+    # gate/up, 128 x 128 for QKV, 128 x 64 for o and down), each with a partial
+    # last block of rows
+    dec, _, _ = _run(full_pm, orc_full, synth.FULL, [29, 3], rows=1088, max_pages=4, tag="pfrows",
+                     frames_after=1)
+    dec.close()
+
+
+def test_prefill_2048_rows(small_pm, orc_small):
+    # 2048 rows of the small model: 128 x 128 blocks for QKV and the gate/up,
+    # 128 x 64 for o and down; ragged sequences, one of a single token
+    rng = np.random.default_rng(20)
+    lengths = [int(x) for x in rng.integers(40, 400, size=7)] + [1]
+    lengths.append(2048 - sum(lengths) - 5)
+    dec, _, _ = _run(small_pm, orc_small, synth.SMALL, lengths, rows=2048, max_pages=40,
+                     tag="pf2048", frames_after=1)
+    dec.close()
+
+
 def test_prefill_full_model_int8(full_pm_i8, orc_full_i8):
     dec, _, _ = _run(full_pm_i8, orc_full_i8, synth.FULL, [33], rows=64, max_pages=4, tag="pfi8",
                      frames_after=1)
