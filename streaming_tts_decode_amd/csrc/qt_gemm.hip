@@ -447,43 +447,60 @@ __device__ __forceinline__ void rows_tile(int& mblk, int& nblk) {
 // Norm factors of a block's BM activation rows mb .. mb + BM - 1, the consumer side
 // of an RMSNorm: s_inv[r] = 1 / sqrt(sum of row mb + r's ss_in slots / K + eps), or 1
 // without a norm.  The slots are [slots][ss_in_ld] floats.  Each of the NT threads
-// takes four consecutive rows of every G-th slot (G = NT / (BM / 4)) and issues all
-// of its loads before adding any, so the sums cost one memory round trip rather
-// than one per slot; the G partials are then added in order through LDS.  (M is a
-// multiple of 16, so a group of four rows lies wholly before or wholly past M.)
-template <int BM, int NT>
+// takes four consecutive rows of every G-th slot (G = NT / (BM / 4)), U slots per
+// batch, and issues a batch's loads before adding any, so the sums cost one memory
+// round trip per batch rather than one per slot; the G partials are then added in
+// order through LDS.  `mid` runs between the first batch's loads and their use
+// (the caller's first operand copies, which then fly with them).  Rows past M read
+// row M - 1 and count nothing.  Ends with a plain barrier, which waits for no
+// memory operation other than the LDS writes of the partials.
+template <int BM, int NT, int U, typename Mid>
 __device__ __forceinline__ void norm_factors(const GemmArgs& a, int mb, float* s_inv,
-                                             float (*s_part)[BM]) {
-  constexpr int TPS = BM / 4, G = NT / TPS, U = 8;
+                                             float (*s_part)[BM], Mid mid) {
+  constexpr int TPS = BM / 4, G = NT / TPS;
   static_assert(NT % TPS == 0, "row groups must divide over the threads");
   const int tid = threadIdx.x;
   if (!a.ss_in) {
     for (int r = tid; r < BM; r += NT) s_inv[r] = 1.f;
+    mid();
     return;
   }
   const int g = tid / TPS, c = tid - g * TPS;
   const int m = mb + 4 * c, S = a.ss_in_slots;
+  const int mm = min(m, a.M - 4);  // (M is a multiple of 16)
+  const bool live = m < a.M;
   float4 part = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (m < a.M) {
-    for (int s0 = g; s0 < S; s0 += U * G) {
-      float4 v[U];
+  auto batch = [&](float4 (&v)[U], int s0) {
 #pragma unroll
-      for (int k = 0; k < U; ++k) {  // (slots past the end re-read the last one)
-        const int sl = min(s0 + k * G, S - 1);
-        v[k] = *reinterpret_cast<const float4*>(a.ss_in + (size_t)sl * a.ss_in_ld + m);
-      }
-#pragma unroll
-      for (int k = 0; k < U; ++k)
-        if (s0 + k * G < S) {
-          part.x += v[k].x;
-          part.y += v[k].y;
-          part.z += v[k].z;
-          part.w += v[k].w;
-        }
+    for (int k = 0; k < U; ++k) {  // (slots past the end re-read the last one)
+      const int sl = min(s0 + k * G, S - 1);
+      v[k] = *reinterpret_cast<const float4*>(a.ss_in + (size_t)sl * a.ss_in_ld + mm);
     }
+  };
+  auto add = [&](const float4 (&v)[U], int s0) {
+#pragma unroll
+    for (int k = 0; k < U; ++k)
+      if (live && s0 + k * G < S) {
+        part.x += v[k].x;
+        part.y += v[k].y;
+        part.z += v[k].z;
+        part.w += v[k].w;
+      }
+  };
+  {
+    float4 v[U];
+    batch(v, g);
+    mid();
+    add(v, g);
+  }
+  for (int s0 = g + U * G; s0 < S; s0 += U * G) {
+    float4 v[U];
+    batch(v, s0);
+    add(v, s0);
   }
   *reinterpret_cast<float4*>(&s_part[g][4 * c]) = part;
-  __syncthreads();
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
   for (int r = tid; r < BM; r += NT) {
     float ss = 0.f;
     for (int q = 0; q < G; ++q) ss += s_part[q][r];
@@ -506,7 +523,7 @@ __global__ __launch_bounds__(256) void k_gemm_rows(GemmArgs a) {
   const int m0 = mb + 16 * TM * (wave >> 1);
   const int M = a.M, ld = a.act_ld;
   const int ksteps = a.K / (32 * SUB);
-  norm_factors<BM, 256>(a, mb, s_inv, s_part);
+  norm_factors<BM, 256, 8>(a, mb, s_inv, s_part, [] {});
   const uint4* W = reinterpret_cast<const uint4*>(a.W) + (size_t)(n0 >> 4) * ksteps * 64 + lane;
   const uint4* Hq = reinterpret_cast<const uint4*>(a.act) + (size_t)q * ld;
   bool mrow[TM];
@@ -670,7 +687,7 @@ __global__ __launch_bounds__(256) void k_gemm_rows_pipe(GemmArgs a) {
   const int M = a.M, ld = a.act_ld;
   const int ksteps = a.K / 32;
   const int nst = ksteps / KU;  // stages (the launcher checks that KU divides the K steps)
-  norm_factors<BM, 256>(a, mb, s_inv, s_part);
+  norm_factors<BM, 256, 8>(a, mb, s_inv, s_part, [] {});
   const uint4* W = reinterpret_cast<const uint4*>(a.W) + (size_t)(nb0 >> 4) * ksteps * 64;
   const uint4* H = reinterpret_cast<const uint4*>(a.act);
   // copy stage g (K steps g*KU .. g*KU+KU-1) into buffer buf: piece p of the stage
@@ -828,7 +845,6 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_mx(GemmArgs a) {
   const int nb0 = a.row0 + BN * nblk;
   const int M = a.M, ld = a.act_ld;
   const int ksteps = a.K / 32;
-  norm_factors<BM, 64 * NW>(a, mb, s_inv, s_part);
   const uint4* W = reinterpret_cast<const uint4*>(a.W) + (size_t)(nb0 >> 4) * ksteps * 64;
   const uint4* H = reinterpret_cast<const uint4*>(a.act);
   // copy K step j into ring slot j % NS: piece p < WT is weight tile p, else the
@@ -934,16 +950,18 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_mx(GemmArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  __syncthreads();  // (s_inv; before any copy, so that this barrier waits for none)
+  // the ring's first NS steps are copied while the norm sums are in flight
+  norm_factors<BM, 64 * NW, 16>(a, mb, s_inv, s_part, [&] {
 #pragma unroll
-  for (int st = 0; st < NS; ++st)
-    if (st < ksteps) issue(st);
-  // step 0 in: younger issued steps, min(NS, ksteps) - 1 of them
+    for (int st = 0; st < NS; ++st)
+      if (st < ksteps) issue(st);
+  });
+  // step 0 in (younger issued steps: min(NS, ksteps) - 1 of them), s_inv written
   if (NS <= ksteps) {
-    if (NHI == 0 || wave < NHI) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PHI * (NS - 1)) : "memory");
-    else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PLO * (NS - 1)) : "memory");
+    if (NHI == 0 || wave < NHI) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(PHI * (NS - 1)) : "memory");
+    else asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(PLO * (NS - 1)) : "memory");
   } else {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   }
   __builtin_amdgcn_s_barrier();
   u32x4 w0[2][TN], a0[2][TM], w1[2][TN], a1[2][TM];
@@ -952,51 +970,151 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_mx(GemmArgs a) {
     body(j, w0, a0, w1, a1);
     body(j + 1, w1, a1, w0, a0);
   }
+  // ---- epilogue.  The ring is free once every wave is past its last step; it
+  // stages the block's outputs so that they leave as whole rows (f32 rows for a
+  // store or a residual) or whole 16-byte chunk rows (half outputs) rather than as
+  // the accumulators' scattered 16-byte pieces.
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  __syncthreads();
   bool over = false;
+  constexpr int NT = 64 * NW, VLD = BN + 4, C4 = BN / 4;
+  constexpr bool stage_u = (BN / 16) * BM * 16 <= NS * STEP;              // SwiGLU halves
+  constexpr bool stage_v = BM * VLD * 4 + BM * BN * 2 <= NS * STEP;      // f32 tile + halves
+  // accumulator (t, u), lane l, group g: activation row r, weight rows nl .. nl + 3
+  // (local to the block)
+  auto for_each_group = [&](auto&& f) {
 #pragma unroll
-  for (int u = 0; u < TM; ++u) {
-    const int r = 32 * TM * wy + 32 * u + (lane & 31);
-    const int m = mb + r;
-    if (m >= M) continue;  // (lanes l and l ^ 32 hold the same row and leave together)
-    const float inv = s_inv[r];
+    for (int u = 0; u < TM; ++u) {
+      const int r = 32 * TM * wy + 32 * u + (lane & 31);
+      const float inv = s_inv[r];
 #pragma unroll
-    for (int t = 0; t < TN; ++t) {
-      const int nt = nb0 + 32 * TN * wx + 32 * t;  // first weight row of the 32 x 32 tile
+      for (int t = 0; t < TN; ++t)
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {  // 16-row halves of the tile
-        float ss = 0.f;
-#pragma unroll
-        for (int g = 2 * s; g < 2 * s + 2; ++g) {
-          const int nb = nt + 8 * g + 4 * (lane >> 5);
+        for (int g = 0; g < 4; ++g) {
+          const int nl = 32 * TN * wx + 32 * t + 8 * g + 4 * (lane >> 5);
           float v[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] = acc[t][u][4 * g + e] * inv;
-          if (a.epi == EPI_STORE) {
-            *reinterpret_cast<float4*>(a.out_f32 + (size_t)m * a.out_ld + nb) =
-                make_float4(v[0], v[1], v[2], v[3]);
-          } else if (a.epi == EPI_SWIGLU) {
-            const uint32_t pk = (uint32_t)f2h_chk(silu(v[0]) * v[1], over) |
-                                ((uint32_t)f2h_chk(silu(v[2]) * v[3], over) << 16);
-            *reinterpret_cast<uint32_t*>(a.u + chunked(m, nb >> 1, a.u_ld)) = pk;
-          } else {  // EPI_RESID
-            float* xp = a.out_f32 + (size_t)m * a.out_ld + nb;
-            const float4 x0 = *reinterpret_cast<const float4*>(xp);
-            const float x[4] = {x0.x + v[0], x0.y + v[1], x0.z + v[2], x0.w + v[3]};
-            *reinterpret_cast<float4*>(xp) = make_float4(x[0], x[1], x[2], x[3]);
-            if (a.u_gain) {
-              uint32_t h2[2];
+          f(r, nl, v);
+        }
+    }
+  };
+  if (a.epi == EPI_SWIGLU && stage_u) {
+    // SwiGLU of each (gate, up) pair -> output column nl / 2, staged as chunk rows
+    // [BN / 16 chunks][BM rows][8 halves]; then copied out 64 rows x 16 bytes at a time
+    uint32_t* ut = reinterpret_cast<uint32_t*>(lds);
+    for_each_group([&](int r, int nl, const float (&v)[4]) {
+      const int oc = nl >> 1;
+      ut[((oc >> 3) * BM + r) * 4 + ((oc & 7) >> 1)] =
+          (uint32_t)f2h_chk(silu(v[0]) * v[1], over) | ((uint32_t)f2h_chk(silu(v[2]) * v[3], over) << 16);
+    });
+    __syncthreads();
+    for (int p = wave; p < (BN / 16) * (BM / 64); p += NW) {  // (wave-uniform)
+      const int c = p / (BM / 64), r = 64 * (p % (BM / 64)) + lane, m = mb + r;
+      const uint4 val = *reinterpret_cast<const uint4*>(ut + (c * BM + r) * 4);
+      if (m < M) *reinterpret_cast<uint4*>(a.u + chunked(m, (nb0 >> 1) + 8 * c, a.u_ld)) = val;
+    }
+  } else if (a.epi != EPI_SWIGLU && stage_v) {
+    // f32 tile [BM][BN + 4] (the padding keeps the lanes' 16-byte writes apart)
+    float* vt = reinterpret_cast<float*>(lds);
+    for_each_group([&](int r, int nl, const float (&v)[4]) {
+      *reinterpret_cast<float4*>(vt + r * VLD + nl) = make_float4(v[0], v[1], v[2], v[3]);
+    });
+    __syncthreads();
+    // thread i: row i / C4, columns 4 (i % C4) .. + 3; a wave covers whole rows
+    if (a.epi == EPI_STORE) {
+      for (int i = tid; i < BM * C4; i += NT) {
+        const int r = i / C4, c4 = i - r * C4, m = mb + r;
+        if (m < M)
+          *reinterpret_cast<float4*>(a.out_f32 + (size_t)m * a.out_ld + nb0 + 4 * c4) =
+              *reinterpret_cast<const float4*>(vt + r * VLD + 4 * c4);
+      }
+    } else {  // EPI_RESID: x += v; u = half(x * gain) staged as chunk rows; 16-column sums
+      uint2* ut = reinterpret_cast<uint2*>(lds + BM * VLD * 4);  // [BN / 8][BM][2]
+      for (int i = tid; i < BM * C4; i += NT) {  // (every lane runs every trip: 4 TM TN)
+        const int r = i / C4, c4 = i - r * C4, m = mb + r, n = nb0 + 4 * c4;
+        const bool live = m < M;
+        const float4 v = *reinterpret_cast<const float4*>(vt + r * VLD + 4 * c4);
+        float x[4] = {0.f, 0.f, 0.f, 0.f};
+        if (live) {
+          float* xp = a.out_f32 + (size_t)m * a.out_ld + n;
+          const float4 x0 = *reinterpret_cast<const float4*>(xp);
+          x[0] = x0.x + v.x;
+          x[1] = x0.y + v.y;
+          x[2] = x0.z + v.z;
+          x[3] = x0.w + v.w;
+          *reinterpret_cast<float4*>(xp) = make_float4(x[0], x[1], x[2], x[3]);
+        }
+        if (a.u_gain) {
+          uint32_t h2[2];
 #pragma unroll
-              for (int e = 0; e < 2; ++e)
-                h2[e] = (uint32_t)f2h_chk(x[2 * e] * bf2f(a.u_gain[nb + 2 * e]), over) |
-                        ((uint32_t)f2h_chk(x[2 * e + 1] * bf2f(a.u_gain[nb + 2 * e + 1]), over) << 16);
-              *reinterpret_cast<uint2*>(a.u + chunked(m, nb, a.u_ld)) = make_uint2(h2[0], h2[1]);
-              ss += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+          for (int e = 0; e < 2; ++e)
+            h2[e] = (uint32_t)f2h_chk(x[2 * e] * bf2f(a.u_gain[n + 2 * e]), over) |
+                    ((uint32_t)f2h_chk(x[2 * e + 1] * bf2f(a.u_gain[n + 2 * e + 1]), over) << 16);
+          ut[((c4 >> 1) * BM + r) * 2 + (c4 & 1)] = make_uint2(h2[0], h2[1]);
+          // the 16 columns of a sum are four consecutive lanes
+          float ss = x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+          ss += __shfl_xor(ss, 1);
+          ss += __shfl_xor(ss, 2);
+          if (live && (c4 & 3) == 0) a.ss_out[(size_t)(n >> 4) * a.ss_out_ld + m] = ss;
+        }
+      }
+      if (a.u_gain) {
+        __syncthreads();
+        for (int p = wave; p < (BN / 8) * (BM / 64); p += NW) {  // (wave-uniform)
+          const int c = p / (BM / 64), r = 64 * (p % (BM / 64)) + lane, m = mb + r;
+          const uint4 val = *reinterpret_cast<const uint4*>(ut + (c * BM + r) * 2);
+          if (m < M) *reinterpret_cast<uint4*>(a.u + chunked(m, nb0 + 8 * c, a.u_ld)) = val;
+        }
+      }
+    }
+  } else {
+    // (tiles too large to stage: the accumulators' pieces go out directly)
+#pragma unroll
+    for (int u = 0; u < TM; ++u) {
+      const int r = 32 * TM * wy + 32 * u + (lane & 31);
+      const int m = mb + r;
+      if (m >= M) continue;  // (lanes l and l ^ 32 hold the same row and leave together)
+      const float inv = s_inv[r];
+#pragma unroll
+      for (int t = 0; t < TN; ++t) {
+        const int nt = nb0 + 32 * TN * wx + 32 * t;  // first weight row of the 32 x 32 tile
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {  // 16-row halves of the tile
+          float ss = 0.f;
+#pragma unroll
+          for (int g = 2 * s; g < 2 * s + 2; ++g) {
+            const int nb = nt + 8 * g + 4 * (lane >> 5);
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = acc[t][u][4 * g + e] * inv;
+            if (a.epi == EPI_STORE) {
+              *reinterpret_cast<float4*>(a.out_f32 + (size_t)m * a.out_ld + nb) =
+                  make_float4(v[0], v[1], v[2], v[3]);
+            } else if (a.epi == EPI_SWIGLU) {
+              const uint32_t pk = (uint32_t)f2h_chk(silu(v[0]) * v[1], over) |
+                                  ((uint32_t)f2h_chk(silu(v[2]) * v[3], over) << 16);
+              *reinterpret_cast<uint32_t*>(a.u + chunked(m, nb >> 1, a.u_ld)) = pk;
+            } else {  // EPI_RESID
+              float* xp = a.out_f32 + (size_t)m * a.out_ld + nb;
+              const float4 x0 = *reinterpret_cast<const float4*>(xp);
+              const float x[4] = {x0.x + v[0], x0.y + v[1], x0.z + v[2], x0.w + v[3]};
+              *reinterpret_cast<float4*>(xp) = make_float4(x[0], x[1], x[2], x[3]);
+              if (a.u_gain) {
+                uint32_t h2[2];
+#pragma unroll
+                for (int e = 0; e < 2; ++e)
+                  h2[e] = (uint32_t)f2h_chk(x[2 * e] * bf2f(a.u_gain[nb + 2 * e]), over) |
+                          ((uint32_t)f2h_chk(x[2 * e + 1] * bf2f(a.u_gain[nb + 2 * e + 1]), over) << 16);
+                *reinterpret_cast<uint2*>(a.u + chunked(m, nb, a.u_ld)) = make_uint2(h2[0], h2[1]);
+                ss += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+              }
             }
           }
-        }
-        if (a.epi == EPI_RESID && a.u_gain) {
-          ss += __shfl_xor(ss, 32);
-          if (lane < 32) a.ss_out[(size_t)((nt + 16 * s) >> 4) * a.ss_out_ld + m] = ss;
+          if (a.epi == EPI_RESID && a.u_gain) {
+            ss += __shfl_xor(ss, 32);
+            if (lane < 32) a.ss_out[(size_t)((nt + 16 * s) >> 4) * a.ss_out_ld + m] = ss;
+          }
         }
       }
     }
