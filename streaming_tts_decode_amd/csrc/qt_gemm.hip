@@ -825,42 +825,47 @@ __global__ __launch_bounds__(256) void k_gemm_rows_pipe(GemmArgs a) {
 // activation row l & 31 of the 32 x 32 tile, so a lane holds four consecutive
 // weight rows per group: the SwiGLU pairs (even, odd) and the 16-row sums of
 // squares (two groups and the lane 32 apart) stay within reach.
-template <int TM, int TN, int WGM, int WGN, int NS>
-__global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_mx(GemmArgs a) {
-  constexpr int NW = WGM * WGN;
+template <int TM, int TN, int WGM, int WGN, int NS, int KS>
+__global__ __launch_bounds__(64 * WGM * WGN * KS) void k_gemm_mx(GemmArgs a) {
+  constexpr int NL = WGM * WGN;                     // waves per K group
+  constexpr int NW = NL * KS;
   constexpr int BM = 32 * TM * WGM, BN = 32 * TN * WGN;
   constexpr int WT = BN / 16, AP = BM / 16;         // 1 KB pieces per K step
-  constexpr int P = WT + AP;
+  constexpr int P = KS * (WT + AP);                 // pieces per stage
   constexpr int PHI = (P + NW - 1) / NW, PLO = P / NW, NHI = P % NW;  // copies per wave
   constexpr int STEP = 64 * (BN + BM);              // bytes per K step
+  constexpr int STAGE = KS * STEP;
   static_assert(BM % 64 == 0, "activation pieces are 64 rows");
-  __shared__ __attribute__((aligned(16))) uint8_t lds[NS * STEP];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[NS * STAGE];
   __shared__ float s_inv[BM];
   __shared__ __attribute__((aligned(16))) float s_part[64 * NW / (BM / 4)][BM];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wx = wave % WGN, wy = wave / WGN;
+  const int kg = wave / NL, wl = wave - kg * NL;  // K group, wave within it
+  const int wx = wl % WGN, wy = wl / WGN;
   int mblk, nblk;
   rows_tile(mblk, nblk);
   const int mb = BM * mblk;
   const int nb0 = a.row0 + BN * nblk;
   const int M = a.M, ld = a.act_ld;
-  const int ksteps = a.K / 32;
+  const int ksteps = a.K / 32, nst = ksteps / KS;  // (the launcher checks that 2 KS divides ksteps)
   const uint4* W = reinterpret_cast<const uint4*>(a.W) + (size_t)(nb0 >> 4) * ksteps * 64;
   const uint4* H = reinterpret_cast<const uint4*>(a.act);
-  // copy K step j into ring slot j % NS: piece p < WT is weight tile p, else the
-  // activation rows 64 h .. 64 h + 63 of chunk c (rows past M re-read row M - 1;
-  // their products are never stored)
-  auto copy_one = [&](int j, int r) {  // this wave's r-th piece of step j
+  // copy stage s (K steps KS s .. KS s + KS - 1) into ring slot s % NS: piece p is
+  // K step KS s + p / (WT + AP), within it x = p % (WT + AP): weight tile x < WT,
+  // else the activation rows 64 h .. 64 h + 63 of chunk c (rows past M re-read row
+  // M - 1; their products are never stored)
+  auto copy_one = [&](int s, int r) {  // this wave's r-th piece of stage s
     const int p = wave + NW * r;         // (wave-uniform)
     if (r < PLO || p < P) {
-      uint8_t* base = lds + (j % NS) * STEP;
+      const int kk = p / (WT + AP), x = p % (WT + AP), j = KS * s + kk;
+      uint8_t* base = lds + (s % NS) * STAGE + kk * STEP;
       const uint4* src;
       uint8_t* dst;
-      if (p < WT) {
-        src = W + ((size_t)p * ksteps + j) * 64 + lane;
-        dst = base + p * 1024;
+      if (x < WT) {
+        src = W + ((size_t)x * ksteps + j) * 64 + lane;
+        dst = base + x * 1024;
       } else {
-        const int y = p - WT, c = y / (BM / 64), h = y % (BM / 64);
+        const int y = x - WT, c = y / (BM / 64), h = y % (BM / 64);
         const int row = min(mb + 64 * h + lane, M - 1);
         src = H + (size_t)(4 * j + c) * ld + row;
         dst = base + WT * 1024 + (c * BM + 64 * h) * 16;
@@ -869,9 +874,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_mx(GemmArgs a) {
                                        (void __attribute__((address_space(3)))*)dst, 16, 0, 0);
     }
   };
-  auto issue = [&](int j) {
+  auto issue = [&](int s) {
 #pragma unroll
-    for (int r = 0; r < PHI; ++r) copy_one(j, r);
+    for (int r = 0; r < PHI; ++r) copy_one(s, r);
   };
   f32x16 acc[TN][TM];
 #pragma unroll
@@ -891,10 +896,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_mx(GemmArgs a) {
   for (int u = 0; u < TM; ++u)
     offa[u] = (uint32_t)(WT * 1024 + ((lane >> 5) * BM + 32 * TM * wy + 32 * u + (lane & 31)) * 16);
   const uint32_t lds0 = (uint32_t)(uintptr_t)lds;
-  // fragment r of step j: r < 2 TN the weights' (half r / TN, tile r % TN), then
-  // the activations' (half, tile) in the same order
-  auto read_one = [&](int j, int r, u32x4 (&wv)[2][TN], u32x4 (&av)[2][TM]) {
-    const uint32_t sb = lds0 + (uint32_t)((j % NS) * STEP);
+  // fragment r of this wave's K step of stage s: r < 2 TN the weights' (half
+  // r / TN, tile r % TN), then the activations' (half, tile) in the same order
+  auto read_one = [&](int s, int r, u32x4 (&wv)[2][TN], u32x4 (&av)[2][TM]) {
+    const uint32_t sb = lds0 + (uint32_t)((s % NS) * STAGE + kg * STEP);
     if (r < 2 * TN) {
       const int h = r / TN, t = r % TN;
       wv[h][t] = lds_read16(sb + offw[t] + 32 * 16 * h);
@@ -903,14 +908,15 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_mx(GemmArgs a) {
       av[h][u] = lds_read16(sb + offa[u] + 2 * BM * 16 * h);
     }
   };
-  auto read = [&](int j, u32x4 (&wv)[2][TN], u32x4 (&av)[2][TM]) {
+  auto read = [&](int s, u32x4 (&wv)[2][TN], u32x4 (&av)[2][TM]) {
 #pragma unroll
-    for (int r = 0; r < 2 * (TN + TM); ++r) read_one(j, r, wv, av);
+    for (int r = 0; r < 2 * (TN + TM); ++r) read_one(s, r, wv, av);
   };
-  // Step j: its fragments were read during step j - 1.  Once they are in (and so
-  // this wave is done with slot j % NS) and this wave's copies of step j + 1 have
-  // landed, one barrier lets the slot be refilled with step j + NS and step j + 1
-  // be read.  Those reads and copies are interleaved with step j's products, one
+  // Stage s: K group g takes its K step KS s + g (KS > 1: two or more waves per
+  // SIMD, so that one wave's waits overlap another's products).  A wave's fragments
+  // of stage s were read during stage s - 1.  Once they are in (and so this wave is
+  // done with slot s % NS) and this wave's copies of stage s + 1 have landed, one
+  // barrier lets the slot be refilled with stage s + NS and stage s + 1 be read.  Those reads and copies are interleaved with step j's products, one
   // group after each product: a wave issues them while the matrix unit works,
   // which it could not do with the products issued back to back (with one wave per
   // SIMD, nothing else would keep the unit busy meanwhile).  The reads go with the
@@ -918,7 +924,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_mx(GemmArgs a) {
   // copies with the second half.
   constexpr int NMF = 2 * TN * TM, HALF = NMF / 2, NRD = 2 * (TN + TM);
   auto body = [&](int j, u32x4 (&wv)[2][TN], u32x4 (&av)[2][TM], u32x4 (&wn)[2][TN],
-                  u32x4 (&an)[2][TM]) {
+                  u32x4 (&an)[2][TM]) {  // (j: the stage)
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -927,14 +933,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_mx(GemmArgs a) {
 #pragma unroll
       for (int u = 0; u < TM; ++u) asm volatile("" : "+v"(av[h][u]));
     }
-    if (j + NS - 1 < ksteps) {  // younger issued steps than j + 1: NS - 2 of them
+    if (j + NS - 1 < nst) {  // younger issued stages than j + 1: NS - 2 of them
       if (NHI == 0 || wave < NHI) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PHI * (NS - 2)) : "memory");
       else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PLO * (NS - 2)) : "memory");
     } else {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     __builtin_amdgcn_s_barrier();
-    const bool more_reads = j + 1 < ksteps, more_copies = j + NS < ksteps;
+    const bool more_reads = j + 1 < nst, more_copies = j + NS < nst;
 #pragma unroll
     for (int f = 0; f < NMF; ++f) {
       const int h = f / (TN * TM), t = (f / TM) % TN, u = f % TM;
@@ -954,10 +960,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_mx(GemmArgs a) {
   norm_factors<BM, 64 * NW, 16>(a, mb, s_inv, s_part, [&] {
 #pragma unroll
     for (int st = 0; st < NS; ++st)
-      if (st < ksteps) issue(st);
+      if (st < nst) issue(st);
   });
-  // step 0 in (younger issued steps: min(NS, ksteps) - 1 of them), s_inv written
-  if (NS <= ksteps) {
+  // stage 0 in (younger issued stages: min(NS, nst) - 1 of them), s_inv written
+  if (NS <= nst) {
     if (NHI == 0 || wave < NHI) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(PHI * (NS - 1)) : "memory");
     else asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(PLO * (NS - 1)) : "memory");
   } else {
@@ -966,7 +972,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_mx(GemmArgs a) {
   __builtin_amdgcn_s_barrier();
   u32x4 w0[2][TN], a0[2][TM], w1[2][TN], a1[2][TM];
   read(0, w0, a0);
-  for (int j = 0; j < ksteps; j += 2) {  // (K is a multiple of 64: ksteps is even)
+  for (int j = 0; j < nst; j += 2) {  // (nst is even)
     body(j, w0, a0, w1, a1);
     body(j + 1, w1, a1, w0, a0);
   }
@@ -976,13 +982,42 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_mx(GemmArgs a) {
   // the accumulators' scattered 16-byte pieces.
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
   __syncthreads();
+  if constexpr (KS > 1) {
+    // the K groups' partial sums: groups g > 0 leave theirs in LDS, group 0 adds
+    // them in group order
+    constexpr int NA = TN * TM * 16;
+    float* red = reinterpret_cast<float*>(lds);  // [KS - 1][NL][NA][64]
+    static_assert((KS - 1) * NL * NA * 64 * 4 <= NS * STAGE, "partials fit the ring");
+    if (kg > 0) {
+#pragma unroll
+      for (int t = 0; t < TN; ++t)
+#pragma unroll
+        for (int u = 0; u < TM; ++u)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            red[(((kg - 1) * NL + wl) * NA + (t * TM + u) * 16 + e) * 64 + lane] = acc[t][u][e];
+    }
+    __syncthreads();
+    if (kg == 0) {
+      for (int g2 = 1; g2 < KS; ++g2)
+#pragma unroll
+        for (int t = 0; t < TN; ++t)
+#pragma unroll
+          for (int u = 0; u < TM; ++u)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+              acc[t][u][e] += red[(((g2 - 1) * NL + wl) * NA + (t * TM + u) * 16 + e) * 64 + lane];
+    }
+    __syncthreads();
+  }
   bool over = false;
   constexpr int NT = 64 * NW, VLD = BN + 4, C4 = BN / 4;
-  constexpr bool stage_u = (BN / 16) * BM * 16 <= NS * STEP;              // SwiGLU halves
-  constexpr bool stage_v = BM * VLD * 4 + BM * BN * 2 <= NS * STEP;      // f32 tile + halves
+  constexpr bool stage_u = (BN / 16) * BM * 16 <= NS * STAGE;              // SwiGLU halves
+  constexpr bool stage_v = BM * VLD * 4 + BM * BN * 2 <= NS * STAGE;      // f32 tile + halves
   // accumulator (t, u), lane l, group g: activation row r, weight rows nl .. nl + 3
-  // (local to the block)
+  // (local to the block); K group 0 holds the sums
   auto for_each_group = [&](auto&& f) {
+    if (kg != 0) return;
 #pragma unroll
     for (int u = 0; u < TM; ++u) {
       const int r = 32 * TM * wy + 32 * u + (lane & 31);
@@ -1070,6 +1105,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm_mx(GemmArgs a) {
     }
   } else {
     // (tiles too large to stage: the accumulators' pieces go out directly)
+    if (kg == 0)
 #pragma unroll
     for (int u = 0; u < TM; ++u) {
       const int r = 32 * TM * wy + 32 * u + (lane & 31);
@@ -1231,15 +1267,17 @@ hipError_t launch_gemm_rows(const GemmArgs& a, hipStream_t s) {
   if (!i8 && !a.scale) {
     const long long m256 = (a.M + 255) / 256, m128 = (a.M + 127) / 128;
     if (a.nrows % 192 == 0 && m256 * (a.nrows / 192) >= kCUs) {
-      launch_kernel((k_gemm_mx<2, 2, 4, 3, 5>), dim3((unsigned)m256, a.nrows / 192), dim3(768), s, a);
+      launch_kernel((k_gemm_mx<2, 2, 4, 3, 5, 1>), dim3((unsigned)m256, a.nrows / 192), dim3(768), s, a);
       return hipGetLastError();
     }
-    if (m128 * (a.nrows / 128) >= kCUs) {
-      launch_kernel((k_gemm_mx<2, 2, 2, 2, 8>), dim3((unsigned)m128, a.nrows / 128), dim3(256), s, a);
+    // (the 4-wave tiles take their K steps in two groups of waves: stages of two
+    // steps, so K must be a multiple of 128)
+    if (a.K % 128 == 0 && m128 * (a.nrows / 128) >= kCUs) {
+      launch_kernel((k_gemm_mx<2, 2, 2, 2, 4, 2>), dim3((unsigned)m128, a.nrows / 128), dim3(512), s, a);
       return hipGetLastError();
     }
-    if (m128 * (a.nrows / 64) >= kCUs) {
-      launch_kernel((k_gemm_mx<2, 1, 2, 2, 10>), dim3((unsigned)m128, a.nrows / 64), dim3(256), s, a);
+    if (a.K % 128 == 0 && m128 * (a.nrows / 64) >= kCUs) {
+      launch_kernel((k_gemm_mx<2, 1, 2, 2, 5, 2>), dim3((unsigned)m128, a.nrows / 64), dim3(512), s, a);
       return hipGetLastError();
     }
   }
