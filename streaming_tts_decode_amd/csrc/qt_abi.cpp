@@ -1020,7 +1020,6 @@ qt_status enqueue_prefill(const qt_model* m, const qt_prefill_args* a, const qt_
     g.epi = EPI_STORE;
     g.out_f32 = qkv;
     g.out_ld = w.qkv_ld;
-    if ((r = run(g))) return r;
     PrefillQkArgs q{};
     q.qkv = qkv;
     q.R = R;
@@ -1037,7 +1036,9 @@ qt_status enqueue_prefill(const qt_model* m, const qt_prefill_args* a, const qt_
     q.max_pages = a->max_pages;
     q.rowinfo = rowinfo;
     q.status = a->status;
-    QT_LAUNCH(launch_prefill_qk(q, R, T.rope_theta, st));
+    bool qk_done = false;  // (the projection's epilogue does the q/k pass when it can)
+    QT_LAUNCH(launch_gemm_rows(g, st, &q, T.rope_theta, &qk_done));
+    if (!qk_done) QT_LAUNCH(launch_prefill_qk(q, R, T.rope_theta, st));
     PrefillAttnArgs at{};
     at.qkv = qkv;
     at.qkv_ld = w.qkv_ld;

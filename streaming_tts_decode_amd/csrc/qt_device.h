@@ -181,5 +181,30 @@ __device__ __forceinline__ uint4 load_nt(const uint4* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// The inverse frequency of RoPE pair l (dimensions l and l + 64) in revolutions
+// per position, theta^(-2l/128) / (2 pi), in double.
+__device__ __forceinline__ double rope_inv_rev(int l, float theta_log2) {
+  return exp2(-(double)(2 * l) * (double)theta_log2 / 128.0) *
+         0.15915494309189533576888376337251;  // 1 / (2 pi)
+}
+
+// Per-head RMSNorm + rotate-half RoPE of one 128-vector held by one wave, lane l
+// holding elements l (v0) and l + 64 (v1), the two halves of its RoPE pair: the
+// norm is one wave reduction and the rotation stays in the lane, so no block
+// barrier is needed.  The angle pos * inv_rev is reduced to [0, 1) revolutions
+// in double; the hardware sine and cosine take it from there.
+__device__ __forceinline__ void norm_rope_pair(float& v0, float& v1, float g0, float g1, float eps,
+                                               double inv_rev, int pos) {
+  const float f = 1.0f / sqrtf(wave_sum(v0 * v0 + v1 * v1) * (1.0f / 128.0f) + eps);
+  v0 = v0 * f * g0;
+  v1 = v1 * f * g1;
+  double rev = (double)pos * inv_rev;
+  rev -= floor(rev);
+  const float sn = __builtin_amdgcn_sinf((float)rev), cs = __builtin_amdgcn_cosf((float)rev);
+  const float r0 = v0 * cs - v1 * sn, r1 = v1 * cs + v0 * sn;
+  v0 = r0;
+  v1 = r1;
+}
+
 }  // namespace dev
 }  // namespace qt

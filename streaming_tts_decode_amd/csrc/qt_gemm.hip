@@ -826,7 +826,7 @@ __global__ __launch_bounds__(256) void k_gemm_rows_pipe(GemmArgs a) {
 // weight rows per group: the SwiGLU pairs (even, odd) and the 16-row sums of
 // squares (two groups and the lane 32 apart) stay within reach.
 template <int TM, int TN, int WGM, int WGN, int NS, int KS>
-__global__ __launch_bounds__(64 * WGM * WGN * KS) void k_gemm_mx(GemmArgs a) {
+__global__ __launch_bounds__(64 * WGM * WGN * KS) void k_gemm_mx(GemmArgs a, PrefillQkArgs qk, float theta_log2) {
   constexpr int NL = WGM * WGN;                     // waves per K group
   constexpr int NW = NL * KS;
   constexpr int BM = 32 * TM * WGM, BN = 32 * TN * WGN;
@@ -1052,12 +1052,84 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS) void k_gemm_mx(GemmArgs a) {
   } else if (a.epi != EPI_SWIGLU && stage_v) {
     // f32 tile [BM][BN + 4] (the padding keeps the lanes' 16-byte writes apart)
     float* vt = reinterpret_cast<float*>(lds);
+    // q/k pass in the epilogue: a tile of 128 columns is one head (see below); each
+    // row's position and, for k and v, its page are looked up once, while the tile
+    // is staged, into int2 s_row[BM] after the tile: (rotation position, page or
+    // -1 none, -2 past the table, -3 bad page)
+    const bool fused = a.epi == EPI_STORE && BN == 128 && qk.qkv;
+    const int q_dim = qk.n_q * 128, kv_dim = qk.n_kv * 128, col0 = nb0;
+    const int kind = col0 < q_dim ? 0 : (col0 < q_dim + kv_dim ? 1 : 2);  // q, k, v
+    int2* s_row = reinterpret_cast<int2*>(lds + BM * VLD * 4);
+    int row_sq = -1, row_pos = 0;
+    if (fused && tid < BM) {
+      const int m = min(mb + tid, M - 1);
+      row_sq = qk.rowinfo[2 * m];
+      row_pos = qk.rowinfo[2 * m + 1];
+    }
     for_each_group([&](int r, int nl, const float (&v)[4]) {
       *reinterpret_cast<float4*>(vt + r * VLD + nl) = make_float4(v[0], v[1], v[2], v[3]);
     });
+    if (fused && tid < BM) {
+      int pg = -1;
+      if (kind > 0 && row_sq >= 0) {
+        if (row_pos >= qk.max_pages * kPage) {
+          pg = -2;
+        } else {
+          pg = qk.page_table[(size_t)row_sq * qk.max_pages + row_pos / kPage];
+          if (pg < 0 || pg >= qk.num_pages) pg = -3;
+        }
+      }
+      s_row[tid] = make_int2(row_sq >= 0 ? row_pos : 0, pg);
+    }
     __syncthreads();
     // thread i: row i / C4, columns 4 (i % C4) .. + 3; a wave covers whole rows
-    if (a.epi == EPI_STORE) {
+    if (fused) {
+      // The tile is one head of the prompt's q, k or v for BM rows: each wave takes
+      // whole rows, lane l elements l and l + 64, and applies what the separate
+      // q/k pass would (same arithmetic, same order): q and k are normalised and
+      // rotated; q goes back into qkv scaled by 1/sqrt(128), k and v to their pages.
+      static_assert(BM * VLD * 4 + BM * 8 <= NS * STAGE || BN != 128, "row table fits");
+      const int h = (col0 - q_dim - (kind == 2 ? kv_dim : 0)) >> 7;
+      const uint16_t* gain = kind == 0 ? qk.q_norm : qk.k_norm;
+      const float g0 = bf2f(gain[lane]), g1 = bf2f(gain[lane + 64]);
+      const double inv_rev = rope_inv_rev(lane, theta_log2);
+      uint16_t* dst = kind == 1 ? qk.k_pool : qk.v_pool;
+      constexpr int RR = 4;  // rows per pass: independent reductions and rotations
+      for (int r0 = wave * RR; r0 < BM; r0 += NW * RR) {
+        float v0[RR], v1[RR];
+        int2 ri[RR];
+#pragma unroll
+        for (int k = 0; k < RR; ++k) {  // (rows past BM are read clamped, never written)
+          const int r = min(r0 + k, BM - 1);
+          v0[k] = vt[r * VLD + lane];
+          v1[k] = vt[r * VLD + lane + 64];
+          ri[k] = s_row[r];
+        }
+        if (kind < 2)
+#pragma unroll
+          for (int k = 0; k < RR; ++k) norm_rope_pair(v0[k], v1[k], g0, g1, qk.eps, inv_rev, ri[k].x);
+#pragma unroll
+        for (int k = 0; k < RR; ++k) {
+          const int m = mb + r0 + k;
+          if (m >= M || r0 + k >= BM) break;  // (wave-uniform)
+          if (kind == 0) {
+            float* row = qk.qkv + (size_t)m * qk.qkv_ld + col0;
+            row[lane] = v0[k] * kInvSqrtHd;
+            row[lane + 64] = v1[k] * kInvSqrtHd;
+            continue;
+          }
+          const int pg = ri[k].y;
+          if (pg < 0) {  // -1: a row past every sequence
+            if (kind == 1 && lane == 0 && pg == -2) atomicOr(qk.status, QT_STATUS_KV_OVERFLOW);
+            if (kind == 1 && lane == 0 && pg == -3) atomicOr(qk.status, QT_STATUS_BAD_PAGE);
+            continue;
+          }
+          const size_t off = ((size_t)pg * qk.n_kv + h) * (kPage * 128) + (size_t)(ri[k].x % kPage) * 128;
+          dst[off + lane] = f2bf(v0[k]);
+          dst[off + lane + 64] = f2bf(v1[k]);
+        }
+      }
+    } else if (a.epi == EPI_STORE) {
       for (int i = tid; i < BM * C4; i += NT) {
         const int r = i / C4, c4 = i - r * C4, m = mb + r;
         if (m < M)
@@ -1252,7 +1324,10 @@ void gemm_kernel_name(const GemmArgs& a, char* buf, int len) {
            a.keep_w ? "true" : "false", p.tiles);
 }
 
-hipError_t launch_gemm_rows(const GemmArgs& a, hipStream_t s) {
+hipError_t launch_gemm_rows(const GemmArgs& a, hipStream_t s, const PrefillQkArgs* qk, float theta,
+                             bool* qk_done) {
+  if (qk_done) *qk_done = false;
+  const PrefillQkArgs none{};
   if (a.M < 1 || a.nrows <= 0 || (a.nrows % 128) || (a.row0 % kGemmRows) ||
       a.row0 + a.nrows > a.N || a.K <= 0 || (a.K % 64) || a.act_ld < a.M || (a.M % 16))
     return hipErrorInvalidValue;
@@ -1267,17 +1342,26 @@ hipError_t launch_gemm_rows(const GemmArgs& a, hipStream_t s) {
   if (!i8 && !a.scale) {
     const long long m256 = (a.M + 255) / 256, m128 = (a.M + 127) / 128;
     if (a.nrows % 192 == 0 && m256 * (a.nrows / 192) >= kCUs) {
-      launch_kernel((k_gemm_mx<2, 2, 4, 3, 5, 1>), dim3((unsigned)m256, a.nrows / 192), dim3(768), s, a);
+      launch_kernel((k_gemm_mx<2, 2, 4, 3, 5, 1>), dim3((unsigned)m256, a.nrows / 192), dim3(768), s, a, none,
+                    0.f);
       return hipGetLastError();
     }
     // (the 4-wave tiles take their K steps in two groups of waves: stages of two
     // steps, so K must be a multiple of 128)
     if (a.K % 128 == 0 && m128 * (a.nrows / 128) >= kCUs) {
-      launch_kernel((k_gemm_mx<2, 2, 2, 2, 4, 2>), dim3((unsigned)m128, a.nrows / 128), dim3(512), s, a);
+      // 128-column tiles of a QKV projection are whole heads: the q/k pass is done
+      // in the epilogue (whole matrix, rows as the pass expects, 2 q heads per kv head)
+      const bool fuse = qk && a.epi == EPI_STORE && a.row0 == 0 && qk->qkv == a.out_f32 &&
+                        qk->qkv_ld == a.out_ld && qk->R == a.M && qk->n_q == 2 * qk->n_kv &&
+                        a.nrows == (qk->n_q + 2 * qk->n_kv) * 128;
+      launch_kernel((k_gemm_mx<2, 2, 2, 2, 4, 2>), dim3((unsigned)m128, a.nrows / 128), dim3(512), s, a,
+                    fuse ? *qk : none, fuse ? (float)log2((double)theta) : 0.f);
+      if (qk_done) *qk_done = fuse;
       return hipGetLastError();
     }
     if (a.K % 128 == 0 && m128 * (a.nrows / 64) >= kCUs) {
-      launch_kernel((k_gemm_mx<2, 1, 2, 2, 5, 2>), dim3((unsigned)m128, a.nrows / 64), dim3(512), s, a);
+      launch_kernel((k_gemm_mx<2, 1, 2, 2, 5, 2>), dim3((unsigned)m128, a.nrows / 64), dim3(512), s, a, none,
+                    0.f);
       return hipGetLastError();
     }
   }

@@ -438,7 +438,11 @@ void gemm_kernel_name(const GemmArgs& a, char* buf, int len);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 // Many activation rows (M a multiple of 16; nrows a multiple of 128): EPI_STORE,
 // EPI_RESID and EPI_SWIGLU, one 16-row statistics slot per 16 weight rows.
-hipError_t launch_gemm_rows(const GemmArgs& a, hipStream_t s);
+// qk: the prompt's q/k pass that follows a QKV projection; when the projection's
+// tiles are whole heads the pass is done in its epilogue and *qk_done is set, else
+// the caller launches it.
+hipError_t launch_gemm_rows(const GemmArgs& a, hipStream_t s, const PrefillQkArgs* qk = nullptr,
+                            float theta = 0.f, bool* qk_done = nullptr);
 hipError_t launch_attn_paged(const AttnPagedArgs& a, int B, float theta, hipStream_t s);
 hipError_t launch_attn_pred(const AttnPredArgs& a, float theta, hipStream_t s);
 hipError_t launch_frame_begin(const FrameBeginArgs& a, hipStream_t s);

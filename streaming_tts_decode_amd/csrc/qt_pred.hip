@@ -441,23 +441,6 @@ struct AttnSmem {
   float lsum[2][2];
 };
 
-__device__ __forceinline__ double rope_inv_rev(int l, float theta_log2) {
-  return exp2(-(double)(2 * l) * (double)theta_log2 / 128.0) * 0.15915494309189533576888376337251;
-}
-
-__device__ __forceinline__ void norm_rope_pair(float& v0, float& v1, float g0, float g1, float eps,
-                                               double inv_rev, int pos) {
-  const float f = 1.0f / sqrtf(wave_sum(v0 * v0 + v1 * v1) * (1.0f / 128.0f) + eps);
-  v0 = v0 * f * g0;
-  v1 = v1 * f * g1;
-  double rev = (double)pos * inv_rev;
-  rev -= floor(rev);
-  const float sn = __builtin_amdgcn_sinf((float)rev), cs = __builtin_amdgcn_cosf((float)rev);
-  const float r0 = v0 * cs - v1 * sn, r1 = v1 * cs + v0 * sn;
-  v0 = r0;
-  v1 = r1;
-}
-
 __device__ void stage_attn(const Ctx& c, const PredPersistArgs& a, AttnSmem& sm) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = c.r;

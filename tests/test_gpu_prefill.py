@@ -128,13 +128,15 @@ def test_prefill_graph_replays_other_packings(small_pm):
     dec.close()
 
 
-def test_prefill_overflow_sets_status(small_pm):
+@pytest.mark.parametrize("rows", [48, 2048])
+def test_prefill_overflow_sets_status(small_pm, rows):
+    # (2048 rows: the q/k pass runs in the QKV projection's epilogue)
     torch = small_pm.torch
     from streaming_tts_decode_amd import STATUS_KV_OVERFLOW
     from streaming_tts_decode_amd.runtime import Decoder
     t = synth.SMALL.talker
     dec = Decoder(small_pm, batch=1, max_pages=2)  # 32 positions
-    dec.prefill_setup(48)
+    dec.prefill_setup(rows)
     dec.prefill_inputs([synth.normal_bf16("pfo", (40, t.hidden))])
     dec.status.zero_()
     dec.prefill()
