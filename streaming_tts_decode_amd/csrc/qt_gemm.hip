@@ -1138,26 +1138,40 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS) void k_gemm_mx(GemmArgs a, Pre
       }
     } else {  // EPI_RESID: x += v; u = half(x * gain) staged as chunk rows; 16-column sums
       uint2* ut = reinterpret_cast<uint2*>(lds + BM * VLD * 4);  // [BN / 8][BM][2]
-      for (int i = tid; i < BM * C4; i += NT) {  // (every lane runs every trip: 4 TM TN)
+      // every trip's residual and gains are loaded before any is stored back (a
+      // store to x between them would keep the compiler from issuing the next
+      // trip's load early: one memory round trip per trip)
+      constexpr int IT = BM * C4 / NT;  // trips per thread (every lane runs every trip)
+      float4 xo[IT];
+      uint2 gn[IT];
+#pragma unroll
+      for (int k = 0; k < IT; ++k) {
+        const int i = tid + k * NT, r = i / C4, c4 = i - r * C4, m = min(mb + r, M - 1);
+        const int n = nb0 + 4 * c4;
+        xo[k] = *reinterpret_cast<const float4*>(a.out_f32 + (size_t)m * a.out_ld + n);
+        gn[k] = a.u_gain ? *reinterpret_cast<const uint2*>(a.u_gain + n) : make_uint2(0u, 0u);
+      }
+#pragma unroll
+      for (int k = 0; k < IT; ++k) {
+        const int i = tid + k * NT;
         const int r = i / C4, c4 = i - r * C4, m = mb + r, n = nb0 + 4 * c4;
         const bool live = m < M;
         const float4 v = *reinterpret_cast<const float4*>(vt + r * VLD + 4 * c4);
         float x[4] = {0.f, 0.f, 0.f, 0.f};
         if (live) {
-          float* xp = a.out_f32 + (size_t)m * a.out_ld + n;
-          const float4 x0 = *reinterpret_cast<const float4*>(xp);
-          x[0] = x0.x + v.x;
-          x[1] = x0.y + v.y;
-          x[2] = x0.z + v.z;
-          x[3] = x0.w + v.w;
-          *reinterpret_cast<float4*>(xp) = make_float4(x[0], x[1], x[2], x[3]);
+          x[0] = xo[k].x + v.x;
+          x[1] = xo[k].y + v.y;
+          x[2] = xo[k].z + v.z;
+          x[3] = xo[k].w + v.w;
+          *reinterpret_cast<float4*>(a.out_f32 + (size_t)m * a.out_ld + n) = make_float4(x[0], x[1], x[2], x[3]);
         }
         if (a.u_gain) {
+          const float g[4] = {bf_lo(gn[k].x), bf_hi(gn[k].x), bf_lo(gn[k].y), bf_hi(gn[k].y)};
           uint32_t h2[2];
 #pragma unroll
           for (int e = 0; e < 2; ++e)
-            h2[e] = (uint32_t)f2h_chk(x[2 * e] * bf2f(a.u_gain[n + 2 * e]), over) |
-                    ((uint32_t)f2h_chk(x[2 * e + 1] * bf2f(a.u_gain[n + 2 * e + 1]), over) << 16);
+            h2[e] = (uint32_t)f2h_chk(x[2 * e] * g[2 * e], over) |
+                    ((uint32_t)f2h_chk(x[2 * e + 1] * g[2 * e + 1], over) << 16);
           ut[((c4 >> 1) * BM + r) * 2 + (c4 & 1)] = make_uint2(h2[0], h2[1]);
           // the 16 columns of a sum are four consecutive lanes
           float ss = x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
