@@ -173,6 +173,41 @@ def test_prefill_2048_rows(small_pm, orc_small):
     dec.close()
 
 
+def test_prefill_bench_prompt_first_layers(full_pm, full_weights):
+    """The benchmark's prompt configuration: the full model, one 1024-token prompt in
+    1024 rows (every projection in its large-tile form, the q/k pass in the QKV
+    epilogue).  The keys and values of layers 0 and 1 at all 1024 positions depend
+    on those layers only, so an oracle over the first two layers of the same
+    weights checks them exactly as the full-depth oracle would."""
+    import dataclasses
+    import oracle
+    from streaming_tts_decode_amd.runtime import Decoder
+    d = synth.FULL
+    t = d.talker
+    d2 = dataclasses.replace(d, talker=dataclasses.replace(t, layers=2))
+    orc2 = oracle.OracleModel(d2, full_weights)
+    T = 1024
+    prompt = synth.normal_bf16("pfbench.prompt", (T, t.hidden))
+    log(f"[prefill] bench prompt: 1 x {T} in {T} rows, layers 0-1 against a 2-layer oracle")
+    dec = Decoder(full_pm, batch=1, max_pages=T // 16)
+    dec.prefill_setup(T)
+    dec.prefill_inputs([prompt])
+    dec.status.zero_()
+    dec.prefill()
+    full_pm.torch.cuda.synchronize()
+    assert int(dec.status.item()) == 0
+    pre = orc2.prefill(prompt, capacity=T)
+    pages = dec.page_table_np[0, :T // 16]
+    for name, pool, ref in (("K", dec.k_pages, pre["kc"]), ("V", dec.v_pages, pre["vc"])):
+        got = _bf16(pool[:2, pages].cpu().numpy().view(np.uint16))
+        got = got.transpose(0, 1, 3, 2, 4).reshape(2, T, t.n_kv, t.head_dim)
+        scale = np.abs(ref).max(axis=(1, 3), keepdims=True)
+        err = np.abs(got - ref[:, :T]) / scale
+        log(f"[parity] bench prompt {name}: max error {err.max():.3g} of the head scale")
+        assert err.max() <= 2e-2, f"bench prompt {name}: max error {err.max():.3g} of the head scale"
+    dec.close()
+
+
 def test_prefill_full_model_int8(full_pm_i8, orc_full_i8):
     dec, _, _ = _run(full_pm_i8, orc_full_i8, synth.FULL, [33], rows=64, max_pages=4, tag="pfi8",
                      frames_after=1)
