@@ -811,11 +811,12 @@ __global__ __launch_bounds__(256) void k_gemm_rows_pipe(GemmArgs a) {
 // rows) tile as TN x TM accumulators of 32 x 32; WGM x WGN waves make a block of
 // BM = 32 TM WGM rows by BN = 32 TN WGN weight rows.  Every operand byte is
 // copied once per block from global memory into LDS by the load unit
-// (global_load_lds, 16 bytes per lane at the wave's LDS base + 16 x lane), one
-// 32-wide K step per stage, NS stages in the ring; each wave then reads its
-// fragments from LDS.  Per K step the LDS holds the BN/16 weight tiles as packed
-// (1 KB each, lane order of the 16-row tile) and the activations as 4 chunks of
-// BM rows x 16 bytes.
+// (global_load_lds, 16 bytes per lane at the wave's LDS base + 16 x lane), KS
+// 32-wide K steps per stage, NS stages in the ring; each wave then reads its
+// fragments from LDS.  KS > 1 splits the K steps over KS groups of waves (group g
+// takes step KS s + g of stage s), whose partial sums are added at the end.  Per K
+// step the LDS holds the BN/16 weight tiles as packed (1 KB each, lane order of
+// the 16-row tile) and the activations as 4 chunks of BM rows x 16 bytes.
 //
 // Fragment reads are conflict-free: for the weights, lane l takes row l & 31 of
 // the 32-row block (tile (l >> 4) & 1 of the two, row l & 15 in it) at chunk
@@ -916,15 +917,14 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS) void k_gemm_mx(GemmArgs a, Pre
   // SIMD, so that one wave's waits overlap another's products).  A wave's fragments
   // of stage s were read during stage s - 1.  Once they are in (and so this wave is
   // done with slot s % NS) and this wave's copies of stage s + 1 have landed, one
-  // barrier lets the slot be refilled with stage s + NS and stage s + 1 be read.  Those reads and copies are interleaved with step j's products, one
-  // group after each product: a wave issues them while the matrix unit works,
-  // which it could not do with the products issued back to back (with one wave per
-  // SIMD, nothing else would keep the unit busy meanwhile).  The reads go with the
-  // first half of the products, so that they are in before the next step; the
-  // copies with the second half.
+  // barrier lets the slot be refilled with stage s + NS and stage s + 1 be read.
+  // Those reads and copies are placed between stage s's products, one group after
+  // each product (the reads with the first half, so that they are in before the
+  // next stage; the copies with the second half), fenced so that the scheduler
+  // keeps that order.
   constexpr int NMF = 2 * TN * TM, HALF = NMF / 2, NRD = 2 * (TN + TM);
-  auto body = [&](int j, u32x4 (&wv)[2][TN], u32x4 (&av)[2][TM], u32x4 (&wn)[2][TN],
-                  u32x4 (&an)[2][TM]) {  // (j: the stage)
+  auto body = [&](int s, u32x4 (&wv)[2][TN], u32x4 (&av)[2][TM], u32x4 (&wn)[2][TN],
+                  u32x4 (&an)[2][TM]) {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -933,14 +933,14 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS) void k_gemm_mx(GemmArgs a, Pre
 #pragma unroll
       for (int u = 0; u < TM; ++u) asm volatile("" : "+v"(av[h][u]));
     }
-    if (j + NS - 1 < nst) {  // younger issued stages than j + 1: NS - 2 of them
+    if (s + NS - 1 < nst) {  // younger issued stages than s + 1: NS - 2 of them
       if (NHI == 0 || wave < NHI) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PHI * (NS - 2)) : "memory");
       else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PLO * (NS - 2)) : "memory");
     } else {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     __builtin_amdgcn_s_barrier();
-    const bool more_reads = j + 1 < nst, more_copies = j + NS < nst;
+    const bool more_reads = s + 1 < nst, more_copies = s + NS < nst;
 #pragma unroll
     for (int f = 0; f < NMF; ++f) {
       const int h = f / (TN * TM), t = (f / TM) % TN, u = f % TM;
@@ -949,14 +949,14 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS) void k_gemm_mx(GemmArgs a, Pre
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int r = 0; r < NRD; ++r)
-        if (r * HALF / NRD == f && more_reads) read_one(j + 1, r, wn, an);
+        if (r * HALF / NRD == f && more_reads) read_one(s + 1, r, wn, an);
 #pragma unroll
       for (int c = 0; c < PHI; ++c)
-        if (HALF + c * (NMF - HALF) / PHI == f && more_copies) copy_one(j + NS, c);
+        if (HALF + c * (NMF - HALF) / PHI == f && more_copies) copy_one(s + NS, c);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // the ring's first NS steps are copied while the norm sums are in flight
+  // the ring's first NS stages are copied while the norm sums are in flight
   norm_factors<BM, 64 * NW, 16>(a, mb, s_inv, s_part, [&] {
 #pragma unroll
     for (int st = 0; st < NS; ++st)
@@ -972,9 +972,9 @@ __global__ __launch_bounds__(64 * WGM * WGN * KS) void k_gemm_mx(GemmArgs a, Pre
   __builtin_amdgcn_s_barrier();
   u32x4 w0[2][TN], a0[2][TM], w1[2][TN], a1[2][TM];
   read(0, w0, a0);
-  for (int j = 0; j < nst; j += 2) {  // (nst is even)
-    body(j, w0, a0, w1, a1);
-    body(j + 1, w1, a1, w0, a0);
+  for (int s = 0; s < nst; s += 2) {  // (nst is even)
+    body(s, w0, a0, w1, a1);
+    body(s + 1, w1, a1, w0, a0);
   }
   // ---- epilogue.  The ring is free once every wave is past its last step; it
   // stages the block's outputs so that they leave as whole rows (f32 rows for a
