@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define QT_ABI_VERSION 2
+#define QT_ABI_VERSION 3
 
 typedef enum {
   QT_OK = 0,
@@ -396,10 +396,14 @@ typedef enum {
   QT_KERNEL_ATTN_PRED = 3,   /* k_attn_pred: the same over the predictor's frame-local KV */
   QT_KERNEL_EMBED = 4,       /* k_embed: codebook-embedding gather of a predictor step */
   QT_KERNEL_FRAME_END = 5,   /* k_frame_end: tokens out, kv_len advance */
-  QT_KERNEL_PREDICTOR = 6    /* k_pred_persist: every code-predictor step of the frame in one
+  QT_KERNEL_PREDICTOR = 6,   /* k_pred_persist: every code-predictor step of the frame in one
                                 launch (QT_PREDICTOR=persistent; see qt_frame_decode); by
                                 default the predictor runs as QT_KERNEL_EMBED / GEMM /
                                 ATTN_PRED launches */
+  QT_KERNEL_ATTN_MERGE = 7   /* k_attn_merge: the Talker attention's split partials merged in
+                                split order, after each QT_KERNEL_ATTN_PAGED launch of a frame
+                                of 16 sessions or more (below 16, the last split to finish
+                                merges them inside k_attn_paged) */
 } qt_kernel_kind;
 
 typedef struct {
@@ -420,8 +424,11 @@ typedef struct qt_trace qt_trace;
 /* Create a trace handle holding timing events for up to max_launches launches. */
 qt_status qt_trace_create(int32_t max_launches, qt_trace** out);
 
-/* Number of kernel launches one frame of this mode and batch makes. */
-qt_status qt_frame_launch_count(const qt_model_cfg* cfg, int32_t mode, int32_t* n);
+/* Number of kernel launches one frame of this mode and batch (1..32 sessions) makes:
+ * *n receives it.  From 16 sessions on, each Talker layer adds a QT_KERNEL_ATTN_MERGE
+ * launch.  QT_E_INVALID_ARG for a NULL pointer, a mode outside qt_mode or a batch
+ * outside 1..32; a cfg that qt_model_create would refuse is refused the same way. */
+qt_status qt_frame_launch_count(const qt_model_cfg* cfg, int32_t mode, int32_t batch, int32_t* n);
 
 /* Enqueue one frame exactly as qt_frame_decode (same arguments and checks) with the
  * trace's events recorded around its launches.  QT_E_CAPACITY, before anything is

@@ -42,7 +42,7 @@ EXPORTED = ["qt_last_error", "qt_abi_version", "qt_validate_cfg", "qt_packed_byt
 SCHED_MAX_BUCKETS, SCHED_MAX_BATCH, SCHED_MAX_SESSIONS = 8, 32, 4096
 SESSION_FREE, SESSION_RUNNING, SESSION_ENDED_EOS, SESSION_ENDED_MAX = 0, 1, 2, 3
 KERNEL_KINDS = {0: "frame_begin", 1: "gemm", 2: "attn_paged", 3: "attn_pred", 4: "embed",
-                5: "frame_end", 6: "predictor"}
+                5: "frame_end", 6: "predictor", 7: "attn_merge"}
 
 
 class QtError(RuntimeError):
@@ -174,7 +174,8 @@ def lib():
         L.qt_trace_create.restype = st
         L.qt_trace_create.argtypes = [C.c_int32, C.POINTER(_P)]
         L.qt_frame_launch_count.restype = st
-        L.qt_frame_launch_count.argtypes = [C.POINTER(ModelCfg), C.c_int32, C.POINTER(C.c_int32)]
+        L.qt_frame_launch_count.argtypes = [C.POINTER(ModelCfg), C.c_int32, C.c_int32,
+                                            C.POINTER(C.c_int32)]
         L.qt_frame_trace.restype = st
         L.qt_frame_trace.argtypes = frame_args + [_P, _P]
         L.qt_trace_read.restype = st
@@ -337,9 +338,9 @@ def qt_trace_create(max_launches: int) -> int:
     return t.value
 
 
-def qt_frame_launch_count(cfg: ModelCfg, mode: int) -> int:
+def qt_frame_launch_count(cfg: ModelCfg, mode: int, batch: int) -> int:
     n = C.c_int32()
-    _check(lib().qt_frame_launch_count(C.byref(cfg), mode, C.byref(n)), "qt_frame_launch_count")
+    _check(lib().qt_frame_launch_count(C.byref(cfg), mode, batch, C.byref(n)), "qt_frame_launch_count")
     return n.value
 
 

@@ -38,12 +38,13 @@ qt_status fail(qt_status st, const char* fmt, ...) {
 
 qt_status ok() { return QT_OK; }
 
-// Launches of one frame: entry, per Talker layer QKV / attention / o / gate-up /
-// down, the head GEMM, per predictor step the gather, 5-kernel layers and the step
-// head, and the exit kernel.
-int frame_launches(const qt_model_cfg& c, int mode) {
+// Launches of one frame of B sessions: entry, per Talker layer QKV / attention
+// (+ the split merge from kAttnMergeMinBatch sessions on) / o / gate-up / down, the
+// head GEMM, per predictor step the gather, 5-kernel layers and the step head, and
+// the exit kernel.
+int frame_launches(const qt_model_cfg& c, int mode, int B) {
   int n = 3;  // entry, head GEMM, exit
-  if (mode != QT_MODE_PREDICTOR) n += 5 * c.talker.layers;
+  if (mode != QT_MODE_PREDICTOR) n += (attn_merge_separate(B) ? 6 : 5) * c.talker.layers;
   if (mode != QT_MODE_TALKER) n += (c.n_codebooks - 1) * (2 + 5 * c.predictor.layers);
   return n;
 }
@@ -669,6 +670,10 @@ qt_status enqueue_frame(const qt_model* m, const qt_sessions* ss, const qt_kv_ca
         a.status = out->status;
         QT_MARK(QT_KERNEL_ATTN_PAGED, "k_attn_paged", B, nullptr);
         QT_LAUNCH(launch_attn_paged(a, B, T.rope_theta, st));
+        if (attn_merge_separate(B)) {
+          QT_MARK(QT_KERNEL_ATTN_MERGE, "k_attn_merge", B, nullptr);
+          QT_LAUNCH(launch_attn_merge(a, B, st));
+        }
         return ok();
       });
       if (s) return s;
@@ -1525,13 +1530,15 @@ qt_status qt_trace_create(int32_t max_launches, qt_trace** out) {
   return ok();
 }
 
-qt_status qt_frame_launch_count(const qt_model_cfg* cfg, int32_t mode, int32_t* n) {
+qt_status qt_frame_launch_count(const qt_model_cfg* cfg, int32_t mode, int32_t batch, int32_t* n) {
   qt_status st = check_cfg(cfg);
   if (st) return st;
   if (!n) return fail(QT_E_INVALID_ARG, "n is NULL");
   if (mode < QT_MODE_FULL || mode > QT_MODE_PREDICTOR)
     return fail(QT_E_INVALID_ARG, "mode = %d is not a qt_mode", mode);
-  *n = frame_launches(*cfg, mode);
+  if (batch < 1 || batch > kMaxBatch)
+    return fail(QT_E_INVALID_ARG, "batch = %d: expected 1..%d", batch, kMaxBatch);
+  *n = frame_launches(*cfg, mode, batch);
   return ok();
 }
 
@@ -1541,7 +1548,7 @@ qt_status qt_frame_trace(qt_model* model, const qt_sessions* sessions, const qt_
   if (!trace) return fail(QT_E_INVALID_ARG, "trace is NULL");
   qt_status st = check_frame_args(model, sessions, kv, in, out, workspace, workspace_bytes);
   if (st) return st;
-  const int need = frame_launches(model->cfg, in->mode);
+  const int need = frame_launches(model->cfg, in->mode, sessions->batch);
   if (need > (int)trace->info.size())
     return fail(QT_E_CAPACITY, "the frame makes %d launches, the trace holds %d", need,
                 (int)trace->info.size());

@@ -12,6 +12,10 @@ namespace qt {
 constexpr int kHeadDim = 128;   // head dimension the attention kernels are written for
 constexpr int kPage = 16;       // Talker KV page size in positions
 constexpr int kMaxPagesPerSplit = 8;
+// From this many sessions on, the Talker attention's split partials are merged by
+// a launch of their own (k_attn_merge) instead of by the last split to arrive.
+constexpr int kAttnMergeMinBatch = 16;
+inline bool attn_merge_separate(int B) { return B >= kAttnMergeMinBatch; }
 
 // Activations that feed a GEMM are IEEE half (11-bit significand: about eight
 // times finer than bfloat16, which the 28-layer stack amplifies past the logit
@@ -444,6 +448,8 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm_rows(const GemmArgs& a, hipStream_t s, const PrefillQkArgs* qk = nullptr,
                             float theta = 0.f, bool* qk_done = nullptr);
 hipError_t launch_attn_paged(const AttnPagedArgs& a, int B, float theta, hipStream_t s);
+// after launch_attn_paged when attn_merge_separate(B)
+hipError_t launch_attn_merge(const AttnPagedArgs& a, int B, hipStream_t s);
 hipError_t launch_attn_pred(const AttnPredArgs& a, float theta, hipStream_t s);
 hipError_t launch_frame_begin(const FrameBeginArgs& a, hipStream_t s);
 hipError_t launch_embed(const EmbedArgs& a, hipStream_t s);

@@ -16,6 +16,48 @@ namespace {
 
 using namespace dev;
 
+// Merge of query head j's n_active split partials of session b, output dimension d:
+// 16 splits per round trip, every thread loading the splits' (max, sum) and its
+// own dimension of their outputs at once (indices past the last split repeat it
+// and are masked), then folding them into a running (max, sum, output) in split
+// order.  COHERENT: partials written in the same launch by other blocks (device-
+// coherent loads); else written by an earlier launch.
+template <bool COHERENT>
+__device__ __forceinline__ void merge_splits(const AttnPagedArgs& a, int b, int j, int d, int n_active,
+                                             size_t orow) {
+  const float* pb = a.part + ((size_t)b * a.n_q + j) * a.n_splits * 130;
+  float M = -INFINITY, L = 0.f, O = 0.f;
+  for (int c0 = 0; c0 < n_active; c0 += 16) {
+    float mv[16], lv[16], ov[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const float* ps = pb + (size_t)min(c0 + k, n_active - 1) * 130;
+      mv[k] = COHERENT ? dev_load(ps) : ps[0];
+      lv[k] = COHERENT ? dev_load(ps + 1) : ps[1];
+      ov[k] = COHERENT ? dev_load(ps + 2 + d) : ps[2 + d];
+    }
+    float Mc = M;
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      if (c0 + k < n_active) Mc = fmaxf(Mc, mv[k]);
+    const float r = expf(M - Mc);  // 0 on the first chunk (M = -inf, Mc finite)
+    L *= r;
+    O *= r;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      if (c0 + k < n_active) {
+        const float w = expf(mv[k] - Mc);
+        L = fmaf(lv[k], w, L);
+        O = fmaf(ov[k], w, O);
+      }
+    }
+    M = Mc;
+  }
+  bool over = false;
+  a.o[orow] = f2h_chk(O / L, over);
+  if (over) atomicOr(a.status, QT_STATUS_FP16_RANGE);
+}
+
 // ---------------------------------------------------------------------------
 // Talker decode attention over paged KV.  Grid (kv head, session, split): the
 // eight KV heads of one page are adjacent 4 KB pieces of it, and with the head
@@ -34,7 +76,13 @@ using namespace dev;
 // this split's page-table entries and the raw q / k / v values are loaded
 // together; then all of the split's K/V loads are issued, and the q and k
 // normalisation and rotation run while they are in flight.
-template <int PPS>
+//
+// SEP (batches of kAttnMergeMinBatch sessions or more): splits store their
+// partials with plain stores and exit, and k_attn_merge merges them in the next
+// launch, with the same arithmetic.  A block then ends without waiting for its
+// stores and an atomic (two round trips); with four rounds of blocks per launch
+// that shortens the launch by more than the extra launch costs.
+template <int PPS, bool SEP>
 __global__ __launch_bounds__(256) void k_attn_paged(AttnPagedArgs a, float theta_log2) {
   const int h = blockIdx.x, b = blockIdx.y, s = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -236,11 +284,19 @@ __global__ __launch_bounds__(256) void k_attn_paged(AttnPagedArgs a, float theta
     if (over) atomicOr(a.status, QT_STATUS_FP16_RANGE);
     return;
   }
+  float* pp = a.part + (((size_t)b * a.n_q + j0 + jj) * a.n_splits + s) * 130;
+  if (SEP) {  // merged by k_attn_merge, after this launch
+    pp[2 + d] = out;
+    if (d == 0) {
+      pp[0] = mstat[jj];
+      pp[1] = lstat[jj];
+    }
+    return;
+  }
   // Publish this split's partial with device-coherent stores, wait until they
   // are performed, then count the split in.  The last split to arrive reads all
   // partials with device-coherent loads.  (A full agent-scope fence here would
   // write back and invalidate the whole L2 of the XCD once per block.)
-  float* pp = a.part + (((size_t)b * a.n_q + j0 + jj) * a.n_splits + s) * 130;
   dev_store(pp + 2 + d, out);
   if (d == 0) {
     dev_store(pp, mstat[jj]);
@@ -255,42 +311,21 @@ __global__ __launch_bounds__(256) void k_attn_paged(AttnPagedArgs a, float theta
   }
   __syncthreads();
   if (!s_last) return;
-  // merge, 16 splits per round trip: every thread loads the splits' (max, sum)
-  // and its own dimension of their outputs at once (indices past the last split
-  // repeat it and are masked), then folds them into a running (max, sum, output)
-  // in split order
-  const float* pb = a.part + ((size_t)b * a.n_q + j0 + jj) * a.n_splits * 130;
-  float M = -INFINITY, L = 0.f, O = 0.f;
-  for (int c0 = 0; c0 < n_active; c0 += 16) {
-    float mv[16], lv[16], ov[16];
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const float* ps = pb + (size_t)min(c0 + k, n_active - 1) * 130;
-      mv[k] = dev_load(ps);
-      lv[k] = dev_load(ps + 1);
-      ov[k] = dev_load(ps + 2 + d);
-    }
-    float Mc = M;
-#pragma unroll
-    for (int k = 0; k < 16; ++k)
-      if (c0 + k < n_active) Mc = fmaxf(Mc, mv[k]);
-    const float r = expf(M - Mc);  // 0 on the first chunk (M = -inf, Mc finite)
-    L *= r;
-    O *= r;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      if (c0 + k < n_active) {
-        const float w = expf(mv[k] - Mc);
-        L = fmaf(lv[k], w, L);
-        O = fmaf(ov[k], w, O);
-      }
-    }
-    M = Mc;
-  }
-  bool over = false;
-  a.o[orow] = f2h_chk(O / L, over);
-  if (over) atomicOr(a.status, QT_STATUS_FP16_RANGE);
+  merge_splits<true>(a, b, j0 + jj, d, n_active, orow);
   if (tid == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The split partials of k_attn_paged<PPS, true>, merged: grid (KV head, session),
+// thread (jj, d) for query head 2h + jj, dimension d.  Sessions with one split (the
+// output is already written) or an out-of-range position (zeros written) are left.
+__global__ __launch_bounds__(256) void k_attn_merge(AttnPagedArgs a) {
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int jj = tid >> 7, d = tid & 127;
+  const int p = a.kv_len[b];
+  if (p < 0 || p >= a.max_pages * kPage) return;
+  const int n_active = p / (a.pages_per_split * kPage) + 1;
+  if (n_active == 1) return;
+  merge_splits<false>(a, b, 2 * h + jj, d, n_active, chunked(b, (2 * h + jj) * 128 + d, a.o_ld));
 }
 
 // ---------------------------------------------------------------------------
@@ -1320,21 +1355,36 @@ __global__ __launch_bounds__(64) void k_prefill_end(PrefillEndArgs a) {
 }  // namespace
 
 // --------------------------------------------------------------------------- launchers
+template <bool SEP>
+void launch_attn_paged_t(const AttnPagedArgs& a, dim3 grid, float tl, hipStream_t s) {
+  switch (a.pages_per_split) {
+    case 1: launch_kernel(k_attn_paged<1, SEP>, grid, dim3(256), s, a, tl); break;
+    case 2: launch_kernel(k_attn_paged<2, SEP>, grid, dim3(256), s, a, tl); break;
+    case 3: launch_kernel(k_attn_paged<3, SEP>, grid, dim3(256), s, a, tl); break;
+    case 4: launch_kernel(k_attn_paged<4, SEP>, grid, dim3(256), s, a, tl); break;
+    case 5: launch_kernel(k_attn_paged<5, SEP>, grid, dim3(256), s, a, tl); break;
+    case 6: launch_kernel(k_attn_paged<6, SEP>, grid, dim3(256), s, a, tl); break;
+    case 7: launch_kernel(k_attn_paged<7, SEP>, grid, dim3(256), s, a, tl); break;
+    default: launch_kernel(k_attn_paged<8, SEP>, grid, dim3(256), s, a, tl); break;
+  }
+}
+
 hipError_t launch_attn_paged(const AttnPagedArgs& a, int B, float theta, hipStream_t s) {
   if (a.pages_per_split < 1 || a.pages_per_split > kMaxPagesPerSplit || a.n_q != 2 * a.n_kv)
     return hipErrorInvalidValue;
   const dim3 grid(a.n_kv, B, a.n_splits);
   const float tl = (float)log2((double)theta);
-  switch (a.pages_per_split) {
-    case 1: launch_kernel(k_attn_paged<1>, grid, dim3(256), s, a, tl); break;
-    case 2: launch_kernel(k_attn_paged<2>, grid, dim3(256), s, a, tl); break;
-    case 3: launch_kernel(k_attn_paged<3>, grid, dim3(256), s, a, tl); break;
-    case 4: launch_kernel(k_attn_paged<4>, grid, dim3(256), s, a, tl); break;
-    case 5: launch_kernel(k_attn_paged<5>, grid, dim3(256), s, a, tl); break;
-    case 6: launch_kernel(k_attn_paged<6>, grid, dim3(256), s, a, tl); break;
-    case 7: launch_kernel(k_attn_paged<7>, grid, dim3(256), s, a, tl); break;
-    default: launch_kernel(k_attn_paged<8>, grid, dim3(256), s, a, tl); break;
-  }
+  if (attn_merge_separate(B))
+    launch_attn_paged_t<true>(a, grid, tl, s);
+  else
+    launch_attn_paged_t<false>(a, grid, tl, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_merge(const AttnPagedArgs& a, int B, hipStream_t s) {
+  if (a.pages_per_split < 1 || a.pages_per_split > kMaxPagesPerSplit || a.n_q != 2 * a.n_kv)
+    return hipErrorInvalidValue;
+  launch_kernel(k_attn_merge, dim3(a.n_kv, B), dim3(256), s, a);
   return hipGetLastError();
 }
 

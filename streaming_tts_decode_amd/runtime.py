@@ -272,7 +272,7 @@ class Decoder:
         """Run one frame as decode() does with an event around every launch; waits for
         it and returns [(kernel name, kind, info, ms)] in launch order."""
         if self._trace is None:
-            self._trace_n = qt_frame_launch_count(self.cfg, MODES["full"])
+            self._trace_n = qt_frame_launch_count(self.cfg, MODES["full"], self.B)
             self._trace = qt_trace_create(self._trace_n)
         ss, kv, fi, fo = self._descs(mode, forced, sampling=sampling)
         qt_frame_trace(self.model, ss, kv, fi, fo, self.ws_ptr, self.ws_bytes,

@@ -60,7 +60,9 @@ int main() {
   uint64_t pf = 0;
   EXPECT(qt_prefill_workspace_bytes(&c, 100, 4, &pf) == QT_E_SHAPE);
   int32_t n = 0;
-  EXPECT(qt_frame_launch_count(&c, QT_MODE_FULL, &n) == QT_OK && n == 548);
+  EXPECT(qt_frame_launch_count(&c, QT_MODE_FULL, 1, &n) == QT_OK && n == 548);
+  EXPECT(qt_frame_launch_count(&c, QT_MODE_FULL, 32, &n) == QT_OK && n == 576);
+  EXPECT(qt_frame_launch_count(&c, QT_MODE_FULL, 33, &n) == QT_E_INVALID_ARG);
 
   // weight table: a missing tensor, an unknown name and a wrong shape are refused
   // before any device work (the data pointers are never dereferenced)

@@ -153,17 +153,22 @@ def test_frame_and_quantize_argument_errors(qt):
 
 def test_frame_launch_count(qt):
     """Launches per frame: entry + exit + the head GEMM; 5 per Talker layer (QKV,
-    attention, o, gate/up, down); per predictor step a gather, 5 per layer, a head."""
+    attention, o, gate/up, down), 6 from 16 sessions on (the attention's split merge
+    in a launch of its own); per predictor step a gather, 5 per layer, a head."""
     for dims in (synth.FULL, synth.SMALL):
         c = qt.make_cfg(dims)
         t, p, steps = dims.talker.layers, dims.predictor.layers, dims.n_codebooks - 1
-        assert qt.qt_frame_launch_count(c, qt.MODE_FULL) == 3 + 5 * t + steps * (2 + 5 * p)
-        assert qt.qt_frame_launch_count(c, qt.MODE_TALKER) == 3 + 5 * t
-        assert qt.qt_frame_launch_count(c, qt.MODE_PREDICTOR) == 3 + steps * (2 + 5 * p)
-    assert qt.qt_frame_launch_count(qt.make_cfg(synth.FULL), qt.MODE_FULL) == 548
-    with pytest.raises(qt.QtError) as e:
-        qt.qt_frame_launch_count(qt.make_cfg(synth.FULL), 7)
-    assert e.value.status == 1
+        for B in (1, 15, 16, 32):
+            per = 6 if B >= 16 else 5
+            assert qt.qt_frame_launch_count(c, qt.MODE_FULL, B) == 3 + per * t + steps * (2 + 5 * p)
+            assert qt.qt_frame_launch_count(c, qt.MODE_TALKER, B) == 3 + per * t
+            assert qt.qt_frame_launch_count(c, qt.MODE_PREDICTOR, B) == 3 + steps * (2 + 5 * p)
+    assert qt.qt_frame_launch_count(qt.make_cfg(synth.FULL), qt.MODE_FULL, 1) == 548
+    assert qt.qt_frame_launch_count(qt.make_cfg(synth.FULL), qt.MODE_FULL, 32) == 576
+    for mode, B in ((7, 1), (qt.MODE_FULL, 0), (qt.MODE_FULL, 33)):
+        with pytest.raises(qt.QtError) as e:
+            qt.qt_frame_launch_count(qt.make_cfg(synth.FULL), mode, B)
+        assert e.value.status == 1
 
 
 def test_trace_argument_errors(qt):

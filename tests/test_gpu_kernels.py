@@ -53,6 +53,33 @@ def test_small_long_context_full_batch(small_pm, orc_small, lo, hi):
     run_frames(small_pm, orc_small, w, check=[int(np.argmax(L)), int(np.argmin(L))])
 
 
+# ----------------------------------------------------------------- split merge in its own launch
+# From 16 sessions on, the Talker attention's split partials are merged by a launch
+# of their own (k_attn_merge) instead of by the last split to finish.
+def test_sep_merge_boundary_lengths(small_pm, orc_small):
+    """Empty caches and page-boundary lengths at B=16: one-split sessions (written
+    by the split itself) beside sessions merged by the merge launch."""
+    lens = [0, 1, 15, 16, 17, 31, 32, 127, 128, 129, 255, 256, 2, 47, 64, 300]
+    w = small_w("Ssep_edge", batch=len(lens), frames=3, lens=lens)
+    run_frames(small_pm, orc_small, w, check=range(len(lens)))
+
+
+def test_sep_merge_short_sessions(small_pm, orc_small):
+    """20 sessions of at most 3 pages: nearly every session has one split, which the
+    merge launch leaves alone."""
+    lens = [(7 * b) % 40 for b in range(20)]
+    w = small_w("Ssep_short", batch=len(lens), frames=2, lens=lens)
+    run_frames(small_pm, orc_small, w, check=range(len(lens)))
+
+
+def test_sep_merge_long_and_short(small_pm, orc_small):
+    """24 one-page sessions beside 8 of ~4k positions (32 splits each: two merge
+    rounds of 16 partials)."""
+    lens = [5] * 24 + [4090, 4000, 4095, 4050, 4080, 4020, 4060, 4010]
+    w = small_w("Ssep_mix", batch=len(lens), frames=1, lens=lens)
+    run_frames(small_pm, orc_small, w, check=[0, 3, 4, 7, 8, 15, 23, 24])
+
+
 def test_small_graph_replay(small_pm, orc_small):
     w = small_w("Sgraph", batch=6, frames=4, lens=[3, 40, 77, 16, 130, 0], graph=True)
     run_frames(small_pm, orc_small, w, check=range(6), use_graph=True)
@@ -98,8 +125,11 @@ def _forced(w):
     return rng.integers(0, S.cb0_range, size=(w.frames, w.batch, S.n_codebooks)).astype(np.int32)
 
 
-def test_replays_are_bitwise_deterministic_and_equal_eager(small_pm):
-    w = small_w("Sdet", batch=4, frames=3, lens=[600, 5, 333, 48])
+@pytest.mark.parametrize("B", [4, 20])
+def test_replays_are_bitwise_deterministic_and_equal_eager(small_pm, B):
+    """B=4: splits merged by the last to finish; B=20: merged by their own launch."""
+    lens = [600, 5, 333, 48] if B == 4 else [(211 * b + 40) % 900 for b in range(B)]
+    w = small_w(f"Sdet{B}", batch=B, frames=3, lens=lens)
     fi, fz = synth.frame_inputs(w), _forced(w)
     runs = []
     for use_graph in (False, False, True, True):
@@ -112,12 +142,13 @@ def test_replays_are_bitwise_deterministic_and_equal_eager(small_pm):
                 np.testing.assert_array_equal(x, y)
 
 
-@pytest.mark.parametrize("mode", ["full", "predictor"])
-def test_traced_frame_equals_untraced(small_pm, mode):
+@pytest.mark.parametrize("mode,B", [("full", 3), ("predictor", 3), ("full", 16)])
+def test_traced_frame_equals_untraced(small_pm, mode, B):
     """qt_frame_trace runs the same kernels as qt_frame_decode: identical outputs,
-    one timed interval per launch, and launch records that match the frame's structure."""
+    one timed interval per launch, and launch records that match the frame's structure
+    (from 16 sessions on, a split-merge launch after each Talker attention)."""
     import streaming_tts_decode_amd as qt
-    w = small_w("Strace", batch=3, frames=2, lens=[40, 300, 7])
+    w = small_w(f"Strace{B}", batch=B, frames=2, lens=[[40, 300, 7][b % 3] + b for b in range(B)])
     fi, fz = synth.frame_inputs(w), _forced(w)
     plain = _run_eager(_fresh(small_pm, w), w, fi, fz, mode=mode)
     traces = []
@@ -130,13 +161,17 @@ def test_traced_frame_equals_untraced(small_pm, mode):
     t, p = S.talker, S.predictor
     n_steps = S.n_codebooks - 1
     for rec in traces:
-        assert len(rec) == qt.qt_frame_launch_count(small_pm.cfg, qt.MODES[mode])
+        assert len(rec) == qt.qt_frame_launch_count(small_pm.cfg, qt.MODES[mode], B)
         assert rec[0][1] == "frame_begin" and rec[-1][1] == "frame_end"
         assert all(ms > 0 for *_, ms in rec)
         kinds = [k for _, k, _, _ in rec]
         gemms = [li for _, k, li, _ in rec if k == "gemm"]
         n_tl = t.layers if mode == "full" else 0
         assert kinds.count("attn_paged") == n_tl
+        assert kinds.count("attn_merge") == (n_tl if B >= 16 else 0)
+        for i, k in enumerate(kinds):  # a merge follows its attention launch
+            if k == "attn_merge":
+                assert kinds[i - 1] == "attn_paged"
         assert kinds.count("attn_pred") == n_steps * p.layers
         assert kinds.count("embed") == n_steps
         assert len(gemms) == 4 * n_tl + 1 + n_steps * (4 * p.layers + 1)
@@ -155,8 +190,10 @@ def test_traced_frame_equals_untraced(small_pm, mode):
         assert all(li.n_logits == S.code_vocab for li in heads if li.step > 0)
 
 
-def test_page_permutation_invariance(small_pm):
-    w = small_w("Sperm", batch=3, frames=2, lens=[200, 17, 90])
+@pytest.mark.parametrize("B", [3, 18])
+def test_page_permutation_invariance(small_pm, B):
+    lens = [200, 17, 90] if B == 3 else [(97 * b + 17) % 500 for b in range(B)]
+    w = small_w(f"Sperm{B}", batch=B, frames=2, lens=lens)
     fi, fz = synth.frame_inputs(w), _forced(w)
     a = _run_eager(_fresh(small_pm, w, page_seed=1), w, fi, fz)
     b = _run_eager(_fresh(small_pm, w, page_seed=2), w, fi, fz)
@@ -192,9 +229,10 @@ def test_talker_mode_equals_full_mode_codebook0(small_pm):
 
 
 # ----------------------------------------------------------------- device status
-def test_capacity_overflow_is_flagged_and_skipped(small_pm, orc_small):
+@pytest.mark.parametrize("B", [2, 16])
+def test_capacity_overflow_is_flagged_and_skipped(small_pm, orc_small, B):
     from streaming_tts_decode_amd import STATUS_KV_OVERFLOW
-    w = small_w("Sover", batch=2, frames=1, lens=[20, 30])
+    w = small_w(f"Sover{B}", batch=B, frames=1, lens=[20, 30] + [9] * (B - 2))
     dec = _fresh(small_pm, w)
     cap = dec.max_pages * 16
     dec.kv_len[1] = cap  # session 1 is full
@@ -209,21 +247,22 @@ def test_capacity_overflow_is_flagged_and_skipped(small_pm, orc_small):
     assert kv[1] == cap and kv[0] == 21
     # session 0 is still decoded correctly
     t = S.talker
-    kb, vb = synth.gen_kv("Sover", 0, t.layers, 20, t.n_kv, t.head_dim)
+    kb, vb = synth.gen_kv(f"Sover{B}", 0, t.layers, 20, t.n_kv, t.head_dim)
     o = orc_small.run_session("talker", 1, talker_in=fi["talker_in"][:, 0], k_bits=kb, v_bits=vb,
                               length=20)
     compare(dec.logits0.cpu().numpy()[0:1], o["logits0"], S.cb0_range, label="overflow s0")
 
 
-def test_bad_page_and_bad_token_are_flagged(small_pm):
+@pytest.mark.parametrize("B", [2, 16])
+def test_bad_page_and_bad_token_are_flagged(small_pm, B):
     from streaming_tts_decode_amd import STATUS_BAD_PAGE, STATUS_BAD_TOKEN
-    w = small_w("Sbad", batch=2, frames=1, lens=[40, 40])
+    w = small_w(f"Sbad{B}", batch=B, frames=1, lens=[40] * B)
     dec = _fresh(small_pm, w)
     fi = synth.frame_inputs(w)
     pt = dec.page_table.cpu().numpy()
     pt[0, 1] = dec.num_pages + 7  # out of range, read as zeros
     dec.page_table.copy_(dec.torch.from_numpy(pt))
-    forced = np.zeros((2, S.n_codebooks), dtype=np.int32)
+    forced = np.zeros((B, S.n_codebooks), dtype=np.int32)
     forced[1, 2] = S.code_vocab + 3  # out of range
     dec.set_inputs(talker_in=fi["talker_in"][0], forced=forced)
     dec.status.zero_()
