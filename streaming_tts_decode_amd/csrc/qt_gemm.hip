@@ -1373,6 +1373,11 @@ hipError_t launch_gemm_rows(const GemmArgs& a, hipStream_t s, const PrefillQkArg
       if (qk_done) *qk_done = fuse;
       return hipGetLastError();
     }
+    if (a.K % 256 == 0 && m128 * (a.nrows / 64) >= kCUs) {
+      launch_kernel((k_gemm_mx<2, 2, 2, 1, 3, 4>), dim3((unsigned)m128, a.nrows / 64), dim3(512), s, a, none,
+                    0.f);
+      return hipGetLastError();
+    }
     if (a.K % 128 == 0 && m128 * (a.nrows / 64) >= kCUs) {
       launch_kernel((k_gemm_mx<2, 1, 2, 2, 5, 2>), dim3((unsigned)m128, a.nrows / 64), dim3(512), s, a, none,
                     0.f);
