@@ -32,7 +32,7 @@ MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 / bf16 matrix peak, published
 # change, the entry no longer applies and `traffic` is reported as null.
 PMC_TRAFFIC = {
     # profiles/gemm_attention_C4_pmc_traffic.md
-    ("C4", "k_attn_paged"): {"digest": "5910e3e7fb945965", "bytes_per_launch": 164661099},
+    ("C4", "k_attn_paged"): {"digest": "09285f1884fd95bb", "bytes_per_launch": 164666749},
 }
 KERNEL_SOURCES = ["qt_gemm.hip", "qt_kernels.hip", "qt_device.h", "qt_internal.h"]
 
